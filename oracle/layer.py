@@ -1,0 +1,146 @@
+"""The NVFP4-forward / MXFP8-backward expert layer, end to end (test infrastructure).
+
+Pages: agihunt.info page, "Confirmed" (expert layers' forward in NVFP4,
+backpropagation in MXFP8 with requantisation and stochastic rounding; 4/6
+activation quantisation); lhc.media page, the paragraphs on precisions (FP32
+master weights, some BF16 activations), on the backward transposition and
+stochastic rounding, and on dispatching NVFP4 inputs to the experts;
+fourweekmba.com page, "Update" (a token goes to 8 of 384 experts).
+
+Forward (readings where the pages are silent: weights use the plain
+amax->6 scale with one tensor scale per expert matrix; X is quantised once,
+before dispatch, with one tensor scale; H gets one tensor scale per expert):
+
+ 1. Wq_up[e] = NVFP4(W_up[e] [F, d], mode 6); Wq_down[e] = NVFP4(W_down[e] [d, F], mode 6)
+ 2. route: top-k indices and gates; stable permutation by expert
+ 3. Xq = NVFP4(x [T, d], 4/6, one tensor scale)
+ 4. Xq_perm = rows of Xq in expert order (codes and block scales; S_x shared)
+ 5. U = bf16(exact Xq_perm_e . Wq_up[e]^T)
+ 6. H = silu(U) (correctly rounded float32); Hq = NVFP4(H, 4/6, one group per expert)
+ 7. Yp = float32(exact Hq_e . Wq_down[e]^T)
+ 8. y[t] = bf16(acc), acc = 0; for j = 0..k-1: acc = fl(acc + fl(g[t, j] * Yp[row(t, j)]))
+
+Backward (gradients dY, dU in MXFP8 with RNE; forward operands requantised with
+stochastic rounding, stream id 16 * layer + role, role 0 = X_T, 1 = H_T,
+2 = W_up_T, 3 = W_down_T):
+
+ 1. dYp[row(t, j)] = fl(g[t, j] * dy[t]); MXFP8 row-wise [A, d] and transposed per expert
+ 2. Wd_T = requant_sr_t(Wq_down, groups of d rows) -> [E][F][d]
+ 3. dH = float32(exact dYp_row . Wd_T[e]^T)                 [A, F]
+ 4. H_T = requant_sr_t(Hq, groups = experts)                -> [E][F][pad32 M_e]
+ 5. dW_down[e] = float32(exact dYp_col[e] . H_T[e]^T)        [E, d, F]
+ 6. dU = fl(dH * dsilu(U)); MXFP8 row-wise and transposed per expert
+ 7. Wu_T = requant_sr_t(Wq_up, groups of F rows)             -> [E][d][F]
+ 8. dXp = float32(exact dU_row . Wu_T[e]^T)                   [A, d]
+ 9. X_T = requant_sr_t(Xq_perm, groups = experts, S_x)       -> [E][d][pad32 M_e]
+10. dW_up[e] = float32(exact dU_col[e] . X_T[e]^T)          [E, F, d]
+11. dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dXp[row(t, j)])
+"""
+import numpy as np
+
+from . import formats as fmt
+from . import gemm
+from . import mxfp8 as mx
+from . import nvfp4 as nv
+from . import route
+from . import silu
+
+ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
+
+
+def quantize_weights(W_up, W_down):
+    E, F, d = W_up.shape
+    wu = nv.nvfp4_quantize(W_up.reshape(E * F, d), nv.MODE_6, np.arange(E + 1) * F)
+    wd = nv.nvfp4_quantize(W_down.reshape(E * d, F), nv.MODE_6, np.arange(E + 1) * d)
+    return wu, wd
+
+
+def forward(x_bf16, W_up, W_down, logits, k, bias=None, weights_q=None):
+    """x_bf16 [T, d] uint16 bf16 bits; W_up [E, F, d], W_down [E, d, F] float32."""
+    T, d = x_bf16.shape
+    E, F, _ = W_up.shape
+    wu, wd = quantize_weights(W_up, W_down) if weights_q is None else weights_q
+    idx, gates = route.topk_gates(logits, k, bias)
+    P = route.permutation(idx, E)
+    off, perm, inv = P["off"], P["perm"], P["inv_perm"]
+    xq = nv.nvfp4_quantize(x_bf16, nv.MODE_46)
+    src = perm.astype(np.int64) // k
+    xq_perm = dict(codes=xq["codes"][src], sf=xq["sf"][src], ts=xq["ts"])
+    A64 = nv.nvfp4_exact_f64(xq_perm["codes"], xq_perm["sf"], xq_perm["ts"])
+    Bup = nv.nvfp4_exact_f64(wu["codes"], wu["sf"], wu["ts"], np.arange(E + 1) * F).reshape(E, F, d)
+    U = fmt.f64_to_bf16(gemm.grouped_nt(A64, Bup, off))
+    H = silu.silu_f32(U)
+    hq = nv.nvfp4_quantize(H, nv.MODE_46, off)
+    H64 = nv.nvfp4_exact_f64(hq["codes"], hq["sf"], hq["ts"], off)
+    Bdn = nv.nvfp4_exact_f64(wd["codes"], wd["sf"], wd["ts"], np.arange(E + 1) * d).reshape(E, d, F)
+    Yp = gemm.grouped_nt(H64, Bdn, off).astype(np.float32)
+    y = combine(Yp, gates, inv, k)
+    return dict(wu=wu, wd=wd, idx=idx, gates=gates, perm=P, xq=xq, xq_perm=xq_perm,
+                U=U, hq=hq, Yp=Yp, y=y, dims=(T, d, F, E, k))
+
+
+def combine(Yp, gates, inv, k):
+    """y[t] = bf16(sum_j fl(g[t,j] * Yp[row(t,j)])) in order j = 0..k-1."""
+    T = gates.shape[0]
+    d = Yp.shape[1]
+    acc = np.zeros((T, d), dtype=np.float32)
+    inv = np.asarray(inv, dtype=np.int64).reshape(T, k)
+    for j in range(k):
+        acc = (acc + (gates[:, j:j + 1] * Yp[inv[:, j]]).astype(np.float32)).astype(np.float32)
+    return fmt.bf16_round(acc)
+
+
+def unpermute_sum(dXp, inv, T, k):
+    """dx[t] = bf16(sum_j dXp[row(t,j)]) in order j = 0..k-1."""
+    d = dXp.shape[1]
+    acc = np.zeros((T, d), dtype=np.float32)
+    inv = np.asarray(inv, dtype=np.int64).reshape(T, k)
+    for j in range(k):
+        acc = (acc + dXp[inv[:, j]]).astype(np.float32)
+    return fmt.bf16_round(acc)
+
+
+def gated_grad_rows(dy_bf16, gates, perm, k):
+    """dYp[row] = fl(g[t, j] * dy[t]) for the assignment a = perm[row] = t*k + j."""
+    dy = fmt.bf16_to_f32(dy_bf16)
+    a = np.asarray(perm, dtype=np.int64)
+    g = np.asarray(gates, dtype=np.float32).reshape(-1)[a]
+    return (g[:, None] * dy[a // k]).astype(np.float32)
+
+
+def backward(fw, dy_bf16, seed=1, layer=0):
+    T, d, F, E, k = fw["dims"]
+    P = fw["perm"]
+    off, perm, inv = P["off"], P["perm"], P["inv_perm"]
+    sid = lambda role: 16 * layer + role
+    dYp = gated_grad_rows(dy_bf16, fw["gates"], perm, k)
+    dy_row_c, dy_row_s = mx.quantize_rowwise(dYp, mx.RNE)
+    dy_col_c, dy_col_s = mx.quantize_transposed(dYp, off, mx.RNE)
+    wd = fw["wd"]
+    wdT_c, wdT_s = mx.requant_sr_t(wd["codes"], wd["sf"], wd["ts"], np.arange(E + 1) * d,
+                                   True, seed, sid(ROLE_WDOWN))
+    WdT = np.stack(mx.dequant_transposed(wdT_c, wdT_s, np.arange(E + 1) * d, F))   # [E, F, d]
+    dH = gemm.grouped_nt(mx.dequant_rowwise(dy_row_c, dy_row_s), WdT, off).astype(np.float32)
+    hq = fw["hq"]
+    hT_c, hT_s = mx.requant_sr_t(hq["codes"], hq["sf"], hq["ts"], off, True, seed, sid(ROLE_H))
+    HT = mx.dequant_transposed(hT_c, hT_s, off, F)
+    dYc = mx.dequant_transposed(dy_col_c, dy_col_s, off, d)
+    dW_down = gemm.wgrad(dYc, HT).astype(np.float32)
+    dU = (dH * silu.dsilu_f32(fw["U"])).astype(np.float32)
+    du_row_c, du_row_s = mx.quantize_rowwise(dU, mx.RNE)
+    du_col_c, du_col_s = mx.quantize_transposed(dU, off, mx.RNE)
+    wu = fw["wu"]
+    wuT_c, wuT_s = mx.requant_sr_t(wu["codes"], wu["sf"], wu["ts"], np.arange(E + 1) * F,
+                                   True, seed, sid(ROLE_WUP))
+    WuT = np.stack(mx.dequant_transposed(wuT_c, wuT_s, np.arange(E + 1) * F, d))   # [E, d, F]
+    dXp = gemm.grouped_nt(mx.dequant_rowwise(du_row_c, du_row_s), WuT, off).astype(np.float32)
+    xp = fw["xq_perm"]
+    xT_c, xT_s = mx.requant_sr_t(xp["codes"], xp["sf"], xp["ts"], off, False, seed, sid(ROLE_X))
+    XT = mx.dequant_transposed(xT_c, xT_s, off, d)
+    dUc = mx.dequant_transposed(du_col_c, du_col_s, off, F)
+    dW_up = gemm.wgrad(dUc, XT).astype(np.float32)
+    dx = unpermute_sum(dXp, inv, T, k)
+    return dict(dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),
+                wdT=(wdT_c, wdT_s), dH=dH, hT=(hT_c, hT_s), dW_down=dW_down, dU=dU,
+                du_row=(du_row_c, du_row_s), du_col=(du_col_c, du_col_s), wuT=(wuT_c, wuT_s),
+                dXp=dXp, xT=(xT_c, xT_s), dW_up=dW_up, dx=dx)
