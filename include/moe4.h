@@ -1,0 +1,279 @@
+/*
+ * moe4.h - C ABI of the NVFP4-forward / MXFP8-backward MoE expert-layer library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is the expert-layer recipe reported on the pages
+ * about Thinking Machines Lab's "End-to-End 4-Bit Training" post: NVFP4 in the
+ * expert layers' forward pass with a dedicated kernel, MXFP8 in the backward
+ * pass after a dequantise -> transpose -> requantise step with stochastic
+ * rounding (agihunt.info page, "Confirmed"; lhc.media page, paragraphs on
+ * NVFP4, on transposition and on stochastic rounding), and Four-Over-Six
+ * activation quantisation (agihunt.info page, "Confirmed").
+ *
+ * Conventions (every entry point):
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates no device memory; where scratch is needed the caller passes a
+ *    workspace (ws, ws_bytes) sized by the matching *_ws_bytes() query.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Each call
+ *    enqueues its kernels on that stream and returns without synchronising.
+ *  - Return value: 0 on success, a negative MOE4_E* code on error.  On a
+ *    host-side validation error nothing is enqueued; moe4_last_error() returns
+ *    a message for the calling thread.  Nothing throws across the ABI.
+ *  - Preconditions that need the device's data (monotone offsets, indices in
+ *    range, finite inputs) are the caller's; kernels clamp indices so that a
+ *    violated precondition gives wrong values, never an out-of-bounds access.
+ *  - Sizes are int64_t; offsets and indices are int32_t device arrays.
+ *  - Pointers must be 16-byte aligned.
+ *
+ * Formats (row-major everywhere):
+ *  NVFP4: codes [R, C/2] uint8, element 2j of a row in the low nibble of byte
+ *         j (E2M1: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign); block
+ *         scales [R, C/16] uint8 E4M3 (one per 16 consecutive elements of a
+ *         row); one float32 tensor scale per row group.  Value of an element:
+ *         fl(fl(q * sc) * S).
+ *  MXFP8: codes [R, C] uint8 E4M3FN; scales [R, C/32] uint8 E8M0 (value
+ *         2**(byte - 127)), one per 32 consecutive elements along the block
+ *         direction.
+ *  Group-major padded (transposed MXFP8): rows of the source matrix [R, C]
+ *         are cut into groups by off[G+1]; group g is stored at code offset
+ *         C * off_pad[g] as a row-major block [C][P_g], P_g = pad32(R_g) =
+ *         off_pad[g+1] - off_pad[g], padded with zero codes; its scales at
+ *         offset C * off_pad[g] / 32 as [C][P_g / 32].  MX blocks run along
+ *         the source rows and never straddle a group.
+ */
+#ifndef MOE4_H
+#define MOE4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ codes */
+#define MOE4_OK 0
+#define MOE4_EINVAL (-1)      /* bad shape, mode, dtype or NULL pointer        */
+#define MOE4_EALIGN (-2)      /* a pointer is not 16-byte aligned              */
+#define MOE4_EWORKSPACE (-3)  /* workspace missing or too small                */
+#define MOE4_EHIP (-4)        /* a HIP launch failed                           */
+#define MOE4_EUNSUPPORTED (-5)
+
+#define MOE4_BF16 0
+#define MOE4_F32 1
+
+#define MOE4_NVFP4_6 6        /* block scale maps the block amax to 6          */
+#define MOE4_NVFP4_4OVER6 46  /* Four-Over-Six: keep the better of amax->6, ->4 */
+
+#define MOE4_PRE_NONE 0
+#define MOE4_PRE_SILU 1       /* quantise silu(x) (x must be bf16)             */
+
+#define MOE4_RNE 0
+#define MOE4_SR 1
+
+/* ------------------------------------------------------------ diagnostics */
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe4_last_error(void);
+/* Library version string. */
+const char* moe4_version(void);
+
+/* ---------------------------------------------------------------- NVFP4 */
+/*
+ * nvfp4_quant_46 - two-level NVFP4 quantisation with the Four-Over-Six choice.
+ * Pages: lhc.media page, paragraph on NVFP4 (4-bit values, a scale shared by
+ * sixteen values, about 4.5 bits per value); agihunt.info page, "Confirmed"
+ * (activation quantisation chooses between two scaling factors).
+ *
+ * x            [rows, cols] bf16 (dtype MOE4_BF16) or float32 (MOE4_F32).
+ * group_row_off  NULL (one group) or [n_groups+1] ascending row offsets with
+ *              off[0] = 0 and off[n_groups] = rows; each group gets its own
+ *              tensor scale.
+ * mode         MOE4_NVFP4_6 or MOE4_NVFP4_4OVER6.
+ * pre_op       MOE4_PRE_NONE, or MOE4_PRE_SILU to quantise the correctly
+ *              rounded float32 silu(x) of a bf16 x.
+ * codes        out [rows, cols/2];  sf  out [rows, cols/16];
+ * tensor_scale out [n_groups] float32:
+ *              S_g = fl(amax_g / (m_max * 448)), m_max = 4 (4/6) or 6 (mode 6);
+ *              S_g = 1 for an all-zero group.
+ * Per 16-block, candidate m in {6, 4}: sc_m = e4m3_rne(fl(amax_b / fl(m*S)));
+ * q_i = e2m1_rne(fl(x_i * fl(1 / fl(dec(sc_m) * S)))) (signed zeros when sc_m
+ * or the effective scale is 0); error = sequential float32 sum over i of
+ * fl(t*t), t = fl(x_i - fl(fl(q_i*sc_m)*S)); 4 is kept iff err_4 < err_6.
+ * cols % 16 == 0, n_groups >= 1.  ws: nvfp4_quant_46_ws_bytes(n_groups).
+ */
+int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
+                   const int32_t* group_row_off, int32_t n_groups, int mode, int pre_op,
+                   uint8_t* codes, uint8_t* sf, float* tensor_scale,
+                   void* ws, size_t ws_bytes, void* stream);
+size_t nvfp4_quant_46_ws_bytes(int32_t n_groups);
+
+/*
+ * nvfp4_dequant - float32 values fl(fl(q*sc)*S) of an NVFP4 tensor (test and
+ * debugging aid).  ts_per_group = 0: ts[0] applies to every row.
+ */
+int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
+                  const int32_t* group_row_off, int32_t n_groups, int64_t rows, int64_t cols,
+                  float* out, void* stream);
+
+/* ---------------------------------------------------------------- MXFP8 */
+/*
+ * mxfp8_requant_sr_T - NVFP4 [rows, cols] -> dequantise (float32, as
+ * nvfp4_dequant) -> transpose -> MXFP8 with stochastic rounding, in the
+ * group-major padded layout.  Pages: lhc.media page, the paragraphs on
+ * transposition regrouping the values that share a scale and on requantising
+ * the dequantised, transposed values into MXFP8 with stochastic rounding.
+ *
+ * group_row_off / group_off_pad  [n_groups+1] unpadded and padded (pad32)
+ *              row offsets (device); n_groups >= 1.
+ * ts, ts_per_group  tensor scales: one per group, or ts[0] for all rows.
+ * seed, stream_id   stochastic-rounding key.
+ * out_codes    [cols * off_pad[n_groups]], out_sf [cols * off_pad[n_groups] / 32].
+ * MX scale per 32-block: e = least integer with amax <= 448 * 2**e, clamped to
+ * [-127, 127] (e = -127 for an all-zero block).  Element i = r * cols + c (r, c
+ * in the source matrix) rounds |w| = |v| * 2**-e up to the next E4M3 value iff
+ * floor(frac * 2**16) + r16_i >= 2**16, where frac is |w|'s position between
+ * its two E4M3 neighbours and r16_i is 16 bits of the counter hash
+ *   word_j = fmix32(lo32(j) ^ fmix32(K ^ hi32(j))),  j = i >> 1,
+ *   K = fmix32(fmix32(fmix32(lo32(seed)) ^ hi32(seed)) ^ stream_id),
+ *   r16_i = (word_j >> (16 * (i & 1))) & 0xFFFF
+ * (fmix32: MurmurHash3's 32-bit finaliser).  cols % 32 == 0.
+ * max_padded_rows: an upper bound of off_pad[n_groups] (e.g. rows + 31*n_groups)
+ * used to size the grid; the kernels read the real bound from the device.
+ */
+int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
+                       int64_t rows, int64_t cols, const int32_t* group_row_off,
+                       const int32_t* group_off_pad, int32_t n_groups, int64_t max_padded_rows,
+                       uint64_t seed, uint32_t stream_id,
+                       uint8_t* out_codes, uint8_t* out_sf, void* stream);
+
+/*
+ * mxfp8_quant - MXFP8 quantisation of a gradient.  The value of source element
+ * (r, c) is:
+ *   v = x[src(r), c]                                    (no options)
+ *   v = fl(row_scale[a] * x[a / map_div, c]), a = row_map[r]   (row_map given)
+ *   v = fl(x[r, c] * dsilu(u[r, c]))                    (dsilu_src given)
+ * with x bf16 or float32 (dtype), u bf16, dsilu the correctly rounded float32
+ * silu'.  row_map and dsilu_src are exclusive.  rows = number of output rows.
+ * transpose = 0: blocks of 32 along cols, out [rows, cols] + [rows, cols/32].
+ * transpose = 1: blocks along rows per group, group-major padded layout
+ *                (group_row_off, group_off_pad, n_groups, max_padded_rows as in
+ *                mxfp8_requant_sr_T).
+ * rnd: MOE4_RNE, or MOE4_SR with (seed, stream_id) and the same random words
+ *      as mxfp8_requant_sr_T (element index r * cols + c of the [rows, cols]
+ *      matrix of values v).  Pages: the MXFP8 backward of the agihunt.info
+ *      page, "Confirmed".  cols % 32 == 0.
+ */
+int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
+                const int32_t* row_map, int32_t map_div, const float* row_scale,
+                const uint16_t* dsilu_src, int transpose,
+                const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
+                int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
+                uint8_t* out_codes, uint8_t* out_sf, void* stream);
+
+/* ------------------------------------------------------------- routing */
+/*
+ * moe_route_topk - top-k routing and the stable expert permutation.  The pages
+ * describe a token routed to 8 of 384 experts and inputs dispatched to the
+ * experts that hold them (fourweekmba.com page, "Update"; lhc.media page,
+ * paragraph on communication).
+ * logits [T, E] float32, bias [E] or NULL.  z = fl(logit + bias); top-k in
+ * descending z, equal values by lower expert index; gates
+ * g_j = fl(w_j / s), w_j = RN32(exp_f64(fl(z_j - z_0))), s = sequential fp32 sum.
+ * Outputs: topk_idx [T, k] int32, gates [T, k] float32, expert_off [E+1],
+ * expert_off_pad [E+1] (pad32 of the counts), perm [T*k] (row -> assignment
+ * a = t*k + j, rows ordered by (expert, token)), inv_perm [T*k].
+ * 1 <= k <= E <= 1024, k <= 16.  ws: moe_route_topk_ws_bytes(T, E, k).
+ */
+int moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                   int32_t* topk_idx, float* gates, int32_t* expert_off, int32_t* expert_off_pad,
+                   int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+size_t moe_route_topk_ws_bytes(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_gather_rows - NVFP4 dispatch: out row r = source row perm[r] / k (codes
+ * and block scales; the tensor scale is shared).  The local stand-in for the
+ * pages' NVFP4 dispatch (lhc.media page, paragraph on communication).
+ * n_rows_out = T * k; cols % 16 == 0.
+ */
+int moe_gather_rows(const uint8_t* codes, const uint8_t* sf, int64_t n_rows_in, int64_t cols,
+                    const int32_t* perm, int32_t k, int64_t n_rows_out,
+                    uint8_t* out_codes, uint8_t* out_sf, void* stream);
+
+/* --------------------------------------------------------- grouped GEMMs */
+/*
+ * moe_grouped_gemm_fwd - C[rows of e] = A[rows of e] . B[e]^T with NVFP4 A
+ * [M_total, K] (tensor scale a_ts[0], or a_ts[e] if a_ts_per_group) and NVFP4
+ * B [E, N, K] (tensor scale b_ts[e]); rows grouped by expert_off [E+1].
+ * Pages: agihunt.info page, "Confirmed" (NVFP4 expert-layer forward with a
+ * dedicated kernel); fourweekmba.com page, "Why the Gain Is 8%, Not 3x".
+ * The block-scaled products are exact (operands dequantised exactly to f16),
+ * accumulated in float32; the tensor scales are applied in the epilogue.
+ * c [M_total, N]: bf16 (c_dtype MOE4_BF16) or float32.  K % 64 == 0,
+ * N % 64 == 0.
+ */
+int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts, int a_ts_per_group,
+                         const uint8_t* b_codes, const uint8_t* b_sf, const float* b_ts,
+                         const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
+                         void* c, int c_dtype, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd_dgrad - C[rows of e] = A[rows of e] . B[e]^T with MXFP8
+ * A [M_total, K] (+ scales [M_total, K/32]) and MXFP8 B [E, N, K] (+ [E, N,
+ * K/32]); float32 C [M_total, N].  Native block-scaled FP8 MFMA (exact
+ * products, float32 accumulation).  K % 128 == 0, N % 64 == 0.
+ * Pages: agihunt.info page, "Confirmed" (MXFP8 backpropagation).
+ */
+int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
+                               const uint8_t* b_codes, const uint8_t* b_sf,
+                               const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
+                               float* c, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd_wgrad - dW[e] = A_e . B_e^T over expert e's padded token
+ * dimension: A and B in the group-major padded MXFP8 layout, A_e [N1][P_e],
+ * B_e [N2][P_e] with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
+ * beta = 0 overwrites (experts with no rows get zeros), beta = 1 accumulates.
+ * N1 % 64 == 0, N2 % 64 == 0.
+ */
+int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
+                               const uint8_t* b_codes, const uint8_t* b_sf,
+                               const int32_t* expert_off_pad, int32_t E, int64_t N1, int64_t N2,
+                               float* dw, float beta, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd - dgrad and wgrad of one expert linear layer in one
+ * call (both enqueued on `stream`, dgrad first).
+ */
+int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_sf,           /* [M_total, Nout] row-wise */
+                         const uint8_t* wT_codes, const uint8_t* wT_sf,           /* [E, Nin, Nout]           */
+                         const uint8_t* dyT_codes, const uint8_t* dyT_sf,         /* group-major [Nout][P_e]  */
+                         const uint8_t* xT_codes, const uint8_t* xT_sf,           /* group-major [Nin][P_e]   */
+                         const int32_t* expert_off, const int32_t* expert_off_pad, int32_t E,
+                         int64_t M_total, int64_t Nin, int64_t Nout,
+                         float* dx, float* dw, float beta, void* stream);
+
+/* ----------------------------------------------------- combine / scatter */
+/*
+ * moe_combine - y[t] = bf16(acc), acc = 0; for j = 0..k-1:
+ * acc = fl(acc + fl(gates[t,j] * yp[inv_perm[t*k+j]])).  yp [T*k, d] float32.
+ */
+int moe_combine(const float* yp, const float* gates, const int32_t* inv_perm, int64_t T, int32_t k,
+                int64_t d, uint16_t* y, void* stream);
+
+/*
+ * moe_unpermute_sum - dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dxp[inv_perm[t*k+j]]).
+ */
+int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
+                      uint16_t* dx, void* stream);
+
+/*
+ * moe_silu_eval - correctly rounded float32 silu(u) and silu'(u) of bf16 u
+ * (either output may be NULL).  Test aid for the activation fused into
+ * nvfp4_quant_46 (MOE4_PRE_SILU) and mxfp8_quant (dsilu_src).
+ */
+int moe_silu_eval(const uint16_t* u, int64_t n, float* silu_out, float* dsilu_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE4_H */

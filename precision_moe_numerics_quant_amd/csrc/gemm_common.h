@@ -1,0 +1,43 @@
+// Shared pieces of the expert-grouped GEMM kernels (gfx950).
+#pragma once
+#include "moe4_internal.h"
+
+namespace moe4 {
+
+// Find which expert a flat M-tile index belongs to, for rows grouped by
+// off[0..E] and BM rows per tile: tiles of expert e are
+// [sum_{e'<e} ceil(M_e'/BM), ...).  Executed by every wave of the block (each
+// gets the same answer).  Returns false when the index is past the last tile.
+__device__ inline bool find_m_tile(const int32_t* __restrict__ off, int E, int BM, int64_t tile, int& e_out,
+                                   int64_t& tile_in_e) {
+  const int lane = threadIdx.x & 63;
+  int64_t run = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int cnt = 0;
+    if (e < E) {
+      const int m = off[e + 1] - off[e];
+      cnt = m > 0 ? (m + BM - 1) / BM : 0;
+    }
+    int inc = cnt;  // inclusive prefix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    const int total = __shfl(inc, 63, 64);
+    if (tile < run + total) {
+      const bool hit = (tile < run + inc) && (tile >= run + inc - cnt);
+      const unsigned long long b = __ballot(hit);
+      const int src = __ffsll((long long)b) - 1;
+      const int excl = __shfl(inc - cnt, src, 64);
+      e_out = e0 + src;
+      tile_in_e = tile - run - excl;
+      return true;
+    }
+    run += total;
+  }
+  return false;
+}
+
+}  // namespace moe4

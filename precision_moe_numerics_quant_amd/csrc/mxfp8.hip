@@ -1,0 +1,396 @@
+// MXFP8 quantisation kernels (gfx950): the transposed stochastic-rounding
+// requantisation of NVFP4 forward operands, and the row-wise / transposed
+// quantisation of gradients.
+//
+// The requantisation follows the lhc.media page's description of the backward
+// pass (dequantise the forward values, transpose them at higher precision,
+// requantise into MXFP8 with stochastic rounding, because the transpose
+// regroups the values that share a scale).  MXFP8 = E4M3 elements with one E8M0
+// scale per 32 values, the 32 running along the GEMM contraction, which after
+// the transpose is the token (row) dimension of each expert group.
+//
+// Tiling of the transposed kernels: a workgroup of 256 threads takes 32
+// padded rows (one MX block, never straddling a group) x 128 columns.  The
+// tile is staged through LDS transposed; each wave then owns 32 columns, each
+// lane an adjacent column pair over 8 rows, so the pair shares one 32-bit
+// random word and the lane writes 8 contiguous output bytes per column.  The
+// block amax is a 4-lane reduction (xor 16, xor 32).
+#include "act.h"
+#include "moe4_internal.h"
+
+namespace moe4 {
+
+constexpr int TR = 32;    // rows per tile (one MX block)
+constexpr int TC = 128;   // columns per tile
+constexpr int MXT = 256;  // threads
+
+__device__ inline int find_group(const int32_t* off, int G, int64_t r) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// MX scale exponent of a block amax: least e with amax <= 448 * 2**e, clamped
+// to [-127, 127]; -127 for amax = 0.
+__device__ inline int mx_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  int ex = (int)((b >> 23) & 0xFFu);
+  if (ex < 9) return -127;  // amax < 2**-118 <= 448 * 2**-127
+  int E = ex - 127;
+  int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;  // mantissa <= 1.75
+  return e > 127 ? 127 : (e < -127 ? -127 : e);
+}
+
+// E4M3 byte of w (|w| <= 448): RNE, or SR with the 16-bit word r16.
+template <bool SR>
+__device__ inline uint32_t mx_round(float w, uint32_t r16) {
+  if (SR)
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, w, r16 << 16, 1.0f, 0) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(w, 0.0f, 0, false) & 0xFFu;
+}
+
+// Random word of element pair j = i >> 1 (base = seed/stream key).
+__device__ inline uint32_t sr_word(uint32_t base, uint64_t j) {
+  uint32_t key = fmix32(base ^ (uint32_t)(j >> 32));
+  return fmix32((uint32_t)j ^ key);
+}
+
+// Quantise, for one lane, 8 rows x 2 adjacent columns (c, c+1) of values
+// v[row][0..1] that belong to one 32-row MX block shared with the lanes at
+// xor 16 and xor 32; writes 8 code bytes per column and (rseg == 0) the
+// scale bytes.  src_row0: source row of the lane's first row (only for SR
+// indices); rows beyond the group are zeros already.
+template <bool SR>
+__device__ inline void mx_quant_pair_T(const float (&v)[8][2], int rseg, int64_t src_row0, int64_t C, int64_t c,
+                                       uint32_t base, uint8_t* out_c0, uint8_t* out_c1, uint8_t* sf_c0,
+                                       uint8_t* sf_c1) {
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a0 = fmaxf(a0, fabsf(v[i][0]));
+    a1 = fmaxf(a1, fabsf(v[i][1]));
+  }
+  a0 = fmaxf(a0, __shfl_xor(a0, 16, 64));
+  a1 = fmaxf(a1, __shfl_xor(a1, 16, 64));
+  a0 = fmaxf(a0, __shfl_xor(a0, 32, 64));
+  a1 = fmaxf(a1, __shfl_xor(a1, 32, 64));
+  const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
+  const float p0 = __builtin_amdgcn_ldexpf(1.0f, -e0), p1 = __builtin_amdgcn_ldexpf(1.0f, -e1);
+  uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+    if (SR) word = sr_word(base, (uint64_t)((src_row0 + i) * C + c) >> 1);
+    uint32_t b0 = mx_round<SR>(v[i][0] * p0, word & 0xFFFFu);
+    uint32_t b1 = mx_round<SR>(v[i][1] * p1, word >> 16);
+    if (i < 4) { lo0 |= b0 << (8 * i); lo1 |= b1 << (8 * i); }
+    else { hi0 |= b0 << (8 * (i - 4)); hi1 |= b1 << (8 * (i - 4)); }
+  }
+  *reinterpret_cast<u32x2*>(out_c0) = u32x2{lo0, hi0};
+  *reinterpret_cast<u32x2*>(out_c1) = u32x2{lo1, hi1};
+  if (rseg == 0) {
+    *sf_c0 = (uint8_t)(e0 + 127);
+    *sf_c1 = (uint8_t)(e1 + 127);
+  }
+}
+
+// Tile coordinates shared by the transposed kernels.  Returns false if the
+// tile lies beyond the padded extent.
+struct TileT {
+  int g;
+  int64_t pr_in_g;   // first padded row of the tile within its group
+  int64_t P;         // padded rows of the group
+  int64_t src0;      // source row of the tile's first row
+  int64_t nvalid;    // valid (unpadded) rows in the tile (0..32)
+  int64_t out_base;  // code offset of the group block
+};
+
+// A padded extent beyond max_pr (the caller's output size) or a group end past
+// R source rows violates the call's preconditions: such tiles are skipped or
+// clamped, never accessed out of bounds.
+__device__ inline bool tile_coords(const int32_t* off, const int32_t* offp, int G, int64_t C, int64_t R,
+                                   int64_t max_pr, int64_t rt, TileT& t) {
+  const int64_t pr = rt * TR;
+  if (pr >= (int64_t)offp[G] || (int64_t)offp[G] > max_pr) return false;
+  t.g = find_group(offp, G, pr);
+  t.pr_in_g = pr - offp[t.g];
+  t.P = (int64_t)offp[t.g + 1] - offp[t.g];
+  t.src0 = (int64_t)off[t.g] + t.pr_in_g;
+  const int64_t gend = (int64_t)off[t.g + 1] < R ? (int64_t)off[t.g + 1] : R;
+  int64_t n = gend - t.src0;
+  t.nvalid = n < 0 ? 0 : (n > TR ? TR : n);
+  t.out_base = C * (int64_t)offp[t.g];
+  return true;
+}
+
+// ---------------------------------------------------------------- requant-T
+template <bool SR>
+__global__ void __launch_bounds__(MXT) k_requant_T(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
+                                                   const float* __restrict__ ts, int ts_per_group, int64_t C,
+                                                   const int32_t* __restrict__ off, const int32_t* __restrict__ offp,
+                                                   int G, int64_t R, int64_t max_pr, int64_t n_ct, uint32_t base,
+                                                   uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s) {
+  __shared__ __attribute__((aligned(16))) uint8_t lc[TC / 2][TR];  // [byte column][row]
+  __shared__ __attribute__((aligned(16))) uint8_t ls[TC / 16][TR];  // [scale column][row]
+  const int64_t ct = blockIdx.x % n_ct, rt = blockIdx.x / n_ct;
+  TileT t;
+  if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
+  const int64_t c0 = ct * TC;
+  const int tid = threadIdx.x;
+  {  // stage codes: thread -> row tid/8, 8 bytes at byte column (tid%8)*8
+    const int rr = tid >> 3, bc = (tid & 7) * 8;
+    u32x2 w = {0u, 0u};
+    if (rr < t.nvalid && c0 / 2 + bc < C / 2)
+      w = *reinterpret_cast<const u32x2*>(codes + (t.src0 + rr) * (C / 2) + c0 / 2 + bc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lc[bc + j][rr] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+    // scales: thread -> row tid/8, scale column tid%8
+    const int scol = tid & 7;
+    uint8_t s = 0;
+    if (rr < t.nvalid && c0 / 16 + scol < C / 16) s = sf[(t.src0 + rr) * (C / 16) + c0 / 16 + scol];
+    ls[scol][rr] = s;
+  }
+  __syncthreads();
+  const int w = tid >> 6, l = tid & 63;
+  if (c0 + 32 * w >= C) return;  // C % 32 == 0: the wave's 32 columns are all in or all out
+  const int cp = l & 15, rseg = l >> 4;
+  const float S = ts[ts_per_group ? t.g : 0];
+  u32x2 cb = *reinterpret_cast<const u32x2*>(&lc[16 * w + cp][rseg * 8]);
+  u32x2 sb = *reinterpret_cast<const u32x2*>(&ls[2 * w + (cp >> 3)][rseg * 8]);
+  float v[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t byte = (cb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    uint32_t sbyte = (sb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    float scf = e4m3_to_f32(sbyte);
+    f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, scf, 0);
+    float m = mant_factor(scf);
+    float q0 = scf == 0.0f ? 0.0f * p[0] : p[0] * m;   // exact q * sc
+    float q1 = scf == 0.0f ? 0.0f * p[1] : p[1] * m;
+    v[i][0] = q0 * S;                                   // fl(fl(q*sc)*S)
+    v[i][1] = q1 * S;
+  }
+  const int64_t c = c0 + 32 * w + 2 * cp;
+  const int64_t orow = t.pr_in_g + rseg * 8;
+  uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
+  uint8_t* o1 = o0 + t.P;
+  uint8_t* s0 = out_s + t.out_base / 32 + c * (t.P / 32) + t.pr_in_g / 32;
+  uint8_t* s1 = s0 + t.P / 32;
+  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o1, s0, s1);
+}
+
+// ------------------------------------------------------ gradient value loads
+// Source value of output row r, columns c..c+3 (float32).
+struct GradSrc {
+  const void* x;
+  int dtype;
+  const int32_t* row_map;
+  int map_div;
+  const float* row_scale;
+  const uint16_t* dsilu_src;
+};
+
+template <int DT>
+__device__ inline f32x4 load4(const void* x, int64_t idx) {
+  if (DT == MOE4_F32) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + idx);
+  u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(x) + idx);
+  return f32x4{bf16_bits_to_f32(w[0] & 0xFFFFu), bf16_bits_to_f32(w[0] >> 16), bf16_bits_to_f32(w[1] & 0xFFFFu),
+               bf16_bits_to_f32(w[1] >> 16)};
+}
+
+template <int DT, int MODE>  // MODE 0: plain, 1: row map + scale, 2: dsilu
+__device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64_t c, const float* dtab) {
+  if (MODE == 1) {
+    const int32_t a = g.row_map[r];
+    const float sc = g.row_scale ? g.row_scale[a] : 1.0f;
+    f32x4 v = load4<DT>(g.x, (int64_t)(a / g.map_div) * C + c);
+    return f32x4{sc * v[0], sc * v[1], sc * v[2], sc * v[3]};
+  } else if (MODE == 2) {
+    f32x4 v = load4<DT>(g.x, r * C + c);
+    u32x2 u = *reinterpret_cast<const u32x2*>(g.dsilu_src + r * C + c);
+    return f32x4{v[0] * act_eval<true>(u[0] & 0xFFFFu, dtab), v[1] * act_eval<true>(u[0] >> 16, dtab),
+                 v[2] * act_eval<true>(u[1] & 0xFFFFu, dtab), v[3] * act_eval<true>(u[1] >> 16, dtab)};
+  }
+  return load4<DT>(g.x, r * C + c);
+}
+
+// ------------------------------------------------- row-wise gradient quant
+template <int DT, int MODE, bool SR>
+__global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C, uint32_t base,
+                                                 uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
+                                                 const float* __restrict__ act_tab) {
+  __shared__ float tab[MODE == 2 ? ACT_TAB : 1];
+  if (MODE == 2) stage_act_table(tab, act_tab);
+  const int64_t nbr = C / 32;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= R * nbr) return;
+  const int64_t r = blk / nbr, c0 = (blk % nbr) * 32;
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    f32x4 t = grad_vals4<DT, MODE>(g, r, C, c0 + 4 * q, tab);
+    v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+  const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
+  uint32_t outw[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t w0 = 0, w1 = 0;
+    if (SR) {
+      const uint64_t i0 = (uint64_t)(r * C + c0 + 4 * q);
+      w0 = sr_word(base, i0 >> 1);
+      w1 = sr_word(base, (i0 >> 1) + 1);
+    }
+    uint32_t b0 = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu);
+    uint32_t b1 = mx_round<SR>(v[4 * q + 1] * p, w0 >> 16);
+    uint32_t b2 = mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu);
+    uint32_t b3 = mx_round<SR>(v[4 * q + 3] * p, w1 >> 16);
+    outw[q] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+  u32x4* o = reinterpret_cast<u32x4*>(out_c + r * C + c0);
+  o[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+  o[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
+  out_s[blk] = (uint8_t)(e + 127);
+}
+
+// ------------------------------------------------- transposed gradient quant
+template <int DT, int MODE, bool SR>
+__global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, const int32_t* __restrict__ off,
+                                              const int32_t* __restrict__ offp, int G, int64_t max_pr, int64_t n_ct,
+                                              uint32_t base,
+                                              uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
+                                              const float* __restrict__ act_tab) {
+  __shared__ float tab[MODE == 2 ? ACT_TAB : 1];
+  __shared__ float lv[TC][TR + 1];  // [column][row]
+  if (MODE == 2) stage_act_table(tab, act_tab);
+  const int64_t ct = blockIdx.x % n_ct, rt = blockIdx.x / n_ct;
+  TileT t;
+  if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
+  const int64_t c0 = ct * TC;
+  const int tid = threadIdx.x;
+  {  // stage: thread -> row tid/8, 16 columns at (tid%8)*16
+    const int rr = tid >> 3, cc = (tid & 7) * 16;
+    const bool ok = rr < t.nvalid && c0 + cc < C;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v = ok ? grad_vals4<DT, MODE>(g, t.src0 + rr, C, c0 + cc + 4 * q, tab) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lv[cc + 4 * q + j][rr] = v[j];
+    }
+  }
+  __syncthreads();
+  const int w = tid >> 6, l = tid & 63;
+  if (c0 + 32 * w >= C) return;
+  const int cp = l & 15, rseg = l >> 4;
+  const int cl = 32 * w + 2 * cp;
+  float v[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i][0] = lv[cl][rseg * 8 + i];
+    v[i][1] = lv[cl + 1][rseg * 8 + i];
+  }
+  const int64_t c = c0 + cl;
+  const int64_t orow = t.pr_in_g + rseg * 8;
+  uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
+  uint8_t* s0 = out_s + t.out_base / 32 + c * (t.P / 32) + t.pr_in_g / 32;
+  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + t.P / 32);
+}
+
+template <int DT, int MODE>
+static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int64_t C, const int32_t* off,
+                        const int32_t* offp, int G, int64_t max_pr, uint32_t base, uint8_t* oc, uint8_t* os,
+                        const float* tab, hipStream_t s) {
+  if (!transpose) {
+    const int64_t nblk = R * (C / 32);
+    dim3 grid((unsigned)((nblk + 255) / 256));
+    if (sr) hipLaunchKernelGGL((k_mx_rows<DT, MODE, true>), grid, dim3(256), 0, s, g, R, C, base, oc, os, tab);
+    else hipLaunchKernelGGL((k_mx_rows<DT, MODE, false>), grid, dim3(256), 0, s, g, R, C, base, oc, os, tab);
+  } else {
+    const int64_t n_ct = (C + TC - 1) / TC, n_rt = (max_pr + TR - 1) / TR;
+    dim3 grid((unsigned)(n_ct * n_rt));
+    if (sr)
+      hipLaunchKernelGGL((k_mx_T<DT, MODE, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base, oc,
+                         os, tab);
+    else
+      hipLaunchKernelGGL((k_mx_T<DT, MODE, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base,
+                         oc, os, tab);
+  }
+}
+
+}  // namespace moe4
+
+using namespace moe4;
+
+extern "C" int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
+                                  int64_t rows, int64_t cols, const int32_t* group_row_off,
+                                  const int32_t* group_off_pad, int32_t n_groups, int64_t max_padded_rows,
+                                  uint64_t seed, uint32_t stream_id, uint8_t* out_codes, uint8_t* out_sf,
+                                  void* stream) {
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_requant_sr_T: cols must be a positive multiple of 32");
+  MOE4_REQUIRE(n_groups >= 1 && group_row_off && group_off_pad, MOE4_EINVAL, "mxfp8_requant_sr_T: group offsets required");
+  MOE4_REQUIRE(max_padded_rows >= 0 && max_padded_rows % 32 == 0, MOE4_EINVAL,
+               "mxfp8_requant_sr_T: max_padded_rows must be a multiple of 32");
+  MOE4_REQUIRE(codes && sf && ts && out_codes && out_sf, MOE4_EINVAL, "mxfp8_requant_sr_T: NULL pointer");
+  MOE4_REQUIRE(aligned16(codes) && aligned16(out_codes), MOE4_EALIGN, "mxfp8_requant_sr_T: misaligned pointer");
+  if (max_padded_rows == 0) return MOE4_OK;
+  const int64_t n_ct = (cols + TC - 1) / TC, n_rt = max_padded_rows / TR;
+  MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "mxfp8_requant_sr_T: tensor too large");
+  const uint32_t base = sr_base_key(seed, stream_id);
+  hipLaunchKernelGGL((k_requant_T<true>), dim3((unsigned)(n_ct * n_rt)), dim3(MXT), 0, as_stream(stream), codes, sf, ts,
+                     ts_per_group, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct, base,
+                     out_codes, out_sf);
+  return check_launch("mxfp8_requant_sr_T");
+}
+
+extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
+                           int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int transpose,
+                           const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
+                           int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
+                           uint8_t* out_codes, uint8_t* out_sf, void* stream) {
+  MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "mxfp8_quant: dtype must be BF16 or F32");
+  MOE4_REQUIRE(rnd == MOE4_RNE || rnd == MOE4_SR, MOE4_EINVAL, "mxfp8_quant: rnd must be RNE or SR");
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_quant: cols must be a positive multiple of 32");
+  MOE4_REQUIRE(!(row_map && dsilu_src), MOE4_EINVAL, "mxfp8_quant: row_map and dsilu_src are exclusive");
+  MOE4_REQUIRE(!row_map || map_div >= 1, MOE4_EINVAL, "mxfp8_quant: map_div >= 1");
+  MOE4_REQUIRE(x && out_codes && out_sf, MOE4_EINVAL, "mxfp8_quant: NULL pointer");
+  MOE4_REQUIRE(aligned16(x) && aligned16(out_codes) && (!dsilu_src || aligned16(dsilu_src)), MOE4_EALIGN,
+               "mxfp8_quant: misaligned pointer");
+  if (transpose) {
+    MOE4_REQUIRE(n_groups >= 1 && group_row_off && group_off_pad, MOE4_EINVAL, "mxfp8_quant: group offsets required");
+    MOE4_REQUIRE(max_padded_rows >= 0 && max_padded_rows % 32 == 0, MOE4_EINVAL,
+                 "mxfp8_quant: max_padded_rows must be a multiple of 32");
+  }
+  hipStream_t s = as_stream(stream);
+  const float* tab = nullptr;
+  if (dsilu_src) {
+    int rc = ensure_act_tables(s);
+    if (rc) return rc;
+    tab = act_tables_device_ptr() + ACT_TAB;
+  }
+  if ((transpose ? max_padded_rows : rows) == 0) return MOE4_OK;
+  GradSrc g{x, dtype, row_map, map_div, row_scale, dsilu_src};
+  const uint32_t base = sr_base_key(seed, stream_id);
+  const bool sr = rnd == MOE4_SR;
+  const int mode = row_map ? 1 : (dsilu_src ? 2 : 0);
+#define MOE4_GRAD(DT, MODE)                                                                                      \
+  launch_grad<DT, MODE>(transpose, sr, g, rows, cols, group_row_off, group_off_pad, n_groups, max_padded_rows, \
+                        base, out_codes, out_sf, tab, s)
+  if (dtype == MOE4_F32) {
+    if (mode == 0) MOE4_GRAD(MOE4_F32, 0);
+    else if (mode == 1) MOE4_GRAD(MOE4_F32, 1);
+    else MOE4_GRAD(MOE4_F32, 2);
+  } else {
+    if (mode == 0) MOE4_GRAD(MOE4_BF16, 0);
+    else if (mode == 1) MOE4_GRAD(MOE4_BF16, 1);
+    else MOE4_GRAD(MOE4_BF16, 2);
+  }
+#undef MOE4_GRAD
+  return check_launch("mxfp8_quant");
+}

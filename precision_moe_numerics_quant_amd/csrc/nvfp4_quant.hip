@@ -1,0 +1,337 @@
+// NVFP4 quantisation with the Four-Over-Six block-scale choice (gfx950).
+//
+// Two-level scaling as the lhc.media page describes NVFP4 (4-bit values plus
+// a scale per sixteen values) with a float32 tensor scale per row group, and
+// the 4/6 choice of the agihunt.info page, "Confirmed": per 16-block keep the
+// candidate (block amax mapped to 6, or to 4) with the lower squared error.
+//
+// Kernels, in launch order:
+//   k_zero_u32      clear the per-group amax words (workspace)
+//   k_amax          per-group max |x| (float bits, atomicMax: order-free)
+//   k_tensor_scale  S_g = fl(amax_g / (m_max * 448)), 1 for a zero group
+//   k_encode        one thread per 16-element block: both candidates, errors
+//                   in the fixed order, the choice, packed codes + scale byte
+// All float arithmetic is one IEEE binary32 operation per step (the library
+// is built with -ffp-contract=off), with correctly rounded division.
+#include "act.h"
+#include "moe4_internal.h"
+
+namespace moe4 {
+
+__global__ void k_zero_u32(uint32_t* p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Group of row r for offsets off[0..G] (largest g with off[g] <= r).
+__device__ inline int group_of_row(const int32_t* off, int G, int64_t r) {
+  if (off == nullptr) return 0;
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Load 8 consecutive source values of row-major x as float32 (applying SiLU).
+template <int DT, bool SILU>
+__device__ inline void load8(const void* x, int64_t idx, float* v, const float* tab) {
+  if (DT == MOE4_BF16) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+      if (SILU) {
+        v[2 * i] = act_eval<false>(lo, tab);
+        v[2 * i + 1] = act_eval<false>(hi, tab);
+      } else {
+        v[2 * i] = bf16_bits_to_f32(lo);
+        v[2 * i + 1] = bf16_bits_to_f32(hi);
+      }
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + idx);
+    f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+}
+
+constexpr int AMAX_THREADS = 256;
+
+template <int DT, bool SILU>
+__global__ void __launch_bounds__(AMAX_THREADS) k_amax(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                       const int32_t* __restrict__ goff, int G,
+                                                       int rows_per_wg, uint32_t* __restrict__ amax_bits,
+                                                       const float* __restrict__ act_tab) {
+  __shared__ float tab[SILU ? ACT_TAB : 1];
+  __shared__ float red[AMAX_THREADS / 64];
+  __shared__ int s_g0, s_g1;
+  if (SILU) stage_act_table(tab, act_tab);
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  if (r0 >= rows) return;
+  const int64_t r1 = r0 + rows_per_wg < rows ? r0 + rows_per_wg : rows;
+  if (threadIdx.x == 0) {
+    s_g0 = group_of_row(goff, G, r0);
+    s_g1 = group_of_row(goff, G, r1 - 1);
+  }
+  __syncthreads();
+  const int g0 = s_g0, g1 = s_g1;
+  for (int g = g0; g <= g1; ++g) {
+    int64_t a = r0, b = r1;
+    if (goff) {
+      a = goff[g] > r0 ? goff[g] : r0;
+      b = goff[g + 1] < r1 ? goff[g + 1] : r1;
+    }
+    float m = 0.0f;
+    const int64_t n8 = (b - a) * cols / 8;  // cols % 16 == 0
+    const int64_t base = a * cols;
+    for (int64_t i = threadIdx.x; i < n8; i += AMAX_THREADS) {
+      float v[8];
+      load8<DT, SILU>(x, base + i * 8, v, tab);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = red[0];
+      for (int w = 1; w < AMAX_THREADS / 64; ++w) t = fmaxf(t, red[w]);
+      if (b > a) atomicMax(amax_bits + g, __float_as_uint(t));  // t >= 0: bit order = value order
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void k_tensor_scale(const uint32_t* __restrict__ amax_bits, int G, float m_max448,
+                               float* __restrict__ ts) {
+  int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= G) return;
+  float s = __uint_as_float(amax_bits[g]) / m_max448;
+  ts[g] = (s == 0.0f) ? 1.0f : s;
+}
+
+// E4M3 code (RNE, clamp to 448) of a non-negative finite float.
+__device__ inline uint32_t e4m3_rne_u(float u) {
+  u = fminf(u, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xFFu;
+}
+
+struct Cand {
+  uint32_t sc;      // E4M3 scale byte
+  uint32_t q[2];    // 16 packed nibbles
+  float err;
+};
+
+// One candidate of one 16-block (steps: scale, encode, dequantise, error).
+__device__ inline Cand encode_candidate(const float* x, float amax_b, float S, float m) {
+  Cand c;
+  const float d = m * S;
+  const float u = amax_b / d;
+  c.sc = e4m3_rne_u(u);
+  const float scf = e4m3_to_f32(c.sc);
+  const float eff = scf * S;
+  const bool zero = (c.sc == 0u) || (eff == 0.0f);
+  if (zero) {
+    // every code a signed zero: deq = 0, t = x
+    uint32_t q0 = 0, q1 = 0;
+    float err = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t sgn = (__float_as_uint(x[i]) >> 31) << 3;
+      if (i < 8) q0 |= sgn << (4 * i); else q1 |= sgn << (4 * (i - 8));
+      float t = x[i];
+      err = err + t * t;
+    }
+    c.q[0] = q0; c.q[1] = q1; c.err = err;
+    return c;
+  }
+  const float inv = 1.0f / eff;
+  const bool inv_inf = __builtin_isinf(inv);
+  const float mant = mant_factor(scf);
+  uint32_t q0 = 0, q1 = 0;
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    float y0 = x[i] * inv, y1 = x[i + 1] * inv;
+    if (inv_inf) {  // 0 * inf: a zero element stays a signed zero
+      if (x[i] == 0.0f) y0 = x[i];
+      if (x[i + 1] == 0.0f) y1 = x[i + 1];
+    }
+    // E2M1, round to nearest even, saturating, sign kept (scale 1: no rescale)
+    uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+    if (i < 8) q0 |= pk << (4 * i); else q1 |= pk << (4 * (i - 8));
+    // exact q * 2**floor(log2 sc), times the mantissa 1.m: the exact q * sc
+    f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, scf, 0);
+    float p0 = p[0] * mant, p1 = p[1] * mant;
+    float t0 = x[i] - p0 * S;
+    float t1 = x[i + 1] - p1 * S;
+    err = err + t0 * t0;
+    err = err + t1 * t1;
+  }
+  c.q[0] = q0; c.q[1] = q1; c.err = err;
+  return c;
+}
+
+constexpr int ENC_THREADS = 256;
+
+template <int DT, bool SILU, bool FOUR_OVER_SIX>
+__global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        const int32_t* __restrict__ goff, int G,
+                                                        const float* __restrict__ ts,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+                                                        const float* __restrict__ act_tab) {
+  __shared__ float tab[SILU ? ACT_TAB : 1];
+  if (SILU) stage_act_table(tab, act_tab);
+  const int64_t nbr = cols / 16;
+  const int64_t blk = (int64_t)blockIdx.x * ENC_THREADS + threadIdx.x;
+  if (blk >= rows * nbr) return;
+  const int64_t r = blk / nbr;
+  const int g = group_of_row(goff, G, r);
+  const float S = ts[g];
+  float v[16];
+  load8<DT, SILU>(x, blk * 16, v, tab);
+  load8<DT, SILU>(x, blk * 16 + 8, v + 8, tab);
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  Cand best = encode_candidate(v, amax_b, S, 6.0f);
+  if (FOUR_OVER_SIX) {
+    Cand c4 = encode_candidate(v, amax_b, S, 4.0f);
+    if (c4.err < best.err) best = c4;
+  }
+  *reinterpret_cast<u32x2*>(codes + blk * 8) = u32x2{best.q[0], best.q[1]};
+  sf[blk] = (uint8_t)best.sc;
+}
+
+template <int DT, bool SILU>
+static void launch_encode(bool four6, dim3 grid, hipStream_t s, const void* x, int64_t rows, int64_t cols,
+                          const int32_t* goff, int G, const float* ts, uint8_t* codes, uint8_t* sf,
+                          const float* tab) {
+  if (four6)
+    hipLaunchKernelGGL((k_encode<DT, SILU, true>), grid, dim3(ENC_THREADS), 0, s, x, rows, cols, goff, G, ts,
+                       codes, sf, tab);
+  else
+    hipLaunchKernelGGL((k_encode<DT, SILU, false>), grid, dim3(ENC_THREADS), 0, s, x, rows, cols, goff, G, ts,
+                       codes, sf, tab);
+}
+
+__global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
+                          const float* __restrict__ ts, int ts_per_group, const int32_t* __restrict__ goff,
+                          int G, int64_t rows, int64_t cols, float* __restrict__ out) {
+  const int64_t nbr = cols / 16;
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= rows * nbr) return;
+  const int64_t r = blk / nbr;
+  const float S = ts[ts_per_group ? group_of_row(goff, G, r) : 0];
+  const float scf = e4m3_to_f32(sf[blk]);
+  const float mant = mant_factor(scf);
+  u32x2 q = *reinterpret_cast<const u32x2*>(codes + blk * 8);
+  float* o = out + blk * 16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t byte = (q[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, scf, 0);
+    float p0 = scf == 0.0f ? 0.0f * p[0] : p[0] * mant;
+    float p1 = scf == 0.0f ? 0.0f * p[1] : p[1] * mant;
+    o[2 * i] = p0 * S;
+    o[2 * i + 1] = p1 * S;
+  }
+}
+
+__global__ void k_silu_eval(const uint16_t* __restrict__ u, int64_t n, float* __restrict__ so,
+                            float* __restrict__ dso, const float* __restrict__ tabs) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t b = u[i];
+  if (so) so[i] = act_eval<false>(b, tabs);
+  if (dso) dso[i] = act_eval<true>(b, tabs + ACT_TAB);
+}
+
+}  // namespace moe4
+
+using namespace moe4;
+
+extern "C" size_t nvfp4_quant_46_ws_bytes(int32_t n_groups) {
+  return (size_t)(n_groups > 0 ? n_groups : 1) * sizeof(uint32_t);
+}
+
+extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
+                              const int32_t* group_row_off, int32_t n_groups, int mode, int pre_op,
+                              uint8_t* codes, uint8_t* sf, float* tensor_scale,
+                              void* ws, size_t ws_bytes, void* stream) {
+  MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "nvfp4_quant_46: dtype must be BF16 or F32");
+  MOE4_REQUIRE(mode == MOE4_NVFP4_6 || mode == MOE4_NVFP4_4OVER6, MOE4_EINVAL, "nvfp4_quant_46: bad mode");
+  MOE4_REQUIRE(pre_op == MOE4_PRE_NONE || (pre_op == MOE4_PRE_SILU && dtype == MOE4_BF16), MOE4_EINVAL,
+               "nvfp4_quant_46: pre_op SILU needs bf16 input");
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 16 == 0, MOE4_EINVAL, "nvfp4_quant_46: cols must be a positive multiple of 16");
+  MOE4_REQUIRE(n_groups >= 1 && (group_row_off != nullptr || n_groups == 1), MOE4_EINVAL,
+               "nvfp4_quant_46: n_groups >= 1, and group_row_off is required when n_groups > 1");
+  MOE4_REQUIRE(tensor_scale && ws, MOE4_EINVAL, "nvfp4_quant_46: NULL pointer");
+  MOE4_REQUIRE(rows == 0 || (x && codes && sf), MOE4_EINVAL, "nvfp4_quant_46: NULL pointer");
+  MOE4_REQUIRE(aligned16(x) && aligned16(codes), MOE4_EALIGN, "nvfp4_quant_46: x and codes must be 16-byte aligned");
+  MOE4_REQUIRE(ws_bytes >= nvfp4_quant_46_ws_bytes(n_groups), MOE4_EWORKSPACE, "nvfp4_quant_46: workspace too small");
+  hipStream_t s = as_stream(stream);
+  const float* tab = nullptr;
+  if (pre_op == MOE4_PRE_SILU) {
+    int rc = ensure_act_tables(s);
+    if (rc) return rc;
+    tab = act_tables_device_ptr();
+  }
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  const int G = n_groups;
+  hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
+  if (rows > 0) {
+    // about 8 K elements per workgroup
+    int rpw = (int)((8192 + cols - 1) / cols);
+    if (rpw < 1) rpw = 1;
+    dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+    if (dtype == MOE4_BF16 && pre_op == MOE4_PRE_SILU)
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+    else if (dtype == MOE4_BF16)
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, false>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+    else
+      hipLaunchKernelGGL((k_amax<MOE4_F32, false>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+  }
+  const float m448 = (mode == MOE4_NVFP4_4OVER6) ? 4.0f * 448.0f : 6.0f * 448.0f;
+  hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, m448, tensor_scale);
+  if (rows > 0) {
+    const int64_t nblk = rows * (cols / 16);
+    dim3 grid((unsigned)((nblk + ENC_THREADS - 1) / ENC_THREADS));
+    const bool four6 = mode == MOE4_NVFP4_4OVER6;
+    if (dtype == MOE4_BF16 && pre_op == MOE4_PRE_SILU)
+      launch_encode<MOE4_BF16, true>(four6, grid, s, x, rows, cols, group_row_off, G, tensor_scale, codes, sf, tab);
+    else if (dtype == MOE4_BF16)
+      launch_encode<MOE4_BF16, false>(four6, grid, s, x, rows, cols, group_row_off, G, tensor_scale, codes, sf, tab);
+    else
+      launch_encode<MOE4_F32, false>(four6, grid, s, x, rows, cols, group_row_off, G, tensor_scale, codes, sf, tab);
+  }
+  return check_launch("nvfp4_quant_46");
+}
+
+extern "C" int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
+                             const int32_t* group_row_off, int32_t n_groups, int64_t rows, int64_t cols,
+                             float* out, void* stream) {
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 16 == 0, MOE4_EINVAL, "nvfp4_dequant: cols must be a positive multiple of 16");
+  MOE4_REQUIRE(codes && sf && ts && out, MOE4_EINVAL, "nvfp4_dequant: NULL pointer");
+  MOE4_REQUIRE(!ts_per_group || (group_row_off && n_groups >= 1), MOE4_EINVAL, "nvfp4_dequant: groups needed");
+  MOE4_REQUIRE(aligned16(codes) && aligned16(out), MOE4_EALIGN, "nvfp4_dequant: misaligned pointer");
+  if (rows == 0) return MOE4_OK;
+  const int64_t nblk = rows * (cols / 16);
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, as_stream(stream), codes, sf,
+                     ts, ts_per_group, group_row_off, n_groups, rows, cols, out);
+  return check_launch("nvfp4_dequant");
+}
+
+extern "C" int moe_silu_eval(const uint16_t* u, int64_t n, float* silu_out, float* dsilu_out, void* stream) {
+  MOE4_REQUIRE(n >= 0 && (n == 0 || u), MOE4_EINVAL, "moe_silu_eval: bad arguments");
+  hipStream_t s = as_stream(stream);
+  int rc = ensure_act_tables(s);
+  if (rc) return rc;
+  if (n == 0) return MOE4_OK;
+  hipLaunchKernelGGL(k_silu_eval, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, u, n, silu_out, dsilu_out,
+                     act_tables_device_ptr());
+  return check_launch("moe_silu_eval");
+}

@@ -1,0 +1,91 @@
+"""The NVFP4-forward / MXFP8-backward MoE expert layer, chained from the C-ABI calls.
+
+The recipe is the one the pages report for Inkling 2 Small's expert layers
+(agihunt.info page, "Confirmed": NVFP4 forward with a dedicated kernel, MXFP8
+backward with requantisation and stochastic rounding, 4/6 activation
+quantisation; lhc.media page: FP32 master weights, BF16 activations, NVFP4
+dispatch, the dequantise -> transpose -> requantise step).  Every arithmetic
+step runs in the HIP kernels of libmoe4; this module only sequences the calls
+and holds the tensors between them.
+
+Forward:  weights -> NVFP4 (mode 6, per-expert tensor scale); route; x ->
+NVFP4 4/6 (one tensor scale, quantised once before dispatch); gather rows into
+expert order; up GEMM -> U (bf16); silu + NVFP4 4/6 per expert -> Hq; down GEMM
+-> Yp (fp32); gate-weighted combine -> y (bf16).
+
+Backward: g * dy gathered into expert order -> MXFP8 (RNE) row-wise and
+transposed per expert; forward NVFP4 operands -> MXFP8 by the stochastic-
+rounding transposed requantisation (stream 16*layer + role: 0 X, 1 H, 2 W_up,
+3 W_down); dgrad/wgrad grouped GEMMs on native block-scaled MFMA; dU = dH *
+silu'(U) -> MXFP8; un-permuting sum -> dx (bf16).
+"""
+import torch
+
+from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, max_padded_rows, moe_combine, moe_gather_rows,
+               moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
+               moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46)
+
+ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
+
+
+def quantize_weights(w_up, w_down):
+    """NVFP4 (mode 6) of the fp32 masters, one tensor scale per expert matrix."""
+    E, F, d = w_up.shape
+    dev = w_up.device
+    off_f = torch.arange(E + 1, dtype=torch.int32, device=dev) * F
+    off_d = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
+    wu = nvfp4_quant_46(w_up.view(E * F, d), NVFP4_6, off_f)
+    wd = nvfp4_quant_46(w_down.view(E * d, F), NVFP4_6, off_d)
+    return dict(wu=wu, wd=wd, off_f=off_f, off_d=off_d, shape=(E, F, d))
+
+
+def forward(x, w_up, w_down, logits, k, bias=None, wq=None):
+    """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32."""
+    T, d = x.shape
+    E, F, _ = w_up.shape
+    if wq is None:
+        wq = quantize_weights(w_up, w_down)
+    r = moe_route_topk(logits, k, bias)
+    xq = nvfp4_quant_46(x, NVFP4_4OVER6)
+    xq_perm = moe_gather_rows(xq[0], xq[1], r["perm"], k)
+    wu_c, wu_s, wu_t = wq["wu"]
+    wd_c, wd_s, wd_t = wq["wd"]
+    U = moe_grouped_gemm_fwd(xq_perm[0], xq_perm[1], xq[2], wu_c.view(E, F, d // 2), wu_s.view(E, F, d // 16), wu_t,
+                             r["off"], torch.bfloat16)
+    hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU)
+    Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
+                              r["off"], torch.float32, a_ts_per_group=True)
+    y = moe_combine(Yp, r["gates"], r["inv_perm"])
+    return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k))
+
+
+def backward(fw, dy, seed=1, layer=0):
+    """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, ...)."""
+    T, d, F, E, k = fw["dims"]
+    r = fw["route"]
+    A = T * k
+    mpr = max_padded_rows(A, E)
+    sid = lambda role: 16 * layer + role
+    g_flat = r["gates"].view(-1)
+    dy_row = mxfp8_quant(dy, rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat)
+    dy_col = mxfp8_quant(dy, rows=A, transpose=True, row_map=r["perm"], map_div=k, row_scale=g_flat,
+                         group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr)
+    wq = fw["wq"]
+    wd_c, wd_s, wd_t = wq["wd"]
+    wdT = mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, seed, sid(ROLE_WDOWN), max_pr=E * d)
+    dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
+    hq = fw["hq"]
+    hT = mxfp8_requant_sr_T(hq[0], hq[1], hq[2], r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr)
+    dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
+    du_row = mxfp8_quant(dH, dsilu_src=fw["U"])
+    du_col = mxfp8_quant(dH, transpose=True, dsilu_src=fw["U"], group_row_off=r["off"], group_off_pad=r["off_pad"],
+                         max_pr=mpr)
+    wu_c, wu_s, wu_t = wq["wu"]
+    wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
+    dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
+    xp = fw["xq_perm"]
+    xT = mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X), max_pr=mpr)
+    dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d)
+    dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
+    return dict(dx=dx, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
+                du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)

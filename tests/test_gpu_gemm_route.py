@@ -1,0 +1,164 @@
+"""GPU parity of routing, data movement and the grouped GEMMs against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import assert_bytes_equal, bf16_from_bits, cuda_i32, gemm_tol_check, to_np
+from oracle import formats as fmt
+from oracle import gemm as og
+from oracle import layer as olayer
+from oracle import mxfp8 as mx
+from oracle import nvfp4 as nv
+from oracle import route
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import precision_moe_numerics_quant_amd as m4
+
+
+# ---------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k,zipf", [(256, 8, 2, None), (1000, 384, 8, 1.1), (77, 40, 5, None), (64, 1024, 16, None)])
+def test_route_bit_exact(T, E, k, zipf):
+    logits = synth.randn((T, E), 1.0, "cpu", T + E, "logits").numpy()
+    if T == 77:
+        logits = np.round(logits * 2) / 2          # many exact ties
+    bias = None if zipf is None else (-zipf * np.log(np.arange(E) + 1)).astype(np.float32)
+    r = m4.moe_route_topk(torch.from_numpy(logits).cuda(), k, None if bias is None else torch.from_numpy(bias).cuda())
+    idx, gates = route.topk_gates(logits, k, bias)
+    P = route.permutation(idx, E)
+    assert_bytes_equal(to_np(r["idx"]), idx, "topk idx")
+    assert_bytes_equal(to_np(r["gates"]).view(np.uint32), gates.view(np.uint32), "gates")
+    for key in ("off", "off_pad", "perm", "inv_perm"):
+        assert_bytes_equal(to_np(r[key]), P[key], key)
+
+
+def test_route_empty_tokens():
+    r = m4.moe_route_topk(torch.zeros((0, 16), dtype=torch.float32, device="cuda"), 2)
+    assert (to_np(r["off"]) == 0).all() and (to_np(r["off_pad"]) == 0).all()
+
+
+def test_gather_combine_unpermute_bit_exact():
+    T, d, k, E = 200, 128, 3, 6
+    rng = np.random.default_rng(0)
+    xb = synth.bf16_bits(synth.activations(T, d, "cpu", 1))
+    xq = nv.nvfp4_quantize(xb, 46)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    P = route.permutation(idx, E)
+    oc, os_ = m4.moe_gather_rows(torch.from_numpy(xq["codes"]).cuda(), torch.from_numpy(xq["sf"]).cuda(),
+                                 cuda_i32(P["perm"]), k)
+    src = P["perm"] // k
+    assert_bytes_equal(to_np(oc), xq["codes"][src], "gather codes")
+    assert_bytes_equal(to_np(os_), xq["sf"][src], "gather scales")
+    yp = rng.standard_normal((T * k, d)).astype(np.float32)
+    gates = rng.random((T, k)).astype(np.float32)
+    y = m4.moe_combine(torch.from_numpy(yp).cuda(), torch.from_numpy(gates).cuda(), cuda_i32(P["inv_perm"]))
+    assert_bytes_equal(to_np(y), olayer.combine(yp, gates, P["inv_perm"], k), "combine")
+    dx = m4.moe_unpermute_sum(torch.from_numpy(yp).cuda(), cuda_i32(P["inv_perm"]), T, k)
+    assert_bytes_equal(to_np(dx), olayer.unpermute_sum(yp, P["inv_perm"], T, k), "unpermute")
+
+
+# ------------------------------------------------------------------------ GEMMs
+
+def _fwd_operands(M_list, N, K, seed, ts_per_group=False):
+    E = len(M_list)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    M = int(off[-1])
+    xb = synth.bf16_bits(synth.activations(max(M, 1), K, "cpu", seed, outlier_p=0.001, outlier_mul=20.0))[:M]
+    qa = nv.nvfp4_quantize(xb, 46, off if ts_per_group else None)
+    w = synth.randn((E, N, K), 0.02, "cpu", seed, "w_up").numpy()
+    qb = nv.nvfp4_quantize(w.reshape(E * N, K), 6, np.arange(E + 1) * N)
+    return off, qa, qb
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([64], 64, 64), ([5, 0, 0, 257], 512, 1024)])
+def test_grouped_gemm_fwd_tolerance(M_list, N, K, out_dtype):
+    E = len(M_list)
+    per_group = out_dtype == "f32"
+    off, qa, qb = _fwd_operands(M_list, N, K, seed=N + K, ts_per_group=per_group)
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    c = m4.moe_grouped_gemm_fwd(torch.from_numpy(qa["codes"]).cuda(), torch.from_numpy(qa["sf"]).cuda(),
+                                torch.from_numpy(qa["ts"]).cuda(), torch.from_numpy(qb["codes"]).cuda().view(E, N, K // 2),
+                                torch.from_numpy(qb["sf"]).cuda().view(E, N, K // 16), torch.from_numpy(qb["ts"]).cuda(),
+                                cuda_i32(off), tdt, a_ts_per_group=per_group)
+    A64 = nv.nvfp4_exact_f64(qa["codes"], qa["sf"], qa["ts"], off if per_group else None)
+    B64 = nv.nvfp4_exact_f64(qb["codes"], qb["sf"], qb["ts"], np.arange(E + 1) * N).reshape(E, N, K)
+    exact = og.grouped_nt(A64, B64, off)
+    bound = og.abs_bound_nt(A64, B64, off)
+    got = to_np(c)
+    got = fmt.bf16_to_f32(got).astype(np.float64) if out_dtype == "bf16" else got.astype(np.float64)
+    gemm_tol_check(got, exact, bound, "fwd", out_bf16=out_dtype == "bf16")
+
+
+def test_grouped_gemm_fwd_exact_special_case():
+    """Codes in {0, +-0.5, +-1, +-2} with power-of-two scales and small K keep
+    every partial sum exact in float32: the GPU result equals the exact one."""
+    rng = np.random.default_rng(3)
+    E, N, K = 3, 64, 128
+    M_list = [50, 0, 90]
+    off = np.concatenate([[0], np.cumsum(M_list)])
+    M = off[-1]
+    small = np.array([0, 1, 2, 4, 8, 9, 10, 12])     # codes of 0, .5, 1, 2, -0, -.5, -1, -2
+    qa = rng.choice(small, (M, K)); qb = rng.choice(small, (E * N, K))
+    sa = rng.choice([0x38, 0x30, 0x40], (M, K // 16)).astype(np.uint8)         # 1, .5, 2
+    sb = rng.choice([0x38, 0x30, 0x40], (E * N, K // 16)).astype(np.uint8)
+    ta = np.float32([0.25]); tb = np.float32([1.0, 2.0, 0.5])
+    ca, cb = nv.pack_codes(qa), nv.pack_codes(qb)
+    c = m4.moe_grouped_gemm_fwd(torch.from_numpy(ca).cuda(), torch.from_numpy(sa).cuda(), torch.from_numpy(ta).cuda(),
+                                torch.from_numpy(cb).cuda().view(E, N, K // 2), torch.from_numpy(sb).cuda().view(E, N, K // 16),
+                                torch.from_numpy(tb).cuda(), cuda_i32(off), torch.float32)
+    exact = og.grouped_nt(nv.nvfp4_exact_f64(ca, sa, ta), nv.nvfp4_exact_f64(cb, sb, tb, np.arange(E + 1) * N).reshape(E, N, K), off)
+    assert np.array_equal(to_np(c).astype(np.float64), exact)
+
+
+def _mx_rows(M, K, seed, scale=1.0):
+    x = (synth.randn((M, K), scale, "cpu", seed, "dh").numpy())
+    return mx.quantize_rowwise(x, mx.RNE)
+
+
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([256], 128, 4096 // 16), ([3, 200], 96, 96)])
+def test_grouped_gemm_dgrad_tolerance(M_list, N, K):
+    E = len(M_list)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    M = int(off[-1])
+    ac, as_ = _mx_rows(max(M, 1), K, seed=1, scale=1e-3)
+    ac, as_ = ac[:M], as_[:M]
+    bc, bs = _mx_rows(E * N, K, seed=2, scale=0.02)
+    c = m4.moe_grouped_gemm_bwd_dgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(),
+                                      torch.from_numpy(bc).cuda(), torch.from_numpy(bs).cuda(), cuda_i32(off))
+    A64 = mx.dequant_rowwise(ac, as_)
+    B64 = mx.dequant_rowwise(bc, bs).reshape(E, N, K)
+    exact = og.grouped_nt(A64, B64, off)
+    gemm_tol_check(to_np(c).astype(np.float64), exact, og.abs_bound_nt(A64, B64, off), "dgrad")
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_grouped_gemm_wgrad_tolerance(beta):
+    N1, N2 = 160, 96
+    M_list = [0, 37, 130, 1, 64, 300]
+    E = len(M_list)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    offp = mx.padded_offsets(off)
+    M = int(off[-1])
+    a = synth.randn((M, N1), 1e-3, "cpu", 3, "dh").numpy()
+    b = synth.randn((M, N2), 1.0, "cpu", 4, "dh").numpy()
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE)
+    bc, bs = mx.quantize_transposed(b, off, mx.SR, 1, 1)
+    dw0 = np.random.default_rng(5).standard_normal((E, N1, N2)).astype(np.float32)
+    dw = torch.from_numpy(dw0.copy()).cuda()
+    m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
+                                  torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=beta)
+    Al = mx.dequant_transposed(ac, as_, off, N1)
+    Bl = mx.dequant_transposed(bc, bs, off, N2)
+    exact = og.wgrad(Al, Bl)
+    bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
+    got = to_np(dw).astype(np.float64)
+    if beta == 1.0:
+        got = got - dw0.astype(np.float64)
+        bound = bound + np.abs(dw0) * 1e3 * 2.0 ** -24     # the one float32 addition
+    else:
+        assert not got[0].any()                            # empty expert -> zeros
+    gemm_tol_check(got, exact, bound, f"wgrad beta={beta}")

@@ -1,0 +1,229 @@
+"""GPU parity of the whole expert layer and of every GEMM launch at the full
+workload sizes (T = 16384, d = 4096, F = 1536, E = 384, k = 8)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import assert_bytes_equal, cuda_i32, gemm_tol_check, to_np
+from oracle import formats as fmt
+from oracle import gemm as og
+from oracle import layer as olayer
+from oracle import mxfp8 as mx
+from oracle import nvfp4 as nv
+from oracle import route
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import precision_moe_numerics_quant_amd as m4
+    from precision_moe_numerics_quant_amd import layer
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def test_layer_config1_end_to_end():
+    """Tiny layer (T=256, d=256, F=512, E=8, k=2): the stages with identical
+    inputs are bit-exact (routing, X and weight quantisation, dispatch gather),
+    U is within the GEMM tolerance, and the outputs downstream of a GEMM
+    (whose roundings may flip a few codes of H) track the oracle normwise."""
+    inp = synth.config_inputs(1, device="cpu")
+    k = 2
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k)
+    bw = layer.backward(fw, dev["dy"], seed=synth.SR_SEED)
+    x = synth.bf16_bits(inp["x"])
+    ofw = olayer.forward(x, synth.f32_np(inp["w_up"]), synth.f32_np(inp["w_down"]), synth.f32_np(inp["logits"]), k)
+    obw = olayer.backward(ofw, synth.bf16_bits(inp["dy"]), seed=synth.SR_SEED)
+    r = fw["route"]
+    for key in ("off", "off_pad", "perm", "inv_perm"):
+        assert_bytes_equal(to_np(r[key]), ofw["perm"][key], key)
+    assert_bytes_equal(to_np(r["idx"]), ofw["idx"], "idx")
+    assert_bytes_equal(to_np(r["gates"]).view(np.uint32), ofw["gates"].view(np.uint32), "gates")
+    for i, key in enumerate(("codes", "sf")):
+        assert_bytes_equal(to_np(fw["xq"][i]), ofw["xq"][key], "xq " + key)
+        assert_bytes_equal(to_np(fw["xq_perm"][i]), ofw["xq_perm"][key], "xq_perm " + key)
+        assert_bytes_equal(to_np(fw["wq"]["wu"][i]), ofw["wu"][key], "wu " + key)
+        assert_bytes_equal(to_np(fw["wq"]["wd"][i]), ofw["wd"][key], "wd " + key)
+    # the weight requantisations depend only on (bit-exact) weight codes: bit-exact
+    E, d, F = 8, 256, 512
+    assert_bytes_equal(to_np(bw["wdT"][0]), obw["wdT"][0], "W_down requant codes")
+    assert_bytes_equal(to_np(bw["wuT"][0]), obw["wuT"][0], "W_up requant codes")
+    # the X requantisation too (its input is the bit-exact dispatch gather)
+    n = d * ofw["perm"]["off_pad"][-1]
+    assert_bytes_equal(to_np(bw["xT"][0])[:n], obw["xT"][0], "X requant codes")
+    # U: GEMM tolerance against the exact product of the oracle's operands
+    off = ofw["perm"]["off"]
+    A64 = nv.nvfp4_exact_f64(ofw["xq_perm"]["codes"], ofw["xq_perm"]["sf"], ofw["xq_perm"]["ts"])
+    B64 = nv.nvfp4_exact_f64(ofw["wu"]["codes"], ofw["wu"]["sf"], ofw["wu"]["ts"], np.arange(E + 1) * F).reshape(E, F, d)
+    U = fmt.bf16_to_f32(to_np(fw["U"])).astype(np.float64)
+    gemm_tol_check(U, og.grouped_nt(A64, B64, off), og.abs_bound_nt(A64, B64, off), "U", out_bf16=True)
+    same_u = np.mean(to_np(fw["U"]) == ofw["U"])
+    h_codes_same = np.mean(to_np(fw["hq"][0]) == ofw["hq"]["codes"])
+    errs = dict(y=_rel(fmt.bf16_to_f32(to_np(fw["y"])), fmt.bf16_to_f32(ofw["y"])),
+                dx=_rel(fmt.bf16_to_f32(to_np(bw["dx"])), fmt.bf16_to_f32(obw["dx"])),
+                dW_up=_rel(to_np(bw["dW_up"]), obw["dW_up"]),
+                dW_down=_rel(to_np(bw["dW_down"]), obw["dW_down"]))
+    print(f"U bit-identical fraction {same_u:.5f}; H code bytes identical {h_codes_same:.5f}; rel errors {errs}")
+    assert same_u > 0.99 and h_codes_same > 0.98
+    # a flipped H code moves one product term by one NVFP4 step; normwise this stays
+    # at the level of the fraction of flipped codes times the NVFP4 relative step
+    for key, v in errs.items():
+        assert v < 2e-2, (key, v)
+
+
+# ------------------------------------------------------- full-size launches
+
+@pytest.fixture(scope="module")
+def cfg3_route():
+    c = synth.CONFIGS[4]
+    inp = synth.layer_inputs(c["T"], c["d"], c["F"], c["E"], c["k"], device="cuda", seed=0, zipf=c["zipf"],
+                             with_dy=False)
+    logits = synth.f32_np(inp["logits"])
+    bias = synth.f32_np(inp["bias"])
+    r = m4.moe_route_topk(inp["logits"], c["k"], inp["bias"])
+    idx, gates = route.topk_gates(logits, c["k"], bias)
+    P = route.permutation(idx, c["E"])
+    return c, inp, r, idx, gates, P
+
+
+def test_route_full_size(cfg3_route):
+    c, inp, r, idx, gates, P = cfg3_route
+    assert_bytes_equal(to_np(r["idx"]), idx, "idx")
+    assert_bytes_equal(to_np(r["gates"]).view(np.uint32), gates.view(np.uint32), "gates")
+    for key in ("off", "off_pad", "perm", "inv_perm"):
+        assert_bytes_equal(to_np(r[key]), P[key], key)
+    cnt = np.diff(P["off"])
+    assert (cnt == 0).sum() > 50 and cnt.max() > 5000      # Zipf-skewed: many empty experts, a few hot ones
+
+
+def _sample_experts(off):
+    cnt = np.diff(off)
+    order = np.argsort(-cnt, kind="stable")
+    act = order[cnt[order] > 0]
+    return sorted({int(act[0]), int(act[len(act) // 3]), int(act[-1]), int(act[len(act) // 2])})
+
+
+def _rand_nvfp4(rows, cols, seed, lo=0x28, hi=0x48):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    sf = rng.integers(lo, hi, (rows, cols // 16), dtype=np.uint8)
+    return codes, sf
+
+
+def _rand_mxfp8(n, seed, emin=120, emax=130):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, n, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E                     # no NaN codes
+    sf = rng.integers(emin, emax, n // 32, dtype=np.uint8)
+    return codes, sf
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_fwd_gemm_full_size_sampled(cfg3_route, which):
+    c, inp, r, idx, gates, P = cfg3_route
+    E, d, F = c["E"], c["d"], c["F"]
+    A = c["T"] * c["k"]
+    K, N = (d, F) if which == "up" else (F, d)
+    ac, asf = _rand_nvfp4(A, K, 1)
+    bc, bsf = _rand_nvfp4(E * N, K, 2)
+    rng = np.random.default_rng(3)
+    ats = rng.uniform(0.5, 2, E).astype(np.float32)
+    bts = rng.uniform(0.5, 2, E).astype(np.float32)
+    per_group = which == "down"
+    out_dt = torch.bfloat16 if which == "up" else torch.float32
+    cg = m4.moe_grouped_gemm_fwd(torch.from_numpy(ac).cuda(), torch.from_numpy(asf).cuda(),
+                                 torch.from_numpy(ats if per_group else ats[:1]).cuda(),
+                                 torch.from_numpy(bc).cuda().view(E, N, K // 2), torch.from_numpy(bsf).cuda().view(E, N, K // 16),
+                                 torch.from_numpy(bts).cuda(), r["off"], out_dt, a_ts_per_group=per_group)
+    off = P["off"].astype(np.int64)
+    cols = np.r_[np.arange(0, 64), rng.choice(N, 64, replace=False)]
+    for e in _sample_experts(off):
+        rows = np.arange(off[e], off[e + 1])
+        rows = rows if len(rows) <= 24 else np.r_[rows[:8], rng.choice(rows[8:-8], 8, replace=False), rows[-8:]]
+        a64 = nv.nvfp4_exact_f64(ac[rows], asf[rows], ats[e:e + 1] if per_group else ats[:1])
+        b64 = nv.nvfp4_exact_f64(bc[e * N + cols], bsf[e * N + cols], bts[e:e + 1])
+        exact = a64 @ b64.T
+        bound = np.abs(a64) @ np.abs(b64).T
+        got = to_np(cg[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+        got = fmt.bf16_to_f32(got).astype(np.float64) if which == "up" else got.astype(np.float64)
+        gemm_tol_check(got, exact, bound, f"fwd {which} expert {e}", out_bf16=which == "up")
+
+
+def test_dgrad_gemm_full_size_sampled(cfg3_route):
+    c, inp, r, idx, gates, P = cfg3_route
+    E, d, F = c["E"], c["d"], c["F"]
+    A = c["T"] * c["k"]
+    K, N = d, F                                   # dH = dY_row [A, d] . Wd_T[e] [F, d]^T
+    ac, asf = _rand_mxfp8(A * K, 4)
+    bc, bsf = _rand_mxfp8(E * N * K, 5)
+    cg = m4.moe_grouped_gemm_bwd_dgrad(torch.from_numpy(ac).cuda().view(A, K), torch.from_numpy(asf).cuda().view(A, K // 32),
+                                       torch.from_numpy(bc).cuda(), torch.from_numpy(bsf).cuda(), r["off"])
+    off = P["off"].astype(np.int64)
+    rng = np.random.default_rng(6)
+    cols = np.r_[np.arange(0, 32), rng.choice(N, 32, replace=False)]
+    for e in _sample_experts(off):
+        rows = np.arange(off[e], off[e + 1])
+        rows = rows if len(rows) <= 16 else np.r_[rows[:8], rows[-8:]]
+        a64 = mx.dequant_rowwise(ac.reshape(A, K)[rows], asf.reshape(A, K // 32)[rows])
+        bcr = bc.reshape(E, N, K)[e][cols]
+        bsr = bsf.reshape(E, N, K // 32)[e][cols]
+        b64 = mx.dequant_rowwise(bcr, bsr)
+        got = to_np(cg[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]).astype(np.float64)
+        gemm_tol_check(got, a64 @ b64.T, np.abs(a64) @ np.abs(b64).T, f"dgrad expert {e}")
+
+
+def test_wgrad_gemm_full_size_sampled(cfg3_route):
+    c, inp, r, idx, gates, P = cfg3_route
+    E, d, F = c["E"], c["d"], c["F"]
+    offp = P["off_pad"].astype(np.int64)
+    Ptot = int(offp[-1])
+    N1, N2 = d, F                                 # dW_down[e] = dY_col[e] [d][P] . H_T[e] [F][P]^T
+    ac, asf = _rand_mxfp8(N1 * Ptot, 7)
+    bc, bsf = _rand_mxfp8(N2 * Ptot, 8)
+    dw = m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(asf).cuda(),
+                                       torch.from_numpy(bc).cuda(), torch.from_numpy(bsf).cuda(), r["off_pad"], N1, N2)
+    rng = np.random.default_rng(9)
+    empty = np.nonzero(np.diff(offp) == 0)[0]
+    assert not to_np(dw[torch.from_numpy(empty[:4]).cuda()]).any()
+    for e in _sample_experts(P["off"].astype(np.int64)):
+        Pe = int(offp[e + 1] - offp[e])
+        rows = rng.choice(N1, 12, replace=False)
+        cols = rng.choice(N2, 12, replace=False)
+        a = ac[N1 * offp[e]: N1 * offp[e + 1]].reshape(N1, Pe)[rows]
+        as_ = asf[N1 * offp[e] // 32: N1 * offp[e + 1] // 32].reshape(N1, Pe // 32)[rows]
+        b = bc[N2 * offp[e]: N2 * offp[e + 1]].reshape(N2, Pe)[cols]
+        bs = bsf[N2 * offp[e] // 32: N2 * offp[e + 1] // 32].reshape(N2, Pe // 32)[cols]
+        a64 = mx.dequant_rowwise(a, as_)
+        b64 = mx.dequant_rowwise(b, bs)
+        got = to_np(dw[e][torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]).astype(np.float64)
+        gemm_tol_check(got, a64 @ b64.T, np.abs(a64) @ np.abs(b64).T, f"wgrad expert {e}")
+
+
+def test_weight_quant_and_requant_full_size_sampled(cfg3_route):
+    """W_down [384, 4096, 1536] fp32 -> NVFP4 (mode 6, per expert) -> MXFP8 SR
+    transposed, in the benchmark's launches; sampled experts bit-exact."""
+    c, inp, r, idx, gates, P = cfg3_route
+    E, d, F = c["E"], c["d"], c["F"]
+    w = inp["w_down"]
+    wq = layer.quantize_weights(inp["w_up"], w)
+    wd_c, wd_s, wd_t = wq["wd"]
+    wdT = m4.mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, 1, 3, max_pr=E * d)
+    for e in (0, 17, E - 1):
+        we = synth.f32_np(w[e])
+        q = nv.nvfp4_quantize(we, 6)
+        assert to_np(wd_t)[e] == q["ts"][0]
+        assert_bytes_equal(to_np(wd_c.view(E, d, F // 2)[e]), q["codes"], f"W codes expert {e}")
+        assert_bytes_equal(to_np(wd_s.view(E, d, F // 16)[e]), q["sf"], f"W scales expert {e}")
+        # requant of expert e alone: source rows e*d .. (e+1)*d of the stacked matrix
+        v = nv.nvfp4_dequantize(q["codes"], q["sf"], q["ts"])
+        idx_ = (np.uint64(e * d) + np.arange(d, dtype=np.uint64))[None, :] * np.uint64(F) + np.arange(F, dtype=np.uint64)[:, None]
+        cc, ss = mx.quantize_blocks_rows(v.T.reshape(F * d // 32, 32), mx.SR, 1, 3, idx_.reshape(F * d // 32, 32))
+        got_c = to_np(wdT[0][F * d * e: F * d * (e + 1)])
+        got_s = to_np(wdT[1][F * d * e // 32: F * d * (e + 1) // 32])
+        assert_bytes_equal(got_c, cc.reshape(-1), f"W requant codes expert {e}")
+        assert_bytes_equal(got_s, ss.reshape(-1), f"W requant scales expert {e}")

@@ -1,0 +1,277 @@
+"""GPU parity of the quantisers against the oracle: bit-exact codes and scales."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import assert_bytes_equal, bf16_from_bits, cuda_i32, to_np
+from oracle import formats as fmt
+from oracle import mxfp8 as mx
+from oracle import nvfp4 as nv
+from oracle import silu as osilu
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import precision_moe_numerics_quant_amd as m4
+
+
+def _bf16_input(R, C, seed, outliers=True):
+    x = synth.activations(R, C, "cpu", seed, outlier_p=0.001 if outliers else 0.0, outlier_mul=20.0)
+    return synth.bf16_bits(x)
+
+
+# ------------------------------------------------------------------ SiLU tables
+
+def test_silu_tables_exhaustive():
+    bits, s_ref, d_ref = osilu.tables()
+    u = bf16_from_bits(bits)
+    s, d = m4.moe_silu_eval(u)
+    assert_bytes_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32), "silu")
+    assert_bytes_equal(to_np(d).view(np.uint32), d_ref.view(np.uint32), "dsilu")
+
+
+# ------------------------------------------------------------------------ NVFP4
+
+@pytest.mark.parametrize("mode", [m4_mode for m4_mode in (6, 46)])
+@pytest.mark.parametrize("R,C", [(1, 16), (7, 48), (256, 256), (333, 1536)])
+def test_nvfp4_bf16_one_group(R, C, mode):
+    xb = _bf16_input(R, C, seed=R * 7 + C)
+    codes, sf, ts = m4.nvfp4_quant_46(bf16_from_bits(xb), mode)
+    ref = nv.nvfp4_quantize(xb, mode)
+    assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+    assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
+def test_nvfp4_f32_weights_grouped_mode6():
+    E, F, d = 5, 96, 160
+    w = synth.randn((E, F, d), 0.02, "cpu", 3, "w_up").numpy()
+    off = np.arange(E + 1) * F
+    codes, sf, ts = m4.nvfp4_quant_46(torch.from_numpy(w).cuda().view(E * F, d), 6, cuda_i32(off))
+    ref = nv.nvfp4_quantize(w.reshape(E * F, d), 6, off)
+    assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+    assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
+def test_nvfp4_ragged_groups_silu():
+    # empty groups, single-row groups and a group larger than one workgroup's rows
+    R, C = 400, 512
+    off = np.array([0, 0, 1, 1, 90, 91, 300, 400, 400])
+    u = synth.randn((R, C), 1.5, "cpu", 11, "u", torch.bfloat16)
+    ub = synth.bf16_bits(u)
+    codes, sf, ts = m4.nvfp4_quant_46(u.cuda(), 46, cuda_i32(off), m4.PRE_SILU)
+    ref = nv.nvfp4_quantize(osilu.silu_f32(ub), 46, off)
+    assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+    assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
+def test_nvfp4_special_values():
+    # zeros, -0, tiny and huge magnitudes, exact grid points, ties
+    C = 64
+    rows = [np.zeros(C), -np.zeros(C), np.full(C, 1e-38), np.linspace(-6, 6, C), np.full(C, 3e38),
+            np.r_[np.full(C // 2, 0.25), np.full(C // 2, -0.75)], np.float32(2.0) ** np.arange(-32, 32)]
+    x = np.stack(rows).astype(np.float32)
+    for mode in (6, 46):
+        for groups in (None, np.arange(len(rows) + 1)):
+            off_t = None if groups is None else cuda_i32(groups)
+            codes, sf, ts = m4.nvfp4_quant_46(torch.from_numpy(x).cuda(), mode, off_t)
+            ref = nv.nvfp4_quantize(x, mode, groups)
+            assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+            assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+            assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
+def test_nvfp4_power_of_two_equivariance_gpu():
+    xb = _bf16_input(64, 256, seed=5)
+    x = bf16_from_bits(xb)
+    base = m4.nvfp4_quant_46(x, 46)
+    for j in (-9, 4):
+        y = (x.float() * 2.0 ** j).to(torch.bfloat16)
+        q = m4.nvfp4_quant_46(y, 46)
+        assert torch.equal(q[0], base[0]) and torch.equal(q[1], base[1])
+        assert q[2].item() == base[2].item() * 2.0 ** j
+
+
+def test_nvfp4_dequant_matches_oracle():
+    xb = _bf16_input(96, 128, seed=6)
+    codes, sf, ts = m4.nvfp4_quant_46(bf16_from_bits(xb), 46)
+    out = m4.nvfp4_dequant(codes, sf, ts)
+    ref = nv.nvfp4_dequantize(to_np(codes), to_np(sf), to_np(ts))
+    assert_bytes_equal(to_np(out).view(np.uint32), ref.view(np.uint32), "dequant")
+
+
+def test_nvfp4_config2_full_size_sampled_rows():
+    """16384 x 7168 bf16 with 1% of rows x50, in the launch the benchmark times;
+    rows sampled (including outlier rows) are compared with the oracle, which
+    takes the GPU-independent tensor amax from the full input."""
+    cfg = synth.CONFIGS[2]
+    x = synth.config_inputs(2, device="cuda")["x"]
+    codes, sf, ts = m4.nvfp4_quant_46(x, 46)
+    xs = x.float().abs().max().item()
+    S_ref = np.float32(np.float32(xs) / np.float32(1792.0))
+    assert to_np(ts)[0] == S_ref
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.r_[rng.choice(cfg["R"], 48, replace=False), 0, cfg["R"] - 1])
+    big = torch.nonzero(x[:, :64].float().abs().amax(1) > 30).flatten().cpu().numpy()[:8]
+    rows = np.unique(np.r_[rows, big])
+    xb = synth.bf16_bits(x[torch.from_numpy(rows).cuda()])
+    q, sc, _ = nv.quantize_blocks(fmt.bf16_to_f32(xb), np.full(len(rows), S_ref, np.float32), 46)
+    assert_bytes_equal(to_np(sf[torch.from_numpy(rows).cuda()]), sc.astype(np.uint8), "sf")
+    assert_bytes_equal(to_np(codes[torch.from_numpy(rows).cuda()]), nv.pack_codes(q), "codes")
+
+
+# ------------------------------------------------------------------------ MXFP8
+
+def _nvfp4_operand(R, C, seed, groups=None, per_group=True):
+    xb = _bf16_input(R, C, seed)
+    ref = nv.nvfp4_quantize(xb, 46, groups if per_group else None)
+    return ref
+
+
+@pytest.mark.parametrize("R,C,groups", [
+    (64, 128, None),
+    (100, 96, [0, 0, 33, 33, 34, 100]),
+    (517, 256, [0, 200, 201, 480, 517]),
+])
+def test_requant_sr_t_bit_exact(R, C, groups):
+    off = np.array([0, R]) if groups is None else np.array(groups)
+    ref_q = _nvfp4_operand(R, C, R + C, off)
+    offp = mx.padded_offsets(off)
+    c_ref, s_ref = mx.requant_sr_t(ref_q["codes"], ref_q["sf"], ref_q["ts"], off, True, seed=1, stream_id=3)
+    oc, os_ = m4.mxfp8_requant_sr_T(torch.from_numpy(ref_q["codes"]).cuda(), torch.from_numpy(ref_q["sf"]).cuda(),
+                                    torch.from_numpy(ref_q["ts"]).cuda(), cuda_i32(off), cuda_i32(offp), True, 1, 3)
+    n = C * offp[-1]
+    assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "requant scales")
+    assert_bytes_equal(to_np(oc)[:n], c_ref, "requant codes")
+
+
+def test_requant_single_tensor_scale_and_seeds():
+    R, C = 96, 64
+    off = np.array([0, 10, 96])
+    xb = _bf16_input(R, C, 9)
+    ref_q = nv.nvfp4_quantize(xb, 46)
+    offp = mx.padded_offsets(off)
+    for seed, sid in ((1, 0), (7, 1), (1 << 40, 17)):
+        c_ref, s_ref = mx.requant_sr_t(ref_q["codes"], ref_q["sf"], ref_q["ts"], off, False, seed, sid)
+        oc, os_ = m4.mxfp8_requant_sr_T(torch.from_numpy(ref_q["codes"]).cuda(), torch.from_numpy(ref_q["sf"]).cuda(),
+                                        torch.from_numpy(ref_q["ts"]).cuda(), cuda_i32(off), cuda_i32(offp), False,
+                                        seed, sid)
+        n = C * offp[-1]
+        assert_bytes_equal(to_np(oc)[:n], c_ref, f"codes seed {seed}")
+        assert_bytes_equal(to_np(os_)[: n // 32], s_ref, f"scales seed {seed}")
+
+
+def test_sr_conversion_all_random_words():
+    """Every 16-bit random word against the oracle's rounding rule, for values
+    across the E4M3 range (normal, subnormal, negative, grid points)."""
+    vals = np.float32([1.03125, 1.0 + 2 ** -20, 7.77, 300.1, 447.9, 0.0005, 0.0123, -2.3, -0.004, 3.0, 2 ** -7 + 2 ** -20])
+    # one MX block per value: the value at column 0 plus 448 * 2**e-pinning companion so e = 0
+    R = 65536
+    C = 32
+    x = np.zeros((len(vals), R, C), dtype=np.float32)
+    # transposed mode quantises along rows: put the value in every row of column 0 and
+    # make the block amax 448 with a companion row so that e = 0 -> w = v
+    for i, v in enumerate(vals):
+        x[i, :, 0] = v
+    # rows are blocks of 32 along the token dimension: force amax 448 in row 0 of each block
+    x[:, ::32, 0] = 448.0
+    for i in range(len(vals)):
+        off = np.array([0, R])
+        c_ref, s_ref = mx.quantize_transposed(x[i], off, mx.SR, seed=1, stream_id=5)
+        oc, os_ = m4.mxfp8_quant(torch.from_numpy(x[i]).cuda(), transpose=True, group_row_off=cuda_i32(off),
+                                 group_off_pad=cuda_i32(off), max_pr=R, rnd=m4.SR, seed=1, stream_id=5)
+        assert_bytes_equal(to_np(oc), c_ref, f"SR codes value {vals[i]}")
+        assert_bytes_equal(to_np(os_), s_ref, f"SR scales value {vals[i]}")
+
+
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_mxfp8_grad_quant_gated_rows(rnd, transpose):
+    T, d, k, E = 130, 96, 3, 7
+    rng = np.random.default_rng(1)
+    dy = synth.randn((T, d), 1e-3, "cpu", 2, "dy", torch.bfloat16)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    from oracle import route
+    P = route.permutation(idx, E)
+    gates = rng.random((T, k)).astype(np.float32)
+    dyp = (gates.reshape(-1)[P["perm"]][:, None] * fmt.bf16_to_f32(synth.bf16_bits(dy))[P["perm"] // k]).astype(np.float32)
+    A = T * k
+    args = dict(rows=A, row_map=cuda_i32(P["perm"]), map_div=k, row_scale=torch.from_numpy(gates.reshape(-1)).cuda(),
+                rnd=rnd, seed=3, stream_id=4)
+    if transpose:
+        oc, os_ = m4.mxfp8_quant(dy.cuda(), transpose=True, group_row_off=cuda_i32(P["off"]),
+                                 group_off_pad=cuda_i32(P["off_pad"]), **args)
+        c_ref, s_ref = mx.quantize_transposed(dyp, P["off"], rnd, 3, 4)
+        n = d * P["off_pad"][-1]
+        assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
+        assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
+    else:
+        oc, os_ = m4.mxfp8_quant(dy.cuda(), **args)
+        c_ref, s_ref = mx.quantize_rowwise(dyp, rnd, 3, 4)
+        assert_bytes_equal(to_np(oc), c_ref, "codes")
+        assert_bytes_equal(to_np(os_), s_ref, "scales")
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_mxfp8_grad_quant_dsilu(transpose):
+    R, F = 150, 128
+    off = np.array([0, 40, 40, 150])
+    dh = synth.randn((R, F), 1e-3, "cpu", 4, "dh").numpy()
+    u = synth.randn((R, F), 2.0, "cpu", 5, "u", torch.bfloat16)
+    du = (dh * osilu.dsilu_f32(synth.bf16_bits(u))).astype(np.float32)
+    if transpose:
+        offp = mx.padded_offsets(off)
+        oc, os_ = m4.mxfp8_quant(torch.from_numpy(dh).cuda(), transpose=True, dsilu_src=u.cuda(),
+                                 group_row_off=cuda_i32(off), group_off_pad=cuda_i32(offp))
+        c_ref, s_ref = mx.quantize_transposed(du, off, mx.RNE)
+        n = F * offp[-1]
+        assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
+        assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
+    else:
+        oc, os_ = m4.mxfp8_quant(torch.from_numpy(dh).cuda(), dsilu_src=u.cuda())
+        c_ref, s_ref = mx.quantize_rowwise(du, mx.RNE)
+        assert_bytes_equal(to_np(oc), c_ref, "codes")
+        assert_bytes_equal(to_np(os_), s_ref, "scales")
+
+
+def test_requant_config2_full_size_sampled_columns():
+    """16384 x 7168 requant in the benchmark's launch; output rows (source
+    columns) sampled and compared with the oracle on the same NVFP4 input."""
+    x = synth.config_inputs(2, device="cuda")["x"]
+    codes, sf, ts = m4.nvfp4_quant_46(x, 46)
+    R, C = x.shape
+    off = cuda_i32([0, R])
+    oc, os_ = m4.mxfp8_requant_sr_T(codes, sf, ts, off, off, True, 1, 0, max_pr=R)
+    rng = np.random.default_rng(1)
+    cols = np.unique(np.r_[rng.choice(C // 16, 6, replace=False) * 16, C - 16])   # whole NVFP4 blocks
+    for c0 in cols:
+        blk = slice(c0 // 2, c0 // 2 + 8)
+        sub_codes = to_np(codes[:, blk])
+        sub_sf = to_np(sf[:, c0 // 16: c0 // 16 + 1])
+        q = nv.unpack_codes(sub_codes)
+        v = nv.dequant_values(q, np.repeat(sub_sf.astype(np.int64), 16, axis=1), to_np(ts)[0])
+        # element (r, c0 + j) has source index r * C + c0 + j: quantise with that index map
+        got_c = to_np(oc).reshape(C, R)[c0:c0 + 16]
+        got_s = to_np(os_).reshape(C, R // 32)[c0:c0 + 16]
+        vt = v.T.astype(np.float64)
+        nb = R // 32
+        idx = (np.arange(R, dtype=np.uint64)[None, :] * np.uint64(C) + (np.uint64(c0) + np.arange(16, dtype=np.uint64))[:, None])
+        cc, ss = mx.quantize_blocks_rows(v.T.reshape(16 * nb, 32), mx.SR, 1, 0, idx.reshape(16 * nb, 32))
+        assert_bytes_equal(got_c, cc.reshape(16, R), f"codes cols {c0}")
+        assert_bytes_equal(got_s, ss.reshape(16, nb), f"scales cols {c0}")
+
+
+def test_run_twice_deterministic():
+    xb = _bf16_input(300, 512, 12)
+    x = bf16_from_bits(xb)
+    a = m4.nvfp4_quant_46(x, 46)
+    b = m4.nvfp4_quant_46(x, 46)
+    assert all(torch.equal(p, q) for p, q in zip(a, b))
+    off = cuda_i32([0, 300])
+    r1 = m4.mxfp8_requant_sr_T(a[0], a[1], a[2], off, cuda_i32([0, 320]), True, 1, 0)
+    r2 = m4.mxfp8_requant_sr_T(a[0], a[1], a[2], off, cuda_i32([0, 320]), True, 1, 0)
+    n = 512 * 320      # the written extent; the buffers are sized by the padded upper bound
+    assert torch.equal(r1[0][:n], r2[0][:n]) and torch.equal(r1[1][:n // 32], r2[1][:n // 32])
