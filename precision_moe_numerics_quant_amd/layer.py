@@ -28,38 +28,57 @@ from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, max_padded_rows, moe_combin
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
 
-def quantize_weights(w_up, w_down):
-    """NVFP4 (mode 6) of the fp32 masters, one tensor scale per expert matrix."""
+def _tick(timer, name):
+    if timer is not None:
+        timer(name)
+
+
+def quantize_weights(w_up, w_down, timer=None):
+    """NVFP4 (mode 6) of the fp32 masters, one tensor scale per expert matrix.
+
+    ``timer``, if given, is called with a step name after each library call
+    (the benchmark records a HIP event there)."""
     E, F, d = w_up.shape
     dev = w_up.device
     off_f = torch.arange(E + 1, dtype=torch.int32, device=dev) * F
     off_d = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
+    _tick(timer, None)
     wu = nvfp4_quant_46(w_up.view(E * F, d), NVFP4_6, off_f)
+    _tick(timer, "F1 W_up quant")
     wd = nvfp4_quant_46(w_down.view(E * d, F), NVFP4_6, off_d)
+    _tick(timer, "F1 W_down quant")
     return dict(wu=wu, wd=wd, off_f=off_f, off_d=off_d, shape=(E, F, d))
 
 
-def forward(x, w_up, w_down, logits, k, bias=None, wq=None):
+def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None):
     """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32."""
     T, d = x.shape
     E, F, _ = w_up.shape
     if wq is None:
-        wq = quantize_weights(w_up, w_down)
+        wq = quantize_weights(w_up, w_down, timer)
+    _tick(timer, None)
     r = moe_route_topk(logits, k, bias)
+    _tick(timer, "F2-F3 route + permutation")
     xq = nvfp4_quant_46(x, NVFP4_4OVER6)
+    _tick(timer, "F4 X quant (NVFP4 4/6)")
     xq_perm = moe_gather_rows(xq[0], xq[1], r["perm"], k)
+    _tick(timer, "F5 dispatch gather")
     wu_c, wu_s, wu_t = wq["wu"]
     wd_c, wd_s, wd_t = wq["wd"]
     U = moe_grouped_gemm_fwd(xq_perm[0], xq_perm[1], xq[2], wu_c.view(E, F, d // 2), wu_s.view(E, F, d // 16), wu_t,
                              r["off"], torch.bfloat16)
+    _tick(timer, "F6 up GEMM (NVFP4)")
     hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU)
+    _tick(timer, "F7 SiLU + H quant (NVFP4 4/6)")
     Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
                               r["off"], torch.float32, a_ts_per_group=True)
+    _tick(timer, "F8 down GEMM (NVFP4)")
     y = moe_combine(Yp, r["gates"], r["inv_perm"])
+    _tick(timer, "F9 combine")
     return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k))
 
 
-def backward(fw, dy, seed=1, layer=0):
+def backward(fw, dy, seed=1, layer=0, timer=None):
     """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, ...)."""
     T, d, F, E, k = fw["dims"]
     r = fw["route"]
@@ -67,25 +86,39 @@ def backward(fw, dy, seed=1, layer=0):
     mpr = max_padded_rows(A, E)
     sid = lambda role: 16 * layer + role
     g_flat = r["gates"].view(-1)
+    _tick(timer, None)
     dy_row = mxfp8_quant(dy, rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat)
+    _tick(timer, "B1 dY quant row-wise (MXFP8)")
     dy_col = mxfp8_quant(dy, rows=A, transpose=True, row_map=r["perm"], map_div=k, row_scale=g_flat,
                          group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr)
+    _tick(timer, "B1 dY quant transposed (MXFP8)")
     wq = fw["wq"]
     wd_c, wd_s, wd_t = wq["wd"]
     wdT = mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, seed, sid(ROLE_WDOWN), max_pr=E * d)
+    _tick(timer, "B2 W_down requant SR-T")
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
+    _tick(timer, "B3 down dgrad (MXFP8)")
     hq = fw["hq"]
     hT = mxfp8_requant_sr_T(hq[0], hq[1], hq[2], r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr)
+    _tick(timer, "B4 H requant SR-T")
     dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
+    _tick(timer, "B5 down wgrad (MXFP8)")
     du_row = mxfp8_quant(dH, dsilu_src=fw["U"])
+    _tick(timer, "B6 SiLU' + dU quant row-wise")
     du_col = mxfp8_quant(dH, transpose=True, dsilu_src=fw["U"], group_row_off=r["off"], group_off_pad=r["off_pad"],
                          max_pr=mpr)
+    _tick(timer, "B6 SiLU' + dU quant transposed")
     wu_c, wu_s, wu_t = wq["wu"]
     wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
+    _tick(timer, "B7 W_up requant SR-T")
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
+    _tick(timer, "B8 up dgrad (MXFP8)")
     xp = fw["xq_perm"]
     xT = mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X), max_pr=mpr)
+    _tick(timer, "B9 X requant SR-T")
     dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d)
+    _tick(timer, "B10 up wgrad (MXFP8)")
     dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
+    _tick(timer, "B11 un-permute sum")
     return dict(dx=dx, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
                 du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)
