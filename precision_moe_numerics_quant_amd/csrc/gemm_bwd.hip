@@ -11,87 +11,153 @@
 // Operand layout of the 32x32x64 scaled MFMA (measured on gfx950): lane l
 // (g = l / 32, i = l % 32) holds row i's bytes k in [16g, 16g+16) and
 // [32+16g, 32+16g+16) of the 64-wide K chunk, and supplies the scale of row i,
-// K block g.  Tile 128 x 128 x 128 bytes, 256 threads as 2 x 2 waves of
-// 64 x 64; next slab prefetched into registers during the MFMAs.
+// K block g.
+//
+// Kernel shape: BM x BN tile, K slabs of 64 bytes (one MFMA step), 256
+// threads as 2 x 2 waves of (BM/2) x (BN/2).  Operands are read with raw
+// buffer loads (32-bit offsets from a per-operand descriptor whose range check
+// returns zeros past the tensor and for masked K tails, so no load branches);
+// the whole slab's MFMA operands are held in registers; slab s is fetched
+// into one of two register sets three slabs ahead, written to LDS one slab
+// ahead (LDS rows unpadded with XOR-swizzled 16-byte chunks: conflict-free
+// slab writes and fragment reads), and its MFMAs overlap the next slab's LDS
+// traffic.  The epilogue stages the float32 tile through LDS so every global
+// store is a 16-byte, row-contiguous write.
+#include <stdlib.h>
+
 #include "gemm_common.h"
 #include "moe4_internal.h"
 
 namespace moe4 {
 
 namespace bwd {
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row
 constexpr int THREADS = 256;
+constexpr int BK = 64;
+constexpr int LDS_STRIDE = BK;  // bytes per LDS row: unpadded, 16-byte chunks XOR-swizzled by row
+// physical 16-byte chunk of logical chunk c in row r: a wave's 64 slab writes
+// fill 1 KB contiguously and 16 lanes reading one logical chunk of 16
+// consecutive rows hit 16 distinct 4-bank groups
+__device__ inline int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+constexpr uint32_t OOB = 0x80000000u;  // offset past every operand: loads return 0
 }  // namespace bwd
 
-struct Fp8Frag {
-  u32x4 q[4];  // 64 bytes
-  uint32_t s;  // 2 scale bytes
-};
-
-// Row `row` of an MXFP8 operand with row stride ld (bytes) and scale row
-// stride ld/32; 64 bytes at k0 + half*64, masked to k < klen.
-__device__ inline Fp8Frag load_fp8_frag(const uint8_t* codes, const uint8_t* sf, int64_t row, bool valid, int64_t ld,
-                                        int64_t klen, int64_t k0, int half) {
-  Fp8Frag f;
-  const int64_t kb = k0 + half * 64;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const bool ok = valid && kb + 16 * c < klen;
-    f.q[c] = ok ? *reinterpret_cast<const u32x4*>(codes + row * ld + kb + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
-  f.s = 0u;
-  if (valid) {
-    const uint8_t* sp = sf + row * (ld / 32) + kb / 32;
-    if (kb < klen) f.s |= (uint32_t)sp[0];
-    if (kb + 32 < klen) f.s |= (uint32_t)sp[1] << 8;
-  }
-  return f;
+// Buffer descriptor of a wave-uniform range (kept in scalar registers).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  // readfirstlane yields a signed 32-bit int: go through uint32_t so that the
+  // low word is zero-extended (a sign-extended low word would corrupt the base)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t au = ((uint64_t)hi << 32) | (uint64_t)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(au), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 
-__device__ inline void store_fp8_frag(const Fp8Frag& f, uint8_t* dst_row, uint8_t* dst_scale_row, int half) {
-  u32x4* d = reinterpret_cast<u32x4*>(dst_row + half * 64);
+// One operand's slab in registers: ROWS rows x 64 bytes.  Thread t loads the
+// 16-byte chunk t % 4 of rows t / 4 + 64 j, and the 2 scale bytes of row t.
+template <int ROWS>
+struct MxSlab {
+  u32x4 q[ROWS / 64];
+  uint32_t s0, s1;  // scale bytes of K blocks 0 and 1 (combined only when written to LDS)
+};
+
+template <int ROWS>
+struct MxOperand {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t off[ROWS / 64];  // byte offset of the thread's rows (k excluded)
+  uint32_t soff;            // byte offset of the thread's scale row (t < ROWS)
+  uint32_t klen;
+
+  __device__ void init(const uint8_t* c, const uint8_t* s, int64_t rows_total, int64_t ld, int64_t row0, int64_t kl) {
+    codes = make_rsrc(c, (uint64_t)rows_total * ld);
+    scales = make_rsrc(s, (uint64_t)rows_total * (ld / 32));
+    klen = (uint32_t)kl;
+    const int t = threadIdx.x;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) d[c] = f.q[c];
-  dst_scale_row[half * 2] = (uint8_t)(f.s & 0xFFu);
-  dst_scale_row[half * 2 + 1] = (uint8_t)(f.s >> 8);
+    for (int j = 0; j < ROWS / 64; ++j) {
+      const int64_t row = row0 + t / 4 + 64 * j;
+      off[j] = row < rows_total ? (uint32_t)(row * ld + (t % 4) * 16) : bwd::OOB;
+    }
+    const int64_t row = row0 + t;
+    soff = (t < ROWS && row < rows_total) ? (uint32_t)(row * (ld / 32)) : bwd::OOB;
+  }
+
+  // k0 past the contraction yields zeros (the descriptor's range check).
+  __device__ void load(MxSlab<ROWS>& r, uint32_t k0) const {
+    const int t = threadIdx.x;
+    const bool kok = k0 + (t % 4) * 16 < klen;
+#pragma unroll
+    for (int j = 0; j < ROWS / 64; ++j) {
+      const uint32_t o = (kok && off[j] != bwd::OOB) ? off[j] + k0 : bwd::OOB;
+      r.q[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(codes, o, 0, 0));
+    }
+    const uint32_t so = (soff == bwd::OOB || k0 >= klen) ? bwd::OOB : soff + k0 / 32;
+    r.s0 = __builtin_amdgcn_raw_buffer_load_b8(scales, so, 0, 0);
+    r.s1 = __builtin_amdgcn_raw_buffer_load_b8(scales, (k0 + 32 < klen && so != bwd::OOB) ? so + 1u : bwd::OOB, 0, 0);
+  }
+};
+
+// Scale bytes go to LDS as [half h][block b][lane row li][fragment f] with
+// row = h * ROWS/2 + 32 f + li, so a lane reads the scales of all its
+// fragments for one K block as a single dword.
+template <int ROWS>
+__device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_t* lds_s) {
+  constexpr int F = ROWS / 64;  // 32-row fragments per half
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < ROWS / 64; ++j)
+    *reinterpret_cast<u32x4*>(lds + (t / 4 + 64 * j) * bwd::LDS_STRIDE + bwd::swz(t / 4 + 64 * j, t % 4) * 16) =
+        r.q[j];
+  if (t < ROWS) {
+    const int h = t / (ROWS / 2), f = (t % (ROWS / 2)) / 32, li = t % 32;
+    lds_s[((h * 2 + 0) * 32 + li) * F + f] = (uint8_t)r.s0;
+    lds_s[((h * 2 + 1) * 32 + li) * F + f] = (uint8_t)r.s1;
+  }
 }
 
 // MODE 0: dgrad (A rows grouped by expert_off, B [E][N][K], C [M_total][N]);
 // MODE 1: wgrad (per expert e: A_e [N1][P_e], B_e [N2][P_e], C = dw[e]).
-template <int MODE>
-__global__ void __launch_bounds__(bwd::THREADS) k_gemm_mx(const uint8_t* __restrict__ a_codes,
-                                                          const uint8_t* __restrict__ a_sf,
-                                                          const uint8_t* __restrict__ b_codes,
-                                                          const uint8_t* __restrict__ b_sf,
-                                                          const int32_t* __restrict__ off, int E, int64_t M1,
-                                                          int64_t N, int64_t K, int64_t n_ntiles, int64_t n_mtiles,
-                                                          float* __restrict__ c, float beta) {
+template <int MODE, int BM, int BN, int MINB>
+__global__ void __launch_bounds__(bwd::THREADS, MINB) k_gemm_mx(const uint8_t* __restrict__ a_codes,
+                                                                const uint8_t* __restrict__ a_sf,
+                                                                const uint8_t* __restrict__ b_codes,
+                                                                const uint8_t* __restrict__ b_sf,
+                                                                const int32_t* __restrict__ off, int E, int64_t M1,
+                                                                int64_t N, int64_t K, int64_t n_ntiles,
+                                                                int64_t n_mtiles, float* __restrict__ c, float beta) {
   using namespace bwd;
-  __shared__ __attribute__((aligned(16))) uint8_t la[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t lb[BN * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t las[BM * 4];
-  __shared__ __attribute__((aligned(16))) uint8_t lbs[BN * 4];
-  const int64_t nt = blockIdx.x % n_ntiles;
-  int64_t row0, row_end, klen, lda, ldc;
+  constexpr int WM = BM / 2, MI = WM / 32;  // wave rows, 32-row fragments per wave
+  constexpr int WN = BN / 2, NJ = WN / 32;  // wave cols, 32-col fragments per wave
+  constexpr int A_BYTES = BM * LDS_STRIDE, B_BYTES = BN * LDS_STRIDE;
+  constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * 2;
+  constexpr int BS = WN + 8;  // epilogue band row stride (floats): rows 4 apart land 32 banks apart
+  constexpr int SMEM = STAGE > 4 * 32 * BS * 4 ? STAGE : 4 * 32 * BS * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+
+  const int64_t n_all = MODE == 0 ? n_ntiles * n_mtiles : n_ntiles * n_mtiles * E;
+  const int64_t tile = xcd_tile(blockIdx.x, n_all);
+  if (tile >= n_all) return;
+  const int64_t nt = tile % n_ntiles;
+  int64_t row0, row_end, klen, arows, ld;
   const uint8_t *A, *As, *B, *Bs;
   float* C;
   if (MODE == 0) {
     int e;
     int64_t mt;
-    if (!find_m_tile(off, E, BM, blockIdx.x / n_ntiles, e, mt)) return;
+    if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
     row0 = (int64_t)off[e] + mt * BM;
     row_end = (int64_t)off[e + 1] < M1 ? (int64_t)off[e + 1] : M1;  // M1 = M_total here
     klen = K;
-    lda = K;
+    ld = K;
+    arows = M1;
     A = a_codes;
     As = a_sf;
     B = b_codes + (int64_t)e * N * K;
     Bs = b_sf + (int64_t)e * N * (K / 32);
     C = c;
-    ldc = N;
   } else {
-    const int64_t rest = blockIdx.x / n_ntiles;
+    const int64_t rest = tile / n_ntiles;
     const int e = (int)(rest / n_mtiles);
     const int64_t mt = rest % n_mtiles;
     if (e >= E) return;
@@ -99,81 +165,171 @@ __global__ void __launch_bounds__(bwd::THREADS) k_gemm_mx(const uint8_t* __restr
     klen = (int64_t)off[e + 1] - p0;  // padded token count (multiple of 32)
     row0 = mt * BM;
     row_end = M1;
-    lda = klen;
+    ld = klen;
+    arows = M1;
     A = a_codes + M1 * p0;
     As = a_sf + M1 * p0 / 32;
     B = b_codes + N * p0;
     Bs = b_sf + N * p0 / 32;
     C = c + (int64_t)e * M1 * N;
-    ldc = N;
     if (klen == 0 && beta != 0.0f) return;  // nothing to add
   }
   const int64_t n0 = nt * BN;
   const int tid = threadIdx.x;
-  const int lrow = tid >> 1, half = tid & 1;
-  const bool a_ok = row0 + lrow < row_end;
-  const bool b_ok = n0 + lrow < N;
   const int w = tid >> 6, l = tid & 63;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
   const int g = l >> 5, li = l & 31;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  Fp8Frag fa, fb;
-  if (klen > 0) {
-    fa = load_fp8_frag(A, As, row0 + lrow, a_ok, lda, klen, 0, half);
-    fb = load_fp8_frag(B, Bs, n0 + lrow, b_ok, lda, klen, 0, half);
-  }
-  for (int64_t k0 = 0; k0 < klen; k0 += BK) {
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+
+  MxOperand<BM> opa;
+  MxOperand<BN> opb;
+  opa.init(A, As, arows, ld, row0, klen);
+  opb.init(B, Bs, N, ld, n0, klen);
+  // Slab s is loaded into register set s % 2 three slabs ahead, written to
+  // LDS one slab ahead, and read into the fragment registers (which hold a
+  // whole slab's MFMA operands) right after the previous slab's MFMAs.
+  MxSlab<BM> ra0, ra1;
+  MxSlab<BN> rb0, rb1;
+  const int64_t nk = (klen + BK - 1) / BK;
+  uint8_t* la = smem;
+  uint8_t* lb = smem + A_BYTES;
+  uint8_t* las = smem + A_BYTES + B_BYTES;
+  uint8_t* lbs = las + BM * 2;
+  i32x8 fa[MI], fb[NJ];
+  int sa[MI], sb[NJ];
+  auto read_frags = [&]() {
+    uint32_t sa_w[(MI + 3) / 4], sb_w[(NJ + 3) / 4];
+#pragma unroll
+    for (int q = 0; q < (MI + 3) / 4; ++q)
+      sa_w[q] = *reinterpret_cast<const uint32_t*>(las + (((w >> 1) * 2 + g) * 32 + li) * MI + 4 * q);
+#pragma unroll
+    for (int q = 0; q < (NJ + 3) / 4; ++q)
+      sb_w[q] = *reinterpret_cast<const uint32_t*>(lbs + (((w & 1) * 2 + g) * 32 + li) * NJ + 4 * q);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm + i * 32 + li;
+      const uint8_t* p = la + r * LDS_STRIDE;
+      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, g));
+      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, 2 + g));
+      fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      sa[i] = (sa_w[i / 4] >> (8 * (i % 4))) & 0xFF;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn + j * 32 + li;
+      const uint8_t* p = lb + r * LDS_STRIDE;
+      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, g));
+      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, 2 + g));
+      fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      sb[j] = (sb_w[j / 4] >> (8 * (j % 4))) & 0xFF;
+    }
+  };
+  auto mfmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+  };
+  auto stage = [&](const MxSlab<BM>& ra, const MxSlab<BN>& rb) {
+    store_mx_slab<BM>(ra, la, las);
+    store_mx_slab<BN>(rb, lb, lbs);
+  };
+  // One slab: write slab s+1 to LDS, fetch slab s+3, MFMAs of slab s, read
+  // slab s+1.  Past the last slab the loads return zeros and the LDS traffic
+  // is unused, so the body has no branches.
+  auto step = [&](uint32_t s, MxSlab<BM>& ra_next, MxSlab<BN>& rb_next) {
     __syncthreads();
-    store_fp8_frag(fa, la + lrow * LDS_STRIDE, las + lrow * 4, half);
-    store_fp8_frag(fb, lb + lrow * LDS_STRIDE, lbs + lrow * 4, half);
+    stage(ra_next, rb_next);
+    opa.load(ra_next, (s + 3) * BK);
+    opb.load(rb_next, (s + 3) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    if (k0 + BK < klen) {
-      fa = load_fp8_frag(A, As, row0 + lrow, a_ok, lda, klen, k0 + BK, half);
-      fb = load_fp8_frag(B, Bs, n0 + lrow, b_ok, lda, klen, k0 + BK, half);
-    }
-#pragma unroll
-    for (int kc = 0; kc < BK; kc += 64) {
-      i32x8 av[2], bv[2];
-      int sa[2], sb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint8_t* pa = la + (wm + i * 32 + li) * LDS_STRIDE + kc + 16 * g;
-        const uint8_t* pb = lb + (wn + i * 32 + li) * LDS_STRIDE + kc + 16 * g;
-        i32x4 a0 = *reinterpret_cast<const i32x4*>(pa), a1 = *reinterpret_cast<const i32x4*>(pa + 32);
-        i32x4 b0 = *reinterpret_cast<const i32x4*>(pb), b1 = *reinterpret_cast<const i32x4*>(pb + 32);
-        av[i] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        bv[i] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        sa[i] = las[(wm + i * 32 + li) * 4 + kc / 32 + g];
-        sb[i] = lbs[(wn + i * 32 + li) * 4 + kc / 32 + g];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv[j], acc[i][j], 0, 0, 0, sa[i], 0,
-                                                                      sb[j]);
-    }
+    read_frags();
+  };
+  if (nk > 0) {
+    opa.load(ra0, 0);
+    opb.load(rb0, 0);
+    stage(ra0, rb0);
+    opa.load(ra1, BK);
+    opb.load(rb1, BK);
+    opa.load(ra0, 2 * BK);
+    opb.load(rb0, 2 * BK);
+    __syncthreads();
+    read_frags();
   }
+  uint32_t it = 0;
+  for (; it + 1 < (uint32_t)nk; it += 2) {
+    step(it, ra1, rb1);
+    step(it + 1, ra0, rb0);
+  }
+  if (it < (uint32_t)nk) step(it, ra1, rb1);
+  // Epilogue: each wave stages 32-row bands of its tile in LDS (row stride
+  // WN + 4 floats) and writes them back as 16-byte row-contiguous stores.
+  float* band = reinterpret_cast<float*>(smem) + w * (32 * BS);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn + j * 32 + li;
-      if (col >= N) continue;
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row >= row_end) continue;
-        float* p = C + row * ldc + col;
-        if (MODE == 1 && beta != 0.0f) *p = *p + acc[i][j][v];
-        else *p = acc[i][j][v];
+      for (int v = 0; v < 16; ++v) band[((v >> 2) * 8 + g * 4 + (v & 3)) * BS + j * 32 + li] = acc[i][j][v];
+    __builtin_amdgcn_wave_barrier();
+    constexpr int QPR = WN / 4;  // column quads per row
+#pragma unroll
+    for (int q = 0; q < 32 * QPR / 64; ++q) {
+      const int idx = q * 64 + l;
+      const int rr = idx / QPR, cq = idx % QPR;
+      const int64_t row = row0 + wm + i * 32 + rr;
+      const int64_t col = n0 + wn + cq * 4;
+      if (row < row_end && col < N) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * BS + cq * 4);
+        f32x4* p = reinterpret_cast<f32x4*>(C + row * N + col);
+        if (MODE == 1 && beta != 0.0f) {
+          f32x4 o = *p;
+          v = f32x4{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+        }
+        __builtin_nontemporal_store(v, p);
       }
     }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int MODE, int BM, int BN, int MINB>
+static void launch_mx_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, const int32_t* off,
+                        int E, int64_t M1, int64_t N, int64_t K, float* c, float beta, hipStream_t s) {
+  const int64_t n_nt = (N + BN - 1) / BN;
+  const int64_t n_mt = MODE == 0 ? (M1 + BM - 1) / BM + E : (M1 + BM - 1) / BM;
+  const int64_t n_tiles = MODE == 0 ? n_nt * n_mt : n_nt * n_mt * E;
+  hipLaunchKernelGGL((k_gemm_mx<MODE, BM, BN, MINB>), dim3((unsigned)xcd_grid(n_tiles)), dim3(bwd::THREADS), 0, s, ac,
+                     as, bc, bs, off, E, M1, N, K, n_nt, n_mt, c, beta);
+}
+
+// Configuration choice (MOE4_MX_TILE overrides, for tuning): 0 = 256x256,
+// 1 = 128x128 (2 blocks/CU), 2 = 128x256.
+static int mx_tile_choice() {
+  static int v = [] {
+    const char* e = getenv("MOE4_MX_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+template <int MODE>
+static void launch_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, const int32_t* off,
+                      int E, int64_t M1, int64_t N, int64_t K, float* c, float beta, hipStream_t s) {
+  switch (mx_tile_choice()) {
+    case 1: launch_mx_t<MODE, 128, 128, 2>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
+    case 2: launch_mx_t<MODE, 128, 256, 1>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
+    default: launch_mx_t<MODE, 256, 256, 1>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
+  }
 }
 
 }  // namespace moe4
@@ -189,12 +345,10 @@ extern "C" int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t*
   MOE4_REQUIRE(M_total == 0 || (a_codes && a_sf && c), MOE4_EINVAL, "moe_grouped_gemm_bwd_dgrad: NULL pointer");
   MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(c), MOE4_EALIGN,
                "moe_grouped_gemm_bwd_dgrad: misaligned pointer");
+  MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_bwd_dgrad: A and each expert's B must stay below 2 GiB");
   if (M_total == 0) return MOE4_OK;
-  const int64_t n_nt = (N + bwd::BN - 1) / bwd::BN;
-  const int64_t n_mt = (M_total + bwd::BM - 1) / bwd::BM + E;
-  MOE4_REQUIRE(n_nt * n_mt < ((int64_t)1 << 31), MOE4_EINVAL, "moe_grouped_gemm_bwd_dgrad: too large");
-  hipLaunchKernelGGL((k_gemm_mx<0>), dim3((unsigned)(n_nt * n_mt)), dim3(bwd::THREADS), 0, as_stream(stream), a_codes,
-                     a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, n_nt, n_mt, c, 0.0f);
+  launch_mx<0>(a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c, 0.0f, as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_dgrad");
 }
 
@@ -208,11 +362,9 @@ extern "C" int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t*
                "moe_grouped_gemm_bwd_wgrad: NULL pointer");
   MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(dw), MOE4_EALIGN,
                "moe_grouped_gemm_bwd_wgrad: misaligned pointer");
-  const int64_t n_nt = (N2 + bwd::BN - 1) / bwd::BN;
-  const int64_t n_mt = (N1 + bwd::BM - 1) / bwd::BM;
-  MOE4_REQUIRE(n_nt * n_mt * E < ((int64_t)1 << 31), MOE4_EINVAL, "moe_grouped_gemm_bwd_wgrad: too large");
-  hipLaunchKernelGGL((k_gemm_mx<1>), dim3((unsigned)(n_nt * n_mt * E)), dim3(bwd::THREADS), 0, as_stream(stream),
-                     a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, (int64_t)0, n_nt, n_mt, dw, beta);
+  MOE4_REQUIRE(((N2 + 127) / 128) * ((N1 + 127) / 128) * E < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_bwd_wgrad: too large");
+  launch_mx<1>(a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, (int64_t)0, dw, beta, as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_wgrad");
 }
 

@@ -4,6 +4,19 @@
 
 namespace moe4 {
 
+// XCD-aware tile order.  MI355X dispatches consecutive workgroups round-robin
+// over its 8 XCDs (each with its own L2); mapping workgroup b to tile
+// (b % 8) * ceil(n/8) + b / 8 gives each XCD a contiguous run of tiles, so the
+// tiles that share an operand slab (e.g. all N-tiles of one M-tile) run on the
+// same XCD and hit the same L2.  The grid is rounded up to a multiple of 8;
+// workgroups whose tile is >= n exit.
+constexpr int N_XCD = 8;
+__host__ __device__ inline int64_t xcd_grid(int64_t n) { return (n + N_XCD - 1) / N_XCD * N_XCD; }
+__device__ inline int64_t xcd_tile(int64_t b, int64_t n) {
+  const int64_t per = (n + N_XCD - 1) / N_XCD;
+  return (b % N_XCD) * per + b / N_XCD;
+}
+
 // Find which expert a flat M-tile index belongs to, for rows grouped by
 // off[0..E] and BM rows per tile: tiles of expert e are
 // [sum_{e'<e} ceil(M_e'/BM), ...).  Executed by every wave of the block (each
@@ -31,8 +44,9 @@ __device__ inline bool find_m_tile(const int32_t* __restrict__ off, int E, int B
       const unsigned long long b = __ballot(hit);
       const int src = __ffsll((long long)b) - 1;
       const int excl = __shfl(inc - cnt, src, 64);
-      e_out = e0 + src;
-      tile_in_e = tile - run - excl;
+      // wave-uniform results: keep them in scalar registers
+      e_out = __builtin_amdgcn_readfirstlane(e0 + src);
+      tile_in_e = __builtin_amdgcn_readfirstlane((int)(tile - run - excl));
       return true;
     }
     run += total;
