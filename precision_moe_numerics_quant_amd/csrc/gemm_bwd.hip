@@ -21,8 +21,7 @@
 // into one of two register sets three slabs ahead, written to LDS one slab
 // ahead (LDS rows unpadded with XOR-swizzled 16-byte chunks: conflict-free
 // slab writes and fragment reads), and its MFMAs overlap the next slab's LDS
-// traffic.  The epilogue stages the float32 tile through LDS so every global
-// store is a 16-byte, row-contiguous write.
+// traffic.
 #include <stdlib.h>
 
 #include "gemm_common.h"
@@ -116,133 +115,125 @@ __device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_
   }
 }
 
-// MODE 0: dgrad (A rows grouped by expert_off, B [E][N][K], C [M_total][N]);
-// MODE 1: wgrad (per expert e: A_e [N1][P_e], B_e [N2][P_e], C = dw[e]).
-template <int MODE, int BM, int BN, int MINB>
-__global__ void __launch_bounds__(bwd::THREADS, MINB) k_gemm_mx(const uint8_t* __restrict__ a_codes,
-                                                                const uint8_t* __restrict__ a_sf,
-                                                                const uint8_t* __restrict__ b_codes,
-                                                                const uint8_t* __restrict__ b_sf,
-                                                                const int32_t* __restrict__ off, int E, int64_t M1,
-                                                                int64_t N, int64_t K, int64_t n_ntiles,
-                                                                int64_t n_mtiles, float* __restrict__ c, float beta) {
-  using namespace bwd;
-  constexpr int WM = BM / 2, MI = WM / 32;  // wave rows, 32-row fragments per wave
-  constexpr int WN = BN / 2, NJ = WN / 32;  // wave cols, 32-col fragments per wave
-  constexpr int A_BYTES = BM * LDS_STRIDE, B_BYTES = BN * LDS_STRIDE;
-  constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * 2;
-  constexpr int BS = WN + 8;  // epilogue band row stride (floats): rows 4 apart land 32 banks apart
-  constexpr int SMEM = STAGE > 4 * 32 * BS * 4 ? STAGE : 4 * 32 * BS * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+// Per-workgroup MFMA machinery shared by the two kernels, as a macro of
+// lambdas over the kernel's locals (fragments, accumulators, LDS pointers):
+// one slab in LDS, the wave's fragments of it in registers.  256 threads as
+// 2 x 2 waves of (BM/2) x (BN/2).  In the 32x32 MFMA layout lane l holds, for
+// value v, row (v/4)*8 + (l/32)*4 + v%4 and column l%32 of the fragment, so
+// each epilogue store instruction writes two full 128-byte row segments
+// (partial-line stores cost far more).
+#define MOE4_MX_CORE(BM, BN)                                                                                      \
+  constexpr int WM = (BM) / 2, MI = WM / 32, WN = (BN) / 2, NJ = WN / 32;                                      \
+  constexpr int A_BYTES = (BM) * bwd::LDS_STRIDE, B_BYTES = (BN) * bwd::LDS_STRIDE;                            \
+  constexpr int STAGE = A_BYTES + B_BYTES + ((BM) + (BN)) * 2;                                                 \
+  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE];                                                 \
+  uint8_t* const la = smem;                                                                                    \
+  uint8_t* const lb = smem + A_BYTES;                                                                          \
+  uint8_t* const las = smem + A_BYTES + B_BYTES;                                                               \
+  uint8_t* const lbs = las + (BM) * 2;                                                                         \
+  const int w = threadIdx.x >> 6, g = (threadIdx.x >> 5) & 1, li = threadIdx.x & 31;                           \
+  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;                                                             \
+  f32x16 acc[MI][NJ];                                                                                          \
+  i32x8 fa[MI], fb[NJ];                                                                                        \
+  int sa[MI], sb[NJ];                                                                                          \
+  auto zero_acc = [&]() {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] =   \
+        f32x16{};                                                                                              \
+  };                                                                                                           \
+  auto stage = [&](const MxSlab<BM>& ra, const MxSlab<BN>& rb) {                                               \
+    store_mx_slab<BM>(ra, la, las);                                                                            \
+    store_mx_slab<BN>(rb, lb, lbs);                                                                            \
+  };                                                                                                           \
+  auto read_frags = [&]() {                                                                                    \
+    uint32_t sa_w[(MI + 3) / 4], sb_w[(NJ + 3) / 4];                                                           \
+    _Pragma("unroll") for (int q = 0; q < (MI + 3) / 4; ++q) sa_w[q] =                                         \
+        *reinterpret_cast<const uint32_t*>(las + (((w >> 1) * 2 + g) * 32 + li) * MI + 4 * q);                \
+    _Pragma("unroll") for (int q = 0; q < (NJ + 3) / 4; ++q) sb_w[q] =                                         \
+        *reinterpret_cast<const uint32_t*>(lbs + (((w & 1) * 2 + g) * 32 + li) * NJ + 4 * q);                 \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                                           \
+      const int r = wm + i * 32 + li;                                                                          \
+      const uint8_t* p = la + r * bwd::LDS_STRIDE;                                                             \
+      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, g));                                     \
+      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, 2 + g));                                 \
+      fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};                                   \
+      sa[i] = (sa_w[i / 4] >> (8 * (i % 4))) & 0xFF;                                                           \
+    }                                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                           \
+      const int r = wn + j * 32 + li;                                                                          \
+      const uint8_t* p = lb + r * bwd::LDS_STRIDE;                                                             \
+      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, g));                                     \
+      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, 2 + g));                                 \
+      fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};                                   \
+      sb[j] = (sb_w[j / 4] >> (8 * (j % 4))) & 0xFF;                                                           \
+    }                                                                                                          \
+  };                                                                                                           \
+  auto mfmas = [&]() {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] =   \
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);   \
+  };                                                                                                           \
+  /* C[row0 + r][n0 + c] (+)= tile; rows >= row_end, columns >= N skipped  */                                  \
+  auto store_tile = [&](float* C, int64_t ldc, int64_t row0, int64_t row_end, int64_t n0, int64_t N,          \
+                        float beta) {                                                                          \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int j = 0; j < NJ; ++j) {            \
+      const int64_t col = n0 + wn + j * 32 + li;                                                               \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                                         \
+        const int64_t row = row0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);                              \
+        if (row < row_end && col < N) {                                                                        \
+          float* p = C + row * ldc + col;                                                                      \
+          float val = acc[i][j][v];                                                                            \
+          if (beta != 0.0f) val = *p + val;                                                                    \
+          __builtin_nontemporal_store(val, p);                                                                 \
+        }                                                                                                      \
+      }                                                                                                        \
+    }                                                                                                          \
+  };                                                                                                           \
+  /* zeros over the same region: each wave writes whole rows of its part,  */                                  \
+  /* 16 bytes per lane                                                      */                                  \
+  auto zero_tile = [&](float* C, int64_t ldc, int64_t row0, int64_t row_end, int64_t n0, int64_t N) {          \
+    constexpr int LPR = WN / 4; /* lanes per row */                                                            \
+    _Pragma("unroll") for (int k = 0; k < WM * LPR / 64; ++k) {                                                \
+      const int idx = k * 64 + (threadIdx.x & 63);                                                             \
+      const int64_t row = row0 + wm + idx / LPR, col = n0 + wn + (idx % LPR) * 4;                              \
+      if (row < row_end && col < N)                                                                            \
+        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(C + row * ldc + col)); \
+    }                                                                                                          \
+  };                                                                                                           \
+  zero_acc()
 
-  const int64_t n_all = MODE == 0 ? n_ntiles * n_mtiles : n_ntiles * n_mtiles * E;
+// dgrad: A [M_total][K] with rows grouped by expert_off, B [E][N][K],
+// C [M_total][N].  One workgroup per tile (XCD-aware order, N tile fastest:
+// every M tile holds up to BM rows of one expert, so tiles carry even work).
+template <int BM, int BN, int MINB>
+__global__ void __launch_bounds__(bwd::THREADS, MINB) k_dgrad_mx(const uint8_t* __restrict__ a_codes,
+                                                                 const uint8_t* __restrict__ a_sf,
+                                                                 const uint8_t* __restrict__ b_codes,
+                                                                 const uint8_t* __restrict__ b_sf,
+                                                                 const int32_t* __restrict__ off, int E,
+                                                                 int64_t M_total, int64_t N, int64_t K,
+                                                                 int64_t n_ntiles, int64_t n_all,
+                                                                 float* __restrict__ c) {
+  using namespace bwd;
   const int64_t tile = xcd_tile(blockIdx.x, n_all);
   if (tile >= n_all) return;
   const int64_t nt = tile % n_ntiles;
-  int64_t row0, row_end, klen, arows, ld;
-  const uint8_t *A, *As, *B, *Bs;
-  float* C;
-  if (MODE == 0) {
-    int e;
-    int64_t mt;
-    if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
-    row0 = (int64_t)off[e] + mt * BM;
-    row_end = (int64_t)off[e + 1] < M1 ? (int64_t)off[e + 1] : M1;  // M1 = M_total here
-    klen = K;
-    ld = K;
-    arows = M1;
-    A = a_codes;
-    As = a_sf;
-    B = b_codes + (int64_t)e * N * K;
-    Bs = b_sf + (int64_t)e * N * (K / 32);
-    C = c;
-  } else {
-    const int64_t rest = tile / n_ntiles;
-    const int e = (int)(rest / n_mtiles);
-    const int64_t mt = rest % n_mtiles;
-    if (e >= E) return;
-    const int64_t p0 = off[e];
-    klen = (int64_t)off[e + 1] - p0;  // padded token count (multiple of 32)
-    row0 = mt * BM;
-    row_end = M1;
-    ld = klen;
-    arows = M1;
-    A = a_codes + M1 * p0;
-    As = a_sf + M1 * p0 / 32;
-    B = b_codes + N * p0;
-    Bs = b_sf + N * p0 / 32;
-    C = c + (int64_t)e * M1 * N;
-    if (klen == 0 && beta != 0.0f) return;  // nothing to add
-  }
+  int e;
+  int64_t mt;
+  if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
+  const int64_t row0 = (int64_t)off[e] + mt * BM;
+  const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
   const int64_t n0 = nt * BN;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
-  const int g = l >> 5, li = l & 31;
-
-  f32x16 acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-
+  MOE4_MX_CORE(BM, BN);
   MxOperand<BM> opa;
   MxOperand<BN> opb;
-  opa.init(A, As, arows, ld, row0, klen);
-  opb.init(B, Bs, N, ld, n0, klen);
+  opa.init(a_codes, a_sf, M_total, K, row0, K);
+  opb.init(b_codes + (int64_t)e * N * K, b_sf + (int64_t)e * N * (K / 32), N, K, n0, K);
   // Slab s is loaded into register set s % 2 three slabs ahead, written to
-  // LDS one slab ahead, and read into the fragment registers (which hold a
-  // whole slab's MFMA operands) right after the previous slab's MFMAs.
+  // LDS one slab ahead, and read into the fragment registers right after the
+  // previous slab's MFMAs.  Past the last slab the loads return zeros and the
+  // LDS traffic is unused, so the body has no branches.
   MxSlab<BM> ra0, ra1;
   MxSlab<BN> rb0, rb1;
-  const int64_t nk = (klen + BK - 1) / BK;
-  uint8_t* la = smem;
-  uint8_t* lb = smem + A_BYTES;
-  uint8_t* las = smem + A_BYTES + B_BYTES;
-  uint8_t* lbs = las + BM * 2;
-  i32x8 fa[MI], fb[NJ];
-  int sa[MI], sb[NJ];
-  auto read_frags = [&]() {
-    uint32_t sa_w[(MI + 3) / 4], sb_w[(NJ + 3) / 4];
-#pragma unroll
-    for (int q = 0; q < (MI + 3) / 4; ++q)
-      sa_w[q] = *reinterpret_cast<const uint32_t*>(las + (((w >> 1) * 2 + g) * 32 + li) * MI + 4 * q);
-#pragma unroll
-    for (int q = 0; q < (NJ + 3) / 4; ++q)
-      sb_w[q] = *reinterpret_cast<const uint32_t*>(lbs + (((w & 1) * 2 + g) * 32 + li) * NJ + 4 * q);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = wm + i * 32 + li;
-      const uint8_t* p = la + r * LDS_STRIDE;
-      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, g));
-      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, 2 + g));
-      fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      sa[i] = (sa_w[i / 4] >> (8 * (i % 4))) & 0xFF;
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = wn + j * 32 + li;
-      const uint8_t* p = lb + r * LDS_STRIDE;
-      i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, g));
-      i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, 2 + g));
-      fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      sb[j] = (sb_w[j / 4] >> (8 * (j % 4))) & 0xFF;
-    }
-  };
-  auto mfmas = [&]() {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
-  };
-  auto stage = [&](const MxSlab<BM>& ra, const MxSlab<BN>& rb) {
-    store_mx_slab<BM>(ra, la, las);
-    store_mx_slab<BN>(rb, lb, lbs);
-  };
-  // One slab: write slab s+1 to LDS, fetch slab s+3, MFMAs of slab s, read
-  // slab s+1.  Past the last slab the loads return zeros and the LDS traffic
-  // is unused, so the body has no branches.
+  const uint32_t nk = (uint32_t)((K + BK - 1) / BK);
   auto step = [&](uint32_t s, MxSlab<BM>& ra_next, MxSlab<BN>& rb_next) {
     __syncthreads();
     stage(ra_next, rb_next);
@@ -254,7 +245,7 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_gemm_mx(const uint8_t* _
     __syncthreads();
     read_frags();
   };
-  if (nk > 0) {
+  if (nk > 0) {  // (always; as a branch it keeps the 256 x 256 variant from spilling)
     opa.load(ra0, 0);
     opb.load(rb0, 0);
     stage(ra0, rb0);
@@ -266,69 +257,192 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_gemm_mx(const uint8_t* _
     read_frags();
   }
   uint32_t it = 0;
-  for (; it + 1 < (uint32_t)nk; it += 2) {
+  for (; it + 1 < nk; it += 2) {
     step(it, ra1, rb1);
     step(it + 1, ra0, rb0);
   }
-  if (it < (uint32_t)nk) step(it, ra1, rb1);
-  // Epilogue: each wave stages 32-row bands of its tile in LDS (row stride
-  // WN + 4 floats) and writes them back as 16-byte row-contiguous stores.
-  float* band = reinterpret_cast<float*>(smem) + w * (32 * BS);
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) band[((v >> 2) * 8 + g * 4 + (v & 3)) * BS + j * 32 + li] = acc[i][j][v];
-    __builtin_amdgcn_wave_barrier();
-    constexpr int QPR = WN / 4;  // column quads per row
-#pragma unroll
-    for (int q = 0; q < 32 * QPR / 64; ++q) {
-      const int idx = q * 64 + l;
-      const int rr = idx / QPR, cq = idx % QPR;
-      const int64_t row = row0 + wm + i * 32 + rr;
-      const int64_t col = n0 + wn + cq * 4;
-      if (row < row_end && col < N) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * BS + cq * 4);
-        f32x4* p = reinterpret_cast<f32x4*>(C + row * N + col);
-        if (MODE == 1 && beta != 0.0f) {
-          f32x4 o = *p;
-          v = f32x4{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
-        }
-        __builtin_nontemporal_store(v, p);
+  if (it < nk) step(it, ra1, rb1);
+  store_tile(c, N, row0, row_end, n0, N, 0.0f);
+}
+
+// wgrad: per expert e, A_e [N1][P_e] and B_e [N2][P_e] (group-major padded
+// transposed MXFP8, contraction over the expert's P_e padded tokens) ->
+// dw[e] [N1][N2].  Persistent: workgroup b walks tiles b, b + grid, ... of
+// the expert-major tile order (consecutive tiles of one expert land on
+// different workgroups, so heavy experts spread over the chip and their
+// operands are read while still cached), and feeds one continuous slab
+// stream across its tiles: the loads of the next tile's first slabs overlap
+// the current tile's last MFMAs and the epilogue stores drain under the
+// next tile's work.  Experts without tokens only get their zero tile
+// (nothing for beta = 1).
+template <int BM, int BN, int MINB>
+__global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* __restrict__ a_codes,
+                                                                 const uint8_t* __restrict__ a_sf,
+                                                                 const uint8_t* __restrict__ b_codes,
+                                                                 const uint8_t* __restrict__ b_sf,
+                                                                 const int32_t* __restrict__ off, int E,
+                                                                 int64_t N1, int64_t N2, int64_t n_ntiles,
+                                                                 int64_t n_all, float* __restrict__ dw,
+                                                                 float beta) {
+  using namespace bwd;
+  const int64_t per_e = n_all / E;  // tiles per expert
+  const int64_t stride = gridDim.x;
+  MOE4_MX_CORE(BM, BN);
+  // the expert offsets, staged in LDS when they fit (the walk reads them per tile)
+  constexpr int OFF_LDS = 2048;
+  __shared__ int32_t s_off[OFF_LDS];
+  if (E < OFF_LDS) {
+    for (int i = threadIdx.x; i <= E; i += THREADS) s_off[i] = off[i];
+    __syncthreads();
+  }
+  const int32_t* offs = E < OFF_LDS ? s_off : off;
+  auto klen_of = [&](int64_t t) {
+    const int e = (int)(t / per_e);
+    return (int64_t)offs[e + 1] - offs[e];
+  };
+  // next tile at or after t (in the workgroup's walk) whose expert has
+  // tokens; tiles of empty experts met on the way get zeros if fill
+  auto next_tile = [&](int64_t t, bool fill) {
+    while (t < n_all && klen_of(t) == 0) {
+      if (fill && beta == 0.0f) {
+        const int e = (int)(t / per_e);
+        const int64_t rest = t % per_e;
+        zero_tile(dw + (int64_t)e * N1 * N2, N2, (rest / n_ntiles) * BM, N1, (rest % n_ntiles) * BN, N2);
       }
+      t += stride;
     }
-    __builtin_amdgcn_wave_barrier();
+    return t;
+  };
+  // load cursor: tile lt, slab ls of lnk
+  MxOperand<BM> opa;
+  MxOperand<BN> opb;
+  int64_t lt = 0;
+  uint32_t ls = 0, lnk = 0;
+  auto set_load_tile = [&](int64_t t) {
+    lt = t;
+    ls = 0;
+    if (t < n_all) {
+      const int e = (int)(t / per_e);
+      const int64_t rest = t % per_e;
+      const int64_t p0 = offs[e], kl = (int64_t)offs[e + 1] - p0;
+      opa.init(a_codes + N1 * p0, a_sf + N1 * p0 / 32, N1, kl, (rest / n_ntiles) * BM, kl);
+      opb.init(b_codes + N2 * p0, b_sf + N2 * p0 / 32, N2, kl, (rest % n_ntiles) * BN, kl);
+      lnk = (uint32_t)((kl + BK - 1) / BK);
+    } else {  // past the walk: zero-range loads
+      opa.klen = 0;
+      opb.klen = 0;
+      lnk = 0xFFFFFFFFu;
+    }
+  };
+  auto load_next = [&](MxSlab<BM>& ra, MxSlab<BN>& rb) {
+    opa.load(ra, ls * BK);
+    opb.load(rb, ls * BK);
+    if (++ls == lnk) set_load_tile(next_tile(lt + stride, false));
+  };
+  // compute cursor: tile ct, slab cs of cnk
+  int64_t ct = next_tile(blockIdx.x, true);
+  if (ct >= n_all) return;
+  uint32_t cs = 0, cnk = (uint32_t)((klen_of(ct) + BK - 1) / BK);
+  set_load_tile(ct);
+  MxSlab<BM> ra0, ra1;
+  MxSlab<BN> rb0, rb1;
+  if (cnk > 0) {  // (always; as a branch it eases register allocation)
+    load_next(ra0, rb0);
+    stage(ra0, rb0);
+    load_next(ra1, rb1);
+    load_next(ra0, rb0);
+    __syncthreads();
+    read_frags();
+  }
+  // one slab: write slab s+1 to LDS, fetch slab s+3, MFMAs of slab s, read
+  // slab s+1; after a tile's last slab, its epilogue
+  auto step = [&](MxSlab<BM>& ra_next, MxSlab<BN>& rb_next) -> bool {
+    __syncthreads();
+    stage(ra_next, rb_next);
+    load_next(ra_next, rb_next);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_frags();
+    if (++cs == cnk) {
+      const int e = (int)(ct / per_e);
+      const int64_t rest = ct % per_e;
+      store_tile(dw + (int64_t)e * N1 * N2, N2, (rest / n_ntiles) * BM, N1, (rest % n_ntiles) * BN, N2, beta);
+      zero_acc();
+      ct = next_tile(ct + stride, true);
+      if (ct >= n_all) return false;
+      cs = 0;
+      cnk = (uint32_t)((klen_of(ct) + BK - 1) / BK);
+    }
+    return true;
+  };
+  while (step(ra1, rb1) && step(ra0, rb0)) {
   }
 }
 
-template <int MODE, int BM, int BN, int MINB>
-static void launch_mx_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, const int32_t* off,
-                        int E, int64_t M1, int64_t N, int64_t K, float* c, float beta, hipStream_t s) {
+static int cu_count() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
+// Tile choice (MOE4_MX_TILE for dgrad / MOE4_MX_TILE_W for wgrad override,
+// for tuning): 0 = 256x256, 1 = 128x128 (2 blocks/CU), 2 = 128x256.  dgrad
+// defaults to 256x256, wgrad to 128x128 (its 256x256 variant spills).
+static int mx_tile_choice(int mode) {
+  static int v[2] = {[] {
+                       const char* e = getenv("MOE4_MX_TILE");
+                       return e ? atoi(e) : 0;
+                     }(),
+                     [] {
+                       const char* e = getenv("MOE4_MX_TILE_W");
+                       return e ? atoi(e) : 1;
+                     }()};
+  return v[mode];
+}
+
+template <int BM, int BN, int MINB>
+static void launch_dgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                           const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   const int64_t n_nt = (N + BN - 1) / BN;
-  const int64_t n_mt = MODE == 0 ? (M1 + BM - 1) / BM + E : (M1 + BM - 1) / BM;
-  const int64_t n_tiles = MODE == 0 ? n_nt * n_mt : n_nt * n_mt * E;
-  hipLaunchKernelGGL((k_gemm_mx<MODE, BM, BN, MINB>), dim3((unsigned)xcd_grid(n_tiles)), dim3(bwd::THREADS), 0, s, ac,
-                     as, bc, bs, off, E, M1, N, K, n_nt, n_mt, c, beta);
+  const int64_t n_all = n_nt * ((M + BM - 1) / BM + E);
+  hipLaunchKernelGGL((k_dgrad_mx<BM, BN, MINB>), dim3((unsigned)xcd_grid(n_all)), dim3(bwd::THREADS), 0, s, ac, as,
+                     bc, bs, off, E, M, N, K, n_nt, n_all, c);
 }
 
-// Configuration choice (MOE4_MX_TILE overrides, for tuning): 0 = 256x256,
-// 1 = 128x128 (2 blocks/CU), 2 = 128x256.
-static int mx_tile_choice() {
-  static int v = [] {
-    const char* e = getenv("MOE4_MX_TILE");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+template <int BM, int BN, int MINB>
+static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                           const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
+  const int64_t n_nt = (N2 + BN - 1) / BN;
+  const int64_t n_all = n_nt * ((N1 + BM - 1) / BM) * E;
+  int64_t grid = (int64_t)cu_count() * MINB;
+  if (grid > n_all) grid = n_all;
+  hipLaunchKernelGGL((k_wgrad_mx<BM, BN, MINB>), dim3((unsigned)grid), dim3(bwd::THREADS), 0, s, ac, as, bc, bs, off,
+                     E, N1, N2, n_nt, n_all, dw, beta);
 }
 
-template <int MODE>
-static void launch_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, const int32_t* off,
-                      int E, int64_t M1, int64_t N, int64_t K, float* c, float beta, hipStream_t s) {
-  switch (mx_tile_choice()) {
-    case 1: launch_mx_t<MODE, 128, 128, 2>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
-    case 2: launch_mx_t<MODE, 128, 256, 1>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
-    default: launch_mx_t<MODE, 256, 256, 1>(ac, as, bc, bs, off, E, M1, N, K, c, beta, s); break;
+static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                         const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
+  switch (mx_tile_choice(0)) {
+    case 1: launch_dgrad_t<128, 128, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 2: launch_dgrad_t<128, 256, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    default: launch_dgrad_t<256, 256, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+  }
+}
+
+static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                         const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
+  switch (mx_tile_choice(1)) {
+    case 1: launch_wgrad_t<128, 128, 2>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
+    case 2: launch_wgrad_t<128, 256, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
+    default: launch_wgrad_t<256, 256, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
   }
 }
 
@@ -348,7 +462,7 @@ extern "C" int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t*
   MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_bwd_dgrad: A and each expert's B must stay below 2 GiB");
   if (M_total == 0) return MOE4_OK;
-  launch_mx<0>(a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c, 0.0f, as_stream(stream));
+  launch_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c, as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_dgrad");
 }
 
@@ -364,7 +478,7 @@ extern "C" int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t*
                "moe_grouped_gemm_bwd_wgrad: misaligned pointer");
   MOE4_REQUIRE(((N2 + 127) / 128) * ((N1 + 127) / 128) * E < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_bwd_wgrad: too large");
-  launch_mx<1>(a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, (int64_t)0, dw, beta, as_stream(stream));
+  launch_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, dw, beta, as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_wgrad");
 }
 

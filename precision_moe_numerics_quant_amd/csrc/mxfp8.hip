@@ -127,59 +127,167 @@ __device__ inline bool tile_coords(const int32_t* off, const int32_t* offp, int 
 }
 
 // ---------------------------------------------------------------- requant-T
-template <bool SR>
-__global__ void __launch_bounds__(MXT) k_requant_T(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
-                                                   const float* __restrict__ ts, int ts_per_group, int64_t C,
-                                                   const int32_t* __restrict__ off, const int32_t* __restrict__ offp,
-                                                   int G, int64_t R, int64_t max_pr, int64_t n_ct, uint32_t base,
-                                                   uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s) {
-  __shared__ __attribute__((aligned(16))) uint8_t lc[TC / 2][TR];  // [byte column][row]
-  __shared__ __attribute__((aligned(16))) uint8_t ls[TC / 16][TR];  // [scale column][row]
-  const int64_t ct = blockIdx.x % n_ct, rt = blockIdx.x / n_ct;
-  TileT t;
-  if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
-  const int64_t c0 = ct * TC;
-  const int tid = threadIdx.x;
-  {  // stage codes: thread -> row tid/8, 8 bytes at byte column (tid%8)*8
-    const int rr = tid >> 3, bc = (tid & 7) * 8;
-    u32x2 w = {0u, 0u};
-    if (rr < t.nvalid && c0 / 2 + bc < C / 2)
-      w = *reinterpret_cast<const u32x2*>(codes + (t.src0 + rr) * (C / 2) + c0 / 2 + bc);
+// Workgroup: 4 waves over 4 consecutive MX blocks (128 padded rows) x 512
+// columns.  Lane l of wave w takes columns c0 + 8l .. c0 + 8l + 7 of block w:
+// one 32-bit code word (8 E2M1 codes) and one E4M3 scale byte per row, so the
+// block amax of each column needs no cross-lane reduction.  The MXFP8 bytes
+// are staged in LDS as [column][128 rows] (16-byte chunks XOR-swizzled by
+// column) and leave as 128-byte column runs, 8 lanes per run.
+namespace rq {
+constexpr int WAVES = 4, THREADS = 64 * WAVES, LCOLS = 8, COLS = 64 * LCOLS, ROWS = 32 * WAVES;
+__device__ inline int swz(int col, int chunk) { return chunk ^ ((col >> 3) & 7); }
+}  // namespace rq
+
+// Exact q * sc of the 8 codes of one row (byte p of cw -> columns 2p, 2p+1);
+// a zero scale gives signed zeros.
+__device__ inline void dequant8(uint32_t cw, uint32_t sbyte, float (&q)[8]) {
+  const float scf = e4m3_to_f32(sbyte);
+  const float m = scf == 0.0f ? 0.0f : mant_factor(scf);
+  f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 0);
+  f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 1);
+  f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 2);
+  f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 3);
+  q[0] = d0[0] * m; q[1] = d0[1] * m; q[2] = d1[0] * m; q[3] = d1[1] * m;
+  q[4] = d2[0] * m; q[5] = d2[1] * m; q[6] = d3[0] * m; q[7] = d3[1] * m;
+}
+
+// SR E4M3 of v into byte sel of old (sel is a constant after unrolling).
+__device__ inline uint32_t sr_fp8_into(uint32_t old, float v, uint32_t r, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, v, r, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, v, r, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, v, r, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, v, r, 1.0f, 3);
+  }
+}
+
+// SR quantisation of one lane's 8 columns x nvalid rows into ob[column][dword]
+// (byte i % 4 of dword i / 4 = row i).  FAST: every element pair index of the
+// block is below 2**32, so the per-pair key is the constant key0.
+template <bool FAST>
+__device__ inline void requant_block(const uint32_t (&cw)[32], const uint32_t (&sb)[32], int nvalid, float S,
+                                     const float (&pc)[8], int64_t j0, int64_t jstride, uint32_t base,
+                                     uint32_t key0, uint32_t (&ob)[8][8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lc[bc + j][rr] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
-    // scales: thread -> row tid/8, scale column tid%8
-    const int scol = tid & 7;
-    uint8_t s = 0;
-    if (rr < t.nvalid && c0 / 16 + scol < C / 16) s = sf[(t.src0 + rr) * (C / 16) + c0 / 16 + scol];
-    ls[scol][rr] = s;
+  for (int i = 0; i < 32; ++i) {
+    if (i < nvalid) {
+      float q[8];
+      dequant8(cw[i], sb[i], q);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int64_t j = j0 + (int64_t)i * jstride + p;
+        const uint32_t key = FAST ? key0 : fmix32(base ^ (uint32_t)((uint64_t)j >> 32));
+        const uint32_t word = fmix32((uint32_t)j ^ key);
+        const float v0 = q[2 * p] * S, v1 = q[2 * p + 1] * S;  // fl(fl(q*sc)*S)
+        ob[2 * p][i / 4] = sr_fp8_into(ob[2 * p][i / 4], v0 * pc[2 * p], word << 16, i % 4);
+        ob[2 * p + 1][i / 4] = sr_fp8_into(ob[2 * p + 1][i / 4], v1 * pc[2 * p + 1], word & 0xFFFF0000u, i % 4);
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ sf,
+                                                           const float* __restrict__ ts, int ts_per_group, int64_t C,
+                                                           const int32_t* __restrict__ off,
+                                                           const int32_t* __restrict__ offp, int G, int64_t R,
+                                                           int64_t max_pr, int64_t n_ct, uint32_t base,
+                                                           uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s) {
+  using namespace rq;
+  __shared__ __attribute__((aligned(16))) uint8_t lq[COLS * ROWS];
+  __shared__ uint8_t lsf[COLS * WAVES];  // [column][block]
+  __shared__ int64_t lblk[WAVES][2];     // block's output offset at column 0, and P (0: no block)
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * COLS;
+  const int64_t pr = ((int64_t)(blockIdx.x / n_ct) * WAVES + w) * 32;
+  const int64_t ptot = offp[G];
+  const bool present = pr < ptot && ptot <= max_pr;
+  int64_t P = 0, pr_in_g = 0, src0 = 0, obase = 0;
+  int nvalid = 0, g = 0;
+  if (present) {
+    g = find_group(offp, G, pr);
+    pr_in_g = pr - offp[g];
+    P = (int64_t)offp[g + 1] - offp[g];
+    src0 = (int64_t)off[g] + pr_in_g;
+    const int64_t gend = (int64_t)off[g + 1] < R ? (int64_t)off[g + 1] : R;
+    const int64_t n = gend - src0;
+    nvalid = n < 0 ? 0 : (n > 32 ? 32 : (int)n);
+    obase = C * (int64_t)offp[g] + pr_in_g;
+  }
+  if (l == 0) {
+    lblk[w][0] = obase;
+    lblk[w][1] = P;
+  }
+  const int64_t c = c0 + LCOLS * l;
+  uint32_t ob[8][8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ob[q][k] = 0u;
+  int ex[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ex[q] = -127;
+  if (nvalid > 0 && c < C) {
+    uint32_t cw[32], sb[32];
+    const uint8_t* crow = codes + src0 * (C / 2) + c / 2;
+    const uint8_t* srow = sf + src0 * (C / 16) + c / 16;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {  // rows past the group repeat its last row and are never used
+      const int64_t ri = i < nvalid ? i : nvalid - 1;
+      cw[i] = *reinterpret_cast<const uint32_t*>(crow + ri * (C / 2));
+      sb[i] = srow[ri * (C / 16)];
+    }
+    const float S = ts[ts_per_group ? g : 0];
+    float am[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am[q] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i < nvalid) {
+        float q8[8];
+        dequant8(cw[i], sb[i], q8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q] * S));
+      }
+    }
+    float pc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ex[q] = mx_exponent(am[q]);
+      pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
+    }
+    const int64_t j0 = src0 * (C / 2) + c / 2;  // pair index of (row src0, column c)
+    const uint32_t key0 = fmix32(base);
+    if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
+      requant_block<true>(cw, sb, nvalid, S, pc, j0, C / 2, base, key0, ob);
+    else
+      requant_block<false>(cw, sb, nvalid, S, pc, j0, C / 2, base, key0, ob);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int col = LCOLS * l + q;
+    *reinterpret_cast<u32x4*>(lq + col * ROWS + swz(col, 2 * w) * 16) = u32x4{ob[q][0], ob[q][1], ob[q][2], ob[q][3]};
+    *reinterpret_cast<u32x4*>(lq + col * ROWS + swz(col, 2 * w + 1) * 16) =
+        u32x4{ob[q][4], ob[q][5], ob[q][6], ob[q][7]};
+    lsf[col * WAVES + w] = (uint8_t)(ex[q] + 127);
   }
   __syncthreads();
-  const int w = tid >> 6, l = tid & 63;
-  if (c0 + 32 * w >= C) return;  // C % 32 == 0: the wave's 32 columns are all in or all out
-  const int cp = l & 15, rseg = l >> 4;
-  const float S = ts[ts_per_group ? t.g : 0];
-  u32x2 cb = *reinterpret_cast<const u32x2*>(&lc[16 * w + cp][rseg * 8]);
-  u32x2 sb = *reinterpret_cast<const u32x2*>(&ls[2 * w + (cp >> 3)][rseg * 8]);
-  float v[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t byte = (cb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    uint32_t sbyte = (sb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    float scf = e4m3_to_f32(sbyte);
-    f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, scf, 0);
-    float m = mant_factor(scf);
-    float q0 = scf == 0.0f ? 0.0f * p[0] : p[0] * m;   // exact q * sc
-    float q1 = scf == 0.0f ? 0.0f * p[1] : p[1] * m;
-    v[i][0] = q0 * S;                                   // fl(fl(q*sc)*S)
-    v[i][1] = q1 * S;
+#pragma unroll 4
+  for (int it = 0; it < COLS * 8 / THREADS; ++it) {
+    const int idx = it * THREADS + tid;
+    const int col = idx >> 3, chunk = idx & 7, b = chunk >> 1;
+    const int64_t Pb = lblk[b][1], gc = c0 + col;
+    if (Pb != 0 && gc < C)
+      *reinterpret_cast<u32x4*>(out_c + lblk[b][0] + gc * Pb + (chunk & 1) * 16) =
+          *reinterpret_cast<const u32x4*>(lq + col * ROWS + swz(col, chunk) * 16);
   }
-  const int64_t c = c0 + 32 * w + 2 * cp;
-  const int64_t orow = t.pr_in_g + rseg * 8;
-  uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
-  uint8_t* o1 = o0 + t.P;
-  uint8_t* s0 = out_s + t.out_base / 32 + c * (t.P / 32) + t.pr_in_g / 32;
-  uint8_t* s1 = s0 + t.P / 32;
-  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o1, s0, s1);
+#pragma unroll
+  for (int it = 0; it < COLS * WAVES / THREADS; ++it) {
+    const int idx = it * THREADS + tid;
+    const int col = idx >> 2, b = idx & 3;
+    const int64_t Pb = lblk[b][1], gc = c0 + col;
+    if (Pb != 0 && gc < C) out_s[lblk[b][0] / 32 + gc * (Pb / 32)] = lsf[col * WAVES + b];
+  }
 }
 
 // ------------------------------------------------------ gradient value loads
@@ -340,10 +448,10 @@ extern "C" int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const
   MOE4_REQUIRE(codes && sf && ts && out_codes && out_sf, MOE4_EINVAL, "mxfp8_requant_sr_T: NULL pointer");
   MOE4_REQUIRE(aligned16(codes) && aligned16(out_codes), MOE4_EALIGN, "mxfp8_requant_sr_T: misaligned pointer");
   if (max_padded_rows == 0) return MOE4_OK;
-  const int64_t n_ct = (cols + TC - 1) / TC, n_rt = max_padded_rows / TR;
+  const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (max_padded_rows + rq::ROWS - 1) / rq::ROWS;
   MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "mxfp8_requant_sr_T: tensor too large");
   const uint32_t base = sr_base_key(seed, stream_id);
-  hipLaunchKernelGGL((k_requant_T<true>), dim3((unsigned)(n_ct * n_rt)), dim3(MXT), 0, as_stream(stream), codes, sf, ts,
+  hipLaunchKernelGGL(k_requant_T, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, as_stream(stream), codes, sf, ts,
                      ts_per_group, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct, base,
                      out_codes, out_sf);
   return check_launch("mxfp8_requant_sr_T");

@@ -162,3 +162,34 @@ def test_grouped_gemm_wgrad_tolerance(beta):
     else:
         assert not got[0].any()                            # empty expert -> zeros
     gemm_tol_check(got, exact, bound, f"wgrad beta={beta}")
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_grouped_gemm_wgrad_many_experts(beta):
+    """More tiles than resident workgroups: each workgroup walks several tiles,
+    including empty experts, one-slab experts and multi-slab experts in a row."""
+    N1, N2, E = 256, 192, 300
+    rng = np.random.default_rng(11)
+    M_list = rng.choice([0, 0, 0, 1, 31, 32, 33, 64, 100, 200, 257], E)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    offp = mx.padded_offsets(off)
+    M = int(off[-1])
+    a = synth.randn((M, N1), 1.0, "cpu", 6, "dh").numpy()
+    b = synth.randn((M, N2), 1e-2, "cpu", 7, "dh").numpy()
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE)
+    bc, bs = mx.quantize_transposed(b, off, mx.RNE)
+    dw0 = np.random.default_rng(8).standard_normal((E, N1, N2)).astype(np.float32)
+    dw = torch.from_numpy(dw0.copy()).cuda()
+    m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
+                                  torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=beta)
+    Al = mx.dequant_transposed(ac, as_, off, N1)
+    Bl = mx.dequant_transposed(bc, bs, off, N2)
+    exact = og.wgrad(Al, Bl)
+    bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
+    got = to_np(dw).astype(np.float64)
+    if beta == 1.0:
+        got = got - dw0.astype(np.float64)
+        bound = bound + np.abs(dw0) * 1e3 * 2.0 ** -24
+    else:
+        assert not got[M_list == 0].any()
+    gemm_tol_check(got, exact, bound, f"wgrad many experts beta={beta}")
