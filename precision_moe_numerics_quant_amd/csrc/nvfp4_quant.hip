@@ -7,7 +7,8 @@
 //
 // Kernels, in launch order:
 //   k_zero_u32      clear the per-group amax words (workspace)
-//   k_amax          per-group max |x| (float bits, atomicMax: order-free)
+//   k_amax          per-group max |x| (float bits, atomicMax: order-free);
+//                   persistent coalesced walk
 //   k_tensor_scale  S_g = fl(amax_g / (m_max * 448)), 1 for a zero group
 //   k_encode        one thread per 16-element block: both candidates, errors
 //                   in the fixed order, the choice, packed codes + scale byte
@@ -58,51 +59,136 @@ __device__ inline void load8(const void* x, int64_t idx, float* v, const float* 
   }
 }
 
-constexpr int AMAX_THREADS = 256;
+// ------------------------------------------------------------ chunk walk
+// Both passes walk the flat row-major tensor in chunks of 1024 elements; each
+// wave of the persistent grid owns a contiguous run of chunks and keeps the
+// next chunk's loads in flight while it works on the current one.  Lane l reads
+// the 16-byte pieces k*64 + l (k < NLD) of its chunk, so every load
+// instruction covers 1 KB contiguously; a piece holds EPL elements and a
+// 16-element block spans LPB = 16 / EPL adjacent lanes.
+template <int DT>
+struct Walk {
+  static constexpr int EPL = DT == MOE4_F32 ? 4 : 8;
+  static constexpr int NLD = 16 / EPL;
+  static constexpr int LPB = 16 / EPL;
+  static constexpr int CHUNK = 1024;
+};
+
+// EPL source values of piece index p (element p * EPL) as float32, SiLU applied.
+template <int DT, bool SILU>
+__device__ inline void load_piece(const void* x, int64_t p, float (&v)[Walk<DT>::EPL], const float* tab) {
+  if (DT == MOE4_F32) {
+    f32x4 a = reinterpret_cast<const f32x4*>(x)[p];
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  } else {
+    u32x4 w = reinterpret_cast<const u32x4*>(x)[p];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+      v[2 * i] = SILU ? act_eval<false>(lo, tab) : bf16_bits_to_f32(lo);
+      v[2 * i + 1] = SILU ? act_eval<false>(hi, tab) : bf16_bits_to_f32(hi);
+    }
+  }
+}
+
+// Group of row r, searching forward from g (rows only grow along a wave's walk).
+__device__ inline int group_from(const int32_t* off, int G, int g, int64_t r) {
+  while (g + 1 < G && (int64_t)off[g + 1] <= r) ++g;
+  return g;
+}
+
+// A wave's walk: the contiguous chunk range [c, c_end) (block distribution,
+// so group boundaries are met rarely), the group gw of the current rows and
+// the row where it ends (cached: the common chunk needs no offset loads).
+struct WaveWalk {
+  int64_t c, c_end;
+  int gw;
+  int64_t g_end;
+  __device__ void init(int64_t n_chunks, int chunk, int64_t cols, const int32_t* goff, int G) {
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / 64);
+    const int64_t per = (n_chunks + n_waves - 1) / n_waves;
+    c = wave * per;
+    c_end = c + per < n_chunks ? c + per : n_chunks;
+    gw = 0;
+    g_end = INT64_MAX;
+    if (goff && c < c_end) {
+      gw = group_of_row(goff, G, c * chunk / cols);
+      g_end = gw + 1 < G ? (int64_t)goff[gw + 1] : INT64_MAX;
+    }
+  }
+  // move gw forward to the group of row r
+  __device__ void advance(const int32_t* goff, int G, int64_t r) {
+    if (r < g_end) return;
+    gw = group_from(goff, G, gw, r);
+    g_end = gw + 1 < G ? (int64_t)goff[gw + 1] : INT64_MAX;
+  }
+};
+
+constexpr int QTHREADS = 256;
 
 template <int DT, bool SILU>
-__global__ void __launch_bounds__(AMAX_THREADS) k_amax(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                       const int32_t* __restrict__ goff, int G,
-                                                       int rows_per_wg, uint32_t* __restrict__ amax_bits,
-                                                       const float* __restrict__ act_tab) {
+__global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                   const int32_t* __restrict__ goff, int G,
+                                                   uint32_t* __restrict__ amax_bits,
+                                                   const float* __restrict__ act_tab) {
+  using W = Walk<DT>;
   __shared__ float tab[SILU ? ACT_TAB : 1];
-  __shared__ float red[AMAX_THREADS / 64];
-  __shared__ int s_g0, s_g1;
-  if (SILU) stage_act_table(tab, act_tab);
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
-  if (r0 >= rows) return;
-  const int64_t r1 = r0 + rows_per_wg < rows ? r0 + rows_per_wg : rows;
-  if (threadIdx.x == 0) {
-    s_g0 = group_of_row(goff, G, r0);
-    s_g1 = group_of_row(goff, G, r1 - 1);
+  if (SILU) {
+    stage_act_table(tab, act_tab);
+    __syncthreads();
   }
-  __syncthreads();
-  const int g0 = s_g0, g1 = s_g1;
-  for (int g = g0; g <= g1; ++g) {
-    int64_t a = r0, b = r1;
-    if (goff) {
-      a = goff[g] > r0 ? goff[g] : r0;
-      b = goff[g + 1] < r1 ? goff[g + 1] : r1;
-    }
-    float m = 0.0f;
-    const int64_t n8 = (b - a) * cols / 8;  // cols % 16 == 0
-    const int64_t base = a * cols;
-    for (int64_t i = threadIdx.x; i < n8; i += AMAX_THREADS) {
-      float v[8];
-      load8<DT, SILU>(x, base + i * 8, v, tab);
+  const int64_t n = rows * cols, n_chunks = (n + W::CHUNK - 1) / W::CHUNK;
+  const int l = threadIdx.x & 63;
+  WaveWalk ww;
+  ww.init(n_chunks, W::CHUNK, cols, goff, G);
+  float m = 0.0f;  // this lane's running maximum of group ww.gw
+  auto load_chunk = [&](int64_t c, float (&v)[W::NLD][W::EPL]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int k = 0; k < W::NLD; ++k) {
+      const int64_t p = c * (W::CHUNK / W::EPL) + k * 64 + l;
+      if (c < ww.c_end && p * W::EPL < n) load_piece<DT, SILU>(x, p, v[k], tab);
+      else
+#pragma unroll
+        for (int i = 0; i < W::EPL; ++i) v[k][i] = 0.0f;
     }
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = red[0];
-      for (int w = 1; w < AMAX_THREADS / 64; ++w) t = fmaxf(t, red[w]);
-      if (b > a) atomicMax(amax_bits + g, __float_as_uint(t));  // t >= 0: bit order = value order
+  };
+  float v[W::NLD][W::EPL], vn[W::NLD][W::EPL];
+  load_chunk(ww.c, v);
+  for (int64_t c = ww.c; c < ww.c_end; ++c) {
+    load_chunk(c + 1, vn);  // next chunk in flight while this one is reduced
+    const int64_t e0 = c * W::CHUNK;
+    const int64_t r_last = ((e0 + W::CHUNK < n ? e0 + W::CHUNK : n) - 1) / cols;
+    if (r_last < ww.g_end) {
+#pragma unroll
+      for (int k = 0; k < W::NLD; ++k)
+#pragma unroll
+        for (int i = 0; i < W::EPL; ++i) m = fmaxf(m, fabsf(v[k][i]));
+    } else {  // the chunk reaches past group gw: per-piece groups, then move on
+#pragma unroll
+      for (int k = 0; k < W::NLD; ++k) {
+        const int64_t e = e0 + (int64_t)(k * 64 + l) * W::EPL;
+        if (e < n) {
+          float t = 0.0f;
+#pragma unroll
+          for (int i = 0; i < W::EPL; ++i) t = fmaxf(t, fabsf(v[k][i]));
+          const int gp = group_from(goff, G, ww.gw, e / cols);
+          if (gp == ww.gw) m = fmaxf(m, t);
+          else atomicMax(amax_bits + gp, __float_as_uint(t));
+        }
+      }
+      const float t = wave_max(m);
+      if (l == 0) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+      m = 0.0f;
+      ww.advance(goff, G, r_last);
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < W::NLD; ++k)
+#pragma unroll
+      for (int i = 0; i < W::EPL; ++i) v[k][i] = vn[k][i];
   }
+  const float t = wave_max(m);
+  if (l == 0 && ww.c < ww.c_end) atomicMax(amax_bits + ww.gw, __float_as_uint(t));  // t >= 0: bit order = value order
 }
 
 __global__ void k_tensor_scale(const uint32_t* __restrict__ amax_bits, int G, float m_max448,
@@ -182,11 +268,13 @@ __global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__
                                                         const int32_t* __restrict__ goff, int G,
                                                         const float* __restrict__ ts,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
-                                                        const float* __restrict__ act_tab) {
+                                                        const float* __restrict__ act_tab, int bpt) {
   __shared__ float tab[SILU ? ACT_TAB : 1];
   if (SILU) stage_act_table(tab, act_tab);
   const int64_t nbr = cols / 16;
-  const int64_t blk = (int64_t)blockIdx.x * ENC_THREADS + threadIdx.x;
+  // bpt blocks per thread (SiLU: amortises the table staging)
+  for (int it = 0; it < bpt; ++it) {
+  const int64_t blk = ((int64_t)blockIdx.x * bpt + it) * ENC_THREADS + threadIdx.x;
   if (blk >= rows * nbr) return;
   const int64_t r = blk / nbr;
   const int g = group_of_row(goff, G, r);
@@ -204,18 +292,43 @@ __global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__
   }
   *reinterpret_cast<u32x2*>(codes + blk * 8) = u32x2{best.q[0], best.q[1]};
   sf[blk] = (uint8_t)best.sc;
+  }
+}
+
+static int cu_count_q() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
+// Persistent grid: enough 1024-element wave chunks, at most 8 workgroups per CU.
+static dim3 walk_grid(int64_t n) {
+  const int64_t waves = (n + 1023) / 1024;
+  int64_t wg = (waves + QTHREADS / 64 - 1) / (QTHREADS / 64);
+  const int64_t cap = (int64_t)cu_count_q() * 8;
+  if (wg > cap) wg = cap;
+  if (wg < 1) wg = 1;
+  return dim3((unsigned)wg);
 }
 
 template <int DT, bool SILU>
 static void launch_encode(bool four6, dim3 grid, hipStream_t s, const void* x, int64_t rows, int64_t cols,
                           const int32_t* goff, int G, const float* ts, uint8_t* codes, uint8_t* sf,
                           const float* tab) {
+  const int bpt = SILU ? 16 : 1;
+  grid.x = (unsigned)((rows * (cols / 16) + (int64_t)ENC_THREADS * bpt - 1) / ((int64_t)ENC_THREADS * bpt));
   if (four6)
     hipLaunchKernelGGL((k_encode<DT, SILU, true>), grid, dim3(ENC_THREADS), 0, s, x, rows, cols, goff, G, ts,
-                       codes, sf, tab);
+                       codes, sf, tab, bpt);
   else
     hipLaunchKernelGGL((k_encode<DT, SILU, false>), grid, dim3(ENC_THREADS), 0, s, x, rows, cols, goff, G, ts,
-                       codes, sf, tab);
+                       codes, sf, tab, bpt);
 }
 
 __global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
@@ -284,16 +397,13 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   const int G = n_groups;
   hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
   if (rows > 0) {
-    // about 8 K elements per workgroup
-    int rpw = (int)((8192 + cols - 1) / cols);
-    if (rpw < 1) rpw = 1;
-    dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+    const dim3 grid = walk_grid(rows * cols);
     if (dtype == MOE4_BF16 && pre_op == MOE4_PRE_SILU)
-      hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
     else if (dtype == MOE4_BF16)
-      hipLaunchKernelGGL((k_amax<MOE4_BF16, false>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
     else
-      hipLaunchKernelGGL((k_amax<MOE4_F32, false>), grid, dim3(AMAX_THREADS), 0, s, x, rows, cols, group_row_off, G, rpw, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_F32, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
   }
   const float m448 = (mode == MOE4_NVFP4_4OVER6) ? 4.0f * 448.0f : 6.0f * 448.0f;
   hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, m448, tensor_scale);

@@ -55,6 +55,32 @@ def test_nvfp4_f32_weights_grouped_mode6():
     assert_bytes_equal(to_np(codes), ref["codes"], "codes")
 
 
+def test_nvfp4_f32_weights_grouped_mode6_many_chunks():
+    """More 1024-element chunks than resident waves: each wave walks several
+    chunks and crosses expert boundaries (per-expert amax and scale)."""
+    E, F, d = 16, 512, 2048
+    w = synth.randn((E, F, d), 0.02, "cpu", 9, "w_up").numpy()
+    w[3] *= 40.0                                   # one expert with a much larger range
+    w[7] = 0.0                                     # one all-zero expert (S = 1)
+    off = np.arange(E + 1) * F
+    codes, sf, ts = m4.nvfp4_quant_46(torch.from_numpy(w).cuda().view(E * F, d), 6, cuda_i32(off))
+    ref = nv.nvfp4_quantize(w.reshape(E * F, d), 6, off)
+    assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+    assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
+def test_nvfp4_bf16_46_many_chunks_ragged_groups():
+    R, C = 8192, 1024
+    off = np.array([0, 100, 100, 4000, 8192])
+    xb = synth.bf16_bits(synth.activations(R, C, "cpu", 3, outlier_p=0.001, outlier_mul=20.0))
+    codes, sf, ts = m4.nvfp4_quant_46(bf16_from_bits(xb), 46, cuda_i32(off))
+    ref = nv.nvfp4_quantize(xb, 46, off)
+    assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+    assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+
+
 def test_nvfp4_ragged_groups_silu():
     # empty groups, single-row groups and a group larger than one workgroup's rows
     R, C = 400, 512
