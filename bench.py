@@ -75,6 +75,91 @@ def work_table(c, off, off_pad):
     }
 
 
+# the library kernel behind each call (several calls may launch one kernel)
+KERNEL_OF = {
+    "F1 W_up quant": "nvfp4 quant (k_amax + k_encode), fp32", "F1 W_down quant": "nvfp4 quant (k_amax + k_encode), fp32",
+    "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
+    "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd", "F8 down GEMM (NVFP4)": "k_gemm_fwd",
+    "F7 SiLU + H quant (NVFP4 4/6)": "nvfp4 quant 4/6 silu", "F9 combine": "k_combine",
+    "B1 dY quant row-wise (MXFP8)": "k_mx_rows", "B1 dY quant transposed (MXFP8)": "k_mx_T",
+    "B2 W_down requant SR-T": "k_requant_T", "B7 W_up requant SR-T": "k_requant_T",
+    "B4 H requant SR-T": "k_requant_T (H)", "B9 X requant SR-T": "k_requant_T (X)",
+    "B3 down dgrad (MXFP8)": "k_dgrad_mx", "B8 up dgrad (MXFP8)": "k_dgrad_mx",
+    "B5 down wgrad (MXFP8)": "k_wgrad_mx", "B10 up wgrad (MXFP8)": "k_wgrad_mx",
+    "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
+    "B11 un-permute sum": "k_combine (unpermute)",
+}
+
+# calls that launch several kernels (zero, amax, scale, encode; route's
+# four): not candidates for the single dominant kernel
+MULTI_KERNEL_CALLS = {"F1 W_up quant", "F1 W_down quant", "F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)",
+                      "F7 SiLU + H quant (NVFP4 4/6)"}
+
+# rocprofv3 --pmc summaries (FETCH_SIZE and WRITE_SIZE passes, scaled by a
+# plain copy of known size) of a kernel, with the hash of its source file:
+# the HBM bytes per launch are reported only while that source is unchanged.
+PMC_PROFILE = {"k_wgrad_mx": ("profiles/k_wgrad_mx_T16384_E384_pmc.md",
+                              "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip")}
+
+
+def source_sha256(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_traffic(kernel):
+    if kernel not in PMC_PROFILE:
+        return None
+    prof, src = PMC_PROFILE[kernel]
+    path = os.path.join(ROOT, prof)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and " = " in line:
+                k, v = line[2:].split(" = ", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != source_sha256(src):
+        return None                      # the kernel changed since the counters were taken
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def pmc_summary(fetch_csv, write_csv, kernel_pat, copy_bytes=1 << 30):
+    """Markdown summary of two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE;
+    KiB per dispatch): the kernel's average per launch, scaled by the factor
+    the same counter shows for the calibration copy (copy_bytes read and
+    written by torch's copy kernel)."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    pick = lambda d, pat: [v for k, vs in d.items() if pat in k for v in vs]
+    kf, kw = pick(fe, kernel_pat), pick(wr, kernel_pat)
+    # the calibration copies are the run's last and largest copy dispatches
+    cf = sorted(pick(fe, "copyBuffer") or pick(fe, "copy_kernel"))[-3:]
+    cw = sorted(pick(wr, "copyBuffer") or pick(wr, "copy_kernel"))[-3:]
+    ref_kib = copy_bytes / 1024.0
+    f_fetch = float(np.median(cf)) / ref_kib
+    f_write = float(np.median(cw)) / ref_kib
+    fetch_b = float(np.mean(kf)) * 1024.0 / f_fetch
+    write_b = float(np.mean(kw)) * 1024.0 / f_write
+    return (f"- kernel = `{kernel_pat}` ({len(kf)} FETCH / {len(kw)} WRITE dispatches)\n"
+            f"- fetch_kib_per_launch = {np.mean(kf):.1f}\n- write_kib_per_launch = {np.mean(kw):.1f}\n"
+            f"- copy_fetch_factor = {f_fetch:.4f}\n- copy_write_factor = {f_write:.4f}\n"
+            f"- hbm_fetch_bytes_per_launch = {fetch_b:.4e}\n- hbm_write_bytes_per_launch = {write_b:.4e}\n"
+            f"- hbm_bytes_per_launch = {fetch_b + write_b:.4e}\n")
+
+
 def gpu_run(steps, warmup):
     import precision_moe_numerics_quant_amd as m4
     from precision_moe_numerics_quant_amd import layer
@@ -129,13 +214,61 @@ def gpu_run(steps, warmup):
     return c, ms_step, wall, per, off, off_pad
 
 
+def quantizer_microbench(reps=20):
+    """16384 x 7168 bf16 (1% of rows x50): NVFP4 4/6 quantisation (one group)
+    and the dequant -> transpose -> MXFP8 SR requantisation of its result.
+    Median of reps runs, each timed with HIP events on the library's stream."""
+    import precision_moe_numerics_quant_amd as m4
+    cfg = synth.CONFIGS[2]
+    R, C = cfg["R"], cfg["C"]
+    x = synth.config_inputs(2, device="cuda")["x"]
+    off = torch.tensor([0, R], dtype=torch.int32, device="cuda")
+    q = m4.nvfp4_quant_46(x, m4.NVFP4_4OVER6)
+    m4.mxfp8_requant_sr_T(q[0], q[1], q[2], off, off, False, synth.SR_SEED, 0)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_q = timed(lambda: m4.nvfp4_quant_46(x, m4.NVFP4_4OVER6))
+    t_r = timed(lambda: m4.mxfp8_requant_sr_T(q[0], q[1], q[2], off, off, False, synth.SR_SEED, 0))
+    n = R * C
+    bytes_q = n * 2 * 2 + n * 9 / 16          # two bf16 reads (amax, encode) + codes and scales
+    bytes_q1 = n * 2 + n * 9 / 16             # one-read basis
+    bytes_r = n * 9 / 16 + n * 33 / 32        # NVFP4 in, MXFP8 out
+    return {"workload": f"bf16 {R}x{C}, 1% of rows x50 (warm caches, median of {reps})",
+            "nvfp4_46_quant": {"ms": round(t_q, 4), "GBps": round(bytes_q / t_q / 1e6, 1),
+                               "frac_hbm": round(bytes_q / t_q / 1e6 / (PEAK_HBM / 1e9), 4),
+                               "GBps_one_read_basis": round(bytes_q1 / t_q / 1e6, 1)},
+            "mxfp8_requant_sr_T": {"ms": round(t_r, 4), "GBps": round(bytes_r / t_r / 1e6, 1),
+                                   "frac_hbm": round(bytes_r / t_r / 1e6 / (PEAK_HBM / 1e9), 4)}}
+
+
+def copy_calibration(n_bytes=1 << 30, reps=3):
+    """A plain device copy of known size (for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings to bytes)."""
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline():
     """The oracle on a bounded sample of the same workload: the expert layer's
-    forward + backward for the first 256 tokens routed top-2 among the first 2
+    forward + backward for the first 512 tokens routed top-2 among the first 2
     experts (d = 4096, F = 1536 full size), timed on this host's cores."""
     from oracle import layer as olayer
     c = synth.CONFIGS[CFG_ID]
-    Ts, Es, ks = 256, 2, 2
+    Ts, Es, ks = 512, 2, 2
     full = synth.layer_inputs(Ts, c["d"], c["F"], Es, ks, device="cpu", seed=0, zipf=c["zipf"])
     x = synth.bf16_bits(full["x"])
     wu, wd = synth.f32_np(full["w_up"]), synth.f32_np(full["w_down"])
@@ -161,7 +294,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-call table to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a 1 GiB device copy (reference kernel for rocprofv3 byte counters)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
+                    help="print the traffic summary of two rocprofv3 --pmc csv files and exit (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary), end="")
+        print(f"- source_sha256 = {source_sha256(PMC_PROFILE['k_wgrad_mx'][1])}")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -195,19 +336,30 @@ def main():
             gemm_flops += amount
             gemm_ms += ms
         calls[name] = entry
-    dom = max(per, key=lambda n: np.mean(per[n]))
-    kind = table[dom][0]
-    ms_dom = float(np.mean(per[dom]))
-    if kind == "hbm":
-        roof = {"bound": "hbm", "achieved": table[dom][1] / (ms_dom * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    # dominant kernel: the one with the largest share of the step (calls that
+    # launch the same kernel are pooled: e.g. both wgrad projections)
+    fam = {}
+    for name in per:
+        if name not in MULTI_KERNEL_CALLS:
+            fam.setdefault(KERNEL_OF[name], []).append(name)
+    dom_k = max(fam, key=lambda k: sum(np.mean(per[n]) for n in fam[k]))
+    names = fam[dom_k]
+    ms_dom = float(np.mean([t for n in names for t in per[n]]))
+    kind = table[names[0]][0]
+    if kind == "hbm" or len(table[names[0]]) > 2:   # wgrad: fp32 dW writes bound it (HBM floor > MFMA floor)
+        work = float(np.mean([table[n][2] if len(table[n]) > 2 else table[n][1] for n in names]))
+        roof = {"bound": "hbm", "achieved": work / (ms_dom * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": table[dom][1] / (ms_dom * 1e-3) / 1e12, "peak": peaks[kind] / 1e12,
+        work = float(np.mean([table[n][1] for n in names]))
+        roof = {"bound": "mfma", "achieved": work / (ms_dom * 1e-3) / 1e12, "peak": peaks[kind] / 1e12,
                 "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["achieved"] = round(roof["achieved"], 2)
-    roof["frac"] = round(roof["frac"], 4)
-    roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["kernel"] = dom_k
+    roof["calls"] = names
+    roof["ms_per_launch"] = round(ms_dom, 4)
+    roof["algorithmic_bytes_per_launch" if roof["bound"] == "hbm" else "algorithmic_flop_per_launch"] = work
+    roof["traffic"] = pmc_traffic(dom_k)
     step_gemm_flops = 6 * 2.0 * c["T"] * c["k"] * c["d"] * c["F"]
     out = {
         "metric": "expert grouped-GEMM TFLOPS (NVFP4 fwd, MXFP8 bwd) + quantizer GB/s, % of peak",
@@ -220,7 +372,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-fwd/mxfp8-bwd (f16 and fp8 MFMA, fp32 accumulate)",
+        "dtype": "f16 mfma (fwd, exact nvfp4 dequant) / fp8 mfma (bwd), fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "moe_expert_layer_fwd_bwd", "tokens": c["T"], "d_model": c["d"], "d_expert": c["F"],
                    "experts": c["E"], "top_k": c["k"], "router_bias": "zipf1.1", "active_experts": int((np.diff(off) > 0).sum()),
@@ -229,7 +381,10 @@ def main():
         "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "breakdown": calls,
         "roofline": roof,
+        "quantizer_microbench": quantizer_microbench(),
     }
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     if args.breakdown:
