@@ -209,7 +209,7 @@ int moe_gather_rows(const uint8_t* codes, const uint8_t* sf, int64_t n_rows_in, 
  * The block-scaled products are exact (operands dequantised exactly to f16),
  * accumulated in float32; the tensor scales are applied in the epilogue.
  * c [M_total, N]: bf16 (c_dtype MOE4_BF16) or float32.  K % 64 == 0,
- * N % 64 == 0.
+ * N % 32 == 0; a_codes, b_codes and c 16-byte aligned (MOE4_EALIGN).
  */
 int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts, int a_ts_per_group,
                          const uint8_t* b_codes, const uint8_t* b_sf, const float* b_ts,
@@ -220,7 +220,8 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const floa
  * moe_grouped_gemm_bwd_dgrad - C[rows of e] = A[rows of e] . B[e]^T with MXFP8
  * A [M_total, K] (+ scales [M_total, K/32]) and MXFP8 B [E, N, K] (+ [E, N,
  * K/32]); float32 C [M_total, N].  Native block-scaled FP8 MFMA (exact
- * products, float32 accumulation).  K % 128 == 0, N % 64 == 0.
+ * products, float32 accumulation).  K % 32 == 0, N % 32 == 0; A and each
+ * expert's B below 2 GiB (32-bit buffer offsets).
  * Pages: agihunt.info page, "Confirmed" (MXFP8 backpropagation).
  */
 int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
@@ -233,7 +234,7 @@ int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
  * dimension: A and B in the group-major padded MXFP8 layout, A_e [N1][P_e],
  * B_e [N2][P_e] with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
  * beta = 0 overwrites (experts with no rows get zeros), beta = 1 accumulates.
- * N1 % 64 == 0, N2 % 64 == 0.
+ * N1 % 32 == 0, N2 % 32 == 0.
  */
 int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
                                const uint8_t* b_codes, const uint8_t* b_sf,
