@@ -40,6 +40,14 @@ __device__ inline int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 constexpr uint32_t OOB = 0x80000000u;  // offset past every operand: loads return 0
 }  // namespace bwd
 
+// Workgroup barrier that the scheduler may not move any instruction across
+// (plain __syncthreads() lets MFMAs, which touch no memory, sink past it).
+__device__ __forceinline__ void pinned_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Buffer descriptor of a wave-uniform range (kept in scalar registers).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
@@ -53,19 +61,22 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes
                                            __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 
-// One operand's slab in registers: ROWS rows x 64 bytes.  Thread t loads the
-// 16-byte chunk t % 4 of rows t / 4 + 64 j, and the 2 scale bytes of row t.
-template <int ROWS>
+// One operand's slab in registers: ROWS rows x 64 bytes, NT threads.  Thread
+// t loads the 16-byte chunk t % 4 of rows t / 4 + (NT / 4) j, and the 2 scale
+// bytes of row t (t < ROWS).
+template <int ROWS, int NT>
 struct MxSlab {
-  u32x4 q[ROWS / 64];
+  static constexpr int NQ = ROWS * 4 / NT;
+  u32x4 q[NQ];
   uint32_t s0, s1;  // scale bytes of K blocks 0 and 1 (combined only when written to LDS)
 };
 
-template <int ROWS>
+template <int ROWS, int NT>
 struct MxOperand {
+  static constexpr int NQ = ROWS * 4 / NT;
   __amdgpu_buffer_rsrc_t codes, scales;
-  uint32_t off[ROWS / 64];  // byte offset of the thread's rows (k excluded)
-  uint32_t soff;            // byte offset of the thread's scale row (t < ROWS)
+  uint32_t off[NQ];  // byte offset of the thread's rows (k excluded)
+  uint32_t soff;     // byte offset of the thread's scale row (t < ROWS)
   uint32_t klen;
 
   __device__ void init(const uint8_t* c, const uint8_t* s, int64_t rows_total, int64_t ld, int64_t row0, int64_t kl) {
@@ -74,8 +85,8 @@ struct MxOperand {
     klen = (uint32_t)kl;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < ROWS / 64; ++j) {
-      const int64_t row = row0 + t / 4 + 64 * j;
+    for (int j = 0; j < NQ; ++j) {
+      const int64_t row = row0 + t / 4 + (NT / 4) * j;
       off[j] = row < rows_total ? (uint32_t)(row * ld + (t % 4) * 16) : bwd::OOB;
     }
     const int64_t row = row0 + t;
@@ -83,11 +94,11 @@ struct MxOperand {
   }
 
   // k0 past the contraction yields zeros (the descriptor's range check).
-  __device__ void load(MxSlab<ROWS>& r, uint32_t k0) const {
+  __device__ void load(MxSlab<ROWS, NT>& r, uint32_t k0) const {
     const int t = threadIdx.x;
     const bool kok = k0 + (t % 4) * 16 < klen;
 #pragma unroll
-    for (int j = 0; j < ROWS / 64; ++j) {
+    for (int j = 0; j < NQ; ++j) {
       const uint32_t o = (kok && off[j] != bwd::OOB) ? off[j] + k0 : bwd::OOB;
       r.q[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(codes, o, 0, 0));
     }
@@ -97,42 +108,54 @@ struct MxOperand {
   }
 };
 
-// Scale bytes go to LDS as [half h][block b][lane row li][fragment f] with
-// row = h * ROWS/2 + 32 f + li, so a lane reads the scales of all its
-// fragments for one K block as a single dword.
-template <int ROWS>
-__device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_t* lds_s) {
-  constexpr int F = ROWS / 64;  // 32-row fragments per half
+// Scale bytes go to LDS as [part h][block b][lane row li][fragment f] with
+// row = h * ROWS/PARTS + 32 f + li (PARTS = waves along this operand's
+// rows), so a lane reads the scales of all its fragments for one K block
+// with one small LDS read.
+template <int ROWS, int NT, int PARTS>
+__device__ inline void store_mx_slab(const MxSlab<ROWS, NT>& r, uint8_t* lds, uint8_t* lds_s) {
+  constexpr int F = ROWS / (32 * PARTS);  // 32-row fragments per part
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < ROWS / 64; ++j)
-    *reinterpret_cast<u32x4*>(lds + (t / 4 + 64 * j) * bwd::LDS_STRIDE + bwd::swz(t / 4 + 64 * j, t % 4) * 16) =
-        r.q[j];
-  if (t < ROWS) {
-    const int h = t / (ROWS / 2), f = (t % (ROWS / 2)) / 32, li = t % 32;
+  for (int j = 0; j < MxSlab<ROWS, NT>::NQ; ++j) {
+    const int row = t / 4 + (NT / 4) * j;
+    *reinterpret_cast<u32x4*>(lds + row * bwd::LDS_STRIDE + bwd::swz(row, t % 4) * 16) = r.q[j];
+  }
+  if (NT <= ROWS || t < ROWS) {  // (no branch when every thread has a row: keeps the step one basic block)
+    const int h = t / (ROWS / PARTS), f = (t % (ROWS / PARTS)) / 32, li = t % 32;
     lds_s[((h * 2 + 0) * 32 + li) * F + f] = (uint8_t)r.s0;
     lds_s[((h * 2 + 1) * 32 + li) * F + f] = (uint8_t)r.s1;
   }
 }
 
+// F scale bytes (one per fragment) from LDS as one integer, byte f = fragment f.
+template <int F>
+__device__ inline uint32_t lds_scale_bytes(const uint8_t* p) {
+  if (F == 4) return *reinterpret_cast<const uint32_t*>(p);
+  if (F == 2) return *reinterpret_cast<const uint16_t*>(p);
+  return *p;
+}
+
 // Per-workgroup MFMA machinery shared by the two kernels, as a macro of
 // lambdas over the kernel's locals (fragments, accumulators, LDS pointers):
-// one slab in LDS, the wave's fragments of it in registers.  256 threads as
-// 2 x 2 waves of (BM/2) x (BN/2).  In the 32x32 MFMA layout lane l holds, for
-// value v, row (v/4)*8 + (l/32)*4 + v%4 and column l%32 of the fragment, so
-// each epilogue store instruction writes two full 128-byte row segments
+// one slab in LDS, the wave's fragments of it in registers.  WVM x WVN waves
+// of (BM/WVM) x (BN/WVN).  In the 32x32 MFMA layout lane l holds, for value
+// v, row (v/4)*8 + (l/32)*4 + v%4 and column l%32 of the fragment, so each
+// epilogue store instruction writes two full 128-byte row segments
 // (partial-line stores cost far more).
-#define MOE4_MX_CORE(BM, BN)                                                                                      \
-  constexpr int WM = (BM) / 2, MI = WM / 32, WN = (BN) / 2, NJ = WN / 32;                                      \
+#define MOE4_MX_CORE(BM, BN, WVM, WVN, NBUF)                                                                      \
+  constexpr int NT = 64 * (WVM) * (WVN);                                                                       \
+  constexpr int WM = (BM) / (WVM), MI = WM / 32, WN = (BN) / (WVN), NJ = WN / 32;                              \
   constexpr int A_BYTES = (BM) * bwd::LDS_STRIDE, B_BYTES = (BN) * bwd::LDS_STRIDE;                            \
   constexpr int STAGE = A_BYTES + B_BYTES + ((BM) + (BN)) * 2;                                                 \
-  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE];                                                 \
+  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE * (NBUF)];                                      \
   uint8_t* const la = smem;                                                                                    \
   uint8_t* const lb = smem + A_BYTES;                                                                          \
   uint8_t* const las = smem + A_BYTES + B_BYTES;                                                               \
   uint8_t* const lbs = las + (BM) * 2;                                                                         \
   const int w = threadIdx.x >> 6, g = (threadIdx.x >> 5) & 1, li = threadIdx.x & 31;                           \
-  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;                                                             \
+  const int wmi = w / (WVN), wni = w % (WVN);                                                                  \
+  const int wm = wmi * WM, wn = wni * WN;                                                                      \
   f32x16 acc[MI][NJ];                                                                                          \
   i32x8 fa[MI], fb[NJ];                                                                                        \
   int sa[MI], sb[NJ];                                                                                          \
@@ -140,23 +163,20 @@ __device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_
     _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] =   \
         f32x16{};                                                                                              \
   };                                                                                                           \
-  auto stage = [&](const MxSlab<BM>& ra, const MxSlab<BN>& rb) {                                               \
-    store_mx_slab<BM>(ra, la, las);                                                                            \
-    store_mx_slab<BN>(rb, lb, lbs);                                                                            \
+  auto stage = [&](const MxSlab<BM, NT>& ra, const MxSlab<BN, NT>& rb) {                                       \
+    store_mx_slab<BM, NT, WVM>(ra, la, las);                                                                   \
+    store_mx_slab<BN, NT, WVN>(rb, lb, lbs);                                                                   \
   };                                                                                                           \
   auto read_frags = [&]() {                                                                                    \
-    uint32_t sa_w[(MI + 3) / 4], sb_w[(NJ + 3) / 4];                                                           \
-    _Pragma("unroll") for (int q = 0; q < (MI + 3) / 4; ++q) sa_w[q] =                                         \
-        *reinterpret_cast<const uint32_t*>(las + (((w >> 1) * 2 + g) * 32 + li) * MI + 4 * q);                \
-    _Pragma("unroll") for (int q = 0; q < (NJ + 3) / 4; ++q) sb_w[q] =                                         \
-        *reinterpret_cast<const uint32_t*>(lbs + (((w & 1) * 2 + g) * 32 + li) * NJ + 4 * q);                 \
+    const uint32_t sa_w = lds_scale_bytes<MI>(las + ((wmi * 2 + g) * 32 + li) * MI);                          \
+    const uint32_t sb_w = lds_scale_bytes<NJ>(lbs + ((wni * 2 + g) * 32 + li) * NJ);                          \
     _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                                           \
       const int r = wm + i * 32 + li;                                                                          \
       const uint8_t* p = la + r * bwd::LDS_STRIDE;                                                             \
       i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, g));                                     \
       i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, 2 + g));                                 \
       fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};                                   \
-      sa[i] = (sa_w[i / 4] >> (8 * (i % 4))) & 0xFF;                                                           \
+      sa[i] = (sa_w >> (8 * i)) & 0xFF;                                                                        \
     }                                                                                                          \
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                                           \
       const int r = wn + j * 32 + li;                                                                          \
@@ -164,7 +184,7 @@ __device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_
       i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, g));                                     \
       i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * bwd::swz(r, 2 + g));                                 \
       fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};                                   \
-      sb[j] = (sb_w[j / 4] >> (8 * (j % 4))) & 0xFF;                                                           \
+      sb[j] = (sb_w >> (8 * j)) & 0xFF;                                                                        \
     }                                                                                                          \
   };                                                                                                           \
   auto mfmas = [&]() {                                                                                         \
@@ -203,15 +223,15 @@ __device__ inline void store_mx_slab(const MxSlab<ROWS>& r, uint8_t* lds, uint8_
 // dgrad: A [M_total][K] with rows grouped by expert_off, B [E][N][K],
 // C [M_total][N].  One workgroup per tile (XCD-aware order, N tile fastest:
 // every M tile holds up to BM rows of one expert, so tiles carry even work).
-template <int BM, int BN, int MINB>
-__global__ void __launch_bounds__(bwd::THREADS, MINB) k_dgrad_mx(const uint8_t* __restrict__ a_codes,
-                                                                 const uint8_t* __restrict__ a_sf,
-                                                                 const uint8_t* __restrict__ b_codes,
-                                                                 const uint8_t* __restrict__ b_sf,
-                                                                 const int32_t* __restrict__ off, int E,
-                                                                 int64_t M_total, int64_t N, int64_t K,
-                                                                 int64_t n_ntiles, int64_t n_all,
-                                                                 float* __restrict__ c) {
+template <int BM, int BN, int WVM, int WVN, int MINB, int DEPTH>
+__global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_dgrad_mx(const uint8_t* __restrict__ a_codes,
+                                                                   const uint8_t* __restrict__ a_sf,
+                                                                   const uint8_t* __restrict__ b_codes,
+                                                                   const uint8_t* __restrict__ b_sf,
+                                                                   const int32_t* __restrict__ off, int E,
+                                                                   int64_t M_total, int64_t N, int64_t K,
+                                                                   int64_t n_ntiles, int64_t n_all,
+                                                                   float* __restrict__ c) {
   using namespace bwd;
   const int64_t tile = xcd_tile(blockIdx.x, n_all);
   if (tile >= n_all) return;
@@ -222,46 +242,153 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_dgrad_mx(const uint8_t* 
   const int64_t row0 = (int64_t)off[e] + mt * BM;
   const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
   const int64_t n0 = nt * BN;
-  MOE4_MX_CORE(BM, BN);
-  MxOperand<BM> opa;
-  MxOperand<BN> opb;
+  MOE4_MX_CORE(BM, BN, WVM, WVN, (DEPTH == 4 ? 2 : 1));
+  MxOperand<BM, NT> opa;
+  MxOperand<BN, NT> opb;
   opa.init(a_codes, a_sf, M_total, K, row0, K);
   opb.init(b_codes + (int64_t)e * N * K, b_sf + (int64_t)e * N * (K / 32), N, K, n0, K);
-  // Slab s is loaded into register set s % 2 three slabs ahead, written to
-  // LDS one slab ahead, and read into the fragment registers right after the
-  // previous slab's MFMAs.  Past the last slab the loads return zeros and the
-  // LDS traffic is unused, so the body has no branches.
-  MxSlab<BM> ra0, ra1;
-  MxSlab<BN> rb0, rb1;
   const uint32_t nk = (uint32_t)((K + BK - 1) / BK);
-  auto step = [&](uint32_t s, MxSlab<BM>& ra_next, MxSlab<BN>& rb_next) {
-    __syncthreads();
-    stage(ra_next, rb_next);
-    opa.load(ra_next, (s + 3) * BK);
-    opb.load(rb_next, (s + 3) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas();
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    read_frags();
-  };
-  if (nk > 0) {  // (always; as a branch it keeps the 256 x 256 variant from spilling)
-    opa.load(ra0, 0);
-    opb.load(rb0, 0);
-    stage(ra0, rb0);
-    opa.load(ra1, BK);
-    opb.load(rb1, BK);
-    opa.load(ra0, 2 * BK);
-    opb.load(rb0, 2 * BK);
-    __syncthreads();
-    read_frags();
+  if (DEPTH == 3) {
+    // Slab s is loaded into register set s % 2 three slabs ahead, written to
+    // LDS one slab ahead, and read into the fragment registers right after
+    // the previous slab's MFMAs.  Past the last slab the loads return zeros
+    // and the LDS traffic is unused, so the body has no branches.
+    MxSlab<BM, NT> ra0, ra1;
+    MxSlab<BN, NT> rb0, rb1;
+    auto step = [&](uint32_t s, MxSlab<BM, NT>& ra_next, MxSlab<BN, NT>& rb_next) {
+      pinned_barrier();
+      stage(ra_next, rb_next);
+      opa.load(ra_next, (s + 3) * BK);
+      opb.load(rb_next, (s + 3) * BK);
+      mfmas();
+      pinned_barrier();
+      read_frags();
+    };
+    if (nk > 0) {  // (always; as a branch it keeps the 256 x 256 variant from spilling)
+      opa.load(ra0, 0);
+      opb.load(rb0, 0);
+      stage(ra0, rb0);
+      opa.load(ra1, BK);
+      opb.load(rb1, BK);
+      opa.load(ra0, 2 * BK);
+      opb.load(rb0, 2 * BK);
+      __syncthreads();
+      read_frags();
+    }
+    uint32_t it = 0;
+    for (; it + 1 < nk; it += 2) {
+      step(it, ra1, rb1);
+      step(it + 1, ra0, rb0);
+    }
+    if (it < nk) step(it, ra1, rb1);
+  } else if (DEPTH == 4) {
+    // Double-buffered LDS, one barrier per slab.  Step s: write slab s + 2
+    // (register set s % 2) into LDS buffer s % 2 (slab s's fragments were
+    // read out at step s - 1), fetch slab s + 4 into that register set, and
+    // run slab s's MFMAs while reading slab s + 1's fragments from buffer
+    // (s + 1) % 2 into the other fragment set.
+    MxSlab<BM, NT> r0a, r1a;
+    MxSlab<BN, NT> r0b, r1b;
+    i32x8 ga[MI], gb[NJ];
+    int tsa[MI], tsb[NJ];
+    auto read_into = [&](int buf, i32x8 (&xa)[MI], i32x8 (&xb)[NJ], int (&ya)[MI], int (&yb)[NJ]) {
+      const uint8_t* pa = la + buf * STAGE;
+      const uint8_t* pb = lb + buf * STAGE;
+      const uint32_t sa_w = lds_scale_bytes<MI>(las + buf * STAGE + ((wmi * 2 + g) * 32 + li) * MI);
+      const uint32_t sb_w = lds_scale_bytes<NJ>(lbs + buf * STAGE + ((wni * 2 + g) * 32 + li) * NJ);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm + i * 32 + li;
+        const uint8_t* q = pa + r * LDS_STRIDE;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(q + 16 * swz(r, g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(q + 16 * swz(r, 2 + g));
+        xa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        ya[i] = (sa_w >> (8 * i)) & 0xFF;
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = wn + j * 32 + li;
+        const uint8_t* q = pb + r * LDS_STRIDE;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(q + 16 * swz(r, g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(q + 16 * swz(r, 2 + g));
+        xb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        yb[j] = (sb_w >> (8 * j)) & 0xFF;
+      }
+    };
+    auto mfma_with = [&](const i32x8 (&xa)[MI], const i32x8 (&xb)[NJ], const int (&ya)[MI], const int (&yb)[NJ]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
+    };
+    auto stage_to = [&](int buf, const MxSlab<BM, NT>& xa, const MxSlab<BN, NT>& xb) {
+      store_mx_slab<BM, NT, WVM>(xa, la + buf * STAGE, las + buf * STAGE);
+      store_mx_slab<BN, NT, WVN>(xb, lb + buf * STAGE, lbs + buf * STAGE);
+    };
+    // one step; CUR = s % 2 (LDS buffer and register set of slab s + 2)
+    auto pstep = [&](uint32_t s, int cur, MxSlab<BM, NT>& xa, MxSlab<BN, NT>& xb, const i32x8 (&fa_c)[MI],
+                     const i32x8 (&fb_c)[NJ], const int (&sa_c)[MI], const int (&sb_c)[NJ], i32x8 (&fa_n)[MI],
+                     i32x8 (&fb_n)[NJ], int (&sa_n)[MI], int (&sb_n)[NJ]) {
+      pinned_barrier();
+      stage_to(cur, xa, xb);
+      opa.load(xa, (s + 4) * BK);
+      opb.load(xb, (s + 4) * BK);
+      mfma_with(fa_c, fb_c, sa_c, sb_c);
+      read_into(cur ^ 1, fa_n, fb_n, sa_n, sb_n);
+#pragma unroll
+      for (int k = 0; k < MI * NJ; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+    };
+    if (nk > 0) {
+      opa.load(r0a, 0);
+      opb.load(r0b, 0);
+      opa.load(r1a, BK);
+      opb.load(r1b, BK);
+      stage_to(0, r0a, r0b);
+      opa.load(r0a, 2 * BK);
+      opb.load(r0b, 2 * BK);
+      stage_to(1, r1a, r1b);
+      opa.load(r1a, 3 * BK);
+      opb.load(r1b, 3 * BK);
+      __syncthreads();
+      read_into(0, fa, fb, sa, sb);
+    }
+    uint32_t it = 0;
+    for (; it + 1 < nk; it += 2) {
+      pstep(it, 0, r0a, r0b, fa, fb, sa, sb, ga, gb, tsa, tsb);
+      pstep(it + 1, 1, r1a, r1b, ga, gb, tsa, tsb, fa, fb, sa, sb);
+    }
+    if (it < nk) pstep(it, 0, r0a, r0b, fa, fb, sa, sb, ga, gb, tsa, tsb);
+  } else {
+    // One register set: slab s + 2 is loaded while slab s + 1 waits in it to
+    // be written to LDS (for layouts with two waves per SIMD, whose second
+    // wave covers the shorter lead).
+    MxSlab<BM, NT> ra;
+    MxSlab<BN, NT> rb;
+    if (nk > 0) {
+      opa.load(ra, 0);
+      opb.load(rb, 0);
+      stage(ra, rb);
+      opa.load(ra, BK);
+      opb.load(rb, BK);
+      __syncthreads();
+      read_frags();
+    }
+    for (uint32_t s = 0; s < nk; ++s) {
+      __syncthreads();
+      stage(ra, rb);
+      opa.load(ra, (s + 2) * BK);
+      opb.load(rb, (s + 2) * BK);
+      mfmas();
+      pinned_barrier();
+      read_frags();
+    }
   }
-  uint32_t it = 0;
-  for (; it + 1 < nk; it += 2) {
-    step(it, ra1, rb1);
-    step(it + 1, ra0, rb0);
-  }
-  if (it < nk) step(it, ra1, rb1);
   store_tile(c, N, row0, row_end, n0, N, 0.0f);
 }
 
@@ -275,8 +402,8 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_dgrad_mx(const uint8_t* 
 // the current tile's last MFMAs and the epilogue stores drain under the
 // next tile's work.  Experts without tokens only get their zero tile
 // (nothing for beta = 1).
-template <int BM, int BN, int MINB>
-__global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* __restrict__ a_codes,
+template <int BM, int BN, int WVM, int WVN, int MINB>
+__global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t* __restrict__ a_codes,
                                                                  const uint8_t* __restrict__ a_sf,
                                                                  const uint8_t* __restrict__ b_codes,
                                                                  const uint8_t* __restrict__ b_sf,
@@ -287,12 +414,12 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* 
   using namespace bwd;
   const int64_t per_e = n_all / E;  // tiles per expert
   const int64_t stride = gridDim.x;
-  MOE4_MX_CORE(BM, BN);
+  MOE4_MX_CORE(BM, BN, WVM, WVN, 1);
   // the expert offsets, staged in LDS when they fit (the walk reads them per tile)
   constexpr int OFF_LDS = 2048;
   __shared__ int32_t s_off[OFF_LDS];
   if (E < OFF_LDS) {
-    for (int i = threadIdx.x; i <= E; i += THREADS) s_off[i] = off[i];
+    for (int i = threadIdx.x; i <= E; i += NT) s_off[i] = off[i];
     __syncthreads();
   }
   const int32_t* offs = E < OFF_LDS ? s_off : off;
@@ -314,8 +441,8 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* 
     return t;
   };
   // load cursor: tile lt, slab ls of lnk
-  MxOperand<BM> opa;
-  MxOperand<BN> opb;
+  MxOperand<BM, NT> opa;
+  MxOperand<BN, NT> opb;
   int64_t lt = 0;
   uint32_t ls = 0, lnk = 0;
   auto set_load_tile = [&](int64_t t) {
@@ -334,7 +461,7 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* 
       lnk = 0xFFFFFFFFu;
     }
   };
-  auto load_next = [&](MxSlab<BM>& ra, MxSlab<BN>& rb) {
+  auto load_next = [&](MxSlab<BM, NT>& ra, MxSlab<BN, NT>& rb) {
     opa.load(ra, ls * BK);
     opb.load(rb, ls * BK);
     if (++ls == lnk) set_load_tile(next_tile(lt + stride, false));
@@ -344,8 +471,8 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* 
   if (ct >= n_all) return;
   uint32_t cs = 0, cnk = (uint32_t)((klen_of(ct) + BK - 1) / BK);
   set_load_tile(ct);
-  MxSlab<BM> ra0, ra1;
-  MxSlab<BN> rb0, rb1;
+  MxSlab<BM, NT> ra0, ra1;
+  MxSlab<BN, NT> rb0, rb1;
   if (cnk > 0) {  // (always; as a branch it eases register allocation)
     load_next(ra0, rb0);
     stage(ra0, rb0);
@@ -356,14 +483,12 @@ __global__ void __launch_bounds__(bwd::THREADS, MINB) k_wgrad_mx(const uint8_t* 
   }
   // one slab: write slab s+1 to LDS, fetch slab s+3, MFMAs of slab s, read
   // slab s+1; after a tile's last slab, its epilogue
-  auto step = [&](MxSlab<BM>& ra_next, MxSlab<BN>& rb_next) -> bool {
-    __syncthreads();
+  auto step = [&](MxSlab<BM, NT>& ra_next, MxSlab<BN, NT>& rb_next) -> bool {
+    pinned_barrier();
     stage(ra_next, rb_next);
     load_next(ra_next, rb_next);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas();
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    pinned_barrier();
     read_frags();
     if (++cs == cnk) {
       const int e = (int)(ct / per_e);
@@ -393,13 +518,10 @@ static int cu_count() {
   return n[dev];
 }
 
-// Tile choice (MOE4_MX_TILE for dgrad / MOE4_MX_TILE_W for wgrad override,
-// for tuning): 0 = 256x256, 1 = 128x128 (2 blocks/CU), 2 = 128x256.  dgrad
-// defaults to 256x256, wgrad to 128x128 (its 256x256 variant spills).
 static int mx_tile_choice(int mode) {
   static int v[2] = {[] {
                        const char* e = getenv("MOE4_MX_TILE");
-                       return e ? atoi(e) : 0;
+                       return e ? atoi(e) : 6;
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
@@ -408,41 +530,53 @@ static int mx_tile_choice(int mode) {
   return v[mode];
 }
 
-template <int BM, int BN, int MINB>
+template <int BM, int BN, int WVM, int WVN, int MINB, int DEPTH = 3>
 static void launch_dgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                            const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   const int64_t n_nt = (N + BN - 1) / BN;
   const int64_t n_all = n_nt * ((M + BM - 1) / BM + E);
-  hipLaunchKernelGGL((k_dgrad_mx<BM, BN, MINB>), dim3((unsigned)xcd_grid(n_all)), dim3(bwd::THREADS), 0, s, ac, as,
-                     bc, bs, off, E, M, N, K, n_nt, n_all, c);
+  hipLaunchKernelGGL((k_dgrad_mx<BM, BN, WVM, WVN, MINB, DEPTH>), dim3((unsigned)xcd_grid(n_all)), dim3(64 * WVM * WVN), 0,
+                     s, ac, as, bc, bs, off, E, M, N, K, n_nt, n_all, c);
 }
 
-template <int BM, int BN, int MINB>
+template <int BM, int BN, int WVM, int WVN, int MINB>
 static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                            const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
   const int64_t n_nt = (N2 + BN - 1) / BN;
   const int64_t n_all = n_nt * ((N1 + BM - 1) / BM) * E;
   int64_t grid = (int64_t)cu_count() * MINB;
   if (grid > n_all) grid = n_all;
-  hipLaunchKernelGGL((k_wgrad_mx<BM, BN, MINB>), dim3((unsigned)grid), dim3(bwd::THREADS), 0, s, ac, as, bc, bs, off,
-                     E, N1, N2, n_nt, n_all, dw, beta);
+  hipLaunchKernelGGL((k_wgrad_mx<BM, BN, WVM, WVN, MINB>), dim3((unsigned)grid), dim3(64 * WVM * WVN), 0, s, ac, as,
+                     bc, bs, off, E, N1, N2, n_nt, n_all, dw, beta);
 }
 
+// Tile configurations (MOE4_MX_TILE for dgrad / MOE4_MX_TILE_W for wgrad
+// override, for tuning): 0 = 256x256 with 2x2 waves, 1 = 128x128 2x2 waves
+// (2 blocks/CU), 2 = 128x256 2x2, 3 = 256x256 with 2x4 waves (two waves per
+// SIMD), 4 = 256x256 with 4x2 waves (3 and 4 with one prefetch register
+// set), 5 = 256x256 2x2 with one register set, 6 = 256x256 2x2 with
+// double-buffered LDS and one barrier per slab (the dgrad default), 7 = as 6
+// with 2x4 waves.
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   switch (mx_tile_choice(0)) {
-    case 1: launch_dgrad_t<128, 128, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 2: launch_dgrad_t<128, 256, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    default: launch_dgrad_t<256, 256, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 1: launch_dgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 2: launch_dgrad_t<128, 256, 2, 2, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 3: launch_dgrad_t<256, 256, 2, 4, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 4: launch_dgrad_t<256, 256, 4, 2, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 5: launch_dgrad_t<256, 256, 2, 2, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 6: launch_dgrad_t<256, 256, 2, 2, 1, 4>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    case 7: launch_dgrad_t<256, 256, 2, 4, 1, 4>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
+    default: launch_dgrad_t<256, 256, 2, 2, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
   }
 }
 
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
   switch (mx_tile_choice(1)) {
-    case 1: launch_wgrad_t<128, 128, 2>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
-    case 2: launch_wgrad_t<128, 256, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
-    default: launch_wgrad_t<256, 256, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
+    case 3: launch_wgrad_t<256, 256, 2, 4, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
+    case 4: launch_wgrad_t<256, 256, 4, 2, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
+    default: launch_wgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
   }
 }
 
