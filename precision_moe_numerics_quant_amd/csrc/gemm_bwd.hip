@@ -392,6 +392,157 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_dgrad_mx(const uint8_t
   store_tile(c, N, row0, row_end, n0, N, 0.0f);
 }
 
+// dgrad with direct-to-LDS loads (K % 128 == 0).  256 x 256 tile, K slabs of
+// 128 bytes (two MFMA steps), two LDS buffers.  Each load instruction of a
+// wave fills 1 KB of LDS (lane i -> bytes 16 i .. 16 i + 15), i.e. 8 rows of
+// 128 bytes: whole cache lines per row.  Rows keep their 16-byte chunks
+// XOR-swizzled by (row >> 1) & 7, so the 16 lanes of a b128 fragment read
+// (16 consecutive rows, one logical chunk) hit 16 distinct 4-bank groups;
+// the swizzle is applied through the global address each lane fetches.  The
+// 4 scale bytes of a row (the slab's 4 K blocks) arrive as one dword.  One
+// barrier per slab: after it the next slab's loads are issued into the other
+// buffer, and they land while this slab's 32 MFMAs per wave run.  Rows past
+// the operands are clamped to the last row (valid memory; their results are
+// never stored), so no load is out of range.
+namespace dmag {
+constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
+constexpr int CODE = 256 * BK;  // bytes per operand per buffer
+constexpr int SC = 256 * 4;     // scale bytes per operand per buffer
+__device__ inline int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+typedef __attribute__((address_space(3))) void* lds_ptr;
+}  // namespace dmag
+
+__global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __restrict__ a_codes,
+                                                          const uint8_t* __restrict__ a_sf,
+                                                          const uint8_t* __restrict__ b_codes,
+                                                          const uint8_t* __restrict__ b_sf,
+                                                          const int32_t* __restrict__ off, int E, int64_t M_total,
+                                                          int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all,
+                                                          float* __restrict__ c) {
+  using namespace dmag;
+  __shared__ __attribute__((aligned(16))) uint8_t la0[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t la1[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t lb1[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[SC];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[SC];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[SC];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[SC];
+  const int64_t tile = xcd_tile(blockIdx.x, n_all);
+  if (tile >= n_all) return;
+  const int64_t nt = tile % n_ntiles;
+  int e;
+  int64_t mt;
+  if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
+  const int64_t row0 = (int64_t)off[e] + mt * BM;
+  const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
+  const int64_t n0 = nt * BN;
+  const int tid = threadIdx.x, l = tid & 63, g = (l >> 5) & 1, li = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar (M0)
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const uint8_t* Bc = b_codes + (int64_t)e * N * K;
+  const uint8_t* Bs = b_sf + (int64_t)e * N * (K / 32);
+  const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * K);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * (K / 32));
+  const __amdgpu_buffer_rsrc_t rbc = make_rsrc(Bc, (uint64_t)N * K);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(Bs, (uint64_t)N * (K / 32));
+  // per-lane source offsets (k excluded): instruction q of wave w fills LDS
+  // rows (4 q + w) * 8 + l / 8, physical chunk l % 8
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (4 * q + w) * 8 + (l >> 3);
+    const int ch = swz(row, l & 7);
+    const int64_t ra = row0 + row < M_total ? row0 + row : M_total - 1;
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    aoff[q] = (uint32_t)(ra * K + 16 * ch);
+    boff[q] = (uint32_t)(rb * K + 16 * ch);
+  }
+  const int64_t sra = row0 + w * 64 + l < M_total ? row0 + w * 64 + l : M_total - 1;
+  const int64_t srb = n0 + w * 64 + l < N ? n0 + w * 64 + l : N - 1;
+  const uint32_t asoff = (uint32_t)(sra * (K / 32)), bsoff = (uint32_t)(srb * (K / 32));
+  auto issue = [&](uint8_t* la, uint8_t* lb, uint8_t* sa, uint8_t* sb, uint32_t k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(la + (4 * q + w) * 1024), 16, aoff[q] + k0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(lb + (4 * q + w) * 1024), 16, boff[q] + k0, 0, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + w * 256), 4, asoff + k0 / 32, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + w * 256), 4, bsoff + k0 / 32, 0, 0, 0);
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fa[4], fb[4];
+      int ya[4], yb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + i * 32 + li;
+        const uint8_t* p = la + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        ya[i] = sa[r * 4 + ks * 2 + g];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn + j * 32 + li;
+        const uint8_t* p = lb + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        yb[j] = sb[r * 4 + ks * 2 + g];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
+    }
+  };
+  // Step s: wait for this wave's loads of slab s and its LDS reads of slab
+  // s - 1, barrier (everyone's slab s has landed, nobody still reads the
+  // other buffer), issue slab s + 1 into the other buffer, compute slab s.
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const uint32_t nk = (uint32_t)(K / BK);
+  issue(la0, lb0, sa0, sb0, 0);
+  uint32_t s = 0;
+  for (; s + 2 <= nk; s += 2) {
+    sync();
+    issue(la1, lb1, sa1, sb1, (s + 1) * BK);
+    compute(la0, lb0, sa0, sb0);
+    sync();
+    if (s + 2 < nk) issue(la0, lb0, sa0, sb0, (s + 2) * BK);
+    compute(la1, lb1, sa1, sb1);
+  }
+  if (s < nk) {
+    sync();
+    compute(la0, lb0, sa0, sb0);
+  }
+  // epilogue: direct stores, two full 128-byte row segments per instruction
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn + j * 32 + li;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < row_end && col < N) __builtin_nontemporal_store(acc[i][j][v], c + row * N + col);
+      }
+    }
+}
+
 // wgrad: per expert e, A_e [N1][P_e] and B_e [N2][P_e] (group-major padded
 // transposed MXFP8, contraction over the expert's P_e padded tokens) ->
 // dw[e] [N1][N2].  Persistent: workgroup b walks tiles b, b + grid, ... of
@@ -506,6 +657,164 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
   }
 }
 
+// wgrad with direct-to-LDS loads: 256 x 256 tiles, K slabs of 128 padded
+// tokens, two LDS buffers, one tile per workgroup in expert-fastest order
+// (tile t -> expert t % E: every expert's tiles spread over all XCDs, which
+// the hardware fills round-robin).  A tile of an expert without tokens
+// writes its zeros (beta = 0) and exits.  K tails (P_e is a multiple of 32)
+// come as zeros from the range check: chunks and scale blocks at or past the
+// expert's token count use an out-of-range offset, and out-of-range direct
+// loads write zeros.  Scale bytes arrive one per lane (as zero-extended
+// dwords: LDS scale layout [block][row] of dwords), since an expert's scale
+// rows need not be 4-byte aligned.
+__global__ void __launch_bounds__(dmag::NT, 1) k_wgrad_dma(const uint8_t* __restrict__ a_codes,
+                                                          const uint8_t* __restrict__ a_sf,
+                                                          const uint8_t* __restrict__ b_codes,
+                                                          const uint8_t* __restrict__ b_sf,
+                                                          const int32_t* __restrict__ off, int E, int64_t N1,
+                                                          int64_t N2, int64_t n_ntiles, float* __restrict__ dw,
+                                                          float beta) {
+  using namespace dmag;
+  constexpr int SCW = 4 * 256 * 4;  // scale dwords per operand per buffer
+  __shared__ __attribute__((aligned(16))) uint8_t la0[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t la1[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t lb1[CODE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[SCW];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[SCW];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[SCW];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[SCW];
+  const int e = (int)(blockIdx.x % E);
+  const int64_t rest = blockIdx.x / E;
+  const int64_t m0 = (rest / n_ntiles) * BM, c0 = (rest % n_ntiles) * BN;
+  const int64_t p0 = off[e];
+  const int64_t kl = (int64_t)off[e + 1] - p0;
+  const int tid = threadIdx.x, l = tid & 63, g = (l >> 5) & 1, li = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  float* C = dw + (int64_t)e * N1 * N2;
+  if (kl == 0) {  // no tokens: zeros for beta = 0, whole 16-byte rows per wave
+    if (beta != 0.0f) return;
+#pragma unroll 4
+    for (int k = 0; k < 128 * 32 / 64; ++k) {
+      const int idx = k * 64 + l;
+      const int64_t row = m0 + wm + idx / 32, col = c0 + wn + (idx % 32) * 4;
+      if (row < N1 && col < N2)
+        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(C + row * N2 + col));
+    }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes + N1 * p0, (uint64_t)N1 * kl);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf + N1 * p0 / 32, (uint64_t)N1 * (kl / 32));
+  const __amdgpu_buffer_rsrc_t rbc = make_rsrc(b_codes + N2 * p0, (uint64_t)N2 * kl);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_sf + N2 * p0 / 32, (uint64_t)N2 * (kl / 32));
+  const uint32_t klen = (uint32_t)kl;
+  uint32_t arow[8], brow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (4 * q + w) * 8 + (l >> 3);
+    const int64_t ra = m0 + row < N1 ? m0 + row : N1 - 1;
+    const int64_t rb = c0 + row < N2 ? c0 + row : N2 - 1;
+    arow[q] = (uint32_t)(ra * kl + 16 * swz(row, l & 7));
+    brow[q] = (uint32_t)(rb * kl + 16 * swz(row, l & 7));
+  }
+  const int64_t sra = m0 + w * 64 + l < N1 ? m0 + w * 64 + l : N1 - 1;
+  const int64_t srb = c0 + w * 64 + l < N2 ? c0 + w * 64 + l : N2 - 1;
+  const uint32_t asrow = (uint32_t)(sra * (kl / 32)), bsrow = (uint32_t)(srb * (kl / 32));
+  auto issue = [&](uint8_t* la, uint8_t* lb, uint8_t* sa, uint8_t* sb, uint32_t k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // the lane's logical chunk (row + l / 8 has the same (row >> 1) & 7
+      // for every q, as 4 q + w steps rows by multiples of 8)
+      const bool ok = k0 + 16 * (uint32_t)swz((4 * q + w) * 8 + (l >> 3), l & 7) < klen;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(la + (4 * q + w) * 1024), 16,
+                                               ok ? arow[q] + k0 : 0x80000000u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(lb + (4 * q + w) * 1024), 16,
+                                               ok ? brow[q] + k0 : 0x80000000u, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool ok = k0 + 32 * b < klen;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + (b * 256 + w * 64) * 4), 1,
+                                               ok ? asrow + k0 / 32 + b : 0x80000000u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + (b * 256 + w * 64) * 4), 1,
+                                               ok ? bsrow + k0 / 32 + b : 0x80000000u, 0, 0, 0);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fa[4], fb[4];
+      int ya[4], yb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + i * 32 + li;
+        const uint8_t* p = la + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        ya[i] = sa[((ks * 2 + g) * 256 + r) * 4];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn + j * 32 + li;
+        const uint8_t* p = lb + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        yb[j] = sb[((ks * 2 + g) * 256 + r) * 4];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
+    }
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const uint32_t nk = (klen + BK - 1) / BK;
+  issue(la0, lb0, sa0, sb0, 0);
+  uint32_t s = 0;
+  for (; s + 2 <= nk; s += 2) {
+    sync();
+    issue(la1, lb1, sa1, sb1, (s + 1) * BK);
+    compute(la0, lb0, sa0, sb0);
+    sync();
+    if (s + 2 < nk) issue(la0, lb0, sa0, sb0, (s + 2) * BK);
+    compute(la1, lb1, sa1, sb1);
+  }
+  if (s < nk) {
+    sync();
+    compute(la0, lb0, sa0, sb0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = c0 + wn + j * 32 + li;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < N1 && col < N2) {
+          float* p = C + row * N2 + col;
+          float val = acc[i][j][v];
+          if (beta != 0.0f) val = *p + val;
+          __builtin_nontemporal_store(val, p);
+        }
+      }
+    }
+}
+
 static int cu_count() {
   static int n[64] = {0};
   int dev = 0;
@@ -521,7 +830,7 @@ static int cu_count() {
 static int mx_tile_choice(int mode) {
   static int v[2] = {[] {
                        const char* e = getenv("MOE4_MX_TILE");
-                       return e ? atoi(e) : 6;
+                       return e ? atoi(e) : 8;
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
@@ -555,11 +864,23 @@ static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 // (2 blocks/CU), 2 = 128x256 2x2, 3 = 256x256 with 2x4 waves (two waves per
 // SIMD), 4 = 256x256 with 4x2 waves (3 and 4 with one prefetch register
 // set), 5 = 256x256 2x2 with one register set, 6 = 256x256 2x2 with
-// double-buffered LDS and one barrier per slab (the dgrad default), 7 = as 6
-// with 2x4 waves.
+// double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves,
+// 8 = direct-to-LDS loads (k_dgrad_dma / k_wgrad_dma; the dgrad default when
+// K % 128 == 0, else 6).  wgrad defaults to the persistent 128x128 kernel:
+// with few experts holding most tokens, one-tile-per-workgroup grids end in
+// a long tail of heavy tiles.
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
-  switch (mx_tile_choice(0)) {
+  int choice = mx_tile_choice(0);
+  if (choice == 8 && K % dmag::BK != 0) choice = 6;
+  if (choice == 8) {
+    const int64_t n_nt = (N + dmag::BN - 1) / dmag::BN;
+    const int64_t n_all = n_nt * ((M + dmag::BM - 1) / dmag::BM + E);
+    hipLaunchKernelGGL(k_dgrad_dma, dim3((unsigned)xcd_grid(n_all)), dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, M, N,
+                       K, n_nt, n_all, c);
+    return;
+  }
+  switch (choice) {
     case 1: launch_dgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
     case 2: launch_dgrad_t<128, 256, 2, 2, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
     case 3: launch_dgrad_t<256, 256, 2, 4, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
@@ -573,6 +894,13 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
 
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
+  if (mx_tile_choice(1) == 8) {
+    const int64_t n_nt = (N2 + dmag::BN - 1) / dmag::BN;
+    const int64_t n_all = n_nt * ((N1 + dmag::BM - 1) / dmag::BM) * E;
+    hipLaunchKernelGGL(k_wgrad_dma, dim3((unsigned)n_all), dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, N1, N2, n_nt,
+                       dw, beta);
+    return;
+  }
   switch (mx_tile_choice(1)) {
     case 3: launch_wgrad_t<256, 256, 2, 4, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
     case 4: launch_wgrad_t<256, 256, 4, 2, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
