@@ -24,6 +24,8 @@
 // traffic.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "moe4_internal.h"
 
@@ -475,13 +477,18 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+  // 32-row fragments of this wave that hold rows of the expert (small
+  // experts leave most of a 256-row tile empty: their MFMAs are skipped)
+  const int64_t left = row_end - (row0 + wm);
+  const int mi_valid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32)));
+  auto compute_n = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb, auto miv) {
+    constexpr int MIV = decltype(miv)::value;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       i32x8 fa[4], fb[4];
       int ya[4], yb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MIV; ++i) {
         const int r = wm + i * 32 + li;
         const uint8_t* p = la + r * BK;
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
@@ -499,11 +506,14 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
         yb[j] = sb[r * 4 + ks * 2 + g];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MIV; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
     }
+  };
+  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+    if (mi_valid > 0) compute_n(la, lb, sa, sb, std::integral_constant<int, 4>{});
   };
   // Step s: wait for this wave's loads of slab s and its LDS reads of slab
   // s - 1, barrier (everyone's slab s has landed, nobody still reads the
