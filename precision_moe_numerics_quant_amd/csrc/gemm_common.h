@@ -54,4 +54,17 @@ __device__ inline bool find_m_tile(const int32_t* __restrict__ off, int E, int B
   return false;
 }
 
+// Buffer descriptor of a wave-uniform range (kept in scalar registers).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  // readfirstlane yields a signed 32-bit int: go through uint32_t so that the
+  // low word is zero-extended (a sign-extended low word would corrupt the base)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t au = ((uint64_t)hi << 32) | (uint64_t)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(au), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
+}
+
 }  // namespace moe4

@@ -205,6 +205,261 @@ __global__ void __launch_bounds__(fwd::THREADS, MINB) k_gemm_fwd(const uint8_t* 
   }
 }
 
+// ------------------------------------------------ direct-to-LDS variant
+// K % 256 == 0.  256 x 256 tile, 4 waves of 128 x 128, K slabs of 256
+// elements: 128 code bytes and 16 scale bytes per row, both fetched straight
+// into LDS (each load instruction of a wave fills 1 KB: 8 whole 128-byte
+// rows of codes, or 64 rows of scales), two LDS buffers, one barrier per
+// slab.  Each wave dequantises its own fragments in registers right before
+// the f16 MFMAs (hardware FP4 -> f16 by the scale's power of two, times the
+// mantissa 1.m: exact), so LDS holds the 4-bit data only.  The slab's 256 K
+// positions are assigned to MFMA steps in an order that both operands share
+// (a dot product does not depend on it): lane half g takes elements
+// 128 g + 8 ks .. 128 g + 8 ks + 7 at step ks, i.e. the contiguous bytes
+// 64 g .. 64 g + 63 of its row over the slab's 16 steps, and the 8 scale bytes
+// 8 g .. 8 g + 7.  Code rows keep their 16-byte chunks XOR-swizzled by
+// (row >> 1) & 7 (applied through the fetched global address) so that 16
+// lanes reading one chunk of 16 consecutive rows hit distinct bank groups.
+namespace fdma {
+constexpr int BKE = 256, RB = BKE / 2, NT = 256;  // RB: code bytes per row and slab
+__device__ inline int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+typedef __attribute__((address_space(3))) void* lds_ptr;
+}  // namespace fdma
+
+// 8 exact f16 values of one k step: code dword (8 E2M1 codes), the E4M3
+// scale as float (its power of two applies in the convert) and its mantissa.
+__device__ inline f16x8 dequant8_f16(uint32_t codes, float scf, f16x2 m2) {
+  f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scf, 0);
+  f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scf, 1);
+  f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scf, 2);
+  f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scf, 3);
+  h0 = h0 * m2;
+  h1 = h1 * m2;
+  h2 = h2 * m2;
+  h3 = h3 * m2;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+template <bool OUT_BF16, int BM, int BN>
+__device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_codes,
+                                                             const uint8_t* __restrict__ a_sf,
+                                                             const float* __restrict__ a_ts, int a_ts_per_group,
+                                                             const uint8_t* __restrict__ b_codes,
+                                                             const uint8_t* __restrict__ b_sf,
+                                                             const float* __restrict__ b_ts,
+                                                             const int32_t* __restrict__ off, int E, int64_t M_total,
+                                                             int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all,
+                                                             void* __restrict__ c) {
+  using namespace fdma;
+  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NJ = WN / 32;
+  constexpr int QA = BM / 32, QB = BN / 32;   // 1 KB code loads per wave and slab
+  constexpr int SA = BM / 64, SB = BN / 64;   // 64-row scale loads per slab (dealt to the waves)
+  __shared__ __attribute__((aligned(16))) uint8_t la0[BM * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[BN * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t la1[BM * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t lb1[BN * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[BM * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[BN * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[BM * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[BN * 16];
+  const int64_t tile = xcd_tile(blockIdx.x, n_all);
+  if (tile >= n_all) return;
+  const int64_t nt = tile % n_ntiles;
+  int e;
+  int64_t mt;
+  if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
+  const int64_t row0 = (int64_t)off[e] + mt * BM;
+  const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
+  const int64_t n0 = nt * BN;
+  const int tid = threadIdx.x, l = tid & 63, g = (l >> 5) & 1, li = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
+  const int64_t KB = K / 2, KS = K / 16;  // code and scale bytes per row
+  const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * KB);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * KS);
+  const __amdgpu_buffer_rsrc_t rbc = make_rsrc(b_codes + (int64_t)e * N * KB, (uint64_t)N * KB);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
+  // Rows past the operands are clamped to the last row (valid memory; their
+  // results are never stored), so every load is in range.
+  uint32_t aoff[QA], boff[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = (4 * q + w) * 8 + (l >> 3);
+    const int64_t ra = row0 + row < M_total ? row0 + row : M_total - 1;
+    aoff[q] = (uint32_t)(ra * KB + 16 * swz(row, l & 7));
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int row = (4 * q + w) * 8 + (l >> 3);
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    boff[q] = (uint32_t)(rb * KB + 16 * swz(row, l & 7));
+  }
+  // scale loads: 64 rows (16 bytes each) per instruction; instruction t of
+  // the SA + SB is issued by wave t % 4
+  uint32_t soff[(SA + SB + 3) / 4];
+#pragma unroll
+  for (int k = 0; k < (SA + SB + 3) / 4; ++k) {
+    const int t = 4 * k + w;
+    int64_t r = 0;
+    if (t < SA) r = row0 + t * 64 + l < M_total ? row0 + t * 64 + l : M_total - 1;
+    else if (t < SA + SB) r = n0 + (t - SA) * 64 + l < N ? n0 + (t - SA) * 64 + l : N - 1;
+    soff[k] = (uint32_t)(r * KS);
+  }
+  auto issue = [&](uint8_t* la, uint8_t* lb, uint8_t* sa, uint8_t* sb, uint32_t ke0) {
+    const uint32_t kb = ke0 / 2;
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(la + (4 * q + w) * 1024), 16, aoff[q] + kb, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(lb + (4 * q + w) * 1024), 16, boff[q] + kb, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < (SA + SB + 3) / 4; ++k) {
+      const int t = 4 * k + w;  // wave-uniform
+      if (t < SA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + t * 1024), 16, soff[k] + ke0 / 16, 0, 0, 0);
+      else if (t < SA + SB)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + (t - SA) * 1024), 16, soff[k] + ke0 / 16, 0, 0, 0);
+    }
+  };
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  // one slab: 4 groups of 4 k steps; per group each fragment's 16 code bytes
+  // (one b128 read) and, per pair of steps, its scale
+  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+    u32x2 sca[MI], scb[NJ];  // the lane's 8 scale bytes per fragment
+#pragma unroll
+    for (int i = 0; i < MI; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) scb[j] = *reinterpret_cast<const u32x2*>(sb + (wn + j * 32 + li) * 16 + 8 * g);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      u32x4 ca[MI], cb[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm + i * 32 + li;
+        ca[i] = *reinterpret_cast<const u32x4*>(la + r * RB + 16 * swz(r, 4 * g + grp));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = wn + j * 32 + li;
+        cb[j] = *reinterpret_cast<const u32x4*>(lb + r * RB + 16 * swz(r, 4 * g + grp));
+      }
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {  // pairs of k steps share a 16-element scale block
+        float sfa[MI], sfb[NJ];
+        f16x2 ma[MI], mb[NJ];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const uint32_t byte = (sca[i][grp >> 1] >> (8 * ((grp & 1) * 2 + hp))) & 0xFFu;
+          sfa[i] = e4m3_to_f32(byte);
+          const _Float16 mh = (_Float16)mant_factor(sfa[i]);
+          ma[i] = f16x2{mh, mh};
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const uint32_t byte = (scb[j][grp >> 1] >> (8 * ((grp & 1) * 2 + hp))) & 0xFFu;
+          sfb[j] = e4m3_to_f32(byte);
+          const _Float16 mh = (_Float16)mant_factor(sfb[j]);
+          mb[j] = f16x2{mh, mh};
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int kq = hp * 2 + st;  // step within the group: code dword kq
+          f16x8 av[MI], bv[NJ];
+#pragma unroll
+          for (int i = 0; i < MI; ++i) av[i] = dequant8_f16(ca[i][kq], sfa[i], ma[i]);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) bv[j] = dequant8_f16(cb[j][kq], sfb[j], mb[j]);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // waves whose rows all lie past a small expert's last row skip their MFMAs
+  const int64_t left = row_end - (row0 + wm);
+  const int active = __builtin_amdgcn_readfirstlane(left > 0 ? 1 : 0);
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const uint32_t nk = (uint32_t)(K / BKE);
+  issue(la0, lb0, sa0, sb0, 0);
+  uint32_t s = 0;
+  for (; s + 2 <= nk; s += 2) {
+    sync();
+    issue(la1, lb1, sa1, sb1, (s + 1) * BKE);
+    if (active) compute(la0, lb0, sa0, sb0);
+    sync();
+    if (s + 2 < nk) issue(la0, lb0, sa0, sb0, (s + 2) * BKE);
+    if (active) compute(la1, lb1, sa1, sb1);
+  }
+  if (s < nk) {
+    sync();
+    if (active) compute(la0, lb0, sa0, sb0);
+  }
+  // Epilogue: 32-row bands of each wave's tile through LDS (free after the
+  // last barrier), scaled by S_a * S_b, written as row-contiguous 16-byte
+  // (f32) or 8-byte (bf16) stores.
+  sync();
+  const float sab = a_ts[a_ts_per_group ? e : 0] * b_ts[e];
+  constexpr int BS = WN + 4;
+  // each wave's 32-row float band in its own freed code buffer
+  float* band = reinterpret_cast<float*>(w == 0 ? la0 : (w == 1 ? lb0 : (w == 2 ? la1 : lb1)));
+  static_assert(32 * BS * 4 <= (BM < BN ? BM : BN) * RB, "epilogue band does not fit a code buffer");
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) band[((v >> 2) * 8 + g * 4 + (v & 3)) * BS + j * 32 + li] = acc[i][j][v] * sab;
+    __builtin_amdgcn_wave_barrier();
+    constexpr int QPR = WN / 4;  // column quads per band row
+#pragma unroll
+    for (int q = 0; q < 32 * QPR / 64; ++q) {
+      const int idx = q * 64 + l;
+      const int rr = idx / QPR, cq = idx % QPR;
+      const int64_t row = row0 + wm + i * 32 + rr;
+      const int64_t col = n0 + wn + cq * 4;
+      if (row < row_end && col < N) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * BS + cq * 4);
+        if (OUT_BF16) {
+          u32x2 o = {f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c) + row * N + col) = o;
+        } else {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(c) + row * N + col));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One kernel per configuration (the body is a device template).
+#define MOE4_FWD_DMA_KERNEL(NAME, OUT_BF16, BM, BN, MINB)                                                          \
+  __global__ void __launch_bounds__(fdma::NT, MINB)                                                               \
+      NAME(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,  \
+           int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,             \
+           const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,    \
+           int64_t K, int64_t n_ntiles, int64_t n_all, void* __restrict__ c) {                                    \
+    gemm_fwd_dma_body<OUT_BF16, BM, BN>(a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, off, E, M_total, \
+                                        N, K, n_ntiles, n_all, c);                                                 \
+  }
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_256, true, 256, 256, 1)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_256, false, 256, 256, 1)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_128, true, 128, 128, 2)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2)
+#undef MOE4_FWD_DMA_KERNEL
+
 template <bool OUT_BF16, int BM, int BN, int MINB>
 static void launch_fwd_t(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
                          const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
@@ -215,12 +470,29 @@ static void launch_fwd_t(hipStream_t s, const uint8_t* ac, const uint8_t* as, co
                      as, ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, c);
 }
 
+template <bool OUT_BF16, int BM, int BN, int MINB>
+static void launch_fwd_dma(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
+                           const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
+                           int64_t N, int64_t K, void* c) {
+  const int64_t n_nt = (N + BN - 1) / BN;
+  const int64_t n_all = n_nt * ((M + BM - 1) / BM + E);
+  const dim3 grid((unsigned)xcd_grid(n_all));
+  if (BM == 256)
+    hipLaunchKernelGGL(OUT_BF16 ? k_gemm_fwd_dma_bf16_256 : k_gemm_fwd_dma_f32_256, grid, dim3(fdma::NT), 0, s, ac, as,
+                       ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, n_all, c);
+  else
+    hipLaunchKernelGGL(OUT_BF16 ? k_gemm_fwd_dma_bf16_128 : k_gemm_fwd_dma_f32_128, grid, dim3(fdma::NT), 0, s, ac, as,
+                       ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, n_all, c);
+}
+
 // Configuration choice (MOE4_FWD_TILE overrides, for tuning): 0 = 128x128
-// (2 blocks/CU), 1 = 256x256, 2 = 128x256.
+// register-staged (2 blocks/CU), 1 = 256x256, 2 = 128x256, 8 = direct-to-LDS
+// 256x256, 9 = direct-to-LDS 128x128 (2 blocks/CU; the default when
+// K % 256 == 0, else 0).
 static int fwd_tile_choice() {
   static int v = [] {
     const char* e = getenv("MOE4_FWD_TILE");
-    return e ? atoi(e) : 0;
+    return e ? atoi(e) : 9;
   }();
   return v;
 }
@@ -229,7 +501,17 @@ template <bool OUT_BF16>
 static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
                        const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
                        int64_t N, int64_t K, void* c) {
-  switch (fwd_tile_choice()) {
+  int choice = fwd_tile_choice();
+  if ((choice == 8 || choice == 9) && K % fdma::BKE != 0) choice = 0;
+  if (choice == 8) {
+    launch_fwd_dma<OUT_BF16, 256, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
+    return;
+  }
+  if (choice == 9) {
+    launch_fwd_dma<OUT_BF16, 128, 128, 2>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
+    return;
+  }
+  switch (choice) {
     case 1: launch_fwd_t<OUT_BF16, 256, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
     case 2: launch_fwd_t<OUT_BF16, 128, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
     default: launch_fwd_t<OUT_BF16, 128, 128, 2>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
