@@ -79,13 +79,14 @@ def work_table(c, off, off_pad):
 KERNEL_OF = {
     "F1 W_up quant": "nvfp4 quant (k_amax + k_encode), fp32", "F1 W_down quant": "nvfp4 quant (k_amax + k_encode), fp32",
     "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
-    "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd", "F8 down GEMM (NVFP4)": "k_gemm_fwd",
+    "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_dma_bf16_128",
+    "F8 down GEMM (NVFP4)": "k_gemm_fwd_dma_f32_128",
     "F7 SiLU + H quant (NVFP4 4/6)": "nvfp4 quant 4/6 silu", "F9 combine": "k_combine",
     "B1 dY quant row-wise (MXFP8)": "k_mx_rows", "B1 dY quant transposed (MXFP8)": "k_mx_T",
     "B2 W_down requant SR-T": "k_requant_T", "B7 W_up requant SR-T": "k_requant_T",
     "B4 H requant SR-T": "k_requant_T (H)", "B9 X requant SR-T": "k_requant_T (X)",
-    "B3 down dgrad (MXFP8)": "k_dgrad_mx", "B8 up dgrad (MXFP8)": "k_dgrad_mx",
-    "B5 down wgrad (MXFP8)": "k_wgrad_mx", "B10 up wgrad (MXFP8)": "k_wgrad_mx",
+    "B3 down dgrad (MXFP8)": "k_dgrad_dma_256", "B8 up dgrad (MXFP8)": "k_dgrad_dma_256",
+    "B5 down wgrad (MXFP8)": "k_wgrad_ws", "B10 up wgrad (MXFP8)": "k_wgrad_ws",
     "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
     "B11 un-permute sum": "k_combine (unpermute)",
 }
@@ -98,7 +99,7 @@ MULTI_KERNEL_CALLS = {"F1 W_up quant", "F1 W_down quant", "F2-F3 route + permuta
 # rocprofv3 --pmc summaries (FETCH_SIZE and WRITE_SIZE passes, scaled by a
 # plain copy of known size) of a kernel, with the hash of its source file:
 # the HBM bytes per launch are reported only while that source is unchanged.
-PMC_PROFILE = {"k_wgrad_mx": ("profiles/k_wgrad_mx_T16384_E384_pmc.md",
+PMC_PROFILE = {"k_wgrad_ws": ("profiles/k_wgrad_ws_T16384_E384_pmc.md",
                               "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip")}
 
 
@@ -301,7 +302,7 @@ def main():
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary), end="")
-        print(f"- source_sha256 = {source_sha256(PMC_PROFILE['k_wgrad_mx'][1])}")
+        print(f"- source_sha256 = {source_sha256(PMC_PROFILE[args.pmc_summary[2]][1])}")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",

@@ -38,7 +38,10 @@
  *         are cut into groups by off[G+1]; group g is stored at code offset
  *         C * off_pad[g] as a row-major block [C][P_g], P_g = pad32(R_g) =
  *         off_pad[g+1] - off_pad[g], padded with zero codes; its scales at
- *         offset C * off_pad[g] / 32 as [C][P_g / 32].  MX blocks run along
+ *         offset C * off_pad[g] / 32, row-major [C][P_g / 32] (MOE4_SF_ROWS)
+ *         or block-major [P_g / 32][C] (MOE4_SF_BLOCKS: per 32-row block, the
+ *         scales of all C columns in order, so the scales of consecutive
+ *         columns for one block are consecutive bytes).  MX blocks run along
  *         the source rows and never straddle a group.
  */
 #ifndef MOE4_H
@@ -70,6 +73,9 @@ extern "C" {
 
 #define MOE4_RNE 0
 #define MOE4_SR 1
+
+#define MOE4_SF_ROWS 0        /* group-major scales [C][P_g/32]                */
+#define MOE4_SF_BLOCKS 1      /* group-major scales [P_g/32][C]                */
 
 /* ------------------------------------------------------------ diagnostics */
 /* Message of the last failing call on this thread ("" if none). */
@@ -127,6 +133,7 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int 
  *              row offsets (device); n_groups >= 1.
  * ts, ts_per_group  tensor scales: one per group, or ts[0] for all rows.
  * seed, stream_id   stochastic-rounding key.
+ * sf_layout    MOE4_SF_ROWS or MOE4_SF_BLOCKS (arrangement of out_sf).
  * out_codes    [cols * off_pad[n_groups]], out_sf [cols * off_pad[n_groups] / 32].
  * MX scale per 32-block: e = least integer with amax <= 448 * 2**e, clamped to
  * [-127, 127] (e = -127 for an all-zero block).  Element i = r * cols + c (r, c
@@ -143,7 +150,7 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int 
 int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
                        int64_t rows, int64_t cols, const int32_t* group_row_off,
                        const int32_t* group_off_pad, int32_t n_groups, int64_t max_padded_rows,
-                       uint64_t seed, uint32_t stream_id,
+                       uint64_t seed, uint32_t stream_id, int sf_layout,
                        uint8_t* out_codes, uint8_t* out_sf, void* stream);
 
 /*
@@ -156,8 +163,9 @@ int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts,
  * silu'.  row_map and dsilu_src are exclusive.  rows = number of output rows.
  * transpose = 0: blocks of 32 along cols, out [rows, cols] + [rows, cols/32].
  * transpose = 1: blocks along rows per group, group-major padded layout
- *                (group_row_off, group_off_pad, n_groups, max_padded_rows as in
- *                mxfp8_requant_sr_T).
+ *                with row-major scales (group_row_off, group_off_pad,
+ *                n_groups, max_padded_rows as in mxfp8_requant_sr_T);
+ * transpose = 2: as 1 with block-major scales (MOE4_SF_BLOCKS).
  * rnd: MOE4_RNE, or MOE4_SR with (seed, stream_id) and the same random words
  *      as mxfp8_requant_sr_T (element index r * cols + c of the [rows, cols]
  *      matrix of values v).  Pages: the MXFP8 backward of the agihunt.info
@@ -231,8 +239,9 @@ int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
 
 /*
  * moe_grouped_gemm_bwd_wgrad - dW[e] = A_e . B_e^T over expert e's padded token
- * dimension: A and B in the group-major padded MXFP8 layout, A_e [N1][P_e],
- * B_e [N2][P_e] with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
+ * dimension: A and B in the group-major padded MXFP8 layout with block-major
+ * scales (MOE4_SF_BLOCKS), A_e [N1][P_e] (scales [P_e/32][N1]), B_e [N2][P_e]
+ * (scales [P_e/32][N2]) with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
  * beta = 0 overwrites (experts with no rows get zeros), beta = 1 accumulates.
  * N1 % 32 == 0, N2 % 32 == 0.
  */

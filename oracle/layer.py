@@ -35,6 +35,10 @@ stochastic rounding, stream id 16 * layer + role, role 0 = X_T, 1 = H_T,
  9. X_T = requant_sr_t(Xq_perm, groups = experts, S_x)       -> [E][d][pad32 M_e]
 10. dW_up[e] = float32(exact dU_col[e] . X_T[e]^T)          [E, F, d]
 11. dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dXp[row(t, j)])
+
+The transposed operands of the weight-gradient products (dYp_col, H_T, dU_col,
+X_T) keep their scales block-major (SF_BLOCKS), the requantised weights
+row-major (SF_ROWS): storage only, the values are the same either way.
 """
 import numpy as np
 
@@ -115,29 +119,29 @@ def backward(fw, dy_bf16, seed=1, layer=0):
     sid = lambda role: 16 * layer + role
     dYp = gated_grad_rows(dy_bf16, fw["gates"], perm, k)
     dy_row_c, dy_row_s = mx.quantize_rowwise(dYp, mx.RNE)
-    dy_col_c, dy_col_s = mx.quantize_transposed(dYp, off, mx.RNE)
+    dy_col_c, dy_col_s = mx.quantize_transposed(dYp, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
     wd = fw["wd"]
     wdT_c, wdT_s = mx.requant_sr_t(wd["codes"], wd["sf"], wd["ts"], np.arange(E + 1) * d,
                                    True, seed, sid(ROLE_WDOWN))
     WdT = np.stack(mx.dequant_transposed(wdT_c, wdT_s, np.arange(E + 1) * d, F))   # [E, F, d]
     dH = gemm.grouped_nt(mx.dequant_rowwise(dy_row_c, dy_row_s), WdT, off).astype(np.float32)
     hq = fw["hq"]
-    hT_c, hT_s = mx.requant_sr_t(hq["codes"], hq["sf"], hq["ts"], off, True, seed, sid(ROLE_H))
-    HT = mx.dequant_transposed(hT_c, hT_s, off, F)
-    dYc = mx.dequant_transposed(dy_col_c, dy_col_s, off, d)
+    hT_c, hT_s = mx.requant_sr_t(hq["codes"], hq["sf"], hq["ts"], off, True, seed, sid(ROLE_H), mx.SF_BLOCKS)
+    HT = mx.dequant_transposed(hT_c, hT_s, off, F, mx.SF_BLOCKS)
+    dYc = mx.dequant_transposed(dy_col_c, dy_col_s, off, d, mx.SF_BLOCKS)
     dW_down = gemm.wgrad(dYc, HT).astype(np.float32)
     dU = (dH * silu.dsilu_f32(fw["U"])).astype(np.float32)
     du_row_c, du_row_s = mx.quantize_rowwise(dU, mx.RNE)
-    du_col_c, du_col_s = mx.quantize_transposed(dU, off, mx.RNE)
+    du_col_c, du_col_s = mx.quantize_transposed(dU, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
     wu = fw["wu"]
     wuT_c, wuT_s = mx.requant_sr_t(wu["codes"], wu["sf"], wu["ts"], np.arange(E + 1) * F,
                                    True, seed, sid(ROLE_WUP))
     WuT = np.stack(mx.dequant_transposed(wuT_c, wuT_s, np.arange(E + 1) * F, d))   # [E, d, F]
     dXp = gemm.grouped_nt(mx.dequant_rowwise(du_row_c, du_row_s), WuT, off).astype(np.float32)
     xp = fw["xq_perm"]
-    xT_c, xT_s = mx.requant_sr_t(xp["codes"], xp["sf"], xp["ts"], off, False, seed, sid(ROLE_X))
-    XT = mx.dequant_transposed(xT_c, xT_s, off, d)
-    dUc = mx.dequant_transposed(du_col_c, du_col_s, off, F)
+    xT_c, xT_s = mx.requant_sr_t(xp["codes"], xp["sf"], xp["ts"], off, False, seed, sid(ROLE_X), mx.SF_BLOCKS)
+    XT = mx.dequant_transposed(xT_c, xT_s, off, d, mx.SF_BLOCKS)
+    dUc = mx.dequant_transposed(du_col_c, du_col_s, off, F, mx.SF_BLOCKS)
     dW_up = gemm.wgrad(dUc, XT).astype(np.float32)
     dx = unpermute_sum(dXp, inv, T, k)
     return dict(dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),

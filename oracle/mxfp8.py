@@ -24,9 +24,14 @@ MX block of 32 values v_i:
 Transposed, grouped layout ("group-major padded"): for a source matrix [R, C]
 whose rows are cut into groups by offsets off[G+1], group g contributes a block
 [C][pad32(R_g)] (rows of the block run along the source rows), padded with
-zeros that do not change amax and encode as 0x00; the scales form
-[C][pad32(R_g)/32].  Blocks of 32 therefore run along the source rows and never
-straddle a group.  The groups are stored one after another in group order.
+zeros that do not change amax and encode as 0x00.  Its scales are stored
+either row-major, [C][pad32(R_g)/32] (SF_ROWS: a row of the block with its
+blocks in order), or block-major, [pad32(R_g)/32][C] (SF_BLOCKS: for each
+32-row block of the group, the scales of all C columns in column order).
+Blocks of 32 run along the source rows and never straddle a group.  The groups
+are stored one after another in group order, the scales of group g starting at
+C * off_pad[g] / 32 in both arrangements.  The arrangement is storage only:
+which scale belongs to which 32 values does not depend on it.
 """
 import numpy as np
 
@@ -37,6 +42,8 @@ from . import srhash
 MX_BLOCK = 32
 RNE = 0
 SR = 1
+SF_ROWS = "rows"
+SF_BLOCKS = "blocks"
 
 
 def mx_scale_exponent(amax):
@@ -118,13 +125,16 @@ def padded_offsets(group_row_off):
     return np.concatenate([[0], np.cumsum(pads)]).astype(np.int64)
 
 
-def quantize_transposed(x32, group_row_off=None, rnd=RNE, seed=0, stream_id=0):
+def quantize_transposed(x32, group_row_off=None, rnd=RNE, seed=0, stream_id=0, sf_layout=SF_ROWS):
     """MXFP8 of x [R, C] with blocks along the rows, group-major padded layout.
 
     Returns codes (1-D, length C * off_pad[G]) and sf (1-D, length
     C * off_pad[G] / 32), group g's block starting at C * off_pad[g] (codes)
-    and C * off_pad[g] / 32 (scales), each block row-major [C][pad32(R_g)].
+    and C * off_pad[g] / 32 (scales); codes row-major [C][pad32(R_g)], scales
+    [C][pad32(R_g)/32] (SF_ROWS) or [pad32(R_g)/32][C] (SF_BLOCKS).
     """
+    if sf_layout not in (SF_ROWS, SF_BLOCKS):
+        raise ValueError("sf_layout must be SF_ROWS or SF_BLOCKS")
     x32 = np.asarray(x32, dtype=np.float32)
     R, C = x32.shape
     off = np.array([0, R], dtype=np.int64) if group_row_off is None else np.asarray(group_row_off, dtype=np.int64)
@@ -146,15 +156,16 @@ def quantize_transposed(x32, group_row_off=None, rnd=RNE, seed=0, stream_id=0):
         c_, s_ = quantize_blocks_rows(blk.reshape(C * nb, MX_BLOCK), rnd, seed, stream_id,
                                       src.reshape(C * nb, MX_BLOCK))
         codes[C * offp[g]: C * offp[g + 1]] = c_.reshape(-1)
-        sf[C * offp[g] // MX_BLOCK: C * offp[g + 1] // MX_BLOCK] = s_.reshape(-1)
+        s_ = s_.reshape(C, nb)
+        sf[C * offp[g] // MX_BLOCK: C * offp[g + 1] // MX_BLOCK] = (s_ if sf_layout == SF_ROWS else s_.T).reshape(-1)
     return codes, sf
 
 
-def requant_sr_t(codes, sf, ts, group_row_off=None, ts_per_group=True, seed=1, stream_id=0):
+def requant_sr_t(codes, sf, ts, group_row_off=None, ts_per_group=True, seed=1, stream_id=0, sf_layout=SF_ROWS):
     """NVFP4 [R, C] -> dequantise (float32) -> transpose -> MXFP8 SR.
 
     ts: tensor scales, one per group if ``ts_per_group`` else one for all rows.
-    Output layout as ``quantize_transposed``.
+    Output layout as ``quantize_transposed`` (``sf_layout`` likewise).
     """
     q = nv.unpack_codes(codes)
     R, C = q.shape
@@ -166,7 +177,7 @@ def requant_sr_t(codes, sf, ts, group_row_off=None, ts_per_group=True, seed=1, s
         ts_rows[off[g]:off[g + 1]] = ts[g] if ts_per_group else ts[0]
     sc = np.repeat(np.asarray(sf, dtype=np.int64), nv.BLOCK, axis=1)
     v = nv.dequant_values(q, sc, ts_rows[:, None])
-    return quantize_transposed(v, off, SR, seed, stream_id)
+    return quantize_transposed(v, off, SR, seed, stream_id, sf_layout)
 
 
 def dequant_rowwise(codes, sf):
@@ -177,7 +188,7 @@ def dequant_rowwise(codes, sf):
     return fmt.e4m3_decode(c) * s
 
 
-def dequant_transposed(codes, sf, group_row_off, C):
+def dequant_transposed(codes, sf, group_row_off, C, sf_layout=SF_ROWS):
     """Exact float64 values of a group-major padded tensor: list of [C, pad32(R_g)]."""
     off = np.asarray(group_row_off, dtype=np.int64)
     offp = padded_offsets(off)
@@ -185,6 +196,7 @@ def dequant_transposed(codes, sf, group_row_off, C):
     for g in range(len(off) - 1):
         P = offp[g + 1] - offp[g]
         c_ = np.asarray(codes[C * offp[g]: C * offp[g + 1]]).reshape(C, P)
-        s_ = np.asarray(sf[C * offp[g] // MX_BLOCK: C * offp[g + 1] // MX_BLOCK]).reshape(C, P // MX_BLOCK)
+        s_ = np.asarray(sf[C * offp[g] // MX_BLOCK: C * offp[g + 1] // MX_BLOCK])
+        s_ = s_.reshape(C, P // MX_BLOCK) if sf_layout == SF_ROWS else s_.reshape(P // MX_BLOCK, C).T
         out.append(fmt.e4m3_decode(c_) * np.repeat(fmt.e8m0_decode(s_), MX_BLOCK, axis=1))
     return out

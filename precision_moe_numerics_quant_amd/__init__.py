@@ -19,6 +19,7 @@ BF16, F32 = 0, 1
 NVFP4_6, NVFP4_4OVER6 = 6, 46
 PRE_NONE, PRE_SILU = 0, 1
 RNE, SR = 0, 1
+SF_ROWS, SF_BLOCKS = 0, 1   # group-major scale arrangement: [C][P_g/32] or [P_g/32][C]
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -38,7 +39,7 @@ _SIGS = {
     "nvfp4_dequant": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _i32, _i64, _i64, _c_void_p,
                              _c_void_p]),
     "mxfp8_requant_sr_T": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i32,
-                                  _i64, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
+                                  _i64, _u64, _u32, _int, _c_void_p, _c_void_p, _c_void_p]),
     "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _c_void_p,
                            _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_route_topk": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -154,8 +155,9 @@ def nvfp4_dequant(codes, sf, ts, group_row_off=None, ts_per_group=False):
 # --------------------------------------------------------------------- MXFP8
 
 def mxfp8_requant_sr_T(codes, sf, ts, group_row_off, group_off_pad, ts_per_group=True, seed=1, stream_id=0,
-                       max_pr=None):
-    """NVFP4 [R, C] -> MXFP8 SR, group-major padded: (codes [C*P], sf [C*P/32]) with P = max_pr."""
+                       max_pr=None, sf_layout=SF_ROWS):
+    """NVFP4 [R, C] -> MXFP8 SR, group-major padded: (codes [C*P], sf [C*P/32]) with P = max_pr;
+    scales row-major per group (SF_ROWS) or block-major (SF_BLOCKS)."""
     R, H = codes.shape
     C = 2 * H
     G = group_row_off.numel() - 1
@@ -166,15 +168,18 @@ def mxfp8_requant_sr_T(codes, sf, ts, group_row_off, group_off_pad, ts_per_group
     oc = _empty((C * max_pr,), torch.uint8, codes)
     os_ = _empty((C * max_pr // 32,), torch.uint8, codes)
     rc = lib().mxfp8_requant_sr_T(_p(codes), _p(sf), _p(ts), int(ts_per_group), R, C, _p(group_row_off),
-                                  _p(group_off_pad), G, max_pr, seed, stream_id, _p(oc), _p(os_), _stream())
+                                  _p(group_off_pad), G, max_pr, seed, stream_id, int(sf_layout), _p(oc), _p(os_),
+                                  _stream())
     _check(rc, "mxfp8_requant_sr_T")
     return oc, os_
 
 
 def mxfp8_quant(x, rows=None, transpose=False, row_map=None, map_div=1, row_scale=None, dsilu_src=None,
-                group_row_off=None, group_off_pad=None, max_pr=None, rnd=RNE, seed=0, stream_id=0):
+                group_row_off=None, group_off_pad=None, max_pr=None, rnd=RNE, seed=0, stream_id=0,
+                sf_layout=SF_ROWS):
     """MXFP8 of a gradient (see moe4.h).  Row mode -> ([rows, C], [rows, C/32]);
-    transposed -> (codes [C*max_pr], sf [C*max_pr/32])."""
+    transposed -> (codes [C*max_pr], sf [C*max_pr/32]), scales per group
+    row-major (SF_ROWS) or block-major (SF_BLOCKS)."""
     dt = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
     if dt is None:
         raise ValueError("mxfp8_quant: x must be bf16 or float32")
@@ -198,7 +203,8 @@ def mxfp8_quant(x, rows=None, transpose=False, row_map=None, map_div=1, row_scal
         max_pr = 0
         oc = _empty((R, C), torch.uint8, x)
         os_ = _empty((R, C // 32), torch.uint8, x)
-    rc = lib().mxfp8_quant(_p(x), dt, R, C, _p(row_map), map_div, _p(row_scale), _p(dsilu_src), int(transpose),
+    mode = 0 if not transpose else (2 if sf_layout == SF_BLOCKS else 1)
+    rc = lib().mxfp8_quant(_p(x), dt, R, C, _p(row_map), map_div, _p(row_scale), _p(dsilu_src), mode,
                            _p(group_row_off), _p(group_off_pad), G, max_pr, rnd, seed, stream_id, _p(oc), _p(os_),
                            _stream())
     _check(rc, "mxfp8_quant")

@@ -53,7 +53,8 @@ __device__ __forceinline__ void pinned_barrier() {
 
 // One operand's slab in registers: ROWS rows x 64 bytes, NT threads.  Thread
 // t loads the 16-byte chunk t % 4 of rows t / 4 + (NT / 4) j, and the 2 scale
-// bytes of row t (t < ROWS).
+// bytes of row t (t < ROWS).  Scales are row-major [rows][ld/32] or, with
+// sf_blocks, block-major [ld/32][rows].
 template <int ROWS, int NT>
 struct MxSlab {
   static constexpr int NQ = ROWS * 4 / NT;
@@ -66,10 +67,12 @@ struct MxOperand {
   static constexpr int NQ = ROWS * 4 / NT;
   __amdgpu_buffer_rsrc_t codes, scales;
   uint32_t off[NQ];  // byte offset of the thread's rows (k excluded)
-  uint32_t soff;     // byte offset of the thread's scale row (t < ROWS)
+  uint32_t soff;     // byte offset of the thread's row's first scale (t < ROWS)
+  uint32_t sbs;      // byte stride between consecutive K blocks of a row's scales
   uint32_t klen;
 
-  __device__ void init(const uint8_t* c, const uint8_t* s, int64_t rows_total, int64_t ld, int64_t row0, int64_t kl) {
+  __device__ void init(const uint8_t* c, const uint8_t* s, int64_t rows_total, int64_t ld, int64_t row0, int64_t kl,
+                       bool sf_blocks = false) {
     codes = make_rsrc(c, (uint64_t)rows_total * ld);
     scales = make_rsrc(s, (uint64_t)rows_total * (ld / 32));
     klen = (uint32_t)kl;
@@ -80,7 +83,8 @@ struct MxOperand {
       off[j] = row < rows_total ? (uint32_t)(row * ld + (t % 4) * 16) : bwd::OOB;
     }
     const int64_t row = row0 + t;
-    soff = (t < ROWS && row < rows_total) ? (uint32_t)(row * (ld / 32)) : bwd::OOB;
+    soff = (t < ROWS && row < rows_total) ? (uint32_t)(sf_blocks ? row : row * (ld / 32)) : bwd::OOB;
+    sbs = sf_blocks ? (uint32_t)rows_total : 1u;
   }
 
   // k0 past the contraction yields zeros (the descriptor's range check).
@@ -92,9 +96,9 @@ struct MxOperand {
       const uint32_t o = (kok && off[j] != bwd::OOB) ? off[j] + k0 : bwd::OOB;
       r.q[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(codes, o, 0, 0));
     }
-    const uint32_t so = (soff == bwd::OOB || k0 >= klen) ? bwd::OOB : soff + k0 / 32;
+    const uint32_t so = (soff == bwd::OOB || k0 >= klen) ? bwd::OOB : soff + (k0 / 32) * sbs;
     r.s0 = __builtin_amdgcn_raw_buffer_load_b8(scales, so, 0, 0);
-    r.s1 = __builtin_amdgcn_raw_buffer_load_b8(scales, (k0 + 32 < klen && so != bwd::OOB) ? so + 1u : bwd::OOB, 0, 0);
+    r.s1 = __builtin_amdgcn_raw_buffer_load_b8(scales, (k0 + 32 < klen && so != bwd::OOB) ? so + sbs : bwd::OOB, 0, 0);
   }
 };
 
@@ -395,14 +399,14 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_dgrad_mx(const uint8_t
 // the operands are clamped to the last row (valid memory; their results are
 // never stored), so no load is out of range.
 namespace dmag {
-constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
-constexpr int CODE = 256 * BK;  // bytes per operand per buffer
-constexpr int SC = 256 * 4;     // scale bytes per operand per buffer
+constexpr int BM = 256, BN = 256, BK = 128, NT = 256;  // (BM, BN: the wgrad variant's tile)
+constexpr int CODE = 256 * BK;  // bytes per operand per buffer (256-row tiles)
 __device__ inline int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 }  // namespace dmag
 
-__global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __restrict__ a_codes,
+template <int TM, int TN>
+__device__ __forceinline__ void dgrad_dma_body(const uint8_t* __restrict__ a_codes,
                                                           const uint8_t* __restrict__ a_sf,
                                                           const uint8_t* __restrict__ b_codes,
                                                           const uint8_t* __restrict__ b_sf,
@@ -410,26 +414,29 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
                                                           int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all,
                                                           float* __restrict__ c) {
   using namespace dmag;
-  __shared__ __attribute__((aligned(16))) uint8_t la0[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t lb0[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t la1[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t lb1[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[SC];
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[SC];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[SC];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[SC];
+  constexpr int WM = TM / 2, WN = TN / 2, MI = WM / 32, NJ = WN / 32;
+  constexpr int QA = TM / 32, QB = TN / 32;  // 1 KB code loads per wave and slab
+  constexpr int SA = TM / 64, SB = TN / 64;  // 64-row scale loads per slab (dealt to the waves)
+  __shared__ __attribute__((aligned(16))) uint8_t la0[TM * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t lb0[TN * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t la1[TM * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t lb1[TN * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[TM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[TN * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[TM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[TN * 4];
   const int64_t tile = xcd_tile(blockIdx.x, n_all);
   if (tile >= n_all) return;
   const int64_t nt = tile % n_ntiles;
   int e;
   int64_t mt;
-  if (!find_m_tile(off, E, BM, tile / n_ntiles, e, mt)) return;
-  const int64_t row0 = (int64_t)off[e] + mt * BM;
+  if (!find_m_tile(off, E, TM, tile / n_ntiles, e, mt)) return;
+  const int64_t row0 = (int64_t)off[e] + mt * TM;
   const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
-  const int64_t n0 = nt * BN;
+  const int64_t n0 = nt * TN;
   const int tid = threadIdx.x, l = tid & 63, g = (l >> 5) & 1, li = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar (M0)
-  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
   const uint8_t* Bc = b_codes + (int64_t)e * N * K;
   const uint8_t* Bs = b_sf + (int64_t)e * N * (K / 32);
   const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * K);
@@ -438,45 +445,62 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
   const __amdgpu_buffer_rsrc_t rbs = make_rsrc(Bs, (uint64_t)N * (K / 32));
   // per-lane source offsets (k excluded): instruction q of wave w fills LDS
   // rows (4 q + w) * 8 + l / 8, physical chunk l % 8
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[QA], boff[QB];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < QA; ++q) {
     const int row = (4 * q + w) * 8 + (l >> 3);
-    const int ch = swz(row, l & 7);
     const int64_t ra = row0 + row < M_total ? row0 + row : M_total - 1;
-    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-    aoff[q] = (uint32_t)(ra * K + 16 * ch);
-    boff[q] = (uint32_t)(rb * K + 16 * ch);
+    aoff[q] = (uint32_t)(ra * K + 16 * swz(row, l & 7));
   }
-  const int64_t sra = row0 + w * 64 + l < M_total ? row0 + w * 64 + l : M_total - 1;
-  const int64_t srb = n0 + w * 64 + l < N ? n0 + w * 64 + l : N - 1;
-  const uint32_t asoff = (uint32_t)(sra * (K / 32)), bsoff = (uint32_t)(srb * (K / 32));
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int row = (4 * q + w) * 8 + (l >> 3);
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    boff[q] = (uint32_t)(rb * K + 16 * swz(row, l & 7));
+  }
+  // scale loads: 64 rows (one dword = the slab's 4 blocks each) per
+  // instruction; instruction t of the SA + SB is issued by wave t % 4
+  uint32_t soff[(SA + SB + 3) / 4];
+#pragma unroll
+  for (int k = 0; k < (SA + SB + 3) / 4; ++k) {
+    const int t = 4 * k + w;
+    int64_t r = 0;
+    if (t < SA) r = row0 + t * 64 + l < M_total ? row0 + t * 64 + l : M_total - 1;
+    else if (t < SA + SB) r = n0 + (t - SA) * 64 + l < N ? n0 + (t - SA) * 64 + l : N - 1;
+    soff[k] = (uint32_t)(r * (K / 32));
+  }
   auto issue = [&](uint8_t* la, uint8_t* lb, uint8_t* sa, uint8_t* sb, uint32_t k0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < QA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(la + (4 * q + w) * 1024), 16, aoff[q] + k0, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(lb + (4 * q + w) * 1024), 16, boff[q] + k0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < (SA + SB + 3) / 4; ++k) {
+      const int t = 4 * k + w;  // wave-uniform
+      if (t < SA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + t * 256), 4, soff[k] + k0 / 32, 0, 0, 0);
+      else if (t < SA + SB)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + (t - SA) * 256), 4, soff[k] + k0 / 32, 0, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + w * 256), 4, asoff + k0 / 32, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + w * 256), 4, bsoff + k0 / 32, 0, 0, 0);
   };
-  f32x16 acc[4][4];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   // 32-row fragments of this wave that hold rows of the expert (small
   // experts leave most of a 256-row tile empty: their MFMAs are skipped)
   const int64_t left = row_end - (row0 + wm);
-  const int mi_valid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32)));
-  auto compute_n = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb, auto miv) {
-    constexpr int MIV = decltype(miv)::value;
+  const int mi_valid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : 1);
+  auto compute_n = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      i32x8 fa[4], fb[4];
-      int ya[4], yb[4];
+      i32x8 fa[MI], fb[NJ];
+      int ya[MI], yb[NJ];
 #pragma unroll
-      for (int i = 0; i < MIV; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int r = wm + i * 32 + li;
         const uint8_t* p = la + r * BK;
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
@@ -485,7 +509,7 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
         ya[i] = sa[r * 4 + ks * 2 + g];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int r = wn + j * 32 + li;
         const uint8_t* p = lb + r * BK;
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
@@ -494,14 +518,14 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
         yb[j] = sb[r * 4 + ks * 2 + g];
       }
 #pragma unroll
-      for (int i = 0; i < MIV; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
     }
   };
   auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
-    if (mi_valid > 0) compute_n(la, lb, sa, sb, std::integral_constant<int, 4>{});
+    if (mi_valid > 0) compute_n(la, lb, sa, sb);
   };
   // Step s: wait for this wave's loads of slab s and its LDS reads of slab
   // s - 1, barrier (everyone's slab s has landed, nobody still reads the
@@ -529,9 +553,9 @@ __global__ void __launch_bounds__(dmag::NT, 1) k_dgrad_dma(const uint8_t* __rest
   }
   // epilogue: direct stores, two full 128-byte row segments per instruction
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int64_t col = n0 + wn + j * 32 + li;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -601,8 +625,8 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
       const int e = (int)(t / per_e);
       const int64_t rest = t % per_e;
       const int64_t p0 = offs[e], kl = (int64_t)offs[e + 1] - p0;
-      opa.init(a_codes + N1 * p0, a_sf + N1 * p0 / 32, N1, kl, (rest / n_ntiles) * BM, kl);
-      opb.init(b_codes + N2 * p0, b_sf + N2 * p0 / 32, N2, kl, (rest % n_ntiles) * BN, kl);
+      opa.init(a_codes + N1 * p0, a_sf + N1 * p0 / 32, N1, kl, (rest / n_ntiles) * BM, kl, true);
+      opb.init(b_codes + N2 * p0, b_sf + N2 * p0 / 32, N2, kl, (rest % n_ntiles) * BN, kl, true);
       lnk = (uint32_t)((kl + BK - 1) / BK);
     } else {  // past the walk: zero-range loads
       opa.klen = 0;
@@ -655,162 +679,251 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
   }
 }
 
-// wgrad with direct-to-LDS loads: 256 x 256 tiles, K slabs of 128 padded
-// tokens, two LDS buffers, one tile per workgroup in expert-fastest order
-// (tile t -> expert t % E: every expert's tiles spread over all XCDs, which
-// the hardware fills round-robin).  A tile of an expert without tokens
-// writes its zeros (beta = 0) and exits.  K tails (P_e is a multiple of 32)
-// come as zeros from the range check: chunks and scale blocks at or past the
-// expert's token count use an out-of-range offset, and out-of-range direct
-// loads write zeros.  Scale bytes arrive one per lane (as zero-extended
-// dwords: LDS scale layout [block][row] of dwords), since an expert's scale
-// rows need not be 4-byte aligned.
-__global__ void __launch_bounds__(dmag::NT, 1) k_wgrad_dma(const uint8_t* __restrict__ a_codes,
-                                                          const uint8_t* __restrict__ a_sf,
-                                                          const uint8_t* __restrict__ b_codes,
-                                                          const uint8_t* __restrict__ b_sf,
-                                                          const int32_t* __restrict__ off, int E, int64_t N1,
-                                                          int64_t N2, int64_t n_ntiles, float* __restrict__ dw,
-                                                          float beta) {
-  using namespace dmag;
-  constexpr int SCW = 4 * 256 * 4;  // scale dwords per operand per buffer
-  __shared__ __attribute__((aligned(16))) uint8_t la0[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t lb0[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t la1[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t lb1[CODE];
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[SCW];
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[SCW];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[SCW];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[SCW];
-  const int e = (int)(blockIdx.x % E);
-  const int64_t rest = blockIdx.x / E;
-  const int64_t m0 = (rest / n_ntiles) * BM, c0 = (rest % n_ntiles) * BN;
-  const int64_t p0 = off[e];
-  const int64_t kl = (int64_t)off[e + 1] - p0;
-  const int tid = threadIdx.x, l = tid & 63, g = (l >> 5) & 1, li = l & 31;
+// One kernel per configuration (the body is a device template).
+#define MOE4_DGRAD_DMA_KERNEL(NAME, TM, TN, MINB)                                                                  \
+  __global__ void __launch_bounds__(dmag::NT, MINB)                                                               \
+      NAME(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,                                 \
+           const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf, const int32_t* __restrict__ off, \
+           int E, int64_t M_total, int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all, float* __restrict__ c) { \
+    dgrad_dma_body<TM, TN>(a_codes, a_sf, b_codes, b_sf, off, E, M_total, N, K, n_ntiles, n_all, c);             \
+  }
+MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_256, 256, 256, 1)
+MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_128, 128, 128, 2)
+#undef MOE4_DGRAD_DMA_KERNEL
+
+// wgrad, warp-specialized and persistent.  On this architecture one
+// counter tracks a wave's loads and stores together and completes them in
+// issue order, so a wave that both stores a finished tile and waits for its
+// next slab's loads waits for the stores' write acknowledgements too: with
+// tiles of a few slabs that stall dominates.  Here the roles are split:
+// four producer waves only issue direct-to-LDS loads (codes as whole
+// 128-byte row segments; the block-major scales of a slab's 4 K blocks x 64
+// rows as one dword load) into a ring of S stages,
+// and four consumer waves only read LDS, run the MFMAs and store the
+// finished tiles, so no load wait ever queues behind a store.  One barrier
+// per slab: after barrier g the consumers compute slab g from stage g % S
+// while the producers fill stage (g - 1) % S (read by everyone before the
+// barrier) with slab g + S - 1, then wait for slab g + 1 to land.  Both
+// roles walk the same tiles (b, b + grid, ... of the expert-major order) and
+// slab counts, so their barrier counts agree; tiles of experts without
+// tokens are zero-filled by the consumers (beta = 0) without a barrier.
+// K tails, and rows past N1 or N2, come as zeros from out-of-range loads.
+namespace wsg {
+constexpr int TM = 128, TN = 128, BK = 128, S = 4;
+constexpr int NCW = 4, NPW = 4, NT = 64 * (NCW + NPW);
+constexpr int CODE = TM * BK;   // one operand's codes per stage
+constexpr int SCL = 4 * TM;     // one operand's scale bytes per stage: [row half][K block][64 rows]
+constexpr int STAGE = 2 * CODE + 2 * SCL;
+constexpr int I = 9;            // loads per producer wave and slab: 8 code row groups + 1 for the scales
+// s_waitcnt immediates (vmcnt: bits 3:0 and 15:14; expcnt 6:4; lgkmcnt 11:8)
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
+constexpr int MAX_E = 2048;     // expert offsets staged in LDS
+constexpr int NT_STORE = 2;     // buffer-store cache policy: nontemporal
+}  // namespace wsg
+
+__global__ void __launch_bounds__(wsg::NT, 1)
+    k_wgrad_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
+               const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
+               const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, int64_t n_ntiles_, int64_t n_all_,
+               float* __restrict__ dw, float beta) {
+  using namespace wsg;
+  using dmag::lds_ptr;
+  using dmag::swz;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
+  __shared__ int32_t s_off[MAX_E + 1];
+  // tile indices fit 31 bits (checked at launch): 32-bit index arithmetic
+  const uint32_t n_all = (uint32_t)n_all_, n_ntiles = (uint32_t)n_ntiles_, per_e = n_all / (uint32_t)E;
+  const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
-  float* C = dw + (int64_t)e * N1 * N2;
-  if (kl == 0) {  // no tokens: zeros for beta = 0, whole 16-byte rows per wave
-    if (beta != 0.0f) return;
-#pragma unroll 4
-    for (int k = 0; k < 128 * 32 / 64; ++k) {
-      const int idx = k * 64 + l;
-      const int64_t row = m0 + wm + idx / 32, col = c0 + wn + (idx % 32) * 4;
-      if (row < N1 && col < N2)
-        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4*>(C + row * N2 + col));
+  for (int i = tid; i <= E; i += NT) s_off[i] = off[i];
+  __syncthreads();
+  if (w >= NCW) {
+    // ---- producer: wave pw loads half h of operand B (pw >= 2) or A
+    const int pw = w - NCW, h = pw & 1;
+    const bool opb = pw >= 2;
+    const int64_t NR = opb ? N2 : N1;
+    const uint8_t* codes = opb ? b_codes : a_codes;
+    const uint8_t* sf = opb ? b_sf : a_sf;
+    uint32_t pt = blockIdx.x;
+    uint32_t ps = 0, pnk = 0, klen = 0, srow = 0;
+    uint32_t crow[8];
+    __amdgpu_buffer_rsrc_t rc = make_rsrc(codes, 0), rs = make_rsrc(sf, 0);
+    // move to the first tile at or after pt whose expert has tokens
+    auto seek = [&]() -> bool {
+      for (; pt < n_all; pt += gridDim.x) {
+        // (offsets from global memory through the scalar cache: an LDS read
+        // here would make the compiler wait for this wave's direct-to-LDS loads)
+        const uint32_t e = pt / per_e, rest = pt - e * per_e;
+        const int64_t p0 = off[e], kl = (int64_t)off[e + 1] - p0;
+        if (kl == 0) continue;
+        const int64_t r0 = opb ? (int64_t)(rest % n_ntiles) * TN : (int64_t)(rest / n_ntiles) * TM;
+        rc = make_rsrc(codes + NR * p0, (uint64_t)NR * kl);
+        rs = make_rsrc(sf + NR * p0 / 32, (uint64_t)NR * (kl / 32));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = h * 64 + j * 8 + (l >> 3);
+          const int64_t r = r0 + row < NR ? r0 + row : NR - 1;
+          crow[j] = (uint32_t)(r * kl + 16 * swz(row, l & 7));
+        }
+        // lane l: rows r0 + h * 64 + 4 (l % 16) .. + 3 of K block l / 16 of
+        // the slab (block-major scales; NR % 32 == 0 keeps the 4 rows together)
+        const int64_t rr = r0 + h * 64 + (l & 15) * 4;
+        srow = rr < NR ? (uint32_t)((l >> 4) * NR + rr) : bwd::OOB;
+        klen = (uint32_t)kl;
+        pnk = (uint32_t)((kl + BK - 1) / BK);
+        ps = 0;
+        return true;
+      }
+      return false;
+    };
+    bool more = seek();
+    // issue the cursor's slab into stage st and advance the cursor
+    auto issue = [&](int st) {
+      uint8_t* base = ring + st * STAGE;
+      uint8_t* cb = base + (opb ? CODE : 0) + h * 8 * 1024;
+      uint8_t* sb = base + 2 * CODE + (opb ? SCL : 0) + h * 256;
+      const uint32_t k0 = ps * BK;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = k0 + 16 * (uint32_t)swz(h * 64 + j * 8 + (l >> 3), l & 7) < klen;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr)(cb + j * 1024), 16, ok ? crow[j] + k0 : bwd::OOB, 0, 0,
+                                                 0);
+      }
+      const bool sok = srow != bwd::OOB && k0 + 32 * (uint32_t)(l >> 4) < klen;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)sb, 4, sok ? srow + (k0 / 32) * (uint32_t)NR : bwd::OOB, 0,
+                                               0, 0);
+      if (++ps == pnk) {
+        pt += gridDim.x;
+        more = seek();
+      }
+    };
+    uint32_t n_iss = 0;
+    for (int st = 0; st < S - 1 && more; ++st) {
+      issue(st);
+      ++n_iss;
+    }
+    for (uint32_t gs = 0; gs < n_iss; ++gs) {
+      // slab gs landed (later slabs may still be in flight), then the barrier
+      const uint32_t rem = n_iss - 1 - gs;
+      __builtin_amdgcn_sched_barrier(0);
+      if (rem >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * I));
+      else if (rem == 1) __builtin_amdgcn_s_waitcnt(wait_vm(I));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      if (more) {
+        issue((int)((gs + S - 1) % S));
+        ++n_iss;
+      }
     }
     return;
   }
-  const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes + N1 * p0, (uint64_t)N1 * kl);
-  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf + N1 * p0 / 32, (uint64_t)N1 * (kl / 32));
-  const __amdgpu_buffer_rsrc_t rbc = make_rsrc(b_codes + N2 * p0, (uint64_t)N2 * kl);
-  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_sf + N2 * p0 / 32, (uint64_t)N2 * (kl / 32));
-  const uint32_t klen = (uint32_t)kl;
-  uint32_t arow[8], brow[8];
+  // ---- consumers: wave w owns the 64 x 64 quadrant (w / 2, w % 2)
+  constexpr int MI = 2, NJ = 2;
+  const int g = (l >> 5) & 1, li = l & 31;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = (4 * q + w) * 8 + (l >> 3);
-    const int64_t ra = m0 + row < N1 ? m0 + row : N1 - 1;
-    const int64_t rb = c0 + row < N2 ? c0 + row : N2 - 1;
-    arow[q] = (uint32_t)(ra * kl + 16 * swz(row, l & 7));
-    brow[q] = (uint32_t)(rb * kl + 16 * swz(row, l & 7));
-  }
-  const int64_t sra = m0 + w * 64 + l < N1 ? m0 + w * 64 + l : N1 - 1;
-  const int64_t srb = c0 + w * 64 + l < N2 ? c0 + w * 64 + l : N2 - 1;
-  const uint32_t asrow = (uint32_t)(sra * (kl / 32)), bsrow = (uint32_t)(srb * (kl / 32));
-  auto issue = [&](uint8_t* la, uint8_t* lb, uint8_t* sa, uint8_t* sb, uint32_t k0) {
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      // the lane's logical chunk (row + l / 8 has the same (row >> 1) & 7
-      // for every q, as 4 q + w steps rows by multiples of 8)
-      const bool ok = k0 + 16 * (uint32_t)swz((4 * q + w) * 8 + (l >> 3), l & 7) < klen;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(la + (4 * q + w) * 1024), 16,
-                                               ok ? arow[q] + k0 : 0x80000000u, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(lb + (4 * q + w) * 1024), 16,
-                                               ok ? brow[q] + k0 : 0x80000000u, 0, 0, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bool ok = k0 + 32 * b < klen;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)(sa + (b * 256 + w * 64) * 4), 1,
-                                               ok ? asrow + k0 / 32 + b : 0x80000000u, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)(sb + (b * 256 + w * 64) * 4), 1,
-                                               ok ? bsrow + k0 / 32 + b : 0x80000000u, 0, 0, 0);
-    }
-  };
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t* base) {
+    const uint8_t* la = base;
+    const uint8_t* lb = base + CODE;
+    const uint8_t* sa = base + 2 * CODE;
+    const uint8_t* sb = base + 2 * CODE + SCL;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      i32x8 fa[4], fb[4];
-      int ya[4], yb[4];
+      i32x8 fa[MI], fb[NJ];
+      int ya[MI], yb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int r = wm + i * 32 + li;
         const uint8_t* p = la + r * BK;
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
         const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
         fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        ya[i] = sa[((ks * 2 + g) * 256 + r) * 4];
+        ya[i] = sa[(r >> 6) * 256 + (ks * 2 + g) * 64 + (r & 63)];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int r = wn + j * 32 + li;
         const uint8_t* p = lb + r * BK;
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
         const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
         fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        yb[j] = sb[((ks * 2 + g) * 256 + r) * 4];
+        yb[j] = sb[(r >> 6) * 256 + (ks * 2 + g) * 64 + (r & 63)];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
     }
   };
-  auto sync = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  const uint32_t nk = (klen + BK - 1) / BK;
-  issue(la0, lb0, sa0, sb0, 0);
-  uint32_t s = 0;
-  for (; s + 2 <= nk; s += 2) {
-    sync();
-    issue(la1, lb1, sa1, sb1, (s + 1) * BK);
-    compute(la0, lb0, sa0, sb0);
-    sync();
-    if (s + 2 < nk) issue(la0, lb0, sa0, sb0, (s + 2) * BK);
-    compute(la1, lb1, sa1, sb1);
-  }
-  if (s < nk) {
-    sync();
-    compute(la0, lb0, sa0, sb0);
-  }
+  uint32_t gs = 0;  // slab of the stream
+  // output stores: buffer stores off one per-lane offset (row g * 4, column
+  // li of a fragment) plus a uniform offset per value; N1 and N2 are
+  // multiples of 32, so each 32 x 32 fragment is wholly inside or outside
+  const uint32_t ld = (uint32_t)N2 * 4;  // row pitch in bytes
+  const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * 4;
+  for (uint32_t t = blockIdx.x; t < n_all; t += gridDim.x) {
+    const uint32_t e = t / per_e, rest = t - e * per_e;
+    const uint32_t mt = rest / n_ntiles, nt = rest - mt * n_ntiles;
+    const int64_t m0 = (int64_t)mt * TM, c0 = (int64_t)nt * TN;
+    const int kl = s_off[e + 1] - s_off[e];
+    float* C = dw + (int64_t)e * N1 * N2;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (uint64_t)N1 * N2 * 4);
+    if (kl == 0) {  // no tokens: zeros for beta = 0; 4 rows x 64 columns per store
+      if (beta != 0.0f) continue;
+      const bool cok = c0 + wn + (l & 15) * 4 < N2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = c0 + wn + j * 32 + li;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row < N1 && col < N2) {
-          float* p = C + row * N2 + col;
-          float val = acc[i][j][v];
-          if (beta != 0.0f) val = *p + val;
-          __builtin_nontemporal_store(val, p);
-        }
+      for (int k = 0; k < 16; ++k) {
+        const int64_t row = m0 + wm + k * 4 + (l >> 4);
+        const uint32_t o = (uint32_t)(row * N2 + c0 + wn + (l & 15) * 4) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128((__attribute__((ext_vector_type(4))) unsigned){0u, 0u, 0u, 0u}, rC,
+                                               row < N1 && cok ? o : bwd::OOB, 0, NT_STORE);
       }
+      continue;
     }
+    const uint32_t nk = (uint32_t)((kl + BK - 1) / BK);
+    for (uint32_t s = 0; s < nk; ++s, ++gs) {
+      // this wave's reads of the previous slab are done; barrier g
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      compute(ring + (gs % S) * STAGE);
+    }
+    // epilogue: two full 128-byte row segments per store instruction
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t r = m0 + wm + i * 32, c = c0 + wn + j * 32;
+        if (r < N1 && c < N2) {
+          const uint32_t fo = (uint32_t)(r * N2 + c) * 4;
+          if (beta == 0.0f) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rC, lane_off,
+                                                    fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld, NT_STORE);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const uint32_t so = fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld;
+              const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC, lane_off, so, 0));
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old + acc[i][j][v]), rC, lane_off, so, NT_STORE);
+            }
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      }
+  }
 }
 
 static int cu_count() {
@@ -832,7 +945,7 @@ static int mx_tile_choice(int mode) {
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
-                       return e ? atoi(e) : 1;
+                       return e ? atoi(e) : 10;
                      }()};
   return v[mode];
 }
@@ -862,20 +975,22 @@ static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 // (2 blocks/CU), 2 = 128x256 2x2, 3 = 256x256 with 2x4 waves (two waves per
 // SIMD), 4 = 256x256 with 4x2 waves (3 and 4 with one prefetch register
 // set), 5 = 256x256 2x2 with one register set, 6 = 256x256 2x2 with
-// double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves,
-// 8 = direct-to-LDS loads (k_dgrad_dma / k_wgrad_dma; the dgrad default when
-// K % 128 == 0, else 6).  wgrad defaults to the persistent 128x128 kernel:
-// with few experts holding most tokens, one-tile-per-workgroup grids end in
-// a long tail of heavy tiles.
+// double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves;
+// dgrad only: 8 = direct-to-LDS loads, 256x256 (the default when
+// K % 128 == 0, else 6), 9 = as 8 with 128x128 tiles at 2 blocks/CU; wgrad
+// only: 10 = the warp-specialized persistent kernel (the default; needs
+// E <= 2048 and 32-bit tile and output indices, else configuration 1, the
+// persistent register-staged kernel).
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   int choice = mx_tile_choice(0);
-  if (choice == 8 && K % dmag::BK != 0) choice = 6;
-  if (choice == 8) {
-    const int64_t n_nt = (N + dmag::BN - 1) / dmag::BN;
-    const int64_t n_all = n_nt * ((M + dmag::BM - 1) / dmag::BM + E);
-    hipLaunchKernelGGL(k_dgrad_dma, dim3((unsigned)xcd_grid(n_all)), dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, M, N,
-                       K, n_nt, n_all, c);
+  if ((choice == 8 || choice == 9) && K % dmag::BK != 0) choice = 6;
+  if (choice == 8 || choice == 9) {
+    const int T = choice == 8 ? 256 : 128;
+    const int64_t n_nt = (N + T - 1) / T;
+    const int64_t n_all = n_nt * ((M + T - 1) / T + E);
+    hipLaunchKernelGGL(choice == 8 ? k_dgrad_dma_256 : k_dgrad_dma_128, dim3((unsigned)xcd_grid(n_all)),
+                       dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, M, N, K, n_nt, n_all, c);
     return;
   }
   switch (choice) {
@@ -892,11 +1007,15 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
 
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
-  if (mx_tile_choice(1) == 8) {
-    const int64_t n_nt = (N2 + dmag::BN - 1) / dmag::BN;
-    const int64_t n_all = n_nt * ((N1 + dmag::BM - 1) / dmag::BM) * E;
-    hipLaunchKernelGGL(k_wgrad_dma, dim3((unsigned)n_all), dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, N1, N2, n_nt,
-                       dw, beta);
+  const int wc = mx_tile_choice(1);
+  const int64_t ws_all = (N2 + wsg::TN - 1) / wsg::TN * ((N1 + wsg::TM - 1) / wsg::TM) * E;
+  if (wc == 10 && E <= wsg::MAX_E && ws_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
+    const int64_t n_nt = (N2 + wsg::TN - 1) / wsg::TN;
+    const int64_t n_all = ws_all;
+    int64_t grid = cu_count();
+    if (grid > n_all) grid = n_all;
+    hipLaunchKernelGGL(k_wgrad_ws, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2, n_nt,
+                       n_all, dw, beta);
     return;
   }
   switch (mx_tile_choice(1)) {

@@ -191,18 +191,18 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
                                                            const float* __restrict__ ts, int ts_per_group, int64_t C,
                                                            const int32_t* __restrict__ off,
                                                            const int32_t* __restrict__ offp, int G, int64_t R,
-                                                           int64_t max_pr, int64_t n_ct, uint32_t base,
+                                                           int64_t max_pr, int64_t n_ct, uint32_t base, int sfb,
                                                            uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s) {
   using namespace rq;
   __shared__ __attribute__((aligned(16))) uint8_t lq[COLS * ROWS];
   __shared__ uint8_t lsf[COLS * WAVES];  // [column][block]
-  __shared__ int64_t lblk[WAVES][2];     // block's output offset at column 0, and P (0: no block)
+  __shared__ int64_t lblk[WAVES][3];     // block's code offset at column 0, P (0: no block), scale offset at column 0
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * COLS;
   const int64_t pr = ((int64_t)(blockIdx.x / n_ct) * WAVES + w) * 32;
   const int64_t ptot = offp[G];
   const bool present = pr < ptot && ptot <= max_pr;
-  int64_t P = 0, pr_in_g = 0, src0 = 0, obase = 0;
+  int64_t P = 0, pr_in_g = 0, src0 = 0, obase = 0, sbase = 0;
   int nvalid = 0, g = 0;
   if (present) {
     g = find_group(offp, G, pr);
@@ -213,10 +213,12 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     const int64_t n = gend - src0;
     nvalid = n < 0 ? 0 : (n > 32 ? 32 : (int)n);
     obase = C * (int64_t)offp[g] + pr_in_g;
+    sbase = C * (int64_t)offp[g] / 32 + (sfb ? (pr_in_g / 32) * C : pr_in_g / 32);
   }
   if (l == 0) {
     lblk[w][0] = obase;
     lblk[w][1] = P;
+    lblk[w][2] = sbase;
   }
   const int64_t c = c0 + LCOLS * l;
   uint32_t ob[8][8];
@@ -281,12 +283,14 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
       *reinterpret_cast<u32x4*>(out_c + lblk[b][0] + gc * Pb + (chunk & 1) * 16) =
           *reinterpret_cast<const u32x4*>(lq + col * ROWS + swz(col, chunk) * 16);
   }
+  // scale bytes: row-major (column stride P/32; a thread's 4 blocks are
+  // consecutive) or block-major (consecutive columns are consecutive bytes)
 #pragma unroll
   for (int it = 0; it < COLS * WAVES / THREADS; ++it) {
     const int idx = it * THREADS + tid;
-    const int col = idx >> 2, b = idx & 3;
+    const int col = sfb ? idx % COLS : idx >> 2, b = sfb ? idx / COLS : idx & 3;
     const int64_t Pb = lblk[b][1], gc = c0 + col;
-    if (Pb != 0 && gc < C) out_s[lblk[b][0] / 32 + gc * (Pb / 32)] = lsf[col * WAVES + b];
+    if (Pb != 0 && gc < C) out_s[lblk[b][2] + (sfb ? gc : gc * (Pb / 32))] = lsf[col * WAVES + b];
   }
 }
 
@@ -372,7 +376,7 @@ __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C
 template <int DT, int MODE, bool SR>
 __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, const int32_t* __restrict__ off,
                                               const int32_t* __restrict__ offp, int G, int64_t max_pr, int64_t n_ct,
-                                              uint32_t base,
+                                              uint32_t base, int sfb,
                                               uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
                                               const float* __restrict__ act_tab) {
   __shared__ float tab[MODE == 2 ? ACT_TAB : 1];
@@ -407,8 +411,9 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
   const int64_t c = c0 + cl;
   const int64_t orow = t.pr_in_g + rseg * 8;
   uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
-  uint8_t* s0 = out_s + t.out_base / 32 + c * (t.P / 32) + t.pr_in_g / 32;
-  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + t.P / 32);
+  // scale of (column c, block pr_in_g / 32): row-major [C][P/32] or block-major [P/32][C]
+  uint8_t* s0 = out_s + t.out_base / 32 + (sfb ? (t.pr_in_g / 32) * C + c : c * (t.P / 32) + t.pr_in_g / 32);
+  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + (sfb ? 1 : t.P / 32));
 }
 
 template <int DT, int MODE>
@@ -423,12 +428,13 @@ static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int
   } else {
     const int64_t n_ct = (C + TC - 1) / TC, n_rt = (max_pr + TR - 1) / TR;
     dim3 grid((unsigned)(n_ct * n_rt));
+    const int sfb = transpose == 2;
     if (sr)
-      hipLaunchKernelGGL((k_mx_T<DT, MODE, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base, oc,
-                         os, tab);
+      hipLaunchKernelGGL((k_mx_T<DT, MODE, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base, sfb,
+                         oc, os, tab);
     else
       hipLaunchKernelGGL((k_mx_T<DT, MODE, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base,
-                         oc, os, tab);
+                         sfb, oc, os, tab);
   }
 }
 
@@ -439,12 +445,14 @@ using namespace moe4;
 extern "C" int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
                                   int64_t rows, int64_t cols, const int32_t* group_row_off,
                                   const int32_t* group_off_pad, int32_t n_groups, int64_t max_padded_rows,
-                                  uint64_t seed, uint32_t stream_id, uint8_t* out_codes, uint8_t* out_sf,
-                                  void* stream) {
+                                  uint64_t seed, uint32_t stream_id, int sf_layout, uint8_t* out_codes,
+                                  uint8_t* out_sf, void* stream) {
   MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_requant_sr_T: cols must be a positive multiple of 32");
   MOE4_REQUIRE(n_groups >= 1 && group_row_off && group_off_pad, MOE4_EINVAL, "mxfp8_requant_sr_T: group offsets required");
   MOE4_REQUIRE(max_padded_rows >= 0 && max_padded_rows % 32 == 0, MOE4_EINVAL,
                "mxfp8_requant_sr_T: max_padded_rows must be a multiple of 32");
+  MOE4_REQUIRE(sf_layout == MOE4_SF_ROWS || sf_layout == MOE4_SF_BLOCKS, MOE4_EINVAL,
+               "mxfp8_requant_sr_T: sf_layout must be MOE4_SF_ROWS or MOE4_SF_BLOCKS");
   MOE4_REQUIRE(codes && sf && ts && out_codes && out_sf, MOE4_EINVAL, "mxfp8_requant_sr_T: NULL pointer");
   MOE4_REQUIRE(aligned16(codes) && aligned16(out_codes), MOE4_EALIGN, "mxfp8_requant_sr_T: misaligned pointer");
   if (max_padded_rows == 0) return MOE4_OK;
@@ -453,7 +461,7 @@ extern "C" int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const
   const uint32_t base = sr_base_key(seed, stream_id);
   hipLaunchKernelGGL(k_requant_T, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, as_stream(stream), codes, sf, ts,
                      ts_per_group, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct, base,
-                     out_codes, out_sf);
+                     (int)(sf_layout == MOE4_SF_BLOCKS), out_codes, out_sf);
   return check_launch("mxfp8_requant_sr_T");
 }
 
@@ -464,6 +472,7 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
                            uint8_t* out_codes, uint8_t* out_sf, void* stream) {
   MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "mxfp8_quant: dtype must be BF16 or F32");
   MOE4_REQUIRE(rnd == MOE4_RNE || rnd == MOE4_SR, MOE4_EINVAL, "mxfp8_quant: rnd must be RNE or SR");
+  MOE4_REQUIRE(transpose >= 0 && transpose <= 2, MOE4_EINVAL, "mxfp8_quant: transpose must be 0, 1 or 2");
   MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_quant: cols must be a positive multiple of 32");
   MOE4_REQUIRE(!(row_map && dsilu_src), MOE4_EINVAL, "mxfp8_quant: row_map and dsilu_src are exclusive");
   MOE4_REQUIRE(!row_map || map_div >= 1, MOE4_EINVAL, "mxfp8_quant: map_div >= 1");

@@ -21,7 +21,7 @@ silu'(U) -> MXFP8; un-permuting sum -> dx (bf16).
 """
 import torch
 
-from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, max_padded_rows, moe_combine, moe_gather_rows,
+from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, SF_BLOCKS, max_padded_rows, moe_combine, moe_gather_rows,
                moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
                moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46)
 
@@ -90,7 +90,7 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     dy_row = mxfp8_quant(dy, rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat)
     _tick(timer, "B1 dY quant row-wise (MXFP8)")
     dy_col = mxfp8_quant(dy, rows=A, transpose=True, row_map=r["perm"], map_div=k, row_scale=g_flat,
-                         group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr)
+                         group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr, sf_layout=SF_BLOCKS)
     _tick(timer, "B1 dY quant transposed (MXFP8)")
     wq = fw["wq"]
     wd_c, wd_s, wd_t = wq["wd"]
@@ -99,14 +99,15 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
     _tick(timer, "B3 down dgrad (MXFP8)")
     hq = fw["hq"]
-    hT = mxfp8_requant_sr_T(hq[0], hq[1], hq[2], r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr)
+    hT = mxfp8_requant_sr_T(hq[0], hq[1], hq[2], r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr,
+                            sf_layout=SF_BLOCKS)
     _tick(timer, "B4 H requant SR-T")
     dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
     _tick(timer, "B5 down wgrad (MXFP8)")
     du_row = mxfp8_quant(dH, dsilu_src=fw["U"])
     _tick(timer, "B6 SiLU' + dU quant row-wise")
     du_col = mxfp8_quant(dH, transpose=True, dsilu_src=fw["U"], group_row_off=r["off"], group_off_pad=r["off_pad"],
-                         max_pr=mpr)
+                         max_pr=mpr, sf_layout=SF_BLOCKS)
     _tick(timer, "B6 SiLU' + dU quant transposed")
     wu_c, wu_s, wu_t = wq["wu"]
     wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
@@ -114,7 +115,8 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")
     xp = fw["xq_perm"]
-    xT = mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X), max_pr=mpr)
+    xT = mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X), max_pr=mpr,
+                            sf_layout=SF_BLOCKS)
     _tick(timer, "B9 X requant SR-T")
     dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d)
     _tick(timer, "B10 up wgrad (MXFP8)")

@@ -145,14 +145,14 @@ def test_grouped_gemm_wgrad_tolerance(beta):
     M = int(off[-1])
     a = synth.randn((M, N1), 1e-3, "cpu", 3, "dh").numpy()
     b = synth.randn((M, N2), 1.0, "cpu", 4, "dh").numpy()
-    ac, as_ = mx.quantize_transposed(a, off, mx.RNE)
-    bc, bs = mx.quantize_transposed(b, off, mx.SR, 1, 1)
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    bc, bs = mx.quantize_transposed(b, off, mx.SR, 1, 1, sf_layout=mx.SF_BLOCKS)
     dw0 = np.random.default_rng(5).standard_normal((E, N1, N2)).astype(np.float32)
     dw = torch.from_numpy(dw0.copy()).cuda()
     m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
                                   torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=beta)
-    Al = mx.dequant_transposed(ac, as_, off, N1)
-    Bl = mx.dequant_transposed(bc, bs, off, N2)
+    Al = mx.dequant_transposed(ac, as_, off, N1, mx.SF_BLOCKS)
+    Bl = mx.dequant_transposed(bc, bs, off, N2, mx.SF_BLOCKS)
     exact = og.wgrad(Al, Bl)
     bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
     got = to_np(dw).astype(np.float64)
@@ -176,14 +176,14 @@ def test_grouped_gemm_wgrad_many_experts(beta):
     M = int(off[-1])
     a = synth.randn((M, N1), 1.0, "cpu", 6, "dh").numpy()
     b = synth.randn((M, N2), 1e-2, "cpu", 7, "dh").numpy()
-    ac, as_ = mx.quantize_transposed(a, off, mx.RNE)
-    bc, bs = mx.quantize_transposed(b, off, mx.RNE)
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    bc, bs = mx.quantize_transposed(b, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
     dw0 = np.random.default_rng(8).standard_normal((E, N1, N2)).astype(np.float32)
     dw = torch.from_numpy(dw0.copy()).cuda()
     m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
                                   torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=beta)
-    Al = mx.dequant_transposed(ac, as_, off, N1)
-    Bl = mx.dequant_transposed(bc, bs, off, N2)
+    Al = mx.dequant_transposed(ac, as_, off, N1, mx.SF_BLOCKS)
+    Bl = mx.dequant_transposed(bc, bs, off, N2, mx.SF_BLOCKS)
     exact = og.wgrad(Al, Bl)
     bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
     got = to_np(dw).astype(np.float64)
@@ -193,3 +193,60 @@ def test_grouped_gemm_wgrad_many_experts(beta):
     else:
         assert not got[M_list == 0].any()
     gemm_tol_check(got, exact, bound, f"wgrad many experts beta={beta}")
+
+
+@pytest.mark.parametrize("M_list,N1,N2", [
+    ([0] * 5 + [2000] + [0] * 6 + [1, 0, 33, 0], 128, 128),   # 16 tiles: two workgroups per XCD, most ranges empty
+    ([700], 512, 512),                                         # one expert cut into several XCD ranges
+    ([3, 0, 1500, 64, 0, 0, 31, 900] * 3, 256, 128),          # 48 tiles, heavy experts next to empty ones
+])
+def test_grouped_gemm_wgrad_skewed_xcd_ranges(M_list, N1, N2):
+    """Tile counts that are multiples of 8 but below the resident grid, with
+    token counts skewed so that the cost-balanced per-XCD ranges cut inside
+    experts, or hold only empty experts."""
+    M_list = np.array(M_list)
+    E = len(M_list)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    offp = mx.padded_offsets(off)
+    M = int(off[-1])
+    a = synth.randn((M, N1), 1.0, "cpu", 9, "dh").numpy()
+    b = synth.randn((M, N2), 1.0, "cpu", 10, "dh").numpy()
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    bc, bs = mx.quantize_transposed(b, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    dw = torch.full((E, N1, N2), float("nan"), dtype=torch.float32, device="cuda")
+    m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
+                                  torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=0.0)
+    Al = mx.dequant_transposed(ac, as_, off, N1, mx.SF_BLOCKS)
+    Bl = mx.dequant_transposed(bc, bs, off, N2, mx.SF_BLOCKS)
+    exact = og.wgrad(Al, Bl)
+    bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
+    got = to_np(dw).astype(np.float64)
+    assert np.isfinite(got).all()                          # every tile written
+    assert not got[M_list == 0].any()
+    gemm_tol_check(got, exact, bound, "wgrad skewed")
+
+
+def test_grouped_gemm_wgrad_more_experts_than_offset_staging():
+    """More experts than the warp-specialized kernel stages offsets for: the
+    register-staged persistent kernel takes over, same results."""
+    N1, N2, E = 64, 32, 2100
+    rng = np.random.default_rng(21)
+    M_list = rng.choice([0, 0, 0, 0, 1, 5, 32, 40], E)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    offp = mx.padded_offsets(off)
+    M = int(off[-1])
+    a = synth.randn((M, N1), 1.0, "cpu", 12, "dh").numpy()
+    b = synth.randn((M, N2), 1.0, "cpu", 13, "dh").numpy()
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    bc, bs = mx.quantize_transposed(b, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    dw = torch.full((E, N1, N2), float("nan"), dtype=torch.float32, device="cuda")
+    m4.moe_grouped_gemm_bwd_wgrad(torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda(),
+                                  torch.from_numpy(bs).cuda(), cuda_i32(offp), N1, N2, dw=dw, beta=0.0)
+    Al = mx.dequant_transposed(ac, as_, off, N1, mx.SF_BLOCKS)
+    Bl = mx.dequant_transposed(bc, bs, off, N2, mx.SF_BLOCKS)
+    exact = og.wgrad(Al, Bl)
+    bound = og.wgrad([np.abs(x) for x in Al], [np.abs(x) for x in Bl])
+    got = to_np(dw).astype(np.float64)
+    assert np.isfinite(got).all()
+    assert not got[M_list == 0].any()
+    gemm_tol_check(got, exact, bound, "wgrad fallback")

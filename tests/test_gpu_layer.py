@@ -195,9 +195,10 @@ def test_wgrad_gemm_full_size_sampled(cfg3_route):
         rows = rng.choice(N1, 12, replace=False)
         cols = rng.choice(N2, 12, replace=False)
         a = ac[N1 * offp[e]: N1 * offp[e + 1]].reshape(N1, Pe)[rows]
-        as_ = asf[N1 * offp[e] // 32: N1 * offp[e + 1] // 32].reshape(N1, Pe // 32)[rows]
+        # (block-major scales: [P_e/32][N] per expert)
+        as_ = asf[N1 * offp[e] // 32: N1 * offp[e + 1] // 32].reshape(Pe // 32, N1).T[rows]
         b = bc[N2 * offp[e]: N2 * offp[e + 1]].reshape(N2, Pe)[cols]
-        bs = bsf[N2 * offp[e] // 32: N2 * offp[e + 1] // 32].reshape(N2, Pe // 32)[cols]
+        bs = bsf[N2 * offp[e] // 32: N2 * offp[e + 1] // 32].reshape(Pe // 32, N2).T[cols]
         a64 = mx.dequant_rowwise(a, as_)
         b64 = mx.dequant_rowwise(b, bs)
         got = to_np(dw[e][torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]).astype(np.float64)

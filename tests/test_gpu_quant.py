@@ -15,6 +15,9 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import precision_moe_numerics_quant_amd as m4
 
+SF_ROWS, SF_BLOCKS = 0, 1                                   # the library's scale-arrangement codes
+LAYOUTS = {SF_ROWS: mx.SF_ROWS, SF_BLOCKS: mx.SF_BLOCKS}    # ... and the oracle's names for them
+
 
 def _bf16_input(R, C, seed, outliers=True):
     x = synth.activations(R, C, "cpu", seed, outlier_p=0.001 if outliers else 0.0, outlier_mul=20.0)
@@ -161,14 +164,18 @@ def _nvfp4_operand(R, C, seed, groups=None, per_group=True):
     (64, 128, None),
     (100, 96, [0, 0, 33, 33, 34, 100]),
     (517, 256, [0, 200, 201, 480, 517]),
+    (300, 1056, [0, 7, 7, 299, 300]),
 ])
-def test_requant_sr_t_bit_exact(R, C, groups):
+@pytest.mark.parametrize("lay", [SF_ROWS, SF_BLOCKS])
+def test_requant_sr_t_bit_exact(R, C, groups, lay):
     off = np.array([0, R]) if groups is None else np.array(groups)
     ref_q = _nvfp4_operand(R, C, R + C, off)
     offp = mx.padded_offsets(off)
-    c_ref, s_ref = mx.requant_sr_t(ref_q["codes"], ref_q["sf"], ref_q["ts"], off, True, seed=1, stream_id=3)
+    c_ref, s_ref = mx.requant_sr_t(ref_q["codes"], ref_q["sf"], ref_q["ts"], off, True, seed=1, stream_id=3,
+                                   sf_layout=LAYOUTS[lay])
     oc, os_ = m4.mxfp8_requant_sr_T(torch.from_numpy(ref_q["codes"]).cuda(), torch.from_numpy(ref_q["sf"]).cuda(),
-                                    torch.from_numpy(ref_q["ts"]).cuda(), cuda_i32(off), cuda_i32(offp), True, 1, 3)
+                                    torch.from_numpy(ref_q["ts"]).cuda(), cuda_i32(off), cuda_i32(offp), True, 1, 3,
+                                    sf_layout=lay)
     n = C * offp[-1]
     assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "requant scales")
     assert_bytes_equal(to_np(oc)[:n], c_ref, "requant codes")
@@ -214,7 +221,7 @@ def test_sr_conversion_all_random_words():
 
 
 @pytest.mark.parametrize("rnd", [0, 1])
-@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("transpose", [False, "rows", "blocks"])
 def test_mxfp8_grad_quant_gated_rows(rnd, transpose):
     T, d, k, E = 130, 96, 3, 7
     rng = np.random.default_rng(1)
@@ -228,9 +235,10 @@ def test_mxfp8_grad_quant_gated_rows(rnd, transpose):
     args = dict(rows=A, row_map=cuda_i32(P["perm"]), map_div=k, row_scale=torch.from_numpy(gates.reshape(-1)).cuda(),
                 rnd=rnd, seed=3, stream_id=4)
     if transpose:
+        lay = SF_ROWS if transpose == "rows" else SF_BLOCKS
         oc, os_ = m4.mxfp8_quant(dy.cuda(), transpose=True, group_row_off=cuda_i32(P["off"]),
-                                 group_off_pad=cuda_i32(P["off_pad"]), **args)
-        c_ref, s_ref = mx.quantize_transposed(dyp, P["off"], rnd, 3, 4)
+                                 group_off_pad=cuda_i32(P["off_pad"]), sf_layout=lay, **args)
+        c_ref, s_ref = mx.quantize_transposed(dyp, P["off"], rnd, 3, 4, sf_layout=LAYOUTS[lay])
         n = d * P["off_pad"][-1]
         assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
         assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
@@ -241,7 +249,7 @@ def test_mxfp8_grad_quant_gated_rows(rnd, transpose):
         assert_bytes_equal(to_np(os_), s_ref, "scales")
 
 
-@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("transpose", [False, "rows", "blocks"])
 def test_mxfp8_grad_quant_dsilu(transpose):
     R, F = 150, 128
     off = np.array([0, 40, 40, 150])
@@ -250,9 +258,10 @@ def test_mxfp8_grad_quant_dsilu(transpose):
     du = (dh * osilu.dsilu_f32(synth.bf16_bits(u))).astype(np.float32)
     if transpose:
         offp = mx.padded_offsets(off)
+        lay = SF_ROWS if transpose == "rows" else SF_BLOCKS
         oc, os_ = m4.mxfp8_quant(torch.from_numpy(dh).cuda(), transpose=True, dsilu_src=u.cuda(),
-                                 group_row_off=cuda_i32(off), group_off_pad=cuda_i32(offp))
-        c_ref, s_ref = mx.quantize_transposed(du, off, mx.RNE)
+                                 group_row_off=cuda_i32(off), group_off_pad=cuda_i32(offp), sf_layout=lay)
+        c_ref, s_ref = mx.quantize_transposed(du, off, mx.RNE, sf_layout=LAYOUTS[lay])
         n = F * offp[-1]
         assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
         assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
@@ -263,14 +272,15 @@ def test_mxfp8_grad_quant_dsilu(transpose):
         assert_bytes_equal(to_np(os_), s_ref, "scales")
 
 
-def test_requant_config2_full_size_sampled_columns():
+@pytest.mark.parametrize("lay", [SF_ROWS, SF_BLOCKS])
+def test_requant_config2_full_size_sampled_columns(lay):
     """16384 x 7168 requant in the benchmark's launch; output rows (source
     columns) sampled and compared with the oracle on the same NVFP4 input."""
     x = synth.config_inputs(2, device="cuda")["x"]
     codes, sf, ts = m4.nvfp4_quant_46(x, 46)
     R, C = x.shape
     off = cuda_i32([0, R])
-    oc, os_ = m4.mxfp8_requant_sr_T(codes, sf, ts, off, off, True, 1, 0, max_pr=R)
+    oc, os_ = m4.mxfp8_requant_sr_T(codes, sf, ts, off, off, True, 1, 0, max_pr=R, sf_layout=lay)
     rng = np.random.default_rng(1)
     cols = np.unique(np.r_[rng.choice(C // 16, 6, replace=False) * 16, C - 16])   # whole NVFP4 blocks
     for c0 in cols:
@@ -281,7 +291,7 @@ def test_requant_config2_full_size_sampled_columns():
         v = nv.dequant_values(q, np.repeat(sub_sf.astype(np.int64), 16, axis=1), to_np(ts)[0])
         # element (r, c0 + j) has source index r * C + c0 + j: quantise with that index map
         got_c = to_np(oc).reshape(C, R)[c0:c0 + 16]
-        got_s = to_np(os_).reshape(C, R // 32)[c0:c0 + 16]
+        got_s = (to_np(os_).reshape(C, R // 32) if lay == SF_ROWS else to_np(os_).reshape(R // 32, C).T)[c0:c0 + 16]
         vt = v.T.astype(np.float64)
         nb = R // 32
         idx = (np.arange(R, dtype=np.uint64)[None, :] * np.uint64(C) + (np.uint64(c0) + np.arange(16, dtype=np.uint64))[:, None])

@@ -136,9 +136,9 @@ def test_transposed_layout_exact_values():
     off = np.array([0, 3, 3, 40, 72, 150])          # includes an empty group and ragged tails
     # values k * 2**-3 with |k| < 16 are E4M3-exact under any block scale <= the amax's
     x = (rng.integers(-15, 16, (R, C)) * 0.125).astype(np.float32)
-    for rnd in (mx.RNE, mx.SR):
-        codes, sf = mx.quantize_transposed(x, off, rnd, seed=1, stream_id=2)
-        blocks = mx.dequant_transposed(codes, sf, off, C)
+    for rnd, lay in ((mx.RNE, mx.SF_ROWS), (mx.SR, mx.SF_ROWS), (mx.RNE, mx.SF_BLOCKS)):
+        codes, sf = mx.quantize_transposed(x, off, rnd, seed=1, stream_id=2, sf_layout=lay)
+        blocks = mx.dequant_transposed(codes, sf, off, C, lay)
         offp = mx.padded_offsets(off)
         assert len(codes) == C * offp[-1]
         for g in range(len(off) - 1):
@@ -146,6 +146,33 @@ def test_transposed_layout_exact_values():
             assert blocks[g].shape == (C, mx.pad32(Rg))
             assert np.array_equal(blocks[g][:, :Rg], x[off[g]:off[g + 1]].T.astype(np.float64))
             assert not blocks[g][:, Rg:].any()
+
+
+@pytest.mark.parametrize("sf_layout", [mx.SF_ROWS, mx.SF_BLOCKS])
+def test_transposed_scale_positions(sf_layout):
+    """Each (column, 32-row block) of a group gets a planted amax of
+    448 * 2**k, whose scale byte must be k + 127 (the least exponent with
+    amax <= 448 * 2**e), at the position the layout names: row-major
+    [C][P/32] or block-major [P/32][C], after the group's C * off_pad / 32."""
+    rng = np.random.default_rng(9)
+    R, C = 130, 96
+    off = np.array([0, 40, 40, 130])                # an empty group, ragged tails
+    offp = mx.padded_offsets(off)
+    x = (rng.uniform(-1.0, 1.0, (R, C)) * 2.0 ** -8).astype(np.float32)
+    want = {}
+    for g in range(len(off) - 1):
+        for b in range((off[g + 1] - off[g] + 31) // 32):
+            rows = np.arange(off[g] + 32 * b, min(off[g] + 32 * b + 32, off[g + 1]))
+            for c in range(C):
+                k = (c + 3 * b + g) % 7 - 3
+                x[rows[(c + b) % len(rows)], c] = np.float32(448.0 * 2.0 ** k) * (1 if c % 2 else -1)
+                want[(g, b, c)] = k + 127
+    _, sf = mx.quantize_transposed(x, off, mx.RNE, sf_layout=sf_layout)
+    assert len(sf) == C * offp[-1] // 32
+    for (g, b, c), byte in want.items():
+        nb = (offp[g + 1] - offp[g]) // 32
+        pos = C * offp[g] // 32 + (c * nb + b if sf_layout == mx.SF_ROWS else b * C + c)
+        assert sf[pos] == byte, (g, b, c)
 
 
 def test_requant_sr_t_exact_grid_and_unbiased():
