@@ -72,6 +72,7 @@ def work_table(c, off, off_pad):
         "B9 X requant SR-T": ("hbm", A * d * nv + d * Ptot * mxb),
         "B10 up wgrad (MXFP8)": ("fp8", gem, wg_bytes(F, d)),
         "B11 un-permute sum": ("hbm", A * d * 4.0 + T * d * 2.0),
+        "B12 gate gradient": ("hbm", A * d * 4.0 + T * d * 2.0 + A * 8.0),
     }
 
 
@@ -88,7 +89,7 @@ KERNEL_OF = {
     "B3 down dgrad (MXFP8)": "k_dgrad_dma_256", "B8 up dgrad (MXFP8)": "k_dgrad_dma_256",
     "B5 down wgrad (MXFP8)": "k_wgrad_ws", "B10 up wgrad (MXFP8)": "k_wgrad_ws",
     "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
-    "B11 un-permute sum": "k_combine (unpermute)",
+    "B11 un-permute sum": "k_combine (unpermute)", "B12 gate gradient": "k_dgates",
 }
 
 # calls that launch several kernels (zero, amax, scale, encode; route's

@@ -82,6 +82,10 @@ extern "C" {
 const char* moe4_last_error(void);
 /* Library version string. */
 const char* moe4_version(void);
+/* Waits for the stream (a synchronising debugging aid, never called by the
+ * library itself) and reports a failed launch or a device-side error as
+ * MOE4_EHIP with the runtime's message. */
+int moe4_debug_check(void* stream);
 
 /* ---------------------------------------------------------------- NVFP4 */
 /*
@@ -275,6 +279,18 @@ int moe_combine(const float* yp, const float* gates, const int32_t* inv_perm, in
  */
 int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                       uint16_t* dx, void* stream);
+
+/*
+ * moe_dgates - gate gradient dg[t*k+j] = sum_c dy[t,c] * yp[inv_perm[t*k+j], c]:
+ * the derivative of moe_combine's weighted sum in gates[t,j] (the combine is
+ * the local stand-in for the pages' return of expert outputs: lhc.media page,
+ * paragraph on communication).  dy [T, d] bf16, yp [T*k, d] float32 (the
+ * forward's expert outputs), dg [T, k] float32 out.  Float32 accumulation:
+ * each lane sums its columns 8l + 512i in order, then a fixed butterfly over
+ * the 64 lanes (deterministic).  d % 8 == 0; dy and yp 16-byte aligned.
+ */
+int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
+               float* dg, void* stream);
 
 /*
  * moe_silu_eval - correctly rounded float32 silu(u) and silu'(u) of bf16 u

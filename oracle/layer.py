@@ -35,6 +35,9 @@ stochastic rounding, stream id 16 * layer + role, role 0 = X_T, 1 = H_T,
  9. X_T = requant_sr_t(Xq_perm, groups = experts, S_x)       -> [E][d][pad32 M_e]
 10. dW_up[e] = float32(exact dU_col[e] . X_T[e]^T)          [E, F, d]
 11. dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dXp[row(t, j)])
+12. dg[t, j] = <dy[t], Yp[row(t, j)]>: the gate gradient, the derivative of the
+    combine's weighted sum in g[t, j] (exact here; a float32 sum of d products
+    in the library)
 
 The transposed operands of the weight-gradient products (dYp_col, H_T, dU_col,
 X_T) keep their scales block-major (SF_BLOCKS), the requantised weights
@@ -104,6 +107,16 @@ def unpermute_sum(dXp, inv, T, k):
     return fmt.bf16_round(acc)
 
 
+def dgates(dy_bf16, Yp, inv, k):
+    """dg[t, j] = sum_c dy[t, c] * Yp[row(t, j), c], row(t, j) = inv[t*k + j]
+    (float64: every product of a bf16 and a float32 is exact)."""
+    dy = fmt.bf16_to_f32(dy_bf16).astype(np.float64)
+    T = dy.shape[0]
+    rows = np.asarray(inv, dtype=np.int64).reshape(T, k)
+    Y = np.asarray(Yp, dtype=np.float64)
+    return np.stack([np.einsum("tc,tc->t", dy, Y[rows[:, j]]) for j in range(k)], axis=1)
+
+
 def gated_grad_rows(dy_bf16, gates, perm, k):
     """dYp[row] = fl(g[t, j] * dy[t]) for the assignment a = perm[row] = t*k + j."""
     dy = fmt.bf16_to_f32(dy_bf16)
@@ -144,7 +157,8 @@ def backward(fw, dy_bf16, seed=1, layer=0):
     dUc = mx.dequant_transposed(du_col_c, du_col_s, off, F, mx.SF_BLOCKS)
     dW_up = gemm.wgrad(dUc, XT).astype(np.float32)
     dx = unpermute_sum(dXp, inv, T, k)
-    return dict(dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),
+    dg = dgates(dy_bf16, fw["Yp"], inv, k)
+    return dict(dg=dg, dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),
                 wdT=(wdT_c, wdT_s), dH=dH, hT=(hT_c, hT_s), dW_down=dW_down, dU=dU,
                 du_row=(du_row_c, du_row_s), du_col=(du_col_c, du_col_s), wuT=(wuT_c, wuT_s),
                 dXp=dXp, xT=(xT_c, xT_s), dW_up=dW_up, dx=dx)

@@ -42,6 +42,8 @@ _SIGS = {
                                   _i64, _u64, _u32, _int, _c_void_p, _c_void_p, _c_void_p]),
     "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _c_void_p,
                            _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_dgates": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
+    "moe4_debug_check": (_int, [_c_void_p]),
     "moe_route_topk": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "moe_route_topk_ws_bytes": (_size, [_i64, _i32, _i32]),
@@ -297,6 +299,23 @@ def moe_unpermute_sum(dxp, inv_perm, T, k):
     rc = lib().moe_unpermute_sum(_p(dxp), _p(inv_perm), T, k, d, _p(dx), _stream())
     _check(rc, "moe_unpermute_sum")
     return dx
+
+
+def moe_dgates(dy, yp, inv_perm, k):
+    """Gate gradient dg [T, k] float32: dg[t, j] = <dy[t], yp[inv_perm[t*k + j]]>."""
+    _dev(dy, torch.bfloat16, "dy")
+    _dev(yp, torch.float32, "yp")
+    _dev(inv_perm, torch.int32, "inv_perm")
+    T, d = dy.shape
+    dg = _empty((T, k), torch.float32, dy)
+    rc = lib().moe_dgates(_p(dy), _p(yp), _p(inv_perm), T, k, d, _p(dg), _stream())
+    _check(rc, "moe_dgates")
+    return dg
+
+
+def moe4_debug_check():
+    """Synchronise the current stream and raise on a failed launch or device error."""
+    _check(lib().moe4_debug_check(_stream()), "moe4_debug_check")
 
 
 def moe_silu_eval(u):

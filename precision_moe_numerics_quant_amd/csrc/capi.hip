@@ -69,3 +69,10 @@ const float* act_tables_device_ptr() {
 
 extern "C" const char* moe4_last_error(void) { return moe4::t_last_error.c_str(); }
 extern "C" const char* moe4_version(void) { return "moe4 0.1 gfx950"; }
+
+extern "C" int moe4_debug_check(void* stream) {
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return moe4::fail(MOE4_EHIP, std::string("moe4_debug_check: ") + hipGetErrorString(e));
+  return MOE4_OK;
+}

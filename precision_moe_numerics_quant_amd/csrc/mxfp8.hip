@@ -161,28 +161,44 @@ __device__ inline uint32_t sr_fp8_into(uint32_t old, float v, uint32_t r, int se
   }
 }
 
-// SR quantisation of one lane's 8 columns x nvalid rows into ob[column][dword]
-// (byte i % 4 of dword i / 4 = row i).  FAST: every element pair index of the
-// block is below 2**32, so the per-pair key is the constant key0.
-template <bool FAST>
-__device__ inline void requant_block(const uint32_t (&cw)[32], const uint32_t (&sb)[32], int nvalid, float S,
+// SR quantisation of one lane's 8 columns x nvalid rows; each group of 4
+// rows leaves as one dword per column (byte i % 4 = row i) through
+// put(k, column, dword), k = row group.  Rows past nvalid are zero codes.
+// FAST: every element pair index of the block is below 2**32, so the
+// per-pair key is the constant key0 and the index arithmetic is 32-bit.
+// FULL: all 32 rows are valid (no row masks).
+template <bool FAST, bool FULL, typename Put>
+__device__ inline void requant_block(const uint32_t (&cw)[32], const uint32_t (&sbp)[8], int nvalid, float S,
                                      const float (&pc)[8], int64_t j0, int64_t jstride, uint32_t base,
-                                     uint32_t key0, uint32_t (&ob)[8][8]) {
+                                     uint32_t key0, Put put) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < nvalid) {
-      float q[8];
-      dequant8(cw[i], sb[i], q);
+  for (int k = 0; k < 8; ++k) {
+    uint32_t od[8];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int64_t j = j0 + (int64_t)i * jstride + p;
-        const uint32_t key = FAST ? key0 : fmix32(base ^ (uint32_t)((uint64_t)j >> 32));
-        const uint32_t word = fmix32((uint32_t)j ^ key);
-        const float v0 = q[2 * p] * S, v1 = q[2 * p + 1] * S;  // fl(fl(q*sc)*S)
-        ob[2 * p][i / 4] = sr_fp8_into(ob[2 * p][i / 4], v0 * pc[2 * p], word << 16, i % 4);
-        ob[2 * p + 1][i / 4] = sr_fp8_into(ob[2 * p + 1][i / 4], v1 * pc[2 * p + 1], word & 0xFFFF0000u, i % 4);
+    for (int q = 0; q < 8; ++q) od[q] = 0u;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * k + ii;
+      if (FULL || i < nvalid) {
+        float q[8];
+        dequant8(cw[i], (sbp[k] >> (8 * ii)) & 0xFFu, q);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          uint32_t word;
+          if (FAST) {
+            word = fmix32(((uint32_t)j0 + (uint32_t)i * (uint32_t)jstride + (uint32_t)p) ^ key0);
+          } else {
+            const int64_t j = j0 + (int64_t)i * jstride + p;
+            word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));
+          }
+          const float v0 = q[2 * p] * S, v1 = q[2 * p + 1] * S;  // fl(fl(q*sc)*S)
+          od[2 * p] = sr_fp8_into(od[2 * p], v0 * pc[2 * p], word << 16, ii);
+          od[2 * p + 1] = sr_fp8_into(od[2 * p + 1], v1 * pc[2 * p + 1], word & 0xFFFF0000u, ii);
+        }
       }
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) put(k, q, od[q]);
   }
 }
 
@@ -221,25 +237,30 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     lblk[w][2] = sbase;
   }
   const int64_t c = c0 + LCOLS * l;
-  uint32_t ob[8][8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ob[q][k] = 0u;
+  // row group k (rows 4k..4k+3 of block w) of column col: dword k % 4 of
+  // 16-byte chunk 2w + k / 4 of the column's LDS run
+  auto put = [&](int k, int q, uint32_t v) {
+    const int col = LCOLS * l + q;
+    *reinterpret_cast<uint32_t*>(lq + col * ROWS + swz(col, 2 * w + (k >> 2)) * 16 + (k & 3) * 4) = v;
+  };
   int ex[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) ex[q] = -127;
   if (nvalid > 0 && c < C) {
-    uint32_t cw[32], sb[32];
+    uint32_t cw[32], sbp[8];  // code words; scale bytes packed 4 rows per register
     const uint8_t* crow = codes + src0 * (C / 2) + c / 2;
     const uint8_t* srow = sf + src0 * (C / 16) + c / 16;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sbp[k] = 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {  // rows past the group repeat its last row and are never used
       const int64_t ri = i < nvalid ? i : nvalid - 1;
       cw[i] = *reinterpret_cast<const uint32_t*>(crow + ri * (C / 2));
-      sb[i] = srow[ri * (C / 16)];
+      sbp[i >> 2] |= (uint32_t)srow[ri * (C / 16)] << (8 * (i & 3));
     }
     const float S = ts[ts_per_group ? g : 0];
+    // block amax of fl(fl(q*sc)*S) per column: fl(max |q*sc| * S), as
+    // rounding a product by S > 0 keeps the order of the exact q*sc
     float am[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) am[q] = 0.0f;
@@ -247,32 +268,34 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     for (int i = 0; i < 32; ++i) {
       if (i < nvalid) {
         float q8[8];
-        dequant8(cw[i], sb[i], q8);
+        dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q8);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q] * S));
+        for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
       }
     }
     float pc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      ex[q] = mx_exponent(am[q]);
+      ex[q] = mx_exponent(am[q] * S);
       pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
     }
     const int64_t j0 = src0 * (C / 2) + c / 2;  // pair index of (row src0, column c)
     const uint32_t key0 = fmix32(base);
-    if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
-      requant_block<true>(cw, sb, nvalid, S, pc, j0, C / 2, base, key0, ob);
+    const bool fast = j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32);
+    if (fast && nvalid == 32)
+      requant_block<true, true>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
+    else if (fast)
+      requant_block<true, false>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
     else
-      requant_block<false>(cw, sb, nvalid, S, pc, j0, C / 2, base, key0, ob);
+      requant_block<false, false>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
+  } else {  // no valid rows (padding block or columns past C): zero codes
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) put(k, q, 0u);
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int col = LCOLS * l + q;
-    *reinterpret_cast<u32x4*>(lq + col * ROWS + swz(col, 2 * w) * 16) = u32x4{ob[q][0], ob[q][1], ob[q][2], ob[q][3]};
-    *reinterpret_cast<u32x4*>(lq + col * ROWS + swz(col, 2 * w + 1) * 16) =
-        u32x4{ob[q][4], ob[q][5], ob[q][6], ob[q][7]};
-    lsf[col * WAVES + w] = (uint8_t)(ex[q] + 127);
-  }
+  for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
   __syncthreads();
 #pragma unroll 4
   for (int it = 0; it < COLS * 8 / THREADS; ++it) {

@@ -277,7 +277,13 @@ __global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__
   const int64_t blk = ((int64_t)blockIdx.x * bpt + it) * ENC_THREADS + threadIdx.x;
   if (blk >= rows * nbr) return;
   const int64_t r = blk / nbr;
-  const int g = group_of_row(goff, G, r);
+  // group of the row: one search per wave (uniform: scalar loads) from the
+  // wave's first row, then a short step forward for lanes past a boundary
+  const int64_t r_wave = (int64_t)__builtin_amdgcn_readfirstlane((int)(r & 0x7FFFFFFF)) |
+                         ((int64_t)__builtin_amdgcn_readfirstlane((int)(r >> 31)) << 31);
+  int g = __builtin_amdgcn_readfirstlane(group_of_row(goff, G, r_wave));
+  if (goff != nullptr && g + 1 < G && (int64_t)goff[g + 1] <= r)  // (goff[g + 1]: a scalar load)
+    while (g + 1 < G && (int64_t)goff[g + 1] <= r) ++g;
   const float S = ts[g];
   float v[16];
   load8<DT, SILU>(x, blk * 16, v, tab);

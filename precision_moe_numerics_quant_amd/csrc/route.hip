@@ -185,6 +185,41 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yp, c
   *reinterpret_cast<u32x2*>(y + t * d + c) = out;
 }
 
+// Gate gradient: dg[t, j] = sum_c dy[t, c] * yp[inv[t*k + j], c], one wave per
+// token.  Lane l takes columns 8 l + 512 i (16-byte bf16 loads of dy, two
+// 16-byte loads of yp), accumulates in float32 in column order, then the
+// wave sums the 64 lane totals in a fixed butterfly order (deterministic).
+__global__ void __launch_bounds__(256) k_dgates(const uint16_t* __restrict__ dy, const float* __restrict__ yp,
+                                                const int32_t* __restrict__ inv, int64_t T, int k, int64_t d,
+                                                int64_t n_rows, float* __restrict__ dg) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  const uint16_t* dyr = dy + t * d;
+  for (int j = 0; j < k; ++j) {
+    int64_t row = inv[t * k + j];
+    row = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+    const float* ypr = yp + row * d;
+    float acc = 0.0f;
+    for (int64_t c = 8 * l; c < d; c += 512) {
+      const u32x4 g = *reinterpret_cast<const u32x4*>(dyr + c);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ypr + c);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ypr + c + 4);
+      acc = acc + bf16_bits_to_f32(g[0] & 0xFFFFu) * a[0];
+      acc = acc + bf16_bits_to_f32(g[0] >> 16) * a[1];
+      acc = acc + bf16_bits_to_f32(g[1] & 0xFFFFu) * a[2];
+      acc = acc + bf16_bits_to_f32(g[1] >> 16) * a[3];
+      acc = acc + bf16_bits_to_f32(g[2] & 0xFFFFu) * b[0];
+      acc = acc + bf16_bits_to_f32(g[2] >> 16) * b[1];
+      acc = acc + bf16_bits_to_f32(g[3] & 0xFFFFu) * b[2];
+      acc = acc + bf16_bits_to_f32(g[3] >> 16) * b[3];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);
+    if (l == 0) dg[t * k + j] = acc;
+  }
+}
+
 }  // namespace moe4
 
 using namespace moe4;
@@ -261,4 +296,15 @@ extern "C" int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int6
   hipLaunchKernelGGL((k_combine<false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), dxp,
                      nullptr, inv_perm, T, k, d, T * k, dx);
   return check_launch("moe_unpermute_sum");
+}
+
+extern "C" int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* inv_perm, int64_t T, int32_t k,
+                          int64_t d, float* dg, void* stream) {
+  MOE4_REQUIRE(T >= 0 && k >= 1 && d > 0 && d % 8 == 0, MOE4_EINVAL, "moe_dgates: bad sizes (d % 8 == 0)");
+  MOE4_REQUIRE(T == 0 || (dy && yp && inv_perm && dg), MOE4_EINVAL, "moe_dgates: NULL pointer");
+  MOE4_REQUIRE(aligned16(dy) && aligned16(yp), MOE4_EALIGN, "moe_dgates: misaligned pointer");
+  if (T == 0) return MOE4_OK;
+  hipLaunchKernelGGL(k_dgates, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, as_stream(stream), dy, yp, inv_perm, T, k,
+                     d, T * k, dg);
+  return check_launch("moe_dgates");
 }

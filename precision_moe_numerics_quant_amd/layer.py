@@ -17,12 +17,13 @@ Backward: g * dy gathered into expert order -> MXFP8 (RNE) row-wise and
 transposed per expert; forward NVFP4 operands -> MXFP8 by the stochastic-
 rounding transposed requantisation (stream 16*layer + role: 0 X, 1 H, 2 W_up,
 3 W_down); dgrad/wgrad grouped GEMMs on native block-scaled MFMA; dU = dH *
-silu'(U) -> MXFP8; un-permuting sum -> dx (bf16).
+silu'(U) -> MXFP8; un-permuting sum -> dx (bf16); gate gradient
+dg[t, j] = <dy[t], Yp[row(t, j)]> (float32).
 """
 import torch
 
 from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, SF_BLOCKS, max_padded_rows, moe_combine, moe_gather_rows,
-               moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
+               moe_dgates, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
                moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
@@ -122,5 +123,7 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     _tick(timer, "B10 up wgrad (MXFP8)")
     dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
     _tick(timer, "B11 un-permute sum")
-    return dict(dx=dx, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
+    dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
+    _tick(timer, "B12 gate gradient")
+    return dict(dx=dx, dg=dg, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
                 du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)

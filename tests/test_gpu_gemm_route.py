@@ -250,3 +250,17 @@ def test_grouped_gemm_wgrad_more_experts_than_offset_staging():
     assert np.isfinite(got).all()
     assert not got[M_list == 0].any()
     gemm_tol_check(got, exact, bound, "wgrad fallback")
+
+
+@pytest.mark.parametrize("T,k,d", [(37, 3, 200), (4, 1, 8), (130, 8, 4096)])
+def test_dgates_tolerance(T, k, d):
+    """dg[t, j] = <dy[t], Yp[inv[t*k + j]]> against the oracle's exact sums."""
+    rng = np.random.default_rng(T + d)
+    inv = rng.permutation(T * k).astype(np.int32)
+    yp = rng.standard_normal((T * k, d)).astype(np.float32)
+    dy_t = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    dy = synth.bf16_bits(dy_t)
+    dg = to_np(m4.moe_dgates(dy_t.cuda(), torch.from_numpy(yp).cuda(), cuda_i32(inv), k)).astype(np.float64)
+    exact = olayer.dgates(dy, yp, inv, k)
+    bound = olayer.dgates(dy & 0x7FFF, np.abs(yp), inv, k)
+    gemm_tol_check(dg, exact, bound, f"dgates T={T} k={k} d={d}")

@@ -67,7 +67,8 @@ def test_layer_config1_end_to_end():
     errs = dict(y=_rel(fmt.bf16_to_f32(to_np(fw["y"])), fmt.bf16_to_f32(ofw["y"])),
                 dx=_rel(fmt.bf16_to_f32(to_np(bw["dx"])), fmt.bf16_to_f32(obw["dx"])),
                 dW_up=_rel(to_np(bw["dW_up"]), obw["dW_up"]),
-                dW_down=_rel(to_np(bw["dW_down"]), obw["dW_down"]))
+                dW_down=_rel(to_np(bw["dW_down"]), obw["dW_down"]),
+                dg=_rel(to_np(bw["dg"]).astype(np.float64), obw["dg"]))
     print(f"U bit-identical fraction {same_u:.5f}; H code bytes identical {h_codes_same:.5f}; rel errors {errs}")
     assert same_u > 0.99 and h_codes_same > 0.98
     # a flipped H code moves one product term by one NVFP4 step; normwise this stays
@@ -228,3 +229,27 @@ def test_weight_quant_and_requant_full_size_sampled(cfg3_route):
         got_s = to_np(wdT[1][F * d * e // 32: F * d * (e + 1) // 32])
         assert_bytes_equal(got_c, cc.reshape(-1), f"W requant codes expert {e}")
         assert_bytes_equal(got_s, ss.reshape(-1), f"W requant scales expert {e}")
+
+
+def test_dgates_full_size_sampled(cfg3_route):
+    """Gate gradient at T=16384, d=4096, k=8 in the benchmark's launch; sampled
+    tokens against the oracle's exact sums."""
+    c, inp, r, idx, gates, P = cfg3_route
+    T, d, k = c["T"], c["d"], c["k"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    yp = torch.randn(T * k, d, device="cuda", generator=g)
+    dy = (torch.randn(T, d, device="cuda", generator=g) * 1e-2).to(torch.bfloat16)
+    dg = to_np(m4.moe_dgates(dy, yp, r["inv_perm"], k)).astype(np.float64)
+    inv = to_np(r["inv_perm"]).astype(np.int64)
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.r_[rng.choice(T, 40, replace=False), 0, T - 1])
+    rows = inv.reshape(T, k)[toks].reshape(-1)
+    dy_s = to_np(dy[torch.from_numpy(toks).cuda()].view(torch.int16)).view(np.uint16)
+    yp_rows = to_np(yp[torch.from_numpy(rows).cuda()])
+    yp_s = np.zeros((len(toks) * k, d), dtype=np.float32)
+    yp_s[:] = yp_rows
+    local_inv = np.arange(len(toks) * k, dtype=np.int32)
+    exact = olayer.dgates(dy_s, yp_s, local_inv, k)
+    bound = olayer.dgates(dy_s & 0x7FFF, np.abs(yp_s), local_inv, k)
+    gemm_tol_check(dg[toks], exact, bound, "dgates")

@@ -95,3 +95,44 @@ def test_backward_shapes_and_wgrad_reference():
         ref = bw["dYp"][r0:r1].astype(np.float64).T @ H[r0:r1]
         rel = np.linalg.norm(bw["dW_down"][e] - ref) / max(np.linalg.norm(ref), 1e-30)
         assert rel < 0.2
+
+
+def test_dgates_one_hot_rows():
+    """Rows of Yp that are (row + 1) times the unit vector e_(row mod d) make
+    dg[t, j] = (row + 1) * dy[t, row mod d], row = inv[t*k + j]: pins the
+    row mapping and the sum without the oracle's own dot product."""
+    rng = np.random.default_rng(3)
+    T, d, k = 50, 24, 3
+    A = T * k
+    inv = rng.permutation(A).astype(np.int32)
+    Yp = np.zeros((A, d), dtype=np.float32)
+    Yp[np.arange(A), np.arange(A) % d] = np.arange(A) + 1.0
+    dy = synth.bf16_bits(torch.randn(T, d).to(torch.bfloat16))
+    dg = layer.dgates(dy, Yp, inv, k)
+    dyf = fmt.bf16_to_f32(dy)
+    rows = inv.reshape(T, k)
+    want = (rows + 1.0) * dyf[np.arange(T)[:, None], rows % d]
+    assert np.array_equal(dg, want.astype(np.float64))
+
+
+def test_dgates_brute_force_and_combine_link():
+    """Plain loops on a tiny case, and sum_j g * dg = <dy, sum_j g * Yp[row]>
+    (the combine's weighted sum before rounding)."""
+    rng = np.random.default_rng(4)
+    T, d, k = 6, 5, 2
+    inv = rng.permutation(T * k).astype(np.int32)
+    Yp = rng.standard_normal((T * k, d)).astype(np.float32)
+    dy = synth.bf16_bits(torch.randn(T, d).to(torch.bfloat16))
+    dyf = fmt.bf16_to_f32(dy)
+    dg = layer.dgates(dy, Yp, inv, k)
+    for t in range(T):
+        for j in range(k):
+            s = 0.0
+            for c in range(d):
+                s += float(dyf[t, c]) * float(Yp[inv[t * k + j], c])
+            assert abs(dg[t, j] - s) <= 1e-12 * (1 + abs(s))
+    g = rng.random((T, k))
+    lhs = (g * dg).sum(axis=1)
+    comb = np.stack([sum(g[t, j] * Yp[inv[t * k + j]].astype(np.float64) for j in range(k)) for t in range(T)])
+    rhs = (dyf.astype(np.float64) * comb).sum(axis=1)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
