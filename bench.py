@@ -3,12 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch: NVFP4 weight
-quantisation of the fp32 masters, routing and permutation, X quantisation
-(4/6), dispatch gather, up GEMM, SiLU + H quantisation (4/6), down GEMM,
-combine; then the backward: gradient MXFP8 quantisation (row-wise and
-transposed), the three SR requantisations of weights and activations (four
-with both weights), dgrad and wgrad grouped GEMMs for both projections, dU
-quantisation with SiLU', un-permuting sum.  Workload: T = 16384 tokens,
+quantisation of the fp32 masters (with, in the same pass, the weights' SR
+transposed MXFP8 copies for the backward), routing and permutation, X
+quantisation (4/6), dispatch gather, up GEMM, SiLU + H quantisation (4/6),
+down GEMM, combine; then the backward: gradient MXFP8 quantisation (row-wise
+and transposed), the SR requantisations of H and X, dgrad and wgrad grouped
+GEMMs for both projections, dU quantisation with SiLU', un-permuting sum,
+gate gradient.  Workload: T = 16384 tokens,
 d = 4096, F = 1536, 384 experts, top-8 routing from N(0,1) logits with a
 Zipf(1.1) expert bias; upstream gradient N(0, 1e-3); synthetic seeded inputs
 resident in HBM before the timed region.
@@ -50,8 +51,9 @@ def work_table(c, off, off_pad):
     gem = 2.0 * A * d * F
     wg_bytes = lambda n1, n2: E * n1 * n2 * 4.0 + (n1 + n2) * Ptot * mxb
     return {
-        "F1 W_up quant": ("hbm", E * F * d * (8.0 + nv)),
-        "F1 W_down quant": ("hbm", E * F * d * (8.0 + nv)),
+        # two fp32 reads (amax, then encode), the NVFP4 write and the backward's MXFP8 copy
+        "F1 W_up quant (+ requant)": ("hbm", E * F * d * (8.0 + nv + mxb)),
+        "F1 W_down quant (+ requant)": ("hbm", E * F * d * (8.0 + nv + mxb)),
         "F2-F3 route + permutation": ("hbm", T * E * 4.0 + A * 16.0),
         "F4 X quant (NVFP4 4/6)": ("hbm", T * d * (4.0 + nv)),
         "F5 dispatch gather": ("hbm", 2.0 * A * d * nv),
@@ -78,7 +80,8 @@ def work_table(c, off, off_pad):
 
 # the library kernel behind each call (several calls may launch one kernel)
 KERNEL_OF = {
-    "F1 W_up quant": "nvfp4 quant (k_amax + k_encode), fp32", "F1 W_down quant": "nvfp4 quant (k_amax + k_encode), fp32",
+    "F1 W_up quant (+ requant)": "k_amax + k_encode_requant_T",
+    "F1 W_down quant (+ requant)": "k_amax + k_encode_requant_T",
     "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
     "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_dma_bf16_128",
     "F8 down GEMM (NVFP4)": "k_gemm_fwd_dma_f32_128",
@@ -94,7 +97,7 @@ KERNEL_OF = {
 
 # calls that launch several kernels (zero, amax, scale, encode; route's
 # four): not candidates for the single dominant kernel
-MULTI_KERNEL_CALLS = {"F1 W_up quant", "F1 W_down quant", "F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)",
+MULTI_KERNEL_CALLS = {"F1 W_up quant (+ requant)", "F1 W_down quant (+ requant)", "F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)",
                       "F7 SiLU + H quant (NVFP4 4/6)"}
 
 # rocprofv3 --pmc summaries (FETCH_SIZE and WRITE_SIZE passes, scaled by a
@@ -180,7 +183,8 @@ def gpu_run(steps, warmup):
         events.append((name, ev))
 
     def step(t=None):
-        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t)
+        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t,
+                           seed=synth.SR_SEED)
         bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED, timer=t)
         return fw, bw
 

@@ -118,6 +118,28 @@ int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
 size_t nvfp4_quant_46_ws_bytes(int32_t n_groups);
 
 /*
+ * nvfp4_quant_requant_T - weights: both low-precision copies in one pass.
+ * Byte for byte the result of nvfp4_quant_46 on float32 x [rows, cols] in
+ * mode MOE4_NVFP4_6 with n_groups equal row groups (one tensor scale each),
+ * followed by mxfp8_requant_sr_T of that result with ts per group, the same
+ * groups and MOE4_SF_ROWS: the forward NVFP4 operand and the backward
+ * transposed MXFP8 operand of a weight matrix (lhc.media page, the paragraphs
+ * on FP32 master weights and on requantising the dequantised, transposed
+ * values with stochastic rounding; agihunt.info page, "Confirmed").
+ * rows = n_groups * R_g with R_g % 32 == 0, so no padding: mx_codes
+ * [cols * rows] holds group g's [cols][R_g] block at cols * g * R_g, mx_sf
+ * [cols * rows / 32] its [cols][R_g / 32] scales at cols * g * R_g / 32.
+ * codes [rows, cols/2], sf [rows, cols/16], tensor_scale [n_groups] as in
+ * nvfp4_quant_46; seed, stream_id as in mxfp8_requant_sr_T.  cols % 32 == 0;
+ * x, codes and mx_codes 16-byte aligned.
+ * ws: nvfp4_quant_requant_T_ws_bytes(n_groups) bytes.
+ */
+int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups,
+                          uint8_t* codes, uint8_t* sf, float* tensor_scale, uint64_t seed, uint32_t stream_id,
+                          uint8_t* mx_codes, uint8_t* mx_sf, void* ws, size_t ws_bytes, void* stream);
+size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups);
+
+/*
  * nvfp4_dequant - float32 values fl(fl(q*sc)*S) of an NVFP4 tensor (test and
  * debugging aid).  ts_per_group = 0: ts[0] applies to every row.
  */
@@ -247,7 +269,8 @@ int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
  * scales (MOE4_SF_BLOCKS), A_e [N1][P_e] (scales [P_e/32][N1]), B_e [N2][P_e]
  * (scales [P_e/32][N2]) with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
  * beta = 0 overwrites (experts with no rows get zeros), beta = 1 accumulates.
- * N1 % 32 == 0, N2 % 32 == 0.
+ * N1 % 32 == 0, N2 % 32 == 0; each expert's operands (N1 * P_e and N2 * P_e
+ * bytes) below 2 GiB (32-bit buffer offsets).
  */
 int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
                                const uint8_t* b_codes, const uint8_t* b_sf,

@@ -36,6 +36,9 @@ _SIGS = {
     "nvfp4_quant_46": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _int, _int, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _size, _c_void_p]),
     "nvfp4_quant_46_ws_bytes": (_size, [_i32]),
+    "nvfp4_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _u64, _u32,
+                                     _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "nvfp4_quant_requant_T_ws_bytes": (_size, [_i32]),
     "nvfp4_dequant": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _i32, _i64, _i64, _c_void_p,
                              _c_void_p]),
     "mxfp8_requant_sr_T": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i32,
@@ -142,6 +145,23 @@ def nvfp4_quant_46(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE):
                               _p(ws), ws.numel(), _stream())
     _check(rc, "nvfp4_quant_46")
     return codes, sf, ts
+
+
+def nvfp4_quant_requant_T(x, n_groups, seed=1, stream_id=0):
+    """Weights [G*R_g, C] float32 -> NVFP4 mode 6 (codes, sf, ts per group) and
+    its transposed MXFP8 SR copy (mx_codes [C*rows], mx_sf [C*rows/32]) in one pass."""
+    _dev(x, torch.float32, "x")
+    R, C = x.shape
+    codes = _empty((R, C // 2), torch.uint8, x)
+    sf = _empty((R, C // 16), torch.uint8, x)
+    ts = _empty((n_groups,), torch.float32, x)
+    mc = _empty((C * R,), torch.uint8, x)
+    ms = _empty((C * R // 32,), torch.uint8, x)
+    ws = _ws(lib().nvfp4_quant_requant_T_ws_bytes(n_groups), x)
+    rc = lib().nvfp4_quant_requant_T(_p(x), R, C, n_groups, _p(codes), _p(sf), _p(ts), seed, stream_id, _p(mc),
+                                     _p(ms), _p(ws), ws.numel(), _stream())
+    _check(rc, "nvfp4_quant_requant_T")
+    return codes, sf, ts, mc, ms
 
 
 def nvfp4_dequant(codes, sf, ts, group_row_off=None, ts_per_group=False):

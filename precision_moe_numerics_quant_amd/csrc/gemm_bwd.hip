@@ -705,7 +705,10 @@ MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_128, 128, 128, 2)
 // while the producers fill stage (g - 1) % S (read by everyone before the
 // barrier) with slab g + S - 1, then wait for slab g + 1 to land.  Both
 // roles walk the same tiles (b, b + grid, ... of the expert-major order) and
-// slab counts, so their barrier counts agree; tiles of experts without
+// slab counts, so their barrier counts agree.  Within an expert the column
+// blocks run fastest, so concurrently running workgroups write whole rows of
+// dW between them (ordering by the larger dimension instead cuts the
+// operands' per-XCD re-fetch but scatters the writes, which measured slower); tiles of experts without
 // tokens are zero-filled by the consumers (beta = 0) without a barrier.
 // K tails, and rows past N1 or N2, come as zeros from out-of-range loads.
 namespace wsg {
@@ -734,6 +737,11 @@ __global__ void __launch_bounds__(wsg::NT, 1)
   __shared__ int32_t s_off[MAX_E + 1];
   // tile indices fit 31 bits (checked at launch): 32-bit index arithmetic
   const uint32_t n_all = (uint32_t)n_all_, n_ntiles = (uint32_t)n_ntiles_, per_e = n_all / (uint32_t)E;
+  // tile rest (within its expert) -> (row block, column block)
+  auto tile_mn = [&](uint32_t rest, uint32_t& mt, uint32_t& nt) {
+    mt = rest / n_ntiles;
+    nt = rest - mt * n_ntiles;
+  };
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i <= E; i += NT) s_off[i] = off[i];
@@ -757,14 +765,16 @@ __global__ void __launch_bounds__(wsg::NT, 1)
         const uint32_t e = pt / per_e, rest = pt - e * per_e;
         const int64_t p0 = off[e], kl = (int64_t)off[e + 1] - p0;
         if (kl == 0) continue;
-        const int64_t r0 = opb ? (int64_t)(rest % n_ntiles) * TN : (int64_t)(rest / n_ntiles) * TM;
+        uint32_t mt, nt;
+        tile_mn(rest, mt, nt);
+        const int64_t r0 = opb ? (int64_t)nt * TN : (int64_t)mt * TM;
         rc = make_rsrc(codes + NR * p0, (uint64_t)NR * kl);
         rs = make_rsrc(sf + NR * p0 / 32, (uint64_t)NR * (kl / 32));
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int row = h * 64 + j * 8 + (l >> 3);
-          const int64_t r = r0 + row < NR ? r0 + row : NR - 1;
-          crow[j] = (uint32_t)(r * kl + 16 * swz(row, l & 7));
+          const uint32_t r = (uint32_t)(r0 + row < NR ? r0 + row : NR - 1);
+          crow[j] = r * (uint32_t)kl + 16u * (uint32_t)swz(row, l & 7);
         }
         // lane l: rows r0 + h * 64 + 4 (l % 16) .. + 3 of K block l / 16 of
         // the slab (block-major scales; NR % 32 == 0 keeps the 4 rows together)
@@ -871,7 +881,8 @@ __global__ void __launch_bounds__(wsg::NT, 1)
   const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * 4;
   for (uint32_t t = blockIdx.x; t < n_all; t += gridDim.x) {
     const uint32_t e = t / per_e, rest = t - e * per_e;
-    const uint32_t mt = rest / n_ntiles, nt = rest - mt * n_ntiles;
+    uint32_t mt, nt;
+    tile_mn(rest, mt, nt);
     const int64_t m0 = (int64_t)mt * TM, c0 = (int64_t)nt * TN;
     const int kl = s_off[e + 1] - s_off[e];
     float* C = dw + (int64_t)e * N1 * N2;

@@ -12,10 +12,15 @@
 //   k_tensor_scale  S_g = fl(amax_g / (m_max * 448)), 1 for a zero group
 //   k_encode        one thread per 16-element block: both candidates, errors
 //                   in the fixed order, the choice, packed codes + scale byte
+// and, for weights, k_encode_requant_T in place of k_encode: the mode-6 codes
+// and, from them, the stochastic-rounding transposed MXFP8 copy the backward
+// pass needs (one pass over the float32 masters instead of two kernels).
 // All float arithmetic is one IEEE binary32 operation per step (the library
 // is built with -ffp-contract=off), with correctly rounded division.
 #include "act.h"
 #include "moe4_internal.h"
+#include "mx_requant.h"
+#include "nvfp4_enc.h"
 
 namespace moe4 {
 
@@ -199,68 +204,6 @@ __global__ void k_tensor_scale(const uint32_t* __restrict__ amax_bits, int G, fl
   ts[g] = (s == 0.0f) ? 1.0f : s;
 }
 
-// E4M3 code (RNE, clamp to 448) of a non-negative finite float.
-__device__ inline uint32_t e4m3_rne_u(float u) {
-  u = fminf(u, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xFFu;
-}
-
-struct Cand {
-  uint32_t sc;      // E4M3 scale byte
-  uint32_t q[2];    // 16 packed nibbles
-  float err;
-};
-
-// One candidate of one 16-block (steps: scale, encode, dequantise, error).
-__device__ inline Cand encode_candidate(const float* x, float amax_b, float S, float m) {
-  Cand c;
-  const float d = m * S;
-  const float u = amax_b / d;
-  c.sc = e4m3_rne_u(u);
-  const float scf = e4m3_to_f32(c.sc);
-  const float eff = scf * S;
-  const bool zero = (c.sc == 0u) || (eff == 0.0f);
-  if (zero) {
-    // every code a signed zero: deq = 0, t = x
-    uint32_t q0 = 0, q1 = 0;
-    float err = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t sgn = (__float_as_uint(x[i]) >> 31) << 3;
-      if (i < 8) q0 |= sgn << (4 * i); else q1 |= sgn << (4 * (i - 8));
-      float t = x[i];
-      err = err + t * t;
-    }
-    c.q[0] = q0; c.q[1] = q1; c.err = err;
-    return c;
-  }
-  const float inv = 1.0f / eff;
-  const bool inv_inf = __builtin_isinf(inv);
-  const float mant = mant_factor(scf);
-  uint32_t q0 = 0, q1 = 0;
-  float err = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    float y0 = x[i] * inv, y1 = x[i + 1] * inv;
-    if (inv_inf) {  // 0 * inf: a zero element stays a signed zero
-      if (x[i] == 0.0f) y0 = x[i];
-      if (x[i + 1] == 0.0f) y1 = x[i + 1];
-    }
-    // E2M1, round to nearest even, saturating, sign kept (scale 1: no rescale)
-    uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
-    if (i < 8) q0 |= pk << (4 * i); else q1 |= pk << (4 * (i - 8));
-    // exact q * 2**floor(log2 sc), times the mantissa 1.m: the exact q * sc
-    f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, scf, 0);
-    float p0 = p[0] * mant, p1 = p[1] * mant;
-    float t0 = x[i] - p0 * S;
-    float t1 = x[i + 1] - p1 * S;
-    err = err + t0 * t0;
-    err = err + t1 * t1;
-  }
-  c.q[0] = q0; c.q[1] = q1; c.err = err;
-  return c;
-}
-
 constexpr int ENC_THREADS = 256;
 
 template <int DT, bool SILU, bool FOUR_OVER_SIX>
@@ -335,6 +278,120 @@ static void launch_encode(bool four6, dim3 grid, hipStream_t s, const void* x, i
   else
     hipLaunchKernelGGL((k_encode<DT, SILU, false>), grid, dim3(ENC_THREADS), 0, s, x, rows, cols, goff, G, ts,
                        codes, sf, tab, bpt);
+}
+
+// Group offsets g * grows of G equal groups (the amax walk takes offsets).
+__global__ void k_uniform_offsets(int32_t* __restrict__ off, int G, int64_t grows) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g <= G) off[g] = (int32_t)(g * grows);
+}
+
+// Weights, fused: float32 [G * grows, C] -> NVFP4 mode 6 (codes, scales; the
+// tensor scales come from the amax pass) and, from the same codes and the
+// same steps as k_requant_T, the transposed MXFP8 stochastic-rounding copy
+// (group-major, grows rows per group, no padding, row-major scales).  Tiling
+// as k_requant_T: 4 waves x (32 rows = one MX block) x 512 columns; lane l of
+// wave w takes columns c0 + 8l .. c0 + 8l + 7 of the wave's 32 rows, so lanes
+// 2m and 2m+1 hold one 16-element NVFP4 block (its amax through one shuffle)
+// and each lane keeps its 32 code words for the requantisation.  Rows are
+// read in groups of 4 with the next group's loads in flight.
+__global__ void __launch_bounds__(rq::THREADS) k_encode_requant_T(const float* __restrict__ x, int64_t C,
+                                                                  int64_t grows, int G, int64_t n_ct,
+                                                                  const float* __restrict__ ts, uint32_t base,
+                                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+                                                                  uint8_t* __restrict__ out_c,
+                                                                  uint8_t* __restrict__ out_s) {
+  using namespace rq;
+  __shared__ __attribute__((aligned(16))) uint8_t lq[COLS * ROWS];
+  __shared__ uint8_t lsf[COLS * WAVES];  // [column][block]
+  __shared__ int64_t lblk[WAVES][3];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * COLS;
+  const int64_t r0 = ((int64_t)(blockIdx.x / n_ct) * WAVES + w) * 32;  // the wave's first row
+  const bool present = r0 < grows * G;
+  const int g = present ? (int)(r0 / grows) : 0;
+  const int64_t pr_in_g = r0 - (int64_t)g * grows;
+  if (l == 0) {
+    lblk[w][0] = C * (int64_t)g * grows + pr_in_g;
+    lblk[w][1] = present ? grows : 0;
+    lblk[w][2] = C * (int64_t)g * grows / 32 + pr_in_g / 32;
+  }
+  const int64_t c = c0 + LCOLS * l;
+  auto put = [&](int k, int q, uint32_t v) {
+    const int col = LCOLS * l + q;
+    *reinterpret_cast<uint32_t*>(lq + col * ROWS + swz(col, 2 * w + (k >> 2)) * 16 + (k & 3) * 4) = v;
+  };
+  int ex[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ex[q] = -127;
+  if (present && c < C) {  // (C % 16 == 0: both lanes of a 16-block agree)
+    const float S = ts[g];
+    const float* xr = x + r0 * C + c;
+    uint32_t cw[32], sbp[8];
+    float am[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sbp[k] = 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am[q] = 0.0f;
+    f32x4 vb[2][4][2];
+    auto load_group = [&](int k, f32x4 (&b)[4][2]) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(xr + (int64_t)(4 * k + ii) * C);
+        b[ii][0] = p[0];
+        b[ii][1] = p[1];
+      }
+    };
+    load_group(0, vb[0]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k + 1 < 8) load_group(k + 1, vb[(k + 1) & 1]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * k + ii;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = vb[k & 1][ii][0][e];
+          v[4 + e] = vb[k & 1][ii][1][e];
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));  // the block's other half
+        uint32_t sc;
+        cw[i] = encode_half(v, a, S, 6.0f, sc);
+        sbp[k] |= sc << (8 * ii);
+        *reinterpret_cast<uint32_t*>(codes + (r0 + i) * (C / 2) + c / 2) = cw[i];
+        if ((l & 1) == 0) sf[(r0 + i) * (C / 16) + c / 16] = (uint8_t)sc;
+        float q8[8];
+        dequant8(cw[i], sc, q8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
+      }
+    }
+    float pc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ex[q] = mx_exponent(am[q] * S);
+      pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
+    }
+    const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
+    const uint32_t key0 = fmix32(base);
+    if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
+      requant_block<true, true>(cw, sbp, 32, S, pc, j0, C / 2, base, key0, put);
+    else
+      requant_block<false, true>(cw, sbp, 32, S, pc, j0, C / 2, base, key0, put);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) put(k, q, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
+  __syncthreads();
+  rq_store_tile(lq, lsf, lblk, c0, C, 0, out_c, out_s);
 }
 
 __global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
@@ -425,6 +482,46 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
       launch_encode<MOE4_F32, false>(four6, grid, s, x, rows, cols, group_row_off, G, tensor_scale, codes, sf, tab);
   }
   return check_launch("nvfp4_quant_46");
+}
+
+extern "C" size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups) {
+  const size_t g = (size_t)(n_groups > 0 ? n_groups : 1);
+  return (g * sizeof(uint32_t) + 15) / 16 * 16 + (g + 1) * sizeof(int32_t);
+}
+
+extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint8_t* codes,
+                                     uint8_t* sf, float* tensor_scale, uint64_t seed, uint32_t stream_id,
+                                     uint8_t* mx_codes, uint8_t* mx_sf, void* ws, size_t ws_bytes, void* stream) {
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL,
+               "nvfp4_quant_requant_T: cols must be a positive multiple of 32");
+  MOE4_REQUIRE(n_groups >= 1 && rows % n_groups == 0 && (rows / n_groups) % 32 == 0, MOE4_EINVAL,
+               "nvfp4_quant_requant_T: rows must split into n_groups equal groups of a multiple of 32 rows");
+  MOE4_REQUIRE(rows / n_groups < ((int64_t)1 << 31) / 2 && rows < ((int64_t)1 << 31), MOE4_EINVAL,
+               "nvfp4_quant_requant_T: too many rows");
+  MOE4_REQUIRE(tensor_scale && ws, MOE4_EINVAL, "nvfp4_quant_requant_T: NULL pointer");
+  MOE4_REQUIRE(rows == 0 || (x && codes && sf && mx_codes && mx_sf), MOE4_EINVAL, "nvfp4_quant_requant_T: NULL pointer");
+  MOE4_REQUIRE(aligned16(x) && aligned16(codes) && aligned16(mx_codes), MOE4_EALIGN,
+               "nvfp4_quant_requant_T: x, codes and mx_codes must be 16-byte aligned");
+  MOE4_REQUIRE(ws_bytes >= nvfp4_quant_requant_T_ws_bytes(n_groups), MOE4_EWORKSPACE,
+               "nvfp4_quant_requant_T: workspace too small");
+  hipStream_t s = as_stream(stream);
+  const int G = n_groups;
+  const int64_t grows = rows / G;
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  int32_t* off = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ((size_t)G * sizeof(uint32_t) + 15) / 16 * 16);
+  hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
+  hipLaunchKernelGGL(k_uniform_offsets, dim3((G + 1 + 255) / 256), dim3(256), 0, s, off, G, grows);
+  if (rows > 0)
+    hipLaunchKernelGGL((k_amax<MOE4_F32, false>), walk_grid(rows * cols), dim3(QTHREADS), 0, s, x, rows, cols, off, G,
+                       amax, nullptr);
+  hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, 6.0f * 448.0f, tensor_scale);
+  if (rows > 0) {
+    const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (rows + rq::ROWS - 1) / rq::ROWS;
+    MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "nvfp4_quant_requant_T: tensor too large");
+    hipLaunchKernelGGL(k_encode_requant_T, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, s, x, cols, grows, G,
+                       n_ct, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
+  }
+  return check_launch("nvfp4_quant_requant_T");
 }
 
 extern "C" int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,

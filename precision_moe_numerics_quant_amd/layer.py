@@ -24,7 +24,7 @@ import torch
 
 from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, SF_BLOCKS, max_padded_rows, moe_combine, moe_gather_rows,
                moe_dgates, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
-               moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46)
+               moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
@@ -34,8 +34,10 @@ def _tick(timer, name):
         timer(name)
 
 
-def quantize_weights(w_up, w_down, timer=None):
-    """NVFP4 (mode 6) of the fp32 masters, one tensor scale per expert matrix.
+def quantize_weights(w_up, w_down, timer=None, seed=1, layer=0):
+    """NVFP4 (mode 6) of the fp32 masters, one tensor scale per expert matrix,
+    and in the same pass the backward's transposed MXFP8 SR copies (wuT, wdT;
+    SR stream 16*layer + role, as the backward would requantise them).
 
     ``timer``, if given, is called with a step name after each library call
     (the benchmark records a HIP event there)."""
@@ -44,19 +46,21 @@ def quantize_weights(w_up, w_down, timer=None):
     off_f = torch.arange(E + 1, dtype=torch.int32, device=dev) * F
     off_d = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
     _tick(timer, None)
-    wu = nvfp4_quant_46(w_up.view(E * F, d), NVFP4_6, off_f)
-    _tick(timer, "F1 W_up quant")
-    wd = nvfp4_quant_46(w_down.view(E * d, F), NVFP4_6, off_d)
-    _tick(timer, "F1 W_down quant")
-    return dict(wu=wu, wd=wd, off_f=off_f, off_d=off_d, shape=(E, F, d))
+    u = nvfp4_quant_requant_T(w_up.view(E * F, d), E, seed, 16 * layer + ROLE_WUP)
+    _tick(timer, "F1 W_up quant (+ requant)")
+    dn = nvfp4_quant_requant_T(w_down.view(E * d, F), E, seed, 16 * layer + ROLE_WDOWN)
+    _tick(timer, "F1 W_down quant (+ requant)")
+    return dict(wu=u[:3], wd=dn[:3], wuT=u[3:], wdT=dn[3:], sr=(seed, layer), off_f=off_f, off_d=off_d,
+                shape=(E, F, d))
 
 
-def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None):
-    """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32."""
+def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0):
+    """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32.
+    (seed, layer): the SR key of the weights' backward copies made here."""
     T, d = x.shape
     E, F, _ = w_up.shape
     if wq is None:
-        wq = quantize_weights(w_up, w_down, timer)
+        wq = quantize_weights(w_up, w_down, timer, seed, layer)
     _tick(timer, None)
     r = moe_route_topk(logits, k, bias)
     _tick(timer, "F2-F3 route + permutation")
@@ -95,8 +99,11 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     _tick(timer, "B1 dY quant transposed (MXFP8)")
     wq = fw["wq"]
     wd_c, wd_s, wd_t = wq["wd"]
-    wdT = mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, seed, sid(ROLE_WDOWN), max_pr=E * d)
-    _tick(timer, "B2 W_down requant SR-T")
+    if wq.get("sr") == (seed, layer):  # requantised with the forward's weight quantisation
+        wdT = wq["wdT"]
+    else:
+        wdT = mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, seed, sid(ROLE_WDOWN), max_pr=E * d)
+        _tick(timer, "B2 W_down requant SR-T")
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
     _tick(timer, "B3 down dgrad (MXFP8)")
     hq = fw["hq"]
@@ -111,8 +118,11 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
                          max_pr=mpr, sf_layout=SF_BLOCKS)
     _tick(timer, "B6 SiLU' + dU quant transposed")
     wu_c, wu_s, wu_t = wq["wu"]
-    wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
-    _tick(timer, "B7 W_up requant SR-T")
+    if wq.get("sr") == (seed, layer):
+        wuT = wq["wuT"]
+    else:
+        wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
+        _tick(timer, "B7 W_up requant SR-T")
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")
     xp = fw["xq_perm"]

@@ -34,7 +34,7 @@ def test_layer_config1_end_to_end():
     inp = synth.config_inputs(1, device="cpu")
     k = 2
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
-    fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k)
+    fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k, seed=synth.SR_SEED)
     bw = layer.backward(fw, dev["dy"], seed=synth.SR_SEED)
     x = synth.bf16_bits(inp["x"])
     ofw = olayer.forward(x, synth.f32_np(inp["w_up"]), synth.f32_np(inp["w_down"]), synth.f32_np(inp["logits"]), k)
@@ -208,13 +208,16 @@ def test_wgrad_gemm_full_size_sampled(cfg3_route):
 
 def test_weight_quant_and_requant_full_size_sampled(cfg3_route):
     """W_down [384, 4096, 1536] fp32 -> NVFP4 (mode 6, per expert) -> MXFP8 SR
-    transposed, in the benchmark's launches; sampled experts bit-exact."""
+    transposed, in the benchmark's launches (the fused weight pass and the
+    separate requantisation); sampled experts bit-exact."""
     c, inp, r, idx, gates, P = cfg3_route
     E, d, F = c["E"], c["d"], c["F"]
     w = inp["w_down"]
     wq = layer.quantize_weights(inp["w_up"], w)
     wd_c, wd_s, wd_t = wq["wd"]
     wdT = m4.mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, 1, 3, max_pr=E * d)
+    # the fused pass's copy equals the separate requantisation, whole tensor
+    assert torch.equal(wq["wdT"][0], wdT[0]) and torch.equal(wq["wdT"][1], wdT[1])
     for e in (0, 17, E - 1):
         we = synth.f32_np(w[e])
         q = nv.nvfp4_quantize(we, 6)

@@ -311,3 +311,33 @@ def test_run_twice_deterministic():
     r2 = m4.mxfp8_requant_sr_T(a[0], a[1], a[2], off, cuda_i32([0, 320]), True, 1, 0)
     n = 512 * 320      # the written extent; the buffers are sized by the padded upper bound
     assert torch.equal(r1[0][:n], r2[0][:n]) and torch.equal(r1[1][:n // 32], r2[1][:n // 32])
+
+
+@pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96)])
+def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
+    """nvfp4_quant_requant_T equals nvfp4_quant_46 (mode 6, G equal groups)
+    followed by mxfp8_requant_sr_T (row-major scales), byte for byte, against
+    the oracle's two steps."""
+    R = G * Rg
+    rng = np.random.default_rng(G * 1000 + C)
+    w = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
+    w[rng.random((R, C)) < 0.002] *= 40.0                       # outliers
+    w[Rg:2 * Rg] *= 0.0 if G > 2 else 1.0                        # an all-zero group
+    off = np.arange(G + 1) * Rg
+    q = nv.nvfp4_quantize(w, nv.MODE_6, off)
+    mc_ref, ms_ref = mx.requant_sr_t(q["codes"], q["sf"], q["ts"], off, True, seed=7, stream_id=19)
+    codes, sf, ts, mc, ms = m4.nvfp4_quant_requant_T(torch.from_numpy(w).cuda(), G, seed=7, stream_id=19)
+    assert_bytes_equal(to_np(codes), q["codes"], "codes")
+    assert_bytes_equal(to_np(sf), q["sf"], "scales")
+    assert_bytes_equal(to_np(ts).view(np.uint32), np.asarray(q["ts"], dtype=np.float32).view(np.uint32), "ts")
+    assert_bytes_equal(to_np(mc), mc_ref, "mx codes")
+    assert_bytes_equal(to_np(ms), ms_ref, "mx scales")
+
+
+def test_fused_weight_quant_rejects_bad_shapes():
+    w = torch.zeros(64, 48, device="cuda")
+    with pytest.raises(m4.Moe4Error):
+        m4.nvfp4_quant_requant_T(w, 2)                               # cols % 32 != 0
+    w = torch.zeros(96, 64, device="cuda")
+    with pytest.raises(m4.Moe4Error):
+        m4.nvfp4_quant_requant_T(w, 2)                               # groups of 48 rows
