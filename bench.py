@@ -9,7 +9,7 @@ quantisation (4/6), dispatch gather, up GEMM, SiLU + H quantisation (4/6),
 down GEMM, combine; then the backward: gradient MXFP8 quantisation (row-wise
 and transposed), the SR requantisations of H and X, dgrad and wgrad grouped
 GEMMs for both projections, dU quantisation with SiLU', un-permuting sum,
-gate gradient.  Workload: T = 16384 tokens,
+gate gradient and the router backward into the logits.  Workload: T = 16384 tokens,
 d = 4096, F = 1536, 384 experts, top-8 routing from N(0,1) logits with a
 Zipf(1.1) expert bias; upstream gradient N(0, 1e-3); synthetic seeded inputs
 resident in HBM before the timed region.
@@ -75,6 +75,7 @@ def work_table(c, off, off_pad):
         "B10 up wgrad (MXFP8)": ("fp8", gem, wg_bytes(F, d)),
         "B11 un-permute sum": ("hbm", A * d * 4.0 + T * d * 2.0),
         "B12 gate gradient": ("hbm", A * d * 4.0 + T * d * 2.0 + A * 8.0),
+        "B13 router backward": ("hbm", T * E * 4.0 + A * 12.0),
     }
 
 
@@ -93,6 +94,7 @@ KERNEL_OF = {
     "B5 down wgrad (MXFP8)": "k_wgrad_ws", "B10 up wgrad (MXFP8)": "k_wgrad_ws",
     "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
     "B11 un-permute sum": "k_combine (unpermute)", "B12 gate gradient": "k_dgates",
+    "B13 router backward": "k_route_backward",
 }
 
 # calls that launch several kernels (zero, amax, scale, encode; route's

@@ -224,6 +224,21 @@ int moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,
 size_t moe_route_topk_ws_bytes(int64_t T, int32_t E, int32_t k);
 
 /*
+ * moe_route_backward - gradient in the router logits from the gate gradient
+ * (moe_dgates): the gates of moe_route_topk are a softmax of z = logit + bias
+ * over the k selected experts, so for token t, slot j (expert e_j = topk_idx[t,j]):
+ *   s = 0; for i = 0..k-1: s = fl(s + fl(g_i * dg_i));
+ *   dlogits[t, e_j] = fl(g_j * fl(dg_j - s)),  dlogits[t, e] = 0 otherwise
+ * (float32, no fused multiply-add; the top-k choice itself has no gradient).
+ * The routing itself is the local stand-in for the pages' 8-of-384 routing
+ * (fourweekmba.com page, "Update").  dg, gates [T, k] float32, topk_idx
+ * [T, k] int32 (distinct experts per token), dlogits [T, E] float32 out.
+ * 1 <= k <= min(E, 16).
+ */
+int moe_route_backward(const float* dg, const float* gates, const int32_t* topk_idx, int64_t T, int32_t E,
+                       int32_t k, float* dlogits, void* stream);
+
+/*
  * moe_gather_rows - NVFP4 dispatch: out row r = source row perm[r] / k (codes
  * and block scales; the tensor scale is shared).  The local stand-in for the
  * pages' NVFP4 dispatch (lhc.media page, paragraph on communication).

@@ -38,6 +38,8 @@ stochastic rounding, stream id 16 * layer + role, role 0 = X_T, 1 = H_T,
 12. dg[t, j] = <dy[t], Yp[row(t, j)]>: the gate gradient, the derivative of the
     combine's weighted sum in g[t, j] (exact here; a float32 sum of d products
     in the library)
+13. dlogits = route_backward(fl32(dg), g, idx): the softmax backward over each
+    token's selected experts (route.py)
 
 The transposed operands of the weight-gradient products (dYp_col, H_T, dU_col,
 X_T) keep their scales block-major (SF_BLOCKS), the requantised weights
@@ -158,7 +160,8 @@ def backward(fw, dy_bf16, seed=1, layer=0):
     dW_up = gemm.wgrad(dUc, XT).astype(np.float32)
     dx = unpermute_sum(dXp, inv, T, k)
     dg = dgates(dy_bf16, fw["Yp"], inv, k)
-    return dict(dg=dg, dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),
+    dlogits = route.route_backward(dg.astype(np.float32), fw["gates"], fw["idx"], E)
+    return dict(dg=dg, dlogits=dlogits, dYp=dYp, dy_row=(dy_row_c, dy_row_s), dy_col=(dy_col_c, dy_col_s),
                 wdT=(wdT_c, wdT_s), dH=dH, hT=(hT_c, hT_s), dW_down=dW_down, dU=dU,
                 du_row=(du_row_c, du_row_s), du_col=(du_col_c, du_col_s), wuT=(wuT_c, wuT_s),
                 dXp=dXp, xT=(xT_c, xT_s), dW_up=dW_up, dx=dx)

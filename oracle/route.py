@@ -17,6 +17,14 @@ expert-grouped matrices are ordered by (expert ascending, token ascending),
 i.e. a stable counting sort of the assignments by expert.  off[e] is the
 number of assignments to experts below e; off_pad[e] sums pad32 of the counts;
 perm[row] = a and inv_perm[a] = row.
+
+Router backward (not on the pages either; the derivative of the gates above):
+the gates are a softmax of z over the selected set, so with dg[t, j] the
+gradient of the loss in g[t, j], dz[t, e_j] = g_j * (dg_j - sum_i g_i * dg_i)
+for the k selected experts e_j and 0 for the others (the top-k selection has
+no gradient).  In float32, one operation at a time: s = 0; for i = 0..k-1:
+s = fl(s + fl(g_i * dg_i)); dz_j = fl(g_j * fl(dg_j - s)).  Since z = logit +
+bias, this is also the gradient in the logits.
 """
 import numpy as np
 
@@ -71,3 +79,20 @@ def permutation(idx, E):
         inv[a] = row
     return dict(off=off.astype(np.int32), off_pad=off_pad.astype(np.int32),
                 perm=perm.astype(np.int32), inv_perm=inv.astype(np.int32))
+
+
+def route_backward(dg, gates, idx, E):
+    """dlogits [T, E] float32 from dg [T, k] (gradient in the gates), the
+    forward's gates [T, k] and top-k indices idx [T, k]."""
+    dg = np.asarray(dg, dtype=np.float32)
+    gates = np.asarray(gates, dtype=np.float32)
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = gates.shape
+    out = np.zeros((T, E), dtype=np.float32)
+    for t in range(T):
+        s = F32(0.0)
+        for i in range(k):
+            s = F32(s + F32(gates[t, i] * dg[t, i]))
+        for j in range(k):
+            out[t, idx[t, j]] = F32(gates[t, j] * F32(dg[t, j] - s))
+    return out

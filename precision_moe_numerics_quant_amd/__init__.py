@@ -45,6 +45,7 @@ _SIGS = {
                                   _i64, _u64, _u32, _int, _c_void_p, _c_void_p, _c_void_p]),
     "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _c_void_p,
                            _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_route_backward": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_dgates": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe4_debug_check": (_int, [_c_void_p]),
     "moe_route_topk": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -331,6 +332,18 @@ def moe_dgates(dy, yp, inv_perm, k):
     rc = lib().moe_dgates(_p(dy), _p(yp), _p(inv_perm), T, k, d, _p(dg), _stream())
     _check(rc, "moe_dgates")
     return dg
+
+
+def moe_route_backward(dg, gates, topk_idx, E):
+    """dlogits [T, E] float32: softmax backward over each token's selected experts."""
+    _dev(dg, torch.float32, "dg")
+    _dev(gates, torch.float32, "gates")
+    _dev(topk_idx, torch.int32, "topk_idx")
+    T, k = gates.shape
+    out = _empty((T, E), torch.float32, gates)
+    rc = lib().moe_route_backward(_p(dg), _p(gates), _p(topk_idx), T, E, k, _p(out), _stream())
+    _check(rc, "moe_route_backward")
+    return out
 
 
 def moe4_debug_check():

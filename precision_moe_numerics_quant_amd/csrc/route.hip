@@ -220,6 +220,29 @@ __global__ void __launch_bounds__(256) k_dgates(const uint16_t* __restrict__ dy,
   }
 }
 
+// Router backward: the gates are a softmax of z over the selected experts,
+// so dz[t, e_j] = g_j * (dg_j - s), s = sum_i g_i * dg_i (float32, in slot
+// order, no fused multiply-add), and 0 for the experts not selected.  One
+// wave per token; lane l writes experts l, l + 64, ... (one store each).
+__global__ void __launch_bounds__(256) k_route_backward(const float* __restrict__ dg, const float* __restrict__ gates,
+                                                        const int32_t* __restrict__ idx, int64_t T, int E, int k,
+                                                        float* __restrict__ dz) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* g = gates + t * k;
+  const float* d = dg + t * k;
+  const int32_t* ix = idx + t * k;
+  float s = 0.0f;
+  for (int i = 0; i < k; ++i) s = s + g[i] * d[i];
+  for (int e = l; e < E; e += 64) {
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j)
+      if (ix[j] == e) v = g[j] * (d[j] - s);
+    dz[t * E + e] = v;
+  }
+}
+
 }  // namespace moe4
 
 using namespace moe4;
@@ -307,4 +330,15 @@ extern "C" int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* in
   hipLaunchKernelGGL(k_dgates, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, as_stream(stream), dy, yp, inv_perm, T, k,
                      d, T * k, dg);
   return check_launch("moe_dgates");
+}
+
+extern "C" int moe_route_backward(const float* dg, const float* gates, const int32_t* topk_idx, int64_t T, int32_t E,
+                                  int32_t k, float* dlogits, void* stream) {
+  MOE4_REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= MAXK && k <= E, MOE4_EINVAL,
+               "moe_route_backward: need T >= 0, 1 <= k <= min(E, 16)");
+  MOE4_REQUIRE(T == 0 || (dg && gates && topk_idx && dlogits), MOE4_EINVAL, "moe_route_backward: NULL pointer");
+  if (T == 0) return MOE4_OK;
+  hipLaunchKernelGGL(k_route_backward, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, as_stream(stream), dg, gates,
+                     topk_idx, T, E, k, dlogits);
+  return check_launch("moe_route_backward");
 }

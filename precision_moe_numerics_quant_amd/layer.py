@@ -18,12 +18,13 @@ transposed per expert; forward NVFP4 operands -> MXFP8 by the stochastic-
 rounding transposed requantisation (stream 16*layer + role: 0 X, 1 H, 2 W_up,
 3 W_down); dgrad/wgrad grouped GEMMs on native block-scaled MFMA; dU = dH *
 silu'(U) -> MXFP8; un-permuting sum -> dx (bf16); gate gradient
-dg[t, j] = <dy[t], Yp[row(t, j)]> (float32).
+dg[t, j] = <dy[t], Yp[row(t, j)]> (float32) and its softmax backward into the
+router logits.
 """
 import torch
 
 from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, SF_BLOCKS, max_padded_rows, moe_combine, moe_gather_rows,
-               moe_dgates, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
+               moe_dgates, moe_route_backward, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
                moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
@@ -135,5 +136,7 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     _tick(timer, "B11 un-permute sum")
     dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
     _tick(timer, "B12 gate gradient")
-    return dict(dx=dx, dg=dg, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
+    dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
+    _tick(timer, "B13 router backward")
+    return dict(dx=dx, dg=dg, dlogits=dlogits, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
                 du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)

@@ -29,7 +29,7 @@ def test_header_declares_the_named_calls():
     names = declared_functions()
     for n in ("nvfp4_quant_46", "nvfp4_quant_requant_T", "mxfp8_requant_sr_T", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
               "moe_grouped_gemm_bwd_dgrad", "moe_grouped_gemm_bwd_wgrad", "moe_route_topk", "mxfp8_quant",
-              "moe_dgates", "moe4_debug_check"):
+              "moe_dgates", "moe_route_backward", "moe4_debug_check"):
         assert n in names
 
 

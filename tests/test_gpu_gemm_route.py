@@ -264,3 +264,16 @@ def test_dgates_tolerance(T, k, d):
     exact = olayer.dgates(dy, yp, inv, k)
     bound = olayer.dgates(dy & 0x7FFF, np.abs(yp), inv, k)
     gemm_tol_check(dg, exact, bound, f"dgates T={T} k={k} d={d}")
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 384, 8), (5, 4, 1), (64, 1024, 16), (77, 40, 5)])
+def test_route_backward_bit_exact(T, E, k):
+    """Softmax backward into the logits: the library's float32 steps equal the
+    oracle's, bit for bit, on the forward's own gates and indices."""
+    rng = np.random.default_rng(T * 7 + E)
+    logits = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32))
+    r = m4.moe_route_topk(logits.cuda(), k)
+    dg = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32))
+    got = to_np(m4.moe_route_backward(dg.cuda(), r["gates"], r["idx"], E))
+    want = route.route_backward(dg.numpy(), to_np(r["gates"]), to_np(r["idx"]), E)
+    assert_bytes_equal(got.view(np.uint32), want.view(np.uint32), "dlogits")

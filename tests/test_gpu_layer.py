@@ -68,7 +68,8 @@ def test_layer_config1_end_to_end():
                 dx=_rel(fmt.bf16_to_f32(to_np(bw["dx"])), fmt.bf16_to_f32(obw["dx"])),
                 dW_up=_rel(to_np(bw["dW_up"]), obw["dW_up"]),
                 dW_down=_rel(to_np(bw["dW_down"]), obw["dW_down"]),
-                dg=_rel(to_np(bw["dg"]).astype(np.float64), obw["dg"]))
+                dg=_rel(to_np(bw["dg"]).astype(np.float64), obw["dg"]),
+                dlogits=_rel(to_np(bw["dlogits"]).astype(np.float64), obw["dlogits"]))
     print(f"U bit-identical fraction {same_u:.5f}; H code bytes identical {h_codes_same:.5f}; rel errors {errs}")
     assert same_u > 0.99 and h_codes_same > 0.98
     # a flipped H code moves one product term by one NVFP4 step; normwise this stays

@@ -146,3 +146,45 @@ def test_wgrad_shapes_and_empty_expert():
     dw = gemm.wgrad(A, B)
     assert dw.shape == (3, 4, 3) and not dw[1].any()
     assert np.allclose(dw[2], A[2] @ B[2].T)
+
+
+def test_route_backward_matches_finite_differences():
+    """The router backward against central differences of a float64 softmax
+    over the selected experts (the function whose derivative it is), with
+    the loss L = sum_j dg_j * g_j(z)."""
+    rng = np.random.default_rng(12)
+    T, E, k = 20, 9, 4
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, gates = route.topk_gates(logits, k)
+    dg = rng.standard_normal((T, k)).astype(np.float32)
+    dz = route.route_backward(dg, gates, idx, E)
+    h = 1e-6
+    for t in range(T):
+        sel = idx[t].astype(np.int64)
+        zt = logits[t].astype(np.float64)
+
+        def loss(z):
+            w = np.exp(z[sel] - z[sel].max())
+            return float(np.dot(dg[t].astype(np.float64), w / w.sum()))
+        for e in range(E):
+            zp, zm = zt.copy(), zt.copy()
+            zp[e] += h
+            zm[e] -= h
+            fd = (loss(zp) - loss(zm)) / (2 * h)
+            # float32 gates and sums: agreement to a few float32 ulps of the terms
+            assert abs(dz[t, e] - fd) <= 1e-5 * (1 + np.abs(dg[t]).sum()), (t, e, dz[t, e], fd)
+        assert not dz[t][np.setdiff1d(np.arange(E), sel)].any()       # unselected experts: exactly 0
+
+
+def test_route_backward_shift_invariance_and_k1():
+    """Softmax gradients sum to zero over the selected set (up to float32
+    rounding); with k = 1 the single gate is 1 and its gradient is exactly 0."""
+    rng = np.random.default_rng(13)
+    logits = rng.standard_normal((30, 12)).astype(np.float32)
+    idx, gates = route.topk_gates(logits, 5)
+    dg = rng.standard_normal((30, 5)).astype(np.float32)
+    dz = route.route_backward(dg, gates, idx, 12)
+    assert np.all(np.abs(dz.sum(axis=1)) <= 1e-5 * (1 + np.abs(dg).sum(axis=1)))
+    idx1, g1 = route.topk_gates(logits, 1)
+    assert np.all(g1 == 1.0)
+    assert not route.route_backward(dg[:, :1], g1, idx1, 12).any()
