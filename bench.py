@@ -272,11 +272,12 @@ def copy_calibration(n_bytes=1 << 30, reps=3):
 
 def cpu_baseline():
     """The oracle on a bounded sample of the same workload: the expert layer's
-    forward + backward for the first 512 tokens routed top-2 among the first 2
-    experts (d = 4096, F = 1536 full size), timed on this host's cores."""
+    forward + backward for the first 1024 tokens routed top-2 among the first 2
+    experts (d = 4096, F = 1536 full size), timed on this host's cores (about
+    10-15 s of CPU work)."""
     from oracle import layer as olayer
     c = synth.CONFIGS[CFG_ID]
-    Ts, Es, ks = 512, 2, 2
+    Ts, Es, ks = 1024, 2, 2
     full = synth.layer_inputs(Ts, c["d"], c["F"], Es, ks, device="cpu", seed=0, zipf=c["zipf"])
     x = synth.bf16_bits(full["x"])
     wu, wd = synth.f32_np(full["w_up"]), synth.f32_np(full["w_down"])
