@@ -14,6 +14,10 @@ d = 4096, F = 1536, 384 experts, top-8 routing from N(0,1) logits with a
 Zipf(1.1) expert bias; upstream gradient N(0, 1e-3); synthetic seeded inputs
 resident in HBM before the timed region.
 
+The same layer with an MXFP8 forward (the pages' higher-precision layers,
+and their full-MXFP8 baseline) is timed on the same inputs afterwards and
+reported under `mxfp8_forward_variant`.
+
 Printed: one JSON line.  `value` is the step's grouped-GEMM work (6 GEMMs,
 2*M*N*K each, padding excluded) divided by the whole step time; the
 per-call breakdown (HIP events recorded on the stream the library launches
@@ -219,7 +223,30 @@ def gpu_run(steps, warmup):
         prev = ev
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
-    return c, ms_step, wall, per, off, off_pad
+    del fw, bw
+    # the MXFP8-forward variant of the same layer on the same inputs
+    def step_mx(t=None):
+        fw = layer.forward_mx(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t)
+        layer.backward_mx(fw, inp["dy"], seed=synth.SR_SEED, timer=t)
+    for _ in range(warmup):
+        step_mx()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step_mx()
+    end.record()
+    torch.cuda.synchronize()
+    ms_mx = start.elapsed_time(end) / steps
+    events.clear()
+    step_mx(timer)
+    torch.cuda.synchronize()
+    per_mx = {}
+    prev = None
+    for name, ev in events:
+        if prev is not None and name is not None:
+            per_mx[name] = round(prev.elapsed_time(ev), 4)
+        prev = ev
+    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx)
 
 
 def quantizer_microbench(reps=20):
@@ -272,12 +299,12 @@ def copy_calibration(n_bytes=1 << 30, reps=3):
 
 def cpu_baseline():
     """The oracle on a bounded sample of the same workload: the expert layer's
-    forward + backward for the first 1024 tokens routed top-2 among the first 2
+    forward + backward for the first 1536 tokens routed top-2 among the first 2
     experts (d = 4096, F = 1536 full size), timed on this host's cores (about
     10-15 s of CPU work)."""
     from oracle import layer as olayer
     c = synth.CONFIGS[CFG_ID]
-    Ts, Es, ks = 1024, 2, 2
+    Ts, Es, ks = 1536, 2, 2
     full = synth.layer_inputs(Ts, c["d"], c["F"], Es, ks, device="cpu", seed=0, zipf=c["zipf"])
     x = synth.bf16_bits(full["x"])
     wu, wd = synth.f32_np(full["w_up"]), synth.f32_np(full["w_down"])
@@ -316,7 +343,7 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad = gpu_run(args.steps, args.warmup)
+    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx) = gpu_run(args.steps, args.warmup)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
     calls = {}
@@ -391,6 +418,15 @@ def main():
         "breakdown": calls,
         "roofline": roof,
         "quantizer_microbench": quantizer_microbench(),
+        # the same layer with an MXFP8 forward (the pages' higher-precision
+        # layers, and their full-MXFP8 baseline): whole step, and per call (ms)
+        "mxfp8_forward_variant": {
+            "ms_per_step": round(ms_mx, 3),
+            "value": round(step_gemm_flops / (ms_mx * 1e-3) / 1e12, 2),
+            "fwd_gemm_tflops": {n: round(2.0 * c["T"] * c["k"] * c["d"] * c["F"] / (per_mx[n] * 1e-3) / 1e12, 1)
+                                for n in ("F6 up GEMM (MXFP8)", "F8 down GEMM (MXFP8)") if n in per_mx},
+            "breakdown_ms": per_mx,
+        },
     }
     if args.copy_calibration:
         copy_calibration()

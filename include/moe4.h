@@ -180,13 +180,31 @@ int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts,
                        uint8_t* out_codes, uint8_t* out_sf, void* stream);
 
 /*
- * mxfp8_quant - MXFP8 quantisation of a gradient.  The value of source element
- * (r, c) is:
+ * mxfp8_requant_mx_sr_T - as mxfp8_requant_sr_T for a forward operand that is
+ * itself MXFP8 row-wise (codes [rows, cols] E4M3, scales [rows, cols/32]
+ * E8M0, no tensor scale): exact values code * 2**(scale - 127) -> transpose ->
+ * MXFP8 with stochastic rounding (same exponent rule, random words and
+ * layouts).  For the layers the pages keep in MXFP8 (agihunt.info page,
+ * "Confirmed": the last 16.6% of layers; lhc.media page, the paragraph on
+ * requantising dequantised, transposed values with stochastic rounding).
+ */
+int mxfp8_requant_mx_sr_T(const uint8_t* codes, const uint8_t* sf, int64_t rows, int64_t cols,
+                          const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
+                          int64_t max_padded_rows, uint64_t seed, uint32_t stream_id, int sf_layout,
+                          uint8_t* out_codes, uint8_t* out_sf, void* stream);
+
+/*
+ * mxfp8_quant - MXFP8 quantisation of a gradient (or, for the MXFP8-forward
+ * layer, of a forward operand).  The value of source element (r, c) is:
  *   v = x[src(r), c]                                    (no options)
- *   v = fl(row_scale[a] * x[a / map_div, c]), a = row_map[r]   (row_map given)
+ *   v = fl(row_scale[a] * x[a / map_div, c]), a = row_map[r]   (row_map given;
+ *       row_scale may be NULL: a plain gather)
  *   v = fl(x[r, c] * dsilu(u[r, c]))                    (dsilu_src given)
- * with x bf16 or float32 (dtype), u bf16, dsilu the correctly rounded float32
- * silu'.  row_map and dsilu_src are exclusive.  rows = number of output rows.
+ *   v = silu(x[r, c])                                   (pre_op MOE4_PRE_SILU)
+ * with x bf16 or float32 (dtype), u bf16, silu / dsilu the correctly rounded
+ * float32 silu and silu' of a bf16 value (MOE4_PRE_SILU needs bf16 x).
+ * row_map, dsilu_src and MOE4_PRE_SILU are exclusive.  rows = number of
+ * output rows.
  * transpose = 0: blocks of 32 along cols, out [rows, cols] + [rows, cols/32].
  * transpose = 1: blocks along rows per group, group-major padded layout
  *                with row-major scales (group_row_off, group_off_pad,
@@ -199,7 +217,7 @@ int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const float* ts,
  */
 int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
                 const int32_t* row_map, int32_t map_div, const float* row_scale,
-                const uint16_t* dsilu_src, int transpose,
+                const uint16_t* dsilu_src, int pre_op, int transpose,
                 const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
                 int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
                 uint8_t* out_codes, uint8_t* out_sf, void* stream);
@@ -277,6 +295,18 @@ int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t* a_sf,
                                const uint8_t* b_codes, const uint8_t* b_sf,
                                const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
                                float* c, void* stream);
+
+/*
+ * moe_grouped_gemm_mx - the same product as moe_grouped_gemm_bwd_dgrad with
+ * a choice of output: c_dtype MOE4_F32 (identical to the dgrad call) or
+ * MOE4_BF16 (the float32 result rounded to nearest even; needs K % 128 ==
+ * 0).  The forward GEMMs of the MXFP8 layers (agihunt.info page,
+ * "Confirmed": the last 16.6% of layers in MXFP8; fourweekmba.com page, the
+ * MXFP8 rate in the hardware table).
+ */
+int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, const uint8_t* b_codes, const uint8_t* b_sf,
+                        const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
+                        void* c, int c_dtype, void* stream);
 
 /*
  * moe_grouped_gemm_bwd_wgrad - dW[e] = A_e . B_e^T over expert e's padded token

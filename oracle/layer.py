@@ -128,20 +128,27 @@ def gated_grad_rows(dy_bf16, gates, perm, k):
 
 
 def backward(fw, dy_bf16, seed=1, layer=0):
+    """The backward of ``forward`` (steps 1-13 above)."""
+    def req(q, off, ts_per_group, role, layout):
+        return mx.requant_sr_t(q["codes"], q["sf"], q["ts"], off, ts_per_group, seed, 16 * layer + role, layout)
+    return _backward(fw, dy_bf16, req)
+
+
+def _backward(fw, dy_bf16, req):
+    """Backward steps; req(q, group offsets, ts per group, role, scale layout)
+    is the transposed SR requantisation of the forward operand q."""
     T, d, F, E, k = fw["dims"]
     P = fw["perm"]
     off, perm, inv = P["off"], P["perm"], P["inv_perm"]
-    sid = lambda role: 16 * layer + role
     dYp = gated_grad_rows(dy_bf16, fw["gates"], perm, k)
     dy_row_c, dy_row_s = mx.quantize_rowwise(dYp, mx.RNE)
     dy_col_c, dy_col_s = mx.quantize_transposed(dYp, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
     wd = fw["wd"]
-    wdT_c, wdT_s = mx.requant_sr_t(wd["codes"], wd["sf"], wd["ts"], np.arange(E + 1) * d,
-                                   True, seed, sid(ROLE_WDOWN))
+    wdT_c, wdT_s = req(wd, np.arange(E + 1) * d, True, ROLE_WDOWN, mx.SF_ROWS)
     WdT = np.stack(mx.dequant_transposed(wdT_c, wdT_s, np.arange(E + 1) * d, F))   # [E, F, d]
     dH = gemm.grouped_nt(mx.dequant_rowwise(dy_row_c, dy_row_s), WdT, off).astype(np.float32)
     hq = fw["hq"]
-    hT_c, hT_s = mx.requant_sr_t(hq["codes"], hq["sf"], hq["ts"], off, True, seed, sid(ROLE_H), mx.SF_BLOCKS)
+    hT_c, hT_s = req(hq, off, True, ROLE_H, mx.SF_BLOCKS)
     HT = mx.dequant_transposed(hT_c, hT_s, off, F, mx.SF_BLOCKS)
     dYc = mx.dequant_transposed(dy_col_c, dy_col_s, off, d, mx.SF_BLOCKS)
     dW_down = gemm.wgrad(dYc, HT).astype(np.float32)
@@ -149,12 +156,11 @@ def backward(fw, dy_bf16, seed=1, layer=0):
     du_row_c, du_row_s = mx.quantize_rowwise(dU, mx.RNE)
     du_col_c, du_col_s = mx.quantize_transposed(dU, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
     wu = fw["wu"]
-    wuT_c, wuT_s = mx.requant_sr_t(wu["codes"], wu["sf"], wu["ts"], np.arange(E + 1) * F,
-                                   True, seed, sid(ROLE_WUP))
+    wuT_c, wuT_s = req(wu, np.arange(E + 1) * F, True, ROLE_WUP, mx.SF_ROWS)
     WuT = np.stack(mx.dequant_transposed(wuT_c, wuT_s, np.arange(E + 1) * F, d))   # [E, d, F]
     dXp = gemm.grouped_nt(mx.dequant_rowwise(du_row_c, du_row_s), WuT, off).astype(np.float32)
     xp = fw["xq_perm"]
-    xT_c, xT_s = mx.requant_sr_t(xp["codes"], xp["sf"], xp["ts"], off, False, seed, sid(ROLE_X), mx.SF_BLOCKS)
+    xT_c, xT_s = req(xp, off, False, ROLE_X, mx.SF_BLOCKS)
     XT = mx.dequant_transposed(xT_c, xT_s, off, d, mx.SF_BLOCKS)
     dUc = mx.dequant_transposed(du_col_c, du_col_s, off, F, mx.SF_BLOCKS)
     dW_up = gemm.wgrad(dUc, XT).astype(np.float32)
@@ -165,3 +171,45 @@ def backward(fw, dy_bf16, seed=1, layer=0):
                 wdT=(wdT_c, wdT_s), dH=dH, hT=(hT_c, hT_s), dW_down=dW_down, dU=dU,
                 du_row=(du_row_c, du_row_s), du_col=(du_col_c, du_col_s), wuT=(wuT_c, wuT_s),
                 dXp=dXp, xT=(xT_c, xT_s), dW_up=dW_up, dx=dx)
+
+
+# ------------------------------------------------ MXFP8-forward variant
+#
+# The layers the pages keep at higher precision run their forward in MXFP8
+# (agihunt.info page, "Confirmed": the last 16.6% of layers in MXFP8;
+# lhc.media page: the final sixth of the layers), and full MXFP8 training is
+# the pages' baseline (fourweekmba.com page, "Why the Gain Is 8%, Not 3x").
+# Readings: x, the weights and H are quantised to MXFP8 with round to nearest
+# even along the forward contraction (blocks of 32, no tensor scale); U is
+# stored in bf16 as in the NVFP4 forward; the backward is the same, except
+# that the requantisations read the MXFP8 forward operands.
+
+def forward_mx(x_bf16, W_up, W_down, logits, k, bias=None):
+    T, d = x_bf16.shape
+    E, F, _ = W_up.shape
+    wu_c, wu_s = mx.quantize_rowwise(W_up.reshape(E * F, d).astype(np.float32), mx.RNE)
+    wd_c, wd_s = mx.quantize_rowwise(W_down.reshape(E * d, F).astype(np.float32), mx.RNE)
+    idx, gates = route.topk_gates(logits, k, bias)
+    P = route.permutation(idx, E)
+    off, perm, inv = P["off"], P["perm"], P["inv_perm"]
+    xf = fmt.bf16_to_f32(x_bf16)
+    xp_c, xp_s = mx.quantize_rowwise(xf[perm.astype(np.int64) // k], mx.RNE)
+    A64 = mx.dequant_rowwise(xp_c, xp_s)
+    Bup = mx.dequant_rowwise(wu_c, wu_s).reshape(E, F, d)
+    U = fmt.f64_to_bf16(gemm.grouped_nt(A64, Bup, off))
+    H = silu.silu_f32(U)
+    h_c, h_s = mx.quantize_rowwise(H, mx.RNE)
+    Bdn = mx.dequant_rowwise(wd_c, wd_s).reshape(E, d, F)
+    Yp = gemm.grouped_nt(mx.dequant_rowwise(h_c, h_s), Bdn, off).astype(np.float32)
+    y = combine(Yp, gates, inv, k)
+    mxq = lambda c, s_: dict(codes=c, sf=s_)
+    return dict(wu=mxq(wu_c, wu_s), wd=mxq(wd_c, wd_s), idx=idx, gates=gates, perm=P, xq_perm=mxq(xp_c, xp_s),
+                U=U, hq=mxq(h_c, h_s), Yp=Yp, y=y, dims=(T, d, F, E, k))
+
+
+def backward_mx(fw, dy_bf16, seed=1, layer=0):
+    """The backward of ``forward_mx``: as ``backward``, with the transposed
+    SR requantisations reading MXFP8 forward operands."""
+    def req(q, off, ts_per_group, role, layout):
+        return mx.requant_mx_sr_t(q["codes"], q["sf"], off, seed, 16 * layer + role, layout)
+    return _backward(fw, dy_bf16, req)

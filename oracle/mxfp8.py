@@ -180,6 +180,16 @@ def requant_sr_t(codes, sf, ts, group_row_off=None, ts_per_group=True, seed=1, s
     return quantize_transposed(v, off, SR, seed, stream_id, sf_layout)
 
 
+def requant_mx_sr_t(codes, sf, group_row_off=None, seed=1, stream_id=0, sf_layout=SF_ROWS):
+    """MXFP8 row-wise [R, C] (codes, scales [R, C/32]) -> exact values ->
+    transpose -> MXFP8 SR: the same requantisation for a forward operand that
+    is itself MXFP8 (no tensor scale).  Output layout as ``quantize_transposed``."""
+    v = dequant_rowwise(codes, sf).astype(np.float32)       # exact: E4M3 times a power of two
+    R = v.shape[0]
+    off = np.array([0, R], dtype=np.int64) if group_row_off is None else np.asarray(group_row_off, dtype=np.int64)
+    return quantize_transposed(v, off, SR, seed, stream_id, sf_layout)
+
+
 def dequant_rowwise(codes, sf):
     """Exact float64 values of row-wise MXFP8 [R, C]."""
     c = np.asarray(codes)

@@ -43,8 +43,12 @@ _SIGS = {
                              _c_void_p]),
     "mxfp8_requant_sr_T": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i32,
                                   _i64, _u64, _u32, _int, _c_void_p, _c_void_p, _c_void_p]),
-    "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _c_void_p,
-                           _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
+    "mxfp8_requant_mx_sr_T": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i64, _u64,
+                                     _u32, _int, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_grouped_gemm_mx": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i64, _i64,
+                                   _c_void_p, _int, _c_void_p]),
+    "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _int,
+                           _c_void_p, _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_route_backward": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_dgates": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe4_debug_check": (_int, [_c_void_p]),
@@ -197,9 +201,26 @@ def mxfp8_requant_sr_T(codes, sf, ts, group_row_off, group_off_pad, ts_per_group
     return oc, os_
 
 
+def mxfp8_requant_mx_sr_T(codes, sf, group_row_off, group_off_pad, seed=1, stream_id=0, max_pr=None,
+                          sf_layout=SF_ROWS):
+    """MXFP8 row-wise [R, C] -> MXFP8 SR transposed, group-major padded: (codes [C*P], sf [C*P/32])."""
+    R, C = codes.shape
+    G = group_row_off.numel() - 1
+    _dev(group_row_off, torch.int32, "group_row_off")
+    _dev(group_off_pad, torch.int32, "group_off_pad")
+    if max_pr is None:
+        max_pr = max_padded_rows(R, G)
+    oc = _empty((C * max_pr,), torch.uint8, codes)
+    os_ = _empty((C * max_pr // 32,), torch.uint8, codes)
+    rc = lib().mxfp8_requant_mx_sr_T(_p(codes), _p(sf), R, C, _p(group_row_off), _p(group_off_pad), G, max_pr, seed,
+                                     stream_id, int(sf_layout), _p(oc), _p(os_), _stream())
+    _check(rc, "mxfp8_requant_mx_sr_T")
+    return oc, os_
+
+
 def mxfp8_quant(x, rows=None, transpose=False, row_map=None, map_div=1, row_scale=None, dsilu_src=None,
                 group_row_off=None, group_off_pad=None, max_pr=None, rnd=RNE, seed=0, stream_id=0,
-                sf_layout=SF_ROWS):
+                sf_layout=SF_ROWS, pre_op=PRE_NONE):
     """MXFP8 of a gradient (see moe4.h).  Row mode -> ([rows, C], [rows, C/32]);
     transposed -> (codes [C*max_pr], sf [C*max_pr/32]), scales per group
     row-major (SF_ROWS) or block-major (SF_BLOCKS)."""
@@ -227,7 +248,7 @@ def mxfp8_quant(x, rows=None, transpose=False, row_map=None, map_div=1, row_scal
         oc = _empty((R, C), torch.uint8, x)
         os_ = _empty((R, C // 32), torch.uint8, x)
     mode = 0 if not transpose else (2 if sf_layout == SF_BLOCKS else 1)
-    rc = lib().mxfp8_quant(_p(x), dt, R, C, _p(row_map), map_div, _p(row_scale), _p(dsilu_src), mode,
+    rc = lib().mxfp8_quant(_p(x), dt, R, C, _p(row_map), map_div, _p(row_scale), _p(dsilu_src), pre_op, mode,
                            _p(group_row_off), _p(group_off_pad), G, max_pr, rnd, seed, stream_id, _p(oc), _p(os_),
                            _stream())
     _check(rc, "mxfp8_quant")
@@ -289,6 +310,19 @@ def moe_grouped_gemm_bwd_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off):
     rc = lib().moe_grouped_gemm_bwd_dgrad(_p(a_codes), _p(a_sf), _p(b_codes), _p(b_sf), _p(expert_off), E, M, N, K,
                                           _p(c), _stream())
     _check(rc, "moe_grouped_gemm_bwd_dgrad")
+    return c
+
+
+def moe_grouped_gemm_mx(a_codes, a_sf, b_codes, b_sf, expert_off, out_dtype=torch.float32):
+    """MXFP8 A [M, K] x MXFP8 B [E, N, K] per expert -> C [M, N] (float32 or bf16)."""
+    M, K = a_codes.shape
+    E = expert_off.numel() - 1
+    N = b_codes.numel() // (E * K)
+    cd = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    c = _empty((M, N), out_dtype, a_codes)
+    rc = lib().moe_grouped_gemm_mx(_p(a_codes), _p(a_sf), _p(b_codes), _p(b_sf), _p(expert_off), E, M, N, K, _p(c),
+                                   cd, _stream())
+    _check(rc, "moe_grouped_gemm_mx")
     return c
 
 

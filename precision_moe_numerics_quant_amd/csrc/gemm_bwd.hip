@@ -405,14 +405,15 @@ __device__ inline int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 }  // namespace dmag
 
-template <int TM, int TN>
+// OUT_BF16: C is bf16 (round to nearest even), else float32.
+template <int TM, int TN, bool OUT_BF16>
 __device__ __forceinline__ void dgrad_dma_body(const uint8_t* __restrict__ a_codes,
                                                           const uint8_t* __restrict__ a_sf,
                                                           const uint8_t* __restrict__ b_codes,
                                                           const uint8_t* __restrict__ b_sf,
                                                           const int32_t* __restrict__ off, int E, int64_t M_total,
                                                           int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all,
-                                                          float* __restrict__ c) {
+                                                          void* __restrict__ c) {
   using namespace dmag;
   constexpr int WM = TM / 2, WN = TN / 2, MI = WM / 32, NJ = WN / 32;
   constexpr int QA = TM / 32, QB = TN / 32;  // 1 KB code loads per wave and slab
@@ -560,7 +561,13 @@ __device__ __forceinline__ void dgrad_dma_body(const uint8_t* __restrict__ a_cod
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = row0 + wm + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row < row_end && col < N) __builtin_nontemporal_store(acc[i][j][v], c + row * N + col);
+        if (row < row_end && col < N) {
+          if (OUT_BF16)
+            __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(acc[i][j][v]),
+                                        static_cast<uint16_t*>(c) + row * N + col);
+          else
+            __builtin_nontemporal_store(acc[i][j][v], static_cast<float*>(c) + row * N + col);
+        }
       }
     }
 }
@@ -680,15 +687,16 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
 }
 
 // One kernel per configuration (the body is a device template).
-#define MOE4_DGRAD_DMA_KERNEL(NAME, TM, TN, MINB)                                                                  \
+#define MOE4_DGRAD_DMA_KERNEL(NAME, TM, TN, MINB, BF16)                                                            \
   __global__ void __launch_bounds__(dmag::NT, MINB)                                                               \
       NAME(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,                                 \
            const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf, const int32_t* __restrict__ off, \
-           int E, int64_t M_total, int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all, float* __restrict__ c) { \
-    dgrad_dma_body<TM, TN>(a_codes, a_sf, b_codes, b_sf, off, E, M_total, N, K, n_ntiles, n_all, c);             \
+           int E, int64_t M_total, int64_t N, int64_t K, int64_t n_ntiles, int64_t n_all, void* __restrict__ c) {  \
+    dgrad_dma_body<TM, TN, BF16>(a_codes, a_sf, b_codes, b_sf, off, E, M_total, N, K, n_ntiles, n_all, c);       \
   }
-MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_256, 256, 256, 1)
-MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_128, 128, 128, 2)
+MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_256, 256, 256, 1, false)
+MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_128, 128, 128, 2, false)
+MOE4_DGRAD_DMA_KERNEL(k_mx_gemm_dma_256_bf16, 256, 256, 1, true)
 #undef MOE4_DGRAD_DMA_KERNEL
 
 // wgrad, warp-specialized and persistent.  On this architecture one
@@ -1054,6 +1062,29 @@ extern "C" int moe_grouped_gemm_bwd_dgrad(const uint8_t* a_codes, const uint8_t*
   if (M_total == 0) return MOE4_OK;
   launch_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c, as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_dgrad");
+}
+
+extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, const uint8_t* b_codes,
+                                   const uint8_t* b_sf, const int32_t* expert_off, int32_t E, int64_t M_total,
+                                   int64_t N, int64_t K, void* c, int c_dtype, void* stream) {
+  MOE4_REQUIRE(c_dtype == MOE4_F32 || c_dtype == MOE4_BF16, MOE4_EINVAL, "moe_grouped_gemm_mx: c_dtype must be F32 or BF16");
+  if (c_dtype == MOE4_F32)
+    return moe_grouped_gemm_bwd_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, static_cast<float*>(c),
+                                      stream);
+  MOE4_REQUIRE(E >= 1 && M_total >= 0 && N > 0 && K > 0 && K % dmag::BK == 0 && N % 32 == 0, MOE4_EINVAL,
+               "moe_grouped_gemm_mx: bf16 output needs K % 128 == 0 and N % 32 == 0");
+  MOE4_REQUIRE(b_codes && b_sf && expert_off, MOE4_EINVAL, "moe_grouped_gemm_mx: NULL pointer");
+  MOE4_REQUIRE(M_total == 0 || (a_codes && a_sf && c), MOE4_EINVAL, "moe_grouped_gemm_mx: NULL pointer");
+  MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(c), MOE4_EALIGN,
+               "moe_grouped_gemm_mx: misaligned pointer");
+  MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_mx: A and each expert's B must stay below 2 GiB");
+  if (M_total == 0) return MOE4_OK;
+  const int64_t n_nt = (N + 255) / 256;
+  const int64_t n_all = n_nt * ((M_total + 255) / 256 + E);
+  hipLaunchKernelGGL(k_mx_gemm_dma_256_bf16, dim3((unsigned)xcd_grid(n_all)), dim3(dmag::NT), 0, as_stream(stream),
+                     a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, n_nt, n_all, c);
+  return check_launch("moe_grouped_gemm_mx");
 }
 
 extern "C" int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf, const uint8_t* b_codes,

@@ -41,6 +41,15 @@ __device__ inline void dequant8(uint32_t cw, uint32_t sbyte, float (&q)[8]) {
   q[4] = d2[0] * m; q[5] = d2[1] * m; q[6] = d3[0] * m; q[7] = d3[1] * m;
 }
 
+// Exact values of 8 E4M3 codes of one row (byte p of w -> column p) under
+// the row's E8M0 scale byte e: code * 2**(e - 127), exact in float32 (the
+// smallest, 2**-9 * 2**-127, is a float32 subnormal; denormals are kept).
+__device__ inline void dequant8_mx(u32x2 w, uint32_t e, float (&q)[8]) {
+  const int sh = (int)e - 127;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) q[p] = __builtin_amdgcn_ldexpf(e4m3_to_f32((w[p >> 2] >> (8 * (p & 3))) & 0xFFu), sh);
+}
+
 // SR E4M3 of v into byte sel of old (sel is a constant after unrolling).
 __device__ inline uint32_t sr_fp8_into(uint32_t old, float v, uint32_t r, int sel) {
   switch (sel) {
@@ -57,10 +66,10 @@ __device__ inline uint32_t sr_fp8_into(uint32_t old, float v, uint32_t r, int se
 // FAST: every element pair index of the block is below 2**32, so the
 // per-pair key is the constant key0 and the index arithmetic is 32-bit.
 // FULL: all 32 rows are valid (no row masks).
-template <bool FAST, bool FULL, typename Put>
-__device__ inline void requant_block(const uint32_t (&cw)[32], const uint32_t (&sbp)[8], int nvalid, float S,
-                                     const float (&pc)[8], int64_t j0, int64_t jstride, uint32_t base,
-                                     uint32_t key0, Put put) {
+// deq(i, q) gives row i's 8 exact source values (before the factor S).
+template <bool FAST, bool FULL, typename Deq, typename Put>
+__device__ inline void requant_block(Deq deq, int nvalid, float S, const float (&pc)[8], int64_t j0, int64_t jstride,
+                                     uint32_t base, uint32_t key0, Put put) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     uint32_t od[8];
@@ -71,7 +80,7 @@ __device__ inline void requant_block(const uint32_t (&cw)[32], const uint32_t (&
       const int i = 4 * k + ii;
       if (FULL || i < nvalid) {
         float q[8];
-        dequant8(cw[i], (sbp[k] >> (8 * ii)) & 0xFFu, q);
+        deq(i, q);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t word;

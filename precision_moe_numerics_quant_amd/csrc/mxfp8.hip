@@ -117,6 +117,9 @@ __device__ inline bool tile_coords(const int32_t* off, const int32_t* offp, int 
 }
 
 // ---------------------------------------------------------------- requant-T
+// MX: the source is MXFP8 row-wise (codes [R, C], E8M0 scales [R, C/32], no
+// tensor scale: S = 1) instead of NVFP4.
+template <bool MX>
 __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ sf,
                                                            const float* __restrict__ ts, int ts_per_group, int64_t C,
@@ -162,18 +165,31 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
 #pragma unroll
   for (int q = 0; q < 8; ++q) ex[q] = -127;
   if (nvalid > 0 && c < C) {
-    uint32_t cw[32], sbp[8];  // code words; scale bytes packed 4 rows per register
-    const uint8_t* crow = codes + src0 * (C / 2) + c / 2;
-    const uint8_t* srow = sf + src0 * (C / 16) + c / 16;
+    // code words (NVFP4: 8 E2M1 codes in one dword; MXFP8: 8 E4M3 bytes in
+    // two); scale bytes packed 4 rows per register
+    uint32_t cw[32][MX ? 2 : 1], sbp[8];
+    const uint8_t* crow = MX ? codes + src0 * C + c : codes + src0 * (C / 2) + c / 2;
+    const uint8_t* srow = MX ? sf + src0 * (C / 32) + c / 32 : sf + src0 * (C / 16) + c / 16;
 #pragma unroll
     for (int k = 0; k < 8; ++k) sbp[k] = 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {  // rows past the group repeat its last row and are never used
       const int64_t ri = i < nvalid ? i : nvalid - 1;
-      cw[i] = *reinterpret_cast<const uint32_t*>(crow + ri * (C / 2));
-      sbp[i >> 2] |= (uint32_t)srow[ri * (C / 16)] << (8 * (i & 3));
+      if (MX) {
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(crow + ri * C);
+        cw[i][0] = wv[0];
+        cw[i][MX ? 1 : 0] = wv[1];
+      } else {
+        cw[i][0] = *reinterpret_cast<const uint32_t*>(crow + ri * (C / 2));
+      }
+      sbp[i >> 2] |= (uint32_t)srow[ri * (MX ? C / 32 : C / 16)] << (8 * (i & 3));
     }
-    const float S = ts[ts_per_group ? g : 0];
+    const float S = MX ? 1.0f : ts[ts_per_group ? g : 0];
+    auto deq = [&](int i, float (&q)[8]) {
+      const uint32_t sb = (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      if (MX) dequant8_mx(u32x2{cw[i][0], cw[i][MX ? 1 : 0]}, sb, q);
+      else dequant8(cw[i][0], sb, q);
+    };
     // block amax of fl(fl(q*sc)*S) per column: fl(max |q*sc| * S), as
     // rounding a product by S > 0 keeps the order of the exact q*sc
     float am[8];
@@ -183,7 +199,7 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     for (int i = 0; i < 32; ++i) {
       if (i < nvalid) {
         float q8[8];
-        dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q8);
+        deq(i, q8);
 #pragma unroll
         for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
       }
@@ -198,11 +214,11 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     const uint32_t key0 = fmix32(base);
     const bool fast = j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32);
     if (fast && nvalid == 32)
-      requant_block<true, true>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
+      requant_block<true, true>(deq, nvalid, S, pc, j0, C / 2, base, key0, put);
     else if (fast)
-      requant_block<true, false>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
+      requant_block<true, false>(deq, nvalid, S, pc, j0, C / 2, base, key0, put);
     else
-      requant_block<false, false>(cw, sbp, nvalid, S, pc, j0, C / 2, base, key0, put);
+      requant_block<false, false>(deq, nvalid, S, pc, j0, C / 2, base, key0, put);
   } else {  // no valid rows (padding block or columns past C): zero codes
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -234,7 +250,7 @@ __device__ inline f32x4 load4(const void* x, int64_t idx) {
                bf16_bits_to_f32(w[1] >> 16)};
 }
 
-template <int DT, int MODE>  // MODE 0: plain, 1: row map + scale, 2: dsilu
+template <int DT, int MODE>  // MODE 0: plain, 1: row map + scale, 2: x * dsilu(u), 3: silu(x) (x bf16)
 __device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64_t c, const float* dtab) {
   if (MODE == 1) {
     const int32_t a = g.row_map[r];
@@ -246,6 +262,10 @@ __device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64
     u32x2 u = *reinterpret_cast<const u32x2*>(g.dsilu_src + r * C + c);
     return f32x4{v[0] * act_eval<true>(u[0] & 0xFFFFu, dtab), v[1] * act_eval<true>(u[0] >> 16, dtab),
                  v[2] * act_eval<true>(u[1] & 0xFFFFu, dtab), v[3] * act_eval<true>(u[1] >> 16, dtab)};
+  } else if (MODE == 3) {  // (the table is the silu one)
+    u32x2 u = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(g.x) + r * C + c);
+    return f32x4{act_eval<false>(u[0] & 0xFFFFu, dtab), act_eval<false>(u[0] >> 16, dtab),
+                 act_eval<false>(u[1] & 0xFFFFu, dtab), act_eval<false>(u[1] >> 16, dtab)};
   }
   return load4<DT>(g.x, r * C + c);
 }
@@ -255,8 +275,8 @@ template <int DT, int MODE, bool SR>
 __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C, uint32_t base,
                                                  uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
                                                  const float* __restrict__ act_tab) {
-  __shared__ float tab[MODE == 2 ? ACT_TAB : 1];
-  if (MODE == 2) stage_act_table(tab, act_tab);
+  __shared__ float tab[MODE >= 2 ? ACT_TAB : 1];
+  if (MODE >= 2) stage_act_table(tab, act_tab);
   const int64_t nbr = C / 32;
   const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (blk >= R * nbr) return;
@@ -300,9 +320,9 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
                                               uint32_t base, int sfb,
                                               uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
                                               const float* __restrict__ act_tab) {
-  __shared__ float tab[MODE == 2 ? ACT_TAB : 1];
+  __shared__ float tab[MODE >= 2 ? ACT_TAB : 1];
   __shared__ float lv[TC][TR + 1];  // [column][row]
-  if (MODE == 2) stage_act_table(tab, act_tab);
+  if (MODE >= 2) stage_act_table(tab, act_tab);
   const int64_t ct = blockIdx.x % n_ct, rt = blockIdx.x / n_ct;
   TileT t;
   if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
@@ -380,16 +400,37 @@ extern "C" int mxfp8_requant_sr_T(const uint8_t* codes, const uint8_t* sf, const
   const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (max_padded_rows + rq::ROWS - 1) / rq::ROWS;
   MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "mxfp8_requant_sr_T: tensor too large");
   const uint32_t base = sr_base_key(seed, stream_id);
-  hipLaunchKernelGGL(k_requant_T, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, as_stream(stream), codes, sf, ts,
+  hipLaunchKernelGGL(k_requant_T<false>, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, as_stream(stream), codes, sf, ts,
                      ts_per_group, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct, base,
                      (int)(sf_layout == MOE4_SF_BLOCKS), out_codes, out_sf);
   return check_launch("mxfp8_requant_sr_T");
 }
 
+extern "C" int mxfp8_requant_mx_sr_T(const uint8_t* codes, const uint8_t* sf, int64_t rows, int64_t cols,
+                                     const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
+                                     int64_t max_padded_rows, uint64_t seed, uint32_t stream_id, int sf_layout,
+                                     uint8_t* out_codes, uint8_t* out_sf, void* stream) {
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_requant_mx_sr_T: cols must be a positive multiple of 32");
+  MOE4_REQUIRE(n_groups >= 1 && group_row_off && group_off_pad, MOE4_EINVAL, "mxfp8_requant_mx_sr_T: group offsets required");
+  MOE4_REQUIRE(max_padded_rows >= 0 && max_padded_rows % 32 == 0, MOE4_EINVAL,
+               "mxfp8_requant_mx_sr_T: max_padded_rows must be a multiple of 32");
+  MOE4_REQUIRE(sf_layout == MOE4_SF_ROWS || sf_layout == MOE4_SF_BLOCKS, MOE4_EINVAL,
+               "mxfp8_requant_mx_sr_T: sf_layout must be MOE4_SF_ROWS or MOE4_SF_BLOCKS");
+  MOE4_REQUIRE(codes && sf && out_codes && out_sf, MOE4_EINVAL, "mxfp8_requant_mx_sr_T: NULL pointer");
+  MOE4_REQUIRE(aligned16(codes) && aligned16(out_codes), MOE4_EALIGN, "mxfp8_requant_mx_sr_T: misaligned pointer");
+  if (max_padded_rows == 0) return MOE4_OK;
+  const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (max_padded_rows + rq::ROWS - 1) / rq::ROWS;
+  MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "mxfp8_requant_mx_sr_T: tensor too large");
+  hipLaunchKernelGGL(k_requant_T<true>, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, as_stream(stream), codes,
+                     sf, nullptr, 0, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct,
+                     sr_base_key(seed, stream_id), (int)(sf_layout == MOE4_SF_BLOCKS), out_codes, out_sf);
+  return check_launch("mxfp8_requant_mx_sr_T");
+}
+
 extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
-                           int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int transpose,
-                           const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
-                           int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
+                           int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int pre_op,
+                           int transpose, const int32_t* group_row_off, const int32_t* group_off_pad,
+                           int32_t n_groups, int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
                            uint8_t* out_codes, uint8_t* out_sf, void* stream) {
   MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "mxfp8_quant: dtype must be BF16 or F32");
   MOE4_REQUIRE(rnd == MOE4_RNE || rnd == MOE4_SR, MOE4_EINVAL, "mxfp8_quant: rnd must be RNE or SR");
@@ -397,6 +438,8 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
   MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL, "mxfp8_quant: cols must be a positive multiple of 32");
   MOE4_REQUIRE(!(row_map && dsilu_src), MOE4_EINVAL, "mxfp8_quant: row_map and dsilu_src are exclusive");
   MOE4_REQUIRE(!row_map || map_div >= 1, MOE4_EINVAL, "mxfp8_quant: map_div >= 1");
+  MOE4_REQUIRE(pre_op == MOE4_PRE_NONE || (pre_op == MOE4_PRE_SILU && dtype == MOE4_BF16 && !row_map && !dsilu_src),
+               MOE4_EINVAL, "mxfp8_quant: pre_op SILU needs bf16 x and excludes row_map and dsilu_src");
   MOE4_REQUIRE(x && out_codes && out_sf, MOE4_EINVAL, "mxfp8_quant: NULL pointer");
   MOE4_REQUIRE(aligned16(x) && aligned16(out_codes) && (!dsilu_src || aligned16(dsilu_src)), MOE4_EALIGN,
                "mxfp8_quant: misaligned pointer");
@@ -407,16 +450,16 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
   }
   hipStream_t s = as_stream(stream);
   const float* tab = nullptr;
-  if (dsilu_src) {
+  if (dsilu_src || pre_op == MOE4_PRE_SILU) {
     int rc = ensure_act_tables(s);
     if (rc) return rc;
-    tab = act_tables_device_ptr() + ACT_TAB;
+    tab = act_tables_device_ptr() + (dsilu_src ? ACT_TAB : 0);
   }
   if ((transpose ? max_padded_rows : rows) == 0) return MOE4_OK;
   GradSrc g{x, dtype, row_map, map_div, row_scale, dsilu_src};
   const uint32_t base = sr_base_key(seed, stream_id);
   const bool sr = rnd == MOE4_SR;
-  const int mode = row_map ? 1 : (dsilu_src ? 2 : 0);
+  const int mode = row_map ? 1 : (dsilu_src ? 2 : (pre_op == MOE4_PRE_SILU ? 3 : 0));
 #define MOE4_GRAD(DT, MODE)                                                                                      \
   launch_grad<DT, MODE>(transpose, sr, g, rows, cols, group_row_off, group_off_pad, n_groups, max_padded_rows, \
                         base, out_codes, out_sf, tab, s)
@@ -427,7 +470,8 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
   } else {
     if (mode == 0) MOE4_GRAD(MOE4_BF16, 0);
     else if (mode == 1) MOE4_GRAD(MOE4_BF16, 1);
-    else MOE4_GRAD(MOE4_BF16, 2);
+    else if (mode == 2) MOE4_GRAD(MOE4_BF16, 2);
+    else MOE4_GRAD(MOE4_BF16, 3);
   }
 #undef MOE4_GRAD
   return check_launch("mxfp8_quant");

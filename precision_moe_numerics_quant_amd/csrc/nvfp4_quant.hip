@@ -378,10 +378,11 @@ __global__ void __launch_bounds__(rq::THREADS) k_encode_requant_T(const float* _
     }
     const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
     const uint32_t key0 = fmix32(base);
+    auto deq = [&](int i, float (&q)[8]) { dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
     if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
-      requant_block<true, true>(cw, sbp, 32, S, pc, j0, C / 2, base, key0, put);
+      requant_block<true, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
     else
-      requant_block<false, true>(cw, sbp, 32, S, pc, j0, C / 2, base, key0, put);
+      requant_block<false, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k)

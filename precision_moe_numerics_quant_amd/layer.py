@@ -23,9 +23,10 @@ router logits.
 """
 import torch
 
-from . import (NVFP4_4OVER6, NVFP4_6, PRE_SILU, RNE, SF_BLOCKS, max_padded_rows, moe_combine, moe_gather_rows,
-               moe_dgates, moe_route_backward, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_route_topk,
-               moe_unpermute_sum, mxfp8_quant, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
+from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_dgates,
+               moe_gather_rows, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd,
+               moe_grouped_gemm_mx, moe_route_backward, moe_route_topk, moe_unpermute_sum, mxfp8_quant,
+               mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
@@ -85,32 +86,53 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
 
 
 def backward(fw, dy, seed=1, layer=0, timer=None):
-    """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, ...)."""
+    """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, dg, dlogits, ...)."""
+    T, d, F, E, k = fw["dims"]
+    r = fw["route"]
+    mpr = max_padded_rows(T * k, E)
+    sid = lambda role: 16 * layer + role
+    wq = fw["wq"]
+    pre = wq.get("sr") == (seed, layer)  # the weights were requantised with their forward quantisation
+
+    def wreq(name, w, goff, role, rows):
+        if pre:
+            return wq[name], None
+        return mxfp8_requant_sr_T(*w, goff, goff, True, seed, sid(role), max_pr=rows), True
+    hq, xp = fw["hq"], fw["xq_perm"]
+    return _backward_chain(fw, dy, timer, dict(
+        wdT=lambda: wreq("wdT", wq["wd"], wq["off_d"], ROLE_WDOWN, E * d),
+        hT=lambda: (mxfp8_requant_sr_T(*hq, r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr,
+                                       sf_layout=SF_BLOCKS), True),
+        wuT=lambda: wreq("wuT", wq["wu"], wq["off_f"], ROLE_WUP, E * F),
+        xT=lambda: (mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X),
+                                       max_pr=mpr, sf_layout=SF_BLOCKS), True)))
+
+
+def _backward_chain(fw, dy, timer, req):
+    """The backward calls in order; req[name]() gives the transposed MXFP8
+    operand 'wdT', 'hT', 'wuT' or 'xT' and whether a library call made it
+    (for the timer)."""
     T, d, F, E, k = fw["dims"]
     r = fw["route"]
     A = T * k
     mpr = max_padded_rows(A, E)
-    sid = lambda role: 16 * layer + role
     g_flat = r["gates"].view(-1)
+
+    def get(name, label):
+        out, called = req[name]()
+        if called:
+            _tick(timer, label)
+        return out
     _tick(timer, None)
     dy_row = mxfp8_quant(dy, rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat)
     _tick(timer, "B1 dY quant row-wise (MXFP8)")
     dy_col = mxfp8_quant(dy, rows=A, transpose=True, row_map=r["perm"], map_div=k, row_scale=g_flat,
                          group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr, sf_layout=SF_BLOCKS)
     _tick(timer, "B1 dY quant transposed (MXFP8)")
-    wq = fw["wq"]
-    wd_c, wd_s, wd_t = wq["wd"]
-    if wq.get("sr") == (seed, layer):  # requantised with the forward's weight quantisation
-        wdT = wq["wdT"]
-    else:
-        wdT = mxfp8_requant_sr_T(wd_c, wd_s, wd_t, wq["off_d"], wq["off_d"], True, seed, sid(ROLE_WDOWN), max_pr=E * d)
-        _tick(timer, "B2 W_down requant SR-T")
+    wdT = get("wdT", "B2 W_down requant SR-T")
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
     _tick(timer, "B3 down dgrad (MXFP8)")
-    hq = fw["hq"]
-    hT = mxfp8_requant_sr_T(hq[0], hq[1], hq[2], r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr,
-                            sf_layout=SF_BLOCKS)
-    _tick(timer, "B4 H requant SR-T")
+    hT = get("hT", "B4 H requant SR-T")
     dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
     _tick(timer, "B5 down wgrad (MXFP8)")
     du_row = mxfp8_quant(dH, dsilu_src=fw["U"])
@@ -118,18 +140,10 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     du_col = mxfp8_quant(dH, transpose=True, dsilu_src=fw["U"], group_row_off=r["off"], group_off_pad=r["off_pad"],
                          max_pr=mpr, sf_layout=SF_BLOCKS)
     _tick(timer, "B6 SiLU' + dU quant transposed")
-    wu_c, wu_s, wu_t = wq["wu"]
-    if wq.get("sr") == (seed, layer):
-        wuT = wq["wuT"]
-    else:
-        wuT = mxfp8_requant_sr_T(wu_c, wu_s, wu_t, wq["off_f"], wq["off_f"], True, seed, sid(ROLE_WUP), max_pr=E * F)
-        _tick(timer, "B7 W_up requant SR-T")
+    wuT = get("wuT", "B7 W_up requant SR-T")
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")
-    xp = fw["xq_perm"]
-    xT = mxfp8_requant_sr_T(xp[0], xp[1], fw["xq"][2], r["off"], r["off_pad"], False, seed, sid(ROLE_X), max_pr=mpr,
-                            sf_layout=SF_BLOCKS)
-    _tick(timer, "B9 X requant SR-T")
+    xT = get("xT", "B9 X requant SR-T")
     dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d)
     _tick(timer, "B10 up wgrad (MXFP8)")
     dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
@@ -138,5 +152,71 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
     _tick(timer, "B12 gate gradient")
     dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
     _tick(timer, "B13 router backward")
-    return dict(dx=dx, dg=dg, dlogits=dlogits, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row, dy_col=dy_col, wdT=wdT, hT=hT,
-                du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)
+    return dict(dx=dx, dg=dg, dlogits=dlogits, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row,
+                dy_col=dy_col, wdT=wdT, hT=hT, du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)
+
+
+# ------------------------------------------------ MXFP8-forward variant
+#
+# The layers kept at higher precision (the last sixth) run their forward in
+# MXFP8 on the native block-scaled FP8 MFMA: x (gathered into expert order),
+# the weights and H = silu(U) are quantised to MXFP8 (RNE, blocks along the
+# forward contraction, no tensor scale); U is stored in bf16.  The backward
+# is the same chain as above with the transposed SR requantisations reading
+# the MXFP8 forward operands.
+
+def quantize_weights_mx(w_up, w_down, timer=None):
+    E, F, d = w_up.shape
+    dev = w_up.device
+    off_f = torch.arange(E + 1, dtype=torch.int32, device=dev) * F
+    off_d = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
+    _tick(timer, None)
+    wu = mxfp8_quant(w_up.view(E * F, d))
+    _tick(timer, "F1 W_up quant (MXFP8)")
+    wd = mxfp8_quant(w_down.view(E * d, F))
+    _tick(timer, "F1 W_down quant (MXFP8)")
+    return dict(wu=wu, wd=wd, off_f=off_f, off_d=off_d, shape=(E, F, d))
+
+
+def forward_mx(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None):
+    T, d = x.shape
+    E, F, _ = w_up.shape
+    if wq is None:
+        wq = quantize_weights_mx(w_up, w_down, timer)
+    _tick(timer, None)
+    r = moe_route_topk(logits, k, bias)
+    _tick(timer, "F2-F3 route + permutation")
+    A = T * k
+    xq_perm = mxfp8_quant(x, rows=A, row_map=r["perm"], map_div=k)
+    _tick(timer, "F4-F5 X quant + gather (MXFP8)")
+    wu_c, wu_s = wq["wu"]
+    wd_c, wd_s = wq["wd"]
+    U = moe_grouped_gemm_mx(xq_perm[0], xq_perm[1], wu_c.view(E, F, d), wu_s.view(E, F, d // 32), r["off"],
+                            torch.bfloat16)
+    _tick(timer, "F6 up GEMM (MXFP8)")
+    hq = mxfp8_quant(U, pre_op=PRE_SILU)
+    _tick(timer, "F7 SiLU + H quant (MXFP8)")
+    Yp = moe_grouped_gemm_mx(hq[0], hq[1], wd_c.view(E, d, F), wd_s.view(E, d, F // 32), r["off"])
+    _tick(timer, "F8 down GEMM (MXFP8)")
+    y = moe_combine(Yp, r["gates"], r["inv_perm"])
+    _tick(timer, "F9 combine")
+    return dict(y=y, route=r, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k), mx=True)
+
+
+def backward_mx(fw, dy, seed=1, layer=0, timer=None):
+    """The backward of forward_mx: the requantisations read MXFP8 operands."""
+    T, d, F, E, k = fw["dims"]
+    r = fw["route"]
+    A = T * k
+    mpr = max_padded_rows(A, E)
+    sid = lambda role: 16 * layer + role
+    wq = fw["wq"]
+
+    def req(q, goff, goff_pad, role, layout, max_pr):
+        return mxfp8_requant_mx_sr_T(q[0], q[1], goff, goff_pad, seed, sid(role), max_pr=max_pr,
+                                     sf_layout=layout), True
+    return _backward_chain(fw, dy, timer, dict(
+        wdT=lambda: req(wq["wd"], wq["off_d"], wq["off_d"], ROLE_WDOWN, SF_ROWS, E * d),
+        hT=lambda: req(fw["hq"], r["off"], r["off_pad"], ROLE_H, SF_BLOCKS, mpr),
+        wuT=lambda: req(wq["wu"], wq["off_f"], wq["off_f"], ROLE_WUP, SF_ROWS, E * F),
+        xT=lambda: req(fw["xq_perm"], r["off"], r["off_pad"], ROLE_X, SF_BLOCKS, mpr)))

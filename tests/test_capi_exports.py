@@ -72,7 +72,7 @@ def test_validation_errors_without_gpu():
                           ctypes.c_size_t(1 << 20), v(0))
     assert rc == -1                                   # k > E
     L.mxfp8_quant.restype = ctypes.c_int
-    rc = L.mxfp8_quant(v(16), 1, ctypes.c_int64(4), ctypes.c_int64(48), v(0), 1, v(0), v(0), 0, v(0), v(0), 0,
+    rc = L.mxfp8_quant(v(16), 1, ctypes.c_int64(4), ctypes.c_int64(48), v(0), 1, v(0), v(0), 0, 0, v(0), v(0), 0,
                        ctypes.c_int64(0), 0, ctypes.c_uint64(0), ctypes.c_uint32(0), v(16), v(16), v(0))
     assert rc == -1                                   # cols % 32
     L.moe_grouped_gemm_fwd.restype = ctypes.c_int

@@ -277,3 +277,27 @@ def test_route_backward_bit_exact(T, E, k):
     got = to_np(m4.moe_route_backward(dg.cuda(), r["gates"], r["idx"], E))
     want = route.route_backward(dg.numpy(), to_np(r["gates"]), to_np(r["idx"]), E)
     assert_bytes_equal(got.view(np.uint32), want.view(np.uint32), "dlogits")
+
+
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 256), ([256], 128, 1024), ([3, 200], 96, 128)])
+def test_grouped_gemm_mx_bf16_and_f32(M_list, N, K):
+    """The MXFP8 forward GEMM: bf16 output within tolerance of the exact
+    product; float32 output identical to the dgrad call."""
+    E = len(M_list)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    M = int(off[-1])
+    a = synth.randn((M, K), 1.0, "cpu", 15, "dh").numpy()
+    b = synth.randn((E * N, K), 0.05, "cpu", 16, "dh").numpy()
+    ac, as_ = mx.quantize_rowwise(a, mx.RNE)
+    bc, bs = mx.quantize_rowwise(b, mx.RNE)
+    args = (torch.from_numpy(ac).cuda(), torch.from_numpy(as_).cuda(), torch.from_numpy(bc).cuda().view(E, N, K),
+            torch.from_numpy(bs).cuda().view(E, N, K // 32), cuda_i32(off))
+    c16 = m4.moe_grouped_gemm_mx(*args, torch.bfloat16)
+    c32 = m4.moe_grouped_gemm_mx(*args, torch.float32)
+    cdg = m4.moe_grouped_gemm_bwd_dgrad(*args)
+    assert torch.equal(c32, cdg)
+    A64 = mx.dequant_rowwise(ac, as_)
+    B64 = mx.dequant_rowwise(bc, bs).reshape(E, N, K)
+    exact = og.grouped_nt(A64, B64, off)
+    got = fmt.bf16_to_f32(to_np(c16.view(torch.int16)).view(np.uint16)).astype(np.float64)
+    gemm_tol_check(got, exact, og.abs_bound_nt(A64, B64, off), "mx gemm bf16", out_bf16=True)

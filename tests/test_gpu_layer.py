@@ -78,6 +78,43 @@ def test_layer_config1_end_to_end():
         assert v < 2e-2, (key, v)
 
 
+def test_layer_mxfp8_forward_config1_end_to_end():
+    """The MXFP8-forward variant on the tiny layer: routing, the MXFP8 weights
+    and the gathered MXFP8 X are bit-exact; the weight requantisations (which
+    read only bit-exact inputs) too; U within the GEMM tolerance (bf16 out);
+    downstream outputs track the oracle normwise."""
+    inp = synth.config_inputs(1, device="cpu")
+    k = 2
+    E, d, F = 8, 256, 512
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    fw = layer.forward_mx(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k)
+    bw = layer.backward_mx(fw, dev["dy"], seed=synth.SR_SEED)
+    x = synth.bf16_bits(inp["x"])
+    ofw = olayer.forward_mx(x, synth.f32_np(inp["w_up"]), synth.f32_np(inp["w_down"]), synth.f32_np(inp["logits"]), k)
+    obw = olayer.backward_mx(ofw, synth.bf16_bits(inp["dy"]), seed=synth.SR_SEED)
+    assert_bytes_equal(to_np(fw["route"]["perm"]), ofw["perm"]["perm"], "perm")
+    for i, key in enumerate(("codes", "sf")):
+        assert_bytes_equal(to_np(fw["wq"]["wu"][i]), ofw["wu"][key], "wu " + key)
+        assert_bytes_equal(to_np(fw["wq"]["wd"][i]), ofw["wd"][key], "wd " + key)
+        assert_bytes_equal(to_np(fw["xq_perm"][i]), ofw["xq_perm"][key], "xq_perm " + key)
+    for key in ("wdT", "wuT"):
+        for i in range(2):
+            assert_bytes_equal(to_np(bw[key][i]), obw[key][i], f"{key} {i}")
+    off = ofw["perm"]["off"]
+    A64 = mx.dequant_rowwise(ofw["xq_perm"]["codes"], ofw["xq_perm"]["sf"])
+    B64 = mx.dequant_rowwise(ofw["wu"]["codes"], ofw["wu"]["sf"]).reshape(E, F, d)
+    U = fmt.bf16_to_f32(to_np(fw["U"].view(torch.int16)).view(np.uint16)).astype(np.float64)
+    gemm_tol_check(U, og.grouped_nt(A64, B64, off), og.abs_bound_nt(A64, B64, off), "U (MXFP8)", out_bf16=True)
+    errs = dict(y=_rel(fmt.bf16_to_f32(to_np(fw["y"])), fmt.bf16_to_f32(ofw["y"])),
+                dx=_rel(fmt.bf16_to_f32(to_np(bw["dx"])), fmt.bf16_to_f32(obw["dx"])),
+                dW_up=_rel(to_np(bw["dW_up"]), obw["dW_up"]),
+                dW_down=_rel(to_np(bw["dW_down"]), obw["dW_down"]),
+                dg=_rel(to_np(bw["dg"]).astype(np.float64), obw["dg"]))
+    print(f"MXFP8 forward: rel errors {errs}")
+    for key, v in errs.items():
+        assert v < 2e-2, (key, v)
+
+
 # ------------------------------------------------------- full-size launches
 
 @pytest.fixture(scope="module")

@@ -341,3 +341,44 @@ def test_fused_weight_quant_rejects_bad_shapes():
     w = torch.zeros(96, 64, device="cuda")
     with pytest.raises(m4.Moe4Error):
         m4.nvfp4_quant_requant_T(w, 2)                               # groups of 48 rows
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_mxfp8_quant_silu_pre_op(transpose):
+    """MXFP8 of silu(U) for bf16 U (the MXFP8 forward's H), bit-exact."""
+    R, F = 150, 128
+    u = synth.randn((R, F), 2.0, "cpu", 14, "u", torch.bfloat16)
+    h = osilu.silu_f32(synth.bf16_bits(u))
+    if transpose:
+        off = np.array([0, 40, 40, 150])
+        offp = mx.padded_offsets(off)
+        oc, os_ = m4.mxfp8_quant(u.cuda(), transpose=True, pre_op=m4.PRE_SILU, group_row_off=cuda_i32(off),
+                                 group_off_pad=cuda_i32(offp))
+        c_ref, s_ref = mx.quantize_transposed(h, off, mx.RNE)
+        n = F * offp[-1]
+        assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
+        assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
+    else:
+        oc, os_ = m4.mxfp8_quant(u.cuda(), pre_op=m4.PRE_SILU)
+        c_ref, s_ref = mx.quantize_rowwise(h, mx.RNE)
+        assert_bytes_equal(to_np(oc), c_ref, "codes")
+        assert_bytes_equal(to_np(os_), s_ref, "scales")
+
+
+@pytest.mark.parametrize("R,C,groups", [(64, 128, None), (100, 96, [0, 0, 33, 33, 34, 100]),
+                                        (517, 1056, [0, 200, 201, 480, 517])])
+@pytest.mark.parametrize("lay", [SF_ROWS, SF_BLOCKS])
+def test_requant_mx_sr_t_bit_exact(R, C, groups, lay):
+    """MXFP8 row-wise -> MXFP8 SR transposed (the MXFP8 forward's operands)."""
+    off = np.array([0, R]) if groups is None else np.array(groups)
+    offp = mx.padded_offsets(off)
+    rng = np.random.default_rng(R + C)
+    x = (rng.standard_normal((R, C)) * np.exp2(rng.integers(-8, 8, (R, 1)))).astype(np.float32)
+    x[rng.random((R, C)) < 0.002] *= 50.0
+    c, s = mx.quantize_rowwise(x, mx.RNE)
+    c_ref, s_ref = mx.requant_mx_sr_t(c, s, off, seed=5, stream_id=33, sf_layout=LAYOUTS[lay])
+    oc, os_ = m4.mxfp8_requant_mx_sr_T(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(), cuda_i32(off),
+                                       cuda_i32(offp), 5, 33, sf_layout=lay)
+    n = C * offp[-1]
+    assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
+    assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")

@@ -6,6 +6,7 @@ import torch
 import synth
 from oracle import formats as fmt
 from oracle import gemm
+from oracle import mxfp8 as mx
 from oracle import layer
 from oracle import nvfp4 as nv
 from oracle import silu
@@ -136,3 +137,36 @@ def test_dgates_brute_force_and_combine_link():
     comb = np.stack([sum(g[t, j] * Yp[inv[t * k + j]].astype(np.float64) for j in range(k)) for t in range(T)])
     rhs = (dyf.astype(np.float64) * comb).sum(axis=1)
     assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp8_forward_dense_reduction():
+    """E = 1, k = 1 and operands exact in MXFP8: U = bf16(x @ W_up^T) exactly,
+    Yp = deq(MXFP8(silu(U))) @ W_down^T, y = bf16(Yp)."""
+    rng = np.random.default_rng(31)
+    T, d, F = 40, 64, 96
+    x = (rng.integers(-3, 4, (T, d)) * 0.5).astype(np.float32)
+    wu = (rng.integers(-3, 4, (1, F, d)) * 0.25).astype(np.float32)
+    wd = (rng.integers(-3, 4, (1, d, F)) * 0.25).astype(np.float32)
+    xb = fmt.f64_to_bf16(x.astype(np.float64))
+    fw = layer.forward_mx(xb, wu, wd, np.zeros((T, 1), np.float32), 1)
+    U = fmt.f64_to_bf16(x.astype(np.float64) @ wu[0].T.astype(np.float64))
+    assert np.array_equal(fw["U"], U)
+    hc, hs = fw["hq"]["codes"], fw["hq"]["sf"]
+    Yp = (mx.dequant_rowwise(hc, hs) @ wd[0].T.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(fw["Yp"], Yp)
+    assert np.array_equal(fw["y"], fmt.bf16_round(Yp))
+
+
+def test_mxfp8_backward_tracks_float64():
+    i = _inputs(seed=7)
+    fw = layer.forward_mx(i["x"], i["w_up"], i["w_down"], i["logits"], 2)
+    bw = layer.backward_mx(fw, i["dy"])
+    T, d, F, E, k = fw["dims"]
+    assert bw["dW_up"].shape == (E, F, d) and bw["dW_down"].shape == (E, d, F) and bw["dx"].shape == (T, d)
+    off = fw["perm"]["off"]
+    H = silu.silu_f32(fw["U"]).astype(np.float64)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        ref = bw["dYp"][r0:r1].astype(np.float64).T @ H[r0:r1]
+        rel = np.linalg.norm(bw["dW_down"][e] - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert rel < 0.1

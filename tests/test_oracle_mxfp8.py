@@ -214,3 +214,31 @@ def test_wgrad_unbiased_over_seeds():
     rel = np.linalg.norm(acc / n - exact) / np.linalg.norm(exact)
     one = np.linalg.norm(U @ mx.dequant_transposed(*mx.requant_sr_t(q["codes"], q["sf"], q["ts"], off, False, 1, 0), off, d)[0].T - exact) / np.linalg.norm(exact)
     assert rel < one / 4          # averaging 128 draws shrinks the error ~ sqrt(128) ~ 11x
+
+
+def test_requant_mx_exact_values_and_unbiased():
+    """MXFP8 -> transpose -> MXFP8 SR: values that are exact in both blockings
+    pass unchanged; in general the requantisation is unbiased over seeds."""
+    rng = np.random.default_rng(21)
+    R, C = 96, 64
+    off = np.array([0, 40, 96])
+    x = (rng.integers(-15, 16, (R, C)) * 0.125).astype(np.float32)
+    c, s = mx.quantize_rowwise(x, mx.RNE)                     # exact: k / 8 with |k| < 16
+    assert np.array_equal(mx.dequant_rowwise(c, s), x.astype(np.float64))
+    for lay in (mx.SF_ROWS, mx.SF_BLOCKS):
+        tc, ts_ = mx.requant_mx_sr_t(c, s, off, seed=3, stream_id=1, sf_layout=lay)
+        blocks = mx.dequant_transposed(tc, ts_, off, C, lay)
+        for g in range(2):
+            assert np.array_equal(blocks[g][:, :off[g + 1] - off[g]], x[off[g]:off[g + 1]].T.astype(np.float64))
+    y = (rng.standard_normal((64, 32)) * np.exp2(rng.integers(-6, 6, (64, 1)))).astype(np.float32)
+    c, s = mx.quantize_rowwise(y, mx.RNE)
+    v = mx.dequant_rowwise(c, s)
+    acc = np.zeros((32, 64))
+    n = 400
+    for seed in range(n):
+        tc, ts_ = mx.requant_mx_sr_t(c, s, None, seed=seed, stream_id=0)
+        acc += mx.dequant_transposed(tc, ts_, [0, 64], 32)[0]
+    err = np.abs(acc / n - v.T)
+    # each SR step is at most one E4M3 grid step of its block: the mean converges
+    step = np.abs(v.T).max(axis=1, keepdims=True) * 2.0 ** -3
+    assert np.all(err <= 4 * step / np.sqrt(n) + 1e-30)
