@@ -85,8 +85,8 @@ def work_table(c, off, off_pad):
 
 # the library kernel behind each call (several calls may launch one kernel)
 KERNEL_OF = {
-    "F1 W_up quant (+ requant)": "k_amax + k_encode_requant_T",
-    "F1 W_down quant (+ requant)": "k_amax + k_encode_requant_T",
+    "F1 W_up quant (+ requant)": "k_encode_requant_T",
+    "F1 W_down quant (+ requant)": "k_encode_requant_T",
     "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
     "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_dma_bf16_128",
     "F8 down GEMM (NVFP4)": "k_gemm_fwd_dma_f32_128",
@@ -101,8 +101,8 @@ KERNEL_OF = {
     "B13 router backward": "k_route_backward",
 }
 
-# calls that launch several kernels (zero, amax, scale, encode; route's
-# four): not candidates for the single dominant kernel
+# calls that launch several kernels (workspace clear + quantiser; zero, amax,
+# scale, encode; route's four): not candidates for the single dominant kernel
 MULTI_KERNEL_CALLS = {"F1 W_up quant (+ requant)", "F1 W_down quant (+ requant)", "F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)",
                       "F7 SiLU + H quant (NVFP4 4/6)"}
 

@@ -12,9 +12,9 @@
 //   k_tensor_scale  S_g = fl(amax_g / (m_max * 448)), 1 for a zero group
 //   k_encode        one thread per 16-element block: both candidates, errors
 //                   in the fixed order, the choice, packed codes + scale byte
-// and, for weights, k_encode_requant_T in place of k_encode: the mode-6 codes
-// and, from them, the stochastic-rounding transposed MXFP8 copy the backward
-// pass needs (one pass over the float32 masters instead of two kernels).
+// and, for weights, k_encode_requant_T in place of all three: the group amax,
+// the mode-6 codes and, from them, the stochastic-rounding transposed MXFP8
+// copy the backward pass needs, in one persistent launch.
 // All float arithmetic is one IEEE binary32 operation per step (the library
 // is built with -ffp-contract=off), with correctly rounded division.
 #include "act.h"
@@ -280,119 +280,208 @@ static void launch_encode(bool four6, dim3 grid, hipStream_t s, const void* x, i
                        codes, sf, tab, bpt);
 }
 
-// Group offsets g * grows of G equal groups (the amax walk takes offsets).
-__global__ void k_uniform_offsets(int32_t* __restrict__ off, int G, int64_t grows) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g <= G) off[g] = (int32_t)(g * grows);
+// Weights, fused: float32 [G * grows, C] -> NVFP4 mode 6 (codes, scales and
+// the per-group tensor scales) and, from the same codes and the same steps as
+// k_requant_T, the transposed MXFP8 stochastic-rounding copy (group-major,
+// grows rows per group, no padding, row-major scales), in one persistent
+// launch.  Tile: 4 waves x (32 rows = one MX block) x 512 columns of one
+// group; lane l of wave w takes columns c0 + 8l .. c0 + 8l + 7 of the wave's
+// 32 rows, so lanes 2m and 2m+1 hold one 16-element NVFP4 block (its amax
+// through one shuffle) and each lane keeps its 32 code words for the
+// requantisation.
+//
+// The group amax must be complete before any of the group's blocks is
+// encoded, so the launch walks the tiles twice, taking tickets from a counter
+// in the workspace: tickets 0 .. n-1 fold tile t into its group's amax,
+// tickets n .. 2n-1 encode tile t - n after waiting for the group's amax
+// count.  Every tile of that group has a lower ticket, taken by a workgroup
+// that is running and never waits during an amax: the wait always ends (and
+// is bounded anyway; a flag in the workspace records a give-up).  One launch
+// instead of amax, tensor-scale and encode kernels removes two launch tails.
+// (Pairing each amax with an encode a few groups behind, so that the encode's
+// re-read hits the memory-side cache, measured slower: the encode is bound by
+// its ALU work and load latency at two workgroups per CU, not by HBM.)
+namespace wq {
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
 }
 
-// Weights, fused: float32 [G * grows, C] -> NVFP4 mode 6 (codes, scales; the
-// tensor scales come from the amax pass) and, from the same codes and the
-// same steps as k_requant_T, the transposed MXFP8 stochastic-rounding copy
-// (group-major, grows rows per group, no padding, row-major scales).  Tiling
-// as k_requant_T: 4 waves x (32 rows = one MX block) x 512 columns; lane l of
-// wave w takes columns c0 + 8l .. c0 + 8l + 7 of the wave's 32 rows, so lanes
-// 2m and 2m+1 hold one 16-element NVFP4 block (its amax through one shuffle)
-// and each lane keeps its 32 code words for the requantisation.  Rows are
-// read in groups of 4 with the next group's loads in flight.
-__global__ void __launch_bounds__(rq::THREADS) k_encode_requant_T(const float* __restrict__ x, int64_t C,
-                                                                  int64_t grows, int G, int64_t n_ct,
-                                                                  const float* __restrict__ ts, uint32_t base,
-                                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
-                                                                  uint8_t* __restrict__ out_c,
+__global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) k_encode_requant_T(const float* __restrict__ x, int64_t C,
+                                                                  int64_t grows, int G, uint32_t n_ct,
+                                                                  uint32_t n_item,
+                                                                  uint32_t* __restrict__ wsu, float* __restrict__ ts,
+                                                                  uint32_t base, uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ sf, uint8_t* __restrict__ out_c,
                                                                   uint8_t* __restrict__ out_s) {
   using namespace rq;
   __shared__ __attribute__((aligned(16))) uint8_t lq[COLS * ROWS];
   __shared__ uint8_t lsf[COLS * WAVES];  // [column][block]
   __shared__ int64_t lblk[WAVES][3];
+  __shared__ float s_red[WAVES];
+  __shared__ float s_S;
+  __shared__ uint32_t s_tk;
+  // Per group the float bits of the amax so far and the number of amax tiles
+  // folded in.  Device-scope atomics are performed at the memory side, so the
+  // two words need no cache fences, only order: the count is bumped after the
+  // maximum has returned, and read before the maximum.
+  uint32_t* amax = wsu;      // [G]
+  uint32_t* done = wsu + G;  // [G]
+  uint32_t* ticket = wsu + 2 * G;
+  uint32_t* gave_up = ticket + 1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * COLS;
-  const int64_t r0 = ((int64_t)(blockIdx.x / n_ct) * WAVES + w) * 32;  // the wave's first row
-  const bool present = r0 < grows * G;
-  const int g = present ? (int)(r0 / grows) : 0;
-  const int64_t pr_in_g = r0 - (int64_t)g * grows;
-  if (l == 0) {
-    lblk[w][0] = C * (int64_t)g * grows + pr_in_g;
-    lblk[w][1] = present ? grows : 0;
-    lblk[w][2] = C * (int64_t)g * grows / 32 + pr_in_g / 32;
-  }
-  const int64_t c = c0 + LCOLS * l;
-  auto put = [&](int k, int q, uint32_t v) {
-    const int col = LCOLS * l + q;
-    *reinterpret_cast<uint32_t*>(lq + col * ROWS + swz(col, 2 * w + (k >> 2)) * 16 + (k & 3) * 4) = v;
-  };
-  int ex[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) ex[q] = -127;
-  if (present && c < C) {  // (C % 16 == 0: both lanes of a 16-block agree)
-    const float S = ts[g];
-    const float* xr = x + r0 * C + c;
-    uint32_t cw[32], sbp[8];
-    float am[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) sbp[k] = 0u;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) am[q] = 0.0f;
-    f32x4 vb[2][4][2];
-    auto load_group = [&](int k, f32x4 (&b)[4][2]) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(xr + (int64_t)(4 * k + ii) * C);
-        b[ii][0] = p[0];
-        b[ii][1] = p[1];
-      }
-    };
-    load_group(0, vb[0]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k + 1 < 8) load_group(k + 1, vb[(k + 1) & 1]);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 4 * k + ii;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = vb[k & 1][ii][0][e];
-          v[4 + e] = vb[k & 1][ii][1][e];
-        }
-        float a = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));  // the block's other half
-        uint32_t sc;
-        cw[i] = encode_half(v, a, S, 6.0f, sc);
-        sbp[k] |= sc << (8 * ii);
-        *reinterpret_cast<uint32_t*>(codes + (r0 + i) * (C / 2) + c / 2) = cw[i];
-        if ((l & 1) == 0) sf[(r0 + i) * (C / 16) + c / 16] = (uint8_t)sc;
-        float q8[8];
-        dequant8(cw[i], sc, q8);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
-      }
-    }
-    float pc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ex[q] = mx_exponent(am[q] * S);
-      pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
-    }
-    const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
-    const uint32_t key0 = fmix32(base);
-    auto deq = [&](int i, float (&q)[8]) { dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
-    if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
-      requant_block<true, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
-    else
-      requant_block<false, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) put(k, q, 0u);
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
+  const uint32_t n_all = (uint32_t)G * n_item, n_tk = 2 * n_all;
+  const uint32_t key0 = fmix32(base);
+  if (tid == 0) s_tk = atomicAdd(ticket, 1u);
   __syncthreads();
-  rq_store_tile(lq, lsf, lblk, c0, C, 0, out_c, out_s);
+  uint32_t t = __builtin_amdgcn_readfirstlane(s_tk);
+  while (t < n_tk) {
+    uint32_t t_next = 0;
+    if (tid == 0) t_next = atomicAdd(ticket, 1u);  // in flight during this ticket
+    if (t < n_all) {  // ---- amax of tile t
+      const uint32_t g = t / n_item, j = t - g * n_item, jr = j / n_ct;
+      const int64_t pr = (int64_t)jr * ROWS + 32 * w, c = (int64_t)(j - jr * n_ct) * COLS + LCOLS * l;
+      float m = 0.0f;
+      if (pr < grows && c < C) {
+        const float* xr = x + ((int64_t)g * grows + pr) * C + c;
+        f32x4 vb[2][4][2];
+        auto load4 = [&](int k, f32x4 (&b)[4][2]) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const f32x4* q = reinterpret_cast<const f32x4*>(xr + (int64_t)(4 * k + ii) * C);
+            b[ii][0] = q[0];
+            b[ii][1] = q[1];
+          }
+        };
+        load4(0, vb[0]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k + 1 < 8) load4(k + 1, vb[(k + 1) & 1]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              m = fmaxf(m, fmaxf(fabsf(vb[k & 1][ii][0][e]), fabsf(vb[k & 1][ii][1][e])));
+        }
+      }
+      m = wave_max(m);
+      if (l == 0) s_red[w] = m;
+      __syncthreads();
+      if (tid == 0) {
+        float mm = s_red[0];
+#pragma unroll
+        for (int q = 1; q < WAVES; ++q) mm = fmaxf(mm, s_red[q]);
+        // mm >= 0: its bit pattern orders as its value, and the old value's
+        // sign bit (always 0) makes the count wait for the maximum's return
+        const uint32_t old = __hip_atomic_fetch_max(amax + g, __float_as_uint(mm), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(done + g, 1u + (old >> 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    else {  // ---- encode + requantise tile t - n_all
+      const uint32_t it = t - n_all, g = it / n_item, j = it - g * n_item, jr = j / n_ct;
+      const int64_t c0 = (int64_t)(j - jr * n_ct) * COLS, pr = (int64_t)jr * ROWS + 32 * w;  // wave's first row in g
+      const bool present = pr < grows;
+      const int64_t r0 = (int64_t)g * grows + pr;
+      if (tid == 0) {
+        uint32_t n = 0, spins = 0;
+        while ((n = __hip_atomic_load(done + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < n_item &&
+               ++spins < wq::SPIN_LIMIT)
+          __builtin_amdgcn_s_sleep(8);
+        if (n < n_item) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // (n >> 31 is 0: the address waits for the count)
+        const float a = __uint_as_float(__hip_atomic_load(amax + g + (n >> 31), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT));
+        const float sv = a / (6.0f * 448.0f);
+        s_S = (sv == 0.0f) ? 1.0f : sv;
+        if (j == 0) ts[g] = s_S;
+      }
+      if (l == 0) {
+        lblk[w][0] = C * (int64_t)g * grows + pr;
+        lblk[w][1] = present ? grows : 0;
+        lblk[w][2] = C * (int64_t)g * grows / 32 + pr / 32;
+      }
+      __syncthreads();
+      const float S = s_S;
+      const int64_t c = c0 + LCOLS * l;
+      auto put = [&](int k, int q, uint32_t v) {
+        const int col = LCOLS * l + q;
+        *reinterpret_cast<uint32_t*>(lq + col * ROWS + swz(col, 2 * w + (k >> 2)) * 16 + (k & 3) * 4) = v;
+      };
+      int ex[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ex[q] = -127;
+      if (present && c < C) {  // (C % 16 == 0: both lanes of a 16-block agree)
+        const float* xr = x + r0 * C + c;
+        uint32_t cw[32], sbp[8];
+        float am[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sbp[k] = 0u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) am[q] = 0.0f;
+        f32x4 vb[2][4][2];
+        auto load_group = [&](int k, f32x4 (&b)[4][2]) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(xr + (int64_t)(4 * k + ii) * C);
+            b[ii][0] = p[0];
+            b[ii][1] = p[1];
+          }
+        };
+        load_group(0, vb[0]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k + 1 < 8) load_group(k + 1, vb[(k + 1) & 1]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * k + ii;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = vb[k & 1][ii][0][e];
+              v[4 + e] = vb[k & 1][ii][1][e];
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+            a = fmaxf(a, __shfl_xor(a, 1, 64));  // the block's other half
+            uint32_t sc;
+            cw[i] = encode_half(v, a, S, 6.0f, sc);
+            sbp[k] |= sc << (8 * ii);
+            *reinterpret_cast<uint32_t*>(codes + (r0 + i) * (C / 2) + c / 2) = cw[i];
+            if ((l & 1) == 0) sf[(r0 + i) * (C / 16) + c / 16] = (uint8_t)sc;
+            float q8[8];
+            dequant8(cw[i], sc, q8);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
+          }
+        }
+        float pc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          ex[q] = mx_exponent(am[q] * S);
+          pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
+        }
+        const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
+        auto deq = [&](int i, float (&q)[8]) { dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
+        if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
+          requant_block<true, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
+        else
+          requant_block<false, true>(deq, 32, S, pc, j0, C / 2, base, key0, put);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) put(k, q, 0u);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
+      __syncthreads();
+      rq_store_tile(lq, lsf, lblk, c0, C, 0, out_c, out_s);
+    }
+    __syncthreads();  // LDS free for the next ticket
+    if (tid == 0) s_tk = t_next;
+    __syncthreads();
+    t = __builtin_amdgcn_readfirstlane(s_tk);
+  }
 }
 
 __global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
@@ -485,9 +574,11 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   return check_launch("nvfp4_quant_46");
 }
 
+// Workspace: amax bits [G], finished amax tiles [G], the ticket counter and
+// the wait give-up flag, all 32-bit words cleared before the launch.
 extern "C" size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups) {
   const size_t g = (size_t)(n_groups > 0 ? n_groups : 1);
-  return (g * sizeof(uint32_t) + 15) / 16 * 16 + (g + 1) * sizeof(int32_t);
+  return (2 * g + 2) * sizeof(uint32_t);
 }
 
 extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint8_t* codes,
@@ -508,20 +599,20 @@ extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols,
   hipStream_t s = as_stream(stream);
   const int G = n_groups;
   const int64_t grows = rows / G;
-  uint32_t* amax = static_cast<uint32_t*>(ws);
-  int32_t* off = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ((size_t)G * sizeof(uint32_t) + 15) / 16 * 16);
-  hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
-  hipLaunchKernelGGL(k_uniform_offsets, dim3((G + 1 + 255) / 256), dim3(256), 0, s, off, G, grows);
-  if (rows > 0)
-    hipLaunchKernelGGL((k_amax<MOE4_F32, false>), walk_grid(rows * cols), dim3(QTHREADS), 0, s, x, rows, cols, off, G,
-                       amax, nullptr);
-  hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, 6.0f * 448.0f, tensor_scale);
-  if (rows > 0) {
-    const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (rows + rq::ROWS - 1) / rq::ROWS;
-    MOE4_REQUIRE(n_ct * n_rt < (int64_t)1 << 31, MOE4_EINVAL, "nvfp4_quant_requant_T: tensor too large");
-    hipLaunchKernelGGL(k_encode_requant_T, dim3((unsigned)(n_ct * n_rt)), dim3(rq::THREADS), 0, s, x, cols, grows, G,
-                       n_ct, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
+  uint32_t* wsu = static_cast<uint32_t*>(ws);
+  const int n_words = 2 * G + 2;
+  hipLaunchKernelGGL(k_zero_u32, dim3((n_words + 255) / 256), dim3(256), 0, s, wsu, n_words);
+  if (rows == 0) {  // empty groups: tensor scale 1
+    hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, wsu, G, 6.0f * 448.0f, tensor_scale);
+    return check_launch("nvfp4_quant_requant_T");
   }
+  const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_item = (grows + rq::ROWS - 1) / rq::ROWS * n_ct;
+  const int64_t n_total = (int64_t)G * n_item;
+  const int64_t slots = (int64_t)cu_count_q() * 2;  // two 64 KB-LDS workgroups per CU
+  MOE4_REQUIRE(2 * n_total + slots < ((int64_t)1 << 31), MOE4_EINVAL, "nvfp4_quant_requant_T: tensor too large");
+  const int64_t grid = 2 * n_total < slots ? 2 * n_total : slots;
+  hipLaunchKernelGGL(k_encode_requant_T, dim3((unsigned)grid), dim3(rq::THREADS), 0, s, x, cols, grows, G,
+                     (uint32_t)n_ct, (uint32_t)n_item, wsu, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
   return check_launch("nvfp4_quant_requant_T");
 }
 

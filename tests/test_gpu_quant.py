@@ -313,7 +313,10 @@ def test_run_twice_deterministic():
     assert torch.equal(r1[0][:n], r2[0][:n]) and torch.equal(r1[1][:n // 32], r2[1][:n // 32])
 
 
-@pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96)])
+# The last two have more tiles than the launch has workgroups (two per CU), so
+# workgroups take many amax and encode tickets each.
+@pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96), (320, 32, 512),
+                                    (200, 96, 1056)])
 def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
     """nvfp4_quant_requant_T equals nvfp4_quant_46 (mode 6, G equal groups)
     followed by mxfp8_requant_sr_T (row-major scales), byte for byte, against
