@@ -945,6 +945,221 @@ __global__ void __launch_bounds__(wsg::NT, 1)
   }
 }
 
+// dgrad, warp-specialised and persistent (K % 128 == 0, N % 128 == 0): the
+// structure of the forward NVFP4 kernel of this library (four producer waves
+// that only issue direct-to-LDS loads into a four-stage ring, four consumer
+// waves that only read LDS, run the MFMAs and store; one barrier per slab;
+// m-tile-major tiles in contiguous per-XCD runs) with 128 x 128 tiles, so a
+// small expert wastes at most 127 padded rows, and the MXFP8 slab of the
+// kernel above: 128 code bytes and 4 scale bytes per row and slab, scales
+// row-major.
+namespace dws {
+constexpr int TM = 128, TN = 128, S = 4, NCW = 4, NT = 64 * (NCW + 4);
+constexpr int CODE = TM * dmag::BK, SCL = TM * 4;  // per operand and stage
+constexpr int STAGE = 2 * CODE + 2 * SCL;
+constexpr int I = 9;  // loads per producer wave and slab: 4 + 4 code row groups, 1 scale group
+}  // namespace dws
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(dws::NT, 1)
+    k_dgrad_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
+               const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
+               const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N, int64_t K,
+               void* __restrict__ c) {
+  using namespace dws;
+  using dmag::lds_ptr;
+  using dmag::swz;
+  using wsg::wait_vm;
+  using wsg::WAIT_LGKM0;
+  constexpr int BK = dmag::BK;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
+  __shared__ uint32_t s_nmt;
+  const __attribute__((address_space(4))) int32_t* coff = (const __attribute__((address_space(4))) int32_t*)off;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // total m-tiles (before any load into LDS is in flight)
+  if (w == 0) {
+    uint32_t n = 0;
+    for (int e = l; e < E; e += 64) n += (uint32_t)((off[e + 1] - off[e] + TM - 1) / TM);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
+    if (l == 0) s_nmt = n;
+  }
+  __syncthreads();
+  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;
+  const uint32_t KS = (uint32_t)(K / 32), nk = (uint32_t)(K / BK);
+  const uint32_t xcd = blockIdx.x % 8, per = (n_all + 7) / 8;
+  const uint32_t stride = (gridDim.x - xcd + 7) / 8;
+  const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
+
+  if (w >= NCW) {
+    // ---- producer pw: rows 32 pw .. 32 pw + 31 of both operands' codes and
+    // one 64-row group of scales (A rows 0-63, A 64-127, B 0-63, B 64-127)
+    const int pw = w - NCW;
+    const bool sopb = pw >= 2;
+    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * K);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * KS);
+    __amdgpu_buffer_rsrc_t rbc = rac, rbs = ras;
+    uint32_t aoff[4], boff[4], soff = 0;
+    MtCursor<TM> cur;
+    uint32_t pt = t0, ps = 0;
+    bool more = false;
+    auto seek = [&]() {
+      more = pt < t_end && cur.seek(off, E, pt / n_nt);
+      if (!more) return;
+      const int e = cur.e;
+      const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
+      const int64_t row0 = (int64_t)coff[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+      rbc = make_rsrc(b_codes + (int64_t)e * N * K, (uint64_t)N * K);
+      rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
+      // rows past the operands are clamped to the last row: valid memory whose
+      // results are never stored
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * pw + 8 * q + (l >> 3);
+        const int64_t ra = row0 + r < M_total ? row0 + r : M_total - 1;
+        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
+        aoff[q] = (uint32_t)ra * (uint32_t)K + 16u * (uint32_t)swz(r, l & 7);
+        boff[q] = (uint32_t)rb * (uint32_t)K + 16u * (uint32_t)swz(r, l & 7);
+      }
+      const int sr = 64 * (pw & 1) + l;
+      const int64_t srow = sopb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
+      soff = (uint32_t)srow * KS;
+      ps = 0;
+    };
+    seek();
+    auto issue = [&](int st) {
+      uint8_t* base = ring + st * STAGE;
+      const uint32_t kb = ps * (uint32_t)BK, ksb = ps * (uint32_t)(BK / 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(base + (4 * pw + q) * 1024), 16, aoff[q] + kb, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + CODE + (4 * pw + q) * 1024), 16, boff[q] + kb, 0,
+                                                 0, 0);
+      uint8_t* sb = base + 2 * CODE + (sopb ? SCL : 0) + (pw & 1) * 256;
+      if (sopb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 4, soff + ksb, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 4, soff + ksb, 0, 0, 0);
+      if (++ps == nk) {
+        pt += stride;
+        seek();
+      }
+    };
+    uint32_t n_iss = 0;
+    for (int st = 0; st < S - 1 && more; ++st) {
+      issue(st);
+      ++n_iss;
+    }
+    for (uint32_t gs = 0; gs < n_iss; ++gs) {
+      // slab gs landed (later slabs may still be in flight), then the barrier
+      const uint32_t rem = n_iss - 1 - gs;
+      __builtin_amdgcn_sched_barrier(0);
+      if (rem >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * I));
+      else if (rem == 1) __builtin_amdgcn_s_waitcnt(wait_vm(I));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      if (more) {
+        issue((int)((gs + S - 1) % S));
+        ++n_iss;
+      }
+    }
+    return;
+  }
+  // ---- consumers: wave w owns the 64 x 64 quadrant (w / 2, w % 2)
+  constexpr int MI = 2, NJ = 2;
+  const int g = (l >> 5) & 1, li = l & 31;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  // one slab: two 64-element k steps; lane half g supplies K chunks
+  // 4 ks + g and 4 ks + 2 + g and the scale of block 2 ks + g
+  auto compute = [&](const uint8_t* base) {
+    const uint8_t* la = base;
+    const uint8_t* lb = base + CODE;
+    const uint8_t* sa = base + 2 * CODE;
+    const uint8_t* sb = base + 2 * CODE + SCL;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fa[MI], fb[NJ];
+      int ya[MI], yb[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm + i * 32 + li;
+        const uint8_t* p = la + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        ya[i] = sa[r * 4 + ks * 2 + g];
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = wn + j * 32 + li;
+        const uint8_t* p = lb + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        yb[j] = sb[r * 4 + ks * 2 + g];
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
+    }
+  };
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  const uint32_t ld = (uint32_t)N * ESZ;  // output row pitch in bytes
+  const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * ESZ;
+  MtCursor<TM> cur;
+  uint32_t gs = 0;
+  for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
+    const int e = cur.e;
+    const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
+    const int64_t row0 = (int64_t)coff[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+    const int64_t row_end = (int64_t)coff[e + 1] < M_total ? (int64_t)coff[e + 1] : M_total;
+    // waves whose rows all lie past the expert's last row skip their MFMAs
+    const bool active = row0 + wm < row_end;
+    for (uint32_t s = 0; s < nk; ++s, ++gs) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      if (active) compute(ring + (gs % S) * STAGE);
+    }
+    // epilogue: each value straight from the accumulators; the descriptor
+    // covers the tile's rows up to the expert's last, so stores of rows past
+    // it are dropped
+    const int64_t nrows = row_end - row0 < TM ? row_end - row0 : TM;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<uint8_t*>(c) + row0 * (int64_t)ld, (uint64_t)nrows * ld);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (active) {
+          const uint32_t fo = (uint32_t)(wm + i * 32) * ld + (uint32_t)(n0 + wn + j * 32) * ESZ;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t so = fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld;
+            if (OUT_BF16)
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(acc[i][j][v]), rC, lane_off, so,
+                                                    wsg::NT_STORE);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rC, lane_off, so, wsg::NT_STORE);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      }
+  }
+}
+
 static int cu_count() {
   static int n[64] = {0};
   int dev = 0;
@@ -960,7 +1175,7 @@ static int cu_count() {
 static int mx_tile_choice(int mode) {
   static int v[2] = {[] {
                        const char* e = getenv("MOE4_MX_TILE");
-                       return e ? atoi(e) : 8;
+                       return e ? atoi(e) : 11;
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
@@ -996,14 +1211,22 @@ static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 // set), 5 = 256x256 2x2 with one register set, 6 = 256x256 2x2 with
 // double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves;
 // dgrad only: 8 = direct-to-LDS loads, 256x256 (the default when
-// K % 128 == 0, else 6), 9 = as 8 with 128x128 tiles at 2 blocks/CU; wgrad
+// K % 128 == 0 and N % 128 != 0, else 6), 9 = as 8 with 128x128 tiles at 2
+// blocks/CU, 11 = the warp-specialized persistent kernel (the default when
+// K % 128 == 0 and N % 128 == 0); wgrad
 // only: 10 = the warp-specialized persistent kernel (the default; needs
 // E <= 2048 and 32-bit tile and output indices, else configuration 1, the
 // persistent register-staged kernel).
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   int choice = mx_tile_choice(0);
-  if ((choice == 8 || choice == 9) && K % dmag::BK != 0) choice = 6;
+  if (choice == 11 && N % dws::TN != 0) choice = 8;
+  if ((choice == 8 || choice == 9 || choice == 11) && K % dmag::BK != 0) choice = 6;
+  if (choice == 11) {
+    hipLaunchKernelGGL(k_dgrad_ws<false>, dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off, E, M, N,
+                       K, static_cast<void*>(c));
+    return;
+  }
   if (choice == 8 || choice == 9) {
     const int T = choice == 8 ? 256 : 128;
     const int64_t n_nt = (N + T - 1) / T;
@@ -1080,6 +1303,11 @@ extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, 
   MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_mx: A and each expert's B must stay below 2 GiB");
   if (M_total == 0) return MOE4_OK;
+  if (N % dws::TN == 0 && mx_tile_choice(0) == 11) {
+    hipLaunchKernelGGL(k_dgrad_ws<true>, dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream), a_codes, a_sf,
+                       b_codes, b_sf, expert_off, E, M_total, N, K, c);
+    return check_launch("moe_grouped_gemm_mx");
+  }
   const int64_t n_nt = (N + 255) / 256;
   const int64_t n_all = n_nt * ((M_total + 255) / 256 + E);
   hipLaunchKernelGGL(k_mx_gemm_dma_256_bf16, dim3((unsigned)xcd_grid(n_all)), dim3(dmag::NT), 0, as_stream(stream),

@@ -226,6 +226,24 @@ __device__ inline int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 }  // namespace fdma
 
+// Exact float value of byte sel of w as an E4M3 code (gfx950's converter
+// decodes the OCP E4M3 format; sel is a constant after unrolling).
+__device__ inline float e4m3_byte_f32(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
+// The mantissa 1.m of a scale (1 for 0) as two equal f16 halves: its three
+// fraction bits move from the float32 to the f16 fraction field.
+__device__ inline f16x2 mant_f16x2(float scf) {
+  const uint32_t h = 0x3C00u | ((__float_as_uint(scf) >> 13) & 0x3FFu);
+  return __builtin_bit_cast(f16x2, h * 0x10001u);
+}
+
 // 8 exact f16 values of one k step: code dword (8 E2M1 codes), the E4M3
 // scale as float (its power of two applies in the convert) and its mantissa.
 __device__ inline f16x8 dequant8_f16(uint32_t codes, float scf, f16x2 m2) {
@@ -240,7 +258,131 @@ __device__ inline f16x8 dequant8_f16(uint32_t codes, float scf, f16x2 m2) {
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-template <bool OUT_BF16, int BM, int BN>
+// One 256-element K slab of a wave's MI x NJ fragments from the LDS layout
+// above (codes [rows][128 bytes], chunks swizzled; scales [rows][16 bytes]):
+// 4 groups of 4 k steps; per group each fragment's 16 code bytes (one b128
+// read) and, per pair of steps, its scale.
+template <int MI, int NJ>
+__device__ __forceinline__ void fp4_slab_mfma(f32x16 (&acc)[MI][NJ], const uint8_t* la, const uint8_t* lb,
+                                              const uint8_t* sa, const uint8_t* sb, int wm, int wn, int g, int li) {
+  using namespace fdma;
+  u32x2 sca[MI], scb[NJ];  // the lane's 8 scale bytes per fragment
+#pragma unroll
+  for (int i = 0; i < MI; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) scb[j] = *reinterpret_cast<const u32x2*>(sb + (wn + j * 32 + li) * 16 + 8 * g);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    u32x4 ca[MI], cb[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm + i * 32 + li;
+      ca[i] = *reinterpret_cast<const u32x4*>(la + r * RB + 16 * swz(r, 4 * g + grp));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn + j * 32 + li;
+      cb[j] = *reinterpret_cast<const u32x4*>(lb + r * RB + 16 * swz(r, 4 * g + grp));
+    }
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {  // pairs of k steps share a 16-element scale block
+      float sfa[MI], sfb[NJ];
+      f16x2 ma[MI], mb[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        sfa[i] = e4m3_byte_f32(sca[i][grp >> 1], (grp & 1) * 2 + hp);
+        ma[i] = mant_f16x2(sfa[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        sfb[j] = e4m3_byte_f32(scb[j][grp >> 1], (grp & 1) * 2 + hp);
+        mb[j] = mant_f16x2(sfb[j]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kq = hp * 2 + st;  // step within the group: code dword kq
+        f16x8 av[MI], bv[NJ];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) av[i] = dequant8_f16(ca[i][kq], sfa[i], ma[i]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bv[j] = dequant8_f16(cb[j][kq], sfb[j], mb[j]);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The same slab as a software pipeline over its 16 k steps: the fragments of
+// step s + 1 are dequantised (and the next group's code words read) while
+// step s's MFMAs run, so the matrix unit need not idle behind the conversions
+// of its own wave when no other wave of the SIMD computes.
+template <int MI, int NJ>
+__device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const uint8_t* la, const uint8_t* lb,
+                                                   const uint8_t* sa, const uint8_t* sb, int wm, int wn, int g,
+                                                   int li) {
+  using namespace fdma;
+  u32x2 sca[MI], scb[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) scb[j] = *reinterpret_cast<const u32x2*>(sb + (wn + j * 32 + li) * 16 + 8 * g);
+  u32x4 ca[2][MI], cb[2][NJ];
+  f16x8 av[2][MI], bv[2][NJ];
+  float sfa[MI], sfb[NJ];
+  f16x2 ma[MI], mb[NJ];
+  auto read_codes = [&](int grp) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm + i * 32 + li;
+      ca[grp & 1][i] = *reinterpret_cast<const u32x4*>(la + r * RB + 16 * swz(r, 4 * g + grp));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn + j * 32 + li;
+      cb[grp & 1][j] = *reinterpret_cast<const u32x4*>(lb + r * RB + 16 * swz(r, 4 * g + grp));
+    }
+  };
+  auto scales = [&](int grp, int hp) {  // step pair hp of group grp shares a 16-element block
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      sfa[i] = e4m3_byte_f32(sca[i][grp >> 1], (grp & 1) * 2 + hp);
+      ma[i] = mant_f16x2(sfa[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      sfb[j] = e4m3_byte_f32(scb[j][grp >> 1], (grp & 1) * 2 + hp);
+      mb[j] = mant_f16x2(sfb[j]);
+    }
+  };
+  auto dequant = [&](int st) {  // step st = 4 grp + kq of the slab
+    const int grp = st >> 2, kq = st & 3;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) av[st & 1][i] = dequant8_f16(ca[grp & 1][i][kq], sfa[i], ma[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bv[st & 1][j] = dequant8_f16(cb[grp & 1][j][kq], sfb[j], mb[j]);
+  };
+  read_codes(0);
+  scales(0, 0);
+  dequant(0);
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    if (st % 4 == 0 && st + 4 < 16) read_codes((st >> 2) + 1);
+    if (st + 1 < 16) {
+      if ((st + 1) % 2 == 0) scales((st + 1) >> 2, ((st + 1) >> 1) & 1);
+      dequant(st + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[st & 1][i], bv[st & 1][j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <bool OUT_BF16, int BM, int BN, bool PIPE>
 __device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_codes,
                                                              const uint8_t* __restrict__ a_sf,
                                                              const float* __restrict__ a_ts, int a_ts_per_group,
@@ -327,60 +469,11 @@ __device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-  // one slab: 4 groups of 4 k steps; per group each fragment's 16 code bytes
-  // (one b128 read) and, per pair of steps, its scale
   auto compute = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
-    u32x2 sca[MI], scb[NJ];  // the lane's 8 scale bytes per fragment
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) scb[j] = *reinterpret_cast<const u32x2*>(sb + (wn + j * 32 + li) * 16 + 8 * g);
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      u32x4 ca[MI], cb[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = wm + i * 32 + li;
-        ca[i] = *reinterpret_cast<const u32x4*>(la + r * RB + 16 * swz(r, 4 * g + grp));
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int r = wn + j * 32 + li;
-        cb[j] = *reinterpret_cast<const u32x4*>(lb + r * RB + 16 * swz(r, 4 * g + grp));
-      }
-#pragma unroll
-      for (int hp = 0; hp < 2; ++hp) {  // pairs of k steps share a 16-element scale block
-        float sfa[MI], sfb[NJ];
-        f16x2 ma[MI], mb[NJ];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const uint32_t byte = (sca[i][grp >> 1] >> (8 * ((grp & 1) * 2 + hp))) & 0xFFu;
-          sfa[i] = e4m3_to_f32(byte);
-          const _Float16 mh = (_Float16)mant_factor(sfa[i]);
-          ma[i] = f16x2{mh, mh};
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const uint32_t byte = (scb[j][grp >> 1] >> (8 * ((grp & 1) * 2 + hp))) & 0xFFu;
-          sfb[j] = e4m3_to_f32(byte);
-          const _Float16 mh = (_Float16)mant_factor(sfb[j]);
-          mb[j] = f16x2{mh, mh};
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int kq = hp * 2 + st;  // step within the group: code dword kq
-          f16x8 av[MI], bv[NJ];
-#pragma unroll
-          for (int i = 0; i < MI; ++i) av[i] = dequant8_f16(ca[i][kq], sfa[i], ma[i]);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) bv[j] = dequant8_f16(cb[j][kq], sfb[j], mb[j]);
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
+    fp4_slab_mfma<MI, NJ>(acc, la, lb, sa, sb, wm, wn, g, li);
+  };
+  auto compute_pipe = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+    fp4_slab_mfma_pipe<MI, NJ>(acc, la, lb, sa, sb, wm, wn, g, li);
   };
   // waves whose rows all lie past a small expert's last row skip their MFMAs
   const int64_t left = row_end - (row0 + wm);
@@ -391,20 +484,24 @@ __device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto slab = [&](const uint8_t* la, const uint8_t* lb, const uint8_t* sa, const uint8_t* sb) {
+    if (PIPE) compute_pipe(la, lb, sa, sb);
+    else compute(la, lb, sa, sb);
+  };
   const uint32_t nk = (uint32_t)(K / BKE);
   issue(la0, lb0, sa0, sb0, 0);
   uint32_t s = 0;
   for (; s + 2 <= nk; s += 2) {
     sync();
     issue(la1, lb1, sa1, sb1, (s + 1) * BKE);
-    if (active) compute(la0, lb0, sa0, sb0);
+    if (active) slab(la0, lb0, sa0, sb0);
     sync();
     if (s + 2 < nk) issue(la0, lb0, sa0, sb0, (s + 2) * BKE);
-    if (active) compute(la1, lb1, sa1, sb1);
+    if (active) slab(la1, lb1, sa1, sb1);
   }
   if (s < nk) {
     sync();
-    if (active) compute(la0, lb0, sa0, sb0);
+    if (active) slab(la0, lb0, sa0, sb0);
   }
   // Epilogue: 32-row bands of each wave's tile through LDS (free after the
   // last barrier), scaled by S_a * S_b, written as row-contiguous 16-byte
@@ -445,20 +542,210 @@ __device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_
 }
 
 // One kernel per configuration (the body is a device template).
-#define MOE4_FWD_DMA_KERNEL(NAME, OUT_BF16, BM, BN, MINB)                                                          \
+#define MOE4_FWD_DMA_KERNEL(NAME, OUT_BF16, BM, BN, MINB, PIPE)                                                         \
   __global__ void __launch_bounds__(fdma::NT, MINB)                                                               \
       NAME(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,  \
            int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,             \
            const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,    \
            int64_t K, int64_t n_ntiles, int64_t n_all, void* __restrict__ c) {                                    \
-    gemm_fwd_dma_body<OUT_BF16, BM, BN>(a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, off, E, M_total, \
+    gemm_fwd_dma_body<OUT_BF16, BM, BN, PIPE>(a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, off, E, M_total, \
                                         N, K, n_ntiles, n_all, c);                                                 \
   }
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_256, true, 256, 256, 1)
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_256, false, 256, 256, 1)
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_128, true, 128, 128, 2)
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_256, true, 256, 256, 1, true)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_256, false, 256, 256, 1, true)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_128, true, 128, 128, 2, false)
+MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2, false)
 #undef MOE4_FWD_DMA_KERNEL
+
+// ------------------------------------------- warp-specialised persistent variant
+// K % 256 == 0.  One workgroup of 8 waves per CU walks 128 x 128 tiles.
+// Four producer waves only issue direct-to-LDS loads of 256-element K slabs
+// (the layout of the kernel above: 16 KB of codes and 2 KB of scales per
+// operand) into a four-stage ring; four consumer waves only read LDS,
+// dequantise and run the f16 MFMAs (64 x 64 each) and store their results
+// straight from the accumulators.  gfx950 counts a wave's loads and stores on
+// one counter that completes in issue order, so a wave that both loads and
+// stores would wait for its stores' acknowledgements before each slab; here
+// no wave does both.  One barrier per slab: producers wait for slab s with an
+// explicit count (the later slabs stay in flight), consumers only for their
+// own LDS reads of slab s - 1.  Tiles: m-tile major (the m-tiles of expert e
+// follow those of e - 1), n fastest; each XCD takes a contiguous run of the
+// tile list (tiles cost the same, so the runs balance) and its workgroups
+// stride through it, so concurrent tiles share A rows and the expert's B in
+// that XCD's L2.
+namespace fws {
+constexpr int TM = 128, TN = 128, S = 4, NCW = 4, NT = 64 * (NCW + 4);
+constexpr int CODE = TM * fdma::RB, SCL = TM * 16;  // per operand and stage
+constexpr int STAGE = 2 * CODE + 2 * SCL;
+constexpr int I = 9;  // loads per producer wave and slab: 4 + 4 code row groups, 1 scale group
+constexpr uint32_t OOB = 0x80000000u;
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
+}  // namespace fws
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(fws::NT, 1)
+    k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
+                  int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
+                  const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,
+                  int64_t K, void* __restrict__ c) {
+  using namespace fws;
+  using fdma::lds_ptr;
+  using fdma::swz;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
+  __shared__ uint32_t s_nmt;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // total m-tiles (before any load into LDS is in flight)
+  if (w == 0) {
+    uint32_t n = 0;
+    for (int e = l; e < E; e += 64) n += (uint32_t)((off[e + 1] - off[e] + TM - 1) / TM);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
+    if (l == 0) s_nmt = n;
+  }
+  __syncthreads();
+  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;  // N % 128 == 0 (checked at launch)
+  const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16), nk = (uint32_t)(K / fdma::BKE);
+  // this workgroup's tiles: t0, t0 + stride, ... < t_end
+  const uint32_t xcd = blockIdx.x % 8, per = (n_all + 7) / 8;
+  const uint32_t stride = (gridDim.x - xcd + 7) / 8;
+  const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
+
+  if (w >= NCW) {
+    // ---- producer pw: rows 32 pw .. 32 pw + 31 of both operands' codes and
+    // one 64-row group of scales (A rows 0-63, A 64-127, B 0-63, B 64-127)
+    const int pw = w - NCW;
+    const bool sopb = pw >= 2;
+    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * KB);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * KS);
+    __amdgpu_buffer_rsrc_t rbc = rac, rbs = ras;
+    uint32_t aoff[4], boff[4], soff = 0;
+    MtCursor<TM> cur;
+    uint32_t pt = t0, ps = 0;
+    bool more = false;
+    auto seek = [&]() {
+      more = pt < t_end && cur.seek(off, E, pt / n_nt);
+      if (!more) return;
+      const int e = cur.e;
+      const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
+      const int64_t row0 = (int64_t)off[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+      rbc = make_rsrc(b_codes + (int64_t)e * N * KB, (uint64_t)N * KB);
+      rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
+      // rows past the operands are clamped to the last row: valid memory whose
+      // results are never stored
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * pw + 8 * q + (l >> 3);
+        const int64_t ra = row0 + r < M_total ? row0 + r : M_total - 1;
+        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
+        aoff[q] = (uint32_t)ra * KB + 16u * (uint32_t)swz(r, l & 7);
+        boff[q] = (uint32_t)rb * KB + 16u * (uint32_t)swz(r, l & 7);
+      }
+      const int sr = 64 * (pw & 1) + l;
+      const int64_t srow = sopb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
+      soff = (uint32_t)srow * KS;
+      ps = 0;
+    };
+    seek();
+    auto issue = [&](int st) {
+      uint8_t* base = ring + st * STAGE;
+      const uint32_t kb = ps * (uint32_t)fdma::RB, ksb = ps * 16u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(base + (4 * pw + q) * 1024), 16, aoff[q] + kb, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + CODE + (4 * pw + q) * 1024), 16, boff[q] + kb, 0,
+                                                 0, 0);
+      uint8_t* sb = base + 2 * CODE + (sopb ? SCL : 0) + (pw & 1) * 1024;
+      if (sopb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 16, soff + ksb, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 16, soff + ksb, 0, 0, 0);
+      if (++ps == nk) {
+        pt += stride;
+        seek();
+      }
+    };
+    uint32_t n_iss = 0;
+    for (int st = 0; st < S - 1 && more; ++st) {
+      issue(st);
+      ++n_iss;
+    }
+    for (uint32_t gs = 0; gs < n_iss; ++gs) {
+      // slab gs landed (later slabs may still be in flight), then the barrier
+      const uint32_t rem = n_iss - 1 - gs;
+      __builtin_amdgcn_sched_barrier(0);
+      if (rem >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * I));
+      else if (rem == 1) __builtin_amdgcn_s_waitcnt(wait_vm(I));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      if (more) {
+        issue((int)((gs + S - 1) % S));
+        ++n_iss;
+      }
+    }
+    return;
+  }
+  // ---- consumers: wave w owns the 64 x 64 quadrant (w / 2, w % 2)
+  constexpr int MI = 2, NJ = 2;
+  const int g = (l >> 5) & 1, li = l & 31;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  const uint32_t ld = (uint32_t)N * ESZ;  // output row pitch in bytes
+  const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * ESZ;
+  MtCursor<TM> cur;
+  uint32_t gs = 0;
+  for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
+    const int e = cur.e;
+    const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
+    const int64_t row0 = (int64_t)off[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+    const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
+    // waves whose rows all lie past the expert's last row skip their MFMAs
+    const bool active = row0 + wm < row_end;
+    for (uint32_t s = 0; s < nk; ++s, ++gs) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      const uint8_t* base = ring + (gs % S) * STAGE;
+      if (active)
+        fp4_slab_mfma_pipe<MI, NJ>(acc, base, base + CODE, base + 2 * CODE, base + 2 * CODE + SCL, wm, wn, g, li);
+    }
+    // epilogue: S_a * S_b, then each value straight from the accumulators;
+    // the descriptor covers the tile's rows up to the expert's last, so
+    // stores of rows past it are dropped
+    const float sab = a_ts[a_ts_per_group ? e : 0] * b_ts[e];
+    const int64_t nrows = row_end - row0 < TM ? row_end - row0 : TM;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<uint8_t*>(c) + row0 * (int64_t)ld, (uint64_t)nrows * ld);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (active) {
+          const uint32_t fo = (uint32_t)(wm + i * 32) * ld + (uint32_t)(n0 + wn + j * 32) * ESZ;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t so = fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld;
+            const float x = acc[i][j][v] * sab;
+            if (OUT_BF16)
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(x), rC, lane_off, so, 2);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rC, lane_off, so, 2);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      }
+  }
+}
 
 template <bool OUT_BF16, int BM, int BN, int MINB>
 static void launch_fwd_t(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
@@ -487,14 +774,27 @@ static void launch_fwd_dma(hipStream_t s, const uint8_t* ac, const uint8_t* as, 
 
 // Configuration choice (MOE4_FWD_TILE overrides, for tuning): 0 = 128x128
 // register-staged (2 blocks/CU), 1 = 256x256, 2 = 128x256, 8 = direct-to-LDS
-// 256x256, 9 = direct-to-LDS 128x128 (2 blocks/CU; the default when
-// K % 256 == 0, else 0).
+// 256x256, 9 = direct-to-LDS 128x128 (2 blocks/CU), 10 = warp-specialised
+// persistent 128x128 (the default when K % 256 == 0 and N % 128 == 0; else 9
+// when K % 256 == 0, else 0).
 static int fwd_tile_choice() {
   static int v = [] {
     const char* e = getenv("MOE4_FWD_TILE");
-    return e ? atoi(e) : 9;
+    return e ? atoi(e) : 10;
   }();
   return v;
+}
+
+static int cu_count_f() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
 }
 
 template <bool OUT_BF16>
@@ -502,7 +802,15 @@ static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, cons
                        const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
                        int64_t N, int64_t K, void* c) {
   int choice = fwd_tile_choice();
-  if ((choice == 8 || choice == 9) && K % fdma::BKE != 0) choice = 0;
+  // the persistent kernel's 32-bit operand offsets and tile indices
+  if (choice == 10 && (N % fws::TN != 0 || M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31)))
+    choice = 9;
+  if ((choice == 8 || choice == 9 || choice == 10) && K % fdma::BKE != 0) choice = 0;
+  if (choice == 10) {
+    hipLaunchKernelGGL(k_gemm_fwd_ws<OUT_BF16>, dim3((unsigned)cu_count_f()), dim3(fws::NT), 0, s, ac, as, ats, apg,
+                       bc, bs, bts, off, E, M, N, K, c);
+    return;
+  }
   if (choice == 8) {
     launch_fwd_dma<OUT_BF16, 256, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
     return;
