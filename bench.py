@@ -88,13 +88,13 @@ KERNEL_OF = {
     "F1 W_up quant (+ requant)": "k_encode_requant_T",
     "F1 W_down quant (+ requant)": "k_encode_requant_T",
     "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
-    "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_dma_bf16_128",
-    "F8 down GEMM (NVFP4)": "k_gemm_fwd_dma_f32_128",
+    "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_ws (bf16)",
+    "F8 down GEMM (NVFP4)": "k_gemm_fwd_ws (f32)",
     "F7 SiLU + H quant (NVFP4 4/6)": "nvfp4 quant 4/6 silu", "F9 combine": "k_combine",
     "B1 dY quant row-wise (MXFP8)": "k_mx_rows", "B1 dY quant transposed (MXFP8)": "k_mx_T",
     "B2 W_down requant SR-T": "k_requant_T", "B7 W_up requant SR-T": "k_requant_T",
     "B4 H requant SR-T": "k_requant_T (H)", "B9 X requant SR-T": "k_requant_T (X)",
-    "B3 down dgrad (MXFP8)": "k_dgrad_dma_256", "B8 up dgrad (MXFP8)": "k_dgrad_dma_256",
+    "B3 down dgrad (MXFP8)": "k_dgrad_ws", "B8 up dgrad (MXFP8)": "k_dgrad_ws",
     "B5 down wgrad (MXFP8)": "k_wgrad_ws", "B10 up wgrad (MXFP8)": "k_wgrad_ws",
     "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
     "B11 un-permute sum": "k_combine (unpermute)", "B12 gate gradient": "k_dgates",

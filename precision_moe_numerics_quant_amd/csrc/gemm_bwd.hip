@@ -952,15 +952,23 @@ __global__ void __launch_bounds__(wsg::NT, 1)
 // m-tile-major tiles in contiguous per-XCD runs) with 128 x 128 tiles, so a
 // small expert wastes at most 127 padded rows, and the MXFP8 slab of the
 // kernel above: 128 code bytes and 4 scale bytes per row and slab, scales
-// row-major.
+// row-major.  TN = 128 (four stages) or 256 (three stages: consumers of
+// 64 x 128, half the operand bytes per MFMA).
 namespace dws {
-constexpr int TM = 128, TN = 128, S = 4, NCW = 4, NT = 64 * (NCW + 4);
-constexpr int CODE = TM * dmag::BK, SCL = TM * 4;  // per operand and stage
-constexpr int STAGE = 2 * CODE + 2 * SCL;
-constexpr int I = 9;  // loads per producer wave and slab: 4 + 4 code row groups, 1 scale group
+constexpr int TM = 128, NCW = 4, NT = 64 * (NCW + 4);
+template <int TN>
+struct Cfg {
+  static constexpr int CODE_A = TM * dmag::BK, CODE_B = TN * dmag::BK;  // per stage
+  static constexpr int SCL_A = TM * 4, SCL_B = TN * 4;
+  static constexpr int STAGE = CODE_A + CODE_B + SCL_A + SCL_B;
+  static constexpr int S = TN == 128 ? 4 : 3;
+  static constexpr int QB = TN / 32;              // B code row groups per producer wave
+  static constexpr int NS = TN == 128 ? 1 : 2;    // scale groups per producer wave
+  static constexpr int I = 4 + QB + NS;           // loads per producer wave and slab
+};
 }  // namespace dws
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int TN>
 __global__ void __launch_bounds__(dws::NT, 1)
     k_dgrad_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
                const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
@@ -971,10 +979,10 @@ __global__ void __launch_bounds__(dws::NT, 1)
   using dmag::swz;
   using wsg::wait_vm;
   using wsg::WAIT_LGKM0;
-  constexpr int BK = dmag::BK;
+  using C = Cfg<TN>;
+  constexpr int BK = dmag::BK, S = C::S, STAGE = C::STAGE, I = C::I;
   __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
   __shared__ uint32_t s_nmt;
-  const __attribute__((address_space(4))) int32_t* coff = (const __attribute__((address_space(4))) int32_t*)off;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // total m-tiles (before any load into LDS is in flight)
@@ -993,14 +1001,28 @@ __global__ void __launch_bounds__(dws::NT, 1)
   const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
 
   if (w >= NCW) {
-    // ---- producer pw: rows 32 pw .. 32 pw + 31 of both operands' codes and
-    // one 64-row group of scales (A rows 0-63, A 64-127, B 0-63, B 64-127)
+    // ---- producer pw: rows 32 pw .. 32 pw + 31 of A's codes, TN / 4 rows of
+    // B's, and 64-row scale groups: TN = 128: A 0-63, A 64-127, B 0-63,
+    // B 64-127; TN = 256: A 0-63 + B 0-63, A 64-127 + B 64-127, B 128-191 +
+    // A 0-63, B 192-255 + A 64-127 (two waves load an A group twice, so that
+    // every producer issues the same number of loads: the waits count them)
     const int pw = w - NCW;
-    const bool sopb = pw >= 2;
     const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * K);
     const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * KS);
     __amdgpu_buffer_rsrc_t rbc = rac, rbs = ras;
-    uint32_t aoff[4], boff[4], soff = 0;
+    // (fixed sizes: the first C::QB and C::NS are used; hipcc's host pass rejects
+    // arrays sized by the template argument inside the lambdas)
+    uint32_t aoff[4], boff[8], soff[2];
+    // scale group k of this wave: operand B?, first row
+    auto sgrp = [&](int k, bool& opb, int& r0) {
+      if (TN == 128) {
+        opb = pw >= 2;
+        r0 = 64 * (pw & 1);
+      } else {  // waves 0, 1: A then B; waves 2, 3: B then A
+        opb = pw < 2 ? k == 1 : k == 0;
+        r0 = opb ? 64 * pw : 64 * (pw & 1);
+      }
+    };
     MtCursor<TM> cur;
     uint32_t pt = t0, ps = 0;
     bool more = false;
@@ -1009,7 +1031,7 @@ __global__ void __launch_bounds__(dws::NT, 1)
       if (!more) return;
       const int e = cur.e;
       const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
-      const int64_t row0 = (int64_t)coff[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+      const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
       rbc = make_rsrc(b_codes + (int64_t)e * N * K, (uint64_t)N * K);
       rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
       // rows past the operands are clamped to the last row: valid memory whose
@@ -1018,13 +1040,23 @@ __global__ void __launch_bounds__(dws::NT, 1)
       for (int q = 0; q < 4; ++q) {
         const int r = 32 * pw + 8 * q + (l >> 3);
         const int64_t ra = row0 + r < M_total ? row0 + r : M_total - 1;
-        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
         aoff[q] = (uint32_t)ra * (uint32_t)K + 16u * (uint32_t)swz(r, l & 7);
+      }
+#pragma unroll
+      for (int q = 0; q < C::QB; ++q) {
+        const int r = (TN / 4) * pw + 8 * q + (l >> 3);
+        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
         boff[q] = (uint32_t)rb * (uint32_t)K + 16u * (uint32_t)swz(r, l & 7);
       }
-      const int sr = 64 * (pw & 1) + l;
-      const int64_t srow = sopb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
-      soff = (uint32_t)srow * KS;
+#pragma unroll
+      for (int k = 0; k < C::NS; ++k) {
+        bool opb;
+        int r0;
+        sgrp(k, opb, r0);
+        const int sr = r0 + l;
+        const int64_t srow = opb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
+        soff[k] = (uint32_t)srow * KS;
+      }
       ps = 0;
     };
     seek();
@@ -1035,12 +1067,18 @@ __global__ void __launch_bounds__(dws::NT, 1)
       for (int q = 0; q < 4; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(base + (4 * pw + q) * 1024), 16, aoff[q] + kb, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + CODE + (4 * pw + q) * 1024), 16, boff[q] + kb, 0,
-                                                 0, 0);
-      uint8_t* sb = base + 2 * CODE + (sopb ? SCL : 0) + (pw & 1) * 256;
-      if (sopb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 4, soff + ksb, 0, 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 4, soff + ksb, 0, 0, 0);
+      for (int q = 0; q < C::QB; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + C::CODE_A + (C::QB * pw + q) * 1024), 16,
+                                                 boff[q] + kb, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < C::NS; ++k) {
+        bool opb;
+        int r0;
+        sgrp(k, opb, r0);
+        uint8_t* sb = base + C::CODE_A + C::CODE_B + (opb ? C::SCL_A : 0) + r0 * 4;
+        if (opb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 4, soff[k] + ksb, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 4, soff[k] + ksb, 0, 0, 0);
+      }
       if (++ps == nk) {
         pt += stride;
         seek();
@@ -1068,10 +1106,10 @@ __global__ void __launch_bounds__(dws::NT, 1)
     }
     return;
   }
-  // ---- consumers: wave w owns the 64 x 64 quadrant (w / 2, w % 2)
-  constexpr int MI = 2, NJ = 2;
+  // ---- consumers: wave w owns the 64 x (TN / 2) block (w / 2, w % 2)
+  constexpr int MI = 2, NJ = TN / 64;
   const int g = (l >> 5) & 1, li = l & 31;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * (TN / 2);
   f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1081,9 +1119,9 @@ __global__ void __launch_bounds__(dws::NT, 1)
   // 4 ks + g and 4 ks + 2 + g and the scale of block 2 ks + g
   auto compute = [&](const uint8_t* base) {
     const uint8_t* la = base;
-    const uint8_t* lb = base + CODE;
-    const uint8_t* sa = base + 2 * CODE;
-    const uint8_t* sb = base + 2 * CODE + SCL;
+    const uint8_t* lb = base + C::CODE_A;
+    const uint8_t* sa = base + C::CODE_A + C::CODE_B;
+    const uint8_t* sb = base + C::CODE_A + C::CODE_B + C::SCL_A;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       i32x8 fa[MI], fb[NJ];
@@ -1121,8 +1159,8 @@ __global__ void __launch_bounds__(dws::NT, 1)
   for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
     const int e = cur.e;
     const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
-    const int64_t row0 = (int64_t)coff[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
-    const int64_t row_end = (int64_t)coff[e + 1] < M_total ? (int64_t)coff[e + 1] : M_total;
+    const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+    const int64_t row_end = (int64_t)ld_const(off, e + 1) < M_total ? (int64_t)ld_const(off, e + 1) : M_total;
     // waves whose rows all lie past the expert's last row skip their MFMAs
     const bool active = row0 + wm < row_end;
     for (uint32_t s = 0; s < nk; ++s, ++gs) {
@@ -1175,7 +1213,7 @@ static int cu_count() {
 static int mx_tile_choice(int mode) {
   static int v[2] = {[] {
                        const char* e = getenv("MOE4_MX_TILE");
-                       return e ? atoi(e) : 11;
+                       return e ? atoi(e) : 12;
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
@@ -1212,19 +1250,26 @@ static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 // double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves;
 // dgrad only: 8 = direct-to-LDS loads, 256x256 (the default when
 // K % 128 == 0 and N % 128 != 0, else 6), 9 = as 8 with 128x128 tiles at 2
-// blocks/CU, 11 = the warp-specialized persistent kernel (the default when
-// K % 128 == 0 and N % 128 == 0); wgrad
+// blocks/CU, 11 = the warp-specialized persistent kernel with 128x128 tiles
+// (the default when K % 128 == 0 and N % 128 == 0 but N % 256 != 0), 12 = the
+// same with 128x256 tiles (the default when K % 128 == 0 and N % 256 == 0);
+// wgrad
 // only: 10 = the warp-specialized persistent kernel (the default; needs
 // E <= 2048 and 32-bit tile and output indices, else configuration 1, the
 // persistent register-staged kernel).
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   int choice = mx_tile_choice(0);
-  if (choice == 11 && N % dws::TN != 0) choice = 8;
-  if ((choice == 8 || choice == 9 || choice == 11) && K % dmag::BK != 0) choice = 6;
-  if (choice == 11) {
-    hipLaunchKernelGGL(k_dgrad_ws<false>, dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off, E, M, N,
-                       K, static_cast<void*>(c));
+  if (choice == 12 && N % 256 != 0) choice = 11;
+  if (choice == 11 && N % 128 != 0) choice = 8;
+  if ((choice == 8 || choice == 9 || choice == 11 || choice == 12) && K % dmag::BK != 0) choice = 6;
+  if (choice == 11 || choice == 12) {
+    if (choice == 12)
+      hipLaunchKernelGGL((k_dgrad_ws<false, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
+                         E, M, N, K, static_cast<void*>(c));
+    else
+      hipLaunchKernelGGL((k_dgrad_ws<false, 128>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
+                         E, M, N, K, static_cast<void*>(c));
     return;
   }
   if (choice == 8 || choice == 9) {
@@ -1303,9 +1348,14 @@ extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, 
   MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_mx: A and each expert's B must stay below 2 GiB");
   if (M_total == 0) return MOE4_OK;
-  if (N % dws::TN == 0 && mx_tile_choice(0) == 11) {
-    hipLaunchKernelGGL(k_dgrad_ws<true>, dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream), a_codes, a_sf,
-                       b_codes, b_sf, expert_off, E, M_total, N, K, c);
+  const int ch = mx_tile_choice(0);
+  if ((ch == 11 || ch == 12) && N % 128 == 0) {
+    if (ch == 12 && N % 256 == 0)
+      hipLaunchKernelGGL((k_dgrad_ws<true, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream),
+                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c);
+    else
+      hipLaunchKernelGGL((k_dgrad_ws<true, 128>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream),
+                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c);
     return check_launch("moe_grouped_gemm_mx");
   }
   const int64_t n_nt = (N + 255) / 256;

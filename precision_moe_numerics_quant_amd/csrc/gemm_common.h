@@ -67,6 +67,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes
                                            __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 
+// Element i of a launch-constant int32 array, through the constant address
+// space: a uniform index then always gives a scalar load (a vector load would
+// make the wave wait for all its outstanding loads and stores).
+__device__ inline int32_t ld_const(const int32_t* p, int i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p))[i];
+}
+
 // Cursor over the m-tiles of the experts in order: (expert, its first m-tile).
 template <int TM>
 struct MtCursor {
@@ -75,12 +83,9 @@ struct MtCursor {
   // advance to the expert holding flat m-tile mi; false past the last one.
   // The offsets come through scalar loads: a vector load here would make the
   // wave wait for all its outstanding loads (or stores) first.
-  __device__ bool seek(const int32_t* __restrict__ off_g, int E, uint32_t mi) {
-    // (read through the constant address space: the offsets do not change
-    // during the launch, and uniform loads from it always use the scalar unit)
-    const __attribute__((address_space(4))) int32_t* off = (const __attribute__((address_space(4))) int32_t*)off_g;
+  __device__ bool seek(const int32_t* __restrict__ off, int E, uint32_t mi) {
     while (e < E) {
-      const int32_t o0 = off[e], o1 = off[e + 1];
+      const int32_t o0 = ld_const(off, e), o1 = ld_const(off, e + 1);
       const uint32_t n = (uint32_t)((o1 - o0 + TM - 1) / TM);
       if (mi < first + n) return true;
       first += n;
