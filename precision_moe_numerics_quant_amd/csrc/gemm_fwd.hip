@@ -574,17 +574,28 @@ MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2, false)
 // stride through it, so concurrent tiles share A rows and the expert's B in
 // that XCD's L2.
 namespace fws {
-constexpr int TM = 128, TN = 128, S = 4, NCW = 4, NT = 64 * (NCW + 4);
-constexpr int CODE = TM * fdma::RB, SCL = TM * 16;  // per operand and stage
-constexpr int STAGE = 2 * CODE + 2 * SCL;
-constexpr int I = 9;  // loads per producer wave and slab: 4 + 4 code row groups, 1 scale group
-constexpr uint32_t OOB = 0x80000000u;
+constexpr int TM = 128;
+// TN = 128: four stages, four consumer waves; TN = 256: two 54 KB stages (all
+// the LDS allows) and eight consumer waves, so that two of a SIMD's three
+// waves compute and one's conversions overlap the other's MFMAs.  Consumers
+// own 64 x 64 blocks either way.
+template <int TN>
+struct Cfg {
+  static constexpr int NCW = TN / 32, NT = 64 * (NCW + 4);
+  static constexpr int CODE_A = TM * fdma::RB, CODE_B = TN * fdma::RB;  // per stage
+  static constexpr int SCL_A = TM * 16, SCL_B = TN * 16;
+  static constexpr int STAGE = CODE_A + CODE_B + SCL_A + SCL_B;
+  static constexpr int S = TN == 128 ? 4 : 2;
+  static constexpr int QB = TN / 32;            // B code row groups per producer wave
+  static constexpr int NS = TN == 128 ? 1 : 2;  // scale groups per producer wave
+  static constexpr int I = 4 + QB + NS;         // loads per producer wave and slab
+};
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
 }  // namespace fws
 
-template <bool OUT_BF16>
-__global__ void __launch_bounds__(fws::NT, 1)
+template <bool OUT_BF16, int TN>
+__global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
                   int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                   const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,
@@ -592,6 +603,8 @@ __global__ void __launch_bounds__(fws::NT, 1)
   using namespace fws;
   using fdma::lds_ptr;
   using fdma::swz;
+  using C = Cfg<TN>;
+  constexpr int S = C::S, STAGE = C::STAGE, I = C::I, NCW = C::NCW;
   __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
   __shared__ uint32_t s_nmt;
   const int tid = threadIdx.x, l = tid & 63;
@@ -605,7 +618,7 @@ __global__ void __launch_bounds__(fws::NT, 1)
     if (l == 0) s_nmt = n;
   }
   __syncthreads();
-  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;  // N % 128 == 0 (checked at launch)
+  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;  // N % TN == 0 (checked at launch)
   const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16), nk = (uint32_t)(K / fdma::BKE);
   // this workgroup's tiles: t0, t0 + stride, ... < t_end
   const uint32_t xcd = blockIdx.x % 8, per = (n_all + 7) / 8;
@@ -613,14 +626,27 @@ __global__ void __launch_bounds__(fws::NT, 1)
   const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
 
   if (w >= NCW) {
-    // ---- producer pw: rows 32 pw .. 32 pw + 31 of both operands' codes and
-    // one 64-row group of scales (A rows 0-63, A 64-127, B 0-63, B 64-127)
+    // ---- producer pw: rows 32 pw .. 32 pw + 31 of A's codes, TN / 4 rows of
+    // B's, and 64-row scale groups: TN = 128: A 0-63, A 64-127, B 0-63,
+    // B 64-127; TN = 256: A 0-63 + B 0-63, A 64-127 + B 64-127, B 128-191 +
+    // A 0-63, B 192-255 + A 64-127 (two waves load an A group twice, so that
+    // every producer issues the same number of loads: the waits count them)
     const int pw = w - NCW;
-    const bool sopb = pw >= 2;
     const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint64_t)M_total * KB);
     const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_sf, (uint64_t)M_total * KS);
     __amdgpu_buffer_rsrc_t rbc = rac, rbs = ras;
-    uint32_t aoff[4], boff[4], soff = 0;
+    // (fixed sizes: the first C::QB and C::NS are used; hipcc's host pass rejects
+    // arrays sized by the template argument inside the lambdas)
+    uint32_t aoff[4], boff[8], soff[2];
+    auto sgrp = [&](int k, bool& opb, int& r0) {  // scale group k: operand B?, first row
+      if (TN == 128) {
+        opb = pw >= 2;
+        r0 = 64 * (pw & 1);
+      } else {  // waves 0, 1: A then B; waves 2, 3: B then A
+        opb = pw < 2 ? k == 1 : k == 0;
+        r0 = opb ? 64 * pw : 64 * (pw & 1);
+      }
+    };
     MtCursor<TM> cur;
     uint32_t pt = t0, ps = 0;
     bool more = false;
@@ -629,7 +655,7 @@ __global__ void __launch_bounds__(fws::NT, 1)
       if (!more) return;
       const int e = cur.e;
       const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
-      const int64_t row0 = (int64_t)off[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+      const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
       rbc = make_rsrc(b_codes + (int64_t)e * N * KB, (uint64_t)N * KB);
       rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
       // rows past the operands are clamped to the last row: valid memory whose
@@ -638,13 +664,23 @@ __global__ void __launch_bounds__(fws::NT, 1)
       for (int q = 0; q < 4; ++q) {
         const int r = 32 * pw + 8 * q + (l >> 3);
         const int64_t ra = row0 + r < M_total ? row0 + r : M_total - 1;
-        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
         aoff[q] = (uint32_t)ra * KB + 16u * (uint32_t)swz(r, l & 7);
+      }
+#pragma unroll
+      for (int q = 0; q < C::QB; ++q) {
+        const int r = (TN / 4) * pw + 8 * q + (l >> 3);
+        const int64_t rb = n0 + r < N ? n0 + r : N - 1;
         boff[q] = (uint32_t)rb * KB + 16u * (uint32_t)swz(r, l & 7);
       }
-      const int sr = 64 * (pw & 1) + l;
-      const int64_t srow = sopb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
-      soff = (uint32_t)srow * KS;
+#pragma unroll
+      for (int k = 0; k < C::NS; ++k) {
+        bool opb;
+        int r0;
+        sgrp(k, opb, r0);
+        const int sr = r0 + l;
+        const int64_t srow = opb ? (n0 + sr < N ? n0 + sr : N - 1) : (row0 + sr < M_total ? row0 + sr : M_total - 1);
+        soff[k] = (uint32_t)srow * KS;
+      }
       ps = 0;
     };
     seek();
@@ -655,12 +691,18 @@ __global__ void __launch_bounds__(fws::NT, 1)
       for (int q = 0; q < 4; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rac, (lds_ptr)(base + (4 * pw + q) * 1024), 16, aoff[q] + kb, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + CODE + (4 * pw + q) * 1024), 16, boff[q] + kb, 0,
-                                                 0, 0);
-      uint8_t* sb = base + 2 * CODE + (sopb ? SCL : 0) + (pw & 1) * 1024;
-      if (sopb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 16, soff + ksb, 0, 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 16, soff + ksb, 0, 0, 0);
+      for (int q = 0; q < C::QB; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbc, (lds_ptr)(base + C::CODE_A + (C::QB * pw + q) * 1024), 16,
+                                                 boff[q] + kb, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < C::NS; ++k) {
+        bool opb;
+        int r0;
+        sgrp(k, opb, r0);
+        uint8_t* sb = base + C::CODE_A + C::CODE_B + (opb ? C::SCL_A : 0) + r0 * 16;
+        if (opb) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr)sb, 16, soff[k] + ksb, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr)sb, 16, soff[k] + ksb, 0, 0, 0);
+      }
       if (++ps == nk) {
         pt += stride;
         seek();
@@ -688,10 +730,10 @@ __global__ void __launch_bounds__(fws::NT, 1)
     }
     return;
   }
-  // ---- consumers: wave w owns the 64 x 64 quadrant (w / 2, w % 2)
+  // ---- consumers: wave w owns the 64 x 64 block (w / (TN / 64), w % (TN / 64))
   constexpr int MI = 2, NJ = 2;
   const int g = (l >> 5) & 1, li = l & 31;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w / (TN / 64)) * 64, wn = (w % (TN / 64)) * 64;
   f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -705,8 +747,8 @@ __global__ void __launch_bounds__(fws::NT, 1)
   for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
     const int e = cur.e;
     const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
-    const int64_t row0 = (int64_t)off[e] + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
-    const int64_t row_end = (int64_t)off[e + 1] < M_total ? (int64_t)off[e + 1] : M_total;
+    const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
+    const int64_t row_end = (int64_t)ld_const(off, e + 1) < M_total ? (int64_t)ld_const(off, e + 1) : M_total;
     // waves whose rows all lie past the expert's last row skip their MFMAs
     const bool active = row0 + wm < row_end;
     for (uint32_t s = 0; s < nk; ++s, ++gs) {
@@ -716,13 +758,14 @@ __global__ void __launch_bounds__(fws::NT, 1)
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       const uint8_t* base = ring + (gs % S) * STAGE;
-      if (active)
-        fp4_slab_mfma_pipe<MI, NJ>(acc, base, base + CODE, base + 2 * CODE, base + 2 * CODE + SCL, wm, wn, g, li);
+      const uint8_t* sa = base + C::CODE_A + C::CODE_B;
+      if (active) fp4_slab_mfma_pipe<MI, NJ>(acc, base, base + C::CODE_A, sa, sa + C::SCL_A, wm, wn, g, li);
     }
     // epilogue: S_a * S_b, then each value straight from the accumulators;
     // the descriptor covers the tile's rows up to the expert's last, so
     // stores of rows past it are dropped
-    const float sab = a_ts[a_ts_per_group ? e : 0] * b_ts[e];
+    const float sab = __int_as_float(ld_const(reinterpret_cast<const int32_t*>(a_ts), a_ts_per_group ? e : 0)) *
+                      __int_as_float(ld_const(reinterpret_cast<const int32_t*>(b_ts), e));
     const int64_t nrows = row_end - row0 < TM ? row_end - row0 : TM;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<uint8_t*>(c) + row0 * (int64_t)ld, (uint64_t)nrows * ld);
 #pragma unroll
@@ -775,12 +818,13 @@ static void launch_fwd_dma(hipStream_t s, const uint8_t* ac, const uint8_t* as, 
 // Configuration choice (MOE4_FWD_TILE overrides, for tuning): 0 = 128x128
 // register-staged (2 blocks/CU), 1 = 256x256, 2 = 128x256, 8 = direct-to-LDS
 // 256x256, 9 = direct-to-LDS 128x128 (2 blocks/CU), 10 = warp-specialised
-// persistent 128x128 (the default when K % 256 == 0 and N % 128 == 0; else 9
-// when K % 256 == 0, else 0).
+// persistent 128x128, 11 = warp-specialised persistent 128x256 (the default
+// when K % 256 == 0 and N % 256 == 0; 10 when K % 256 == 0 and N % 128 == 0;
+// else 9 when K % 256 == 0, else 0).
 static int fwd_tile_choice() {
   static int v = [] {
     const char* e = getenv("MOE4_FWD_TILE");
-    return e ? atoi(e) : 10;
+    return e ? atoi(e) : 11;
   }();
   return v;
 }
@@ -802,13 +846,20 @@ static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, cons
                        const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
                        int64_t N, int64_t K, void* c) {
   int choice = fwd_tile_choice();
-  // the persistent kernel's 32-bit operand offsets and tile indices
-  if (choice == 10 && (N % fws::TN != 0 || M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31)))
+  if (choice == 11 && N % 256 != 0) choice = 10;
+  // the persistent kernels' 32-bit operand offsets and tile indices
+  if ((choice == 10 || choice == 11) &&
+      (N % 128 != 0 || M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31)))
     choice = 9;
-  if ((choice == 8 || choice == 9 || choice == 10) && K % fdma::BKE != 0) choice = 0;
+  if ((choice == 8 || choice == 9 || choice == 10 || choice == 11) && K % fdma::BKE != 0) choice = 0;
   if (choice == 10) {
-    hipLaunchKernelGGL(k_gemm_fwd_ws<OUT_BF16>, dim3((unsigned)cu_count_f()), dim3(fws::NT), 0, s, ac, as, ats, apg,
-                       bc, bs, bts, off, E, M, N, K, c);
+    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 128>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s, ac,
+                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
+    return;
+  }
+  if (choice == 11) {
+    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 256>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<256>::NT), 0, s, ac,
+                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
     return;
   }
   if (choice == 8) {
