@@ -95,7 +95,7 @@ KERNEL_OF = {
     "B2 W_down requant SR-T": "k_requant_T", "B7 W_up requant SR-T": "k_requant_T",
     "B4 H requant SR-T": "k_requant_T (H)", "B9 X requant SR-T": "k_requant_T (X)",
     "B3 down dgrad (MXFP8)": "k_dgrad_ws", "B8 up dgrad (MXFP8)": "k_dgrad_ws",
-    "B5 down wgrad (MXFP8)": "k_wgrad_ws", "B10 up wgrad (MXFP8)": "k_wgrad_ws",
+    "B5 down wgrad (MXFP8)": "k_wgrad_ws256", "B10 up wgrad (MXFP8)": "k_wgrad_ws256",
     "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
     "B11 un-permute sum": "k_combine (unpermute)", "B12 gate gradient": "k_dgates",
     "B13 router backward": "k_route_backward",
@@ -109,7 +109,7 @@ MULTI_KERNEL_CALLS = {"F1 W_up quant (+ requant)", "F1 W_down quant (+ requant)"
 # rocprofv3 --pmc summaries (FETCH_SIZE and WRITE_SIZE passes, scaled by a
 # plain copy of known size) of a kernel, with the hash of its source file:
 # the HBM bytes per launch are reported only while that source is unchanged.
-PMC_PROFILE = {"k_wgrad_ws": ("profiles/k_wgrad_ws_T16384_E384_pmc.md",
+PMC_PROFILE = {"k_wgrad_ws256": ("profiles/k_wgrad_ws256_T16384_E384_pmc.md",
                               "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip")}
 
 

@@ -1198,6 +1198,244 @@ __global__ void __launch_bounds__(dws::NT, 1)
   }
 }
 
+// wgrad with 256 x 128 tiles: k_wgrad_ws's structure, three stages of
+// 49.5 KB (A codes 32 KB, B codes 16 KB, scales 1.5 KB: with the offset table,
+// all the LDS there is), consumers of 128 x 64.  Each 128-row operand block
+// of the 128 x 128 kernel is reloaded for every tile it meets, from L2; the
+// wider tile moves three quarters of those bytes per output.  Producer pw
+// loads A rows 64 pw .. 64 pw + 63 (8 code row groups + their scales), B rows
+// 32 pw .. 32 pw + 31 (4 code row groups) and the scales of B's 64-row half
+// pw / 2 (loaded by two waves: every producer issues 14 loads per slab,
+// which its waits count).
+namespace wsg2 {
+constexpr int TM = 256, TN = 128, BK = 128, S = 3;
+constexpr int CODE_A = TM * BK, CODE_B = TN * BK, SCL_A = 4 * TM, SCL_B = 4 * TN;
+constexpr int STAGE = CODE_A + CODE_B + SCL_A + SCL_B;
+constexpr int I = 14;
+}  // namespace wsg2
+
+__global__ void __launch_bounds__(wsg::NT, 1)
+    k_wgrad_ws256(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
+                  const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
+                  const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, int64_t n_ntiles_, int64_t n_all_,
+                  float* __restrict__ dw, float beta) {
+  using namespace wsg2;
+  using wsg::NCW;
+  using wsg::NT;
+  using wsg::wait_vm;
+  using wsg::WAIT_LGKM0;
+  using wsg::MAX_E;
+  using wsg::NT_STORE;
+  using dmag::lds_ptr;
+  using dmag::swz;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
+  __shared__ int32_t s_off[MAX_E + 1];
+  const uint32_t n_all = (uint32_t)n_all_, n_ntiles = (uint32_t)n_ntiles_, per_e = n_all / (uint32_t)E;
+  auto tile_mn = [&](uint32_t rest, uint32_t& mt, uint32_t& nt) {
+    mt = rest / n_ntiles;
+    nt = rest - mt * n_ntiles;
+  };
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i <= E; i += NT) s_off[i] = off[i];
+  __syncthreads();
+  if (w >= NCW) {
+    const int pw = w - NCW, hb = pw >> 1;
+    uint32_t pt = blockIdx.x;
+    uint32_t ps = 0, pnk = 0, klen = 0, srow_a = 0, srow_b = 0;
+    uint32_t crow_a[8], crow_b[4];
+    __amdgpu_buffer_rsrc_t rca = make_rsrc(a_codes, 0), rsa = make_rsrc(a_sf, 0);
+    __amdgpu_buffer_rsrc_t rcb = rca, rsb = rsa;
+    // move to the first tile at or after pt whose expert has tokens
+    auto seek = [&]() -> bool {
+      for (; pt < n_all; pt += gridDim.x) {
+        // (offsets through the scalar unit: an LDS read here would make the
+        // compiler wait for this wave's direct-to-LDS loads)
+        const uint32_t e = pt / per_e, rest = pt - e * per_e;
+        const int64_t p0 = ld_const(off, (int)e), kl = (int64_t)ld_const(off, (int)e + 1) - p0;
+        if (kl == 0) continue;
+        uint32_t mt, nt;
+        tile_mn(rest, mt, nt);
+        const int64_t ra0 = (int64_t)mt * TM, rb0 = (int64_t)nt * TN;
+        rca = make_rsrc(a_codes + N1 * p0, (uint64_t)N1 * kl);
+        rsa = make_rsrc(a_sf + N1 * p0 / 32, (uint64_t)N1 * (kl / 32));
+        rcb = make_rsrc(b_codes + N2 * p0, (uint64_t)N2 * kl);
+        rsb = make_rsrc(b_sf + N2 * p0 / 32, (uint64_t)N2 * (kl / 32));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 64 * pw + 8 * j + (l >> 3);
+          const uint32_t r = (uint32_t)(ra0 + row < N1 ? ra0 + row : N1 - 1);
+          crow_a[j] = r * (uint32_t)kl + 16u * (uint32_t)swz(row, l & 7);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 32 * pw + 8 * j + (l >> 3);
+          const uint32_t r = (uint32_t)(rb0 + row < N2 ? rb0 + row : N2 - 1);
+          crow_b[j] = r * (uint32_t)kl + 16u * (uint32_t)swz(row, l & 7);
+        }
+        // lane l: rows .. + 4 (l % 16) .. + 3 of K block l / 16 of the slab
+        // (block-major scales; N1, N2 % 32 == 0 keep the 4 rows together)
+        const int64_t rra = ra0 + 64 * pw + (l & 15) * 4, rrb = rb0 + 64 * hb + (l & 15) * 4;
+        srow_a = rra < N1 ? (uint32_t)((l >> 4) * N1 + rra) : bwd::OOB;
+        srow_b = rrb < N2 ? (uint32_t)((l >> 4) * N2 + rrb) : bwd::OOB;
+        klen = (uint32_t)kl;
+        pnk = (uint32_t)((kl + BK - 1) / BK);
+        ps = 0;
+        return true;
+      }
+      return false;
+    };
+    bool more = seek();
+    auto issue = [&](int st) {
+      uint8_t* base = ring + st * STAGE;
+      const uint32_t k0 = ps * BK;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = k0 + 16 * (uint32_t)swz(64 * pw + 8 * j + (l >> 3), l & 7) < klen;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rca, (lds_ptr)(base + (8 * pw + j) * 1024), 16,
+                                                 ok ? crow_a[j] + k0 : bwd::OOB, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = k0 + 16 * (uint32_t)swz(32 * pw + 8 * j + (l >> 3), l & 7) < klen;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (lds_ptr)(base + CODE_A + (4 * pw + j) * 1024), 16,
+                                                 ok ? crow_b[j] + k0 : bwd::OOB, 0, 0, 0);
+      }
+      const bool kok = k0 + 32 * (uint32_t)(l >> 4) < klen;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(base + CODE_A + CODE_B + pw * 256), 4,
+                                               kok && srow_a != bwd::OOB ? srow_a + (k0 / 32) * (uint32_t)N1 : bwd::OOB,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr)(base + CODE_A + CODE_B + SCL_A + hb * 256), 4,
+                                               kok && srow_b != bwd::OOB ? srow_b + (k0 / 32) * (uint32_t)N2 : bwd::OOB,
+                                               0, 0, 0);
+      if (++ps == pnk) {
+        pt += gridDim.x;
+        more = seek();
+      }
+    };
+    uint32_t n_iss = 0;
+    for (int st = 0; st < S - 1 && more; ++st) {
+      issue(st);
+      ++n_iss;
+    }
+    for (uint32_t gs = 0; gs < n_iss; ++gs) {
+      // slab gs landed (later slabs may still be in flight), then the barrier
+      const uint32_t rem = n_iss - 1 - gs;
+      __builtin_amdgcn_sched_barrier(0);
+      if (rem >= 1) __builtin_amdgcn_s_waitcnt(wait_vm(I));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      if (more) {
+        issue((int)((gs + S - 1) % S));
+        ++n_iss;
+      }
+    }
+    return;
+  }
+  // ---- consumers: wave w owns the 128 x 64 block (w / 2, w % 2)
+  constexpr int MI = 4, NJ = 2;
+  const int g = (l >> 5) & 1, li = l & 31;
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 64;
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t* base) {
+    const uint8_t* la = base;
+    const uint8_t* lb = base + CODE_A;
+    const uint8_t* sa = base + CODE_A + CODE_B;
+    const uint8_t* sb = base + CODE_A + CODE_B + SCL_A;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fa[MI], fb[NJ];
+      int ya[MI], yb[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm + i * 32 + li;
+        const uint8_t* p = la + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fa[i] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        ya[i] = sa[(r >> 6) * 256 + (ks * 2 + g) * 64 + (r & 63)];
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = wn + j * 32 + li;
+        const uint8_t* p = lb + r * BK;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + g));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(p + 16 * swz(r, ks * 4 + 2 + g));
+        fb[j] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        yb[j] = sb[(r >> 6) * 256 + (ks * 2 + g) * 64 + (r & 63)];
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ya[i], 0, yb[j]);
+    }
+  };
+  uint32_t gs = 0;
+  const uint32_t ld = (uint32_t)N2 * 4;
+  const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * 4;
+  for (uint32_t t = blockIdx.x; t < n_all; t += gridDim.x) {
+    const uint32_t e = t / per_e, rest = t - e * per_e;
+    uint32_t mt, nt;
+    tile_mn(rest, mt, nt);
+    const int64_t m0 = (int64_t)mt * TM, c0 = (int64_t)nt * TN;
+    const int kl = s_off[e + 1] - s_off[e];
+    float* C = dw + (int64_t)e * N1 * N2;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (uint64_t)N1 * N2 * 4);
+    if (kl == 0) {  // no tokens: zeros for beta = 0; 4 rows x 64 columns per store
+      if (beta != 0.0f) continue;
+      const bool cok = c0 + wn + (l & 15) * 4 < N2;
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k) {
+        const int64_t row = m0 + wm + k * 4 + (l >> 4);
+        const uint32_t o = (uint32_t)(row * N2 + c0 + wn + (l & 15) * 4) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128((__attribute__((ext_vector_type(4))) unsigned){0u, 0u, 0u, 0u}, rC,
+                                               row < N1 && cok ? o : bwd::OOB, 0, NT_STORE);
+      }
+      continue;
+    }
+    const uint32_t nk = (uint32_t)((kl + BK - 1) / BK);
+    for (uint32_t s = 0; s < nk; ++s, ++gs) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      compute(ring + (gs % S) * STAGE);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t r = m0 + wm + i * 32, c = c0 + wn + j * 32;
+        if (r < N1 && c < N2) {
+          const uint32_t fo = (uint32_t)(r * N2 + c) * 4;
+          if (beta == 0.0f) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rC, lane_off,
+                                                    fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld, NT_STORE);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const uint32_t so = fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld;
+              const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC, lane_off, so, 0));
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old + acc[i][j][v]), rC, lane_off, so, NT_STORE);
+            }
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      }
+  }
+}
+
 static int cu_count() {
   static int n[64] = {0};
   int dev = 0;
@@ -1217,7 +1455,7 @@ static int mx_tile_choice(int mode) {
                      }(),
                      [] {
                        const char* e = getenv("MOE4_MX_TILE_W");
-                       return e ? atoi(e) : 10;
+                       return e ? atoi(e) : 13;
                      }()};
   return v[mode];
 }
@@ -1254,8 +1492,9 @@ static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 // (the default when K % 128 == 0 and N % 128 == 0 but N % 256 != 0), 12 = the
 // same with 128x256 tiles (the default when K % 128 == 0 and N % 256 == 0);
 // wgrad
-// only: 10 = the warp-specialized persistent kernel (the default; needs
-// E <= 2048 and 32-bit tile and output indices, else configuration 1, the
+// only: 10 = the warp-specialized persistent kernel with 128x128 tiles, 13 =
+// the same with 256x128 tiles (the default); both need E <= 2048 and 32-bit
+// tile and output indices (13 falls back to 10, 10 to configuration 1, the
 // persistent register-staged kernel).
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
@@ -1295,8 +1534,16 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
   const int wc = mx_tile_choice(1);
+  const int64_t ws2_all = (N2 + wsg2::TN - 1) / wsg2::TN * ((N1 + wsg2::TM - 1) / wsg2::TM) * E;
+  if (wc == 13 && E <= wsg::MAX_E && ws2_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
+    int64_t grid = cu_count();
+    if (grid > ws2_all) grid = ws2_all;
+    hipLaunchKernelGGL(k_wgrad_ws256, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2,
+                       (N2 + wsg2::TN - 1) / wsg2::TN, ws2_all, dw, beta);
+    return;
+  }
   const int64_t ws_all = (N2 + wsg::TN - 1) / wsg::TN * ((N1 + wsg::TM - 1) / wsg::TM) * E;
-  if (wc == 10 && E <= wsg::MAX_E && ws_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
+  if ((wc == 10 || wc == 13) && E <= wsg::MAX_E && ws_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
     const int64_t n_nt = (N2 + wsg::TN - 1) / wsg::TN;
     const int64_t n_all = ws_all;
     int64_t grid = cu_count();
