@@ -65,14 +65,12 @@ def work_table(c, off, off_pad):
         "F7 SiLU + H quant (NVFP4 4/6)": ("hbm", A * F * (4.0 + nv)),
         "F8 down GEMM (NVFP4)": ("f16", gem),
         "F9 combine": ("hbm", A * d * 4.0 + T * d * 2.0 + A * 8.0),
-        "B1 dY quant row-wise (MXFP8)": ("hbm", T * d * 2.0 + A * 8.0 + A * d * mxb),
-        "B1 dY quant transposed (MXFP8)": ("hbm", T * d * 2.0 + A * 8.0 + d * Ptot * mxb),
+        "B1 dY quant row-wise + transposed (MXFP8)": ("hbm", T * d * 2.0 + A * 8.0 + A * d * mxb + d * Ptot * mxb),
         "B2 W_down requant SR-T": ("hbm", E * d * F * (nv + mxb)),
         "B3 down dgrad (MXFP8)": ("fp8", gem),
         "B4 H requant SR-T": ("hbm", A * F * nv + F * Ptot * mxb),
         "B5 down wgrad (MXFP8)": ("fp8", gem, wg_bytes(d, F)),
-        "B6 SiLU' + dU quant row-wise": ("hbm", A * F * (4.0 + 2.0 + mxb)),
-        "B6 SiLU' + dU quant transposed": ("hbm", A * F * 6.0 + F * Ptot * mxb),
+        "B6 SiLU' + dU quant row-wise + transposed": ("hbm", A * F * (4.0 + 2.0 + mxb) + F * Ptot * mxb),
         "B7 W_up requant SR-T": ("hbm", E * d * F * (nv + mxb)),
         "B8 up dgrad (MXFP8)": ("fp8", gem),
         "B9 X requant SR-T": ("hbm", A * d * nv + d * Ptot * mxb),
@@ -91,12 +89,12 @@ KERNEL_OF = {
     "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_ws (bf16)",
     "F8 down GEMM (NVFP4)": "k_gemm_fwd_ws (f32)",
     "F7 SiLU + H quant (NVFP4 4/6)": "nvfp4 quant 4/6 silu", "F9 combine": "k_combine",
-    "B1 dY quant row-wise (MXFP8)": "k_mx_rows", "B1 dY quant transposed (MXFP8)": "k_mx_T",
+    "B1 dY quant row-wise + transposed (MXFP8)": "k_mx_T (rows + T, gather)",
     "B2 W_down requant SR-T": "k_requant_T", "B7 W_up requant SR-T": "k_requant_T",
     "B4 H requant SR-T": "k_requant_T (H)", "B9 X requant SR-T": "k_requant_T (X)",
     "B3 down dgrad (MXFP8)": "k_dgrad_ws", "B8 up dgrad (MXFP8)": "k_dgrad_ws",
     "B5 down wgrad (MXFP8)": "k_wgrad_ws256", "B10 up wgrad (MXFP8)": "k_wgrad_ws256",
-    "B6 SiLU' + dU quant row-wise": "k_mx_rows (dsilu)", "B6 SiLU' + dU quant transposed": "k_mx_T (dsilu)",
+    "B6 SiLU' + dU quant row-wise + transposed": "k_mx_T (rows + T, dsilu)",
     "B11 un-permute sum": "k_combine (unpermute)", "B12 gate gradient": "k_dgates",
     "B13 router backward": "k_route_backward",
 }

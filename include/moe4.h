@@ -224,6 +224,25 @@ int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
                 int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
                 uint8_t* out_codes, uint8_t* out_sf, void* stream);
 
+/*
+ * mxfp8_quant_rows_T - both MXFP8 copies of a gradient from one read: the
+ * row-wise one (the data-gradient operand) and the transposed one per group
+ * (the weight-gradient operand), as in the agihunt.info page, "Confirmed".
+ * Byte for byte the results of mxfp8_quant with transpose = 0 (row_codes
+ * [rows, cols], row_sf [rows, cols/32]) and with transpose = 1 (sf_layout
+ * MOE4_SF_ROWS) or 2 (MOE4_SF_BLOCKS) (t_codes, t_sf), for the same source
+ * options (row_map / row_scale or dsilu_src; no pre_op), rnd, seed and
+ * stream_id.  Needs group_row_off[n_groups] == rows (every row in a group:
+ * rows outside the groups are not written).
+ */
+int mxfp8_quant_rows_T(const void* x, int dtype, int64_t rows, int64_t cols,
+                       const int32_t* row_map, int32_t map_div, const float* row_scale,
+                       const uint16_t* dsilu_src, const int32_t* group_row_off,
+                       const int32_t* group_off_pad, int32_t n_groups, int64_t max_padded_rows,
+                       int rnd, uint64_t seed, uint32_t stream_id, int sf_layout,
+                       uint8_t* row_codes, uint8_t* row_sf, uint8_t* t_codes, uint8_t* t_sf,
+                       void* stream);
+
 /* ------------------------------------------------------------- routing */
 /*
  * moe_route_topk - top-k routing and the stable expert permutation.  The pages

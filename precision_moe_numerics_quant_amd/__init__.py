@@ -49,6 +49,9 @@ _SIGS = {
                                    _c_void_p, _int, _c_void_p]),
     "mxfp8_quant": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _int, _int,
                            _c_void_p, _c_void_p, _i32, _i64, _int, _u64, _u32, _c_void_p, _c_void_p, _c_void_p]),
+    "mxfp8_quant_rows_T": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _i32, _i64, _int, _u64, _u32, _int, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p]),
     "moe_route_backward": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_dgates": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe4_debug_check": (_int, [_c_void_p]),
@@ -253,6 +256,38 @@ def mxfp8_quant(x, rows=None, transpose=False, row_map=None, map_div=1, row_scal
                            _stream())
     _check(rc, "mxfp8_quant")
     return oc, os_
+
+
+def mxfp8_quant_rows_T(x, group_row_off, group_off_pad, rows=None, row_map=None, map_div=1, row_scale=None,
+                       dsilu_src=None, max_pr=None, rnd=RNE, seed=0, stream_id=0, sf_layout=SF_ROWS):
+    """Both MXFP8 copies of a gradient from one read (see moe4.h): returns
+    (row_codes [rows, C], row_sf [rows, C/32], t_codes [C*max_pr], t_sf [C*max_pr/32])."""
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError("mxfp8_quant_rows_T: x must be bf16 or float32")
+    _dev(x, x.dtype, "x")
+    C = x.shape[1]
+    R = (row_map.numel() if row_map is not None else x.shape[0]) if rows is None else rows
+    if row_map is not None:
+        _dev(row_map, torch.int32, "row_map")
+    if row_scale is not None:
+        _dev(row_scale, torch.float32, "row_scale")
+    if dsilu_src is not None:
+        _dev(dsilu_src, torch.bfloat16, "dsilu_src")
+    _dev(group_row_off, torch.int32, "group_row_off")
+    _dev(group_off_pad, torch.int32, "group_off_pad")
+    G = group_row_off.numel() - 1
+    if max_pr is None:
+        max_pr = max_padded_rows(R, G)
+    rc_ = _empty((R, C), torch.uint8, x)
+    rs_ = _empty((R, C // 32), torch.uint8, x)
+    tc = _empty((C * max_pr,), torch.uint8, x)
+    ts = _empty((C * max_pr // 32,), torch.uint8, x)
+    rc = lib().mxfp8_quant_rows_T(_p(x), dt, R, C, _p(row_map), map_div, _p(row_scale), _p(dsilu_src),
+                                  _p(group_row_off), _p(group_off_pad), G, max_pr, rnd, seed, stream_id, sf_layout,
+                                  _p(rc_), _p(rs_), _p(tc), _p(ts), _stream())
+    _check(rc, "mxfp8_quant_rows_T")
+    return rc_, rs_, tc, ts
 
 
 # ------------------------------------------------------------------- routing

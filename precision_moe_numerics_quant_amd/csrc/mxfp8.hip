@@ -16,6 +16,7 @@
 // random word and the lane writes 8 contiguous output bytes per column.  The
 // block amax is a 4-lane reduction (xor 16, xor 32).
 #include "act.h"
+#include "gemm_common.h"
 #include "moe4_internal.h"
 #include "mx_requant.h"
 
@@ -314,16 +315,37 @@ __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C
 }
 
 // ------------------------------------------------- transposed gradient quant
-template <int DT, int MODE, bool SR>
+// ROWS: the same tile also gives the row-wise quantisation of its valid rows
+// (the output of k_mx_rows for the same source, rounding and key), written to
+// row_c [R, C] / row_s [R, C/32]: both operands of a gradient from one read.
+// Every source row lies in one group's tile rows when off[G] == R.
+template <int DT, int MODE, bool SR, bool ROWS>
 __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, const int32_t* __restrict__ off,
                                               const int32_t* __restrict__ offp, int G, int64_t max_pr, int64_t n_ct,
                                               uint32_t base, int sfb,
                                               uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
-                                              const float* __restrict__ act_tab) {
+                                              const float* __restrict__ act_tab, uint8_t* __restrict__ row_c,
+                                              uint8_t* __restrict__ row_s) {
   __shared__ float tab[MODE >= 2 ? ACT_TAB : 1];
   __shared__ float lv[TC][TR + 1];  // [column][row]
   if (MODE >= 2) stage_act_table(tab, act_tab);
-  const int64_t ct = blockIdx.x % n_ct, rt = blockIdx.x / n_ct;
+  // Tile order.  Each column's output run of a 32-row tile is 32 bytes, a
+  // quarter line: for sources read in place, the four row tiles of a 128-row
+  // span with the same columns run back to back on one XCD (contiguous tile
+  // runs per XCD), so its L2 merges the quarters into whole lines before they
+  // go out.  For gathered rows (MODE 1) the column tiles of one row tile run
+  // together instead, so they share the gathered source rows in L2 (measured:
+  // each order is the faster one for its mode).
+  int64_t ct, rt;
+  if (MODE == 1) {
+    ct = blockIdx.x % n_ct;
+    rt = blockIdx.x / n_ct;
+  } else {
+    const int64_t n_all = (int64_t)gridDim.x / N_XCD * N_XCD;
+    const int64_t b = xcd_tile(blockIdx.x, n_all), span = b / (4 * n_ct), in_span = b - span * 4 * n_ct;
+    ct = in_span >> 2;
+    rt = span * 4 + (in_span & 3);
+  }
   TileT t;
   if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
   const int64_t c0 = ct * TC;
@@ -339,6 +361,36 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
     }
   }
   __syncthreads();
+  if (ROWS) {  // thread pair -> (row, 32-column block); each thread 16 columns
+    const int pair = tid >> 1, half = tid & 1, rr = pair >> 2, blk = pair & 3, cl0 = 32 * blk + 16 * half;
+    if (rr < t.nvalid && c0 + 32 * blk < C) {  // (C % 32 == 0: whole blocks; both threads of a pair agree)
+      float v[16];
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[i] = lv[cl0 + i][rr];
+        a = fmaxf(a, fabsf(v[i]));
+      }
+      a = fmaxf(a, __shfl_xor(a, 1, 64));
+      const int e = mx_exponent(a);
+      const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
+      const int64_t r_out = t.src0 + rr, cg = c0 + cl0;
+      uint32_t ow[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w0 = 0, w1 = 0;
+        if (SR) {
+          const uint64_t i0 = (uint64_t)(r_out * C + cg + 4 * q);
+          w0 = sr_word(base, i0 >> 1);
+          w1 = sr_word(base, (i0 >> 1) + 1);
+        }
+        ow[q] = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu) | (mx_round<SR>(v[4 * q + 1] * p, w0 >> 16) << 8) |
+                (mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu) << 16) | (mx_round<SR>(v[4 * q + 3] * p, w1 >> 16) << 24);
+      }
+      *reinterpret_cast<u32x4*>(row_c + r_out * C + cg) = u32x4{ow[0], ow[1], ow[2], ow[3]};
+      if (half == 0) row_s[r_out * (C / 32) + cg / 32] = (uint8_t)(e + 127);
+    }
+  }
   const int w = tid >> 6, l = tid & 63;
   if (c0 + 32 * w >= C) return;
   const int cp = l & 15, rseg = l >> 4;
@@ -360,7 +412,7 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
 template <int DT, int MODE>
 static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int64_t C, const int32_t* off,
                         const int32_t* offp, int G, int64_t max_pr, uint32_t base, uint8_t* oc, uint8_t* os,
-                        const float* tab, hipStream_t s) {
+                        const float* tab, hipStream_t s, uint8_t* rc = nullptr, uint8_t* rs = nullptr) {
   if (!transpose) {
     const int64_t nblk = R * (C / 32);
     dim3 grid((unsigned)((nblk + 255) / 256));
@@ -368,14 +420,24 @@ static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int
     else hipLaunchKernelGGL((k_mx_rows<DT, MODE, false>), grid, dim3(256), 0, s, g, R, C, base, oc, os, tab);
   } else {
     const int64_t n_ct = (C + TC - 1) / TC, n_rt = (max_pr + TR - 1) / TR;
-    dim3 grid((unsigned)(n_ct * n_rt));
+    // (MODE != 1: four row tiles per span and a multiple of 8 workgroups;
+    // tiles past the padded extent exit)
+    dim3 grid((unsigned)(MODE == 1 ? n_ct * n_rt : xcd_grid(n_ct * ((n_rt + 3) / 4 * 4))));
     const int sfb = transpose == 2;
-    if (sr)
-      hipLaunchKernelGGL((k_mx_T<DT, MODE, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base, sfb,
-                         oc, os, tab);
-    else
-      hipLaunchKernelGGL((k_mx_T<DT, MODE, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct, base,
-                         sfb, oc, os, tab);
+    if (rc) {
+      if (sr)
+        hipLaunchKernelGGL((k_mx_T<DT, MODE, true, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
+                           base, sfb, oc, os, tab, rc, rs);
+      else
+        hipLaunchKernelGGL((k_mx_T<DT, MODE, false, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
+                           base, sfb, oc, os, tab, rc, rs);
+    } else if (sr) {
+      hipLaunchKernelGGL((k_mx_T<DT, MODE, true, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
+                         base, sfb, oc, os, tab, nullptr, nullptr);
+    } else {
+      hipLaunchKernelGGL((k_mx_T<DT, MODE, false, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
+                         base, sfb, oc, os, tab, nullptr, nullptr);
+    }
   }
 }
 
@@ -427,11 +489,11 @@ extern "C" int mxfp8_requant_mx_sr_T(const uint8_t* codes, const uint8_t* sf, in
   return check_launch("mxfp8_requant_mx_sr_T");
 }
 
-extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
-                           int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int pre_op,
-                           int transpose, const int32_t* group_row_off, const int32_t* group_off_pad,
-                           int32_t n_groups, int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
-                           uint8_t* out_codes, uint8_t* out_sf, void* stream) {
+static int mxfp8_quant_impl(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
+                            int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int pre_op,
+                            int transpose, const int32_t* group_row_off, const int32_t* group_off_pad,
+                            int32_t n_groups, int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
+                            uint8_t* out_codes, uint8_t* out_sf, uint8_t* row_codes, uint8_t* row_sf, void* stream) {
   MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "mxfp8_quant: dtype must be BF16 or F32");
   MOE4_REQUIRE(rnd == MOE4_RNE || rnd == MOE4_SR, MOE4_EINVAL, "mxfp8_quant: rnd must be RNE or SR");
   MOE4_REQUIRE(transpose >= 0 && transpose <= 2, MOE4_EINVAL, "mxfp8_quant: transpose must be 0, 1 or 2");
@@ -456,13 +518,14 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
     tab = act_tables_device_ptr() + (dsilu_src ? ACT_TAB : 0);
   }
   if ((transpose ? max_padded_rows : rows) == 0) return MOE4_OK;
+  if (row_codes) MOE4_REQUIRE(transpose && aligned16(row_codes) && row_sf, MOE4_EINVAL, "mxfp8_quant: row outputs");
   GradSrc g{x, dtype, row_map, map_div, row_scale, dsilu_src};
   const uint32_t base = sr_base_key(seed, stream_id);
   const bool sr = rnd == MOE4_SR;
   const int mode = row_map ? 1 : (dsilu_src ? 2 : (pre_op == MOE4_PRE_SILU ? 3 : 0));
 #define MOE4_GRAD(DT, MODE)                                                                                      \
   launch_grad<DT, MODE>(transpose, sr, g, rows, cols, group_row_off, group_off_pad, n_groups, max_padded_rows, \
-                        base, out_codes, out_sf, tab, s)
+                        base, out_codes, out_sf, tab, s, row_codes, row_sf)
   if (dtype == MOE4_F32) {
     if (mode == 0) MOE4_GRAD(MOE4_F32, 0);
     else if (mode == 1) MOE4_GRAD(MOE4_F32, 1);
@@ -475,4 +538,28 @@ extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols,
   }
 #undef MOE4_GRAD
   return check_launch("mxfp8_quant");
+}
+
+extern "C" int mxfp8_quant(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
+                           int32_t map_div, const float* row_scale, const uint16_t* dsilu_src, int pre_op,
+                           int transpose, const int32_t* group_row_off, const int32_t* group_off_pad,
+                           int32_t n_groups, int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id,
+                           uint8_t* out_codes, uint8_t* out_sf, void* stream) {
+  return mxfp8_quant_impl(x, dtype, rows, cols, row_map, map_div, row_scale, dsilu_src, pre_op, transpose,
+                          group_row_off, group_off_pad, n_groups, max_padded_rows, rnd, seed, stream_id, out_codes,
+                          out_sf, nullptr, nullptr, stream);
+}
+
+extern "C" int mxfp8_quant_rows_T(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,
+                                  int32_t map_div, const float* row_scale, const uint16_t* dsilu_src,
+                                  const int32_t* group_row_off, const int32_t* group_off_pad, int32_t n_groups,
+                                  int64_t max_padded_rows, int rnd, uint64_t seed, uint32_t stream_id, int sf_layout,
+                                  uint8_t* row_codes, uint8_t* row_sf, uint8_t* t_codes, uint8_t* t_sf,
+                                  void* stream) {
+  MOE4_REQUIRE(sf_layout == MOE4_SF_ROWS || sf_layout == MOE4_SF_BLOCKS, MOE4_EINVAL,
+               "mxfp8_quant_rows_T: sf_layout must be MOE4_SF_ROWS or MOE4_SF_BLOCKS");
+  MOE4_REQUIRE(row_codes && row_sf, MOE4_EINVAL, "mxfp8_quant_rows_T: NULL pointer");
+  return mxfp8_quant_impl(x, dtype, rows, cols, row_map, map_div, row_scale, dsilu_src, MOE4_PRE_NONE,
+                          sf_layout == MOE4_SF_BLOCKS ? 2 : 1, group_row_off, group_off_pad, n_groups,
+                          max_padded_rows, rnd, seed, stream_id, t_codes, t_sf, row_codes, row_sf, stream);
 }

@@ -26,7 +26,7 @@ import torch
 from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_dgates,
                moe_gather_rows, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd,
                moe_grouped_gemm_mx, moe_route_backward, moe_route_topk, moe_unpermute_sum, mxfp8_quant,
-               mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
+               mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
@@ -124,22 +124,21 @@ def _backward_chain(fw, dy, timer, req):
             _tick(timer, label)
         return out
     _tick(timer, None)
-    dy_row = mxfp8_quant(dy, rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat)
-    _tick(timer, "B1 dY quant row-wise (MXFP8)")
-    dy_col = mxfp8_quant(dy, rows=A, transpose=True, row_map=r["perm"], map_div=k, row_scale=g_flat,
-                         group_row_off=r["off"], group_off_pad=r["off_pad"], max_pr=mpr, sf_layout=SF_BLOCKS)
-    _tick(timer, "B1 dY quant transposed (MXFP8)")
+    # B1: both MXFP8 copies of the gated, gathered dY from one read
+    q = mxfp8_quant_rows_T(dy, r["off"], r["off_pad"], rows=A, row_map=r["perm"], map_div=k, row_scale=g_flat,
+                           max_pr=mpr, sf_layout=SF_BLOCKS)
+    dy_row, dy_col = q[:2], q[2:]
+    _tick(timer, "B1 dY quant row-wise + transposed (MXFP8)")
     wdT = get("wdT", "B2 W_down requant SR-T")
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
     _tick(timer, "B3 down dgrad (MXFP8)")
     hT = get("hT", "B4 H requant SR-T")
     dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
     _tick(timer, "B5 down wgrad (MXFP8)")
-    du_row = mxfp8_quant(dH, dsilu_src=fw["U"])
-    _tick(timer, "B6 SiLU' + dU quant row-wise")
-    du_col = mxfp8_quant(dH, transpose=True, dsilu_src=fw["U"], group_row_off=r["off"], group_off_pad=r["off_pad"],
-                         max_pr=mpr, sf_layout=SF_BLOCKS)
-    _tick(timer, "B6 SiLU' + dU quant transposed")
+    # B6: both MXFP8 copies of dU = dH * silu'(U) from one read
+    q = mxfp8_quant_rows_T(dH, r["off"], r["off_pad"], dsilu_src=fw["U"], max_pr=mpr, sf_layout=SF_BLOCKS)
+    du_row, du_col = q[:2], q[2:]
+    _tick(timer, "B6 SiLU' + dU quant row-wise + transposed")
     wuT = get("wuT", "B7 W_up requant SR-T")
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")

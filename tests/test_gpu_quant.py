@@ -249,6 +249,53 @@ def test_mxfp8_grad_quant_gated_rows(rnd, transpose):
         assert_bytes_equal(to_np(os_), s_ref, "scales")
 
 
+@pytest.mark.parametrize("lay", [SF_ROWS, SF_BLOCKS])
+@pytest.mark.parametrize("rnd", [0, 1])                          # RNE, SR
+def test_mxfp8_quant_rows_T_gated_against_oracle(rnd, lay):
+    """Both copies of the gated, gathered dY from one read, against the
+    oracle's row-wise and transposed quantisations (ragged groups, an empty
+    expert, a column count past one 128-column tile)."""
+    T, d, k, E = 130, 160, 3, 7
+    rng = np.random.default_rng(11)
+    dy = synth.randn((T, d), 1e-3, "cpu", 12, "dy", torch.bfloat16)
+    idx = np.stack([rng.permutation(E - 1)[:k] for _ in range(T)])        # expert E - 1 gets no tokens
+    from oracle import route
+    P = route.permutation(idx, E)
+    gates = rng.random((T, k)).astype(np.float32)
+    dyp = (gates.reshape(-1)[P["perm"]][:, None] * fmt.bf16_to_f32(synth.bf16_bits(dy))[P["perm"] // k]).astype(np.float32)
+    A = T * k
+    rc_, rs_, tc, ts = m4.mxfp8_quant_rows_T(dy.cuda(), cuda_i32(P["off"]), cuda_i32(P["off_pad"]), rows=A,
+                                             row_map=cuda_i32(P["perm"]), map_div=k,
+                                             row_scale=torch.from_numpy(gates.reshape(-1)).cuda(), rnd=rnd, seed=3,
+                                             stream_id=4, sf_layout=lay)
+    c_ref, s_ref = mx.quantize_rowwise(dyp, rnd, 3, 4)
+    assert_bytes_equal(to_np(rc_), c_ref, "row codes")
+    assert_bytes_equal(to_np(rs_), s_ref, "row scales")
+    c_ref, s_ref = mx.quantize_transposed(dyp, P["off"], rnd, 3, 4, sf_layout=LAYOUTS[lay])
+    n = d * P["off_pad"][-1]
+    assert_bytes_equal(to_np(tc)[:n], c_ref, "transposed codes")
+    assert_bytes_equal(to_np(ts)[: n // 32], s_ref, "transposed scales")
+
+
+@pytest.mark.parametrize("rnd", [0, 1])                          # RNE, SR
+def test_mxfp8_quant_rows_T_dsilu_matches_separate_calls(rnd):
+    """SiLU'-scaled float32 gradient: the fused call equals the two separate
+    calls byte for byte (each pinned to the oracle above)."""
+    R, F = 300, 256
+    off = np.array([0, 40, 40, 170, 300])
+    dh = torch.from_numpy(synth.randn((R, F), 1e-3, "cpu", 14, "dh").numpy()).cuda()
+    u = synth.randn((R, F), 2.0, "cpu", 15, "u", torch.bfloat16).cuda()
+    offp = mx.padded_offsets(off)
+    kw = dict(dsilu_src=u, rnd=rnd, seed=9, stream_id=2)
+    rc_, rs_, tc, ts = m4.mxfp8_quant_rows_T(dh, cuda_i32(off), cuda_i32(offp), sf_layout=SF_BLOCKS, **kw)
+    oc, os_ = m4.mxfp8_quant(dh, **kw)
+    tc2, ts2 = m4.mxfp8_quant(dh, transpose=True, group_row_off=cuda_i32(off), group_off_pad=cuda_i32(offp),
+                              sf_layout=SF_BLOCKS, **kw)
+    assert torch.equal(rc_, oc) and torch.equal(rs_, os_)
+    n = F * offp[-1]
+    assert torch.equal(tc[:n], tc2[:n]) and torch.equal(ts[: n // 32], ts2[: n // 32])
+
+
 @pytest.mark.parametrize("transpose", [False, "rows", "blocks"])
 def test_mxfp8_grad_quant_dsilu(transpose):
     R, F = 150, 128
