@@ -74,7 +74,11 @@ def _fwd_operands(M_list, N, K, seed, ts_per_group=False):
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([64], 64, 64), ([5, 0, 0, 257], 512, 1024)])
+# (N, K) pick the kernels: 192 x 320 and 64 x 64 the register-staged one,
+# 160 x 256 the 128 x 128 direct-to-LDS one, 384 x 512 the warp-specialised
+# 128 x 128 one, 512 x 1024 the warp-specialised 128 x 256 one
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([64], 64, 64), ([5, 0, 0, 257], 512, 1024),
+                                        ([5, 300, 0, 129], 160, 256), ([0, 37, 130, 1, 300], 384, 512)])
 def test_grouped_gemm_fwd_tolerance(M_list, N, K, out_dtype):
     E = len(M_list)
     per_group = out_dtype == "f32"
@@ -119,7 +123,10 @@ def _mx_rows(M, K, seed, scale=1.0):
     return mx.quantize_rowwise(x, mx.RNE)
 
 
-@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([256], 128, 4096 // 16), ([3, 200], 96, 96)])
+# 192 x 320 and 96 x 96: register-staged kernel; 128 x 256: warp-specialised
+# 128 x 128; 256 x 384: warp-specialised 128 x 256 (three slabs)
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([256], 128, 4096 // 16), ([3, 200], 96, 96),
+                                        ([0, 37, 130, 1, 300], 256, 384)])
 def test_grouped_gemm_dgrad_tolerance(M_list, N, K):
     E = len(M_list)
     off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
@@ -199,6 +206,7 @@ def test_grouped_gemm_wgrad_many_experts(beta):
     ([0] * 5 + [2000] + [0] * 6 + [1, 0, 33, 0], 128, 128),   # 16 tiles: two workgroups per XCD, most ranges empty
     ([700], 512, 512),                                         # one expert cut into several XCD ranges
     ([3, 0, 1500, 64, 0, 0, 31, 900] * 3, 256, 128),          # 48 tiles, heavy experts next to empty ones
+    ([50, 0, 700, 5], 288, 160),                               # a 256-row tile with 32 valid rows
 ])
 def test_grouped_gemm_wgrad_skewed_xcd_ranges(M_list, N1, N2):
     """Tile counts that are multiples of 8 but below the resident grid, with
@@ -279,7 +287,9 @@ def test_route_backward_bit_exact(T, E, k):
     assert_bytes_equal(got.view(np.uint32), want.view(np.uint32), "dlogits")
 
 
-@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 256), ([256], 128, 1024), ([3, 200], 96, 128)])
+# warp-specialised kernels for N = 128 (128 x 128) and N = 512 (128 x 256)
+@pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 256), ([256], 128, 1024), ([3, 200], 96, 128),
+                                        ([0, 37, 130, 1, 300], 512, 256)])
 def test_grouped_gemm_mx_bf16_and_f32(M_list, N, K):
     """The MXFP8 forward GEMM: bf16 output within tolerance of the exact
     product; float32 output identical to the dgrad call."""
