@@ -30,8 +30,9 @@ __device__ inline int swz(int col, int chunk) { return chunk ^ ((col >> 3) & 7);
 
 // Exact q * sc of the 8 codes of one row (byte p of cw -> columns 2p, 2p+1);
 // a zero scale gives signed zeros.
+template <bool FIELDS = false>
 __device__ inline void dequant8(uint32_t cw, uint32_t sbyte, float (&q)[8]) {
-  const float scf = e4m3_to_f32(sbyte);
+  const float scf = e4m3_decode<FIELDS>(sbyte);
   const float m = scf == 0.0f ? 0.0f : mant_factor(scf);
   f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 0);
   f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 1);
@@ -59,6 +60,14 @@ __device__ inline uint32_t sr_fp8_into(uint32_t old, float v, uint32_t r, int se
     default: return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(old, v, r, 1.0f, 3);
   }
 }
+
+// Whether fl(fl(q * S) * 2^-ex) == fl(q * (S * 2^-ex)) for every dequantised
+// NVFP4 value q of a block and its MX exponent ex: for 2^-100 <= S < 2^8 the
+// products q * S (|q| in [2^-10, 2688] or 0) and S * 2^-ex (ex in [-118, 12]
+// for a nonzero column) stay normal and finite and the result is above 2^-14,
+// so scaling by the power of two commutes with rounding; a column with
+// ex = -127 is then all zeros, and a factor 0 keeps the signed zeros.
+__device__ inline bool fold_scale_ok(float S) { return S >= 0x1p-100f && S < 0x1p8f; }
 
 // SR quantisation of one lane's 8 columns x nvalid rows; each group of 4
 // rows leaves as one dword per column (byte i % 4 = row i) through

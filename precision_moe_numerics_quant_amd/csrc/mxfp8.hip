@@ -214,7 +214,12 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
     const int64_t j0 = src0 * (C / 2) + c / 2;  // pair index of (row src0, column c)
     const uint32_t key0 = fmix32(base);
     const bool fast = j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32);
-    if (fast && nvalid == 32)
+    if (!MX && fast && nvalid == 32 && fold_scale_ok(S)) {  // one multiply by S * 2^-ex per value
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = ex[q] == -127 ? 0.0f : S * pc[q];
+      requant_block<true, true>(deq, nvalid, 1.0f, f, j0, C / 2, base, key0, put);
+    } else if (fast && nvalid == 32)
       requant_block<true, true>(deq, nvalid, S, pc, j0, C / 2, base, key0, put);
     else if (fast)
       requant_block<true, false>(deq, nvalid, S, pc, j0, C / 2, base, key0, put);
