@@ -359,12 +359,14 @@ int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_sf,         
 /*
  * moe_combine - y[t] = bf16(acc), acc = 0; for j = 0..k-1:
  * acc = fl(acc + fl(gates[t,j] * yp[inv_perm[t*k+j]])).  yp [T*k, d] float32.
+ * 1 <= k <= 16, d % 4 == 0.
  */
 int moe_combine(const float* yp, const float* gates, const int32_t* inv_perm, int64_t T, int32_t k,
                 int64_t d, uint16_t* y, void* stream);
 
 /*
  * moe_unpermute_sum - dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dxp[inv_perm[t*k+j]]).
+ * 1 <= k <= 16, d % 4 == 0.
  */
 int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                       uint16_t* dx, void* stream);
@@ -376,7 +378,8 @@ int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int3
  * paragraph on communication).  dy [T, d] bf16, yp [T*k, d] float32 (the
  * forward's expert outputs), dg [T, k] float32 out.  Float32 accumulation:
  * each lane sums its columns 8l + 512i in order, then a fixed butterfly over
- * the 64 lanes (deterministic).  d % 8 == 0; dy and yp 16-byte aligned.
+ * the 64 lanes (deterministic).  1 <= k <= 16, d % 8 == 0; dy and yp 16-byte
+ * aligned.
  */
 int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                float* dg, void* stream);

@@ -166,18 +166,33 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yp, c
   const int64_t nq = d / 4;
   if (q >= T * nq) return;
   const int64_t t = q / nq, c = (q % nq) * 4;
+  // all k row indices, then all k row loads in flight, then the sum in slot
+  // order (k <= MAXK, checked at launch)
+  int64_t rows[MAXK];
+  float g[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      const int64_t row = inv[t * k + j];
+      rows[j] = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+      g[j] = GATED ? gates[t * k + j] : 1.0f;
+    }
+  }
+  f32x4 v[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const f32x4*>(yp + rows[j] * d + c);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < k; ++j) {
-    int64_t row = inv[t * k + j];
-    row = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
-    f32x4 v = *reinterpret_cast<const f32x4*>(yp + row * d + c);
-    if (GATED) {
-      const float g = gates[t * k + j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = acc[i] + g * v[i];
-    } else {
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      if (GATED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = acc[i] + v[i];
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + g[j] * v[j][i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + v[j][i];
+      }
     }
   }
   u32x2 out = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
@@ -299,7 +314,8 @@ extern "C" int moe_gather_rows(const uint8_t* codes, const uint8_t* sf, int64_t 
 
 extern "C" int moe_combine(const float* yp, const float* gates, const int32_t* inv_perm, int64_t T, int32_t k,
                            int64_t d, uint16_t* y, void* stream) {
-  MOE4_REQUIRE(T >= 0 && k >= 1 && d > 0 && d % 4 == 0, MOE4_EINVAL, "moe_combine: bad sizes (d % 4 == 0)");
+  MOE4_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && d > 0 && d % 4 == 0, MOE4_EINVAL,
+               "moe_combine: bad sizes (1 <= k <= 16, d % 4 == 0)");
   MOE4_REQUIRE(T == 0 || (yp && gates && inv_perm && y), MOE4_EINVAL, "moe_combine: NULL pointer");
   MOE4_REQUIRE(aligned16(yp) && aligned16(y), MOE4_EALIGN, "moe_combine: misaligned pointer");
   if (T == 0) return MOE4_OK;
@@ -311,7 +327,8 @@ extern "C" int moe_combine(const float* yp, const float* gates, const int32_t* i
 
 extern "C" int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                                  uint16_t* dx, void* stream) {
-  MOE4_REQUIRE(T >= 0 && k >= 1 && d > 0 && d % 4 == 0, MOE4_EINVAL, "moe_unpermute_sum: bad sizes (d % 4 == 0)");
+  MOE4_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && d > 0 && d % 4 == 0, MOE4_EINVAL,
+               "moe_unpermute_sum: bad sizes (1 <= k <= 16, d % 4 == 0)");
   MOE4_REQUIRE(T == 0 || (dxp && inv_perm && dx), MOE4_EINVAL, "moe_unpermute_sum: NULL pointer");
   MOE4_REQUIRE(aligned16(dxp) && aligned16(dx), MOE4_EALIGN, "moe_unpermute_sum: misaligned pointer");
   if (T == 0) return MOE4_OK;
@@ -323,7 +340,8 @@ extern "C" int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int6
 
 extern "C" int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* inv_perm, int64_t T, int32_t k,
                           int64_t d, float* dg, void* stream) {
-  MOE4_REQUIRE(T >= 0 && k >= 1 && d > 0 && d % 8 == 0, MOE4_EINVAL, "moe_dgates: bad sizes (d % 8 == 0)");
+  MOE4_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && d > 0 && d % 8 == 0, MOE4_EINVAL,
+               "moe_dgates: bad sizes (1 <= k <= 16, d % 8 == 0)");
   MOE4_REQUIRE(T == 0 || (dy && yp && inv_perm && dg), MOE4_EINVAL, "moe_dgates: NULL pointer");
   MOE4_REQUIRE(aligned16(dy) && aligned16(yp), MOE4_EALIGN, "moe_dgates: misaligned pointer");
   if (T == 0) return MOE4_OK;
