@@ -32,6 +32,7 @@ route     top-k routing, gates and the stable expert permutation
 silu      correctly rounded SiLU and SiLU' tables over all bf16 inputs
 gemm      float64 grouped GEMMs on exactly dequantised operands
 layer     the whole expert layer, forward and backward
+combine_q the combine-path quantiser (block Hadamard + 8-bit fixed-point MX)
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py``
 against closed forms, brute force, library routines or invariants; the pages
