@@ -221,6 +221,7 @@ def gpu_run(steps, warmup):
         prev = ev
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
+    payload = combine_payload_bench(fw, c)
     del fw, bw
     # the MXFP8-forward variant of the same layer on the same inputs
     def step_mx(t=None):
@@ -244,7 +245,47 @@ def gpu_run(steps, warmup):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
-    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx)
+    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload
+
+
+def combine_payload_bench(fw, c, reps=20):
+    """The combine with the expert outputs sent as the 8.25-bit payload (32-point
+    Hadamard + 8-bit fixed point, E8M0 scale per 32) on this step's Yp and
+    routing: the sender's quantiser and the receiver's decode + combine, each
+    the median of reps runs timed with HIP events on the library's stream,
+    against the float32 combine of the same rows."""
+    import precision_moe_numerics_quant_amd as m4
+    Yp, r = fw["Yp"], fw["route"]
+    T, k, d = c["T"], c["k"], c["d"]
+    A = T * k
+    codes, sf = m4.moe_hmx8_quant(Yp)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_q = timed(lambda: m4.moe_hmx8_quant(Yp))
+    t_c = timed(lambda: m4.moe_combine_hmx8(codes, sf, r["gates"], r["inv_perm"]))
+    t_f = timed(lambda: m4.moe_combine(Yp, r["gates"], r["inv_perm"]))
+    pay = A * d * (1 + 1 / 32)
+    b_q = A * d * 4 + pay
+    b_c = pay + A * 8 + T * d * 2
+    b_f = A * d * 4 + A * 8 + T * d * 2
+
+    def rate(b, t):
+        return {"ms": round(t, 4), "GBps": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / (PEAK_HBM / 1e9), 4)}
+
+    return {"bits_per_value": 8.0 * pay / (A * d), "payload_bytes": int(pay), "float32_bytes": A * d * 4,
+            "bf16_bytes": A * d * 2, "quant": rate(b_q, t_q), "combine_from_payload": rate(b_c, t_c),
+            "float32_combine": rate(b_f, t_f)}
 
 
 def quantizer_microbench(reps=20):
@@ -341,7 +382,7 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx) = gpu_run(args.steps, args.warmup)
+    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload = gpu_run(args.steps, args.warmup)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
     calls = {}
@@ -425,6 +466,8 @@ def main():
                                 for n in ("F6 up GEMM (MXFP8)", "F8 down GEMM (MXFP8)") if n in per_mx},
             "breakdown_ms": per_mx,
         },
+        # the combine fed by the 8.25-bit payload the pages send back between GPUs
+        "combine_payload_8p25": payload,
     }
     if args.copy_calibration:
         copy_calibration()

@@ -384,6 +384,50 @@ int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int3
 int moe_dgates(const uint16_t* dy, const float* yp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                float* dg, void* stream);
 
+/* ------------------------------------------- combine-path quantiser (8.25 bits) */
+/*
+ * The expert results travelling back for the combine are sent as 8-bit
+ * fixed-point values with one E8M0 scale per 32 values after a Hadamard
+ * transform that spreads extreme values over each block; 16 bits per value
+ * become 8.25 (lhc.media page, paragraph on communication).  The page names
+ * the element format "S2F6" and gives nothing more; it is read here as signed
+ * fixed point with 2 integer bits (sign included) and 6 fraction bits, the
+ * element of OCP's MXINT8:
+ *  - transform: the unnormalised Sylvester H_32 (entries +-1) over each block
+ *    of 32 consecutive values of a row, in float32 as five butterfly stages
+ *    (a, b) -> (a + b, a - b) with partner distance 1, 2, 4, 8, 16;
+ *  - scale: e = floor(log2 max|y|) over the block, clamped to [-127, 127]
+ *    (-127 for an all-zero block), one byte e + 127;
+ *  - codes: int8 c = clamp(rne(y * 2^(6 - e)), -127, 127), worth c * 2^(e - 6).
+ * Inputs must be finite with |x| <= 2^122.  Rows are contiguous; cols % 32 == 0.
+ */
+
+/*
+ * moe_hmx8_quant - x [rows, cols] float32 (16-byte aligned) -> codes int8
+ * [rows, cols] (8-byte aligned) and scales uint8 [rows, cols/32].  Buffers are
+ * the caller's (device memory).  Returns MOE4_EINVAL / MOE4_EALIGN on bad
+ * sizes or pointers (nothing launched).
+ */
+int moe_hmx8_quant(const float* x, int64_t rows, int64_t cols, int8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_hmx8_dequant - exact decode of moe_hmx8_quant's payload:
+ * out = H_32 (c * 2^(e - 6)) / 32 per block, float32 [rows, cols] (16-byte
+ * aligned).  The integer butterflies and the power-of-two scale make every
+ * value exact.
+ */
+int moe_hmx8_dequant(const int8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, float* out,
+                     void* stream);
+
+/*
+ * moe_combine_hmx8 - moe_combine over the decoded payload: y[t] = bf16(acc),
+ * acc = 0; for j = 0..k-1: acc = fl(acc + fl(gates[t,j] * Yhat[inv_perm[t*k+j]])),
+ * Yhat the exact decode of codes / scales ([T*k, d], the moe_hmx8_quant layout).
+ * y [T, d] bf16 and codes 16-byte aligned; 1 <= k <= 16, d % 32 == 0.
+ */
+int moe_combine_hmx8(const int8_t* codes, const uint8_t* scales, const float* gates, const int32_t* inv_perm,
+                     int64_t T, int32_t k, int64_t d, uint16_t* y, void* stream);
+
 /*
  * moe_silu_eval - correctly rounded float32 silu(u) and silu'(u) of bf16 u
  * (either output may be NULL).  Test aid for the activation fused into

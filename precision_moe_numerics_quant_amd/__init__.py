@@ -71,6 +71,10 @@ _SIGS = {
     "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_unpermute_sum": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_silu_eval": (_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_hmx8_quant": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_hmx8_dequant": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
+    "moe_combine_hmx8": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p,
+                                _c_void_p]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -380,6 +384,34 @@ def moe_combine(yp, gates, inv_perm):
     y = _empty((T, d), torch.bfloat16, yp)
     rc = lib().moe_combine(_p(yp), _p(gates), _p(inv_perm), T, k, d, _p(y), _stream())
     _check(rc, "moe_combine")
+    return y
+
+
+def moe_hmx8_quant(x):
+    """Combine-path payload of x [rows, cols] float32: (codes int8, scales uint8 [rows, cols/32])."""
+    _dev(x, torch.float32, "moe_hmx8_quant")
+    rows, cols = x.shape
+    codes = _empty((rows, cols), torch.int8, x)
+    sf = _empty((rows, cols // 32), torch.uint8, x)
+    rc = lib().moe_hmx8_quant(_p(x), rows, cols, _p(codes), _p(sf), _stream())
+    _check(rc, "moe_hmx8_quant")
+    return codes, sf
+
+
+def moe_hmx8_dequant(codes, sf):
+    rows, cols = codes.shape
+    out = _empty((rows, cols), torch.float32, codes)
+    rc = lib().moe_hmx8_dequant(_p(codes), _p(sf), rows, cols, _p(out), _stream())
+    _check(rc, "moe_hmx8_dequant")
+    return out
+
+
+def moe_combine_hmx8(codes, sf, gates, inv_perm):
+    T, k = gates.shape
+    d = codes.shape[1]
+    y = _empty((T, d), torch.bfloat16, codes)
+    rc = lib().moe_combine_hmx8(_p(codes), _p(sf), _p(gates), _p(inv_perm), T, k, d, _p(y), _stream())
+    _check(rc, "moe_combine_hmx8")
     return y
 
 

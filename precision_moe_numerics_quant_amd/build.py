@@ -16,7 +16,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe4.so")
-SOURCES = ["capi.hip", "nvfp4_quant.hip", "mxfp8.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip"]
+SOURCES = ["capi.hip", "nvfp4_quant.hip", "mxfp8.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "combine_q.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]

@@ -23,8 +23,8 @@ router logits.
 """
 import torch
 
-from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_dgates,
-               moe_gather_rows, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd,
+from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_combine_hmx8,
+               moe_dgates, moe_gather_rows, moe_hmx8_quant, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd,
                moe_grouped_gemm_mx, moe_route_backward, moe_route_topk, moe_unpermute_sum, mxfp8_quant,
                mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
@@ -56,9 +56,13 @@ def quantize_weights(w_up, w_down, timer=None, seed=1, layer=0):
                 shape=(E, F, d))
 
 
-def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0):
+def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0, combine_payload=False):
     """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32.
-    (seed, layer): the SR key of the weights' backward copies made here."""
+    (seed, layer): the SR key of the weights' backward copies made here.
+    combine_payload: send the expert outputs to the combine as the 8.25-bit
+    payload (32-point Hadamard + 8-bit fixed point with an E8M0 scale per 32,
+    lhc.media page, paragraph on communication) instead of float32; the
+    backward treats that quantisation as the identity."""
     T, d = x.shape
     E, F, _ = w_up.shape
     if wq is None:
@@ -80,9 +84,17 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
     Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
                               r["off"], torch.float32, a_ts_per_group=True)
     _tick(timer, "F8 down GEMM (NVFP4)")
-    y = moe_combine(Yp, r["gates"], r["inv_perm"])
-    _tick(timer, "F9 combine")
-    return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k))
+    payload = None
+    if combine_payload:
+        payload = moe_hmx8_quant(Yp)
+        _tick(timer, "F9a Yp -> 8.25-bit payload (Hadamard + 8-bit)")
+        y = moe_combine_hmx8(payload[0], payload[1], r["gates"], r["inv_perm"])
+        _tick(timer, "F9b combine from the payload")
+    else:
+        y = moe_combine(Yp, r["gates"], r["inv_perm"])
+        _tick(timer, "F9 combine")
+    return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k),
+                payload=payload)
 
 
 def backward(fw, dy, seed=1, layer=0, timer=None):

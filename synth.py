@@ -27,7 +27,7 @@ import numpy as np
 import torch
 
 TENSOR_IDS = {"x": 1, "w_up": 2, "w_down": 3, "logits": 4, "dy": 5, "rows": 6, "outlier": 7,
-              "u": 8, "dh": 9, "misc": 10}
+              "u": 8, "dh": 9, "misc": 10, "yp": 11}
 
 
 def generator(device, seed, tensor):

@@ -78,6 +78,31 @@ def test_layer_config1_end_to_end():
         assert v < 2e-2, (key, v)
 
 
+def test_layer_config1_combine_payload():
+    """The same tiny layer with the expert outputs sent to the combine as the
+    8.25-bit payload (Hadamard + 8-bit fixed point): the payload tracks the
+    oracle's quantisation of its own Yp (Yp differs only by GEMM rounding) and y
+    stays within the 8-bit format's error of the oracle's float32 combine."""
+    from oracle import combine_q as cq
+    inp = synth.config_inputs(1, device="cpu")
+    k = 2
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k, seed=synth.SR_SEED,
+                       combine_payload=True)
+    x = synth.bf16_bits(inp["x"])
+    ofw = olayer.forward(x, synth.f32_np(inp["w_up"]), synth.f32_np(inp["w_down"]), synth.f32_np(inp["logits"]), k)
+    c_o, s_o = cq.quantize(ofw["Yp"])
+    same_c = np.mean(to_np(fw["payload"][0]) == c_o)
+    same_s = np.mean(to_np(fw["payload"][1]) == s_o)
+    y_pay = fmt.bf16_to_f32(cq.combine_payload(c_o, s_o, ofw["gates"], ofw["perm"]["inv_perm"], k))
+    e_fmt = _rel(y_pay, fmt.bf16_to_f32(ofw["y"]))        # the format's own error, oracle side
+    e_gpu = _rel(fmt.bf16_to_f32(to_np(fw["y"])), fmt.bf16_to_f32(ofw["y"]))
+    print(f"payload codes identical {same_c:.5f}, scales {same_s:.5f}; rel error of y: format {e_fmt:.3g}, "
+          f"GPU {e_gpu:.3g}")
+    assert same_c > 0.98 and same_s > 0.99
+    assert e_gpu < 2.0 * e_fmt + 2e-3
+
+
 def test_layer_mxfp8_forward_config1_end_to_end():
     """The MXFP8-forward variant on the tiny layer: routing, the MXFP8 weights
     and the gathered MXFP8 X are bit-exact; the weight requantisations (which
