@@ -225,7 +225,8 @@ def gpu_run(steps, warmup):
     del fw, bw
     # the MXFP8-forward variant of the same layer on the same inputs
     def step_mx(t=None):
-        fw = layer.forward_mx(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t)
+        fw = layer.forward_mx(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t,
+                              seed=synth.SR_SEED)
         layer.backward_mx(fw, inp["dy"], seed=synth.SR_SEED, timer=t)
     for _ in range(warmup):
         step_mx()

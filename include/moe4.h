@@ -196,6 +196,24 @@ int mxfp8_requant_mx_sr_T(const uint8_t* codes, const uint8_t* sf, int64_t rows,
                           uint8_t* out_codes, uint8_t* out_sf, void* stream);
 
 /*
+ * mxfp8_quant_requant_T - weights of the MXFP8-forward layers: both copies in
+ * one pass.  Byte for byte the result of mxfp8_quant on float32 x [rows, cols]
+ * (RNE, row-wise blocks of 32 along the row) followed by mxfp8_requant_mx_sr_T
+ * of that result with n_groups equal row groups, no padding and
+ * MOE4_SF_ROWS (agihunt.info page, "Confirmed": the last 16.6% of layers in
+ * MXFP8; lhc.media page, the paragraphs on FP32 master weights and on
+ * requantising the dequantised, transposed values with stochastic rounding).
+ * rows = n_groups * R_g with R_g % 32 == 0; codes [rows, cols], sf
+ * [rows, cols/32]; t_codes [cols * rows] holds group g's [cols][R_g] block at
+ * cols * g * R_g, t_sf [cols * rows / 32] its [cols][R_g / 32] scales at
+ * cols * g * R_g / 32; seed, stream_id as in mxfp8_requant_mx_sr_T.
+ * cols % 32 == 0; x, codes and t_codes 16-byte aligned.  No workspace.
+ */
+int mxfp8_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint64_t seed,
+                          uint32_t stream_id, uint8_t* codes, uint8_t* sf, uint8_t* t_codes, uint8_t* t_sf,
+                          void* stream);
+
+/*
  * mxfp8_quant - MXFP8 quantisation of a gradient (or, for the MXFP8-forward
  * layer, of a forward operand).  The value of source element (r, c) is:
  *   v = x[src(r), c]                                    (no options)

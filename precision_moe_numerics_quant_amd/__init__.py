@@ -71,6 +71,8 @@ _SIGS = {
     "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_unpermute_sum": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_silu_eval": (_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "mxfp8_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _u64, _u32, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p]),
     "moe_hmx8_quant": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "moe_hmx8_dequant": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
     "moe_combine_hmx8": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p,
@@ -174,6 +176,21 @@ def nvfp4_quant_requant_T(x, n_groups, seed=1, stream_id=0):
                                      _p(ms), _p(ws), ws.numel(), _stream())
     _check(rc, "nvfp4_quant_requant_T")
     return codes, sf, ts, mc, ms
+
+
+def mxfp8_quant_requant_T(x, n_groups, seed=1, stream_id=0):
+    """Weights [G*R_g, C] float32 -> MXFP8 RNE row-wise (codes [R, C], sf [R, C/32])
+    and its transposed MXFP8 SR copy (t_codes [C*R], t_sf [C*R/32]) in one pass."""
+    _dev(x, torch.float32, "x")
+    R, C = x.shape
+    codes = _empty((R, C), torch.uint8, x)
+    sf = _empty((R, C // 32), torch.uint8, x)
+    tc = _empty((C * R,), torch.uint8, x)
+    ts = _empty((C * R // 32,), torch.uint8, x)
+    rc = lib().mxfp8_quant_requant_T(_p(x), R, C, n_groups, seed, stream_id, _p(codes), _p(sf), _p(tc), _p(ts),
+                                     _stream())
+    _check(rc, "mxfp8_quant_requant_T")
+    return codes, sf, tc, ts
 
 
 def nvfp4_dequant(codes, sf, ts, group_row_off=None, ts_per_group=False):

@@ -211,6 +211,10 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
       ex[q] = mx_exponent(am[q] * S);
       pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
     }
+    if (MX) {  // decode again below instead of keeping the 256 decoded values live
+#pragma unroll
+      for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(cw[i][0]), "+v"(cw[i][MX ? 1 : 0]));
+    }
     const int64_t j0 = src0 * (C / 2) + c / 2;  // pair index of (row src0, column c)
     const uint32_t key0 = fmix32(base);
     const bool fast = j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32);
@@ -235,6 +239,127 @@ __global__ void __launch_bounds__(rq::THREADS) k_requant_T(const uint8_t* __rest
   for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
   __syncthreads();
   rq_store_tile(lq, lsf, lblk, c0, C, sfb, out_c, out_s);
+}
+
+// ------------------------------------------ weights of the MXFP8 forward
+// Float32 weights [G * grows, C] -> the row-wise MXFP8 RNE copy (blocks of 32
+// along the row, the forward contraction: the bytes of k_mx_rows) and, from
+// those codes with the same steps as k_requant_T<true>, the transposed MXFP8
+// SR copy (group-major, grows rows per group, row-major scales), in one read
+// of the weights.  MXFP8 has no tensor scale, so no tile waits for the rest
+// of its group.  Tile: 4 waves x (32 rows = one transposed MX block) x 512
+// columns of one group; lane l of wave w takes columns c0 + 8l .. c0 + 8l + 7
+// of the wave's 32 rows, so lanes 4m .. 4m + 3 hold one row-wise 32-block
+// (its amax through two shuffles) and each lane keeps its 32 rows' code bytes
+// for the transposed requantisation.
+__global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_mx_quant_requant_T(const float* __restrict__ x, int64_t C, int64_t grows, uint32_t n_ct, uint32_t n_rt,
+                     uint32_t base, uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+                     uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s) {
+  using namespace rq;
+  __shared__ __attribute__((aligned(16))) uint8_t lq[COLS * ROWS];
+  __shared__ uint8_t lsf[COLS * WAVES];  // [column][block]
+  __shared__ int64_t lblk[WAVES][3];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const uint32_t ct = blockIdx.x % n_ct, rest = blockIdx.x / n_ct, rt = rest % n_rt, g = rest / n_rt;
+  const int64_t c0 = (int64_t)ct * COLS, pr = (int64_t)rt * ROWS + 32 * w;  // wave's first row in g
+  const bool present = pr < grows;
+  const int64_t r0 = (int64_t)g * grows + pr;
+  if (l == 0) {
+    lblk[w][0] = C * (int64_t)g * grows + pr;
+    lblk[w][1] = present ? grows : 0;
+    lblk[w][2] = C * (int64_t)g * grows / 32 + pr / 32;
+  }
+  const int64_t c = c0 + LCOLS * l;
+  auto put = [&](int k, int q, uint32_t v) {
+    const int col = LCOLS * l + q;
+    *reinterpret_cast<uint32_t*>(lq + col * ROWS + swz(col, 2 * w + (k >> 2)) * 16 + (k & 3) * 4) = v;
+  };
+  int ex[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ex[q] = -127;
+  if (present && c < C) {  // (C % 32 == 0: the four lanes of a row block agree)
+    const float* xr = x + r0 * C + c;
+    u32x2 cw[32];
+    uint32_t sbp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sbp[k] = 0u;
+    f32x4 vb[2][4][2];
+    auto load_group = [&](int k, f32x4 (&b)[4][2]) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(xr + (int64_t)(4 * k + ii) * C);
+        b[ii][0] = p[0];
+        b[ii][1] = p[1];
+      }
+    };
+    load_group(0, vb[0]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k + 1 < 8) load_group(k + 1, vb[(k + 1) & 1]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * k + ii;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = vb[k & 1][ii][0][e];
+          v[4 + e] = vb[k & 1][ii][1][e];
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));  // the row block's other three lanes
+        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        const int e = mx_exponent(a);
+        const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
+        // RNE per value, two values per conversion (bytes 0-1, then 2-3)
+        uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0] * p, v[1] * p, 0, false);
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2] * p, v[3] * p, (int)lo, true);
+        uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4] * p, v[5] * p, 0, false);
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6] * p, v[7] * p, (int)hi, true);
+        cw[i] = u32x2{lo, hi};
+        *reinterpret_cast<u32x2*>(codes + (r0 + i) * C + c) = cw[i];
+        if ((l & 3) == 0) sf[(r0 + i) * (C / 32) + c / 32] = (uint8_t)(e + 127);
+        sbp[k] |= (uint32_t)(e + 127) << (8 * ii);
+      }
+    }
+    auto deq = [&](int i, float (&q)[8]) { dequant8_mx(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
+    float am[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am[q] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float q8[8];
+      deq(i, q8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
+    }
+    float pc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ex[q] = mx_exponent(am[q]);
+      pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
+    }
+    // decode again below instead of keeping the 256 decoded values live
+#pragma unroll
+    for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(cw[i][0]), "+v"(cw[i][1]));
+    const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
+    const uint32_t key0 = fmix32(base);
+    if (j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32))
+      requant_block<true, true>(deq, 32, 1.0f, pc, j0, C / 2, base, key0, put);
+    else
+      requant_block<false, true>(deq, 32, 1.0f, pc, j0, C / 2, base, key0, put);
+  } else {  // rows past the group or columns past C: zero codes
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) put(k, q, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) lsf[(LCOLS * l + q) * WAVES + w] = (uint8_t)(ex[q] + 127);
+  __syncthreads();
+  rq_store_tile(lq, lsf, lblk, c0, C, 0, out_c, out_s);
 }
 
 // ------------------------------------------------------ gradient value loads
@@ -492,6 +617,26 @@ extern "C" int mxfp8_requant_mx_sr_T(const uint8_t* codes, const uint8_t* sf, in
                      sf, nullptr, 0, cols, group_row_off, group_off_pad, n_groups, rows, max_padded_rows, n_ct,
                      sr_base_key(seed, stream_id), (int)(sf_layout == MOE4_SF_BLOCKS), out_codes, out_sf);
   return check_launch("mxfp8_requant_mx_sr_T");
+}
+
+extern "C" int mxfp8_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint64_t seed,
+                                     uint32_t stream_id, uint8_t* codes, uint8_t* sf, uint8_t* t_codes,
+                                     uint8_t* t_sf, void* stream) {
+  MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE4_EINVAL,
+               "mxfp8_quant_requant_T: cols must be a positive multiple of 32");
+  MOE4_REQUIRE(n_groups >= 1 && rows % n_groups == 0 && (rows / n_groups) % 32 == 0, MOE4_EINVAL,
+               "mxfp8_quant_requant_T: rows must split into n_groups equal groups of a multiple of 32 rows");
+  MOE4_REQUIRE(rows == 0 || (x && codes && sf && t_codes && t_sf), MOE4_EINVAL, "mxfp8_quant_requant_T: NULL pointer");
+  MOE4_REQUIRE(aligned16(x) && aligned16(codes) && aligned16(t_codes), MOE4_EALIGN,
+               "mxfp8_quant_requant_T: x, codes and t_codes must be 16-byte aligned");
+  if (rows == 0) return MOE4_OK;
+  const int64_t grows = rows / n_groups;
+  const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_rt = (grows + rq::ROWS - 1) / rq::ROWS;
+  const int64_t n_tiles = (int64_t)n_groups * n_rt * n_ct;
+  MOE4_REQUIRE(n_tiles < ((int64_t)1 << 31), MOE4_EINVAL, "mxfp8_quant_requant_T: tensor too large");
+  hipLaunchKernelGGL(k_mx_quant_requant_T, dim3((unsigned)n_tiles), dim3(rq::THREADS), 0, as_stream(stream), x, cols,
+                     grows, (uint32_t)n_ct, (uint32_t)n_rt, sr_base_key(seed, stream_id), codes, sf, t_codes, t_sf);
+  return check_launch("mxfp8_quant_requant_T");
 }
 
 static int mxfp8_quant_impl(const void* x, int dtype, int64_t rows, int64_t cols, const int32_t* row_map,

@@ -24,9 +24,10 @@ router logits.
 import torch
 
 from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_combine_hmx8,
-               moe_dgates, moe_gather_rows, moe_hmx8_quant, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd,
-               moe_grouped_gemm_mx, moe_route_backward, moe_route_topk, moe_unpermute_sum, mxfp8_quant,
-               mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
+               moe_dgates, moe_gather_rows, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad,
+               moe_grouped_gemm_fwd, moe_grouped_gemm_mx, moe_hmx8_quant, moe_route_backward, moe_route_topk,
+               moe_unpermute_sum, mxfp8_quant, mxfp8_quant_requant_T, mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T,
+               mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
@@ -176,24 +177,28 @@ def _backward_chain(fw, dy, timer, req):
 # is the same chain as above with the transposed SR requantisations reading
 # the MXFP8 forward operands.
 
-def quantize_weights_mx(w_up, w_down, timer=None):
+def quantize_weights_mx(w_up, w_down, timer=None, seed=1, layer=0):
+    """MXFP8 (RNE) of the fp32 masters and, in the same pass, the backward's
+    transposed MXFP8 SR copies (SR stream 16*layer + role, as backward_mx
+    would requantise them)."""
     E, F, d = w_up.shape
     dev = w_up.device
     off_f = torch.arange(E + 1, dtype=torch.int32, device=dev) * F
     off_d = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
     _tick(timer, None)
-    wu = mxfp8_quant(w_up.view(E * F, d))
-    _tick(timer, "F1 W_up quant (MXFP8)")
-    wd = mxfp8_quant(w_down.view(E * d, F))
-    _tick(timer, "F1 W_down quant (MXFP8)")
-    return dict(wu=wu, wd=wd, off_f=off_f, off_d=off_d, shape=(E, F, d))
+    u = mxfp8_quant_requant_T(w_up.view(E * F, d), E, seed, 16 * layer + ROLE_WUP)
+    _tick(timer, "F1 W_up quant (+ requant, MXFP8)")
+    dn = mxfp8_quant_requant_T(w_down.view(E * d, F), E, seed, 16 * layer + ROLE_WDOWN)
+    _tick(timer, "F1 W_down quant (+ requant, MXFP8)")
+    return dict(wu=u[:2], wd=dn[:2], wuT=u[2:], wdT=dn[2:], sr=(seed, layer), off_f=off_f, off_d=off_d,
+                shape=(E, F, d))
 
 
-def forward_mx(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None):
+def forward_mx(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0):
     T, d = x.shape
     E, F, _ = w_up.shape
     if wq is None:
-        wq = quantize_weights_mx(w_up, w_down, timer)
+        wq = quantize_weights_mx(w_up, w_down, timer, seed, layer)
     _tick(timer, None)
     r = moe_route_topk(logits, k, bias)
     _tick(timer, "F2-F3 route + permutation")
@@ -223,11 +228,18 @@ def backward_mx(fw, dy, seed=1, layer=0, timer=None):
     sid = lambda role: 16 * layer + role
     wq = fw["wq"]
 
+    pre = wq.get("sr") == (seed, layer)  # the weights were requantised with their forward quantisation
+
     def req(q, goff, goff_pad, role, layout, max_pr):
         return mxfp8_requant_mx_sr_T(q[0], q[1], goff, goff_pad, seed, sid(role), max_pr=max_pr,
                                      sf_layout=layout), True
+
+    def wreq(name, q, goff, role, rows):
+        if pre:
+            return wq[name], None
+        return req(q, goff, goff, role, SF_ROWS, rows)
     return _backward_chain(fw, dy, timer, dict(
-        wdT=lambda: req(wq["wd"], wq["off_d"], wq["off_d"], ROLE_WDOWN, SF_ROWS, E * d),
+        wdT=lambda: wreq("wdT", wq["wd"], wq["off_d"], ROLE_WDOWN, E * d),
         hT=lambda: req(fw["hq"], r["off"], r["off_pad"], ROLE_H, SF_BLOCKS, mpr),
-        wuT=lambda: req(wq["wu"], wq["off_f"], wq["off_f"], ROLE_WUP, SF_ROWS, E * F),
+        wuT=lambda: wreq("wuT", wq["wu"], wq["off_f"], ROLE_WUP, E * F),
         xT=lambda: req(fw["xq_perm"], r["off"], r["off_pad"], ROLE_X, SF_BLOCKS, mpr)))

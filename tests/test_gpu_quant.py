@@ -384,6 +384,32 @@ def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
     assert_bytes_equal(to_np(ms), ms_ref, "mx scales")
 
 
+@pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96), (320, 32, 512)])
+def test_fused_mx_weight_quant_requant_bit_exact(G, Rg, C):
+    """mxfp8_quant_requant_T (the MXFP8-forward weights) equals MXFP8 RNE
+    row-wise quantisation followed by the transposed SR requantisation of its
+    result (G equal groups, row-major scales), byte for byte, against the
+    oracle's two steps; rows of tiny (float32-subnormal after scaling) and huge
+    values included."""
+    R = G * Rg
+    rng = np.random.default_rng(G * 1000 + C + 1)
+    w = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
+    w[rng.random((R, C)) < 0.002] *= 40.0                       # outliers
+    w[Rg:2 * Rg] *= 0.0 if G > 2 else 1.0                        # an all-zero group
+    w[0] = (rng.standard_normal(C) * 2.0 ** -130).astype(np.float32)
+    w[1] = (rng.standard_normal(C) * 2.0 ** 100).astype(np.float32)
+    off = np.arange(G + 1) * Rg
+    c_ref, s_ref = mx.quantize_rowwise(w, mx.RNE)
+    tc_ref, ts_ref = mx.requant_mx_sr_t(c_ref, s_ref, off, seed=7, stream_id=19, sf_layout=mx.SF_ROWS)
+    codes, sf, tc, ts = m4.mxfp8_quant_requant_T(torch.from_numpy(w).cuda(), G, seed=7, stream_id=19)
+    assert_bytes_equal(to_np(codes), c_ref, "row codes")
+    assert_bytes_equal(to_np(sf), s_ref, "row scales")
+    assert_bytes_equal(to_np(tc), tc_ref, "transposed codes")
+    assert_bytes_equal(to_np(ts), ts_ref, "transposed scales")
+    with pytest.raises(m4.Moe4Error):
+        m4.mxfp8_quant_requant_T(torch.zeros(96, 64, device="cuda"), 2)   # groups of 48 rows
+
+
 def test_fused_weight_quant_rejects_bad_shapes():
     w = torch.zeros(64, 48, device="cuda")
     with pytest.raises(m4.Moe4Error):
