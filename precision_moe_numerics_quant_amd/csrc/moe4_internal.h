@@ -63,17 +63,6 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 // field e, mantissa m: (1 + m/8) 2^(e-7), subnormal m 2^-9), one instruction.
 __device__ inline float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
-// The same value from the bit fields, in ordinary integer and float
-// instructions: for kernels near the register limit, where the compiler
-// schedules the converter's results early and spills.
-__device__ inline float e4m3_to_f32_fields(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (b & 0x80u) ? -mag : mag;
-}
-template <bool FIELDS>
-__device__ inline float e4m3_decode(uint32_t b) { return FIELDS ? e4m3_to_f32_fields(b) : e4m3_to_f32(b); }
-
 // Mantissa factor 1.m of a positive normal float (its value over 2**floor(log2)).
 __device__ inline float mant_factor(float s) {
   return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);

@@ -30,9 +30,8 @@ __device__ inline int swz(int col, int chunk) { return chunk ^ ((col >> 3) & 7);
 
 // Exact q * sc of the 8 codes of one row (byte p of cw -> columns 2p, 2p+1);
 // a zero scale gives signed zeros.
-template <bool FIELDS = false>
 __device__ inline void dequant8(uint32_t cw, uint32_t sbyte, float (&q)[8]) {
-  const float scf = e4m3_decode<FIELDS>(sbyte);
+  const float scf = e4m3_to_f32(sbyte);
   const float m = scf == 0.0f ? 0.0f : mant_factor(scf);
   f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 0);
   f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scf, 1);
@@ -45,14 +44,11 @@ __device__ inline void dequant8(uint32_t cw, uint32_t sbyte, float (&q)[8]) {
 // Exact values of 8 E4M3 codes of one row (byte p of w -> column p) under
 // the row's E8M0 scale byte e: code * 2**(e - 127), exact in float32 (the
 // smallest, 2**-9 * 2**-127, is a float32 subnormal; denormals are kept).
-// FIELDS: decode from the bit fields (same values; for kernels near the
-// register limit).
-template <bool FIELDS = false>
 __device__ inline void dequant8_mx(u32x2 w, uint32_t e, float (&q)[8]) {
   const int sh = (int)e - 127;
 #pragma unroll
   for (int p = 0; p < 8; ++p)
-    q[p] = __builtin_amdgcn_ldexpf(e4m3_decode<FIELDS>((w[p >> 2] >> (8 * (p & 3))) & 0xFFu), sh);
+    q[p] = __builtin_amdgcn_ldexpf(e4m3_to_f32((w[p >> 2] >> (8 * (p & 3))) & 0xFFu), sh);
 }
 
 // SR E4M3 of v into byte sel of old (sel is a constant after unrolling).

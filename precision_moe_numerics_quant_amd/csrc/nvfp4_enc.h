@@ -71,13 +71,12 @@ __device__ inline Cand encode_candidate(const float* x, float amax_b, float S, f
 // sum: the scale byte and the 8 codes packed as 4 bytes (element 2p in the
 // low nibble of byte p).  The same steps as encode_candidate, so the codes are
 // identical; amax_b is the whole block's.
-template <bool FIELDS = false>
 __device__ inline uint32_t encode_half(const float* x, float amax_b, float S, float m, uint32_t& sc_out) {
   const float d = m * S;
   const float u = amax_b / d;
   const uint32_t sc = e4m3_rne_u(u);
   sc_out = sc;
-  const float scf = e4m3_decode<FIELDS>(sc);
+  const float scf = e4m3_to_f32(sc);
   const float eff = scf * S;
   uint32_t q = 0;
   if (sc == 0u || eff == 0.0f) {

@@ -444,12 +444,12 @@ __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_e
             for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
             a = fmaxf(a, __shfl_xor(a, 1, 64));  // the block's other half
             uint32_t sc;
-            cw[i] = encode_half<true>(v, a, S, 6.0f, sc);
+            cw[i] = encode_half(v, a, S, 6.0f, sc);
             sbp[k] |= sc << (8 * ii);
             *reinterpret_cast<uint32_t*>(codes + (r0 + i) * (C / 2) + c / 2) = cw[i];
             if ((l & 1) == 0) sf[(r0 + i) * (C / 16) + c / 16] = (uint8_t)sc;
             float q8[8];
-            dequant8<true>(cw[i], sc, q8);
+            dequant8(cw[i], sc, q8);
 #pragma unroll
             for (int q = 0; q < 8; ++q) am[q] = fmaxf(am[q], fabsf(q8[q]));
           }
@@ -460,8 +460,11 @@ __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_e
           ex[q] = mx_exponent(am[q] * S);
           pc[q] = __builtin_amdgcn_ldexpf(1.0f, -ex[q]);
         }
+        // decode again below instead of keeping the 256 decoded values live
+#pragma unroll
+        for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(cw[i]));
         const int64_t j0 = r0 * (C / 2) + c / 2;  // pair index of (row r0, column c)
-        auto deq = [&](int i, float (&q)[8]) { dequant8<true>(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
+        auto deq = [&](int i, float (&q)[8]) { dequant8(cw[i], (sbp[i >> 2] >> (8 * (i & 3))) & 0xFFu, q); };
         const bool fast = j0 + 31 * (C / 2) + 3 < ((int64_t)1 << 32);
         if (fold_scale_ok(S)) {  // one multiply by S * 2^-ex per value (the same values)
           float f[8];
