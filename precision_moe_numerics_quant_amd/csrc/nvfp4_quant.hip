@@ -109,6 +109,7 @@ struct WaveWalk {
   int64_t c, c_end;
   int gw;
   int64_t g_end;
+  int64_t ge_elem;  // g_end * cols (the first element past group gw)
   __device__ void init(int64_t n_chunks, int chunk, int64_t cols, const int32_t* goff, int G) {
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / 64);
@@ -117,16 +118,19 @@ struct WaveWalk {
     c_end = c + per < n_chunks ? c + per : n_chunks;
     gw = 0;
     g_end = INT64_MAX;
+    ge_elem = INT64_MAX;
     if (goff && c < c_end) {
       gw = group_of_row(goff, G, c * chunk / cols);
       g_end = gw + 1 < G ? (int64_t)goff[gw + 1] : INT64_MAX;
+      ge_elem = g_end == INT64_MAX ? INT64_MAX : g_end * cols;
     }
   }
   // move gw forward to the group of row r
-  __device__ void advance(const int32_t* goff, int G, int64_t r) {
+  __device__ void advance(const int32_t* goff, int G, int64_t r, int64_t cols) {
     if (r < g_end) return;
     gw = group_from(goff, G, gw, r);
     g_end = gw + 1 < G ? (int64_t)goff[gw + 1] : INT64_MAX;
+    ge_elem = g_end == INT64_MAX ? INT64_MAX : g_end * cols;
   }
 };
 
@@ -138,15 +142,89 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
                                                    uint32_t* __restrict__ amax_bits,
                                                    const float* __restrict__ act_tab) {
   using W = Walk<DT>;
-  __shared__ float tab[SILU ? ACT_TAB : 1];
-  if (SILU) {
-    stage_act_table(tab, act_tab);
-    __syncthreads();
-  }
+  static_assert(!SILU || DT == MOE4_BF16, "SiLU applies to bf16 sources");
   const int64_t n = rows * cols, n_chunks = (n + W::CHUNK - 1) / W::CHUNK;
   const int l = threadIdx.x & 63;
   WaveWalk ww;
   ww.init(n_chunks, W::CHUNK, cols, goff, G);
+  if constexpr (SILU) {
+    // max |silu(u)| over bf16 u without evaluating silu per element.  The
+    // correctly rounded silu is non-decreasing on [0, inf); |silu| is
+    // non-decreasing in u on (-inf, u*] and non-increasing on [u*, 0), u* ~
+    // -1.2785 the minimum of silu; rounding keeps monotonicity, and the
+    // adjacent bf16 values -1.28125 < u* < -1.2734375 split the negatives into
+    // those two ranges.  So the maximum is the largest of silu(largest u >= 0),
+    // |silu(largest u <= -1.28125)| and |silu(smallest u in [-1.2734375, 0))|:
+    // three integer extremes of the bit patterns per lane, and three table
+    // reads per flush.
+    constexpr uint32_t M1 = 0x3FA4u;  // |-1.28125| in bf16; 0x3FA3 is |-1.2734375|
+    uint32_t pmax = 0u, nlo = 0x8000u, nhi = 0u;  // (0x8000: no value <= -1.28125 yet)
+    float mf = 0.0f;                              // pieces folded directly (group boundaries)
+    auto fold = [&](uint32_t b) {
+      const uint32_t m = b & 0x7FFFu;
+      const bool neg = b >= 0x8000u;
+      pmax = max(pmax, neg ? 0u : m);
+      nlo = min(nlo, neg && m >= M1 ? m : 0x8000u);
+      nhi = max(nhi, neg && m < M1 ? m : 0u);
+    };
+    auto lane_amax = [&]() {
+      float t = fmaxf(mf, act_eval<false>(pmax, act_tab));
+      if (nlo < 0x8000u) t = fmaxf(t, fabsf(act_eval<false>(0x8000u | nlo, act_tab)));
+      return fmaxf(t, fabsf(act_eval<false>(0x8000u | nhi, act_tab)));
+    };
+    auto load_raw = [&](int64_t c, u32x4 (&w)[W::NLD]) {
+#pragma unroll
+      for (int k = 0; k < W::NLD; ++k) {
+        const int64_t p = c * (W::CHUNK / W::EPL) + k * 64 + l;
+        w[k] = (c < ww.c_end && p * W::EPL < n) ? reinterpret_cast<const u32x4*>(x)[p] : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    u32x4 w[W::NLD], wn[W::NLD];
+    load_raw(ww.c, w);
+    for (int64_t c = ww.c; c < ww.c_end; ++c) {
+      load_raw(c + 1, wn);
+      const int64_t e0 = c * W::CHUNK;
+      const int64_t e_end = e0 + W::CHUNK < n ? e0 + W::CHUNK : n;
+      if (e_end <= ww.ge_elem) {  // the chunk stays in group gw (no division on the common path)
+#pragma unroll
+        for (int k = 0; k < W::NLD; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            fold(w[k][i] & 0xFFFFu);
+            fold(w[k][i] >> 16);
+          }
+      } else {  // the chunk reaches past group gw: per-piece groups, then move on
+#pragma unroll
+        for (int k = 0; k < W::NLD; ++k) {
+          const int64_t e = e0 + (int64_t)(k * 64 + l) * W::EPL;
+          if (e < n) {
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              t = fmaxf(t, fabsf(act_eval<false>(w[k][i] & 0xFFFFu, act_tab)));
+              t = fmaxf(t, fabsf(act_eval<false>(w[k][i] >> 16, act_tab)));
+            }
+            const int gp = group_from(goff, G, ww.gw, e / cols);
+            if (gp == ww.gw) mf = fmaxf(mf, t);
+            else atomicMax(amax_bits + gp, __float_as_uint(t));
+          }
+        }
+        const float t = wave_max(lane_amax());
+        if (l == 0) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+        pmax = 0u;
+        nlo = 0x8000u;
+        nhi = 0u;
+        mf = 0.0f;
+        ww.advance(goff, G, (e_end - 1) / cols, cols);
+      }
+#pragma unroll
+      for (int k = 0; k < W::NLD; ++k) w[k] = wn[k];
+    }
+    const float t = wave_max(lane_amax());
+    if (l == 0 && ww.c < ww.c_end) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+    return;
+  }
+  const float* tab = act_tab;  // (unused without SiLU)
   float m = 0.0f;  // this lane's running maximum of group ww.gw
   auto load_chunk = [&](int64_t c, float (&v)[W::NLD][W::EPL]) {
 #pragma unroll
@@ -163,8 +241,8 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
   for (int64_t c = ww.c; c < ww.c_end; ++c) {
     load_chunk(c + 1, vn);  // next chunk in flight while this one is reduced
     const int64_t e0 = c * W::CHUNK;
-    const int64_t r_last = ((e0 + W::CHUNK < n ? e0 + W::CHUNK : n) - 1) / cols;
-    if (r_last < ww.g_end) {
+    const int64_t e_end = e0 + W::CHUNK < n ? e0 + W::CHUNK : n;
+    if (e_end <= ww.ge_elem) {  // the chunk stays in group gw (no division on the common path)
 #pragma unroll
       for (int k = 0; k < W::NLD; ++k)
 #pragma unroll
@@ -185,7 +263,7 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
       const float t = wave_max(m);
       if (l == 0) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
       m = 0.0f;
-      ww.advance(goff, G, r_last);
+      ww.advance(goff, G, (e_end - 1) / cols, cols);
     }
 #pragma unroll
     for (int k = 0; k < W::NLD; ++k)
