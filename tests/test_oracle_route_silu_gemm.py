@@ -188,3 +188,26 @@ def test_route_backward_shift_invariance_and_k1():
     idx1, g1 = route.topk_gates(logits, 1)
     assert np.all(g1 == 1.0)
     assert not route.route_backward(dg[:, :1], g1, idx1, 12).any()
+
+
+def test_silu_piecewise_monotone_over_bf16():
+    """The NVFP4 quantiser's SiLU amax takes max |silu| over a group from three
+    extremes of the bf16 inputs.  That rests on a property of the correctly
+    rounded silu, checked here over every finite bf16 value: silu is
+    non-decreasing on [0, inf); below zero, |silu| is non-increasing in |u| for
+    u <= -1.28125 (bf16 0xBFA4) and non-decreasing in |u| for
+    -1.2734375 (0xBFA3) <= u < 0, and those two ranges hold every negative."""
+    from oracle import silu as osl
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    s = osl.silu_f32(bits).astype(np.float64)
+    mag = (bits & 0x7FFF).astype(np.int64)
+    fin = mag < 0x7F80
+    pos = (bits < 0x8000) & fin
+    neg = (bits >= 0x8000) & fin
+    lo = neg & (mag >= 0x3FA4)
+    hi = neg & (mag <= 0x3FA3)
+    assert not np.any(lo & hi) and np.array_equal(lo | hi, neg)
+    for sel, sign in ((pos, 1), (lo, -1), (hi, 1)):
+        o = np.argsort(mag[sel], kind="stable")
+        a = np.abs(s[sel][o])
+        assert np.all(sign * np.diff(a) >= 0)
