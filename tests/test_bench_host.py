@@ -1,0 +1,76 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU refusal, the traffic
+summary of two counter passes and its guard on the kernel's source, and the
+algorithmic work of the calls."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def _csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, v in rows:
+            f.write(f'"{name}",{counter},{v}\n')
+
+
+def test_pmc_summary_scales_by_the_copy(tmp_path):
+    # the copy reads and writes 1 GiB; its counters read half / all of it, so
+    # the kernel's readings scale by 2 (fetch) and 1 (write)
+    kib = (1 << 30) / 1024
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    # (the run's three calibration copies are its largest copy dispatches; a
+    # small copy elsewhere in the run does not count)
+    _csv(f, "FETCH_SIZE", [("k_wgrad_ws256(args)", 1000.0), ("k_wgrad_ws256(args)", 3000.0),
+                           ("__amd_rocclr_copyBuffer", 10.0)] + [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
+    _csv(w, "WRITE_SIZE", [("k_wgrad_ws256(args)", 4000.0), ("k_wgrad_ws256(args)", 4000.0),
+                           ("__amd_rocclr_copyBuffer", 20.0)] + [("__amd_rocclr_copyBuffer", kib)] * 3)
+    out = bench.pmc_summary(str(f), str(w), "k_wgrad_ws256")
+    vals = dict(line[2:].split(" = ", 1) for line in out.strip().splitlines())
+    assert float(vals["copy_fetch_factor"]) == 0.5 and float(vals["copy_write_factor"]) == 1.0
+    fetch = float(vals["hbm_fetch_bytes_per_launch"])
+    write = float(vals["hbm_write_bytes_per_launch"])
+    assert abs(fetch - 2000.0 * 1024 / 0.5) / fetch < 1e-3
+    assert abs(write - 4000.0 * 1024) / write < 1e-3
+
+
+def test_traffic_only_for_the_profiled_source(monkeypatch):
+    kernel = "k_wgrad_ws256"
+    prof, src = bench.PMC_PROFILE[kernel]
+    assert os.path.exists(os.path.join(ROOT, prof)) and os.path.exists(os.path.join(ROOT, src))
+    real = bench.source_sha256
+    monkeypatch.setattr(bench, "source_sha256", lambda rel: "0" * 64)
+    assert bench.pmc_traffic(kernel) is None          # a changed kernel: no figure
+    monkeypatch.setattr(bench, "source_sha256", real)
+    assert bench.pmc_traffic("not_profiled") is None
+
+
+def test_work_table_matches_the_formulas():
+    c = synth.CONFIGS[4]
+    E, T, k, d, F = c["E"], c["T"], c["k"], c["d"], c["F"]
+    rng = np.random.default_rng(0)
+    counts = rng.multinomial(T * k, np.ones(E) / E)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    off_pad = np.concatenate([[0], np.cumsum((counts + 31) // 32 * 32)])
+    t = bench.work_table(c, off, off_pad)
+    gemm = 2.0 * T * k * d * F
+    for name in ("F6 up GEMM (NVFP4)", "F8 down GEMM (NVFP4)", "B3 down dgrad (MXFP8)", "B8 up dgrad (MXFP8)"):
+        assert t[name][1] == gemm
+    P = off_pad[-1]
+    wg = E * d * F * 4 + (d + F) * P * 33 / 32
+    assert abs(t["B5 down wgrad (MXFP8)"][2] - wg) / wg < 1e-12
+    assert abs(t["B10 up wgrad (MXFP8)"][2] - wg) / wg < 1e-12
+    assert t["F9 combine"][1] == T * k * d * 4 + T * d * 2 + T * k * 8   # Yp rows, y, gates + indices
