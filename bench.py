@@ -222,6 +222,7 @@ def gpu_run(steps, warmup):
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
     payload = combine_payload_bench(fw, c)
+    small = small_configs_bench(inp, fw["wq"])
     del fw, bw
     # the MXFP8-forward variant of the same layer on the same inputs
     def step_mx(t=None):
@@ -246,7 +247,55 @@ def gpu_run(steps, warmup):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
-    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload
+    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small
+
+
+def _median_ms(fn, reps):
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def small_configs_bench(inp4, wq, reps=20):
+    """The two small workloads, median of reps calls each (HIP events):
+    the RL-shaped forward (512 tokens, unbiased routing, the weights already
+    quantised, as they are between optimizer steps), bound by streaming the
+    NVFP4 weights, and the tiny layer's whole step (256 tokens, 8 experts),
+    bound by launches."""
+    from precision_moe_numerics_quant_amd import layer
+    c5 = synth.CONFIGS[5]
+    T5, d, F, E, k = c5["T"], c5["d"], c5["F"], c5["E"], c5["k"]
+    x5 = synth.activations(T5, d, "cuda", 0)
+    lg5 = synth.randn((T5, E), 1.0, "cuda", 0, "logits")
+    fwd5 = lambda: layer.forward(x5, inp4["w_up"], inp4["w_down"], lg5, k, None, wq=wq)
+    o = fwd5()
+    active = int((o["route"]["off"][1:] - o["route"]["off"][:-1] > 0).sum().item())
+    t5 = _median_ms(fwd5, reps)
+    w_active = active * 2.0 * F * d * 9.0 / 16.0       # NVFP4 codes + scales of both matrices
+    c1 = synth.CONFIGS[1]
+    inp1 = synth.config_inputs(1, device="cuda")
+    calls = []
+    step1 = lambda t=None: layer.backward(layer.forward(inp1["x"], inp1["w_up"], inp1["w_down"], inp1["logits"],
+                                                        c1["k"], timer=t, seed=synth.SR_SEED),
+                                          inp1["dy"], seed=synth.SR_SEED, timer=t)
+    step1(lambda name: calls.append(name) if name is not None else None)
+    torch.cuda.synchronize()
+    t1 = _median_ms(step1, reps)
+    return {
+        "rl_forward_T512": {"workload": "forward, 512 tokens, top-8 of 384 experts, unbiased logits, d=4096, F=1536, "
+                                        "weights quantised beforehand", "ms": round(t5, 4), "active_experts": active,
+                            "weight_bytes": w_active, "GBps_weights": round(w_active / t5 / 1e6, 1),
+                            "frac_hbm": round(w_active / t5 / 1e6 / (PEAK_HBM / 1e9), 4)},
+        "tiny_layer_T256": {"workload": "forward + backward, 256 tokens, top-2 of 8 experts, d=256, F=512",
+                            "us_per_step": round(t1 * 1000.0, 1), "library_calls_per_step": len(calls),
+                            "us_per_call": round(t1 * 1000.0 / max(len(calls), 1), 1)},
+    }
 
 
 def combine_payload_bench(fw, c, reps=20):
@@ -383,7 +432,7 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload = gpu_run(args.steps, args.warmup)
+    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small = gpu_run(args.steps, args.warmup)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
     calls = {}
@@ -469,6 +518,8 @@ def main():
         },
         # the combine fed by the 8.25-bit payload the pages send back between GPUs
         "combine_payload_8p25": payload,
+        # the small workloads: weight streaming (RL-shaped forward) and launch latency (tiny layer)
+        **small,
     }
     if args.copy_calibration:
         copy_calibration()
