@@ -319,14 +319,14 @@ __device__ __forceinline__ void fp4_slab_mfma(f32x16 (&acc)[MI][NJ], const uint8
 // step s + 1 are dequantised (and the next group's code words read) while
 // step s's MFMAs run, so the matrix unit need not idle behind the conversions
 // of its own wave when no other wave of the SIMD computes.
-template <int MI, int NJ>
+template <int MI, int NJ, int MA = MI>  // MA: the first MA of the MI row fragments are computed
 __device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const uint8_t* la, const uint8_t* lb,
                                                    const uint8_t* sa, const uint8_t* sb, int wm, int wn, int g,
                                                    int li) {
   using namespace fdma;
   u32x2 sca[MI], scb[NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
+  for (int i = 0; i < MA; ++i) sca[i] = *reinterpret_cast<const u32x2*>(sa + (wm + i * 32 + li) * 16 + 8 * g);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) scb[j] = *reinterpret_cast<const u32x2*>(sb + (wn + j * 32 + li) * 16 + 8 * g);
   u32x4 ca[2][MI], cb[2][NJ];
@@ -335,7 +335,7 @@ __device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const 
   f16x2 ma[MI], mb[NJ];
   auto read_codes = [&](int grp) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MA; ++i) {
       const int r = wm + i * 32 + li;
       ca[grp & 1][i] = *reinterpret_cast<const u32x4*>(la + r * RB + 16 * swz(r, 4 * g + grp));
     }
@@ -347,7 +347,7 @@ __device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const 
   };
   auto scales = [&](int grp, int hp) {  // step pair hp of group grp shares a 16-element block
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MA; ++i) {
       sfa[i] = e4m3_byte_f32(sca[i][grp >> 1], (grp & 1) * 2 + hp);
       ma[i] = mant_f16x2(sfa[i]);
     }
@@ -360,7 +360,7 @@ __device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const 
   auto dequant = [&](int st) {  // step st = 4 grp + kq of the slab
     const int grp = st >> 2, kq = st & 3;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) av[st & 1][i] = dequant8_f16(ca[grp & 1][i][kq], sfa[i], ma[i]);
+    for (int i = 0; i < MA; ++i) av[st & 1][i] = dequant8_f16(ca[grp & 1][i][kq], sfa[i], ma[i]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bv[st & 1][j] = dequant8_f16(cb[grp & 1][j][kq], sfb[j], mb[j]);
   };
@@ -375,7 +375,7 @@ __device__ __forceinline__ void fp4_slab_mfma_pipe(f32x16 (&acc)[MI][NJ], const 
       dequant(st + 1);
     }
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MA; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[st & 1][i], bv[st & 1][j], acc[i][j], 0, 0, 0);
@@ -749,8 +749,10 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
     const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
     const int64_t row_end = (int64_t)ld_const(off, e + 1) < M_total ? (int64_t)ld_const(off, e + 1) : M_total;
-    // waves whose rows all lie past the expert's last row skip their MFMAs
-    const bool active = row0 + wm < row_end;
+    // waves whose rows all lie past the expert's last row skip their MFMAs,
+    // and those with only their first 32 rows in it compute those alone (the
+    // other accumulators stay zero and their stores fall past the descriptor)
+    const bool active = row0 + wm < row_end, active2 = row0 + wm + 32 < row_end;
     for (uint32_t s = 0; s < nk; ++s, ++gs) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
@@ -759,7 +761,8 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
       asm volatile("" ::: "memory");
       const uint8_t* base = ring + (gs % S) * STAGE;
       const uint8_t* sa = base + C::CODE_A + C::CODE_B;
-      if (active) fp4_slab_mfma_pipe<MI, NJ>(acc, base, base + C::CODE_A, sa, sa + C::SCL_A, wm, wn, g, li);
+      if (active2) fp4_slab_mfma_pipe<MI, NJ>(acc, base, base + C::CODE_A, sa, sa + C::SCL_A, wm, wn, g, li);
+      else if (active) fp4_slab_mfma_pipe<MI, NJ, 1>(acc, base, base + C::CODE_A, sa, sa + C::SCL_A, wm, wn, g, li);
     }
     // epilogue: S_a * S_b, then each value straight from the accumulators;
     // the descriptor covers the tile's rows up to the expert's last, so
