@@ -34,9 +34,13 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     f, w = tmp_path / "f.csv", tmp_path / "w.csv"
     # (the run's three calibration copies are its largest copy dispatches; a
     # small copy elsewhere in the run does not count)
+    # (the two tiny dispatches stand for the tiny layer's launches of the same
+    # kernel, which the summary leaves out)
     _csv(f, "FETCH_SIZE", [("k_wgrad_ws256(args)", 1000.0), ("k_wgrad_ws256(args)", 3000.0),
+                           ("k_wgrad_ws256(args)", 2.0),
                            ("__amd_rocclr_copyBuffer", 10.0)] + [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
     _csv(w, "WRITE_SIZE", [("k_wgrad_ws256(args)", 4000.0), ("k_wgrad_ws256(args)", 4000.0),
+                           ("k_wgrad_ws256(args)", 3.0),
                            ("__amd_rocclr_copyBuffer", 20.0)] + [("__amd_rocclr_copyBuffer", kib)] * 3)
     out = bench.pmc_summary(str(f), str(w), "k_wgrad_ws256")
     vals = dict(line[2:].split(" = ", 1) for line in out.strip().splitlines())
