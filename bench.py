@@ -290,6 +290,19 @@ def small_configs_bench(inp4, wq, reps=20):
     step1(lambda name: calls.append(name) if name is not None else None)
     torch.cuda.synchronize()
     t1 = _median_ms(step1, reps)
+    # the same step captured once in a graph and replayed (no per-call launch
+    # and binding overhead)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step1()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step1()
+    t1g = _median_ms(graph.replay, reps)
+    del graph
     return {
         "rl_forward_T512": {"workload": "forward, 512 tokens, top-8 of 384 experts, unbiased logits, d=4096, F=1536, "
                                         "weights quantised beforehand", "ms": round(t5, 4), "active_experts": active,
@@ -297,7 +310,8 @@ def small_configs_bench(inp4, wq, reps=20):
                             "frac_hbm": round(w_active / t5 / 1e6 / (PEAK_HBM / 1e9), 4)},
         "tiny_layer_T256": {"workload": "forward + backward, 256 tokens, top-2 of 8 experts, d=256, F=512",
                             "us_per_step": round(t1 * 1000.0, 1), "library_calls_per_step": len(calls),
-                            "us_per_call": round(t1 * 1000.0 / max(len(calls), 1), 1)},
+                            "us_per_call": round(t1 * 1000.0 / max(len(calls), 1), 1),
+                            "us_per_step_graph_replay": round(t1g * 1000.0, 1)},
     }
 
 

@@ -319,3 +319,38 @@ def test_dgates_full_size_sampled(cfg3_route):
     exact = olayer.dgates(dy_s, yp_s, local_inv, k)
     bound = olayer.dgates(dy_s & 0x7FFF, np.abs(yp_s), local_inv, k)
     gemm_tol_check(dg[toks], exact, bound, "dgates")
+
+
+def test_layer_step_graph_replay_matches_eager():
+    """The tiny layer's whole step (forward + backward, 20 library calls)
+    captured in one graph: every replay, with eager steps and host syncs
+    between replays, gives the eager step's outputs bit for bit (the library
+    records no memset nodes; the workspaces are cleared by its own kernels)."""
+    inp = synth.config_inputs(1, device="cpu")
+    k = synth.CONFIGS[1]["k"]
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+
+    def step():
+        fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], dev["logits"], k, seed=synth.SR_SEED)
+        bw = layer.backward(fw, dev["dy"], seed=synth.SR_SEED)
+        return [fw["y"], bw["dx"], bw["dW_up"], bw["dW_down"], bw["dg"], bw["dlogits"]]
+
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "dx", "dW_up", "dW_down", "dg", "dlogits"), outs, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, name)
+        step()                         # eager work between replays
+        torch.cuda.synchronize()
