@@ -70,6 +70,9 @@ extern "C" {
 
 #define MOE4_PRE_NONE 0
 #define MOE4_PRE_SILU 1       /* quantise silu(x) (x must be bf16)             */
+#define MOE4_PRE_SILU_AMAX 2  /* as MOE4_PRE_SILU, with ws[0..n_groups) already  \
+                                 holding each group's max |silu(x)| as float    \
+                                 bits (moe_grouped_gemm_fwd_silu_amax)          */
 
 #define MOE4_RNE 0
 #define MOE4_SR 1
@@ -321,6 +324,23 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const floa
                          const uint8_t* b_codes, const uint8_t* b_sf, const float* b_ts,
                          const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
                          void* c, int c_dtype, void* stream);
+
+/*
+ * moe_grouped_gemm_fwd_silu_amax - moe_grouped_gemm_fwd with bf16 output U,
+ * which also writes, per expert e, the float bits of max |silu(u)| over the
+ * stored bf16 values of e's rows into silu_amax[e] (cleared by the call):
+ * SiLU and the per-expert maximum of the next quantisation folded into the
+ * up GEMM's epilogue (lhc.media page, the paragraph on fused kernels).
+ * nvfp4_quant_46 with pre_op MOE4_PRE_SILU_AMAX and ws = silu_amax then
+ * skips its own amax pass; the result is byte for byte that of
+ * MOE4_PRE_SILU.  silu_amax: E words of device memory (the caller's).
+ * Returns MOE4_EUNSUPPORTED (nothing launched) unless the shape selects the
+ * warp-specialised kernels (K % 256 == 0, N % 128 == 0, 32-bit offsets).
+ */
+int moe_grouped_gemm_fwd_silu_amax(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts, int a_ts_per_group,
+                                   const uint8_t* b_codes, const uint8_t* b_sf, const float* b_ts,
+                                   const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K,
+                                   uint16_t* c, uint32_t* silu_amax, void* stream);
 
 /*
  * moe_grouped_gemm_bwd_dgrad - C[rows of e] = A[rows of e] . B[e]^T with MXFP8

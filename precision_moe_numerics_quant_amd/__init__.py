@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe4.so")
 
 BF16, F32 = 0, 1
 NVFP4_6, NVFP4_4OVER6 = 6, 46
-PRE_NONE, PRE_SILU = 0, 1
+PRE_NONE, PRE_SILU, PRE_SILU_AMAX = 0, 1, 2
+EUNSUPPORTED = -5
 RNE, SR = 0, 1
 SF_ROWS, SF_BLOCKS = 0, 1   # group-major scale arrangement: [C][P_g/32] or [P_g/32][C]
 
@@ -73,6 +74,8 @@ _SIGS = {
     "moe_silu_eval": (_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "mxfp8_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _u64, _u32, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p]),
+    "moe_grouped_gemm_fwd_silu_amax": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p,
+                                              _c_void_p, _i32, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "moe_hmx8_quant": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "moe_hmx8_dequant": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
     "moe_combine_hmx8": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p,
@@ -102,10 +105,14 @@ class Moe4Error(RuntimeError):
     pass
 
 
+class Moe4Unsupported(Moe4Error):
+    """The call does not support this shape or kernel choice (nothing was launched)."""
+
+
 def _check(rc, name):
     if rc != 0:
         msg = lib().moe4_last_error().decode(errors="replace")
-        raise Moe4Error(f"{name} failed ({rc}): {msg}")
+        raise (Moe4Unsupported if rc == EUNSUPPORTED else Moe4Error)(f"{name} failed ({rc}): {msg}")
 
 
 def _p(t):
@@ -141,8 +148,10 @@ def max_padded_rows(rows, n_groups):
 
 # --------------------------------------------------------------------- NVFP4
 
-def nvfp4_quant_46(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE):
-    """NVFP4 of x [R, C] (bf16 or float32) -> (codes [R, C/2] u8, sf [R, C/16] u8, ts [G] f32)."""
+def nvfp4_quant_46(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE, ws=None):
+    """NVFP4 of x [R, C] (bf16 or float32) -> (codes [R, C/2] u8, sf [R, C/16] u8, ts [G] f32).
+    ws: the workspace (uint8 tensor); with PRE_SILU_AMAX it must hold the group amax
+    words written by moe_grouped_gemm_fwd_silu_amax."""
     dt = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
     if dt is None:
         raise ValueError("nvfp4_quant_46: x must be bf16 or float32")
@@ -154,7 +163,8 @@ def nvfp4_quant_46(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE):
     codes = _empty((R, C // 2), torch.uint8, x)
     sf = _empty((R, C // 16), torch.uint8, x)
     ts = _empty((G,), torch.float32, x)
-    ws = _ws(lib().nvfp4_quant_46_ws_bytes(G), x)
+    if ws is None:
+        ws = _ws(lib().nvfp4_quant_46_ws_bytes(G), x)
     rc = lib().nvfp4_quant_46(_p(x), dt, R, C, _p(group_row_off), G, mode, pre_op, _p(codes), _p(sf), _p(ts),
                               _p(ws), ws.numel(), _stream())
     _check(rc, "nvfp4_quant_46")
@@ -355,6 +365,21 @@ def moe_grouped_gemm_fwd(a_codes, a_sf, a_ts, b_codes, b_sf, b_ts, expert_off, o
                                     _p(b_ts), _p(expert_off), E, M, N, 2 * Kh, _p(c), cd, _stream())
     _check(rc, "moe_grouped_gemm_fwd")
     return c
+
+
+def moe_grouped_gemm_fwd_silu_amax(a_codes, a_sf, a_ts, b_codes, b_sf, b_ts, expert_off, a_ts_per_group=False):
+    """moe_grouped_gemm_fwd with bf16 U, plus each expert's max |silu(U)| as float bits
+    in a workspace that nvfp4_quant_46(U, ..., PRE_SILU_AMAX, ws=...) takes.
+    Raises Moe4Unsupported when the shape selects other kernels.  -> (U, ws)"""
+    M, Kh = a_codes.shape
+    E, N, _ = b_codes.shape
+    c = _empty((M, N), torch.bfloat16, a_codes)
+    ws = _ws(lib().nvfp4_quant_46_ws_bytes(E), a_codes)
+    rc = lib().moe_grouped_gemm_fwd_silu_amax(_p(a_codes), _p(a_sf), _p(a_ts), int(a_ts_per_group), _p(b_codes),
+                                              _p(b_sf), _p(b_ts), _p(expert_off), E, M, N, 2 * Kh, _p(c), _p(ws),
+                                              _stream())
+    _check(rc, "moe_grouped_gemm_fwd_silu_amax")
+    return c, ws
 
 
 def moe_grouped_gemm_bwd_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off):

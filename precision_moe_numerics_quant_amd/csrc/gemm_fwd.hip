@@ -21,6 +21,7 @@
 // LDS for row-contiguous 16-byte (f32) or 8-byte (bf16) stores.
 #include <stdlib.h>
 
+#include "act.h"
 #include "gemm_common.h"
 #include "moe4_internal.h"
 
@@ -599,7 +600,8 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
                   int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                   const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,
-                  int64_t K, void* __restrict__ c) {
+                  int64_t K, void* __restrict__ c, uint32_t* __restrict__ silu_amax,
+                  const float* __restrict__ act_tab) {
   using namespace fws;
   using fdma::lds_ptr;
   using fdma::swz;
@@ -771,6 +773,14 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
                       __int_as_float(ld_const(reinterpret_cast<const int32_t*>(b_ts), e));
     const int64_t nrows = row_end - row0 < TM ? row_end - row0 : TM;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<uint8_t*>(c) + row0 * (int64_t)ld, (uint64_t)nrows * ld);
+    // With silu_amax (bf16 U): the expert's max |silu(u)| over the stored
+    // values of its rows, from three extremes of the bf16 patterns (silu is
+    // non-decreasing on [0, inf); |silu| is monotone on each side of its
+    // minimum, split by the adjacent bf16 values -1.28125 and -1.2734375),
+    // then one atomic maximum per wave and tile.
+    constexpr uint32_t M1 = 0x3FA4u;  // |-1.28125| in bf16
+    const bool amx = OUT_BF16 && silu_amax != nullptr && active;
+    uint32_t pmax = 0u, nlo = 0x8000u, nhi = 0u;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -787,9 +797,44 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rC, lane_off, so, 2);
           }
         }
+      }
+    if (amx) {  // the same bf16 values, folded in a pass of their own
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int rows_left = (int)nrows - (wm + i * 32 + g * 4);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            if ((v >> 2) * 8 + (v & 3) < rows_left) {
+              const uint32_t b = f32_to_bf16_bits(acc[i][j][v] * sab);
+              const uint32_t m = b & 0x7FFFu;
+              const bool neg = b >= 0x8000u;
+              pmax = max(pmax, neg ? 0u : m);
+              nlo = min(nlo, neg && m >= M1 ? m : 0x8000u);
+              nhi = max(nhi, neg && m < M1 ? m : 0u);
+            }
+          }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        pmax = max(pmax, (uint32_t)__shfl_xor((int)pmax, o, 64));
+        nlo = min(nlo, (uint32_t)__shfl_xor((int)nlo, o, 64));
+        nhi = max(nhi, (uint32_t)__shfl_xor((int)nhi, o, 64));
+      }
+      if (l == 0) {
+        float t = act_eval<false>(pmax, act_tab);
+        if (nlo < 0x8000u) t = fmaxf(t, fabsf(act_eval<false>(0x8000u | nlo, act_tab)));
+        t = fmaxf(t, fabsf(act_eval<false>(0x8000u | nhi, act_tab)));
+        atomicMax(silu_amax + e, __float_as_uint(t));  // t >= 0: bit order = value order
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-      }
   }
 }
 
@@ -844,10 +889,7 @@ static int cu_count_f() {
   return n[dev];
 }
 
-template <bool OUT_BF16>
-static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
-                       const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
-                       int64_t N, int64_t K, void* c) {
+static int fwd_choice(int64_t M, int64_t N, int64_t K) {
   int choice = fwd_tile_choice();
   if (choice == 11 && N % 256 != 0) choice = 10;
   // the persistent kernels' 32-bit operand offsets and tile indices
@@ -855,14 +897,22 @@ static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, cons
       (N % 128 != 0 || M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31)))
     choice = 9;
   if ((choice == 8 || choice == 9 || choice == 10 || choice == 11) && K % fdma::BKE != 0) choice = 0;
+  return choice;
+}
+
+template <bool OUT_BF16>
+static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
+                       const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
+                       int64_t N, int64_t K, void* c, uint32_t* silu_amax = nullptr, const float* act_tab = nullptr) {
+  const int choice = fwd_choice(M, N, K);
   if (choice == 10) {
     hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 128>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s, ac,
-                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
+                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
     return;
   }
   if (choice == 11) {
     hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 256>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<256>::NT), 0, s, ac,
-                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
+                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
     return;
   }
   if (choice == 8) {
@@ -904,4 +954,38 @@ extern "C" int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf,
   else
     launch_fwd<false>(s, a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K, c);
   return check_launch("moe_grouped_gemm_fwd");
+}
+
+namespace moe4 {
+__global__ void k_zero_amax(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+}  // namespace moe4
+
+extern "C" int moe_grouped_gemm_fwd_silu_amax(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts,
+                                              int a_ts_per_group, const uint8_t* b_codes, const uint8_t* b_sf,
+                                              const float* b_ts, const int32_t* expert_off, int32_t E, int64_t M_total,
+                                              int64_t N, int64_t K, uint16_t* c, uint32_t* silu_amax, void* stream) {
+  MOE4_REQUIRE(E >= 1 && M_total >= 0 && N > 0 && K > 0, MOE4_EINVAL, "moe_grouped_gemm_fwd_silu_amax: bad sizes");
+  MOE4_REQUIRE(K % 64 == 0 && N % 32 == 0, MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_silu_amax: need K % 64 == 0 and N % 32 == 0");
+  MOE4_REQUIRE(a_ts && b_codes && b_sf && b_ts && expert_off && silu_amax, MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_silu_amax: NULL pointer");
+  MOE4_REQUIRE(M_total == 0 || (a_codes && a_sf && c), MOE4_EINVAL, "moe_grouped_gemm_fwd_silu_amax: NULL pointer");
+  MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(c), MOE4_EALIGN,
+               "moe_grouped_gemm_fwd_silu_amax: misaligned pointer");
+  const int choice = fwd_choice(M_total, N, K);
+  MOE4_REQUIRE(M_total == 0 || choice == 10 || choice == 11, MOE4_EUNSUPPORTED,
+               "moe_grouped_gemm_fwd_silu_amax: needs the warp-specialised kernels (K % 256 == 0, N % 128 == 0)");
+  hipStream_t s = as_stream(stream);
+  int rc = ensure_act_tables(s);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_zero_amax, dim3((E + 255) / 256), dim3(256), 0, s, silu_amax, E);
+  if (M_total == 0) return check_launch("moe_grouped_gemm_fwd_silu_amax");
+  MOE4_REQUIRE(((N + 127) / 128) * ((M_total + 127) / 128 + E) < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_silu_amax: too large");
+  launch_fwd<true>(s, a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K, c,
+                   silu_amax, act_tables_device_ptr());
+  return check_launch("moe_grouped_gemm_fwd_silu_amax");
 }

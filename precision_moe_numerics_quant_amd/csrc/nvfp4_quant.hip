@@ -619,8 +619,9 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
                               void* ws, size_t ws_bytes, void* stream) {
   MOE4_REQUIRE(dtype == MOE4_BF16 || dtype == MOE4_F32, MOE4_EINVAL, "nvfp4_quant_46: dtype must be BF16 or F32");
   MOE4_REQUIRE(mode == MOE4_NVFP4_6 || mode == MOE4_NVFP4_4OVER6, MOE4_EINVAL, "nvfp4_quant_46: bad mode");
-  MOE4_REQUIRE(pre_op == MOE4_PRE_NONE || (pre_op == MOE4_PRE_SILU && dtype == MOE4_BF16), MOE4_EINVAL,
-               "nvfp4_quant_46: pre_op SILU needs bf16 input");
+  MOE4_REQUIRE(pre_op == MOE4_PRE_NONE ||
+                   ((pre_op == MOE4_PRE_SILU || pre_op == MOE4_PRE_SILU_AMAX) && dtype == MOE4_BF16),
+               MOE4_EINVAL, "nvfp4_quant_46: pre_op SILU needs bf16 input");
   MOE4_REQUIRE(rows >= 0 && cols > 0 && cols % 16 == 0, MOE4_EINVAL, "nvfp4_quant_46: cols must be a positive multiple of 16");
   MOE4_REQUIRE(n_groups >= 1 && (group_row_off != nullptr || n_groups == 1), MOE4_EINVAL,
                "nvfp4_quant_46: n_groups >= 1, and group_row_off is required when n_groups > 1");
@@ -630,6 +631,8 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   MOE4_REQUIRE(ws_bytes >= nvfp4_quant_46_ws_bytes(n_groups), MOE4_EWORKSPACE, "nvfp4_quant_46: workspace too small");
   hipStream_t s = as_stream(stream);
   const float* tab = nullptr;
+  const bool amax_given = pre_op == MOE4_PRE_SILU_AMAX;  // ws already holds the group amax bits
+  if (amax_given) pre_op = MOE4_PRE_SILU;
   if (pre_op == MOE4_PRE_SILU) {
     int rc = ensure_act_tables(s);
     if (rc) return rc;
@@ -637,8 +640,8 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   }
   uint32_t* amax = static_cast<uint32_t*>(ws);
   const int G = n_groups;
-  hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
-  if (rows > 0) {
+  if (!amax_given) hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
+  if (rows > 0 && !amax_given) {
     const dim3 grid = walk_grid(rows * cols);
     if (dtype == MOE4_BF16 && pre_op == MOE4_PRE_SILU)
       hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);

@@ -23,9 +23,9 @@ router logits.
 """
 import torch
 
-from . import (NVFP4_4OVER6, PRE_SILU, SF_BLOCKS, SF_ROWS, max_padded_rows, moe_combine, moe_combine_hmx8,
-               moe_dgates, moe_gather_rows, moe_grouped_gemm_bwd_dgrad, moe_grouped_gemm_bwd_wgrad,
-               moe_grouped_gemm_fwd, moe_grouped_gemm_mx, moe_hmx8_quant, moe_route_backward, moe_route_topk,
+from . import (NVFP4_4OVER6, PRE_SILU, PRE_SILU_AMAX, SF_BLOCKS, SF_ROWS, Moe4Unsupported, max_padded_rows,
+               moe_combine, moe_combine_hmx8, moe_dgates, moe_gather_rows, moe_grouped_gemm_bwd_dgrad,
+               moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_silu_amax, moe_grouped_gemm_mx, moe_hmx8_quant, moe_route_backward, moe_route_topk,
                moe_unpermute_sum, mxfp8_quant, mxfp8_quant_requant_T, mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T,
                mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
@@ -77,10 +77,19 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
     _tick(timer, "F5 dispatch gather")
     wu_c, wu_s, wu_t = wq["wu"]
     wd_c, wd_s, wd_t = wq["wd"]
-    U = moe_grouped_gemm_fwd(xq_perm[0], xq_perm[1], xq[2], wu_c.view(E, F, d // 2), wu_s.view(E, F, d // 16), wu_t,
-                             r["off"], torch.bfloat16)
+    # F6 with the per-expert SiLU amax of F7 folded into its epilogue (when
+    # the shape takes the warp-specialised kernels), so F7 only encodes
+    try:
+        U, amax_ws = moe_grouped_gemm_fwd_silu_amax(xq_perm[0], xq_perm[1], xq[2], wu_c.view(E, F, d // 2),
+                                                    wu_s.view(E, F, d // 16), wu_t, r["off"])
+    except Moe4Unsupported:
+        U, amax_ws = moe_grouped_gemm_fwd(xq_perm[0], xq_perm[1], xq[2], wu_c.view(E, F, d // 2),
+                                          wu_s.view(E, F, d // 16), wu_t, r["off"], torch.bfloat16), None
     _tick(timer, "F6 up GEMM (NVFP4)")
-    hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU)
+    if amax_ws is None:
+        hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU)
+    else:
+        hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU_AMAX, ws=amax_ws)
     _tick(timer, "F7 SiLU + H quant (NVFP4 4/6)")
     Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
                               r["off"], torch.float32, a_ts_per_group=True)

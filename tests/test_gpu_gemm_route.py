@@ -311,3 +311,34 @@ def test_grouped_gemm_mx_bf16_and_f32(M_list, N, K):
     exact = og.grouped_nt(A64, B64, off)
     got = fmt.bf16_to_f32(to_np(c16.view(torch.int16)).view(np.uint16)).astype(np.float64)
     gemm_tol_check(got, exact, og.abs_bound_nt(A64, B64, off), "mx gemm bf16", out_bf16=True)
+
+
+@pytest.mark.parametrize("M_list,N,K", [([300, 0, 37, 1, 129], 256, 512), ([5, 64, 200], 384, 256),
+                                        ([1000, 3], 1536, 1024)])
+def test_fwd_silu_amax_epilogue_matches_separate_pass(M_list, N, K):
+    """moe_grouped_gemm_fwd_silu_amax (SiLU amax per expert folded into the up
+    GEMM's epilogue) gives the same U, and nvfp4_quant_46 with PRE_SILU_AMAX on
+    its workspace the same H (codes, scales, tensor scales) byte for byte as
+    the plain GEMM followed by nvfp4_quant_46 with PRE_SILU (whose amax pass is
+    pinned to the oracle elsewhere)."""
+    E = len(M_list)
+    off, qa, qb = _fwd_operands(M_list, N, K, seed=N + K + 7)
+    args = (torch.from_numpy(qa["codes"]).cuda(), torch.from_numpy(qa["sf"]).cuda(), torch.from_numpy(qa["ts"]).cuda(),
+            torch.from_numpy(qb["codes"]).cuda().view(E, N, K // 2), torch.from_numpy(qb["sf"]).cuda().view(E, N, K // 16),
+            torch.from_numpy(qb["ts"]).cuda(), cuda_i32(off))
+    u1, ws = m4.moe_grouped_gemm_fwd_silu_amax(*args)
+    u2 = m4.moe_grouped_gemm_fwd(*args, torch.bfloat16)
+    assert torch.equal(u1.view(torch.int16), u2.view(torch.int16))
+    h1 = m4.nvfp4_quant_46(u1, m4.NVFP4_4OVER6, cuda_i32(off), m4.PRE_SILU_AMAX, ws=ws)
+    h2 = m4.nvfp4_quant_46(u2, m4.NVFP4_4OVER6, cuda_i32(off), m4.PRE_SILU)
+    for a, b, what in zip(h1, h2, ("codes", "scales", "tensor scales")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), what
+
+
+def test_fwd_silu_amax_unsupported_shape():
+    off, qa, qb = _fwd_operands([40, 24], 96, 256, seed=5)      # N % 128 != 0: not the warp-specialised kernels
+    with pytest.raises(m4.Moe4Unsupported):
+        m4.moe_grouped_gemm_fwd_silu_amax(
+            torch.from_numpy(qa["codes"]).cuda(), torch.from_numpy(qa["sf"]).cuda(), torch.from_numpy(qa["ts"]).cuda(),
+            torch.from_numpy(qb["codes"]).cuda().view(2, 96, 128), torch.from_numpy(qb["sf"]).cuda().view(2, 96, 16),
+            torch.from_numpy(qb["ts"]).cuda(), cuda_i32(off))
