@@ -62,7 +62,8 @@ def work_table(c, off, off_pad):
         "F4 X quant (NVFP4 4/6)": ("hbm", T * d * (4.0 + nv)),
         "F5 dispatch gather": ("hbm", 2.0 * A * d * nv),
         "F6 up GEMM (NVFP4)": ("f16", gem),
-        "F7 SiLU + H quant (NVFP4 4/6)": ("hbm", A * F * (4.0 + nv)),
+        # (the per-expert SiLU amax is folded into F6's epilogue: one read of U here)
+        "F7 SiLU + H quant (NVFP4 4/6)": ("hbm", A * F * (2.0 + nv)),
         "F8 down GEMM (NVFP4)": ("f16", gem),
         "F9 combine": ("hbm", A * d * 4.0 + T * d * 2.0 + A * 8.0),
         "B1 dY quant row-wise + transposed (MXFP8)": ("hbm", T * d * 2.0 + A * 8.0 + A * d * mxb + d * Ptot * mxb),
