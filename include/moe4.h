@@ -22,6 +22,13 @@
  *  - Preconditions that need the device's data (monotone offsets, indices in
  *    range, finite inputs) are the caller's; kernels clamp indices so that a
  *    violated precondition gives wrong values, never an out-of-bounds access.
+ *    Kernels that clamp a routed row index, and the bounded wait between
+ *    workgroups of nvfp4_quant_requant_T, also set a bit in the library's
+ *    device-side error word, which moe4_debug_check() reports.
+ *  - The library's only device state is that error word (one per device) and
+ *    its constant SiLU / SiLU' tables (data of the code object): no call
+ *    fills anything at run time, so any call may be the first one on a device
+ *    and may be made inside a stream capture.
  *  - Sizes are int64_t; offsets and indices are int32_t device arrays.
  *  - Pointers must be 16-byte aligned.
  *
@@ -61,6 +68,13 @@ extern "C" {
 #define MOE4_EWORKSPACE (-3)  /* workspace missing or too small                */
 #define MOE4_EHIP (-4)        /* a HIP launch failed                           */
 #define MOE4_EUNSUPPORTED (-5)
+#define MOE4_EDEVICE (-6)     /* moe4_debug_check: a kernel reported an error   */
+
+/* Bits of the device-side error word (moe4_debug_check's message names them) */
+#define MOE4_DEVERR_WAIT 1u   /* a bounded wait between workgroups gave up: that
+                                 call's results are wrong                       */
+#define MOE4_DEVERR_INDEX 2u  /* a routed row index outside its range was
+                                 clamped (gather, combine, un-permute, dgates)  */
 
 #define MOE4_BF16 0
 #define MOE4_F32 1
@@ -86,9 +100,22 @@ const char* moe4_last_error(void);
 /* Library version string. */
 const char* moe4_version(void);
 /* Waits for the stream (a synchronising debugging aid, never called by the
- * library itself) and reports a failed launch or a device-side error as
- * MOE4_EHIP with the runtime's message. */
+ * library itself).  Returns MOE4_EHIP with the runtime's message for a failed
+ * launch or a runtime error; otherwise reads and clears the current device's
+ * device-side error word and returns MOE4_EDEVICE, naming the MOE4_DEVERR_*
+ * conditions, if a kernel set any bit since the last check (of any stream:
+ * a check while other streams run may report their errors, or clear a bit
+ * one of them sets meanwhile); else MOE4_OK.  The error word and the
+ * reporting follow the debugging contract of this library's interface: the
+ * kernels cannot check data-dependent preconditions without a
+ * synchronisation, so they clamp and report instead. */
 int moe4_debug_check(void* stream);
+/* Test hook for the error path above: with on != 0, every later
+ * nvfp4_quant_requant_T launch makes its bounded waits wait for a count that
+ * never arrives, with a small spin limit, so each wait gives up and sets
+ * MOE4_DEVERR_WAIT (every kernel still exits; that call's results are
+ * wrong).  on = 0 restores normal operation.  Process-wide; always MOE4_OK. */
+int moe4_debug_force_wait_timeout(int on);
 
 /* ---------------------------------------------------------------- NVFP4 */
 /*
@@ -145,8 +172,14 @@ int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_
 size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups);
 
 /*
- * nvfp4_dequant - float32 values fl(fl(q*sc)*S) of an NVFP4 tensor (test and
- * debugging aid).  ts_per_group = 0: ts[0] applies to every row.
+ * nvfp4_dequant - float32 values fl(fl(q*sc)*S) of an NVFP4 tensor: the
+ * dequantisation that precedes the transpose and requantisation of the
+ * backward (lhc.media page, the paragraph on dequantising the forward values
+ * before transposing them), here as a test and debugging aid.
+ * codes [rows, cols/2], sf [rows, cols/16] as written by nvfp4_quant_46;
+ * ts_per_group = 0: ts[0] applies to every row, 1: ts[g] to the rows of group
+ * g of group_row_off [n_groups+1]; out [rows, cols] float32.  cols % 16 == 0;
+ * codes and out 16-byte aligned.
  */
 int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const float* ts, int ts_per_group,
                   const int32_t* group_row_off, int32_t n_groups, int64_t rows, int64_t cols,
@@ -383,7 +416,17 @@ int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
 
 /*
  * moe_grouped_gemm_bwd - dgrad and wgrad of one expert linear layer in one
- * call (both enqueued on `stream`, dgrad first).
+ * call (both enqueued on `stream`, dgrad first): the MXFP8 backward of the
+ * expert layers (agihunt.info page, "Confirmed"; lhc.media page, the
+ * paragraphs on requantising the transposed operands into MXFP8).
+ * For the linear y = x . W^T with W [E][Nout][Nin] per expert:
+ *   dx (float32 [M_total, Nin]) = moe_grouped_gemm_bwd_dgrad(dy row-wise
+ *       [M_total, Nout], W^T requantised [E][Nin][Nout], expert_off),
+ *   dw (float32 [E, Nout, Nin]) = moe_grouped_gemm_bwd_wgrad(dy transposed
+ *       group-major [Nout][P_e], x transposed group-major [Nin][P_e], both
+ *       with block-major scales, expert_off_pad, beta).
+ * Arguments, layouts and constraints as in the two calls; returns the first
+ * error (nothing enqueued when the dgrad's checks fail).
  */
 int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_sf,           /* [M_total, Nout] row-wise */
                          const uint8_t* wT_codes, const uint8_t* wT_sf,           /* [E, Nin, Nout]           */
@@ -395,16 +438,24 @@ int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_sf,         
 
 /* ----------------------------------------------------- combine / scatter */
 /*
- * moe_combine - y[t] = bf16(acc), acc = 0; for j = 0..k-1:
- * acc = fl(acc + fl(gates[t,j] * yp[inv_perm[t*k+j]])).  yp [T*k, d] float32.
- * 1 <= k <= 16, d % 4 == 0.
+ * moe_combine - the gate-weighted return of the expert outputs to their
+ * tokens, the local stand-in for the pages' combine (lhc.media page,
+ * paragraph on communication; fourweekmba.com page, "Update": a token's
+ * output sums its 8 routed experts): y[t] = bf16(acc), acc = 0; for
+ * j = 0..k-1: acc = fl(acc + fl(gates[t,j] * yp[inv_perm[t*k+j]])).
+ * yp [T*k, d] float32, gates [T, k], inv_perm [T*k] (moe_route_topk), y
+ * [T, d] bf16.  1 <= k <= 16, d % 4 == 0.
  */
 int moe_combine(const float* yp, const float* gates, const int32_t* inv_perm, int64_t T, int32_t k,
                 int64_t d, uint16_t* y, void* stream);
 
 /*
- * moe_unpermute_sum - dx[t] = bf16(acc), acc = 0; for j: acc = fl(acc + dxp[inv_perm[t*k+j]]).
- * 1 <= k <= 16, d % 4 == 0.
+ * moe_unpermute_sum - the backward of the dispatch (lhc.media page,
+ * paragraph on communication: inputs sent to the experts that hold them):
+ * each token's input gradient sums the rows of its k routed copies,
+ * dx[t] = bf16(acc), acc = 0; for j = 0..k-1: acc = fl(acc + dxp[inv_perm[t*k+j]]).
+ * dxp [T*k, d] float32, inv_perm [T*k], dx [T, d] bf16.  1 <= k <= 16,
+ * d % 4 == 0.
  */
 int moe_unpermute_sum(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
                       uint16_t* dx, void* stream);

@@ -19,6 +19,7 @@ BF16, F32 = 0, 1
 NVFP4_6, NVFP4_4OVER6 = 6, 46
 PRE_NONE, PRE_SILU, PRE_SILU_AMAX = 0, 1, 2
 EUNSUPPORTED = -5
+EDEVICE = -6
 RNE, SR = 0, 1
 SF_ROWS, SF_BLOCKS = 0, 1   # group-major scale arrangement: [C][P_g/32] or [P_g/32][C]
 
@@ -56,6 +57,7 @@ _SIGS = {
     "moe_route_backward": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_dgates": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe4_debug_check": (_int, [_c_void_p]),
+    "moe4_debug_force_wait_timeout": (_int, [_int]),
     "moe_route_topk": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "moe_route_topk_ws_bytes": (_size, [_i64, _i32, _i32]),
@@ -109,10 +111,16 @@ class Moe4Unsupported(Moe4Error):
     """The call does not support this shape or kernel choice (nothing was launched)."""
 
 
+class Moe4DeviceError(Moe4Error):
+    """moe4_debug_check found a device-side error report (a clamped index or a
+    bounded wait that gave up)."""
+
+
 def _check(rc, name):
     if rc != 0:
         msg = lib().moe4_last_error().decode(errors="replace")
-        raise (Moe4Unsupported if rc == EUNSUPPORTED else Moe4Error)(f"{name} failed ({rc}): {msg}")
+        cls = {EUNSUPPORTED: Moe4Unsupported, EDEVICE: Moe4DeviceError}.get(rc, Moe4Error)
+        raise cls(f"{name} failed ({rc}): {msg}")
 
 
 def _p(t):
@@ -490,8 +498,14 @@ def moe_route_backward(dg, gates, topk_idx, E):
 
 
 def moe4_debug_check():
-    """Synchronise the current stream and raise on a failed launch or device error."""
+    """Synchronise the current stream; raise Moe4Error on a failed launch and
+    Moe4DeviceError on a device-side error report (which this clears)."""
     _check(lib().moe4_debug_check(_stream()), "moe4_debug_check")
+
+
+def moe4_debug_force_wait_timeout(on):
+    """Test hook: make nvfp4_quant_requant_T's bounded waits give up (see moe4.h)."""
+    _check(lib().moe4_debug_force_wait_timeout(int(bool(on))), "moe4_debug_force_wait_timeout")
 
 
 def moe_silu_eval(u):

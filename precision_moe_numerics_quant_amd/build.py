@@ -6,6 +6,10 @@ Flags: -ffp-contract=off keeps every float operation a separate IEEE
 operation (the quantisers must match their specification bit for bit);
 packed-fp32 instruction selection is disabled; the default correctly rounded
 float32 division is kept.
+
+The SiLU / SiLU' tables are constant data of the library: gen_act_tab.cpp,
+compiled and run on the host first, writes them as the initialiser that
+capi.hip includes (act_tab.inc, in the build directory).
 """
 import os
 import shutil
@@ -18,6 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe4.so")
 SOURCES = ["capi.hip", "nvfp4_quant.hip", "mxfp8.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "combine_q.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 
@@ -25,11 +30,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
 def build(verbose=False, jobs=8):
     tmp = tempfile.mkdtemp(prefix="moe4_build_")
     try:
+        gen = os.path.join(tmp, "gen_act_tab")
+        r = subprocess.run([CXX, "-O2", "-std=c++17", "-o", gen, os.path.join(CSRC, "gen_act_tab.cpp")],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("activation table generator failed to compile:\n" + r.stdout)
+        with open(os.path.join(tmp, "act_tab.inc"), "w") as f:
+            subprocess.run([gen], stdout=f, check=True)
         objs = []
         procs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC] + FLAGS + ["-I", tmp, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd))
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

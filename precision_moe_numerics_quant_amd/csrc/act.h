@@ -2,10 +2,11 @@
 //
 // silu(u) = u / (1 + exp(-u)),  silu'(u) = s * (1 + u * (1 - s)), s = sigmoid(u),
 // both rounded once to float32.  Evaluation:
-//  * |u| in [2**-8, 2**8): a 4096-entry table per function, filled once per
-//    device by evaluating the formula in float64 (whose error, ~1e-16, is far
-//    below the distance of every such entry from a float32 rounding boundary)
-//    and staged through LDS by the kernels that use it;
+//  * |u| in [2**-8, 2**8): a 4096-entry table per function, constant data of
+//    the library written at build time by evaluating the formula in float64
+//    (whose error, ~1e-16, is far below the distance of every such entry from
+//    a float32 rounding boundary), staged through LDS by the kernels that use
+//    it;
 //  * |u| >= 2**8: silu = u (u > 0) or -0 (u < 0); silu' = 1 or -0;
 //  * |u| < 2**-8: the series u/2 + u**2/4 - u**4/48 (silu) and
 //    1/2 + u/2 - u**3/12 (silu'): the float64 sum of the first two terms is
@@ -54,12 +55,6 @@ __device__ inline float dsilu_small(float u) {
   return round_dir(0.5 + 0.5 * x, u > 0.0f ? -1 : 1);
 }
 
-__device__ inline double silu_f64(double x) { return x / (1.0 + exp(-x)); }
-__device__ inline double dsilu_f64(double x) {
-  double s = 1.0 / (1.0 + exp(-x));
-  return s * (1.0 + x * (1.0 - s));
-}
-
 // Evaluate from the bf16 bits, with `tab` the function's 4096-entry table
 // (LDS or global).
 template <bool DERIV>
@@ -75,14 +70,10 @@ __device__ inline float act_eval(uint32_t b, const float* tab) {
   return DERIV ? dsilu_small(u) : silu_small(u);
 }
 
-// Global tables: [0] = silu, [1] = silu'.  Filled by ensure_act_tables().
-extern __device__ float g_act_tab[2][ACT_TAB];
-
-// Enqueues the one-time fill of g_act_tab for the current device on `s`
-// (a no-op after the first call on that device).  Returns 0 or an error code.
-int ensure_act_tables(hipStream_t s);
-// Device address of g_act_tab for the current device.
-const float* act_tables_device_ptr();
+// Device address of the constant tables ([0] = silu, [1] = silu', ACT_TAB
+// floats each) on the current device, in *out.  A symbol query, no stream
+// work.  Returns 0 or an error code.
+int act_tables(const float** out);
 
 // Stage one table (4096 floats) into LDS; every thread of the block calls it.
 __device__ inline void stage_act_table(float* lds, const float* gtab) {

@@ -32,6 +32,10 @@ constexpr int MAXK = 16;
 constexpr int THREADS = 256;
 }  // namespace hq
 
+// This file's device-side error word (moe4_debug_check reads and clears it).
+static __device__ uint32_t g_dev_err;
+uint32_t take_dev_err_combine_q() { return take_device_word(&g_dev_err); }
+
 // quad_perm [1,0,3,2] and [2,3,0,1]: the value of lane q ^ 1 and of lane q ^ 2
 __device__ inline int quad_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
 __device__ inline int quad_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
@@ -135,7 +139,10 @@ __device__ inline void load_slot(const int8_t* __restrict__ codes, const uint8_t
                                  const float* __restrict__ gates, const int32_t* __restrict__ inv, int64_t tk,
                                  int64_t n_rows, int64_t d, int64_t b, u32x4 (&w)[2], uint32_t& s, float& g) {
   int64_t row = inv[tk];
-  row = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+  if (row < 0 || row >= n_rows) {
+    atomicOr(&g_dev_err, MOE4_DEVERR_INDEX);
+    row = row < 0 ? 0 : n_rows - 1;
+  }
   g = gates[tk];
   const int64_t off = row * d + b * hq::BLOCK;
   const u32x4* p = reinterpret_cast<const u32x4*>(codes + off);

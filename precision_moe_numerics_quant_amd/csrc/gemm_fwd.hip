@@ -979,13 +979,14 @@ extern "C" int moe_grouped_gemm_fwd_silu_amax(const uint8_t* a_codes, const uint
   MOE4_REQUIRE(M_total == 0 || choice == 10 || choice == 11, MOE4_EUNSUPPORTED,
                "moe_grouped_gemm_fwd_silu_amax: needs the warp-specialised kernels (K % 256 == 0, N % 128 == 0)");
   hipStream_t s = as_stream(stream);
-  int rc = ensure_act_tables(s);
+  const float* tab = nullptr;
+  int rc = act_tables(&tab);
   if (rc) return rc;
   hipLaunchKernelGGL(k_zero_amax, dim3((E + 255) / 256), dim3(256), 0, s, silu_amax, E);
   if (M_total == 0) return check_launch("moe_grouped_gemm_fwd_silu_amax");
   MOE4_REQUIRE(((N + 127) / 128) * ((M_total + 127) / 128 + E) < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_fwd_silu_amax: too large");
   launch_fwd<true>(s, a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K, c,
-                   silu_amax, act_tables_device_ptr());
+                   silu_amax, tab);
   return check_launch("moe_grouped_gemm_fwd_silu_amax");
 }

@@ -20,6 +20,21 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
     if (!(cond)) return ::moe4::fail((code), (msg));  \
   } while (0)
 
+// Device-side error reports.  Each source file whose kernels can detect a
+// problem on the device keeps a static __device__ error word of its own;
+// kernels OR MOE4_DEVERR_* bits into it on their (rare) error paths, and
+// moe4_debug_check() reads and clears each file's word through the readers
+// below (synchronous copies, current device).
+constexpr uint32_t MOE4_DEVERR_UNREADABLE = 0x80000000u;
+uint32_t take_device_word(const void* symbol);  // read, then clear if non-zero
+uint32_t take_dev_err_nvfp4();
+uint32_t take_dev_err_route();
+uint32_t take_dev_err_combine_q();
+// Test hook (moe4_debug_force_wait_timeout): bounded waits between
+// workgroups wait for a count that never arrives, with a tiny spin limit, so
+// that every wait gives up and reports MOE4_DEVERR_WAIT; kernels still exit.
+bool force_wait_timeout();
+
 // ---------------------------------------------------------------- device side
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -663,9 +663,9 @@ static int mxfp8_quant_impl(const void* x, int dtype, int64_t rows, int64_t cols
   hipStream_t s = as_stream(stream);
   const float* tab = nullptr;
   if (dsilu_src || pre_op == MOE4_PRE_SILU) {
-    int rc = ensure_act_tables(s);
+    int rc = act_tables(&tab);
     if (rc) return rc;
-    tab = act_tables_device_ptr() + (dsilu_src ? ACT_TAB : 0);
+    tab += dsilu_src ? ACT_TAB : 0;
   }
   if ((transpose ? max_padded_rows : rows) == 0) return MOE4_OK;
   if (row_codes) MOE4_REQUIRE(transpose && aligned16(row_codes) && row_sf, MOE4_EINVAL, "mxfp8_quant: row outputs");

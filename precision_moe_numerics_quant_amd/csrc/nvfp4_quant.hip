@@ -374,18 +374,24 @@ static void launch_encode(bool four6, dim3 grid, hipStream_t s, const void* x, i
 // tickets n .. 2n-1 encode tile t - n after waiting for the group's amax
 // count.  Every tile of that group has a lower ticket, taken by a workgroup
 // that is running and never waits during an amax: the wait always ends (and
-// is bounded anyway; a flag in the workspace records a give-up).  One launch
+// is bounded anyway; a give-up sets MOE4_DEVERR_WAIT in this file's device
+// error word, which moe4_debug_check reports).  One launch
 // instead of amax, tensor-scale and encode kernels removes two launch tails.
 // (Pairing each amax with an encode a few groups behind, so that the encode's
 // re-read hits the memory-side cache, measured slower: the encode is bound by
 // its ALU work and load latency at two workgroups per CU, not by HBM.)
 namespace wq {
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
+constexpr uint32_t FORCED_SPIN_LIMIT = 64;  // moe4_debug_force_wait_timeout
 }
+
+// This file's device-side error word (moe4_debug_check reads and clears it).
+static __device__ uint32_t g_dev_err;
+uint32_t take_dev_err_nvfp4() { return take_device_word(&g_dev_err); }
 
 __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) k_encode_requant_T(const float* __restrict__ x, int64_t C,
                                                                   int64_t grows, int G, uint32_t n_ct,
-                                                                  uint32_t n_item,
+                                                                  uint32_t n_item, uint32_t wait_extra, uint32_t spin_limit,
                                                                   uint32_t* __restrict__ wsu, float* __restrict__ ts,
                                                                   uint32_t base, uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ sf, uint8_t* __restrict__ out_c,
@@ -404,7 +410,6 @@ __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_e
   uint32_t* amax = wsu;      // [G]
   uint32_t* done = wsu + G;  // [G]
   uint32_t* ticket = wsu + 2 * G;
-  uint32_t* gave_up = ticket + 1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const uint32_t n_all = (uint32_t)G * n_item, n_tk = 2 * n_all;
   const uint32_t key0 = fmix32(base);
@@ -460,11 +465,13 @@ __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_e
       const bool present = pr < grows;
       const int64_t r0 = (int64_t)g * grows + pr;
       if (tid == 0) {
+        // (wait_extra is 0; the test hook sets it to 1, a count that never
+        // arrives, with a tiny spin_limit)
         uint32_t n = 0, spins = 0;
-        while ((n = __hip_atomic_load(done + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < n_item &&
-               ++spins < wq::SPIN_LIMIT)
+        while ((n = __hip_atomic_load(done + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < n_item + wait_extra &&
+               ++spins < spin_limit)
           __builtin_amdgcn_s_sleep(8);
-        if (n < n_item) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n < n_item + wait_extra) atomicOr(&g_dev_err, MOE4_DEVERR_WAIT);
         // (n >> 31 is 0: the address waits for the count)
         const float a = __uint_as_float(__hip_atomic_load(amax + g + (n >> 31), __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT));
@@ -634,9 +641,8 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   const bool amax_given = pre_op == MOE4_PRE_SILU_AMAX;  // ws already holds the group amax bits
   if (amax_given) pre_op = MOE4_PRE_SILU;
   if (pre_op == MOE4_PRE_SILU) {
-    int rc = ensure_act_tables(s);
+    int rc = act_tables(&tab);
     if (rc) return rc;
-    tab = act_tables_device_ptr();
   }
   uint32_t* amax = static_cast<uint32_t*>(ws);
   const int G = n_groups;
@@ -666,11 +672,11 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   return check_launch("nvfp4_quant_46");
 }
 
-// Workspace: amax bits [G], finished amax tiles [G], the ticket counter and
-// the wait give-up flag, all 32-bit words cleared before the launch.
+// Workspace: amax bits [G], finished amax tiles [G] and the ticket counter,
+// 32-bit words cleared before the launch.
 extern "C" size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups) {
   const size_t g = (size_t)(n_groups > 0 ? n_groups : 1);
-  return (2 * g + 2) * sizeof(uint32_t);
+  return (2 * g + 1) * sizeof(uint32_t);
 }
 
 extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint8_t* codes,
@@ -692,7 +698,7 @@ extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols,
   const int G = n_groups;
   const int64_t grows = rows / G;
   uint32_t* wsu = static_cast<uint32_t*>(ws);
-  const int n_words = 2 * G + 2;
+  const int n_words = 2 * G + 1;
   hipLaunchKernelGGL(k_zero_u32, dim3((n_words + 255) / 256), dim3(256), 0, s, wsu, n_words);
   if (rows == 0) {  // empty groups: tensor scale 1
     hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, wsu, G, 6.0f * 448.0f, tensor_scale);
@@ -703,8 +709,10 @@ extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols,
   const int64_t slots = (int64_t)cu_count_q() * 2;  // two 64 KB-LDS workgroups per CU
   MOE4_REQUIRE(2 * n_total + slots < ((int64_t)1 << 31), MOE4_EINVAL, "nvfp4_quant_requant_T: tensor too large");
   const int64_t grid = 2 * n_total < slots ? 2 * n_total : slots;
+  const bool forced = force_wait_timeout();
   hipLaunchKernelGGL(k_encode_requant_T, dim3((unsigned)grid), dim3(rq::THREADS), 0, s, x, cols, grows, G,
-                     (uint32_t)n_ct, (uint32_t)n_item, wsu, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
+                     (uint32_t)n_ct, (uint32_t)n_item, forced ? 1u : 0u,
+                     forced ? wq::FORCED_SPIN_LIMIT : wq::SPIN_LIMIT, wsu, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
   return check_launch("nvfp4_quant_requant_T");
 }
 
@@ -725,10 +733,11 @@ extern "C" int nvfp4_dequant(const uint8_t* codes, const uint8_t* sf, const floa
 extern "C" int moe_silu_eval(const uint16_t* u, int64_t n, float* silu_out, float* dsilu_out, void* stream) {
   MOE4_REQUIRE(n >= 0 && (n == 0 || u), MOE4_EINVAL, "moe_silu_eval: bad arguments");
   hipStream_t s = as_stream(stream);
-  int rc = ensure_act_tables(s);
+  const float* tab = nullptr;
+  int rc = act_tables(&tab);
   if (rc) return rc;
   if (n == 0) return MOE4_OK;
   hipLaunchKernelGGL(k_silu_eval, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, u, n, silu_out, dsilu_out,
-                     act_tables_device_ptr());
+                     tab);
   return check_launch("moe_silu_eval");
 }

@@ -14,6 +14,20 @@
 
 namespace moe4 {
 
+// This file's device-side error word (moe4_debug_check reads and clears it):
+// indices or offsets outside their range, clamped so that nothing faults.
+static __device__ uint32_t g_dev_err;
+uint32_t take_dev_err_route() { return take_device_word(&g_dev_err); }
+
+// idx clamped to [0, n); a clamp is reported
+__device__ inline int64_t clamp_index(int64_t i, int64_t n) {
+  if (i < 0 || i >= n) {
+    atomicOr(&g_dev_err, MOE4_DEVERR_INDEX);
+    return i < 0 ? 0 : n - 1;
+  }
+  return i;
+}
+
 constexpr int MAXE = 1024;
 constexpr int MAXK = 16;
 
@@ -147,8 +161,8 @@ __global__ void __launch_bounds__(256) k_gather_rows(const uint8_t* __restrict__
                                                      int64_t n_in, int64_t cols, const int32_t* __restrict__ perm,
                                                      int k, uint8_t* __restrict__ oc, uint8_t* __restrict__ os) {
   const int64_t r = blockIdx.x;
-  int64_t src = perm[r] / k;
-  src = src < 0 ? 0 : (src >= n_in ? n_in - 1 : src);
+  const int64_t a = perm[r];
+  const int64_t src = clamp_index(a < 0 ? -1 : a / k, n_in);
   const int64_t cb = cols / 2;  // multiple of 8
   const u32x2* s2 = reinterpret_cast<const u32x2*>(codes + src * cb);
   u32x2* d2 = reinterpret_cast<u32x2*>(oc + r * cb);
@@ -173,8 +187,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yp, c
 #pragma unroll
   for (int j = 0; j < MAXK; ++j) {
     if (j < k) {
-      const int64_t row = inv[t * k + j];
-      rows[j] = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+      rows[j] = clamp_index(inv[t * k + j], n_rows);
       g[j] = GATED ? gates[t * k + j] : 1.0f;
     }
   }
@@ -212,8 +225,7 @@ __global__ void __launch_bounds__(256) k_dgates(const uint16_t* __restrict__ dy,
   if (t >= T) return;
   const uint16_t* dyr = dy + t * d;
   for (int j = 0; j < k; ++j) {
-    int64_t row = inv[t * k + j];
-    row = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+    const int64_t row = clamp_index(inv[t * k + j], n_rows);
     const float* ypr = yp + row * d;
     float acc = 0.0f;
     for (int64_t c = 8 * l; c < d; c += 512) {
