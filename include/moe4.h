@@ -148,6 +148,23 @@ int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
 size_t nvfp4_quant_46_ws_bytes(int32_t n_groups);
 
 /*
+ * nvfp4_quant_46_noalloc - nvfp4_quant_46 without a workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Its scratch (one amax
+ * word per group) is a static device array of the library, 4096 words (16 KB)
+ * per device, held until the process ends; each call clears the words it
+ * uses with a kernel first.  Arguments and results as nvfp4_quant_46 (byte
+ * for byte), except: pre_op MOE4_PRE_NONE or MOE4_PRE_SILU only
+ * (MOE4_PRE_SILU_AMAX takes the GEMM's amax buffer: use nvfp4_quant_46);
+ * 1 <= n_groups <= 4096, else MOE4_EINVAL with nothing enqueued.  Every call
+ * on one device shares that device's array: calls that overlap on one device
+ * (on any streams) race and give wrong results.  Allocates nothing.
+ */
+int nvfp4_quant_46_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
+                           const int32_t* group_row_off, int32_t n_groups, int mode, int pre_op,
+                           uint8_t* codes, uint8_t* sf, float* tensor_scale, void* stream);
+
+/*
  * nvfp4_quant_requant_T - weights: both low-precision copies in one pass.
  * Byte for byte the result of nvfp4_quant_46 on float32 x [rows, cols] in
  * mode MOE4_NVFP4_6 with n_groups equal row groups (one tensor scale each),

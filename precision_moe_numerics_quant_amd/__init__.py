@@ -38,6 +38,8 @@ _SIGS = {
     "nvfp4_quant_46": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _int, _int, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _size, _c_void_p]),
     "nvfp4_quant_46_ws_bytes": (_size, [_i32]),
+    "nvfp4_quant_46_noalloc": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _i32, _int, _int, _c_void_p,
+                                      _c_void_p, _c_void_p, _c_void_p]),
     "nvfp4_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _u64, _u32,
                                      _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "nvfp4_quant_requant_T_ws_bytes": (_size, [_i32]),
@@ -176,6 +178,28 @@ def nvfp4_quant_46(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE, ws
     rc = lib().nvfp4_quant_46(_p(x), dt, R, C, _p(group_row_off), G, mode, pre_op, _p(codes), _p(sf), _p(ts),
                               _p(ws), ws.numel(), _stream())
     _check(rc, "nvfp4_quant_46")
+    return codes, sf, ts
+
+
+def nvfp4_quant_46_noalloc(x, mode=NVFP4_4OVER6, group_row_off=None, pre_op=PRE_NONE, out=None):
+    """nvfp4_quant_46 with the library's static scratch instead of a workspace.
+    out: optional (codes, sf, ts) tensors to write into (nothing is allocated
+    then); otherwise they are allocated here, outside the library call."""
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError("nvfp4_quant_46_noalloc: x must be bf16 or float32")
+    _dev(x, x.dtype, "x")
+    R, C = x.shape
+    G = 1 if group_row_off is None else group_row_off.numel() - 1
+    if group_row_off is not None:
+        _dev(group_row_off, torch.int32, "group_row_off")
+    if out is None:
+        out = (_empty((R, C // 2), torch.uint8, x), _empty((R, C // 16), torch.uint8, x),
+               _empty((G,), torch.float32, x))
+    codes, sf, ts = out
+    rc = lib().nvfp4_quant_46_noalloc(_p(x), dt, R, C, _p(group_row_off), G, mode, pre_op, _p(codes), _p(sf),
+                                      _p(ts), _stream())
+    _check(rc, "nvfp4_quant_46_noalloc")
     return codes, sf, ts
 
 

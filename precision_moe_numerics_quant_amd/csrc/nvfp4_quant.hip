@@ -17,6 +17,9 @@
 // copy the backward pass needs, in one persistent launch.
 // All float arithmetic is one IEEE binary32 operation per step (the library
 // is built with -ffp-contract=off), with correctly rounded division.
+#include <mutex>
+#include <string>
+
 #include "act.h"
 #include "moe4_internal.h"
 #include "mx_requant.h"
@@ -670,6 +673,47 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
       launch_encode<MOE4_F32, false>(four6, grid, s, x, rows, cols, group_row_off, G, tensor_scale, codes, sf, tab);
   }
   return check_launch("nvfp4_quant_46");
+}
+
+// ------------------------------------------------ allocation-free variant
+// nvfp4_quant_46's scratch (the per-group amax words) in a static device
+// array, for callers that cannot allocate.  In host code `scratch` names a
+// host-side stand-in: kernels get the device address that
+// hipGetSymbolAddress gives, looked up once per device (that device current)
+// and kept in g_scratch_ptr.
+constexpr int NOALLOC_MAX_GROUPS = 4096;
+static __device__ __align__(256) uint32_t scratch[NOALLOC_MAX_GROUPS];
+static std::mutex g_scratch_mu;
+static uint32_t* g_scratch_ptr[64];
+
+static int scratch_device_ptr(uint32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MOE4_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE4_EHIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE4_OK;
+}
+
+extern "C" int nvfp4_quant_46_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
+                                      const int32_t* group_row_off, int32_t n_groups, int mode, int pre_op,
+                                      uint8_t* codes, uint8_t* sf, float* tensor_scale, void* stream) {
+  MOE4_REQUIRE(pre_op == MOE4_PRE_NONE || pre_op == MOE4_PRE_SILU, MOE4_EINVAL,
+               "nvfp4_quant_46_noalloc: pre_op must be MOE4_PRE_NONE or MOE4_PRE_SILU");
+  MOE4_REQUIRE(n_groups >= 1 && n_groups <= NOALLOC_MAX_GROUPS, MOE4_EINVAL,
+               "nvfp4_quant_46_noalloc: n_groups must be in [1, 4096] (the static scratch holds 4096 groups)");
+  uint32_t* ws = nullptr;
+  int rc = scratch_device_ptr(&ws);
+  if (rc) return rc;
+  // nvfp4_quant_46 clears the n_groups amax words with a kernel before use
+  return nvfp4_quant_46(x, dtype, rows, cols, group_row_off, n_groups, mode, pre_op, codes, sf, tensor_scale, ws,
+                        (size_t)n_groups * sizeof(uint32_t), stream);
 }
 
 // Workspace: amax bits [G], finished amax tiles [G] and the ticket counter,
