@@ -450,6 +450,24 @@ def moe_grouped_gemm_bwd_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, N1,
     return dw
 
 
+def moe_grouped_gemm_bwd(dy_codes, dy_sf, wT_codes, wT_sf, dyT_codes, dyT_sf, xT_codes, xT_sf, expert_off,
+                         expert_off_pad, Nin, Nout, dw=None, beta=0.0):
+    """dgrad and wgrad of one expert linear in one call: returns (dx float32
+    [M, Nin], dw float32 [E, Nout, Nin]).  dy row-wise [M, Nout], W^T requantised
+    [E][Nin][Nout], dy and x transposed group-major [Nout][P_e] / [Nin][P_e]
+    with block-major scales."""
+    M = dy_codes.shape[0]
+    E = expert_off.numel() - 1
+    dx = _empty((M, Nin), torch.float32, dy_codes)
+    if dw is None:
+        dw = _empty((E, Nout, Nin), torch.float32, dy_codes)
+    rc = lib().moe_grouped_gemm_bwd(_p(dy_codes), _p(dy_sf), _p(wT_codes), _p(wT_sf), _p(dyT_codes), _p(dyT_sf),
+                                    _p(xT_codes), _p(xT_sf), _p(expert_off), _p(expert_off_pad), E, M, Nin, Nout,
+                                    _p(dx), _p(dw), beta, _stream())
+    _check(rc, "moe_grouped_gemm_bwd")
+    return dx, dw
+
+
 # ----------------------------------------------------------- combine / misc
 
 def moe_combine(yp, gates, inv_perm):
