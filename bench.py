@@ -53,7 +53,10 @@ def work_table(c, off, off_pad):
     nv = 9.0 / 16.0            # NVFP4 bytes per element (codes + E4M3 scales)
     mxb = 33.0 / 32.0          # MXFP8 bytes per element (codes + E8M0 scales)
     gem = 2.0 * A * d * F
-    wg_bytes = lambda n1, n2: E * n1 * n2 * 4.0 + (n1 + n2) * Ptot * mxb
+    # wgrad: the active experts' float32 dW (experts without tokens are not
+    # written: the step skips their zero-fill by contract) + both operands
+    E_act = int((np.diff(np.asarray(off)) > 0).sum())
+    wg_bytes = lambda n1, n2: E_act * n1 * n2 * 4.0 + (n1 + n2) * Ptot * mxb
     return {
         # two fp32 reads (amax, then encode), the NVFP4 write and the backward's MXFP8 copy
         "F1 W_up quant (+ requant)": ("hbm", E * F * d * (8.0 + nv + mxb)),
@@ -100,16 +103,26 @@ KERNEL_OF = {
     "B13 router backward": "k_route_backward",
 }
 
-# calls that launch several kernels (workspace clear + quantiser; zero, amax,
-# scale, encode; route's four): not candidates for the single dominant kernel
-MULTI_KERNEL_CALLS = {"F1 W_up quant (+ requant)", "F1 W_down quant (+ requant)", "F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)",
-                      "F7 SiLU + H quant (NVFP4 4/6)"}
+# calls that launch several kernels of comparable length (zero, amax, scale,
+# encode; route's four): not candidates for the single dominant kernel.  (The
+# weight quantisation F1 is one persistent kernel after a workspace clear of a
+# few microseconds: it is a candidate.)
+MULTI_KERNEL_CALLS = {"F2-F3 route + permutation", "F4 X quant (NVFP4 4/6)", "F7 SiLU + H quant (NVFP4 4/6)"}
+
+# the quantisers (float -> NVFP4 / MXFP8 codes) and the data-movement calls
+# (gather, combine, un-permute, gate gradient), pooled separately
+QUANTIZER_CALLS = {"F1 W_up quant (+ requant)", "F1 W_down quant (+ requant)", "F4 X quant (NVFP4 4/6)",
+                   "F7 SiLU + H quant (NVFP4 4/6)", "B1 dY quant row-wise + transposed (MXFP8)", "B4 H requant SR-T",
+                   "B6 SiLU' + dU quant row-wise + transposed", "B9 X requant SR-T"}
+MOVEMENT_CALLS = {"F5 dispatch gather", "F9 combine", "B11 un-permute sum", "B12 gate gradient"}
 
 # rocprofv3 --pmc summaries (FETCH_SIZE and WRITE_SIZE passes, scaled by a
 # plain copy of known size) of a kernel, with the hash of its source file:
 # the HBM bytes per launch are reported only while that source is unchanged.
 PMC_PROFILE = {"k_wgrad_ws256": ("profiles/k_wgrad_ws256_T16384_E384_pmc.md",
-                              "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip")}
+                                 "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip"),
+               "k_encode_requant_T": ("profiles/k_encode_requant_T_E384_4096x1536_pmc.md",
+                                      "precision_moe_numerics_quant_amd/csrc/nvfp4_quant.hip")}
 
 
 def source_sha256(rel):
@@ -173,6 +186,31 @@ def pmc_summary(fetch_csv, write_csv, kernel_pat, copy_bytes=1 << 30):
             f"- hbm_bytes_per_launch = {fetch_b + write_b:.4e}\n")
 
 
+def trace_summary(trace_csv, min_frac=0.1):
+    """Markdown table of a rocprofv3 --kernel-trace csv: per kernel name, the
+    launches at the layer's shape (at least min_frac of that name's longest
+    launch: the run also launches the same kernels for the small workloads)
+    with their count and average duration, and all launches' total."""
+    import csv
+    durs = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            durs.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    total = sum(sum(v) for v in durs.values())
+    rows = []
+    for name, v in durs.items():
+        big = [x for x in v if x >= min_frac * max(v)]
+        rows.append((sum(v), name, len(v), len(big), float(np.mean(big))))
+    rows.sort(reverse=True)
+    out = ["| kernel | launches | at layer shape | avg us at layer shape | total ms (all) | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for tot, name, n, nb, avg in rows[:30]:
+        short = name.split("(")[0] if "<" not in name.split("(")[0] else name.split(")")[0].split("(")[0]
+        out.append(f"| `{short[:90]}` | {n} | {nb} | {avg:.1f} | {tot / 1000.0:.2f} | {100.0 * tot / total:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def gpu_run(steps, warmup):
     import precision_moe_numerics_quant_amd as m4
     from precision_moe_numerics_quant_amd import layer
@@ -193,7 +231,7 @@ def gpu_run(steps, warmup):
     def step(t=None):
         fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t,
                            seed=synth.SR_SEED)
-        bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED, timer=t)
+        bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED, timer=t, skip_empty_dw=True)
         return fw, bw
 
     for _ in range(warmup):
@@ -225,6 +263,7 @@ def gpu_run(steps, warmup):
         prev = ev
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
+    zero_fill = wgrad_zero_fill_bench(fw, bw, c, off)
     payload = combine_payload_bench(fw, c)
     small = small_configs_bench(inp, fw["wq"])
     del fw, bw
@@ -251,7 +290,7 @@ def gpu_run(steps, warmup):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
-    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small
+    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small, zero_fill
 
 
 def _median_ms(fn, reps):
@@ -264,6 +303,30 @@ def _median_ms(fn, reps):
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))
     return float(np.median(ts))
+
+
+def wgrad_zero_fill_bench(fw, bw, c, off, reps=10):
+    """The step's weight gradients leave the experts without tokens unwritten
+    (their gradient is zero, and the route's offsets say which they are).
+    This times both wgrad calls on the step's operands with and without the
+    zero-fill of those experts' dW (median of reps each)."""
+    import precision_moe_numerics_quant_amd as m4
+    d, F, E = c["d"], c["F"], c["E"]
+    op = fw["route"]["off_pad"]
+    dWd, dWu = torch.empty_like(bw["dW_down"]), torch.empty_like(bw["dW_up"])
+
+    def both(skip):
+        m4.moe_grouped_gemm_bwd_wgrad(bw["dy_col"][0], bw["dy_col"][1], bw["hT"][0], bw["hT"][1], op, d, F, dw=dWd,
+                                      skip_empty=skip)
+        m4.moe_grouped_gemm_bwd_wgrad(bw["du_col"][0], bw["du_col"][1], bw["xT"][0], bw["xT"][1], op, F, d, dw=dWu,
+                                      skip_empty=skip)
+    both(False)
+    t_fill = _median_ms(lambda: both(False), reps)
+    t_skip = _median_ms(lambda: both(True), reps)
+    empty = int((np.diff(off) == 0).sum())
+    return {"empty_experts": empty, "zero_fill_bytes": empty * 2.0 * d * F * 4.0,
+            "ms_both_wgrad_skip": round(t_skip, 4), "ms_both_wgrad_zero_fill": round(t_fill, 4),
+            "ms_zero_fill": round(t_fill - t_skip, 4)}
 
 
 def small_configs_bench(inp4, wq, reps=20):
@@ -380,18 +443,41 @@ def quantizer_microbench(reps=20):
             ts.append(a.elapsed_time(b))
         return float(np.median(ts))
 
-    t_q = timed(lambda: m4.nvfp4_quant_46(x, m4.NVFP4_4OVER6))
-    t_r = timed(lambda: m4.mxfp8_requant_sr_T(q[0], q[1], q[2], off, off, False, synth.SR_SEED, 0))
+    # cold: before each timed call, a 1 GiB buffer is written, which evicts
+    # the 4 MB L2s and the 256 MB Infinity Cache
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def cold(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    fq = lambda: m4.nvfp4_quant_46(x, m4.NVFP4_4OVER6)
+    fr = lambda: m4.mxfp8_requant_sr_T(q[0], q[1], q[2], off, off, False, synth.SR_SEED, 0)
+    t_q, t_r = timed(fq), timed(fr)
+    c_q, c_r = cold(fq), cold(fr)
+    del flush
     n = R * C
     bytes_q = n * 2 * 2 + n * 9 / 16          # two bf16 reads (amax, encode) + codes and scales
     bytes_q1 = n * 2 + n * 9 / 16             # one-read basis
     bytes_r = n * 9 / 16 + n * 33 / 32        # NVFP4 in, MXFP8 out
-    return {"workload": f"bf16 {R}x{C}, 1% of rows x50 (warm caches, median of {reps})",
-            "nvfp4_46_quant": {"ms": round(t_q, 4), "GBps": round(bytes_q / t_q / 1e6, 1),
-                               "frac_hbm": round(bytes_q / t_q / 1e6 / (PEAK_HBM / 1e9), 4),
-                               "GBps_one_read_basis": round(bytes_q1 / t_q / 1e6, 1)},
-            "mxfp8_requant_sr_T": {"ms": round(t_r, 4), "GBps": round(bytes_r / t_r / 1e6, 1),
-                                   "frac_hbm": round(bytes_r / t_r / 1e6 / (PEAK_HBM / 1e9), 4)}}
+
+    def rate(b, t):
+        return {"ms": round(t, 4), "GBps": round(b / t / 1e6, 1), "frac_hbm": round(b / t / 1e6 / (PEAK_HBM / 1e9), 4)}
+    return {"workload": f"bf16 {R}x{C}, 1% of rows x50 (median of {reps}; cold: a 1 GiB buffer written before "
+                        f"each call, evicting the L2s and the 256 MB Infinity Cache; warm: back to back)",
+            "nvfp4_46_quant": {"basis": "two bf16 reads + codes and scales", "cold": rate(bytes_q, c_q),
+                               "warm": rate(bytes_q, t_q),
+                               "cold_GBps_one_read_basis": round(bytes_q1 / c_q / 1e6, 1)},
+            "mxfp8_requant_sr_T": {"basis": "NVFP4 read + MXFP8 write", "cold": rate(bytes_r, c_r),
+                                   "warm": rate(bytes_r, t_r)}}
 
 
 def copy_calibration(n_bytes=1 << 30, reps=3):
@@ -441,7 +527,12 @@ def main():
                     help="end with a 1 GiB device copy (reference kernel for rocprofv3 byte counters)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
                     help="print the traffic summary of two rocprofv3 --pmc csv files and exit (no GPU)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace csv and exit (no GPU)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary), end="")
+        return
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary), end="")
         print(f"- source_sha256 = {source_sha256(PMC_PROFILE[args.pmc_summary[2]][1])}")
@@ -450,14 +541,13 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small = gpu_run(args.steps, args.warmup)
+    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small, zero_fill = gpu_run(args.steps, args.warmup)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
     calls = {}
     gemm_flops = 0.0
     gemm_ms = 0.0
-    q_bytes = 0.0
-    q_ms = 0.0
+    pool = {"q": [0.0, 0.0], "m": [0.0, 0.0]}
     for name, times in per.items():
         kind, amount = table[name][0], table[name][1]
         ms = float(np.mean(times))
@@ -465,9 +555,10 @@ def main():
         entry = {"ms": round(ms, 4)}
         if kind == "hbm":
             entry.update(GBps=round(rate / 1e9, 1), frac_hbm=round(rate / PEAK_HBM, 4))
-            if "route" not in name:
-                q_bytes += amount
-                q_ms += ms
+            key = "q" if name in QUANTIZER_CALLS else ("m" if name in MOVEMENT_CALLS else None)
+            if key:
+                pool[key][0] += amount
+                pool[key][1] += ms
         else:
             entry.update(TFLOPs=round(rate / 1e12, 1), frac_peak=round(rate / peaks[kind], 4))
             if kind == "f16":
@@ -521,7 +612,11 @@ def main():
                    "experts": c["E"], "top_k": c["k"], "router_bias": "zipf1.1", "active_experts": int((np.diff(off) > 0).sum()),
                    "max_rows_per_expert": int(np.diff(off).max())},
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
-        "quantizer_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        # pooled over the step's quantiser calls (F1, F4, F7, B1, B4, B6, B9), and
+        # over its data-movement calls (F5, F9, B11, B12): bytes / time
+        "quantizer_gbps": round(pool["q"][0] / (pool["q"][1] * 1e-3) / 1e9, 1),
+        "data_movement_gbps": round(pool["m"][0] / (pool["m"][1] * 1e-3) / 1e9, 1),
+        "wgrad_zero_fill": zero_fill,
         "breakdown": calls,
         "roofline": roof,
         "quantizer_microbench": quantizer_microbench(),

@@ -419,17 +419,24 @@ int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, const uint8
 
 /*
  * moe_grouped_gemm_bwd_wgrad - dW[e] = A_e . B_e^T over expert e's padded token
- * dimension: A and B in the group-major padded MXFP8 layout with block-major
- * scales (MOE4_SF_BLOCKS), A_e [N1][P_e] (scales [P_e/32][N1]), B_e [N2][P_e]
- * (scales [P_e/32][N2]) with P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32;
- * beta = 0 overwrites (experts with no rows get zeros), beta = 1 accumulates.
+ * dimension: the weight-gradient products of the MXFP8 backward (agihunt.info
+ * page, "Confirmed"), float32 master-weight gradients (lhc.media page,
+ * paragraph on the precisions that remain).  A and B in the group-major
+ * padded MXFP8 layout with block-major scales (MOE4_SF_BLOCKS), A_e [N1][P_e]
+ * (scales [P_e/32][N1]), B_e [N2][P_e] (scales [P_e/32][N2]) with
+ * P_e = off_pad[e+1] - off_pad[e].  dw [E, N1, N2] float32; beta = 0
+ * overwrites, beta = 1 accumulates.  Experts with no rows: with beta = 0 their
+ * dw[e] is written with zeros, unless flags holds MOE4_WGRAD_SKIP_EMPTY, which
+ * leaves it untouched (the caller knows them from off_pad: dw[e] is written
+ * iff off_pad[e+1] > off_pad[e]); with beta = 1 nothing is added.
  * N1 % 32 == 0, N2 % 32 == 0; each expert's operands (N1 * P_e and N2 * P_e
  * bytes) below 2 GiB (32-bit buffer offsets).
  */
+#define MOE4_WGRAD_SKIP_EMPTY 1
 int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
                                const uint8_t* b_codes, const uint8_t* b_sf,
                                const int32_t* expert_off_pad, int32_t E, int64_t N1, int64_t N2,
-                               float* dw, float beta, void* stream);
+                               float* dw, float beta, int flags, void* stream);
 
 /*
  * moe_grouped_gemm_bwd - dgrad and wgrad of one expert linear layer in one
@@ -441,7 +448,7 @@ int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf,
  *       [M_total, Nout], W^T requantised [E][Nin][Nout], expert_off),
  *   dw (float32 [E, Nout, Nin]) = moe_grouped_gemm_bwd_wgrad(dy transposed
  *       group-major [Nout][P_e], x transposed group-major [Nin][P_e], both
- *       with block-major scales, expert_off_pad, beta).
+ *       with block-major scales, expert_off_pad, beta, flags).
  * Arguments, layouts and constraints as in the two calls; returns the first
  * error (nothing enqueued when the dgrad's checks fail).
  */
@@ -451,7 +458,7 @@ int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_sf,         
                          const uint8_t* xT_codes, const uint8_t* xT_sf,           /* group-major [Nin][P_e]   */
                          const int32_t* expert_off, const int32_t* expert_off_pad, int32_t E,
                          int64_t M_total, int64_t Nin, int64_t Nout,
-                         float* dx, float* dw, float beta, void* stream);
+                         float* dx, float* dw, float beta, int flags, void* stream);
 
 /* ----------------------------------------------------- combine / scatter */
 /*

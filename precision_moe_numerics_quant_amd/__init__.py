@@ -70,8 +70,8 @@ _SIGS = {
     "moe_grouped_gemm_bwd_dgrad": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i64,
                                           _i64, _c_void_p, _c_void_p]),
     "moe_grouped_gemm_bwd_wgrad": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i64,
-                                          _c_void_p, _f32, _c_void_p]),
-    "moe_grouped_gemm_bwd": (_int, [_c_void_p] * 10 + [_i32, _i64, _i64, _i64, _c_void_p, _c_void_p, _f32,
+                                          _c_void_p, _f32, _int, _c_void_p]),
+    "moe_grouped_gemm_bwd": (_int, [_c_void_p] * 10 + [_i32, _i64, _i64, _i64, _c_void_p, _c_void_p, _f32, _int,
                                                        _c_void_p]),
     "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_unpermute_sum": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
@@ -439,19 +439,24 @@ def moe_grouped_gemm_mx(a_codes, a_sf, b_codes, b_sf, expert_off, out_dtype=torc
     return c
 
 
-def moe_grouped_gemm_bwd_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, N1, N2, dw=None, beta=0.0):
-    """Group-major padded MXFP8 A [N1][P_e], B [N2][P_e] per expert -> dw [E, N1, N2] float32."""
+WGRAD_SKIP_EMPTY = 1
+
+
+def moe_grouped_gemm_bwd_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, N1, N2, dw=None, beta=0.0,
+                               skip_empty=False):
+    """Group-major padded MXFP8 A [N1][P_e], B [N2][P_e] per expert -> dw [E, N1, N2] float32.
+    skip_empty: experts without rows keep whatever dw holds (see moe4.h)."""
     E = expert_off_pad.numel() - 1
     if dw is None:
         dw = _empty((E, N1, N2), torch.float32, a_codes)
     rc = lib().moe_grouped_gemm_bwd_wgrad(_p(a_codes), _p(a_sf), _p(b_codes), _p(b_sf), _p(expert_off_pad), E, N1,
-                                          N2, _p(dw), beta, _stream())
+                                          N2, _p(dw), beta, WGRAD_SKIP_EMPTY if skip_empty else 0, _stream())
     _check(rc, "moe_grouped_gemm_bwd_wgrad")
     return dw
 
 
 def moe_grouped_gemm_bwd(dy_codes, dy_sf, wT_codes, wT_sf, dyT_codes, dyT_sf, xT_codes, xT_sf, expert_off,
-                         expert_off_pad, Nin, Nout, dw=None, beta=0.0):
+                         expert_off_pad, Nin, Nout, dw=None, beta=0.0, skip_empty=False):
     """dgrad and wgrad of one expert linear in one call: returns (dx float32
     [M, Nin], dw float32 [E, Nout, Nin]).  dy row-wise [M, Nout], W^T requantised
     [E][Nin][Nout], dy and x transposed group-major [Nout][P_e] / [Nin][P_e]
@@ -463,7 +468,7 @@ def moe_grouped_gemm_bwd(dy_codes, dy_sf, wT_codes, wT_sf, dyT_codes, dyT_sf, xT
         dw = _empty((E, Nout, Nin), torch.float32, dy_codes)
     rc = lib().moe_grouped_gemm_bwd(_p(dy_codes), _p(dy_sf), _p(wT_codes), _p(wT_sf), _p(dyT_codes), _p(dyT_sf),
                                     _p(xT_codes), _p(xT_sf), _p(expert_off), _p(expert_off_pad), E, M, Nin, Nout,
-                                    _p(dx), _p(dw), beta, _stream())
+                                    _p(dx), _p(dw), beta, WGRAD_SKIP_EMPTY if skip_empty else 0, _stream())
     _check(rc, "moe_grouped_gemm_bwd")
     return dx, dw
 

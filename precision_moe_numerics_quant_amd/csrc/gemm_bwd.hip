@@ -590,7 +590,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
                                                                  const int32_t* __restrict__ off, int E,
                                                                  int64_t N1, int64_t N2, int64_t n_ntiles,
                                                                  int64_t n_all, float* __restrict__ dw,
-                                                                 float beta) {
+                                                                 float beta, bool zero_empty) {
   using namespace bwd;
   const int64_t per_e = n_all / E;  // tiles per expert
   const int64_t stride = gridDim.x;
@@ -611,7 +611,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
   // tokens; tiles of empty experts met on the way get zeros if fill
   auto next_tile = [&](int64_t t, bool fill) {
     while (t < n_all && klen_of(t) == 0) {
-      if (fill && beta == 0.0f) {
+      if (fill && beta == 0.0f && zero_empty) {
         const int e = (int)(t / per_e);
         const int64_t rest = t % per_e;
         zero_tile(dw + (int64_t)e * N1 * N2, N2, (rest / n_ntiles) * BM, N1, (rest % n_ntiles) * BN, N2);
@@ -695,7 +695,6 @@ __global__ void __launch_bounds__(64 * WVM * WVN, MINB) k_wgrad_mx(const uint8_t
     dgrad_dma_body<TM, TN, BF16>(a_codes, a_sf, b_codes, b_sf, off, E, M_total, N, K, n_ntiles, n_all, c);       \
   }
 MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_256, 256, 256, 1, false)
-MOE4_DGRAD_DMA_KERNEL(k_dgrad_dma_128, 128, 128, 2, false)
 MOE4_DGRAD_DMA_KERNEL(k_mx_gemm_dma_256_bf16, 256, 256, 1, true)
 #undef MOE4_DGRAD_DMA_KERNEL
 
@@ -737,7 +736,7 @@ __global__ void __launch_bounds__(wsg::NT, 1)
     k_wgrad_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
                const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, int64_t n_ntiles_, int64_t n_all_,
-               float* __restrict__ dw, float beta) {
+               float* __restrict__ dw, float beta, bool zero_empty) {
   using namespace wsg;
   using dmag::lds_ptr;
   using dmag::swz;
@@ -895,8 +894,8 @@ __global__ void __launch_bounds__(wsg::NT, 1)
     const int kl = s_off[e + 1] - s_off[e];
     float* C = dw + (int64_t)e * N1 * N2;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (uint64_t)N1 * N2 * 4);
-    if (kl == 0) {  // no tokens: zeros for beta = 0; 4 rows x 64 columns per store
-      if (beta != 0.0f) continue;
+    if (kl == 0) {  // no tokens: zeros for beta = 0 (unless skipped); 4 rows x 64 columns per store
+      if (beta != 0.0f || !zero_empty) continue;
       const bool cok = c0 + wn + (l & 15) * 4 < N2;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -1218,7 +1217,7 @@ __global__ void __launch_bounds__(wsg::NT, 1)
     k_wgrad_ws256(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
                   const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                   const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, int64_t n_ntiles_, int64_t n_all_,
-                  float* __restrict__ dw, float beta) {
+                  float* __restrict__ dw, float beta, bool zero_empty) {
   using namespace wsg2;
   using wsg::NCW;
   using wsg::NT;
@@ -1388,8 +1387,8 @@ __global__ void __launch_bounds__(wsg::NT, 1)
     const int kl = s_off[e + 1] - s_off[e];
     float* C = dw + (int64_t)e * N1 * N2;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (uint64_t)N1 * N2 * 4);
-    if (kl == 0) {  // no tokens: zeros for beta = 0; 4 rows x 64 columns per store
-      if (beta != 0.0f) continue;
+    if (kl == 0) {  // no tokens: zeros for beta = 0 (unless skipped); 4 rows x 64 columns per store
+      if (beta != 0.0f || !zero_empty) continue;
       const bool cok = c0 + wn + (l & 15) * 4 < N2;
 #pragma unroll 8
       for (int k = 0; k < 32; ++k) {
@@ -1448,18 +1447,6 @@ static int cu_count() {
   return n[dev];
 }
 
-static int mx_tile_choice(int mode) {
-  static int v[2] = {[] {
-                       const char* e = getenv("MOE4_MX_TILE");
-                       return e ? atoi(e) : 12;
-                     }(),
-                     [] {
-                       const char* e = getenv("MOE4_MX_TILE_W");
-                       return e ? atoi(e) : 13;
-                     }()};
-  return v[mode];
-}
-
 template <int BM, int BN, int WVM, int WVN, int MINB, int DEPTH = 3>
 static void launch_dgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                            const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
@@ -1471,39 +1458,24 @@ static void launch_dgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* 
 
 template <int BM, int BN, int WVM, int WVN, int MINB>
 static void launch_wgrad_t(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
-                           const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
+                           const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, bool zero_empty,
+                           hipStream_t s) {
   const int64_t n_nt = (N2 + BN - 1) / BN;
   const int64_t n_all = n_nt * ((N1 + BM - 1) / BM) * E;
   int64_t grid = (int64_t)cu_count() * MINB;
   if (grid > n_all) grid = n_all;
   hipLaunchKernelGGL((k_wgrad_mx<BM, BN, WVM, WVN, MINB>), dim3((unsigned)grid), dim3(64 * WVM * WVN), 0, s, ac, as,
-                     bc, bs, off, E, N1, N2, n_nt, n_all, dw, beta);
+                     bc, bs, off, E, N1, N2, n_nt, n_all, dw, beta, zero_empty);
 }
 
-// Tile configurations (MOE4_MX_TILE for dgrad / MOE4_MX_TILE_W for wgrad
-// override, for tuning): 0 = 256x256 with 2x2 waves, 1 = 128x128 2x2 waves
-// (2 blocks/CU), 2 = 128x256 2x2, 3 = 256x256 with 2x4 waves (two waves per
-// SIMD), 4 = 256x256 with 4x2 waves (3 and 4 with one prefetch register
-// set), 5 = 256x256 2x2 with one register set, 6 = 256x256 2x2 with
-// double-buffered LDS and one barrier per slab, 7 = as 6 with 2x4 waves;
-// dgrad only: 8 = direct-to-LDS loads, 256x256 (the default when
-// K % 128 == 0 and N % 128 != 0, else 6), 9 = as 8 with 128x128 tiles at 2
-// blocks/CU, 11 = the warp-specialized persistent kernel with 128x128 tiles
-// (the default when K % 128 == 0 and N % 128 == 0 but N % 256 != 0), 12 = the
-// same with 128x256 tiles (the default when K % 128 == 0 and N % 256 == 0);
-// wgrad
-// only: 10 = the warp-specialized persistent kernel with 128x128 tiles, 13 =
-// the same with 256x128 tiles (the default); both need E <= 2048 and 32-bit
-// tile and output indices (13 falls back to 10, 10 to configuration 1, the
-// persistent register-staged kernel).
+// Kernel choice.  dgrad: the warp-specialized persistent kernel with
+// 128x256 tiles when K % 128 == 0 and N % 256 == 0, with 128x128 tiles when
+// N % 128 == 0; else the direct-to-LDS 256x256 kernel when K % 128 == 0;
+// else the register-staged 256x256 kernel (four-deep prefetch).
 static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
-  int choice = mx_tile_choice(0);
-  if (choice == 12 && N % 256 != 0) choice = 11;
-  if (choice == 11 && N % 128 != 0) choice = 8;
-  if ((choice == 8 || choice == 9 || choice == 11 || choice == 12) && K % dmag::BK != 0) choice = 6;
-  if (choice == 11 || choice == 12) {
-    if (choice == 12)
+  if (K % dmag::BK == 0 && N % 128 == 0) {
+    if (N % 256 == 0)
       hipLaunchKernelGGL((k_dgrad_ws<false, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
                          E, M, N, K, static_cast<void*>(c));
     else
@@ -1511,52 +1483,40 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
                          E, M, N, K, static_cast<void*>(c));
     return;
   }
-  if (choice == 8 || choice == 9) {
-    const int T = choice == 8 ? 256 : 128;
-    const int64_t n_nt = (N + T - 1) / T;
-    const int64_t n_all = n_nt * ((M + T - 1) / T + E);
-    hipLaunchKernelGGL(choice == 8 ? k_dgrad_dma_256 : k_dgrad_dma_128, dim3((unsigned)xcd_grid(n_all)),
-                       dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E, M, N, K, n_nt, n_all, c);
+  if (K % dmag::BK == 0) {
+    const int64_t n_nt = (N + 255) / 256;
+    const int64_t n_all = n_nt * ((M + 255) / 256 + E);
+    hipLaunchKernelGGL(k_dgrad_dma_256, dim3((unsigned)xcd_grid(n_all)), dim3(dmag::NT), 0, s, ac, as, bc, bs, off, E,
+                       M, N, K, n_nt, n_all, c);
     return;
   }
-  switch (choice) {
-    case 1: launch_dgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 2: launch_dgrad_t<128, 256, 2, 2, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 3: launch_dgrad_t<256, 256, 2, 4, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 4: launch_dgrad_t<256, 256, 4, 2, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 5: launch_dgrad_t<256, 256, 2, 2, 1, 2>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 6: launch_dgrad_t<256, 256, 2, 2, 1, 4>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    case 7: launch_dgrad_t<256, 256, 2, 4, 1, 4>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-    default: launch_dgrad_t<256, 256, 2, 2, 1>(ac, as, bc, bs, off, E, M, N, K, c, s); break;
-  }
+  launch_dgrad_t<256, 256, 2, 2, 1, 4>(ac, as, bc, bs, off, E, M, N, K, c, s);
 }
 
+// wgrad: the warp-specialized persistent kernel with 256x128 tiles, else
+// with 128x128 tiles (both need E <= 2048 and 32-bit tile and output
+// indices), else the register-staged persistent 128x128 kernel.
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
-                         const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, hipStream_t s) {
-  const int wc = mx_tile_choice(1);
+                         const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, bool zero_empty,
+                         hipStream_t s) {
   const int64_t ws2_all = (N2 + wsg2::TN - 1) / wsg2::TN * ((N1 + wsg2::TM - 1) / wsg2::TM) * E;
-  if (wc == 13 && E <= wsg::MAX_E && ws2_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
+  if (E <= wsg::MAX_E && ws2_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
     int64_t grid = cu_count();
     if (grid > ws2_all) grid = ws2_all;
     hipLaunchKernelGGL(k_wgrad_ws256, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2,
-                       (N2 + wsg2::TN - 1) / wsg2::TN, ws2_all, dw, beta);
+                       (N2 + wsg2::TN - 1) / wsg2::TN, ws2_all, dw, beta, zero_empty);
     return;
   }
   const int64_t ws_all = (N2 + wsg::TN - 1) / wsg::TN * ((N1 + wsg::TM - 1) / wsg::TM) * E;
-  if ((wc == 10 || wc == 13) && E <= wsg::MAX_E && ws_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
+  if (E <= wsg::MAX_E && ws_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
     const int64_t n_nt = (N2 + wsg::TN - 1) / wsg::TN;
-    const int64_t n_all = ws_all;
     int64_t grid = cu_count();
-    if (grid > n_all) grid = n_all;
+    if (grid > ws_all) grid = ws_all;
     hipLaunchKernelGGL(k_wgrad_ws, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2, n_nt,
-                       n_all, dw, beta);
+                       ws_all, dw, beta, zero_empty);
     return;
   }
-  switch (mx_tile_choice(1)) {
-    case 3: launch_wgrad_t<256, 256, 2, 4, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
-    case 4: launch_wgrad_t<256, 256, 4, 2, 1>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
-    default: launch_wgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, N1, N2, dw, beta, s); break;
-  }
+  launch_wgrad_t<128, 128, 2, 2, 2>(ac, as, bc, bs, off, E, N1, N2, dw, beta, zero_empty, s);
 }
 
 }  // namespace moe4
@@ -1595,9 +1555,8 @@ extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, 
   MOE4_REQUIRE(M_total * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_mx: A and each expert's B must stay below 2 GiB");
   if (M_total == 0) return MOE4_OK;
-  const int ch = mx_tile_choice(0);
-  if ((ch == 11 || ch == 12) && N % 128 == 0) {
-    if (ch == 12 && N % 256 == 0)
+  if (N % 128 == 0) {
+    if (N % 256 == 0)
       hipLaunchKernelGGL((k_dgrad_ws<true, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream),
                          a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c);
     else
@@ -1614,17 +1573,19 @@ extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, 
 
 extern "C" int moe_grouped_gemm_bwd_wgrad(const uint8_t* a_codes, const uint8_t* a_sf, const uint8_t* b_codes,
                                           const uint8_t* b_sf, const int32_t* expert_off_pad, int32_t E, int64_t N1,
-                                          int64_t N2, float* dw, float beta, void* stream) {
+                                          int64_t N2, float* dw, float beta, int flags, void* stream) {
   MOE4_REQUIRE(E >= 1 && N1 > 0 && N2 > 0 && N1 % 32 == 0 && N2 % 32 == 0, MOE4_EINVAL,
                "moe_grouped_gemm_bwd_wgrad: need N1 % 32 == 0 and N2 % 32 == 0");
   MOE4_REQUIRE(beta == 0.0f || beta == 1.0f, MOE4_EINVAL, "moe_grouped_gemm_bwd_wgrad: beta must be 0 or 1");
+  MOE4_REQUIRE((flags & ~MOE4_WGRAD_SKIP_EMPTY) == 0, MOE4_EINVAL, "moe_grouped_gemm_bwd_wgrad: unknown flags");
   MOE4_REQUIRE(a_codes && a_sf && b_codes && b_sf && expert_off_pad && dw, MOE4_EINVAL,
                "moe_grouped_gemm_bwd_wgrad: NULL pointer");
   MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(dw), MOE4_EALIGN,
                "moe_grouped_gemm_bwd_wgrad: misaligned pointer");
   MOE4_REQUIRE(((N2 + 127) / 128) * ((N1 + 127) / 128) * E < ((int64_t)1 << 31), MOE4_EINVAL,
                "moe_grouped_gemm_bwd_wgrad: too large");
-  launch_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, dw, beta, as_stream(stream));
+  launch_wgrad(a_codes, a_sf, b_codes, b_sf, expert_off_pad, E, N1, N2, dw, beta, (flags & MOE4_WGRAD_SKIP_EMPTY) == 0,
+               as_stream(stream));
   return check_launch("moe_grouped_gemm_bwd_wgrad");
 }
 
@@ -1632,8 +1593,9 @@ extern "C" int moe_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_s
                                     const uint8_t* wT_sf, const uint8_t* dyT_codes, const uint8_t* dyT_sf,
                                     const uint8_t* xT_codes, const uint8_t* xT_sf, const int32_t* expert_off,
                                     const int32_t* expert_off_pad, int32_t E, int64_t M_total, int64_t Nin,
-                                    int64_t Nout, float* dx, float* dw, float beta, void* stream) {
+                                    int64_t Nout, float* dx, float* dw, float beta, int flags, void* stream) {
   int rc = moe_grouped_gemm_bwd_dgrad(dy_codes, dy_sf, wT_codes, wT_sf, expert_off, E, M_total, Nin, Nout, dx, stream);
   if (rc) return rc;
-  return moe_grouped_gemm_bwd_wgrad(dyT_codes, dyT_sf, xT_codes, xT_sf, expert_off_pad, E, Nout, Nin, dw, beta, stream);
+  return moe_grouped_gemm_bwd_wgrad(dyT_codes, dyT_sf, xT_codes, xT_sf, expert_off_pad, E, Nout, Nin, dw, beta, flags,
+                                    stream);
 }

@@ -552,8 +552,6 @@ __device__ __forceinline__ void gemm_fwd_dma_body(const uint8_t* __restrict__ a_
     gemm_fwd_dma_body<OUT_BF16, BM, BN, PIPE>(a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, off, E, M_total, \
                                         N, K, n_ntiles, n_all, c);                                                 \
   }
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_256, true, 256, 256, 1, true)
-MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_256, false, 256, 256, 1, true)
 MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_bf16_128, true, 128, 128, 2, false)
 MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2, false)
 #undef MOE4_FWD_DMA_KERNEL
@@ -854,29 +852,16 @@ static void launch_fwd_dma(hipStream_t s, const uint8_t* ac, const uint8_t* as, 
                            int64_t N, int64_t K, void* c) {
   const int64_t n_nt = (N + BN - 1) / BN;
   const int64_t n_all = n_nt * ((M + BM - 1) / BM + E);
+  static_assert(BM == 128 && BN == 128 && MINB == 2, "the direct-to-LDS forward kernel is built for 128x128 tiles");
   const dim3 grid((unsigned)xcd_grid(n_all));
-  if (BM == 256)
-    hipLaunchKernelGGL(OUT_BF16 ? k_gemm_fwd_dma_bf16_256 : k_gemm_fwd_dma_f32_256, grid, dim3(fdma::NT), 0, s, ac, as,
-                       ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, n_all, c);
-  else
-    hipLaunchKernelGGL(OUT_BF16 ? k_gemm_fwd_dma_bf16_128 : k_gemm_fwd_dma_f32_128, grid, dim3(fdma::NT), 0, s, ac, as,
-                       ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, n_all, c);
+  hipLaunchKernelGGL(OUT_BF16 ? k_gemm_fwd_dma_bf16_128 : k_gemm_fwd_dma_f32_128, grid, dim3(fdma::NT), 0, s, ac, as,
+                     ats, apg, bc, bs, bts, off, E, M, N, K, n_nt, n_all, c);
 }
 
-// Configuration choice (MOE4_FWD_TILE overrides, for tuning): 0 = 128x128
-// register-staged (2 blocks/CU), 1 = 256x256, 2 = 128x256, 8 = direct-to-LDS
-// 256x256, 9 = direct-to-LDS 128x128 (2 blocks/CU), 10 = warp-specialised
-// persistent 128x128, 11 = warp-specialised persistent 128x256 (the default
-// when K % 256 == 0 and N % 256 == 0; 10 when K % 256 == 0 and N % 128 == 0;
-// else 9 when K % 256 == 0, else 0).
-static int fwd_tile_choice() {
-  static int v = [] {
-    const char* e = getenv("MOE4_FWD_TILE");
-    return e ? atoi(e) : 11;
-  }();
-  return v;
-}
-
+// Kernel choice: 11 = warp-specialised persistent 128x256 (K % 256 == 0 and
+// N % 256 == 0), 10 = the same with 128x128 tiles (N % 128 == 0), both with
+// 32-bit operand offsets and tile indices; else 9 = direct-to-LDS 128x128
+// (2 blocks/CU) when K % 256 == 0; else 0 = 128x128 register-staged.
 static int cu_count_f() {
   static int n[64] = {0};
   int dev = 0;
@@ -890,13 +875,12 @@ static int cu_count_f() {
 }
 
 static int fwd_choice(int64_t M, int64_t N, int64_t K) {
-  int choice = fwd_tile_choice();
-  if (choice == 11 && N % 256 != 0) choice = 10;
+  int choice = N % 256 == 0 ? 11 : 10;
   // the persistent kernels' 32-bit operand offsets and tile indices
   if ((choice == 10 || choice == 11) &&
       (N % 128 != 0 || M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31)))
     choice = 9;
-  if ((choice == 8 || choice == 9 || choice == 10 || choice == 11) && K % fdma::BKE != 0) choice = 0;
+  if (K % fdma::BKE != 0) choice = 0;
   return choice;
 }
 
@@ -915,19 +899,11 @@ static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, cons
                        as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
     return;
   }
-  if (choice == 8) {
-    launch_fwd_dma<OUT_BF16, 256, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
-    return;
-  }
   if (choice == 9) {
     launch_fwd_dma<OUT_BF16, 128, 128, 2>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
     return;
   }
-  switch (choice) {
-    case 1: launch_fwd_t<OUT_BF16, 256, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
-    case 2: launch_fwd_t<OUT_BF16, 128, 256, 1>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
-    default: launch_fwd_t<OUT_BF16, 128, 128, 2>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c); break;
-  }
+  launch_fwd_t<OUT_BF16, 128, 128, 2>(s, ac, as, ats, apg, bc, bs, bts, off, E, M, N, K, c);
 }
 
 }  // namespace moe4

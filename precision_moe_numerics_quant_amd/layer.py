@@ -107,8 +107,11 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
                 payload=payload)
 
 
-def backward(fw, dy, seed=1, layer=0, timer=None):
-    """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, dg, dlogits, ...)."""
+def backward(fw, dy, seed=1, layer=0, timer=None, skip_empty_dw=False):
+    """dy [T, d] bf16 -> dict(dx [T, d] bf16, dW_up [E, F, d] fp32, dW_down [E, d, F] fp32, dg, dlogits, ...).
+    skip_empty_dw: the weight gradients of experts that received no token are
+    left unwritten (their gradient is zero; dW[e] holds a value iff
+    route off[e + 1] > off[e]) instead of being filled with zeros."""
     T, d, F, E, k = fw["dims"]
     r = fw["route"]
     mpr = max_padded_rows(T * k, E)
@@ -121,7 +124,7 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
             return wq[name], None
         return mxfp8_requant_sr_T(*w, goff, goff, True, seed, sid(role), max_pr=rows), True
     hq, xp = fw["hq"], fw["xq_perm"]
-    return _backward_chain(fw, dy, timer, dict(
+    return _backward_chain(fw, dy, timer, skip_empty_dw, dict(
         wdT=lambda: wreq("wdT", wq["wd"], wq["off_d"], ROLE_WDOWN, E * d),
         hT=lambda: (mxfp8_requant_sr_T(*hq, r["off"], r["off_pad"], True, seed, sid(ROLE_H), max_pr=mpr,
                                        sf_layout=SF_BLOCKS), True),
@@ -130,7 +133,7 @@ def backward(fw, dy, seed=1, layer=0, timer=None):
                                        max_pr=mpr, sf_layout=SF_BLOCKS), True)))
 
 
-def _backward_chain(fw, dy, timer, req):
+def _backward_chain(fw, dy, timer, skip_empty_dw, req):
     """The backward calls in order; req[name]() gives the transposed MXFP8
     operand 'wdT', 'hT', 'wuT' or 'xT' and whether a library call made it
     (for the timer)."""
@@ -155,7 +158,8 @@ def _backward_chain(fw, dy, timer, req):
     dH = moe_grouped_gemm_bwd_dgrad(dy_row[0], dy_row[1], wdT[0], wdT[1], r["off"])
     _tick(timer, "B3 down dgrad (MXFP8)")
     hT = get("hT", "B4 H requant SR-T")
-    dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F)
+    dW_down = moe_grouped_gemm_bwd_wgrad(dy_col[0], dy_col[1], hT[0], hT[1], r["off_pad"], d, F,
+                                         skip_empty=skip_empty_dw)
     _tick(timer, "B5 down wgrad (MXFP8)")
     # B6: both MXFP8 copies of dU = dH * silu'(U) from one read
     q = mxfp8_quant_rows_T(dH, r["off"], r["off_pad"], dsilu_src=fw["U"], max_pr=mpr, sf_layout=SF_BLOCKS)
@@ -165,7 +169,8 @@ def _backward_chain(fw, dy, timer, req):
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")
     xT = get("xT", "B9 X requant SR-T")
-    dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d)
+    dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d,
+                                       skip_empty=skip_empty_dw)
     _tick(timer, "B10 up wgrad (MXFP8)")
     dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
     _tick(timer, "B11 un-permute sum")
@@ -228,7 +233,7 @@ def forward_mx(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=
     return dict(y=y, route=r, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k), mx=True)
 
 
-def backward_mx(fw, dy, seed=1, layer=0, timer=None):
+def backward_mx(fw, dy, seed=1, layer=0, timer=None, skip_empty_dw=False):
     """The backward of forward_mx: the requantisations read MXFP8 operands."""
     T, d, F, E, k = fw["dims"]
     r = fw["route"]
@@ -247,7 +252,7 @@ def backward_mx(fw, dy, seed=1, layer=0, timer=None):
         if pre:
             return wq[name], None
         return req(q, goff, goff, role, SF_ROWS, rows)
-    return _backward_chain(fw, dy, timer, dict(
+    return _backward_chain(fw, dy, timer, skip_empty_dw, dict(
         wdT=lambda: wreq("wdT", wq["wd"], wq["off_d"], ROLE_WDOWN, E * d),
         hT=lambda: req(fw["hq"], r["off"], r["off_pad"], ROLE_H, SF_BLOCKS, mpr),
         wuT=lambda: wreq("wuT", wq["wu"], wq["off_f"], ROLE_WUP, E * F),

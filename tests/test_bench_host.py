@@ -78,3 +78,31 @@ def test_work_table_matches_the_formulas():
     assert abs(t["B5 down wgrad (MXFP8)"][2] - wg) / wg < 1e-12
     assert abs(t["B10 up wgrad (MXFP8)"][2] - wg) / wg < 1e-12
     assert t["F9 combine"][1] == T * k * d * 4 + T * d * 2 + T * k * 8   # Yp rows, y, gates + indices
+
+
+def test_wgrad_work_counts_only_active_experts():
+    """The weight gradients of experts without tokens are not written: the
+    wgrad's algorithmic bytes count the active experts' dW only."""
+    c = synth.CONFIGS[4]
+    E, d, F = c["E"], c["d"], c["F"]
+    counts = np.zeros(E, dtype=np.int64)
+    counts[:100] = c["T"] * c["k"] // 100
+    counts[0] += c["T"] * c["k"] - counts.sum()
+    off = np.concatenate([[0], np.cumsum(counts)])
+    off_pad = np.concatenate([[0], np.cumsum((counts + 31) // 32 * 32)])
+    t = bench.work_table(c, off, off_pad)
+    wg = 100 * d * F * 4 + (d + F) * off_pad[-1] * 33 / 32
+    assert abs(t["B5 down wgrad (MXFP8)"][2] - wg) / wg < 1e-12
+
+
+def test_trace_summary_keeps_the_layer_shape_launches(tmp_path):
+    p = tmp_path / "kt.csv"
+    with open(p, "w") as f:
+        f.write("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for dur_ns in (4_000_000, 4_200_000, 7_000, 6_000):           # two layer launches, two tiny ones
+            f.write(f'KERNEL_DISPATCH,"moe4::k_encode_requant_T(float const*)",1000,{1000 + dur_ns}\n')
+        f.write('KERNEL_DISPATCH,"moe4::k_wgrad_ws256(unsigned char const*)",0,2000000\n')
+    out = bench.trace_summary(str(p))
+    row = [line for line in out.splitlines() if "k_encode_requant_T" in line][0]
+    cells = [x.strip() for x in row.strip("|").split("|")]
+    assert cells[1] == "4" and cells[2] == "2" and abs(float(cells[3]) - 4100.0) < 1e-6

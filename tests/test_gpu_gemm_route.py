@@ -234,6 +234,30 @@ def test_grouped_gemm_wgrad_skewed_xcd_ranges(M_list, N1, N2):
     gemm_tol_check(got, exact, bound, "wgrad skewed")
 
 
+@pytest.mark.parametrize("N1,N2,E", [(256, 192, 300), (64, 32, 2100)])
+def test_grouped_gemm_wgrad_skip_empty(N1, N2, E):
+    """MOE4_WGRAD_SKIP_EMPTY: experts without rows keep what dw held (a NaN
+    sentinel here), the others are byte for byte the beta = 0 result; both the
+    warp-specialized kernel and (E > 2048) the register-staged one."""
+    rng = np.random.default_rng(12)
+    M_list = rng.choice([0, 0, 0, 1, 31, 32, 33, 64, 100, 200, 257], E) if E < 1000 else rng.choice([0, 0, 1, 5], E)
+    off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
+    offp = mx.padded_offsets(off)
+    M = int(off[-1])
+    a = synth.randn((M, N1), 1.0, "cpu", 6, "dh").numpy()
+    b = synth.randn((M, N2), 1e-2, "cpu", 7, "dh").numpy()
+    ac, as_ = mx.quantize_transposed(a, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    bc, bs = mx.quantize_transposed(b, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+    args = [torch.from_numpy(t).cuda() for t in (ac, as_, bc, bs)] + [cuda_i32(offp), N1, N2]
+    full = m4.moe_grouped_gemm_bwd_wgrad(*args, beta=0.0)
+    dw = torch.full((E, N1, N2), float("nan"), dtype=torch.float32, device="cuda")
+    m4.moe_grouped_gemm_bwd_wgrad(*args, dw=dw, beta=0.0, skip_empty=True)
+    got = to_np(dw)
+    empty = M_list == 0
+    assert empty.any() and np.isnan(got[empty]).all()
+    assert_bytes_equal(got[~empty].view(np.uint32), to_np(full)[~empty].view(np.uint32), "skip-empty wgrad")
+
+
 def test_grouped_gemm_wgrad_more_experts_than_offset_staging():
     """More experts than the warp-specialized kernel stages offsets for: the
     register-staged persistent kernel takes over, same results."""
