@@ -211,7 +211,40 @@ def trace_summary(trace_csv, min_frac=0.1):
     return "\n".join(out) + "\n"
 
 
-def gpu_run(steps, warmup):
+def busy_summary(pmc_csv, kernels, n_simd=1024, n_cu=256, n_xcd=8, min_frac=0.1):
+    """MFMA and VALU utilisation per kernel from one rocprofv3 --pmc pass of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_VALU, SQ_INSTS_VALU,
+    SQ_INSTS_MFMA and GRBM_GUI_ACTIVE: over the kernel's launches at the
+    layer's shape (GRBM_GUI_ACTIVE at least min_frac of its largest),
+    MfmaUtil = MFMA busy cycles / (active cycles x SIMDs) and VALUBusy =
+    VALU-active cycles / (active cycles x CUs), as rocprofv3's derived
+    metrics define them.  The GRBM_GUI_ACTIVE a dispatch reports is the sum
+    over the chip's 8 XCDs (about 8x the kernel's cycles), so the active
+    cycles are that sum / n_xcd."""
+    import csv
+    vals = {}
+    with open(pmc_csv) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+            vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = ["| kernel | launches | MfmaUtil % | VALUBusy % | VALU insts per launch | MFMA insts per launch |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for pat in kernels:
+        rows = [v for (name, _), v in vals.items() if pat in name and "GRBM_GUI_ACTIVE" in v]
+        if not rows:
+            continue
+        top = max(v["GRBM_GUI_ACTIVE"] for v in rows)
+        rows = [v for v in rows if v["GRBM_GUI_ACTIVE"] >= min_frac * top]
+        act = sum(v["GRBM_GUI_ACTIVE"] for v in rows) / n_xcd
+        mfma = 100.0 * sum(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for v in rows) / (act * n_simd)
+        valu = 100.0 * sum(v.get("SQ_ACTIVE_INST_VALU", 0.0) for v in rows) / (act * n_cu)
+        iv = np.mean([v.get("SQ_INSTS_VALU", 0.0) for v in rows])
+        im = np.mean([v.get("SQ_INSTS_MFMA", 0.0) for v in rows])
+        out.append(f"| `{pat}` | {len(rows)} | {mfma:.1f} | {valu:.1f} | {iv:.3e} | {im:.3e} |")
+    return "\n".join(out) + "\n"
+
+
+def gpu_run(steps, warmup, layer_only=False):
     import precision_moe_numerics_quant_amd as m4
     from precision_moe_numerics_quant_amd import layer
 
@@ -263,6 +296,8 @@ def gpu_run(steps, warmup):
         prev = ev
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
+    if layer_only:          # (profiling runs: the layer's launches only)
+        return c, ms_step, wall, per, off, off_pad, None, None, None, None
     zero_fill = wgrad_zero_fill_bench(fw, bw, c, off)
     payload = combine_payload_bench(fw, c)
     small = small_configs_bench(inp, fw["wq"])
@@ -271,7 +306,7 @@ def gpu_run(steps, warmup):
     def step_mx(t=None):
         fw = layer.forward_mx(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, inp["bias"], timer=t,
                               seed=synth.SR_SEED)
-        layer.backward_mx(fw, inp["dy"], seed=synth.SR_SEED, timer=t)
+        layer.backward_mx(fw, inp["dy"], seed=synth.SR_SEED, timer=t, skip_empty_dw=True)
     for _ in range(warmup):
         step_mx()
     torch.cuda.synchronize()
@@ -529,19 +564,28 @@ def main():
                     help="print the traffic summary of two rocprofv3 --pmc csv files and exit (no GPU)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace csv and exit (no GPU)")
+    ap.add_argument("--busy-summary", nargs="+", metavar="ARG",
+                    help="PMC_CSV KERNEL...: print MFMA / VALU utilisation per kernel and exit (no GPU)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time the layer step only and print its line (for profiler runs: no other workloads)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary), end="")
         return
+    if args.busy_summary:
+        print(busy_summary(args.busy_summary[0], args.busy_summary[1:]), end="")
+        return
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary), end="")
-        print(f"- source_sha256 = {source_sha256(PMC_PROFILE[args.pmc_summary[2]][1])}")
+        if args.pmc_summary[2] in PMC_PROFILE:
+            print(f"- source_sha256 = {source_sha256(PMC_PROFILE[args.pmc_summary[2]][1])}")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small, zero_fill = gpu_run(args.steps, args.warmup)
+    c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill = gpu_run(args.steps, args.warmup,
+                                                                                  args.layer_only)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
     calls = {}
@@ -616,24 +660,28 @@ def main():
         # over its data-movement calls (F5, F9, B11, B12): bytes / time
         "quantizer_gbps": round(pool["q"][0] / (pool["q"][1] * 1e-3) / 1e9, 1),
         "data_movement_gbps": round(pool["m"][0] / (pool["m"][1] * 1e-3) / 1e9, 1),
-        "wgrad_zero_fill": zero_fill,
         "breakdown": calls,
         "roofline": roof,
-        "quantizer_microbench": quantizer_microbench(),
-        # the same layer with an MXFP8 forward (the pages' higher-precision
-        # layers, and their full-MXFP8 baseline): whole step, and per call (ms)
-        "mxfp8_forward_variant": {
-            "ms_per_step": round(ms_mx, 3),
-            "value": round(step_gemm_flops / (ms_mx * 1e-3) / 1e12, 2),
-            "fwd_gemm_tflops": {n: round(2.0 * c["T"] * c["k"] * c["d"] * c["F"] / (per_mx[n] * 1e-3) / 1e12, 1)
-                                for n in ("F6 up GEMM (MXFP8)", "F8 down GEMM (MXFP8)") if n in per_mx},
-            "breakdown_ms": per_mx,
-        },
-        # the combine fed by the 8.25-bit payload the pages send back between GPUs
-        "combine_payload_8p25": payload,
-        # the small workloads: weight streaming (RL-shaped forward) and launch latency (tiny layer)
-        **small,
     }
+    if not args.layer_only:
+        ms_mx, per_mx = mxv
+        out.update({
+            "wgrad_zero_fill": zero_fill,
+            "quantizer_microbench": quantizer_microbench(),
+            # the same layer with an MXFP8 forward (the pages' higher-precision
+            # layers, and their full-MXFP8 baseline): whole step, and per call (ms)
+            "mxfp8_forward_variant": {
+                "ms_per_step": round(ms_mx, 3),
+                "value": round(step_gemm_flops / (ms_mx * 1e-3) / 1e12, 2),
+                "fwd_gemm_tflops": {n: round(2.0 * c["T"] * c["k"] * c["d"] * c["F"] / (per_mx[n] * 1e-3) / 1e12, 1)
+                                    for n in ("F6 up GEMM (MXFP8)", "F8 down GEMM (MXFP8)") if n in per_mx},
+                "breakdown_ms": per_mx,
+            },
+            # the combine fed by the 8.25-bit payload the pages send back between GPUs
+            "combine_payload_8p25": payload,
+            # the small workloads: weight streaming (RL-shaped forward) and launch latency (tiny layer)
+            **small,
+        })
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:
