@@ -299,6 +299,7 @@ def gpu_run(steps, warmup, layer_only=False):
     if layer_only:          # (profiling runs: the layer's launches only)
         return c, ms_step, wall, per, off, off_pad, None, None, None, None
     zero_fill = wgrad_zero_fill_bench(fw, bw, c, off)
+    router_r = router_bench(inp, fw, bw, c)
     payload = combine_payload_bench(fw, c)
     small = small_configs_bench(inp, fw["wq"])
     del fw, bw
@@ -325,7 +326,7 @@ def gpu_run(steps, warmup, layer_only=False):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
-    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, small, zero_fill
+    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, (small, router_r), zero_fill
 
 
 def _median_ms(fn, reps):
@@ -338,6 +339,32 @@ def _median_ms(fn, reps):
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))
     return float(np.median(ts))
+
+
+def router_bench(inp, fw, bw, c, reps=20):
+    """The BF16 router in front of the layer (not part of the step, whose
+    logits are an input): its GEMM on the step's x with [384, 4096] bf16
+    weights, the un-permuting sum with the router's input gradient against the
+    plain one, and the router's weight gradient, on the step's dXp, dlogits
+    and routing (median of reps each)."""
+    import precision_moe_numerics_quant_amd as m4
+    T, d, E, k = c["T"], c["d"], c["E"], c["k"]
+    g = torch.Generator(device="cuda").manual_seed(7)
+    w = (torch.randn((E, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    r = fw["route"]
+    x, dXp, dl = inp["x"], bw["dXp"], bw["dlogits"]
+    t_g = _median_ms(lambda: m4.moe_router_logits(x, w), reps)
+    t_u = _median_ms(lambda: m4.moe_unpermute_sum(dXp, r["inv_perm"], T, k), reps)
+    t_ur = _median_ms(lambda: m4.moe_unpermute_sum_router(dXp, r["inv_perm"], T, k, dl, r["idx"], w), reps)
+    t_w = _median_ms(lambda: m4.moe_router_wgrad(x, dl, r["perm"], r["off"], k), reps)
+    fl = 2.0 * T * E * d
+    wbytes = T * k * d * 2.0 + E * d * 4.0 + T * k * 8.0       # routed x rows, dW_r, perm + dz
+    return {"workload": f"x [{T}, {d}] bf16, W_r [{E}, {d}] bf16, top-{k}",
+            "gemm": {"ms": round(t_g, 4), "TFLOPs": round(fl / t_g / 1e9, 1),
+                     "frac_peak": round(fl / t_g / 1e9 / (PEAK_F16 / 1e12), 4)},
+            "unpermute_plus_router_dx_ms": round(t_ur, 4), "unpermute_ms": round(t_u, 4),
+            "wgrad": {"ms": round(t_w, 4), "GBps": round(wbytes / t_w / 1e6, 1),
+                      "frac_hbm": round(wbytes / t_w / 1e6 / (PEAK_HBM / 1e9), 4)}}
 
 
 def wgrad_zero_fill_bench(fw, bw, c, off, reps=10):
@@ -680,7 +707,8 @@ def main():
             # the combine fed by the 8.25-bit payload the pages send back between GPUs
             "combine_payload_8p25": payload,
             # the small workloads: weight streaming (RL-shaped forward) and launch latency (tiny layer)
-            **small,
+            **small[0],
+            "router_bf16": small[1],
         })
     if args.copy_calibration:
         copy_calibration()

@@ -541,6 +541,47 @@ int moe_hmx8_dequant(const int8_t* codes, const uint8_t* scales, int64_t rows, i
 int moe_combine_hmx8(const int8_t* codes, const uint8_t* scales, const float* gates, const int32_t* inv_perm,
                      int64_t T, int32_t k, int64_t d, uint16_t* y, void* stream);
 
+/* ------------------------------------------------------------------ router */
+/*
+ * The router in front of the expert layer, read as a linear map in BF16: the
+ * pages route each token to 8 of 384 experts (fourweekmba.com page,
+ * "Update") and keep some activations in BF16 (lhc.media page, paragraph on
+ * the precisions that remain); the router's arithmetic is not on the pages.
+ *
+ * moe_router_logits - logits [T, E] float32 = x [T, d] bf16 . w [E, d]^T bf16,
+ * bf16 MFMA with float32 accumulation.  d % 64 == 0; x and w 16-byte aligned;
+ * buffers the caller's.
+ */
+int moe_router_logits(const uint16_t* x, const uint16_t* w, int64_t T, int32_t E, int64_t d, float* logits,
+                      void* stream);
+
+/*
+ * moe_unpermute_sum_router - moe_unpermute_sum with the router's input
+ * gradient added: for token t, column c, with e_j = topk_idx[t, j] and
+ * dz_j = dlogits[t, e_j] (moe_route_backward's output),
+ *   acc = 0; for j = 0..k-1: acc = fl(acc + dxp[inv_perm[t*k+j], c]);
+ *   for j = 0..k-1: acc = fl(acc + fl(dz_j * w[e_j, c]));  dx[t, c] = bf16(acc)
+ * (float32, no fused multiply-add).  dxp [T*k, d] float32 (16-byte aligned),
+ * dlogits [T, E] float32, topk_idx [T, k], w [E, d] bf16 and dx [T, d] bf16
+ * (8-byte aligned).  1 <= k <= min(E, 16), d % 4 == 0.  Out-of-range rows or
+ * experts are clamped and reported (MOE4_DEVERR_INDEX).
+ */
+int moe_unpermute_sum_router(const float* dxp, const int32_t* inv_perm, int64_t T, int32_t k, int64_t d,
+                             const float* dlogits, const int32_t* topk_idx, int32_t E, const uint16_t* w,
+                             uint16_t* dx, void* stream);
+
+/*
+ * moe_router_wgrad - dw [E, d] float32: dw[e, c] = sum over the rows r of
+ * expert e (expert_off from moe_route_topk; t = perm[r] / k) of
+ * dlogits[t, e] * x[t, c].  Float32 sums in a fixed order (each of 16
+ * interleaved row shares in row order, then the 16 shares in order):
+ * deterministic; experts without rows get zeros.  x [T, d] bf16 (8-byte
+ * aligned), dlogits [T, E], perm [T*k], dw 16-byte aligned.
+ * 1 <= k <= E, d % 4 == 0.
+ */
+int moe_router_wgrad(const uint16_t* x, const float* dlogits, const int32_t* perm, const int32_t* expert_off,
+                     int64_t T, int32_t E, int32_t k, int64_t d, float* dw, void* stream);
+
 /*
  * moe_silu_eval - correctly rounded float32 silu(u) and silu'(u) of bf16 u
  * (either output may be NULL).  Test aid for the activation fused into

@@ -76,6 +76,11 @@ _SIGS = {
     "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_unpermute_sum": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
     "moe_silu_eval": (_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_router_logits": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p]),
+    "moe_unpermute_sum_router": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                        _c_void_p, _c_void_p]),
+    "moe_router_wgrad": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
+                                _c_void_p]),
     "mxfp8_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _u64, _u32, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p]),
     "moe_grouped_gemm_fwd_silu_amax": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p,
@@ -542,6 +547,48 @@ def moe_route_backward(dg, gates, topk_idx, E):
     rc = lib().moe_route_backward(_p(dg), _p(gates), _p(topk_idx), T, E, k, _p(out), _stream())
     _check(rc, "moe_route_backward")
     return out
+
+
+# -------------------------------------------------------------------- router
+
+def moe_router_logits(x, w):
+    """BF16 router GEMM: x [T, d] bf16, w [E, d] bf16 -> logits [T, E] float32."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w, torch.bfloat16, "w")
+    T, d = x.shape
+    E = w.shape[0]
+    out = _empty((T, E), torch.float32, x)
+    rc = lib().moe_router_logits(_p(x), _p(w), T, E, d, _p(out), _stream())
+    _check(rc, "moe_router_logits")
+    return out
+
+
+def moe_unpermute_sum_router(dxp, inv_perm, T, k, dlogits, topk_idx, w):
+    """dx [T, d] bf16: the un-permuting sum of dxp plus the router's input
+    gradient sum_j dlogits[t, e_j] * w[e_j] (see moe4.h for the order)."""
+    _dev(dxp, torch.float32, "dxp")
+    _dev(dlogits, torch.float32, "dlogits")
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(w, torch.bfloat16, "w")
+    d = dxp.shape[1]
+    E = w.shape[0]
+    dx = _empty((T, d), torch.bfloat16, dxp)
+    rc = lib().moe_unpermute_sum_router(_p(dxp), _p(inv_perm), T, k, d, _p(dlogits), _p(topk_idx), E, _p(w), _p(dx),
+                                        _stream())
+    _check(rc, "moe_unpermute_sum_router")
+    return dx
+
+
+def moe_router_wgrad(x, dlogits, perm, expert_off, k):
+    """dW_r [E, d] float32 = sum over the tokens routed to e of dlogits[t, e] * x[t]."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(dlogits, torch.float32, "dlogits")
+    T, d = x.shape
+    E = dlogits.shape[1]
+    dw = _empty((E, d), torch.float32, x)
+    rc = lib().moe_router_wgrad(_p(x), _p(dlogits), _p(perm), _p(expert_off), T, E, k, d, _p(dw), _stream())
+    _check(rc, "moe_router_wgrad")
+    return dw
 
 
 def moe4_debug_check():

@@ -20,7 +20,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe4.so")
-SOURCES = ["capi.hip", "nvfp4_quant.hip", "mxfp8.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "combine_q.hip"]
+SOURCES = ["capi.hip", "nvfp4_quant.hip", "mxfp8.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "combine_q.hip", "router.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -78,7 +78,7 @@ extern "C" int moe4_debug_check(void* stream) {
   hipError_t e = hipStreamSynchronize(as_stream(stream));
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail(MOE4_EHIP, std::string("moe4_debug_check: ") + hipGetErrorString(e));
-  const uint32_t bits = take_dev_err_nvfp4() | take_dev_err_route() | take_dev_err_combine_q();
+  const uint32_t bits = take_dev_err_nvfp4() | take_dev_err_route() | take_dev_err_combine_q() | take_dev_err_router();
   if (bits == 0) return MOE4_OK;
   std::string msg = "moe4_debug_check: device-side error";
   if (bits & MOE4_DEVERR_WAIT) msg += "; a bounded wait between workgroups gave up (that call's results are wrong)";

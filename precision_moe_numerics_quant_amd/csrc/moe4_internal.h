@@ -30,6 +30,7 @@ uint32_t take_device_word(const void* symbol);  // read, then clear if non-zero
 uint32_t take_dev_err_nvfp4();
 uint32_t take_dev_err_route();
 uint32_t take_dev_err_combine_q();
+uint32_t take_dev_err_router();
 // Test hook (moe4_debug_force_wait_timeout): bounded waits between
 // workgroups wait for a count that never arrives, with a tiny spin limit, so
 // that every wait gives up and reports MOE4_DEVERR_WAIT; kernels still exit.

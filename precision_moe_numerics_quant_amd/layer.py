@@ -25,9 +25,10 @@ import torch
 
 from . import (NVFP4_4OVER6, PRE_SILU, PRE_SILU_AMAX, SF_BLOCKS, SF_ROWS, Moe4Unsupported, max_padded_rows,
                moe_combine, moe_combine_hmx8, moe_dgates, moe_gather_rows, moe_grouped_gemm_bwd_dgrad,
-               moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_silu_amax, moe_grouped_gemm_mx, moe_hmx8_quant, moe_route_backward, moe_route_topk,
-               moe_unpermute_sum, mxfp8_quant, mxfp8_quant_requant_T, mxfp8_quant_rows_T, mxfp8_requant_mx_sr_T,
-               mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
+               moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_silu_amax, moe_grouped_gemm_mx,
+               moe_hmx8_quant, moe_route_backward, moe_route_topk, moe_router_logits, moe_router_wgrad,
+               moe_unpermute_sum, moe_unpermute_sum_router, mxfp8_quant, mxfp8_quant_requant_T, mxfp8_quant_rows_T,
+               mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
@@ -57,17 +58,25 @@ def quantize_weights(w_up, w_down, timer=None, seed=1, layer=0):
                 shape=(E, F, d))
 
 
-def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0, combine_payload=False):
+def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, layer=0, combine_payload=False,
+            router_w=None):
     """x [T, d] bf16, w_up [E, F, d] / w_down [E, d, F] fp32, logits [T, E] fp32.
     (seed, layer): the SR key of the weights' backward copies made here.
     combine_payload: send the expert outputs to the combine as the 8.25-bit
     payload (32-point Hadamard + 8-bit fixed point with an E8M0 scale per 32,
     lhc.media page, paragraph on communication) instead of float32; the
-    backward treats that quantisation as the identity."""
+    backward treats that quantisation as the identity.
+    router_w: [E, d] bf16 router weights; when given, the logits are made here
+    by the BF16 router GEMM (logits may be None) and the backward adds the
+    router's input gradient to dx and returns its weight gradient."""
     T, d = x.shape
     E, F, _ = w_up.shape
     if wq is None:
         wq = quantize_weights(w_up, w_down, timer, seed, layer)
+    if router_w is not None:
+        _tick(timer, None)
+        logits = moe_router_logits(x, router_w)
+        _tick(timer, "F0 router GEMM (BF16)")
     _tick(timer, None)
     r = moe_route_topk(logits, k, bias)
     _tick(timer, "F2-F3 route + permutation")
@@ -104,7 +113,7 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
         y = moe_combine(Yp, r["gates"], r["inv_perm"])
         _tick(timer, "F9 combine")
     return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k),
-                payload=payload)
+                payload=payload, x=x, router_w=router_w, logits=logits)
 
 
 def backward(fw, dy, seed=1, layer=0, timer=None, skip_empty_dw=False):
@@ -172,14 +181,23 @@ def _backward_chain(fw, dy, timer, skip_empty_dw, req):
     dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d,
                                        skip_empty=skip_empty_dw)
     _tick(timer, "B10 up wgrad (MXFP8)")
-    dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
-    _tick(timer, "B11 un-permute sum")
+    rw = fw.get("router_w")
+    dW_router = None
+    if rw is None:
+        dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
+        _tick(timer, "B11 un-permute sum")
     dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
     _tick(timer, "B12 gate gradient")
     dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
     _tick(timer, "B13 router backward")
+    if rw is not None:
+        # the router's input gradient joins the un-permuting sum; then its weight gradient
+        dx = moe_unpermute_sum_router(dXp, r["inv_perm"], T, k, dlogits, r["idx"], rw)
+        _tick(timer, "B11 un-permute sum (+ router input gradient)")
+        dW_router = moe_router_wgrad(fw["x"], dlogits, r["perm"], r["off"], k)
+        _tick(timer, "B14 router weight gradient")
     return dict(dx=dx, dg=dg, dlogits=dlogits, dW_up=dW_up, dW_down=dW_down, dH=dH, dXp=dXp, dy_row=dy_row,
-                dy_col=dy_col, wdT=wdT, hT=hT, du_row=du_row, du_col=du_col, wuT=wuT, xT=xT)
+                dy_col=dy_col, wdT=wdT, hT=hT, du_row=du_row, du_col=du_col, wuT=wuT, xT=xT, dW_router=dW_router)
 
 
 # ------------------------------------------------ MXFP8-forward variant

@@ -1,0 +1,129 @@
+"""The BF16 router (GPU) against the oracle: the router GEMM per element
+(1e-3 * sum|x*w| + half an ulp), the un-permuting sum with the router's input
+gradient byte for byte, the router's weight gradient per element; the layer
+with its router, teacher-forced; the router GEMM at T=16384, E=384, d=4096 on
+sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import assert_bytes_equal, bf16_from_bits, cuda_i32, gemm_tol_check, to_np
+from oracle import formats as fmt
+from oracle import layer as olayer
+from oracle import route
+from oracle import router
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import precision_moe_numerics_quant_amd as m4
+    from precision_moe_numerics_quant_amd import layer
+
+
+def _bf16_np(shape, std, seed):
+    return fmt.f64_to_bf16(np.random.default_rng(seed).standard_normal(shape) * std)
+
+
+@pytest.mark.parametrize("T,E,d", [(1, 8, 64), (300, 8, 256), (257, 384, 128), (64, 130, 192)])
+def test_router_logits_tolerance(T, E, d):
+    xb = _bf16_np((T, d), 1.0, T + d)
+    wb = _bf16_np((E, d), 0.05, E)
+    got = to_np(m4.moe_router_logits(bf16_from_bits(xb), bf16_from_bits(wb))).astype(np.float64)
+    x = fmt.bf16_to_f32(xb).astype(np.float64)
+    w = fmt.bf16_to_f32(wb).astype(np.float64)
+    gemm_tol_check(got, x @ w.T, np.abs(x) @ np.abs(w).T, "router logits")
+    assert np.array_equal(got.astype(np.float32), got)
+
+
+def test_router_logits_exact_special_case():
+    """Small-integer operands: every partial sum is exact in float32, so the
+    result equals the oracle's bit for bit whatever the summation order."""
+    rng = np.random.default_rng(3)
+    T, E, d = 200, 24, 512
+    xb = fmt.f64_to_bf16(rng.integers(-4, 5, (T, d)).astype(np.float64))
+    wb = fmt.f64_to_bf16(rng.integers(-4, 5, (E, d)).astype(np.float64) * 0.5)
+    got = to_np(m4.moe_router_logits(bf16_from_bits(xb), bf16_from_bits(wb)))
+    assert_bytes_equal(got.view(np.uint32), router.logits(xb, wb).view(np.uint32), "logits")
+
+
+def _routed(T, E, k, d, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 0] += 3.0                                      # a hot expert
+    logits[:, E - 1] -= 30.0                                 # an expert never chosen
+    idx, gates = route.topk_gates(logits, k)
+    P = route.permutation(idx, E)
+    dg = (rng.standard_normal((T, k)) * 1e-2).astype(np.float32)
+    dl = route.route_backward(dg, gates, idx, E)
+    return idx, P, dl
+
+
+@pytest.mark.parametrize("T,E,k,d", [(200, 8, 2, 256), (333, 64, 8, 128), (50, 20, 16, 64)])
+def test_unpermute_sum_router_bit_exact(T, E, k, d):
+    idx, P, dl = _routed(T, E, k, d, T)
+    rng = np.random.default_rng(T + 1)
+    dxp = rng.standard_normal((T * k, d)).astype(np.float32) * 1e-2
+    wb = _bf16_np((E, d), 0.05, E + d)
+    got = m4.moe_unpermute_sum_router(torch.from_numpy(dxp).cuda(), cuda_i32(P["inv_perm"]), T, k,
+                                      torch.from_numpy(dl).cuda(), cuda_i32(idx), bf16_from_bits(wb))
+    want = router.unpermute_sum_router(dxp, P["inv_perm"], T, k, dl, idx, wb)
+    assert_bytes_equal(to_np(got), want, "dx with the router term")
+
+
+@pytest.mark.parametrize("T,E,k,d", [(200, 8, 2, 256), (1000, 64, 8, 4096), (50, 20, 16, 64)])
+def test_router_wgrad_tolerance(T, E, k, d):
+    idx, P, dl = _routed(T, E, k, d, T + 7)
+    xb = _bf16_np((T, d), 1.0, T + 9)
+    dw = m4.moe_router_wgrad(bf16_from_bits(xb), torch.from_numpy(dl).cuda(), cuda_i32(P["perm"]),
+                             cuda_i32(P["off"]), k)
+    got = to_np(dw).astype(np.float64)
+    gemm_tol_check(got, router.weight_grad(xb, dl, idx), router.weight_grad_abs_bound(xb, dl, idx), "dW_router")
+    assert not got[E - 1].any()                              # the expert no token chose
+    again = to_np(m4.moe_router_wgrad(bf16_from_bits(xb), torch.from_numpy(dl).cuda(), cuda_i32(P["perm"]),
+                                      cuda_i32(P["off"]), k))
+    assert np.array_equal(again.view(np.uint32), to_np(dw).view(np.uint32))   # deterministic
+
+
+def test_layer_with_router_teacher_forced():
+    """The tiny layer with its router: the logits per element; routing from the
+    GPU's logits, the fused dx and the router's weight gradient from the GPU's
+    dXp and dlogits (byte for byte and per element)."""
+    inp = synth.config_inputs(1, device="cpu")
+    c = synth.CONFIGS[1]
+    T, d, F, E, k = c["T"], c["d"], c["F"], c["E"], c["k"]
+    wrb = _bf16_np((E, d), 0.05, 11)
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    fw = layer.forward(dev["x"], dev["w_up"], dev["w_down"], None, k, seed=synth.SR_SEED, router_w=bf16_from_bits(wrb))
+    bw = layer.backward(fw, dev["dy"], seed=synth.SR_SEED)
+    torch.cuda.synchronize()
+    xb = synth.bf16_bits(inp["x"])
+    lg = to_np(fw["logits"])
+    x64 = fmt.bf16_to_f32(xb).astype(np.float64)
+    w64 = fmt.bf16_to_f32(wrb).astype(np.float64)
+    gemm_tol_check(lg.astype(np.float64), x64 @ w64.T, np.abs(x64) @ np.abs(w64).T, "layer logits")
+    idx, gates = route.topk_gates(lg, k)
+    P = route.permutation(idx, E)
+    assert_bytes_equal(to_np(fw["route"]["perm"]), P["perm"], "perm from the GPU's logits")
+    dXp = to_np(bw["dXp"])
+    dl = to_np(bw["dlogits"])
+    assert_bytes_equal(to_np(bw["dlogits"]).view(np.uint32),
+                       route.route_backward(to_np(bw["dg"]), gates, idx, E).view(np.uint32), "dlogits")
+    assert_bytes_equal(to_np(bw["dx"]), router.unpermute_sum_router(dXp, P["inv_perm"], T, k, dl, idx, wrb), "dx")
+    gemm_tol_check(to_np(bw["dW_router"]).astype(np.float64), router.weight_grad(xb, dl, idx),
+                   router.weight_grad_abs_bound(xb, dl, idx), "dW_router")
+    # without the router term the same dXp gives the plain un-permuting sum
+    assert not np.array_equal(to_np(bw["dx"]), olayer.unpermute_sum(dXp, P["inv_perm"], T, k))
+
+
+def test_router_logits_full_size_sampled():
+    """T = 16384, E = 384, d = 4096 in one launch; sampled rows per element."""
+    T, E, d = 16384, 384, 4096
+    x = synth.activations(T, d, "cuda", 0)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    w = (torch.randn((E, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    lg = m4.moe_router_logits(x, w)
+    rows = torch.tensor([0, 1, 127, 128, 5000, 9999, T - 1], device="cuda")
+    xs = fmt.bf16_to_f32(to_np(x[rows])).astype(np.float64)
+    w64 = fmt.bf16_to_f32(to_np(w)).astype(np.float64)
+    gemm_tol_check(to_np(lg[rows]).astype(np.float64), xs @ w64.T, np.abs(xs) @ np.abs(w64).T, "logits full size")
