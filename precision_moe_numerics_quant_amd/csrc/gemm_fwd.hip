@@ -836,6 +836,193 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
   }
 }
 
+// ------------------------------------------------ few rows per expert
+// When the experts hold a few rows each (a rollout batch: about 10 of 512
+// tokens' 8 slots per expert), the forward is bound by streaming the NVFP4
+// weights once, and a 128-row M tile would compute mostly padding.  Here the
+// weight rows take the MFMA's M side and the expert's tokens its N side, 16
+// at a time (v_mfma_f32_16x16x32_f16): workgroup (weight-row block, expert),
+// four waves of 32 weight rows (two 16-row MFMA blocks) each, all of the
+// expert's tokens in passes of 16 (an expert of 17 to 32 rows streams its
+// weights twice).  No LDS: every lane
+// loads, per K step of 256 and weight row, 32 code bytes (64 values) and the
+// dword of their four E4M3 scales, two K steps in flight; the token codes
+// (from L2: every weight-row block of the expert reads them) likewise.  Both
+// operands are dequantised exactly to f16 in registers as in the staged
+// kernels (FP4 -> f16 by the scale's power of two, times its mantissa).  K
+// order inside a step: lane group q = lane / 16 holds values 64 q .. 64 q + 63
+// of the step, and MFMA i takes 8 q .. of each group's 8 i .. 8 i + 7: the same
+// for both operands, so each MFMA sums 32 matching products.
+namespace fsk {
+constexpr int NT = 256, WB = 2, WROWS = 16 * WB, KSTEP = 256, TG = 1;   // WB 16-row blocks per wave
+}
+
+struct SkOp {          // one row's share of a K step: 64 values
+  u32x4 q[2];
+  uint32_t s;
+};
+
+__device__ inline void sk_load(SkOp& o, const uint8_t* codes, const uint8_t* sf, int64_t row, int64_t K, int64_t k0,
+                               int qg) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(codes + row * (K / 2) + k0 / 2 + 32 * qg);
+  o.q[0] = p[0];
+  o.q[1] = p[1];
+  o.s = *reinterpret_cast<const uint32_t*>(sf + row * (K / 16) + k0 / 16 + 4 * qg);
+}
+
+// The four blocks' scales of a row share: each as the float32 scale (whose
+// power of two the converter applies) and its mantissa 1.m in f16.
+struct SkScale {
+  float scf;
+  f16x2 m2;
+};
+
+// block blk's scale of a row share
+__device__ inline SkScale sk_scale(const SkOp& o, int blk) {
+  SkScale sc;
+  sc.scf = e4m3_to_f32((o.s >> (8 * blk)) & 0xFFu);
+  const _Float16 mh = (_Float16)mant_factor(sc.scf);
+  sc.m2 = f16x2{mh, mh};
+  return sc;
+}
+
+// f16 values 8 i .. 8 i + 7 of the row's 64 (block i / 2 of four, half i % 2)
+__device__ inline f16x8 sk_deq8(const SkOp& o, const SkScale& sc, int i) {
+  const float scf = sc.scf;
+  const f16x2 m2 = sc.m2;
+  const uint32_t word = o.q[i >> 2][i & 3];     // 8 values = 4 bytes
+  f16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((word >> (8 * b)) & 0xFFu, scf, 0);
+    h = h * m2;
+    r[2 * b] = h[0];
+    r[2 * b + 1] = h[1];
+  }
+  return r;
+}
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(fsk::NT, 3)
+    k_gemm_fwd_skinny(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
+                      const float* __restrict__ a_ts, int a_ts_per_group, const uint8_t* __restrict__ b_codes,
+                      const uint8_t* __restrict__ b_sf, const float* __restrict__ b_ts,
+                      const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N, int64_t K,
+                      void* __restrict__ c, uint32_t* __restrict__ silu_amax, const float* __restrict__ act_tab) {
+  using namespace fsk;
+  const int e = blockIdx.y;
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r0 = off[e], r1 = off[e + 1] < M_total ? off[e + 1] : M_total;
+  const int64_t n0 = (int64_t)blockIdx.x * ((NT / 64) * WROWS) + (int64_t)wv * WROWS;
+  if (r1 <= r0 || n0 >= N) return;                      // no tokens, or no weight rows for this wave
+  const int li = l & 15, qg = l >> 4;
+  const uint8_t* bc = b_codes + (int64_t)e * N * (K / 2);
+  const uint8_t* bs = b_sf + (int64_t)e * N * (K / 16);
+  const float sab = a_ts[a_ts_per_group ? e : 0] * b_ts[e];
+  const int64_t nks = K / KSTEP;
+  const bool amx = OUT_BF16 && silu_amax != nullptr;
+  uint32_t pmax = 0u, nlo = 0x8000u, nhi = 0u;
+  constexpr uint32_t M1 = 0x3FA4u;  // |-1.28125| in bf16: the SiLU amax split (as k_gemm_fwd_ws)
+  for (int64_t p0 = r0; p0 < r1; p0 += 16 * TG) {     // passes of 32 tokens
+    f32x4 acc[WB][TG];
+#pragma unroll
+    for (int b = 0; b < WB; ++b)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int64_t trow[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {    // token rows past the expert are clamped (never stored)
+      const int64_t r = p0 + 16 * t + li;
+      trow[t] = r < r1 ? r : r1 - 1;
+    }
+    // two register sets, named (not indexed by the step's parity, which would
+    // make the compiler select between them and wait for both)
+    SkOp wa[WB], xa[TG], wb[WB], xb[TG];
+    auto fetch = [&](SkOp (&w)[WB], SkOp (&x)[TG], int64_t k0) {
+#pragma unroll
+      for (int b = 0; b < WB; ++b) sk_load(w[b], bc, bs, n0 + 16 * b + li, K, k0, qg);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) sk_load(x[t], a_codes, a_sf, trow[t], K, k0, qg);
+    };
+    auto compute = [&](const SkOp (&w)[WB], const SkOp (&x)[TG]) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {      // the row share's four 16-value scale blocks
+        SkScale ws[WB], xs[TG];
+#pragma unroll
+        for (int b = 0; b < WB; ++b) ws[b] = sk_scale(w[b], blk);
+#pragma unroll
+        for (int t = 0; t < TG; ++t) xs[t] = sk_scale(x[t], blk);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * blk + h;
+          f16x8 xv[TG];
+#pragma unroll
+          for (int t = 0; t < TG; ++t) xv[t] = sk_deq8(x[t], xs[t], i);
+#pragma unroll
+          for (int b = 0; b < WB; ++b) {
+            const f16x8 wvv = sk_deq8(w[b], ws[b], i);
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+              acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wvv, xv[t], acc[b][t], 0, 0, 0);
+          }
+        }
+      }
+    };
+    fetch(wa, xa, 0);
+    for (int64_t ks = 0; ks < nks; ks += 2) {      // the next step in flight during each step
+      if (ks + 1 < nks) fetch(wb, xb, (ks + 1) * KSTEP);
+      compute(wa, xa);
+      if (ks + 1 >= nks) break;
+      if (ks + 2 < nks) fetch(wa, xa, (ks + 2) * KSTEP);
+      compute(wb, xb);
+    }
+    // out[token][n]: lane (li, qg) holds token li of the group and weight rows
+    // n0 + 16 b + 4 qg .. + 3: four consecutive output columns
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const int64_t row = p0 + 16 * t + li;
+      if (row >= r1) continue;
+#pragma unroll
+      for (int b = 0; b < WB; ++b) {
+        const int64_t col = n0 + 16 * b + 4 * qg;
+        const f32x4 v = acc[b][t] * sab;
+        if (OUT_BF16) {
+          const uint32_t h0 = f32_to_bf16_bits(v[0]), h1 = f32_to_bf16_bits(v[1]);
+          const uint32_t h2 = f32_to_bf16_bits(v[2]), h3 = f32_to_bf16_bits(v[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c) + row * N + col) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
+          if (amx) {
+            const uint32_t hb[4] = {h0, h1, h2, h3};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t m = hb[q] & 0x7FFFu;
+              const bool neg = hb[q] >= 0x8000u;
+              pmax = max(pmax, neg ? 0u : m);
+              nlo = min(nlo, neg && m >= M1 ? m : 0x8000u);
+              nhi = max(nhi, neg && m < M1 ? m : 0u);
+            }
+          }
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(c) + row * N + col) = v;
+        }
+      }
+    }
+  }
+  if (amx) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      pmax = max(pmax, (uint32_t)__shfl_xor((int)pmax, o, 64));
+      nlo = min(nlo, (uint32_t)__shfl_xor((int)nlo, o, 64));
+      nhi = max(nhi, (uint32_t)__shfl_xor((int)nhi, o, 64));
+    }
+    if (l == 0) {
+      float t = act_eval<false>(pmax, act_tab);
+      if (nlo < 0x8000u) t = fmaxf(t, fabsf(act_eval<false>(0x8000u | nlo, act_tab)));
+      t = fmaxf(t, fabsf(act_eval<false>(0x8000u | nhi, act_tab)));
+      atomicMax(silu_amax + e, __float_as_uint(t));
+    }
+  }
+}
+
 template <bool OUT_BF16, int BM, int BN, int MINB>
 static void launch_fwd_t(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
                          const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
@@ -874,7 +1061,11 @@ static int cu_count_f() {
   return n[dev];
 }
 
-static int fwd_choice(int64_t M, int64_t N, int64_t K) {
+// 12 = the few-rows-per-expert kernel (k_gemm_fwd_skinny): K % 256 == 0,
+// N % 64 == 0, at most 32 rows per expert on average.
+static int fwd_choice(int64_t M, int64_t N, int64_t K, int E) {
+  if (K % fsk::KSTEP == 0 && N % fsk::WROWS == 0 && M <= (int64_t)32 * E && M * (K / 2) < ((int64_t)1 << 40))
+    return 12;
   int choice = N % 256 == 0 ? 11 : 10;
   // the persistent kernels' 32-bit operand offsets and tile indices
   if ((choice == 10 || choice == 11) &&
@@ -888,7 +1079,14 @@ template <bool OUT_BF16>
 static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, const float* ats, int apg,
                        const uint8_t* bc, const uint8_t* bs, const float* bts, const int32_t* off, int E, int64_t M,
                        int64_t N, int64_t K, void* c, uint32_t* silu_amax = nullptr, const float* act_tab = nullptr) {
-  const int choice = fwd_choice(M, N, K);
+  const int choice = fwd_choice(M, N, K, E);
+  if (choice == 12) {
+    const int64_t wg_rows = (fsk::NT / 64) * fsk::WROWS;
+    const dim3 grid((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)E);
+    hipLaunchKernelGGL((k_gemm_fwd_skinny<OUT_BF16>), grid, dim3(fsk::NT), 0, s, ac, as, ats, apg, bc, bs, bts, off, E,
+                       M, N, K, c, silu_amax, act_tab);
+    return;
+  }
   if (choice == 10) {
     hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 128>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s, ac,
                        as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
@@ -951,17 +1149,18 @@ extern "C" int moe_grouped_gemm_fwd_silu_amax(const uint8_t* a_codes, const uint
   MOE4_REQUIRE(M_total == 0 || (a_codes && a_sf && c), MOE4_EINVAL, "moe_grouped_gemm_fwd_silu_amax: NULL pointer");
   MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(c), MOE4_EALIGN,
                "moe_grouped_gemm_fwd_silu_amax: misaligned pointer");
-  const int choice = fwd_choice(M_total, N, K);
-  MOE4_REQUIRE(M_total == 0 || choice == 10 || choice == 11, MOE4_EUNSUPPORTED,
-               "moe_grouped_gemm_fwd_silu_amax: needs the warp-specialised kernels (K % 256 == 0, N % 128 == 0)");
+  const int choice = fwd_choice(M_total, N, K, E);
+  MOE4_REQUIRE(M_total == 0 || choice == 10 || choice == 11 || choice == 12, MOE4_EUNSUPPORTED,
+               "moe_grouped_gemm_fwd_silu_amax: needs the warp-specialised or few-rows kernels (K % 256 == 0, "
+               "N % 128 == 0, or N % 64 == 0 with at most 32 rows per expert on average)");
+  MOE4_REQUIRE(((N + 127) / 128) * ((M_total + 127) / 128 + E) < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_silu_amax: too large");
   hipStream_t s = as_stream(stream);
   const float* tab = nullptr;
   int rc = act_tables(&tab);
   if (rc) return rc;
   hipLaunchKernelGGL(k_zero_amax, dim3((E + 255) / 256), dim3(256), 0, s, silu_amax, E);
   if (M_total == 0) return check_launch("moe_grouped_gemm_fwd_silu_amax");
-  MOE4_REQUIRE(((N + 127) / 128) * ((M_total + 127) / 128 + E) < ((int64_t)1 << 31), MOE4_EINVAL,
-               "moe_grouped_gemm_fwd_silu_amax: too large");
   launch_fwd<true>(s, a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K, c,
                    silu_amax, tab);
   return check_launch("moe_grouped_gemm_fwd_silu_amax");

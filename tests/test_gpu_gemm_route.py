@@ -73,12 +73,18 @@ def _fwd_operands(M_list, N, K, seed, ts_per_group=False):
     return off, qa, qb
 
 
+# Few rows per expert (at most 32 on average) take the weight-streaming kernel:
+# ragged experts of 0 .. 33 rows and one of 70 (three 32-token passes)
+_FEW = [0, 1, 2, 3, 5, 9, 10, 13, 16, 17, 31, 32, 33, 70, 0, 4, 8, 12, 1, 0]
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 # (N, K) pick the kernels: 192 x 320 and 64 x 64 the register-staged one,
 # 160 x 256 the 128 x 128 direct-to-LDS one, 384 x 512 the warp-specialised
 # 128 x 128 one, 512 x 1024 the warp-specialised 128 x 256 one
 @pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([64], 64, 64), ([5, 0, 0, 257], 512, 1024),
-                                        ([5, 300, 0, 129], 160, 256), ([0, 37, 130, 1, 300], 384, 512)])
+                                        ([5, 300, 0, 129], 160, 256), ([0, 37, 130, 1, 300], 384, 512),
+                                        (_FEW, 192, 512), ([3, 12, 0, 40, 1, 19], 1536, 1024), ([1], 64, 256)])
 def test_grouped_gemm_fwd_tolerance(M_list, N, K, out_dtype):
     E = len(M_list)
     per_group = out_dtype == "f32"
@@ -97,19 +103,19 @@ def test_grouped_gemm_fwd_tolerance(M_list, N, K, out_dtype):
     gemm_tol_check(got, exact, bound, "fwd", out_bf16=out_dtype == "bf16")
 
 
-def test_grouped_gemm_fwd_exact_special_case():
+@pytest.mark.parametrize("E,N,K,M_list", [(3, 64, 128, [50, 0, 90]), (4, 128, 256, [7, 0, 20, 33])])
+def test_grouped_gemm_fwd_exact_special_case(E, N, K, M_list):
     """Codes in {0, +-0.5, +-1, +-2} with power-of-two scales and small K keep
-    every partial sum exact in float32: the GPU result equals the exact one."""
+    every partial sum exact in float32: the GPU result equals the exact one
+    (the second case takes the few-rows-per-expert kernel)."""
     rng = np.random.default_rng(3)
-    E, N, K = 3, 64, 128
-    M_list = [50, 0, 90]
     off = np.concatenate([[0], np.cumsum(M_list)])
     M = off[-1]
     small = np.array([0, 1, 2, 4, 8, 9, 10, 12])     # codes of 0, .5, 1, 2, -0, -.5, -1, -2
     qa = rng.choice(small, (M, K)); qb = rng.choice(small, (E * N, K))
     sa = rng.choice([0x38, 0x30, 0x40], (M, K // 16)).astype(np.uint8)         # 1, .5, 2
     sb = rng.choice([0x38, 0x30, 0x40], (E * N, K // 16)).astype(np.uint8)
-    ta = np.float32([0.25]); tb = np.float32([1.0, 2.0, 0.5])
+    ta = np.float32([0.25]); tb = np.float32([1.0, 2.0, 0.5, 4.0][:E])
     ca, cb = nv.pack_codes(qa), nv.pack_codes(qb)
     c = m4.moe_grouped_gemm_fwd(torch.from_numpy(ca).cuda(), torch.from_numpy(sa).cuda(), torch.from_numpy(ta).cuda(),
                                 torch.from_numpy(cb).cuda().view(E, N, K // 2), torch.from_numpy(sb).cuda().view(E, N, K // 16),
@@ -338,7 +344,8 @@ def test_grouped_gemm_mx_bf16_and_f32(M_list, N, K):
 
 
 @pytest.mark.parametrize("M_list,N,K", [([300, 0, 37, 1, 129], 256, 512), ([5, 64, 200], 384, 256),
-                                        ([1000, 3], 1536, 1024)])
+                                        ([1000, 3], 1536, 1024), ([3, 12, 0, 40, 1, 19], 256, 512),
+                                        (_FEW, 192, 512)])
 def test_fwd_silu_amax_epilogue_matches_separate_pass(M_list, N, K):
     """moe_grouped_gemm_fwd_silu_amax (SiLU amax per expert folded into the up
     GEMM's epilogue) gives the same U, and nvfp4_quant_46 with PRE_SILU_AMAX on
@@ -360,9 +367,10 @@ def test_fwd_silu_amax_epilogue_matches_separate_pass(M_list, N, K):
 
 
 def test_fwd_silu_amax_unsupported_shape():
-    off, qa, qb = _fwd_operands([40, 24], 96, 256, seed=5)      # N % 128 != 0: not the warp-specialised kernels
+    # K % 256 != 0: neither the warp-specialised nor the few-rows kernels
+    off, qa, qb = _fwd_operands([40, 24], 96, 320, seed=5)
     with pytest.raises(m4.Moe4Unsupported):
         m4.moe_grouped_gemm_fwd_silu_amax(
             torch.from_numpy(qa["codes"]).cuda(), torch.from_numpy(qa["sf"]).cuda(), torch.from_numpy(qa["ts"]).cuda(),
-            torch.from_numpy(qb["codes"]).cuda().view(2, 96, 128), torch.from_numpy(qb["sf"]).cuda().view(2, 96, 16),
+            torch.from_numpy(qb["codes"]).cuda().view(2, 96, 160), torch.from_numpy(qb["sf"]).cuda().view(2, 96, 20),
             torch.from_numpy(qb["ts"]).cuda(), cuda_i32(off))
