@@ -468,6 +468,15 @@ def combine_payload_bench(fw, c, reps=20):
     t_q = timed(lambda: m4.moe_hmx8_quant(Yp))
     t_c = timed(lambda: m4.moe_combine_hmx8(codes, sf, r["gates"], r["inv_perm"]))
     t_f = timed(lambda: m4.moe_combine(Yp, r["gates"], r["inv_perm"]))
+    # the down GEMM alone and with the payload written by its epilogue
+    hq, (wd_c, wd_s, wd_t) = fw["hq"], fw["wq"]["wd"]
+    E, F = c["E"], c["F"]
+    dargs = (hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t, r["off"])
+    t_g = timed(lambda: m4.moe_grouped_gemm_fwd(*dargs, torch.float32, a_ts_per_group=True))
+    try:
+        t_gh = timed(lambda: m4.moe_grouped_gemm_fwd_hmx8(*dargs, a_ts_per_group=True))
+    except m4.Moe4Unsupported:
+        t_gh = None
     pay = A * d * (1 + 1 / 32)
     b_q = A * d * 4 + pay
     b_c = pay + A * 8 + T * d * 2
@@ -478,7 +487,9 @@ def combine_payload_bench(fw, c, reps=20):
 
     return {"bits_per_value": 8.0 * pay / (A * d), "payload_bytes": int(pay), "float32_bytes": A * d * 4,
             "bf16_bytes": A * d * 2, "quant": rate(b_q, t_q), "combine_from_payload": rate(b_c, t_c),
-            "float32_combine": rate(b_f, t_f)}
+            "float32_combine": rate(b_f, t_f), "down_gemm_ms": round(t_g, 4),
+            "down_gemm_with_payload_ms": None if t_gh is None else round(t_gh, 4),
+            "payload_in_epilogue_extra_ms": None if t_gh is None else round(t_gh - t_g, 4)}
 
 
 def quantizer_microbench(reps=20):

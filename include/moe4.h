@@ -541,6 +541,23 @@ int moe_hmx8_dequant(const int8_t* codes, const uint8_t* scales, int64_t rows, i
 int moe_combine_hmx8(const int8_t* codes, const uint8_t* scales, const float* gates, const int32_t* inv_perm,
                      int64_t T, int32_t k, int64_t d, uint16_t* y, void* stream);
 
+/*
+ * moe_grouped_gemm_fwd_hmx8 - moe_grouped_gemm_fwd with float32 output c
+ * [M_total, N] whose epilogue also writes the combine-path payload of the
+ * stored values: codes int8 [M_total, N] and scales uint8 [M_total, N/32],
+ * byte for byte those of moe_hmx8_quant(c).  The down projection's output and
+ * its communication format in one pass (lhc.media page, paragraphs on fused
+ * kernels and on communication).  The three buffers are the caller's (device
+ * memory); c 16-byte aligned.  Returns MOE4_EUNSUPPORTED (nothing launched)
+ * unless the shape selects the warp-specialised kernels (K % 256 == 0,
+ * N % 128 == 0, more than 32 rows per expert on average), MOE4_EINVAL if
+ * M_total * N >= 2^32.
+ */
+int moe_grouped_gemm_fwd_hmx8(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts, int a_ts_per_group,
+                              const uint8_t* b_codes, const uint8_t* b_sf, const float* b_ts,
+                              const int32_t* expert_off, int32_t E, int64_t M_total, int64_t N, int64_t K, float* c,
+                              int8_t* codes, uint8_t* scales, void* stream);
+
 /* ------------------------------------------------------------------ router */
 /*
  * The router in front of the expert layer, read as a linear map in BF16: the

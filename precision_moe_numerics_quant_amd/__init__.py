@@ -89,6 +89,9 @@ _SIGS = {
     "moe_hmx8_dequant": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p]),
     "moe_combine_hmx8": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p,
                                 _c_void_p]),
+    "moe_grouped_gemm_fwd_hmx8": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _i32, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -417,6 +420,22 @@ def moe_grouped_gemm_fwd_silu_amax(a_codes, a_sf, a_ts, b_codes, b_sf, b_ts, exp
                                               _stream())
     _check(rc, "moe_grouped_gemm_fwd_silu_amax")
     return c, ws
+
+
+def moe_grouped_gemm_fwd_hmx8(a_codes, a_sf, a_ts, b_codes, b_sf, b_ts, expert_off, a_ts_per_group=False):
+    """moe_grouped_gemm_fwd with float32 C, plus C's combine-path payload written by the
+    same epilogue.  Raises Moe4Unsupported when the shape selects other kernels.
+    -> (C, codes int8 [M, N], scales uint8 [M, N/32])"""
+    M, Kh = a_codes.shape
+    E, N, _ = b_codes.shape
+    c = _empty((M, N), torch.float32, a_codes)
+    codes = _empty((M, N), torch.int8, a_codes)
+    sf = _empty((M, N // 32), torch.uint8, a_codes)
+    rc = lib().moe_grouped_gemm_fwd_hmx8(_p(a_codes), _p(a_sf), _p(a_ts), int(a_ts_per_group), _p(b_codes),
+                                         _p(b_sf), _p(b_ts), _p(expert_off), E, M, N, 2 * Kh, _p(c), _p(codes),
+                                         _p(sf), _stream())
+    _check(rc, "moe_grouped_gemm_fwd_hmx8")
+    return c, codes, sf
 
 
 def moe_grouped_gemm_bwd_dgrad(a_codes, a_sf, b_codes, b_sf, expert_off):

@@ -593,13 +593,63 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (
 constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
 }  // namespace fws
 
-template <bool OUT_BF16, int TN>
+// ds_swizzle in bit-mask mode: the value of lane (l ^ d) within each group of
+// 32 lanes (d < 32)
+template <int D>
+__device__ inline float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1F));
+}
+
+// The combine-path payload of one stored value y: the 32 lanes of a half-wave
+// hold one row's 32-column block (lane li = its column li).  Writes the lane's
+// int8 code at hv + hs and, from lane 0, the block's E8M0 byte at sv + ss
+// (v: the per-lane part of the offset, s: the wave-uniform part).
+__device__ inline void hmx8_value(float y, int li, __amdgpu_buffer_rsrc_t rH, __amdgpu_buffer_rsrc_t rS, uint32_t hv,
+                                  uint32_t hs, uint32_t sv, uint32_t ss) {
+  float o;
+  o = swz_xor<1>(y);
+  y = (li & 1) ? o - y : y + o;
+  o = swz_xor<2>(y);
+  y = (li & 2) ? o - y : y + o;
+  o = swz_xor<4>(y);
+  y = (li & 4) ? o - y : y + o;
+  o = swz_xor<8>(y);
+  y = (li & 8) ? o - y : y + o;
+  o = swz_xor<16>(y);
+  y = (li & 16) ? o - y : y + o;
+  float am = fabsf(y);
+  am = fmaxf(am, swz_xor<1>(am));
+  am = fmaxf(am, swz_xor<2>(am));
+  am = fmaxf(am, swz_xor<4>(am));
+  am = fmaxf(am, swz_xor<8>(am));
+  am = fmaxf(am, swz_xor<16>(am));
+  int ex = -127;
+  if (am > 0.0f) {
+    ex = __builtin_amdgcn_frexp_expf(am) - 1;
+    ex = ex < -127 ? -127 : ex;
+  }
+  float r = __builtin_rintf(__builtin_amdgcn_ldexpf(y, 6 - ex));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)((int)r & 0xFF), rH, hv, hs, 0);
+  if (li == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(ex + 127), rS, sv, ss, 0);
+}
+
+// HMX8 (float32 output only): the epilogue also writes the combine-path
+// payload of the stored values: per row and 32-column block, the Sylvester
+// H_32 transform as five butterfly stages across the block's 32 lanes
+// (partner distance 1, 2, 4, 8, 16; the lower position keeps a + b, the upper
+// a - b), the block's E8M0 exponent floor(log2 max|y|) (-127 for zeros) and
+// int8 codes rne(y 2^(6 - e)) clamped to +-127: the steps and float32
+// roundings of moe_hmx8_quant, byte for byte.
+template <bool OUT_BF16, int TN, bool HMX8 = false>
 __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
                   int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                   const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,
                   int64_t K, void* __restrict__ c, uint32_t* __restrict__ silu_amax,
-                  const float* __restrict__ act_tab) {
+                  const float* __restrict__ act_tab, int8_t* __restrict__ hcodes = nullptr,
+                  uint8_t* __restrict__ hsf = nullptr) {
+  static_assert(!HMX8 || !OUT_BF16, "the combine-path payload is made from the float32 output");
   using namespace fws;
   using fdma::lds_ptr;
   using fdma::swz;
@@ -742,6 +792,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
   const uint32_t ld = (uint32_t)N * ESZ;  // output row pitch in bytes
   const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * ESZ;
+  const uint32_t h_lane = (uint32_t)(g * 4) * (uint32_t)N + (uint32_t)li, s_lane = (uint32_t)(g * 4) * (uint32_t)(N / 32);
   MtCursor<TM> cur;
   uint32_t gs = 0;
   for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
@@ -778,6 +829,10 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     // then one atomic maximum per wave and tile.
     constexpr uint32_t M1 = 0x3FA4u;  // |-1.28125| in bf16
     const bool amx = OUT_BF16 && silu_amax != nullptr && active;
+    // (HMX8) the payload's codes and scale bytes of the tile's rows
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(HMX8 ? hcodes + row0 * N : nullptr, HMX8 ? (uint64_t)nrows * N : 0);
+    const __amdgpu_buffer_rsrc_t rS =
+        make_rsrc(HMX8 ? hsf + row0 * (N / 32) : nullptr, HMX8 ? (uint64_t)nrows * (N / 32) : 0);
     uint32_t pmax = 0u, nlo = 0x8000u, nhi = 0u;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -793,6 +848,10 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
               __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(x), rC, lane_off, so, 2);
             else
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rC, lane_off, so, 2);
+            if constexpr (HMX8) {
+              const uint32_t r = (uint32_t)(wm + i * 32 + (v >> 2) * 8 + (v & 3)), c0 = (uint32_t)(n0 + wn + j * 32);
+              hmx8_value(x, li, rH, rS, h_lane, r * (uint32_t)N + c0, s_lane, r * (uint32_t)(N / 32) + c0 / 32);
+            }
           }
         }
       }
@@ -846,7 +905,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
 // expert's tokens in passes of 16 (an expert of 17 to 32 rows streams its
 // weights twice).  No LDS: every lane
 // loads, per K step of 256 and weight row, 32 code bytes (64 values) and the
-// dword of their four E4M3 scales, two K steps in flight; the token codes
+// dword of their four E4M3 scales, the next K step in flight; the token codes
 // (from L2: every weight-row block of the expert reads them) likewise.  Both
 // operands are dequantised exactly to f16 in registers as in the staged
 // kernels (FP4 -> f16 by the scale's power of two, times its mantissa).  K
@@ -1128,6 +1187,36 @@ extern "C" int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf,
   else
     launch_fwd<false>(s, a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K, c);
   return check_launch("moe_grouped_gemm_fwd");
+}
+
+extern "C" int moe_grouped_gemm_fwd_hmx8(const uint8_t* a_codes, const uint8_t* a_sf, const float* a_ts,
+                                         int a_ts_per_group, const uint8_t* b_codes, const uint8_t* b_sf,
+                                         const float* b_ts, const int32_t* expert_off, int32_t E, int64_t M_total,
+                                         int64_t N, int64_t K, float* c, int8_t* hcodes, uint8_t* hsf, void* stream) {
+  MOE4_REQUIRE(E >= 1 && M_total >= 0 && N > 0 && K > 0, MOE4_EINVAL, "moe_grouped_gemm_fwd_hmx8: bad sizes");
+  MOE4_REQUIRE(a_ts && b_codes && b_sf && b_ts && expert_off, MOE4_EINVAL, "moe_grouped_gemm_fwd_hmx8: NULL pointer");
+  MOE4_REQUIRE(M_total == 0 || (a_codes && a_sf && c && hcodes && hsf), MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_hmx8: NULL pointer");
+  MOE4_REQUIRE(aligned16(a_codes) && aligned16(b_codes) && aligned16(c), MOE4_EALIGN,
+               "moe_grouped_gemm_fwd_hmx8: misaligned pointer");
+  const int choice = fwd_choice(M_total, N, K, E);
+  MOE4_REQUIRE(M_total == 0 || choice == 10 || choice == 11, MOE4_EUNSUPPORTED,
+               "moe_grouped_gemm_fwd_hmx8: needs the warp-specialised kernels (K % 256 == 0, N % 128 == 0, more "
+               "than 32 rows per expert on average)");
+  MOE4_REQUIRE(M_total * N < ((int64_t)1 << 32), MOE4_EINVAL, "moe_grouped_gemm_fwd_hmx8: payload too large");
+  if (M_total == 0) return MOE4_OK;
+  MOE4_REQUIRE(((N + 127) / 128) * ((M_total + 127) / 128 + E) < ((int64_t)1 << 31), MOE4_EINVAL,
+               "moe_grouped_gemm_fwd_hmx8: too large");
+  hipStream_t s = as_stream(stream);
+  if (choice == 11)
+    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 256, true>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<256>::NT), 0, s,
+                       a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K,
+                       static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
+  else
+    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 128, true>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s,
+                       a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K,
+                       static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
+  return check_launch("moe_grouped_gemm_fwd_hmx8");
 }
 
 namespace moe4 {

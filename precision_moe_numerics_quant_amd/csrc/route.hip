@@ -224,22 +224,44 @@ __global__ void __launch_bounds__(256) k_dgates(const uint16_t* __restrict__ dy,
   const int l = threadIdx.x & 63;
   if (t >= T) return;
   const uint16_t* dyr = dy + t * d;
+  // the token's dy row is read once (kept in registers up to d = 8192) for all
+  // k slots; each lane sums its columns 8 l + 512 i in order either way
+  constexpr int DYC = 16;
+  u32x4 dyc[DYC];
+  const bool cached = d <= 512 * DYC;
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < DYC; ++i) {
+      const int64_t c = 8 * l + 512 * i;
+      dyc[i] = c < d ? *reinterpret_cast<const u32x4*>(dyr + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  auto add8 = [](float acc, const u32x4 g, const f32x4 a, const f32x4 b) {
+    acc = acc + bf16_bits_to_f32(g[0] & 0xFFFFu) * a[0];
+    acc = acc + bf16_bits_to_f32(g[0] >> 16) * a[1];
+    acc = acc + bf16_bits_to_f32(g[1] & 0xFFFFu) * a[2];
+    acc = acc + bf16_bits_to_f32(g[1] >> 16) * a[3];
+    acc = acc + bf16_bits_to_f32(g[2] & 0xFFFFu) * b[0];
+    acc = acc + bf16_bits_to_f32(g[2] >> 16) * b[1];
+    acc = acc + bf16_bits_to_f32(g[3] & 0xFFFFu) * b[2];
+    acc = acc + bf16_bits_to_f32(g[3] >> 16) * b[3];
+    return acc;
+  };
   for (int j = 0; j < k; ++j) {
     const int64_t row = clamp_index(inv[t * k + j], n_rows);
     const float* ypr = yp + row * d;
     float acc = 0.0f;
-    for (int64_t c = 8 * l; c < d; c += 512) {
-      const u32x4 g = *reinterpret_cast<const u32x4*>(dyr + c);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ypr + c);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ypr + c + 4);
-      acc = acc + bf16_bits_to_f32(g[0] & 0xFFFFu) * a[0];
-      acc = acc + bf16_bits_to_f32(g[0] >> 16) * a[1];
-      acc = acc + bf16_bits_to_f32(g[1] & 0xFFFFu) * a[2];
-      acc = acc + bf16_bits_to_f32(g[1] >> 16) * a[3];
-      acc = acc + bf16_bits_to_f32(g[2] & 0xFFFFu) * b[0];
-      acc = acc + bf16_bits_to_f32(g[2] >> 16) * b[1];
-      acc = acc + bf16_bits_to_f32(g[3] & 0xFFFFu) * b[2];
-      acc = acc + bf16_bits_to_f32(g[3] >> 16) * b[3];
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < DYC; ++i) {
+        const int64_t c = 8 * l + 512 * i;
+        if (c < d)
+          acc = add8(acc, dyc[i], *reinterpret_cast<const f32x4*>(ypr + c), *reinterpret_cast<const f32x4*>(ypr + c + 4));
+      }
+    } else {
+      for (int64_t c = 8 * l; c < d; c += 512)
+        acc = add8(acc, *reinterpret_cast<const u32x4*>(dyr + c), *reinterpret_cast<const f32x4*>(ypr + c),
+                   *reinterpret_cast<const f32x4*>(ypr + c + 4));
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);

@@ -25,7 +25,8 @@ import torch
 
 from . import (NVFP4_4OVER6, PRE_SILU, PRE_SILU_AMAX, SF_BLOCKS, SF_ROWS, Moe4Unsupported, max_padded_rows,
                moe_combine, moe_combine_hmx8, moe_dgates, moe_gather_rows, moe_grouped_gemm_bwd_dgrad,
-               moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_silu_amax, moe_grouped_gemm_mx,
+               moe_grouped_gemm_bwd_wgrad, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_hmx8,
+               moe_grouped_gemm_fwd_silu_amax, moe_grouped_gemm_mx,
                moe_hmx8_quant, moe_route_backward, moe_route_topk, moe_router_logits, moe_router_wgrad,
                moe_unpermute_sum, moe_unpermute_sum_router, mxfp8_quant, mxfp8_quant_requant_T, mxfp8_quant_rows_T,
                mxfp8_requant_mx_sr_T, mxfp8_requant_sr_T, nvfp4_quant_46, nvfp4_quant_requant_T)
@@ -100,16 +101,28 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
     else:
         hq = nvfp4_quant_46(U, NVFP4_4OVER6, r["off"], PRE_SILU_AMAX, ws=amax_ws)
     _tick(timer, "F7 SiLU + H quant (NVFP4 4/6)")
-    Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
-                              r["off"], torch.float32, a_ts_per_group=True)
-    _tick(timer, "F8 down GEMM (NVFP4)")
     payload = None
     if combine_payload:
-        payload = moe_hmx8_quant(Yp)
-        _tick(timer, "F9a Yp -> 8.25-bit payload (Hadamard + 8-bit)")
+        # the payload from F8's epilogue when the shape takes the
+        # warp-specialised kernels, else from a pass of its own
+        try:
+            Yp, h_codes, h_sf = moe_grouped_gemm_fwd_hmx8(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2),
+                                                          wd_s.view(E, d, F // 16), wd_t, r["off"],
+                                                          a_ts_per_group=True)
+            payload = (h_codes, h_sf)
+            _tick(timer, "F8+F9a down GEMM (NVFP4) + 8.25-bit payload")
+        except Moe4Unsupported:
+            Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
+                                      r["off"], torch.float32, a_ts_per_group=True)
+            _tick(timer, "F8 down GEMM (NVFP4)")
+            payload = moe_hmx8_quant(Yp)
+            _tick(timer, "F9a Yp -> 8.25-bit payload (Hadamard + 8-bit)")
         y = moe_combine_hmx8(payload[0], payload[1], r["gates"], r["inv_perm"])
         _tick(timer, "F9b combine from the payload")
     else:
+        Yp = moe_grouped_gemm_fwd(hq[0], hq[1], hq[2], wd_c.view(E, d, F // 2), wd_s.view(E, d, F // 16), wd_t,
+                                  r["off"], torch.float32, a_ts_per_group=True)
+        _tick(timer, "F8 down GEMM (NVFP4)")
         y = moe_combine(Yp, r["gates"], r["inv_perm"])
         _tick(timer, "F9 combine")
     return dict(y=y, route=r, xq=xq, xq_perm=xq_perm, U=U, hq=hq, Yp=Yp, wq=wq, dims=(T, d, F, E, k),
