@@ -103,6 +103,38 @@ def test_layer_config1_combine_payload():
     assert e_gpu < 2.0 * e_fmt + 2e-3
 
 
+def test_layer_token_permutation_equivariance_gpu():
+    """Permuting the tokens permutes y, dx, dg and dlogits bit for bit: every
+    per-token result depends on the token's own rows only (the group tensor
+    scales are maxima over sets that a permutation keeps), and the oracle's
+    layer has the same property (pinned on the CPU).  The weight gradients are
+    not compared: their stochastic-rounding draws are keyed by the position in
+    the expert-sorted layout, which a permutation changes."""
+    inp = synth.config_inputs(1, device="cuda")
+    k, T = 2, 256
+    p = torch.from_numpy(np.random.default_rng(21).permutation(T)).cuda()
+    fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, seed=synth.SR_SEED)
+    bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+    fw2 = layer.forward(inp["x"][p], inp["w_up"], inp["w_down"], inp["logits"][p], k, seed=synth.SR_SEED)
+    bw2 = layer.backward(fw2, inp["dy"][p], seed=synth.SR_SEED)
+    assert torch.equal(fw2["y"].view(torch.int16), fw["y"][p].view(torch.int16))
+    assert torch.equal(bw2["dx"].view(torch.int16), bw["dx"][p].view(torch.int16))
+    assert torch.equal(bw2["dg"].view(torch.int32), bw["dg"][p].view(torch.int32))
+    assert torch.equal(bw2["dlogits"].view(torch.int32), bw["dlogits"][p].view(torch.int32))
+
+
+def test_layer_expert_relabelling_equivariance_gpu():
+    """Relabelling the experts (weights and logit columns permuted together)
+    leaves y unchanged bit for bit."""
+    inp = synth.config_inputs(1, device="cuda")
+    k, E = 2, 8
+    q = torch.from_numpy(np.random.default_rng(22).permutation(E)).cuda()
+    y1 = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k)["y"]
+    y2 = layer.forward(inp["x"], inp["w_up"][q].contiguous(), inp["w_down"][q].contiguous(),
+                       inp["logits"][:, q].contiguous(), k)["y"]
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
 def test_layer_mxfp8_forward_config1_end_to_end():
     """The MXFP8-forward variant on the tiny layer: routing, the MXFP8 weights
     and the gathered MXFP8 X are bit-exact; the weight requantisations (which

@@ -124,6 +124,24 @@ def test_nvfp4_power_of_two_equivariance_gpu():
         assert q[2].item() == base[2].item() * 2.0 ** j
 
 
+@pytest.mark.parametrize("pre", ["none", "silu"])
+def test_nvfp4_group_split_invariance_gpu(pre):
+    """Quantising ragged groups in one launch or each group in a launch of its
+    own (other grids, other ticket orders) gives the same bytes."""
+    xb = _bf16_input(600, 512, seed=8)
+    x = bf16_from_bits(xb)
+    off = np.array([0, 100, 100, 357, 361, 600])
+    op = m4.PRE_SILU if pre == "silu" else m4.PRE_NONE
+    whole = m4.nvfp4_quant_46(x, 46, cuda_i32(off), op)
+    for g in range(len(off) - 1):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        if r1 == r0:
+            continue
+        part = m4.nvfp4_quant_46(x[r0:r1].contiguous(), 46, cuda_i32(np.array([0, r1 - r0])), op)
+        assert torch.equal(part[0], whole[0][r0:r1]) and torch.equal(part[1], whole[1][r0:r1]), g
+        assert part[2].view(torch.int32)[0].item() == whole[2].view(torch.int32)[g].item(), g
+
+
 def test_nvfp4_dequant_matches_oracle():
     xb = _bf16_input(96, 128, seed=6)
     codes, sf, ts = m4.nvfp4_quant_46(bf16_from_bits(xb), 46)
