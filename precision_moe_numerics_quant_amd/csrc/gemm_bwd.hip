@@ -1206,6 +1206,41 @@ __global__ void __launch_bounds__(dws::NT, 1)
 // 32 pw .. 32 pw + 31 (4 code row groups) and the scales of B's 64-row half
 // pw / 2 (loaded by two waves: every producer issues 14 loads per slab,
 // which its waits count).
+// An expert's n_mt x n_nt output tiles split into 8 rectangles of pm x pn
+// tiles (xa row parts x 8 / xa column parts), one per XCD: virtual tile
+// v = 8 q + x is tile q (column fastest) of rectangle x, and workgroup b,
+// which runs on XCD b % 8 in a grid that is a multiple of 8, walks the
+// tiles b, b + grid, ...: each XCD's L2 then fetches only its rectangle's
+// operand rows of the expert instead of nearly all of them.  Virtual tiles
+// past the grid (when a dimension does not divide) are skipped.
+struct XcdSplit {
+  uint32_t n_mt, n_nt, xb, pm, pn;
+  __device__ bool tile(uint32_t v, uint32_t& mt, uint32_t& nt) const {
+    const uint32_t x = v & 7u, q = v >> 3, px = x / xb, qm = q / pn;
+    mt = px * pm + qm;
+    nt = (x - px * xb) * pn + (q - qm * pn);
+    return mt < n_mt && nt < n_nt;
+  }
+};
+
+// The split with the fewest operand rows per XCD (counting the virtual
+// tiles that fall outside the grid as extra work).
+static XcdSplit xcd_split(int64_t n_mt, int64_t n_nt, int tm, int tn) {
+  XcdSplit best{};
+  double best_cost = 1e300;
+  for (uint32_t xa = 1; xa <= 8; xa *= 2) {
+    const uint32_t xb = 8 / xa;
+    const uint32_t pm = (uint32_t)((n_mt + xa - 1) / xa), pn = (uint32_t)((n_nt + xb - 1) / xb);
+    const double rows = (double)pm * tm + (double)pn * tn;
+    const double cost = rows * (8.0 * pm * pn) / ((double)n_mt * n_nt);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = XcdSplit{(uint32_t)n_mt, (uint32_t)n_nt, xb, pm, pn};
+    }
+  }
+  return best;
+}
+
 namespace wsg2 {
 constexpr int TM = 256, TN = 128, BK = 128, S = 3;
 constexpr int CODE_A = TM * BK, CODE_B = TN * BK, SCL_A = 4 * TM, SCL_B = 4 * TN;
@@ -1216,7 +1251,7 @@ constexpr int I = 14;
 __global__ void __launch_bounds__(wsg::NT, 1)
     k_wgrad_ws256(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
                   const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
-                  const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, int64_t n_ntiles_, int64_t n_all_,
+                  const int32_t* __restrict__ off, int E, int64_t N1, int64_t N2, XcdSplit xs, int64_t n_all_,
                   float* __restrict__ dw, float beta, bool zero_empty) {
   using namespace wsg2;
   using wsg::NCW;
@@ -1229,11 +1264,8 @@ __global__ void __launch_bounds__(wsg::NT, 1)
   using dmag::swz;
   __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
   __shared__ int32_t s_off[MAX_E + 1];
-  const uint32_t n_all = (uint32_t)n_all_, n_ntiles = (uint32_t)n_ntiles_, per_e = n_all / (uint32_t)E;
-  auto tile_mn = [&](uint32_t rest, uint32_t& mt, uint32_t& nt) {
-    mt = rest / n_ntiles;
-    nt = rest - mt * n_ntiles;
-  };
+  const uint32_t n_all = (uint32_t)n_all_, per_e = n_all / (uint32_t)E;
+  auto tile_mn = [&](uint32_t rest, uint32_t& mt, uint32_t& nt) { return xs.tile(rest, mt, nt); };
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i <= E; i += NT) s_off[i] = off[i];
@@ -1252,9 +1284,8 @@ __global__ void __launch_bounds__(wsg::NT, 1)
         // compiler wait for this wave's direct-to-LDS loads)
         const uint32_t e = pt / per_e, rest = pt - e * per_e;
         const int64_t p0 = ld_const(off, (int)e), kl = (int64_t)ld_const(off, (int)e + 1) - p0;
-        if (kl == 0) continue;
         uint32_t mt, nt;
-        tile_mn(rest, mt, nt);
+        if (kl == 0 || !tile_mn(rest, mt, nt)) continue;
         const int64_t ra0 = (int64_t)mt * TM, rb0 = (int64_t)nt * TN;
         rca = make_rsrc(a_codes + N1 * p0, (uint64_t)N1 * kl);
         rsa = make_rsrc(a_sf + N1 * p0 / 32, (uint64_t)N1 * (kl / 32));
@@ -1382,7 +1413,7 @@ __global__ void __launch_bounds__(wsg::NT, 1)
   for (uint32_t t = blockIdx.x; t < n_all; t += gridDim.x) {
     const uint32_t e = t / per_e, rest = t - e * per_e;
     uint32_t mt, nt;
-    tile_mn(rest, mt, nt);
+    if (!tile_mn(rest, mt, nt)) continue;
     const int64_t m0 = (int64_t)mt * TM, c0 = (int64_t)nt * TN;
     const int kl = s_off[e + 1] - s_off[e];
     float* C = dw + (int64_t)e * N1 * N2;
@@ -1499,12 +1530,13 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
 static void launch_wgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                          const int32_t* off, int E, int64_t N1, int64_t N2, float* dw, float beta, bool zero_empty,
                          hipStream_t s) {
-  const int64_t ws2_all = (N2 + wsg2::TN - 1) / wsg2::TN * ((N1 + wsg2::TM - 1) / wsg2::TM) * E;
+  const XcdSplit xs = xcd_split((N1 + wsg2::TM - 1) / wsg2::TM, (N2 + wsg2::TN - 1) / wsg2::TN, wsg2::TM, wsg2::TN);
+  const int64_t ws2_all = 8ll * xs.pm * xs.pn * E;
   if (E <= wsg::MAX_E && ws2_all < (1ll << 31) && (int64_t)N1 * N2 * 4 < (1ll << 31)) {
     int64_t grid = cu_count();
     if (grid > ws2_all) grid = ws2_all;
-    hipLaunchKernelGGL(k_wgrad_ws256, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2,
-                       (N2 + wsg2::TN - 1) / wsg2::TN, ws2_all, dw, beta, zero_empty);
+    hipLaunchKernelGGL(k_wgrad_ws256, dim3((unsigned)grid), dim3(wsg::NT), 0, s, ac, as, bc, bs, off, E, N1, N2, xs,
+                       ws2_all, dw, beta, zero_empty);
     return;
   }
   const int64_t ws_all = (N2 + wsg::TN - 1) / wsg::TN * ((N1 + wsg::TM - 1) / wsg::TM) * E;
