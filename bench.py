@@ -58,9 +58,10 @@ def work_table(c, off, off_pad):
     E_act = int((np.diff(np.asarray(off)) > 0).sum())
     wg_bytes = lambda n1, n2: E_act * n1 * n2 * 4.0 + (n1 + n2) * Ptot * mxb
     return {
-        # two fp32 reads (amax, then encode), the NVFP4 write and the backward's MXFP8 copy
-        "F1 W_up quant (+ requant)": ("hbm", E * F * d * (8.0 + nv + mxb)),
-        "F1 W_down quant (+ requant)": ("hbm", E * F * d * (8.0 + nv + mxb)),
+        # one fp32 read (each expert matrix stays in registers from its amax to
+        # its encode), the NVFP4 write and the backward's MXFP8 copy
+        "F1 W_up quant (+ requant)": ("hbm", E * F * d * (4.0 + nv + mxb)),
+        "F1 W_down quant (+ requant)": ("hbm", E * F * d * (4.0 + nv + mxb)),
         "F2-F3 route + permutation": ("hbm", T * E * 4.0 + A * 16.0),
         "F4 X quant (NVFP4 4/6)": ("hbm", T * d * (4.0 + nv)),
         "F5 dispatch gather": ("hbm", 2.0 * A * d * nv),
@@ -87,8 +88,8 @@ def work_table(c, off, off_pad):
 
 # the library kernel behind each call (several calls may launch one kernel)
 KERNEL_OF = {
-    "F1 W_up quant (+ requant)": "k_encode_requant_T",
-    "F1 W_down quant (+ requant)": "k_encode_requant_T",
+    "F1 W_up quant (+ requant)": "k_wq_resident",
+    "F1 W_down quant (+ requant)": "k_wq_resident",
     "F2-F3 route + permutation": "route", "F4 X quant (NVFP4 4/6)": "nvfp4 quant 4/6 bf16",
     "F5 dispatch gather": "k_gather_rows", "F6 up GEMM (NVFP4)": "k_gemm_fwd_ws (bf16)",
     "F8 down GEMM (NVFP4)": "k_gemm_fwd_ws (f32)",
@@ -121,8 +122,8 @@ MOVEMENT_CALLS = {"F5 dispatch gather", "F9 combine", "B11 un-permute sum", "B12
 # the HBM bytes per launch are reported only while that source is unchanged.
 PMC_PROFILE = {"k_wgrad_ws256": ("profiles/k_wgrad_ws256_T16384_E384_pmc.md",
                                  "precision_moe_numerics_quant_amd/csrc/gemm_bwd.hip"),
-               "k_encode_requant_T": ("profiles/k_encode_requant_T_E384_4096x1536_pmc.md",
-                                      "precision_moe_numerics_quant_amd/csrc/nvfp4_quant.hip")}
+               "k_wq_resident": ("profiles/k_wq_resident_E384_4096x1536_pmc.md",
+                                 "precision_moe_numerics_quant_amd/csrc/nvfp4_quant.hip")}
 
 
 def source_sha256(rel):

@@ -179,9 +179,9 @@ int nvfp4_quant_46_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
  * codes [rows, cols/2], sf [rows, cols/16], tensor_scale [n_groups] as in
  * nvfp4_quant_46; seed, stream_id as in mxfp8_requant_sr_T.  cols % 32 == 0;
  * x, codes and mx_codes 16-byte aligned.
- * ws: nvfp4_quant_requant_T_ws_bytes(n_groups) bytes, cleared by the call
- * (per-group amax words and tile counts, a work counter); calls in flight at
- * the same time need workspaces of their own.
+ * ws: nvfp4_quant_requant_T_ws_bytes(n_groups) bytes (3 KB per group),
+ * cleared by the call (per-group partial maxima and counts); calls in flight
+ * at the same time need workspaces of their own.
  */
 int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups,
                           uint8_t* codes, uint8_t* sf, float* tensor_scale, uint64_t seed, uint32_t stream_id,

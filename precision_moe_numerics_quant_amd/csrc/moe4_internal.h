@@ -13,6 +13,7 @@ void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
 int check_launch(const char* what);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 #define MOE4_REQUIRE(cond, code, msg)                 \
@@ -88,6 +89,11 @@ __device__ inline float mant_factor(float s) {
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline uint32_t wave_umax(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
   return v;
 }
 

@@ -21,6 +21,7 @@
 #include <string>
 
 #include "act.h"
+#include "gemm_common.h"
 #include "moe4_internal.h"
 #include "mx_requant.h"
 #include "nvfp4_enc.h"
@@ -583,6 +584,284 @@ __global__ void __launch_bounds__(rq::THREADS) __attribute__((amdgpu_waves_per_e
   }
 }
 
+// Weights, fused, one HBM read: the same outputs as k_encode_requant_T for
+// groups whose tiles all fit the chip at once.  Each workgroup owns one
+// 32-row x 256-column tile (rows of 1 KB), the same one in every group (G
+// rounds), and holds its float32 values in registers from the amax to the
+// encode: lane l of wave w takes rows 4 (l / 8) .. + 3 and columns
+// 64 w + 8 (l % 8) .. + 7 of the tile, so a 16-value NVFP4 block lies in the
+// lanes l, l ^ 1 and a 32-row MX block in the lanes l, l ^ 8, l ^ 16, l ^ 32.
+// Four register sets rotate: in round g the workgroup folds group g + 2's
+// tile into its maximum and publishes it, encodes group g (whose tensor
+// scale it took at the end of the previous round) and stores it, takes group
+// g + 1's tensor scale (every workgroup published its part a round earlier,
+// so the wait normally finds it complete) and issues group g + 4's loads into
+// the freed set.  Wave 0 publishes and polls and does no global store (its
+// polls would queue behind the stores, a wave's memory operations
+// completing in order), and loads after its poll; waves 1-3 write the tile's
+// outputs from LDS in 16-byte pieces.  Tiles are numbered so that the four
+// tiles of a 128-row run sit on one XCD (workgroup b runs on XCD b % 8),
+// whose L2 then merges their 32-byte pieces of each MXFP8 column.  The
+// launch needs every workgroup resident (checked against the occupancy on
+// the host); the wait is bounded like k_encode_requant_T's and a give-up sets
+// MOE4_DEVERR_WAIT.
+namespace wr {
+constexpr int WAVES = 4, THREADS = 64 * WAVES, TR = 32, TC = 256, MIN_BLOCKS = 3;
+// Group maxima without atomics: workgroup b stores its tile's maximum, its
+// top bit set as a presence mark (the bits of a maximum, a non-negative
+// float, have it clear), into word b of the group's n_tile workspace words;
+// every workgroup reads all of them back (wave 0, 12 words per lane) until
+// all are present, and takes the same maximum and tensor scale.  A chain of
+// one store and one read per group (returning atomics, chained, cost several
+// memory round trips each, and hundreds of them on one word serialise).
+constexpr int MAX_TILES = 768;
+}
+
+template <int D>
+__device__ inline float wr_xor(float v) {  // lane l ^ D within each 32 lanes (D < 32)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1F));
+}
+
+template <bool FAST>
+__global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
+    k_wq_resident(const float* __restrict__ x, int64_t C, int64_t grows, int G, uint32_t wait_extra,
+                  uint32_t spin_limit, uint32_t* __restrict__ wsu, float* __restrict__ ts, uint32_t base,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ sf, uint8_t* __restrict__ out_c,
+                  uint8_t* __restrict__ out_s) {
+  using namespace wr;
+  __shared__ __attribute__((aligned(16))) uint8_t lq[TC * TR];       // MXFP8 [column][32 rows]
+  __shared__ __attribute__((aligned(16))) uint8_t lcode[TR * TC / 2];  // NVFP4 codes [row][128 bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t lsf[TR * TC / 16];   // NVFP4 scale bytes [row][16]
+  __shared__ uint8_t lmxs[TC];                                         // MX scale byte of each column
+  __shared__ float s_red[WAVES];
+  __shared__ float s_S[2];  // tensor scales of groups g (slot g & 1) and g + 1
+  const uint32_t n_tile = gridDim.x;
+  const int tid = threadIdx.x, l = tid & 63, cg = l & 7, rg = l >> 3;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t key0 = fmix32(base);
+  // this workgroup's tile: 8 consecutive tiles run on 8 XCDs; each XCD takes
+  // runs of 4 row-adjacent tiles (the 128 rows of four MX blocks)
+  const uint32_t ti = blockIdx.x, q = ti >> 3, quad = (q >> 2) * 8 + (ti & 7);
+  const uint32_t n_cb = (uint32_t)(C / TC), rq = quad / n_cb, cb = quad - rq * n_cb;
+  const int64_t rt0 = (int64_t)(4 * rq + (q & 3)) * TR, c0 = (int64_t)cb * TC;
+  const int64_t lrow = rt0 + 4 * rg, lcol = c0 + 64 * w + 8 * cg;  // the lane's first row (in its group) and column
+
+  using Buf = f32x4[8];  // [row i][half h] at 2 i + h
+  // (buffer accesses off one descriptor per group and 32-bit offsets: a
+  // group's tensors stay below 2 GB, checked on the host)
+  const uint32_t ld_off = (uint32_t)(lrow * C + lcol) * 4u;
+  auto load = [&](int g, Buf& b) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)g * grows * C, (uint64_t)grows * C * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, ld_off, (uint32_t)(i * C * 4 + 16 * h), 0);
+        b[2 * i + h] = f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+      }
+  };
+  auto tile_max = [&](const Buf& b) {  // wave maximum to s_red[w]
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(b[k][0]), fabsf(b[k][1])), fmaxf(fabsf(b[k][2]), fabsf(b[k][3]))));
+    m = wave_max(m);
+    if (l == 0) s_red[w] = m;
+  };
+  // (thread 0, after a barrier) this tile's maximum of group g, marked present
+  auto publish = [&](int g) {
+    if (tid == 0) {
+      const float mm = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      __hip_atomic_store(wsu + (size_t)g * n_tile + ti, __float_as_uint(mm) | 0x80000000u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  // (wave 0) group g's tensor scale once every tile's maximum is present;
+  // after one give-up the workgroup stops waiting (a launch that cannot hold
+  // all its workgroups then ends in one spin limit, not one per group)
+  bool gave_up = false;
+  auto take_scale = [&](int g) {
+    const uint32_t* part = wsu + (size_t)g * n_tile;
+    uint32_t spins = 0, mx = 0;
+    bool all = false;
+    while (true) {
+      uint32_t v[MAX_TILES / 64];
+#pragma unroll
+      for (int j = 0; j < MAX_TILES / 64; ++j) {
+        const uint32_t k = (uint32_t)(l + 64 * j);
+        v[j] = k < n_tile ? __hip_atomic_load(part + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0x80000000u;
+      }
+      bool ok = true;
+      mx = 0;
+#pragma unroll
+      for (int j = 0; j < MAX_TILES / 64; ++j) {
+        ok = ok && (v[j] >> 31) != 0u;
+        mx = max(mx, v[j] & 0x7FFFFFFFu);
+      }
+      all = __all(ok) && wait_extra == 0u;
+      if (all || gave_up || ++spins >= spin_limit) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (!all) {
+      gave_up = true;
+      if (l == 0) atomicOr(&g_dev_err, MOE4_DEVERR_WAIT);
+    }
+    const float a = __uint_as_float(wave_umax(mx));
+    const float sv = a / (6.0f * 448.0f);
+    const float S = (sv == 0.0f) ? 1.0f : sv;
+    if (l == 0) {
+      s_S[g & 1] = S;
+      if (ti == 0) ts[g] = S;
+    }
+  };
+  // NVFP4 mode 6 of the lane's 4 x 8 values, then the SR MXFP8 bytes of the
+  // transposed copy, both staged in LDS
+  auto encode = [&](int g, const Buf& b, float S) {
+    int lx = l;
+    asm volatile("" : "+v"(lx));  // (as in store: LDS addresses made here)
+    const int cg = lx & 7, rg = lx >> 3;
+    uint32_t cw[4], scb[4];
+    float am[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v[8] = {b[2 * i][0], b[2 * i][1], b[2 * i][2], b[2 * i][3],
+                          b[2 * i + 1][0], b[2 * i + 1][1], b[2 * i + 1][2], b[2 * i + 1][3]};
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+      a = fmaxf(a, wr_xor<1>(a));  // the block's other half
+      uint32_t sc;
+      cw[i] = encode_half(v, a, S, 6.0f, sc);
+      scb[i] = sc;
+      const int row = 4 * rg + i;
+      *reinterpret_cast<uint32_t*>(lcode + row * (TC / 2) + 32 * w + 4 * cg) = cw[i];
+      if ((cg & 1) == 0) lsf[row * (TC / 16) + 4 * w + (cg >> 1)] = (uint8_t)sc;
+      float q8[8];
+      dequant8(cw[i], sc, q8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf(q8[e]));
+    }
+    float f[8];
+    const bool fold = fold_scale_ok(S);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      am[e] = fmaxf(am[e], wr_xor<8>(am[e]));
+      am[e] = fmaxf(am[e], wr_xor<16>(am[e]));
+      am[e] = fmaxf(am[e], __shfl_xor(am[e], 32, 64));
+      const int ex = mx_exponent(am[e] * S);
+      const float pc = __builtin_amdgcn_ldexpf(1.0f, -ex);
+      f[e] = fold ? (ex == -127 ? 0.0f : S * pc) : pc;
+      if (rg == 0) lmxs[64 * w + 8 * cg + e] = (uint8_t)(ex + 127);
+    }
+    uint32_t od[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) od[e] = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float q8[8];
+      dequant8(cw[i], scb[i], q8);
+      const int64_t jr = ((int64_t)g * grows + lrow + i) * (C / 2) + lcol / 2;  // pair index of the row's first pair
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t word;
+        if (FAST) {
+          word = fmix32(((uint32_t)jr + (uint32_t)p) ^ key0);
+        } else {
+          const int64_t j = jr + p;
+          word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));
+        }
+        // fold: fl(q * (S 2^-ex)), else fl(fl(q * S) * 2^-ex): the same values
+        const float v0 = fold ? q8[2 * p] * f[2 * p] : (q8[2 * p] * S) * f[2 * p];
+        const float v1 = fold ? q8[2 * p + 1] * f[2 * p + 1] : (q8[2 * p + 1] * S) * f[2 * p + 1];
+        od[2 * p] = sr_fp8_into(od[2 * p], v0, word << 16, i);
+        od[2 * p + 1] = sr_fp8_into(od[2 * p + 1], v1, word & 0xFFFF0000u, i);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(lq + (64 * w + 8 * cg + e) * TR + 4 * rg) = od[e];
+  };
+  // (waves 1-3) the staged tile of group g: 960 pieces, 5 per thread, each
+  // 64-piece run of one kind
+  using v4u = __attribute__((ext_vector_type(4))) unsigned int;
+  // (waves 1-3) the staged tile of group g in runs of 64 pieces of one kind,
+  // run r = (w - 1) + 3 k: 8 runs of MXFP8 codes (a column's 32 rows as two
+  // 16-byte pieces), 4 of NVFP4 codes (16 bytes of a row), 4 of MX scale
+  // bytes (one per column) and half a run of NVFP4 scale bytes (16 per row)
+  auto store = [&](int g) {
+    // (the lane index passes through an empty asm so that the addresses
+    // below are made here, not kept live across the rounds)
+    int li = l;
+    asm volatile("" : "+v"(li));
+    const int64_t gel = (int64_t)g * grows * C;  // the group's first element
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int run = (w - 1) + 3 * k, it = 64 * run + li;
+      if (run < 8) {
+        const int col = it >> 1, h = it & 1;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lq + col * TR + 16 * h);
+        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]}, make_rsrc(out_c + gel, (uint64_t)grows * C),
+                                               (uint32_t)((c0 + col) * grows + rt0 + 16 * h), 0, 0);
+      } else if (run < 12) {
+        const int jt = it - 512, row = jt >> 3, h = jt & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lcode + row * (TC / 2) + 16 * h);
+        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
+                                               make_rsrc(codes + gel / 2, (uint64_t)grows * C / 2),
+                                               (uint32_t)((rt0 + row) * (C / 2) + c0 / 2 + 16 * h), 0, 0);
+      } else if (run < 16) {
+        const int col = it - 768;
+        __builtin_amdgcn_raw_buffer_store_b8(lmxs[col], make_rsrc(out_s + gel / 32, (uint64_t)grows * C / 32),
+                                             (uint32_t)((c0 + col) * (grows / 32) + rt0 / 32), 0, 0);
+      } else if (run == 16 && li < TR) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lsf + li * (TC / 16));
+        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
+                                               make_rsrc(sf + gel / 16, (uint64_t)grows * C / 16),
+                                               (uint32_t)((rt0 + li) * (C / 16) + c0 / 16), 0, 0);
+      }
+    }
+  };
+  // round g: X holds group g (its tensor scale in s_S[g & 1]), Y group g + 1
+  // (its maximum published), Z group g + 2 and V group g + 3 (loads may be in
+  // flight).  Every wave loads at the same point, unconditionally (past the
+  // last group it reloads the last one), so no register copies wait for
+  // those loads; wave 0 loads after its poll, so the poll never queues behind
+  // them.
+  auto round = [&](int g, Buf& X, Buf& Y, Buf& Z, Buf& V) {
+    const bool has1 = g + 1 < G, has2 = g + 2 < G;
+    if (has2) tile_max(Z);
+    __syncthreads();
+    if (w == 0 && has2) publish(g + 2);
+    encode(g, X, s_S[g & 1]);
+    __syncthreads();
+    if (w != 0) store(g);
+    else if (has1) take_scale(g + 1);  // (published a round ago)
+    load(g + 4 < G ? g + 4 : G - 1, X);  // X is free: group g + 4
+  };
+  Buf A, B, Cb, D;
+  load(0, A);
+  load(G > 1 ? 1 : 0, B);
+  load(G > 2 ? 2 : G - 1, Cb);
+  load(G > 3 ? 3 : G - 1, D);
+  tile_max(A);
+  __syncthreads();
+  if (w == 0) publish(0);
+  __syncthreads();  // s_red is free again
+  if (G > 1) tile_max(B);
+  __syncthreads();
+  if (w == 0) {
+    if (G > 1) publish(1);
+    take_scale(0);
+  }
+  __syncthreads();  // s_red free, s_S[0] set
+  for (int g = 0; g < G; g += 4) {
+    round(g, A, B, Cb, D);
+    if (g + 1 < G) round(g + 1, B, Cb, D, A);
+    if (g + 2 < G) round(g + 2, Cb, D, A, B);
+    if (g + 3 < G) round(g + 3, D, A, B, Cb);
+  }
+}
+
 __global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
                           const float* __restrict__ ts, int ts_per_group, const int32_t* __restrict__ goff,
                           int G, int64_t rows, int64_t cols, float* __restrict__ out) {
@@ -716,11 +995,30 @@ extern "C" int nvfp4_quant_46_noalloc(const void* x, int dtype, int64_t rows, in
                         (size_t)n_groups * sizeof(uint32_t), stream);
 }
 
-// Workspace: amax bits [G], finished amax tiles [G] and the ticket counter,
-// 32-bit words cleared before the launch.
+// Workgroups of k_wq_resident the device holds at once (its launch needs
+// them all resident), per device and instantiation.
+static int64_t wq_resident_capacity(bool fast) {
+  static int64_t cap[64][2];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev][fast] == 0) {
+    int nb = 0;
+    const hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_wq_resident<true>, wr::THREADS, 0)
+                              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_wq_resident<false>, wr::THREADS, 0);
+    cap[dev][fast] = (e == hipSuccess && nb > 0) ? (int64_t)nb * cu_count_q() : -1;
+  }
+  return cap[dev][fast];
+}
+
+// Workspace (32-bit words, cleared before the launch): k_wq_resident keeps
+// its tiles' maxima there (n_tile <= MAX_TILES words per group);
+// k_encode_requant_T uses the first 2 G + 1 words (amax bits [G], finished
+// amax tiles [G], the ticket counter).
 extern "C" size_t nvfp4_quant_requant_T_ws_bytes(int32_t n_groups) {
   const size_t g = (size_t)(n_groups > 0 ? n_groups : 1);
-  return (2 * g + 1) * sizeof(uint32_t);
+  return g * wr::MAX_TILES * sizeof(uint32_t);  // (>= the ticketed kernel's 2 g + 1 words)
 }
 
 extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols, int32_t n_groups, uint8_t* codes,
@@ -748,15 +1046,31 @@ extern "C" int nvfp4_quant_requant_T(const float* x, int64_t rows, int64_t cols,
     hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, wsu, G, 6.0f * 448.0f, tensor_scale);
     return check_launch("nvfp4_quant_requant_T");
   }
+  const bool forced = force_wait_timeout();
+  const uint32_t base = sr_base_key(seed, stream_id);
+  // one HBM read when every tile of a group fits the chip at once
+  if (grows % (4 * wr::TR) == 0 && cols % wr::TC == 0 && aligned16(sf)) {
+    const int64_t n_tile = (grows / wr::TR) * (cols / wr::TC);
+    const bool fast = rows * (cols / 2) <= ((int64_t)1 << 32);
+    if (n_tile % 32 == 0 && n_tile <= wr::MAX_TILES && n_tile <= wq_resident_capacity(fast)) {
+      auto k = fast ? k_wq_resident<true> : k_wq_resident<false>;
+      const int64_t n_zero = (int64_t)G * n_tile;
+      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n_zero + 255) / 256)), dim3(256), 0, s, wsu, (int)n_zero);
+      hipLaunchKernelGGL(k, dim3((unsigned)n_tile), dim3(wr::THREADS), 0, s, x, cols, grows, G, forced ? 1u : 0u,
+                         forced ? wq::FORCED_SPIN_LIMIT : wq::SPIN_LIMIT, wsu, tensor_scale, base, codes, sf, mx_codes,
+                         mx_sf);
+      return check_launch("nvfp4_quant_requant_T");
+    }
+  }
   const int64_t n_ct = (cols + rq::COLS - 1) / rq::COLS, n_item = (grows + rq::ROWS - 1) / rq::ROWS * n_ct;
   const int64_t n_total = (int64_t)G * n_item;
   const int64_t slots = (int64_t)cu_count_q() * 2;  // two 64 KB-LDS workgroups per CU
   MOE4_REQUIRE(2 * n_total + slots < ((int64_t)1 << 31), MOE4_EINVAL, "nvfp4_quant_requant_T: tensor too large");
   const int64_t grid = 2 * n_total < slots ? 2 * n_total : slots;
-  const bool forced = force_wait_timeout();
   hipLaunchKernelGGL(k_encode_requant_T, dim3((unsigned)grid), dim3(rq::THREADS), 0, s, x, cols, grows, G,
                      (uint32_t)n_ct, (uint32_t)n_item, forced ? 1u : 0u,
-                     forced ? wq::FORCED_SPIN_LIMIT : wq::SPIN_LIMIT, wsu, tensor_scale, sr_base_key(seed, stream_id), codes, sf, mx_codes, mx_sf);
+                     forced ? wq::FORCED_SPIN_LIMIT : wq::SPIN_LIMIT, wsu, tensor_scale, base, codes, sf, mx_codes,
+                     mx_sf);
   return check_launch("nvfp4_quant_requant_T");
 }
 

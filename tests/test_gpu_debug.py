@@ -36,8 +36,10 @@ def test_debug_check_clean():
     m4.moe4_debug_check()
 
 
-def test_forced_wait_timeout_is_reported_then_cleared():
-    G, Rg, C = 6, 64, 512
+# (6, 64, 512) takes the ticketed weight-quantisation kernel, (6, 128, 2048)
+# the single-read one; both have a bounded wait
+@pytest.mark.parametrize("G,Rg,C", [(6, 64, 512), (6, 128, 2048)])
+def test_forced_wait_timeout_is_reported_then_cleared(G, Rg, C):
     rng = np.random.default_rng(11)
     w = (rng.standard_normal((G * Rg, C)) * 0.02).astype(np.float32)
     wt = torch.from_numpy(w).cuda()

@@ -378,10 +378,16 @@ def test_run_twice_deterministic():
     assert torch.equal(r1[0][:n], r2[0][:n]) and torch.equal(r1[1][:n // 32], r2[1][:n // 32])
 
 
-# The last two have more tiles than the launch has workgroups (two per CU), so
-# workgroups take many amax and encode tickets each.
+# The first six take the ticketed kernel; (320, 32, 512) and (200, 96, 1056)
+# have more tiles than the launch has workgroups (two per CU), so workgroups
+# take many amax and encode tickets each.  The rest take the single-read
+# kernel (groups of a multiple of 128 rows and 256 columns, a multiple of 32
+# tiles of 128 x 64): one round or a few, 33 groups (rounds in threes and a
+# tail), 128 tiles per group, and groups whose tensor scales fall outside the
+# range where the MX factor folds into one multiply (tiny and huge values).
 @pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96), (320, 32, 512),
-                                    (200, 96, 1056)])
+                                    (200, 96, 1056), (1, 128, 8192), (2, 512, 512), (3, 256, 1024),
+                                    (7, 128, 2048), (33, 256, 2048), (5, 1024, 512)])
 def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
     """nvfp4_quant_requant_T equals nvfp4_quant_46 (mode 6, G equal groups)
     followed by mxfp8_requant_sr_T (row-major scales), byte for byte, against
@@ -391,6 +397,9 @@ def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
     w = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
     w[rng.random((R, C)) < 0.002] *= 40.0                       # outliers
     w[Rg:2 * Rg] *= 0.0 if G > 2 else 1.0                        # an all-zero group
+    if G > 4:
+        w[3 * Rg:4 * Rg] *= np.float32(2.0 ** -110)              # tensor scale near 2^-120
+        w[4 * Rg:5 * Rg] *= np.float32(2.0 ** 20)                # tensor scale near 2^10
     off = np.arange(G + 1) * Rg
     q = nv.nvfp4_quantize(w, nv.MODE_6, off)
     mc_ref, ms_ref = mx.requant_sr_t(q["codes"], q["sf"], q["ts"], off, True, seed=7, stream_id=19)
