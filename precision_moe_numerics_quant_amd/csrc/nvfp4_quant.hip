@@ -716,10 +716,12 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
   };
   // NVFP4 mode 6 of the lane's 4 x 8 values, then the SR MXFP8 bytes of the
   // transposed copy, both staged in LDS
-  auto encode = [&](int g, const Buf& b, float S) {
+  auto encode = [&](int g, const Buf& b, float S_in) {
     int lx = l;
     asm volatile("" : "+v"(lx));  // (as in store: LDS addresses made here)
     const int cg = lx & 7, rg = lx >> 3;
+    const float S = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(S_in)));  // (wave-uniform)
+    const float d6 = 6.0f * S;
     uint32_t cw[4], scb[4];
     float am[8];
 #pragma unroll
@@ -732,19 +734,32 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
       a = fmaxf(a, wr_xor<1>(a));  // the block's other half
-      uint32_t sc;
-      cw[i] = encode_half(v, a, S, 6.0f, sc);
+      // encode_half's steps; its zero-scale and infinite-reciprocal cases
+      // (tiny values) go through it whenever a lane of the wave meets one
+      const uint32_t sc = e4m3_rne_u(a / d6);
+      const float eff = e4m3_to_f32(sc) * S;
+      const float inv = 1.0f / eff;
+      uint32_t q = 0u;
+      if (__builtin_expect(__any(sc == 0u || eff == 0.0f || __builtin_isinf(inv)), 0)) {
+        uint32_t sc2;
+        q = encode_half(v, a, S, 6.0f, sc2);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          q |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[e] * inv, v[e + 1] * inv, 1.0f, 0) & 0xFFu) << (4 * e);
+      }
+      cw[i] = q;
       scb[i] = sc;
       const int row = 4 * rg + i;
-      *reinterpret_cast<uint32_t*>(lcode + row * (TC / 2) + 32 * w + 4 * cg) = cw[i];
+      *reinterpret_cast<uint32_t*>(lcode + row * (TC / 2) + 32 * w + 4 * cg) = q;
       if ((cg & 1) == 0) lsf[row * (TC / 16) + 4 * w + (cg >> 1)] = (uint8_t)sc;
       float q8[8];
-      dequant8(cw[i], sc, q8);
+      dequant8(q, sc, q8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf(q8[e]));
     }
-    float f[8];
     const bool fold = fold_scale_ok(S);
+    float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       am[e] = fmaxf(am[e], wr_xor<8>(am[e]));
@@ -758,32 +773,32 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
     uint32_t od[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) od[e] = 0u;
+    const int64_t jr0 = ((int64_t)g * grows + lrow) * (C / 2) + lcol / 2;  // pair index of the lane's first pair
+    // fold: fl(q * (S 2^-ex)), else fl(fl(q * S) * 2^-ex): the same values
+    auto sr_rows = [&](auto val) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float q8[8];
-      dequant8(cw[i], scb[i], q8);
-      const int64_t jr = ((int64_t)g * grows + lrow + i) * (C / 2) + lcol / 2;  // pair index of the row's first pair
+      for (int i = 0; i < 4; ++i) {
+        float q8[8];
+        dequant8(cw[i], scb[i], q8);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t word;
-        if (FAST) {
-          word = fmix32(((uint32_t)jr + (uint32_t)p) ^ key0);
-        } else {
-          const int64_t j = jr + p;
-          word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));
+        for (int p = 0; p < 4; ++p) {
+          uint32_t word;
+          if (FAST) {
+            word = fmix32(((uint32_t)jr0 + (uint32_t)i * (uint32_t)(C / 2) + (uint32_t)p) ^ key0);
+          } else {
+            const int64_t j = jr0 + i * (C / 2) + p;
+            word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));
+          }
+          od[2 * p] = sr_fp8_into(od[2 * p], val(q8[2 * p], f[2 * p]), word << 16, i);
+          od[2 * p + 1] = sr_fp8_into(od[2 * p + 1], val(q8[2 * p + 1], f[2 * p + 1]), word & 0xFFFF0000u, i);
         }
-        // fold: fl(q * (S 2^-ex)), else fl(fl(q * S) * 2^-ex): the same values
-        const float v0 = fold ? q8[2 * p] * f[2 * p] : (q8[2 * p] * S) * f[2 * p];
-        const float v1 = fold ? q8[2 * p + 1] * f[2 * p + 1] : (q8[2 * p + 1] * S) * f[2 * p + 1];
-        od[2 * p] = sr_fp8_into(od[2 * p], v0, word << 16, i);
-        od[2 * p + 1] = sr_fp8_into(od[2 * p + 1], v1, word & 0xFFFF0000u, i);
       }
-    }
+    };
+    const float Sv = fold ? 1.0f : S;  // (q * 1 is q)
+    sr_rows([Sv](float q, float fe) { return (q * Sv) * fe; });
 #pragma unroll
     for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(lq + (64 * w + 8 * cg + e) * TR + 4 * rg) = od[e];
   };
-  // (waves 1-3) the staged tile of group g: 960 pieces, 5 per thread, each
-  // 64-piece run of one kind
   using v4u = __attribute__((ext_vector_type(4))) unsigned int;
   // (waves 1-3) the staged tile of group g in runs of 64 pieces of one kind,
   // run r = (w - 1) + 3 k: 8 runs of MXFP8 codes (a column's 32 rows as two
