@@ -593,54 +593,80 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (
 constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
 }  // namespace fws
 
-// ds_swizzle in bit-mask mode: the value of lane (l ^ d) within each group of
-// 32 lanes (d < 32)
-template <int D>
-__device__ inline float swz_xor(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1F));
+// quad_perm [1,0,3,2] and [2,3,0,1]: the value of lane l ^ 1 and of lane l ^ 2
+__device__ inline float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
-// The combine-path payload of one stored value y: the 32 lanes of a half-wave
-// hold one row's 32-column block (lane li = its column li).  Writes the lane's
-// int8 code at hv + hs and, from lane 0, the block's E8M0 byte at sv + ss
-// (v: the per-lane part of the offset, s: the wave-uniform part).
-__device__ inline void hmx8_value(float y, int li, __amdgpu_buffer_rsrc_t rH, __amdgpu_buffer_rsrc_t rS, uint32_t hv,
-                                  uint32_t hs, uint32_t sv, uint32_t ss) {
-  float o;
-  o = swz_xor<1>(y);
-  y = (li & 1) ? o - y : y + o;
-  o = swz_xor<2>(y);
-  y = (li & 2) ? o - y : y + o;
-  o = swz_xor<4>(y);
-  y = (li & 4) ? o - y : y + o;
-  o = swz_xor<8>(y);
-  y = (li & 8) ? o - y : y + o;
-  o = swz_xor<16>(y);
-  y = (li & 16) ? o - y : y + o;
-  float am = fabsf(y);
-  am = fmaxf(am, swz_xor<1>(am));
-  am = fmaxf(am, swz_xor<2>(am));
-  am = fmaxf(am, swz_xor<4>(am));
-  am = fmaxf(am, swz_xor<8>(am));
-  am = fmaxf(am, swz_xor<16>(am));
+// The combine-path payload of 16 rows x 32 columns of one 32 x 32 output
+// fragment (values in the wave's LDS block hb [16 rows][36 floats]): lane l
+// takes row l / 4, columns 8 (l % 4) .. + 7 of the block, so the transform's
+// distance-1, 2, 4 stages stay in the lane and the distance-8 and 16 stages
+// (and the block maximum) pair lanes l ^ 1 and l ^ 2.  Writes the lane's 8
+// int8 codes at row r0 + l / 4, column c0 + 8 (l % 4) of the payload and,
+// from lanes l % 4 == 0, the block's E8M0 byte.
+__device__ inline void hmx8_half(const float* hb, int l, __amdgpu_buffer_rsrc_t rH, __amdgpu_buffer_rsrc_t rS,
+                                 uint32_t r0, uint32_t c0, uint32_t N) {
+  const int r = l >> 2, q = l & 3;
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(hb + r * 36 + 8 * q);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(hb + r * 36 + 8 * q + 4);
+  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & h)) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  // distance 8 and 16: the partner is lane l ^ 1, then l ^ 2; the lower lane
+  // keeps a + b, the upper one a - b with a the lower lane's value
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = dpp_xor1(v[i]);
+    v[i] = (q & 1) ? o - v[i] : v[i] + o;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = dpp_xor2(v[i]);
+    v[i] = (q & 2) ? o - v[i] : v[i] + o;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+  am = fmaxf(am, dpp_xor1(am));
+  am = fmaxf(am, dpp_xor2(am));
   int ex = -127;
   if (am > 0.0f) {
     ex = __builtin_amdgcn_frexp_expf(am) - 1;
     ex = ex < -127 ? -127 : ex;
   }
-  float r = __builtin_rintf(__builtin_amdgcn_ldexpf(y, 6 - ex));
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)((int)r & 0xFF), rH, hv, hs, 0);
-  if (li == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(ex + 127), rS, sv, ss, 0);
+  uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float c = __builtin_rintf(__builtin_amdgcn_ldexpf(v[i], 6 - ex));
+    c = fminf(fmaxf(c, -127.0f), 127.0f);
+    const uint32_t b = ((uint32_t)(int)c & 0xFFu) << (8 * (i & 3));
+    if (i < 4) w0 |= b; else w1 |= b;
+  }
+  const uint32_t row = r0 + (uint32_t)r;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, rH, row * N + c0 + 8u * (uint32_t)q, 0, 0);
+  if (q == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(ex + 127), rS, row * (N / 32) + c0 / 32, 0, 0);
 }
 
 // HMX8 (float32 output only): the epilogue also writes the combine-path
 // payload of the stored values: per row and 32-column block, the Sylvester
-// H_32 transform as five butterfly stages across the block's 32 lanes
-// (partner distance 1, 2, 4, 8, 16; the lower position keeps a + b, the upper
-// a - b), the block's E8M0 exponent floor(log2 max|y|) (-127 for zeros) and
-// int8 codes rne(y 2^(6 - e)) clamped to +-127: the steps and float32
-// roundings of moe_hmx8_quant, byte for byte.
+// H_32 transform as five butterfly stages (partner distance 1, 2, 4, 8, 16;
+// the lower position keeps a + b, the upper a - b), the block's E8M0 exponent
+// floor(log2 max|y|) (-127 for zeros) and int8 codes rne(y 2^(6 - e))
+// clamped to +-127: the steps and float32 roundings of moe_hmx8_quant, byte
+// for byte.  A fragment's lane holds one column of each row; each half of the
+// fragment goes through a 2.3 KB LDS block of the wave to the quantiser's
+// layout (8 consecutive columns per lane: hmx8_half).
 template <bool OUT_BF16, int TN, bool HMX8 = false>
 __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
@@ -657,6 +683,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
   constexpr int S = C::S, STAGE = C::STAGE, I = C::I, NCW = C::NCW;
   __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE];
   __shared__ uint32_t s_nmt;
+  __shared__ __attribute__((aligned(16))) float hbuf[HMX8 ? NCW * 16 * 36 : 4];  // (HMX8) a block per consumer wave
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // total m-tiles (before any load into LDS is in flight)
@@ -792,7 +819,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
   const uint32_t ld = (uint32_t)N * ESZ;  // output row pitch in bytes
   const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * ESZ;
-  const uint32_t h_lane = (uint32_t)(g * 4) * (uint32_t)N + (uint32_t)li, s_lane = (uint32_t)(g * 4) * (uint32_t)(N / 32);
+  float* hb = hbuf + (HMX8 ? w * 16 * 36 : 0);  // (HMX8) this consumer wave's block
   MtCursor<TM> cur;
   uint32_t gs = 0;
   for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
@@ -848,9 +875,14 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
               __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(x), rC, lane_off, so, 2);
             else
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rC, lane_off, so, 2);
-            if constexpr (HMX8) {
-              const uint32_t r = (uint32_t)(wm + i * 32 + (v >> 2) * 8 + (v & 3)), c0 = (uint32_t)(n0 + wn + j * 32);
-              hmx8_value(x, li, rH, rS, h_lane, r * (uint32_t)N + c0, s_lane, r * (uint32_t)(N / 32) + c0 / 32);
+            if constexpr (HMX8) {  // row (v / 4) 8 + 4 g + v % 4 of the fragment, column li
+              hb[((v & 7) >> 2) * 8 * 36 + (g * 4 + (v & 3)) * 36 + li] = x;
+              if ((v & 7) == 7) {  // a 16-row half is in the block
+                asm volatile("" ::: "memory");
+                hmx8_half(hb, l, rH, rS, (uint32_t)(wm + i * 32 + (v >> 3) * 16), (uint32_t)(n0 + wn + j * 32),
+                          (uint32_t)N);
+                asm volatile("" ::: "memory");
+              }
             }
           }
         }
