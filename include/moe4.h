@@ -139,7 +139,9 @@ int moe4_debug_force_wait_timeout(int on);
  * q_i = e2m1_rne(fl(x_i * fl(1 / fl(dec(sc_m) * S)))) (signed zeros when sc_m
  * or the effective scale is 0); error = sequential float32 sum over i of
  * fl(t*t), t = fl(x_i - fl(fl(q_i*sc_m)*S)); 4 is kept iff err_4 < err_6.
- * cols % 16 == 0, n_groups >= 1.  ws: nvfp4_quant_46_ws_bytes(n_groups).
+ * cols % 16 == 0, n_groups >= 1.  ws: nvfp4_quant_46_ws_bytes(n_groups)
+ * (up to eight amax words per group, so that a tensor of few groups does not
+ * serialise its maxima on one word).
  */
 int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
                    const int32_t* group_row_off, int32_t n_groups, int mode, int pre_op,
@@ -150,8 +152,9 @@ size_t nvfp4_quant_46_ws_bytes(int32_t n_groups);
 /*
  * nvfp4_quant_46_noalloc - nvfp4_quant_46 without a workspace, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
- * serving loops, harnesses that forbid allocation).  Its scratch (one amax
- * word per group) is a static device array of the library, 4096 words (16 KB)
+ * serving loops, harnesses that forbid allocation).  Its scratch (the group
+ * amax words, nvfp4_quant_46_ws_bytes(n_groups)) is a static device array of
+ * the library, 4096 words (16 KB)
  * per device, held until the process ends; each call clears the words it
  * uses with a kernel first.  Arguments and results as nvfp4_quant_46 (byte
  * for byte), except: pre_op MOE4_PRE_NONE or MOE4_PRE_SILU only
@@ -383,7 +386,8 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const floa
  * up GEMM's epilogue (lhc.media page, the paragraph on fused kernels).
  * nvfp4_quant_46 with pre_op MOE4_PRE_SILU_AMAX and ws = silu_amax then
  * skips its own amax pass; the result is byte for byte that of
- * MOE4_PRE_SILU.  silu_amax: E words of device memory (the caller's).
+ * MOE4_PRE_SILU.  silu_amax: nvfp4_quant_46_ws_bytes(E) bytes of device
+ * memory (the caller's; the call writes its first E words).
  * Returns MOE4_EUNSUPPORTED (nothing launched) unless the shape selects the
  * warp-specialised kernels (K % 256 == 0, N % 128 == 0, 32-bit offsets).
  */

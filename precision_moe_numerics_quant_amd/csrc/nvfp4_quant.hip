@@ -140,12 +140,47 @@ struct WaveWalk {
 
 constexpr int QTHREADS = 256;
 
+// Group maxima of the amax walk: each group has `slots` words, and workgroup
+// b folds into word b % slots of its group, so that a tensor of one group
+// (thousands of workgroups) does not serialise all its atomics on one word.
+__host__ __device__ inline int amax_slots(int G) { return G <= 512 ? 8 : 1; }
+
+// End of a walk: the workgroup's waves combine their maxima of the same group
+// in LDS, then one atomic maximum per distinct group (waves walk consecutive
+// chunk ranges, so the groups come in ascending order).
+__device__ inline void amax_flush_wg(int gw, float t, bool has, uint32_t* amax_bits, int slots) {
+  __shared__ int s_g[QTHREADS / 64];
+  __shared__ float s_t[QTHREADS / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_g[w] = has ? gw : -1;
+    s_t[w] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t slot = blockIdx.x % (uint32_t)slots;
+    int g = -1;
+    float m = 0.0f;
+    for (int k = 0; k < QTHREADS / 64; ++k) {
+      if (s_g[k] < 0) continue;
+      if (s_g[k] != g) {
+        if (g >= 0) atomicMax(amax_bits + (size_t)g * slots + slot, __float_as_uint(m));
+        g = s_g[k];
+        m = 0.0f;
+      }
+      m = fmaxf(m, s_t[k]);
+    }
+    if (g >= 0) atomicMax(amax_bits + (size_t)g * slots + slot, __float_as_uint(m));  // m >= 0: bit order = value order
+  }
+}
+
 template <int DT, bool SILU>
 __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                    const int32_t* __restrict__ goff, int G,
                                                    uint32_t* __restrict__ amax_bits,
-                                                   const float* __restrict__ act_tab) {
+                                                   const float* __restrict__ act_tab, int slots) {
   using W = Walk<DT>;
+  const uint32_t slot = blockIdx.x % (uint32_t)slots;
   static_assert(!SILU || DT == MOE4_BF16, "SiLU applies to bf16 sources");
   const int64_t n = rows * cols, n_chunks = (n + W::CHUNK - 1) / W::CHUNK;
   const int l = threadIdx.x & 63;
@@ -210,11 +245,11 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
             }
             const int gp = group_from(goff, G, ww.gw, e / cols);
             if (gp == ww.gw) mf = fmaxf(mf, t);
-            else atomicMax(amax_bits + gp, __float_as_uint(t));
+            else atomicMax(amax_bits + (size_t)gp * slots + slot, __float_as_uint(t));
           }
         }
         const float t = wave_max(lane_amax());
-        if (l == 0) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+        if (l == 0) atomicMax(amax_bits + (size_t)ww.gw * slots + slot, __float_as_uint(t));
         pmax = 0u;
         nlo = 0x8000u;
         nhi = 0u;
@@ -224,8 +259,7 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
 #pragma unroll
       for (int k = 0; k < W::NLD; ++k) w[k] = wn[k];
     }
-    const float t = wave_max(lane_amax());
-    if (l == 0 && ww.c < ww.c_end) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+    amax_flush_wg(ww.gw, wave_max(lane_amax()), ww.c < ww.c_end, amax_bits, slots);
     return;
   }
   const float* tab = act_tab;  // (unused without SiLU)
@@ -261,11 +295,11 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
           for (int i = 0; i < W::EPL; ++i) t = fmaxf(t, fabsf(v[k][i]));
           const int gp = group_from(goff, G, ww.gw, e / cols);
           if (gp == ww.gw) m = fmaxf(m, t);
-          else atomicMax(amax_bits + gp, __float_as_uint(t));
+          else atomicMax(amax_bits + (size_t)gp * slots + slot, __float_as_uint(t));
         }
       }
       const float t = wave_max(m);
-      if (l == 0) atomicMax(amax_bits + ww.gw, __float_as_uint(t));
+      if (l == 0) atomicMax(amax_bits + (size_t)ww.gw * slots + slot, __float_as_uint(t));
       m = 0.0f;
       ww.advance(goff, G, (e_end - 1) / cols, cols);
     }
@@ -274,15 +308,16 @@ __global__ void __launch_bounds__(QTHREADS) k_amax(const void* __restrict__ x, i
 #pragma unroll
       for (int i = 0; i < W::EPL; ++i) v[k][i] = vn[k][i];
   }
-  const float t = wave_max(m);
-  if (l == 0 && ww.c < ww.c_end) atomicMax(amax_bits + ww.gw, __float_as_uint(t));  // t >= 0: bit order = value order
+  amax_flush_wg(ww.gw, wave_max(m), ww.c < ww.c_end, amax_bits, slots);
 }
 
 __global__ void k_tensor_scale(const uint32_t* __restrict__ amax_bits, int G, float m_max448,
-                               float* __restrict__ ts) {
+                               float* __restrict__ ts, int slots = 1) {
   int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= G) return;
-  float s = __uint_as_float(amax_bits[g]) / m_max448;
+  uint32_t b = 0u;
+  for (int k = 0; k < slots; ++k) b = max(b, amax_bits[(size_t)g * slots + k]);
+  float s = __uint_as_float(b) / m_max448;
   ts[g] = (s == 0.0f) ? 1.0f : s;
 }
 
@@ -914,7 +949,8 @@ __global__ void k_silu_eval(const uint16_t* __restrict__ u, int64_t n, float* __
 using namespace moe4;
 
 extern "C" size_t nvfp4_quant_46_ws_bytes(int32_t n_groups) {
-  return (size_t)(n_groups > 0 ? n_groups : 1) * sizeof(uint32_t);
+  const int g = n_groups > 0 ? n_groups : 1;
+  return (size_t)g * amax_slots(g) * sizeof(uint32_t);
 }
 
 extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t cols,
@@ -943,18 +979,24 @@ extern "C" int nvfp4_quant_46(const void* x, int dtype, int64_t rows, int64_t co
   }
   uint32_t* amax = static_cast<uint32_t*>(ws);
   const int G = n_groups;
-  if (!amax_given) hipLaunchKernelGGL(k_zero_u32, dim3((G + 255) / 256), dim3(256), 0, s, amax, G);
+  // (with the amax given, ws holds one word per group; the walk uses slots)
+  const int slots = amax_given ? 1 : amax_slots(G);
+  if (!amax_given)
+    hipLaunchKernelGGL(k_zero_u32, dim3((G * slots + 255) / 256), dim3(256), 0, s, amax, G * slots);
   if (rows > 0 && !amax_given) {
     const dim3 grid = walk_grid(rows * cols);
     if (dtype == MOE4_BF16 && pre_op == MOE4_PRE_SILU)
-      hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, true>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab,
+                         slots);
     else if (dtype == MOE4_BF16)
-      hipLaunchKernelGGL((k_amax<MOE4_BF16, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_BF16, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab,
+                         slots);
     else
-      hipLaunchKernelGGL((k_amax<MOE4_F32, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab);
+      hipLaunchKernelGGL((k_amax<MOE4_F32, false>), grid, dim3(QTHREADS), 0, s, x, rows, cols, group_row_off, G, amax, tab,
+                         slots);
   }
   const float m448 = (mode == MOE4_NVFP4_4OVER6) ? 4.0f * 448.0f : 6.0f * 448.0f;
-  hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, m448, tensor_scale);
+  hipLaunchKernelGGL(k_tensor_scale, dim3((G + 255) / 256), dim3(256), 0, s, amax, G, m448, tensor_scale, slots);
   if (rows > 0) {
     const int64_t nblk = rows * (cols / 16);
     dim3 grid((unsigned)((nblk + ENC_THREADS - 1) / ENC_THREADS));
@@ -1005,9 +1047,9 @@ extern "C" int nvfp4_quant_46_noalloc(const void* x, int dtype, int64_t rows, in
   uint32_t* ws = nullptr;
   int rc = scratch_device_ptr(&ws);
   if (rc) return rc;
-  // nvfp4_quant_46 clears the n_groups amax words with a kernel before use
+  // nvfp4_quant_46 clears its amax words (at most 4096) with a kernel before use
   return nvfp4_quant_46(x, dtype, rows, cols, group_row_off, n_groups, mode, pre_op, codes, sf, tensor_scale, ws,
-                        (size_t)n_groups * sizeof(uint32_t), stream);
+                        nvfp4_quant_46_ws_bytes(n_groups), stream);
 }
 
 // Workgroups of k_wq_resident the device holds at once (its launch needs
