@@ -67,6 +67,36 @@ __device__ inline Cand encode_candidate(const float* x, float amax_b, float S, f
   return c;
 }
 
+// encode_candidate for a block whose scale byte and effective scale are
+// nonzero and whose reciprocal is finite (ok = true): the same steps and
+// float32 roundings without the branches of those cases.  ok = false means
+// the caller must use encode_candidate (its result is then not used).
+__device__ inline Cand encode_candidate_fast(const float* x, float amax_b, float S, float m, bool& ok) {
+  Cand c;
+  const float d = m * S;
+  const float u = amax_b / d;
+  c.sc = e4m3_rne_u(u);
+  const float scf = e4m3_to_f32(c.sc);
+  const float eff = scf * S;
+  const float inv = 1.0f / eff;
+  ok = c.sc != 0u && eff != 0.0f && !__builtin_isinf(inv);
+  const float mant = mant_factor(scf);
+  uint32_t q0 = 0, q1 = 0;
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[i] * inv, x[i + 1] * inv, 1.0f, 0) & 0xFFu;
+    if (i < 8) q0 |= pk << (4 * i); else q1 |= pk << (4 * (i - 8));
+    const f32x2 p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, scf, 0);
+    const float t0 = x[i] - (p[0] * mant) * S;
+    const float t1 = x[i + 1] - (p[1] * mant) * S;
+    err = err + t0 * t0;
+    err = err + t1 * t1;
+  }
+  c.q[0] = q0; c.q[1] = q1; c.err = err;
+  return c;
+}
+
 // One half (8 elements) of a 16-block under candidate m, without the error
 // sum: the scale byte and the 8 codes packed as 4 bytes (element 2p in the
 // low nibble of byte p).  The same steps as encode_candidate, so the codes are

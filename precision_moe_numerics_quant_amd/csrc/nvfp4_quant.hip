@@ -334,16 +334,25 @@ __global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__
   const int64_t nbr = cols / 16;
   // bpt blocks per thread (SiLU: amortises the table staging)
   for (int it = 0; it < bpt; ++it) {
-  const int64_t blk = ((int64_t)blockIdx.x * bpt + it) * ENC_THREADS + threadIdx.x;
+  const int64_t blk0 = ((int64_t)blockIdx.x * bpt + it) * ENC_THREADS + (threadIdx.x & ~63);  // the wave's first block
+  const int64_t blk = blk0 + (threadIdx.x & 63);
   if (blk >= rows * nbr) return;
-  const int64_t r = blk / nbr;
-  // group of the row: one search per wave (uniform: scalar loads) from the
-  // wave's first row, then a short step forward for lanes past a boundary
-  const int64_t r_wave = (int64_t)__builtin_amdgcn_readfirstlane((int)(r & 0x7FFFFFFF)) |
-                         ((int64_t)__builtin_amdgcn_readfirstlane((int)(r >> 31)) << 31);
-  int g = __builtin_amdgcn_readfirstlane(group_of_row(goff, G, r_wave));
-  if (goff != nullptr && g + 1 < G && (int64_t)goff[g + 1] <= r)  // (goff[g + 1]: a scalar load)
-    while (g + 1 < G && (int64_t)goff[g + 1] <= r) ++g;
+  int g = 0;
+  if (goff != nullptr) {
+    // group of the row: the wave's first row by one scalar division and one
+    // search (uniform: scalar loads), the lane's row by stepping from there
+    const int64_t bw = (int64_t)__builtin_amdgcn_readfirstlane((int)(blk0 & 0x7FFFFFFF)) |
+                       ((int64_t)__builtin_amdgcn_readfirstlane((int)(blk0 >> 31)) << 31);
+    const int64_t r_wave = bw / nbr;
+    int64_t r = r_wave, rem = bw - r_wave * nbr + (threadIdx.x & 63);
+    while (rem >= nbr) {
+      rem -= nbr;
+      ++r;
+    }
+    g = __builtin_amdgcn_readfirstlane(group_of_row(goff, G, r_wave));
+    if (g + 1 < G && (int64_t)goff[g + 1] <= r)  // (goff[g + 1]: a scalar load)
+      while (g + 1 < G && (int64_t)goff[g + 1] <= r) ++g;
+  }
   const float S = ts[g];
   float v[16];
   load8<DT, SILU>(x, blk * 16, v, tab);
@@ -351,11 +360,17 @@ __global__ void __launch_bounds__(ENC_THREADS) k_encode(const void* __restrict__
   float amax_b = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
-  Cand best = encode_candidate(v, amax_b, S, 6.0f);
-  if (FOUR_OVER_SIX) {
-    Cand c4 = encode_candidate(v, amax_b, S, 4.0f);
-    if (c4.err < best.err) best = c4;
+  // the common case without the zero-scale and infinite-reciprocal branches;
+  // a wave with a lane in either case redoes both candidates with them
+  bool ok6 = true, ok4 = true;
+  Cand best = encode_candidate_fast(v, amax_b, S, 6.0f, ok6);
+  Cand c4;
+  if (FOUR_OVER_SIX) c4 = encode_candidate_fast(v, amax_b, S, 4.0f, ok4);
+  if (__builtin_expect(__any(!(ok6 && ok4)), 0)) {
+    best = encode_candidate(v, amax_b, S, 6.0f);
+    if (FOUR_OVER_SIX) c4 = encode_candidate(v, amax_b, S, 4.0f);
   }
+  if (FOUR_OVER_SIX && c4.err < best.err) best = c4;
   *reinterpret_cast<u32x2*>(codes + blk * 8) = u32x2{best.q[0], best.q[1]};
   sf[blk] = (uint8_t)best.sc;
   }
