@@ -55,6 +55,11 @@ __host__ __device__ inline uint32_t fmix32(uint32_t h) {
   h *= 0x85EBCA6Bu;
   h ^= h >> 13;
   h *= 0xC2B2AE35u;
+#if defined(__HIP_DEVICE_COMPILE__)
+  // the product through an empty asm: otherwise the compiler turns a caller's
+  // left shift of the result into a third (quarter-rate) 32-bit multiply
+  asm("" : "+v"(h));
+#endif
   h ^= h >> 16;
   return h;
 }
@@ -85,16 +90,55 @@ __device__ inline float mant_factor(float s) {
   return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
 }
 
-// Wave-wide reductions (wave64).
+// Cross-lane moves without LDS: DPP within each row of 16 lanes, and the
+// permlane swaps between rows (each returns the value of lane l and of lane
+// l ^ 16, or l ^ 32, in its two results).
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]: lane l ^ 1
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]: lane l ^ 2
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane 7 - l within each 8
+constexpr int DPP_XOR8 = 0x128;         // row_ror 8: lane l ^ 8 within each 16
+__device__ inline float lane_xor1(float v) { return __uint_as_float(dpp_u<DPP_XOR1>(__float_as_uint(v))); }
+__device__ inline float lane_xor2(float v) { return __uint_as_float(dpp_u<DPP_XOR2>(__float_as_uint(v))); }
+__device__ inline float lane_xor8(float v) { return __uint_as_float(dpp_u<DPP_XOR8>(__float_as_uint(v))); }
+// max of the values of lanes l and l ^ 16 / l ^ 32
+__device__ inline float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline uint32_t umax_xor16(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+__device__ inline uint32_t umax_xor32(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+
+// Wave-wide reductions (wave64): the maximum in every lane (each step pairs the two halves of a
+// group of lanes: 2, 4, 8, 16, 32, 64).
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, lane_xor1(v));
+  v = fmaxf(v, lane_xor2(v));
+  v = fmaxf(v, __uint_as_float(dpp_u<DPP_HALF_MIRROR>(__float_as_uint(v))));
+  v = fmaxf(v, lane_xor8(v));
+  v = max_xor16(v);
+  return max_xor32(v);
 }
 __device__ inline uint32_t wave_umax(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
+  v = max(v, dpp_u<DPP_XOR1>(v));
+  v = max(v, dpp_u<DPP_XOR2>(v));
+  v = max(v, dpp_u<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_u<DPP_XOR8>(v));
+  v = umax_xor16(v);
+  return umax_xor32(v);
 }
 
 }  // namespace moe4

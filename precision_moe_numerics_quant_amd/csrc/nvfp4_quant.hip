@@ -667,11 +667,6 @@ constexpr int WAVES = 4, THREADS = 64 * WAVES, TR = 32, TC = 256, MIN_BLOCKS = 3
 constexpr int MAX_TILES = 768;
 }
 
-template <int D>
-__device__ inline float wr_xor(float v) {  // lane l ^ D within each 32 lanes (D < 32)
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1F));
-}
-
 template <bool FAST>
 __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
     k_wq_resident(const float* __restrict__ x, int64_t C, int64_t grows, int G, uint32_t wait_extra,
@@ -783,7 +778,7 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
       float a = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-      a = fmaxf(a, wr_xor<1>(a));  // the block's other half
+      a = fmaxf(a, lane_xor1(a));  // the block's other half
       // encode_half's steps; its zero-scale and infinite-reciprocal cases
       // (tiny values) go through it whenever a lane of the wave meets one
       const uint32_t sc = e4m3_rne_u(a / d6);
@@ -810,15 +805,19 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
     }
     const bool fold = fold_scale_ok(S);
     float f[8];
+    int exs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      am[e] = fmaxf(am[e], wr_xor<8>(am[e]));
-      am[e] = fmaxf(am[e], wr_xor<16>(am[e]));
-      am[e] = fmaxf(am[e], __shfl_xor(am[e], 32, 64));
+      am[e] = fmaxf(am[e], lane_xor8(am[e]));
+      am[e] = max_xor32(max_xor16(am[e]));
       const int ex = mx_exponent(am[e] * S);
       const float pc = __builtin_amdgcn_ldexpf(1.0f, -ex);
       f[e] = fold ? (ex == -127 ? 0.0f : S * pc) : pc;
-      if (rg == 0) lmxs[64 * w + 8 * cg + e] = (uint8_t)(ex + 127);
+      exs[e] = ex;
+    }
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lmxs[64 * w + 8 * cg + e] = (uint8_t)(exs[e] + 127);
     }
     uint32_t od[8];
 #pragma unroll
