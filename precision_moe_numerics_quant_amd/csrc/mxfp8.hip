@@ -64,10 +64,8 @@ __device__ inline void mx_quant_pair_T(const float (&v)[8][2], int rseg, int64_t
     a0 = fmaxf(a0, fabsf(v[i][0]));
     a1 = fmaxf(a1, fabsf(v[i][1]));
   }
-  a0 = fmaxf(a0, __shfl_xor(a0, 16, 64));
-  a1 = fmaxf(a1, __shfl_xor(a1, 16, 64));
-  a0 = fmaxf(a0, __shfl_xor(a0, 32, 64));
-  a1 = fmaxf(a1, __shfl_xor(a1, 32, 64));
+  a0 = max_xor32(max_xor16(a0));
+  a1 = max_xor32(max_xor16(a1));
   const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
   const float p0 = __builtin_amdgcn_ldexpf(1.0f, -e0), p1 = __builtin_amdgcn_ldexpf(1.0f, -e1);
   uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
@@ -309,8 +307,8 @@ k_mx_quant_requant_T(const float* __restrict__ x, int64_t C, int64_t grows, uint
         float a = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));  // the row block's other three lanes
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        a = fmaxf(a, lane_xor1(a));  // the row block's other three lanes
+        a = fmaxf(a, lane_xor2(a));
         const int e = mx_exponent(a);
         const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
         // RNE per value, two values per conversion (bytes 0-1, then 2-3)
@@ -501,7 +499,7 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
         v[i] = lv[cl0 + i][rr];
         a = fmaxf(a, fabsf(v[i]));
       }
-      a = fmaxf(a, __shfl_xor(a, 1, 64));
+      a = fmaxf(a, lane_xor1(a));
       const int e = mx_exponent(a);
       const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
       const int64_t r_out = t.src0 + rr, cg = c0 + cl0;
