@@ -69,14 +69,26 @@ __device__ inline void mx_quant_pair_T(const float (&v)[8][2], int rseg, int64_t
   const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
   const float p0 = __builtin_amdgcn_ldexpf(1.0f, -e0), p1 = __builtin_amdgcn_ldexpf(1.0f, -e1);
   uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+  if (SR) {
+    // pair index of (row src_row0 + i, column c): j0 + i C / 2 (c even)
+    const uint64_t j0 = (uint64_t)(src_row0 * C + c) >> 1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-    if (SR) word = sr_word(base, (uint64_t)((src_row0 + i) * C + c) >> 1);
-    uint32_t b0 = mx_round<SR>(v[i][0] * p0, word & 0xFFFFu);
-    uint32_t b1 = mx_round<SR>(v[i][1] * p1, word >> 16);
-    if (i < 4) { lo0 |= b0 << (8 * i); lo1 |= b1 << (8 * i); }
-    else { hi0 |= b0 << (8 * (i - 4)); hi1 |= b1 << (8 * (i - 4)); }
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = sr_word(base, j0 + (uint64_t)i * (uint64_t)(C >> 1));
+      const uint32_t b0 = mx_round<SR>(v[i][0] * p0, word & 0xFFFFu);
+      const uint32_t b1 = mx_round<SR>(v[i][1] * p1, word >> 16);
+      if (i < 4) { lo0 |= b0 << (8 * i); lo1 |= b1 << (8 * i); }
+      else { hi0 |= b0 << (8 * (i - 4)); hi1 |= b1 << (8 * (i - 4)); }
+    }
+  } else {  // RNE, two values per conversion (each value converted on its own)
+    lo0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0][0] * p0, v[1][0] * p0, 0, false);
+    lo0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2][0] * p0, v[3][0] * p0, (int)lo0, true);
+    hi0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4][0] * p0, v[5][0] * p0, 0, false);
+    hi0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6][0] * p0, v[7][0] * p0, (int)hi0, true);
+    lo1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0][1] * p1, v[1][1] * p1, 0, false);
+    lo1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2][1] * p1, v[3][1] * p1, (int)lo1, true);
+    hi1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4][1] * p1, v[5][1] * p1, 0, false);
+    hi1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6][1] * p1, v[7][1] * p1, (int)hi1, true);
   }
   *reinterpret_cast<u32x2*>(out_c0) = u32x2{lo0, hi0};
   *reinterpret_cast<u32x2*>(out_c1) = u32x2{lo1, hi1};
@@ -399,6 +411,69 @@ __device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64
   return load4<DT>(g.x, r * C + c);
 }
 
+// grad_vals4 for 16 consecutive columns c .. c + 15 (c % 16 == 0, C % 16 ==
+// 0): the source row (and its map and scale) resolved once, 16-byte loads.
+template <int DT, int MODE>
+__device__ inline void grad_vals16(const GradSrc& g, int64_t r, int64_t C, int64_t c, const float* dtab,
+                                   float (&v)[16]) {
+  int64_t src = r;
+  float sc = 1.0f;
+  if (MODE == 1) {
+    const int32_t a = g.row_map[r];
+    if (g.row_scale) sc = g.row_scale[a];
+    src = a / g.map_div;
+  }
+  const int64_t idx = src * C + c;
+  if (MODE == 3) {  // (x holds bf16 bits)
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.x) + idx);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 u = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = act_eval<false>(u[j] & 0xFFFFu, dtab);
+        v[8 * q + 2 * j + 1] = act_eval<false>(u[j] >> 16, dtab);
+      }
+    }
+    return;
+  }
+  if (DT == MOE4_F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(g.x) + idx);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 t = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = t[j];
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.x) + idx);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 u = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = bf16_bits_to_f32(u[j] & 0xFFFFu);
+        v[8 * q + 2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+      }
+    }
+  }
+  if (MODE == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = sc * v[i];
+  } else if (MODE == 2) {
+    const u32x4* pu = reinterpret_cast<const u32x4*>(g.dsilu_src + r * C + c);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 u = pu[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = v[8 * q + 2 * j] * act_eval<true>(u[j] & 0xFFFFu, dtab);
+        v[8 * q + 2 * j + 1] = v[8 * q + 2 * j + 1] * act_eval<true>(u[j] >> 16, dtab);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------- row-wise gradient quant
 template <int DT, int MODE, bool SR>
 __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C, uint32_t base,
@@ -480,13 +555,15 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
   const int tid = threadIdx.x;
   {  // stage: thread -> row tid/8, 16 columns at (tid%8)*16
     const int rr = tid >> 3, cc = (tid & 7) * 16;
-    const bool ok = rr < t.nvalid && c0 + cc < C;
+    float v[16];
+    if (rr < t.nvalid && c0 + cc < C) {
+      grad_vals16<DT, MODE>(g, t.src0 + rr, C, c0 + cc, tab, v);
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v = ok ? grad_vals4<DT, MODE>(g, t.src0 + rr, C, c0 + cc + 4 * q, tab) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lv[cc + 4 * q + j][rr] = v[j];
+      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[cc + j][rr] = v[j];
   }
   __syncthreads();
   if (ROWS) {  // thread pair -> (row, 32-column block); each thread 16 columns
