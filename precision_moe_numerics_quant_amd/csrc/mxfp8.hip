@@ -25,6 +25,7 @@ namespace moe4 {
 constexpr int TR = 32;    // rows per tile (one MX block)
 constexpr int TC = 128;   // columns per tile
 constexpr int MXT = 256;  // threads
+constexpr int MX_T_CPW = 4;  // column tiles per workgroup of the transposed kernels that stage a table
 
 __device__ inline int find_group(const int32_t* off, int G, int64_t r) {
   int lo = 0, hi = G - 1;
@@ -525,7 +526,7 @@ __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C
 template <int DT, int MODE, bool SR, bool ROWS>
 __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, const int32_t* __restrict__ off,
                                               const int32_t* __restrict__ offp, int G, int64_t max_pr, int64_t n_ct,
-                                              uint32_t base, int sfb,
+                                              int cpw, uint32_t base, int sfb,
                                               uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
                                               const float* __restrict__ act_tab, uint8_t* __restrict__ row_c,
                                               uint8_t* __restrict__ row_s) {
@@ -538,80 +539,87 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
   // runs per XCD), so its L2 merges the quarters into whole lines before they
   // go out.  For gathered rows (MODE 1) the column tiles of one row tile run
   // together instead, so they share the gathered source rows in L2 (measured:
-  // each order is the faster one for its mode).
-  int64_t ct, rt;
+  // each order is the faster one for its mode).  A workgroup takes cpw
+  // column tiles of its row tile in turn (the table staged once).
+  const int64_t n_cw = (n_ct + cpw - 1) / cpw;
+  int64_t cw, rt;
   if (MODE == 1) {
-    ct = blockIdx.x % n_ct;
-    rt = blockIdx.x / n_ct;
+    cw = blockIdx.x % n_cw;
+    rt = blockIdx.x / n_cw;
   } else {
     const int64_t n_all = (int64_t)gridDim.x / N_XCD * N_XCD;
-    const int64_t b = xcd_tile(blockIdx.x, n_all), span = b / (4 * n_ct), in_span = b - span * 4 * n_ct;
-    ct = in_span >> 2;
+    const int64_t b = xcd_tile(blockIdx.x, n_all), span = b / (4 * n_cw), in_span = b - span * 4 * n_cw;
+    cw = in_span >> 2;
     rt = span * 4 + (in_span & 3);
   }
   TileT t;
   if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
-  const int64_t c0 = ct * TC;
   const int tid = threadIdx.x;
-  {  // stage: thread -> row tid/8, 16 columns at (tid%8)*16
-    const int rr = tid >> 3, cc = (tid & 7) * 16;
-    float v[16];
-    if (rr < t.nvalid && c0 + cc < C) {
-      grad_vals16<DT, MODE>(g, t.src0 + rr, C, c0 + cc, tab, v);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lv[cc + j][rr] = v[j];
-  }
-  __syncthreads();
-  if (ROWS) {  // thread pair -> (row, 32-column block); each thread 16 columns
-    const int pair = tid >> 1, half = tid & 1, rr = pair >> 2, blk = pair & 3, cl0 = 32 * blk + 16 * half;
-    if (rr < t.nvalid && c0 + 32 * blk < C) {  // (C % 32 == 0: whole blocks; both threads of a pair agree)
+  const int64_t ct_end = (cw + 1) * cpw < n_ct ? (cw + 1) * cpw : n_ct;
+  for (int64_t ct = cw * cpw; ct < ct_end; ++ct) {
+    const int64_t c0 = ct * TC;
+    if (ct != cw * cpw) __syncthreads();  // (the previous tile's readers are done with lv)
+    {  // stage: thread -> row tid/8, 16 columns at (tid%8)*16
+      const int rr = tid >> 3, cc = (tid & 7) * 16;
       float v[16];
-      float a = 0.0f;
+      if (rr < t.nvalid && c0 + cc < C) {
+        grad_vals16<DT, MODE>(g, t.src0 + rr, C, c0 + cc, tab, v);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        v[i] = lv[cl0 + i][rr];
-        a = fmaxf(a, fabsf(v[i]));
+        for (int j = 0; j < 16; ++j) v[j] = 0.0f;
       }
-      a = fmaxf(a, lane_xor1(a));
-      const int e = mx_exponent(a);
-      const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
-      const int64_t r_out = t.src0 + rr, cg = c0 + cl0;
-      uint32_t ow[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t w0 = 0, w1 = 0;
-        if (SR) {
-          const uint64_t i0 = (uint64_t)(r_out * C + cg + 4 * q);
-          w0 = sr_word(base, i0 >> 1);
-          w1 = sr_word(base, (i0 >> 1) + 1);
-        }
-        ow[q] = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu) | (mx_round<SR>(v[4 * q + 1] * p, w0 >> 16) << 8) |
-                (mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu) << 16) | (mx_round<SR>(v[4 * q + 3] * p, w1 >> 16) << 24);
-      }
-      *reinterpret_cast<u32x4*>(row_c + r_out * C + cg) = u32x4{ow[0], ow[1], ow[2], ow[3]};
-      if (half == 0) row_s[r_out * (C / 32) + cg / 32] = (uint8_t)(e + 127);
+      for (int j = 0; j < 16; ++j) lv[cc + j][rr] = v[j];
     }
-  }
-  const int w = tid >> 6, l = tid & 63;
-  if (c0 + 32 * w >= C) return;
-  const int cp = l & 15, rseg = l >> 4;
-  const int cl = 32 * w + 2 * cp;
-  float v[8][2];
+    __syncthreads();
+    if (ROWS) {  // thread pair -> (row, 32-column block); each thread 16 columns
+      const int pair = tid >> 1, half = tid & 1, rr = pair >> 2, blk = pair & 3, cl0 = 32 * blk + 16 * half;
+      if (rr < t.nvalid && c0 + 32 * blk < C) {  // (C % 32 == 0: whole blocks; both threads of a pair agree)
+        float v[16];
+        float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i][0] = lv[cl][rseg * 8 + i];
-    v[i][1] = lv[cl + 1][rseg * 8 + i];
+        for (int i = 0; i < 16; ++i) {
+          v[i] = lv[cl0 + i][rr];
+          a = fmaxf(a, fabsf(v[i]));
+        }
+        a = fmaxf(a, lane_xor1(a));
+        const int e = mx_exponent(a);
+        const float p = __builtin_amdgcn_ldexpf(1.0f, -e);
+        const int64_t r_out = t.src0 + rr, cg = c0 + cl0;
+        uint32_t ow[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w0 = 0, w1 = 0;
+          if (SR) {
+            const uint64_t i0 = (uint64_t)(r_out * C + cg + 4 * q);
+            w0 = sr_word(base, i0 >> 1);
+            w1 = sr_word(base, (i0 >> 1) + 1);
+          }
+          ow[q] = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu) | (mx_round<SR>(v[4 * q + 1] * p, w0 >> 16) << 8) |
+                  (mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu) << 16) |
+                  (mx_round<SR>(v[4 * q + 3] * p, w1 >> 16) << 24);
+        }
+        *reinterpret_cast<u32x4*>(row_c + r_out * C + cg) = u32x4{ow[0], ow[1], ow[2], ow[3]};
+        if (half == 0) row_s[r_out * (C / 32) + cg / 32] = (uint8_t)(e + 127);
+      }
+    }
+    const int w = tid >> 6, l = tid & 63;
+    if (c0 + 32 * w >= C) continue;
+    const int cp = l & 15, rseg = l >> 4;
+    const int cl = 32 * w + 2 * cp;
+    float v[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i][0] = lv[cl][rseg * 8 + i];
+      v[i][1] = lv[cl + 1][rseg * 8 + i];
+    }
+    const int64_t c = c0 + cl;
+    const int64_t orow = t.pr_in_g + rseg * 8;
+    uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
+    // scale of (column c, block pr_in_g / 32): row-major [C][P/32] or block-major [P/32][C]
+    uint8_t* s0 = out_s + t.out_base / 32 + (sfb ? (t.pr_in_g / 32) * C + c : c * (t.P / 32) + t.pr_in_g / 32);
+    mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + (sfb ? 1 : t.P / 32));
   }
-  const int64_t c = c0 + cl;
-  const int64_t orow = t.pr_in_g + rseg * 8;
-  uint8_t* o0 = out_c + t.out_base + c * t.P + orow;
-  // scale of (column c, block pr_in_g / 32): row-major [C][P/32] or block-major [P/32][C]
-  uint8_t* s0 = out_s + t.out_base / 32 + (sfb ? (t.pr_in_g / 32) * C + c : c * (t.P / 32) + t.pr_in_g / 32);
-  mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + (sfb ? 1 : t.P / 32));
 }
 
 template <int DT, int MODE>
@@ -625,23 +633,26 @@ static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int
     else hipLaunchKernelGGL((k_mx_rows<DT, MODE, false>), grid, dim3(256), 0, s, g, R, C, base, oc, os, tab);
   } else {
     const int64_t n_ct = (C + TC - 1) / TC, n_rt = (max_pr + TR - 1) / TR;
+    // column tiles per workgroup: MX_T_CPW with a table to stage, else 1
+    const int cpw = MODE >= 2 ? MX_T_CPW : 1;
+    const int64_t n_cw = (n_ct + cpw - 1) / cpw;
     // (MODE != 1: four row tiles per span and a multiple of 8 workgroups;
     // tiles past the padded extent exit)
-    dim3 grid((unsigned)(MODE == 1 ? n_ct * n_rt : xcd_grid(n_ct * ((n_rt + 3) / 4 * 4))));
+    dim3 grid((unsigned)(MODE == 1 ? n_cw * n_rt : xcd_grid(n_cw * ((n_rt + 3) / 4 * 4))));
     const int sfb = transpose == 2;
     if (rc) {
       if (sr)
         hipLaunchKernelGGL((k_mx_T<DT, MODE, true, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
-                           base, sfb, oc, os, tab, rc, rs);
+                           cpw, base, sfb, oc, os, tab, rc, rs);
       else
         hipLaunchKernelGGL((k_mx_T<DT, MODE, false, true>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
-                           base, sfb, oc, os, tab, rc, rs);
+                           cpw, base, sfb, oc, os, tab, rc, rs);
     } else if (sr) {
       hipLaunchKernelGGL((k_mx_T<DT, MODE, true, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
-                         base, sfb, oc, os, tab, nullptr, nullptr);
+                         cpw, base, sfb, oc, os, tab, nullptr, nullptr);
     } else {
       hipLaunchKernelGGL((k_mx_T<DT, MODE, false, false>), grid, dim3(MXT), 0, s, g, R, C, off, offp, G, max_pr, n_ct,
-                         base, sfb, oc, os, tab, nullptr, nullptr);
+                         cpw, base, sfb, oc, os, tab, nullptr, nullptr);
     }
   }
 }
