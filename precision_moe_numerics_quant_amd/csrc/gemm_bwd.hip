@@ -953,6 +953,46 @@ __global__ void __launch_bounds__(wsg::NT, 1)
 // kernel above: 128 code bytes and 4 scale bytes per row and slab, scales
 // row-major.  TN = 128 (four stages) or 256 (three stages: consumers of
 // 64 x 128, half the operand bytes per MFMA).
+// Tile order of the persistent dgrad.  The 8 XCDs work side by side on one
+// band of SM = (8 / xb) pm m-tiles at a time: XCD x takes the pm x pn
+// rectangle (x / xb, x % xb) of the band (pn n-tiles, n fastest), its
+// workgroups the rectangle's tiles in turn, then the next band.  Each XCD's
+// L2 then holds pm A row blocks and pn B row blocks per band, and the XCDs
+// read the same experts' B rows at about the same time (shared in the
+// Infinity Cache).  q: the XCD's own tile counter.
+struct DgSplit {
+  uint32_t pm, pn, xb;
+  __device__ bool tile(uint32_t x, uint32_t q, uint32_t n_mt, uint32_t n_nt, uint32_t& mi, uint32_t& nt) const {
+    const uint32_t ppn = pm * pn, sb = q / ppn, r = q - sb * ppn, a = r / pn;
+    mi = sb * (8 / xb) * pm + (x / xb) * pm + a;
+    nt = (x % xb) * pn + (r - a * pn);
+    return mi < n_mt && nt < n_nt;
+  }
+};
+
+// The rectangle with the fewest operand rows per tile (TM-row A blocks,
+// TN-row B blocks), counting n-tiles past n_nt as waste: pm pn <= 32 (one
+// tile per workgroup of an XCD of 32 CUs at a time).  A B row (the
+// requantised weights, met first in HBM) counts three A rows: measured on the
+// layer's two dgrads, the order with the fewest B rows per XCD is the
+// fastest of those with the same total.
+static DgSplit dg_split(int64_t n_nt, int tm, int tn) {
+  DgSplit best{1, 1, 1};
+  double best_cost = 1e300;
+  for (uint32_t xb = 1; xb <= 8; xb *= 2) {
+    const uint32_t pn = (uint32_t)((n_nt + xb - 1) / xb);
+    if (pn > 32) continue;
+    const uint32_t pm = 32 / pn;
+    const double cost =
+        ((double)pm * tm + 3.0 * pn * tn) / ((double)pm * pn) * ((double)xb * pn / (double)n_nt);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = DgSplit{pm, pn, xb};
+    }
+  }
+  return best;
+}
+
 namespace dws {
 constexpr int TM = 128, NCW = 4, NT = 64 * (NCW + 4);
 template <int TN>
@@ -971,7 +1011,7 @@ template <bool OUT_BF16, int TN>
 __global__ void __launch_bounds__(dws::NT, 1)
     k_dgrad_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
                const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
-               const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N, int64_t K,
+               const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N, int64_t K, DgSplit sp,
                void* __restrict__ c) {
   using namespace dws;
   using dmag::lds_ptr;
@@ -993,11 +1033,11 @@ __global__ void __launch_bounds__(dws::NT, 1)
     if (l == 0) s_nmt = n;
   }
   __syncthreads();
-  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;
+  const uint32_t n_nt = (uint32_t)(N / TN), n_mt = s_nmt;
   const uint32_t KS = (uint32_t)(K / 32), nk = (uint32_t)(K / BK);
-  const uint32_t xcd = blockIdx.x % 8, per = (n_all + 7) / 8;
-  const uint32_t stride = (gridDim.x - xcd + 7) / 8;
-  const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
+  // this workgroup's tiles: q = q0, q0 + stride, ... of its XCD (see DgSplit)
+  const uint32_t xcd = blockIdx.x % 8, stride = (gridDim.x - xcd + 7) / 8, q0 = blockIdx.x / 8;
+  const uint32_t sm = (8 / sp.xb) * sp.pm, q_end = (n_mt + sm - 1) / sm * (sp.pm * sp.pn);
 
   if (w >= NCW) {
     // ---- producer pw: rows 32 pw .. 32 pw + 31 of A's codes, TN / 4 rows of
@@ -1023,13 +1063,15 @@ __global__ void __launch_bounds__(dws::NT, 1)
       }
     };
     MtCursor<TM> cur;
-    uint32_t pt = t0, ps = 0;
+    uint32_t pt = q0, ps = 0;
     bool more = false;
     auto seek = [&]() {
-      more = pt < t_end && cur.seek(off, E, pt / n_nt);
+      uint32_t mi = 0, nt = 0;
+      while (pt < q_end && !sp.tile(xcd, pt, n_mt, n_nt, mi, nt)) pt += stride;
+      more = pt < q_end && cur.seek(off, E, mi);
       if (!more) return;
       const int e = cur.e;
-      const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
+      const uint32_t mt = mi - cur.first;
       const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
       rbc = make_rsrc(b_codes + (int64_t)e * N * K, (uint64_t)N * K);
       rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
@@ -1155,9 +1197,12 @@ __global__ void __launch_bounds__(dws::NT, 1)
   const uint32_t lane_off = (uint32_t)(g * 4) * ld + (uint32_t)li * ESZ;
   MtCursor<TM> cur;
   uint32_t gs = 0;
-  for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
+  for (uint32_t q = q0; q < q_end; q += stride) {
+    uint32_t mi, nt;
+    if (!sp.tile(xcd, q, n_mt, n_nt, mi, nt)) continue;
+    if (!cur.seek(off, E, mi)) break;
     const int e = cur.e;
-    const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
+    const uint32_t mt = mi - cur.first;
     const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
     const int64_t row_end = (int64_t)ld_const(off, e + 1) < M_total ? (int64_t)ld_const(off, e + 1) : M_total;
     // waves whose rows all lie past the expert's last row skip their MFMAs
@@ -1507,11 +1552,11 @@ static void launch_dgrad(const uint8_t* ac, const uint8_t* as, const uint8_t* bc
                          const int32_t* off, int E, int64_t M, int64_t N, int64_t K, float* c, hipStream_t s) {
   if (K % dmag::BK == 0 && N % 128 == 0) {
     if (N % 256 == 0)
-      hipLaunchKernelGGL((k_dgrad_ws<false, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
-                         E, M, N, K, static_cast<void*>(c));
+      hipLaunchKernelGGL((k_dgrad_ws<false, 256>), dim3((unsigned)(cu_count() < 8 ? 8 : cu_count())), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
+                         E, M, N, K, dg_split(N / 256, dws::TM, 256), static_cast<void*>(c));
     else
-      hipLaunchKernelGGL((k_dgrad_ws<false, 128>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
-                         E, M, N, K, static_cast<void*>(c));
+      hipLaunchKernelGGL((k_dgrad_ws<false, 128>), dim3((unsigned)(cu_count() < 8 ? 8 : cu_count())), dim3(dws::NT), 0, s, ac, as, bc, bs, off,
+                         E, M, N, K, dg_split(N / 128, dws::TM, 128), static_cast<void*>(c));
     return;
   }
   if (K % dmag::BK == 0) {
@@ -1589,11 +1634,11 @@ extern "C" int moe_grouped_gemm_mx(const uint8_t* a_codes, const uint8_t* a_sf, 
   if (M_total == 0) return MOE4_OK;
   if (N % 128 == 0) {
     if (N % 256 == 0)
-      hipLaunchKernelGGL((k_dgrad_ws<true, 256>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream),
-                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c);
+      hipLaunchKernelGGL((k_dgrad_ws<true, 256>), dim3((unsigned)(cu_count() < 8 ? 8 : cu_count())), dim3(dws::NT), 0, as_stream(stream),
+                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, dg_split(N / 256, dws::TM, 256), c);
     else
-      hipLaunchKernelGGL((k_dgrad_ws<true, 128>), dim3((unsigned)cu_count()), dim3(dws::NT), 0, as_stream(stream),
-                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, c);
+      hipLaunchKernelGGL((k_dgrad_ws<true, 128>), dim3((unsigned)(cu_count() < 8 ? 8 : cu_count())), dim3(dws::NT), 0, as_stream(stream),
+                         a_codes, a_sf, b_codes, b_sf, expert_off, E, M_total, N, K, dg_split(N / 128, dws::TM, 128), c);
     return check_launch("moe_grouped_gemm_mx");
   }
   const int64_t n_nt = (N + 255) / 256;
