@@ -130,9 +130,13 @@ def _mx_rows(M, K, seed, scale=1.0):
 
 
 # 192 x 320 and 96 x 96: register-staged kernel; 128 x 256: warp-specialised
-# 128 x 128; 256 x 384: warp-specialised 128 x 256 (three slabs)
+# 128 x 128; 256 x 384: warp-specialised 128 x 256 (three slabs).  The last
+# two cover the warp-specialised kernel's per-XCD tile rectangles over more
+# than one band of m-tiles: N = 1280 (5 n-tiles in rectangles of 3: a
+# rectangle column past the last n-tile) and N = 4096 (16 n-tiles, 2 per XCD)
 @pytest.mark.parametrize("M_list,N,K", [([0, 37, 130, 1, 300], 192, 320), ([256], 128, 4096 // 16), ([3, 200], 96, 96),
-                                        ([0, 37, 130, 1, 300], 256, 384)])
+                                        ([0, 37, 130, 1, 300], 256, 384), ([2100, 3000, 1, 0, 900], 1280, 256),
+                                        ([700, 1500, 3], 4096, 128)])
 def test_grouped_gemm_dgrad_tolerance(M_list, N, K):
     E = len(M_list)
     off = np.concatenate([[0], np.cumsum(M_list)]).astype(np.int64)
