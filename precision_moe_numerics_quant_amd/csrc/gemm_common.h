@@ -95,4 +95,44 @@ struct MtCursor {
   }
 };
 
+// Tile order of the persistent warp-specialised GEMMs over (m-tile, n-tile)
+// (forward and dgrad).  The 8 XCDs work side by side on one
+// band of SM = (8 / xb) pm m-tiles at a time: XCD x takes the pm x pn
+// rectangle (x / xb, x % xb) of the band (pn n-tiles, n fastest), its
+// workgroups the rectangle's tiles in turn, then the next band.  Each XCD's
+// L2 then holds pm A row blocks and pn B row blocks per band, and the XCDs
+// read the same experts' B rows at about the same time (shared in the
+// Infinity Cache).  q: the XCD's own tile counter.
+struct DgSplit {
+  uint32_t pm, pn, xb;
+  __device__ bool tile(uint32_t x, uint32_t q, uint32_t n_mt, uint32_t n_nt, uint32_t& mi, uint32_t& nt) const {
+    const uint32_t ppn = pm * pn, sb = q / ppn, r = q - sb * ppn, a = r / pn;
+    mi = sb * (8 / xb) * pm + (x / xb) * pm + a;
+    nt = (x % xb) * pn + (r - a * pn);
+    return mi < n_mt && nt < n_nt;
+  }
+};
+
+// The rectangle with the fewest operand rows per tile (TM-row A blocks,
+// TN-row B blocks), counting n-tiles past n_nt as waste: pm = 32 / pn (one
+// tile per workgroup of an XCD of 32 CUs at a time; 1 for pn >= 32).  A B row (the
+// requantised weights, met first in HBM) counts three A rows: measured on the
+// layer's dgrads, the order with the fewest B rows per XCD is the
+// fastest of those with the same total.
+inline DgSplit dg_split(int64_t n_nt, int tm, int tn) {
+  DgSplit best{1, 1, 1};
+  double best_cost = 1e300;
+  for (uint32_t xb = 1; xb <= 8; xb *= 2) {
+    const uint32_t pn = (uint32_t)((n_nt + xb - 1) / xb);
+    const uint32_t pm = pn >= 32 ? 1 : 32 / pn;
+    const double cost =
+        ((double)pm * tm + 3.0 * pn * tn) / ((double)pm * pn) * ((double)xb * pn / (double)n_nt);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = DgSplit{pm, pn, xb};
+    }
+  }
+  return best;
+}
+
 }  // namespace moe4

@@ -567,11 +567,10 @@ MOE4_FWD_DMA_KERNEL(k_gemm_fwd_dma_f32_128, false, 128, 128, 2, false)
 // stores would wait for its stores' acknowledgements before each slab; here
 // no wave does both.  One barrier per slab: producers wait for slab s with an
 // explicit count (the later slabs stay in flight), consumers only for their
-// own LDS reads of slab s - 1.  Tiles: m-tile major (the m-tiles of expert e
-// follow those of e - 1), n fastest; each XCD takes a contiguous run of the
-// tile list (tiles cost the same, so the runs balance) and its workgroups
-// stride through it, so concurrent tiles share A rows and the expert's B in
-// that XCD's L2.
+// own LDS reads of slab s - 1.  Tiles: m-tiles in expert order, dealt to the
+// XCDs in rectangles of one band of m-tiles at a time (DgSplit), so that an
+// XCD's concurrent tiles share A rows and B rows in its L2 and all XCDs read
+// the same experts' weights at about the same time.
 namespace fws {
 constexpr int TM = 128;
 // TN = 128: four stages, four consumer waves; TN = 256: two 54 KB stages (all
@@ -672,7 +671,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     k_gemm_fwd_ws(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf, const float* __restrict__ a_ts,
                   int a_ts_per_group, const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_sf,
                   const float* __restrict__ b_ts, const int32_t* __restrict__ off, int E, int64_t M_total, int64_t N,
-                  int64_t K, void* __restrict__ c, uint32_t* __restrict__ silu_amax,
+                  int64_t K, DgSplit sp, void* __restrict__ c, uint32_t* __restrict__ silu_amax,
                   const float* __restrict__ act_tab, int8_t* __restrict__ hcodes = nullptr,
                   uint8_t* __restrict__ hsf = nullptr) {
   static_assert(!HMX8 || !OUT_BF16, "the combine-path payload is made from the float32 output");
@@ -695,12 +694,11 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
     if (l == 0) s_nmt = n;
   }
   __syncthreads();
-  const uint32_t n_nt = (uint32_t)(N / TN), n_all = s_nmt * n_nt;  // N % TN == 0 (checked at launch)
+  const uint32_t n_nt = (uint32_t)(N / TN), n_mt = s_nmt;  // N % TN == 0 (checked at launch)
   const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16), nk = (uint32_t)(K / fdma::BKE);
-  // this workgroup's tiles: t0, t0 + stride, ... < t_end
-  const uint32_t xcd = blockIdx.x % 8, per = (n_all + 7) / 8;
-  const uint32_t stride = (gridDim.x - xcd + 7) / 8;
-  const uint32_t t0 = xcd * per + blockIdx.x / 8, t_end = (xcd + 1) * per < n_all ? (xcd + 1) * per : n_all;
+  // this workgroup's tiles: q = q0, q0 + stride, ... of its XCD (see DgSplit)
+  const uint32_t xcd = blockIdx.x % 8, stride = (gridDim.x - xcd + 7) / 8, q0 = blockIdx.x / 8;
+  const uint32_t sm = (8 / sp.xb) * sp.pm, q_end = (n_mt + sm - 1) / sm * (sp.pm * sp.pn);
 
   if (w >= NCW) {
     // ---- producer pw: rows 32 pw .. 32 pw + 31 of A's codes, TN / 4 rows of
@@ -725,13 +723,15 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
       }
     };
     MtCursor<TM> cur;
-    uint32_t pt = t0, ps = 0;
+    uint32_t pt = q0, ps = 0;
     bool more = false;
     auto seek = [&]() {
-      more = pt < t_end && cur.seek(off, E, pt / n_nt);
+      uint32_t mi = 0, nt = 0;
+      while (pt < q_end && !sp.tile(xcd, pt, n_mt, n_nt, mi, nt)) pt += stride;
+      more = pt < q_end && cur.seek(off, E, mi);
       if (!more) return;
       const int e = cur.e;
-      const uint32_t mt = pt / n_nt - cur.first, nt = pt % n_nt;
+      const uint32_t mt = mi - cur.first;
       const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
       rbc = make_rsrc(b_codes + (int64_t)e * N * KB, (uint64_t)N * KB);
       rbs = make_rsrc(b_sf + (int64_t)e * N * KS, (uint64_t)N * KS);
@@ -822,9 +822,12 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
   float* hb = hbuf + (HMX8 ? w * 16 * 36 : 0);  // (HMX8) this consumer wave's block
   MtCursor<TM> cur;
   uint32_t gs = 0;
-  for (uint32_t t = t0; t < t_end && cur.seek(off, E, t / n_nt); t += stride) {
+  for (uint32_t q = q0; q < q_end; q += stride) {
+    uint32_t mi, nt;
+    if (!sp.tile(xcd, q, n_mt, n_nt, mi, nt)) continue;
+    if (!cur.seek(off, E, mi)) break;
     const int e = cur.e;
-    const uint32_t mt = t / n_nt - cur.first, nt = t % n_nt;
+    const uint32_t mt = mi - cur.first;
     const int64_t row0 = (int64_t)ld_const(off, e) + (int64_t)mt * TM, n0 = (int64_t)nt * TN;
     const int64_t row_end = (int64_t)ld_const(off, e + 1) < M_total ? (int64_t)ld_const(off, e + 1) : M_total;
     // waves whose rows all lie past the expert's last row skip their MFMAs,
@@ -1152,6 +1155,10 @@ static int cu_count_f() {
   return n[dev];
 }
 
+// Persistent grid of the warp-specialised forward kernels: one workgroup per
+// CU, at least one per XCD (the tile order deals each XCD its own tiles).
+static int fws_grid() { return cu_count_f() < 8 ? 8 : cu_count_f(); }
+
 // 12 = the few-rows-per-expert kernel (k_gemm_fwd_skinny): K % 256 == 0,
 // N % 64 == 0, at most 32 rows per expert on average.
 static int fwd_choice(int64_t M, int64_t N, int64_t K, int E) {
@@ -1179,13 +1186,13 @@ static void launch_fwd(hipStream_t s, const uint8_t* ac, const uint8_t* as, cons
     return;
   }
   if (choice == 10) {
-    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 128>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s, ac,
-                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
+    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 128>), dim3((unsigned)fws_grid()), dim3(fws::Cfg<128>::NT), 0, s, ac, as,
+                       ats, apg, bc, bs, bts, off, E, M, N, K, dg_split(N / 128, fws::TM, 128), c, silu_amax, act_tab);
     return;
   }
   if (choice == 11) {
-    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 256>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<256>::NT), 0, s, ac,
-                       as, ats, apg, bc, bs, bts, off, E, M, N, K, c, silu_amax, act_tab);
+    hipLaunchKernelGGL((k_gemm_fwd_ws<OUT_BF16, 256>), dim3((unsigned)fws_grid()), dim3(fws::Cfg<256>::NT), 0, s, ac, as,
+                       ats, apg, bc, bs, bts, off, E, M, N, K, dg_split(N / 256, fws::TM, 256), c, silu_amax, act_tab);
     return;
   }
   if (choice == 9) {
@@ -1241,13 +1248,13 @@ extern "C" int moe_grouped_gemm_fwd_hmx8(const uint8_t* a_codes, const uint8_t* 
                "moe_grouped_gemm_fwd_hmx8: too large");
   hipStream_t s = as_stream(stream);
   if (choice == 11)
-    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 256, true>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<256>::NT), 0, s,
+    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 256, true>), dim3((unsigned)fws_grid()), dim3(fws::Cfg<256>::NT), 0, s,
                        a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K,
-                       static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
+                       dg_split(N / 256, fws::TM, 256), static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
   else
-    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 128, true>), dim3((unsigned)cu_count_f()), dim3(fws::Cfg<128>::NT), 0, s,
+    hipLaunchKernelGGL((k_gemm_fwd_ws<false, 128, true>), dim3((unsigned)fws_grid()), dim3(fws::Cfg<128>::NT), 0, s,
                        a_codes, a_sf, a_ts, a_ts_per_group, b_codes, b_sf, b_ts, expert_off, E, M_total, N, K,
-                       static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
+                       dg_split(N / 128, fws::TM, 128), static_cast<void*>(c), nullptr, nullptr, hcodes, hsf);
   return check_launch("moe_grouped_gemm_fwd_hmx8");
 }
 
