@@ -33,6 +33,18 @@ from . import (NVFP4_4OVER6, PRE_SILU, PRE_SILU_AMAX, SF_BLOCKS, SF_ROWS, Moe4Un
 
 ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 
+_SIDE = {}  # device index -> the backward's second stream (default priority)
+# smallest T * k * d whose untimed backward uses the second stream (below it
+# the stream handoffs cost more than the overlap gains)
+SIDE_STREAM_MIN_ELEMS = 1 << 24
+
+
+def _side_stream(device):
+    s = _SIDE.get(device.index)
+    if s is None:
+        s = _SIDE[device.index] = torch.cuda.Stream(device=device)
+    return s
+
 
 def _tick(timer, name):
     if timer is not None:
@@ -158,12 +170,33 @@ def backward(fw, dy, seed=1, layer=0, timer=None, skip_empty_dw=False):
 def _backward_chain(fw, dy, timer, skip_empty_dw, req):
     """The backward calls in order; req[name]() gives the transposed MXFP8
     operand 'wdT', 'hT', 'wuT' or 'xT' and whether a library call made it
-    (for the timer)."""
+    (for the timer).
+
+    Without a timer (and for T k d >= SIDE_STREAM_MIN_ELEMS), the calls that
+    only read tensors the chain does not write run on a second stream beside
+    it: the gate gradient and the router
+    backward (B12, B13: dy, Yp and the routing) beside B1 (HBM-bound reads
+    beside a VALU-bound quantiser), and the un-permuting sum (B11, from dXp)
+    beside B9 and B10.  The chain's stream waits for the second stream before
+    returning.  Every tensor the second stream reads outlives the call, and
+    the second stream waits for the chain's stream before each of its turns,
+    so no block either stream frees is reused while the other still reads
+    it.  With a timer every call runs in order on one stream, so that each
+    one's time can be read."""
     T, d, F, E, k = fw["dims"]
     r = fw["route"]
     A = T * k
     mpr = max_padded_rows(A, E)
     g_flat = r["gates"].view(-1)
+    rw = fw.get("router_w")
+    side = None
+    if timer is None and dy.is_cuda and A * d >= SIDE_STREAM_MIN_ELEMS:
+        main = torch.cuda.current_stream(dy.device)
+        side = _side_stream(dy.device)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
+            dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
 
     def get(name, label):
         out, called = req[name]()
@@ -190,19 +223,25 @@ def _backward_chain(fw, dy, timer, skip_empty_dw, req):
     wuT = get("wuT", "B7 W_up requant SR-T")
     dXp = moe_grouped_gemm_bwd_dgrad(du_row[0], du_row[1], wuT[0], wuT[1], r["off"])
     _tick(timer, "B8 up dgrad (MXFP8)")
+    if side is not None and rw is None:
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
     xT = get("xT", "B9 X requant SR-T")
     dW_up = moe_grouped_gemm_bwd_wgrad(du_col[0], du_col[1], xT[0], xT[1], r["off_pad"], F, d,
                                        skip_empty=skip_empty_dw)
     _tick(timer, "B10 up wgrad (MXFP8)")
-    rw = fw.get("router_w")
     dW_router = None
-    if rw is None:
-        dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
-        _tick(timer, "B11 un-permute sum")
-    dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
-    _tick(timer, "B12 gate gradient")
-    dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
-    _tick(timer, "B13 router backward")
+    if side is not None:
+        main.wait_stream(side)
+    else:
+        if rw is None:
+            dx = moe_unpermute_sum(dXp, r["inv_perm"], T, k)
+            _tick(timer, "B11 un-permute sum")
+        dg = moe_dgates(dy, fw["Yp"], r["inv_perm"], k)
+        _tick(timer, "B12 gate gradient")
+        dlogits = moe_route_backward(dg, r["gates"], r["idx"], E)
+        _tick(timer, "B13 router backward")
     if rw is not None:
         # the router's input gradient joins the un-permuting sum; then its weight gradient
         dx = moe_unpermute_sum_router(dXp, r["inv_perm"], T, k, dlogits, r["idx"], rw)

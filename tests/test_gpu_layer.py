@@ -353,11 +353,37 @@ def test_dgates_full_size_sampled(cfg3_route):
     gemm_tol_check(dg[toks], exact, bound, "dgates")
 
 
-def test_layer_step_graph_replay_matches_eager():
+def test_backward_second_stream_matches_one_stream(monkeypatch):
+    """The untimed backward with its independent calls (gate gradient, router
+    backward, un-permuting sum) on a second stream gives the one-stream
+    backward's outputs bit for bit."""
+    inp = synth.config_inputs(1, device="cuda")
+    k = synth.CONFIGS[1]["k"]
+    fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, seed=synth.SR_SEED)
+    names = ("dx", "dg", "dlogits", "dW_up", "dW_down")
+    monkeypatch.setattr(layer, "SIDE_STREAM_MIN_ELEMS", 1 << 62)
+    one = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+    one = {n: one[n].clone() for n in names}
+    monkeypatch.setattr(layer, "SIDE_STREAM_MIN_ELEMS", 0)
+    for _ in range(2):
+        two = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+        torch.cuda.synchronize()
+        for n in names:
+            a, b = two[n], one[n]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), n
+
+
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_layer_step_graph_replay_matches_eager(side_stream, monkeypatch):
     """The tiny layer's whole step (forward + backward, 20 library calls)
     captured in one graph: every replay, with eager steps and host syncs
     between replays, gives the eager step's outputs bit for bit (the library
-    records no memset nodes; the workspaces are cleared by its own kernels)."""
+    records no memset nodes; the workspaces are cleared by its own kernels).
+    side_stream: with the backward's second stream (forked from and joined
+    to the capturing stream)."""
+    if side_stream:
+        monkeypatch.setattr(layer, "SIDE_STREAM_MIN_ELEMS", 0)
     inp = synth.config_inputs(1, device="cpu")
     k = synth.CONFIGS[1]["k"]
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
