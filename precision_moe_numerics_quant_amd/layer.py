@@ -91,10 +91,20 @@ def forward(x, w_up, w_down, logits, k, bias=None, wq=None, timer=None, seed=1, 
         logits = moe_router_logits(x, router_w)
         _tick(timer, "F0 router GEMM (BF16)")
     _tick(timer, None)
-    r = moe_route_topk(logits, k, bias)
-    _tick(timer, "F2-F3 route + permutation")
-    xq = nvfp4_quant_46(x, NVFP4_4OVER6)
-    _tick(timer, "F4 X quant (NVFP4 4/6)")
+    if timer is None and x.is_cuda and T * k * d >= SIDE_STREAM_MIN_ELEMS:
+        # routing on the second stream beside X's quantisation (independent)
+        main = torch.cuda.current_stream(x.device)
+        side = _side_stream(x.device)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            r = moe_route_topk(logits, k, bias)
+        xq = nvfp4_quant_46(x, NVFP4_4OVER6)
+        main.wait_stream(side)
+    else:
+        r = moe_route_topk(logits, k, bias)
+        _tick(timer, "F2-F3 route + permutation")
+        xq = nvfp4_quant_46(x, NVFP4_4OVER6)
+        _tick(timer, "F4 X quant (NVFP4 4/6)")
     xq_perm = moe_gather_rows(xq[0], xq[1], r["perm"], k)
     _tick(timer, "F5 dispatch gather")
     wu_c, wu_s, wu_t = wq["wu"]

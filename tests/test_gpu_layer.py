@@ -354,19 +354,25 @@ def test_dgates_full_size_sampled(cfg3_route):
 
 
 def test_backward_second_stream_matches_one_stream(monkeypatch):
-    """The untimed backward with its independent calls (gate gradient, router
-    backward, un-permuting sum) on a second stream gives the one-stream
-    backward's outputs bit for bit."""
+    """The untimed layer with its independent calls on a second stream (the
+    routing beside X's quantisation; the gate gradient, router backward and
+    un-permuting sum beside the backward chain) gives the one-stream layer's
+    outputs bit for bit."""
     inp = synth.config_inputs(1, device="cuda")
     k = synth.CONFIGS[1]["k"]
-    fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, seed=synth.SR_SEED)
-    names = ("dx", "dg", "dlogits", "dW_up", "dW_down")
+    names = ("y", "dx", "dg", "dlogits", "dW_up", "dW_down")
+
+    def run():
+        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, seed=synth.SR_SEED)
+        bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+        bw["y"] = fw["y"]
+        return bw
     monkeypatch.setattr(layer, "SIDE_STREAM_MIN_ELEMS", 1 << 62)
-    one = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+    one = run()
     one = {n: one[n].clone() for n in names}
     monkeypatch.setattr(layer, "SIDE_STREAM_MIN_ELEMS", 0)
     for _ in range(2):
-        two = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
+        two = run()
         torch.cuda.synchronize()
         for n in names:
             a, b = two[n], one[n]
