@@ -36,7 +36,7 @@ ROLE_X, ROLE_H, ROLE_WUP, ROLE_WDOWN = 0, 1, 2, 3
 _SIDE = {}  # device index -> the backward's second stream (default priority)
 # smallest T * k * d whose untimed backward uses the second stream (below it
 # the stream handoffs cost more than the overlap gains)
-SIDE_STREAM_MIN_ELEMS = 1 << 24
+SIDE_STREAM_MIN_ELEMS = 1 << 26
 
 
 def _side_stream(device):
