@@ -353,17 +353,23 @@ def test_dgates_full_size_sampled(cfg3_route):
     gemm_tol_check(dg[toks], exact, bound, "dgates")
 
 
-def test_backward_second_stream_matches_one_stream(monkeypatch):
+@pytest.mark.parametrize("with_router", [False, True])
+def test_backward_second_stream_matches_one_stream(with_router, monkeypatch):
     """The untimed layer with its independent calls on a second stream (the
     routing beside X's quantisation; the gate gradient, router backward and
     un-permuting sum beside the backward chain) gives the one-stream layer's
-    outputs bit for bit."""
+    outputs bit for bit; with_router: the logits from the router GEMM, the
+    router's input gradient in the un-permuting sum (after the join) and its
+    weight gradient."""
     inp = synth.config_inputs(1, device="cuda")
-    k = synth.CONFIGS[1]["k"]
-    names = ("y", "dx", "dg", "dlogits", "dW_up", "dW_down")
+    c = synth.CONFIGS[1]
+    k = c["k"]
+    names = ("y", "dx", "dg", "dlogits", "dW_up", "dW_down") + (("dW_router",) if with_router else ())
+    rw = synth.randn((c["E"], c["d"]), 0.05, "cuda", 11, "misc").to(torch.bfloat16) if with_router else None
 
     def run():
-        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], k, seed=synth.SR_SEED)
+        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], None if with_router else inp["logits"], k,
+                           seed=synth.SR_SEED, router_w=rw)
         bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED)
         bw["y"] = fw["y"]
         return bw
