@@ -26,7 +26,7 @@ int check_launch(const char* what) {
 
 // The SiLU (g_act_tab[0]) and SiLU' (g_act_tab[1]) tables: initialised data
 // of the code object, written at build time by gen_act_tab.cpp (correctly
-// rounded float32 values for |u| in [2**-8, 2**8)) and never written at run
+// rounded float32 values for |u| in [2**-16, 2**8)) and never written at run
 // time.  Nothing fills them, so no call waits for a table and any call may be
 // captured in a graph.  (Not declared const: a const namespace-scope variable
 // has internal linkage, and the runtime's symbol lookup cannot find it.)

@@ -401,19 +401,24 @@ __device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64
     return f32x4{sc * v[0], sc * v[1], sc * v[2], sc * v[3]};
   } else if (MODE == 2) {
     f32x4 v = load4<DT>(g.x, r * C + c);
-    u32x2 u = *reinterpret_cast<const u32x2*>(g.dsilu_src + r * C + c);
-    return f32x4{v[0] * act_eval<true>(u[0] & 0xFFFFu, dtab), v[1] * act_eval<true>(u[0] >> 16, dtab),
-                 v[2] * act_eval<true>(u[1] & 0xFFFFu, dtab), v[3] * act_eval<true>(u[1] >> 16, dtab)};
+    const u32x2 u = *reinterpret_cast<const u32x2*>(g.dsilu_src + r * C + c);
+    const uint32_t uu[2] = {u[0], u[1]};
+    float d[4];
+    act_eval_packed<true>(uu, dtab, d);
+    return f32x4{v[0] * d[0], v[1] * d[1], v[2] * d[2], v[3] * d[3]};
   } else if (MODE == 3) {  // (the table is the silu one)
-    u32x2 u = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(g.x) + r * C + c);
-    return f32x4{act_eval<false>(u[0] & 0xFFFFu, dtab), act_eval<false>(u[0] >> 16, dtab),
-                 act_eval<false>(u[1] & 0xFFFFu, dtab), act_eval<false>(u[1] >> 16, dtab)};
+    const u32x2 u = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(g.x) + r * C + c);
+    const uint32_t uu[2] = {u[0], u[1]};
+    float a[4];
+    act_eval_packed<false>(uu, dtab, a);
+    return f32x4{a[0], a[1], a[2], a[3]};
   }
   return load4<DT>(g.x, r * C + c);
 }
 
 // grad_vals4 for 16 consecutive columns c .. c + 15 (c % 16 == 0, C % 16 ==
-// 0): the source row (and its map and scale) resolved once, 16-byte loads.
+// 0): the source row (and its map and scale) resolved once, 16-byte loads;
+// dtab is the narrow table (stage_act_table_narrow).
 template <int DT, int MODE>
 __device__ inline void grad_vals16(const GradSrc& g, int64_t r, int64_t C, int64_t c, const float* dtab,
                                    float (&v)[16]) {
@@ -432,8 +437,8 @@ __device__ inline void grad_vals16(const GradSrc& g, int64_t r, int64_t C, int64
       const u32x4 u = p[q];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * q + 2 * j] = act_eval<false>(u[j] & 0xFFFFu, dtab);
-        v[8 * q + 2 * j + 1] = act_eval<false>(u[j] >> 16, dtab);
+        v[8 * q + 2 * j] = act_eval_narrow<false>(u[j] & 0xFFFFu, dtab);
+        v[8 * q + 2 * j + 1] = act_eval_narrow<false>(u[j] >> 16, dtab);
       }
     }
     return;
@@ -468,8 +473,8 @@ __device__ inline void grad_vals16(const GradSrc& g, int64_t r, int64_t C, int64
       const u32x4 u = pu[q];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * q + 2 * j] = v[8 * q + 2 * j] * act_eval<true>(u[j] & 0xFFFFu, dtab);
-        v[8 * q + 2 * j + 1] = v[8 * q + 2 * j + 1] * act_eval<true>(u[j] >> 16, dtab);
+        v[8 * q + 2 * j] = v[8 * q + 2 * j] * act_eval_narrow<true>(u[j] & 0xFFFFu, dtab);
+        v[8 * q + 2 * j + 1] = v[8 * q + 2 * j + 1] * act_eval_narrow<true>(u[j] >> 16, dtab);
       }
     }
   }
@@ -530,9 +535,9 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
                                               uint8_t* __restrict__ out_c, uint8_t* __restrict__ out_s,
                                               const float* __restrict__ act_tab, uint8_t* __restrict__ row_c,
                                               uint8_t* __restrict__ row_s) {
-  __shared__ float tab[MODE >= 2 ? ACT_TAB : 1];
+  __shared__ float tab[MODE >= 2 ? ACT_NARROW : 1];  // (the narrow table: LDS for four workgroups per CU)
   __shared__ float lv[TC][TR + 1];  // [column][row]
-  if (MODE >= 2) stage_act_table(tab, act_tab);
+  if (MODE >= 2) stage_act_table_narrow(tab, act_tab);
   // Tile order.  Each column's output run of a 32-row tile is 32 bytes, a
   // quarter line: for sources read in place, the four row tiles of a 128-row
   // span with the same columns run back to back on one XCD (contiguous tile

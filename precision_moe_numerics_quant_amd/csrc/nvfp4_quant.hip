@@ -49,15 +49,17 @@ template <int DT, bool SILU>
 __device__ inline void load8(const void* x, int64_t idx, float* v, const float* tab) {
   if (DT == MOE4_BF16) {
     u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + idx);
+    if (SILU) {
+      const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
+      float t[8];
+      act_eval_packed<false>(ww, tab, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
-      if (SILU) {
-        v[2 * i] = act_eval<false>(lo, tab);
-        v[2 * i + 1] = act_eval<false>(hi, tab);
-      } else {
-        v[2 * i] = bf16_bits_to_f32(lo);
-        v[2 * i + 1] = bf16_bits_to_f32(hi);
+      for (int i = 0; i < 8; ++i) v[i] = t[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
       }
     }
   } else {
@@ -91,11 +93,15 @@ __device__ inline void load_piece(const void* x, int64_t p, float (&v)[Walk<DT>:
     v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
   } else {
     u32x4 w = reinterpret_cast<const u32x4*>(x)[p];
+    if constexpr (SILU) {
+      const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
+      act_eval_packed<false>(ww, tab, v);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
-      v[2 * i] = SILU ? act_eval<false>(lo, tab) : bf16_bits_to_f32(lo);
-      v[2 * i + 1] = SILU ? act_eval<false>(hi, tab) : bf16_bits_to_f32(hi);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
     }
   }
 }

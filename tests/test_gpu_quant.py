@@ -446,6 +446,68 @@ def test_fused_weight_quant_rejects_bad_shapes():
         m4.nvfp4_quant_requant_T(w, 2)                               # groups of 48 rows
 
 
+# bf16 patterns at and around the ends of the SiLU tables: +-0, +-subnormal,
+# +-2**-20, just under 2**-16 and 2**-16 (the first entry), either side of
+# 2**-8, the last entry (255) and 256, 300 (past the table: per-value rules)
+_SILU_EDGES = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x3580, 0xB580, 0x377F, 0xB77F, 0x3780, 0xB780,
+                        0x3B7F, 0xBB7F, 0x3B80, 0xBB80, 0x437F, 0xC37F, 0x4380, 0xC380, 0x4396, 0xC396],
+                       dtype=np.uint16)
+
+
+def _planted_u(R, C, seed, rate=1.0 / 700):
+    """bf16 bits of N(0, 1.5**2) with about `rate` of the entries replaced by
+    _SILU_EDGES: waves that meet one take the per-value path of the SiLU
+    evaluation, the others the table-only path."""
+    ub = synth.bf16_bits(synth.randn((R, C), 1.5, "cpu", seed, "u", torch.bfloat16)).copy()
+    rng = np.random.default_rng(seed)
+    hit = rng.random((R, C)) < rate
+    ub[hit] = rng.choice(_SILU_EDGES, size=int(hit.sum()))
+    return ub
+
+
+@pytest.mark.parametrize("kind", ["nvfp4", "silu_rows", "silu_T", "dsilu_rows", "dsilu_T", "dsilu_rows_T"])
+def test_silu_table_and_per_value_paths(kind):
+    """Every quantiser that evaluates SiLU or SiLU' from bf16 U, on U with
+    table-end patterns planted among normal values, bit-exact to the oracle."""
+    R, C = 520, 256
+    off = np.array([0, 7, 7, 300, 520])
+    offp = mx.padded_offsets(off)
+    n = C * offp[-1]
+    ub = _planted_u(R, C, 31)
+    assert np.isin(_SILU_EDGES, ub).all()
+    u = bf16_from_bits(ub)
+    if kind == "nvfp4":
+        codes, sf, ts = m4.nvfp4_quant_46(u, 46, cuda_i32(off), m4.PRE_SILU)
+        ref = nv.nvfp4_quantize(osilu.silu_f32(ub), 46, off)
+        assert_bytes_equal(to_np(ts).view(np.uint32), ref["ts"].view(np.uint32), "ts")
+        assert_bytes_equal(to_np(sf), ref["sf"], "sf")
+        assert_bytes_equal(to_np(codes), ref["codes"], "codes")
+        return
+    if kind.startswith("silu"):
+        src, ref, kw = u, osilu.silu_f32(ub), dict(pre_op=m4.PRE_SILU)
+    else:
+        dh = synth.randn((R, C), 1e-3, "cpu", 32, "dh").numpy()
+        src, ref, kw = torch.from_numpy(dh).cuda(), (dh * osilu.dsilu_f32(ub)).astype(np.float32), dict(dsilu_src=u)
+    if kind.endswith("rows_T"):
+        rc_, rs_, tc, ts = m4.mxfp8_quant_rows_T(src, cuda_i32(off), cuda_i32(offp), sf_layout=SF_BLOCKS, **kw)
+        c_ref, s_ref = mx.quantize_rowwise(ref, mx.RNE)
+        assert_bytes_equal(to_np(rc_), c_ref, "row codes")
+        assert_bytes_equal(to_np(rs_), s_ref, "row scales")
+        c_ref, s_ref = mx.quantize_transposed(ref, off, mx.RNE, sf_layout=mx.SF_BLOCKS)
+        assert_bytes_equal(to_np(tc)[:n], c_ref, "transposed codes")
+        assert_bytes_equal(to_np(ts)[: n // 32], s_ref, "transposed scales")
+    elif kind.endswith("_T"):
+        oc, os_ = m4.mxfp8_quant(src, transpose=True, group_row_off=cuda_i32(off), group_off_pad=cuda_i32(offp), **kw)
+        c_ref, s_ref = mx.quantize_transposed(ref, off, mx.RNE)
+        assert_bytes_equal(to_np(oc)[:n], c_ref, "codes")
+        assert_bytes_equal(to_np(os_)[: n // 32], s_ref, "scales")
+    else:
+        oc, os_ = m4.mxfp8_quant(src, **kw)
+        c_ref, s_ref = mx.quantize_rowwise(ref, mx.RNE)
+        assert_bytes_equal(to_np(oc), c_ref, "codes")
+        assert_bytes_equal(to_np(os_), s_ref, "scales")
+
+
 @pytest.mark.parametrize("transpose", [False, True])
 def test_mxfp8_quant_silu_pre_op(transpose):
     """MXFP8 of silu(U) for bf16 U (the MXFP8 forward's H), bit-exact."""
