@@ -594,14 +594,19 @@ int moe_unpermute_sum_router(const float* dxp, const int32_t* inv_perm, int64_t 
 /*
  * moe_router_wgrad - dw [E, d] float32: dw[e, c] = sum over the rows r of
  * expert e (expert_off from moe_route_topk; t = perm[r] / k) of
- * dlogits[t, e] * x[t, c].  Float32 sums in a fixed order (each of 16
- * interleaved row shares in row order, then the 16 shares in order):
- * deterministic; experts without rows get zeros.  x [T, d] bf16 (8-byte
- * aligned), dlogits [T, E], perm [T*k], dw 16-byte aligned.
- * 1 <= k <= E, d % 4 == 0.
+ * dlogits[t, e] * x[t, c].  Float32 sums in a fixed order: each expert's rows
+ * in chunks of 128 (each chunk: four interleaved row shares in row order, then
+ * the four shares in order), then the chunks in order; deterministic; experts
+ * without rows get zeros.  x [T, d] bf16, dlogits [T, E], perm [T*k]; x, dw
+ * and ws 16-byte aligned.  1 <= k <= E, d % 8 == 0, T*k < 2^31.
+ * ws: moe_router_wgrad_ws_bytes(T, E, k, d) bytes (the chunk partial rows,
+ * d floats each, for at most ceil(T*k / 128) + E chunks), the caller's,
+ * overwritten.  Offsets that are not monotone within [0, T*k] are clamped and
+ * reported (MOE4_DEVERR_INDEX).
  */
 int moe_router_wgrad(const uint16_t* x, const float* dlogits, const int32_t* perm, const int32_t* expert_off,
-                     int64_t T, int32_t E, int32_t k, int64_t d, float* dw, void* stream);
+                     int64_t T, int32_t E, int32_t k, int64_t d, float* dw, void* ws, size_t ws_bytes, void* stream);
+size_t moe_router_wgrad_ws_bytes(int64_t T, int32_t E, int32_t k, int64_t d);
 
 /*
  * moe_silu_eval - correctly rounded float32 silu(u) and silu'(u) of bf16 u

@@ -80,7 +80,8 @@ _SIGS = {
     "moe_unpermute_sum_router": (_int, [_c_void_p, _c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
                                         _c_void_p, _c_void_p]),
     "moe_router_wgrad": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
-                                _c_void_p]),
+                                _c_void_p, _size, _c_void_p]),
+    "moe_router_wgrad_ws_bytes": (_size, [_i64, _i32, _i32, _i64]),
     "mxfp8_quant_requant_T": (_int, [_c_void_p, _i64, _i64, _i32, _u64, _u32, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p]),
     "moe_grouped_gemm_fwd_silu_amax": (_int, [_c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p,
@@ -605,7 +606,9 @@ def moe_router_wgrad(x, dlogits, perm, expert_off, k):
     T, d = x.shape
     E = dlogits.shape[1]
     dw = _empty((E, d), torch.float32, x)
-    rc = lib().moe_router_wgrad(_p(x), _p(dlogits), _p(perm), _p(expert_off), T, E, k, d, _p(dw), _stream())
+    ws = _ws(lib().moe_router_wgrad_ws_bytes(T, E, k, d), x)
+    rc = lib().moe_router_wgrad(_p(x), _p(dlogits), _p(perm), _p(expert_off), T, E, k, d, _p(dw), _p(ws), ws.numel(),
+                                _stream())
     _check(rc, "moe_router_wgrad")
     return dw
 

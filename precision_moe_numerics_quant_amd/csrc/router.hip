@@ -10,12 +10,16 @@
 //   k_unpermute_router the un-permuting sum of the expert path's input
 //                      gradient plus the router's: dx[t] = bf16(sum_j dXp[row]
 //                      + sum_j dz[t, e_j] * W_r[e_j]), in that float32 order.
-//   k_router_wgrad     dW_r [E, d] = sum over the tokens routed to e of
+//   router wgrad       dW_r [E, d] = sum over the tokens routed to e of
 //                      dz[t, e] * x[t]: sparse (k of E logits per token carry a
 //                      gradient), so a gather-reduce over each expert's routed
-//                      rows, not a dense GEMM; 16 waves per (expert, 256
-//                      columns), each summing an interleaved share of the rows,
-//                      then the 16 partial sums in wave order (deterministic).
+//                      rows, not a dense GEMM.  Each expert's rows are cut into
+//                      chunks of 128, so a popular expert (routing is skewed:
+//                      one expert can hold most tokens) spreads over the whole
+//                      chip: k_router_wgrad_chunks numbers the chunks,
+//                      k_router_wgrad_part sums each (chunk, 512 columns) into
+//                      a float32 partial row, k_router_wgrad_sum adds each
+//                      expert's partials in chunk order (deterministic).
 #include "gemm_common.h"
 #include "moe4_internal.h"
 
@@ -174,59 +178,165 @@ __global__ void __launch_bounds__(256) k_unpermute_router(const float* __restric
 }
 
 namespace rw {
-constexpr int NW = 16, NT = 64 * NW, COLS = 256;   // 4 columns per lane
+constexpr int CH = 128;               // rows per chunk
+constexpr int NW = 4, NT = 64 * NW;   // k_router_wgrad_part: 4 waves
+constexpr int COLS = 512;             // ... 8 columns per lane (one 16-byte load per row)
+constexpr int BATCH = 16;             // ... rows in flight per wave
+constexpr int SCAN_T = 1024;          // k_router_wgrad_chunks: one workgroup
+constexpr int SUM_T = 256, SUM_COLS = 4 * SUM_T;  // k_router_wgrad_sum: 4 columns per thread
 }
 
-// Block (e, column block): dW_r[e, cb .. cb + 255].  Wave w sums rows
-// off[e] + w, off[e] + w + 16, ... (four rows in flight), lane l columns
-// cb + 4 l .. + 3; then the 16 wave sums are added in wave order.
-__global__ void __launch_bounds__(rw::NT) k_router_wgrad(const uint16_t* __restrict__ x,
-                                                         const float* __restrict__ dlogits,
-                                                         const int32_t* __restrict__ perm,
-                                                         const int32_t* __restrict__ off, int64_t T, int E, int k,
-                                                         int64_t d, float* __restrict__ dw) {
+// Chunks of the rows [off[e], off[e+1]) (a span outside [0, A] counts as clipped to it).
+__device__ inline int64_t rw_chunks(const int32_t* off, int e, int64_t A) {
+  int64_t n = (int64_t)off[e + 1] - off[e];
+  n = n < 0 ? 0 : (n > A ? A : n);
+  return (n + rw::CH - 1) / rw::CH;
+}
+
+// One workgroup: coff[e] = first chunk of expert e (exclusive prefix sum of
+// the chunk counts), coff[E] = the number of chunks, chunk_e[c] = the expert
+// of chunk c.  Counts past `bound` (only for offsets that are not monotone
+// within [0, A]) are cut there and reported.
+__global__ void __launch_bounds__(rw::SCAN_T) k_router_wgrad_chunks(const int32_t* __restrict__ off, int E, int64_t A,
+                                                                    int64_t bound, int32_t* __restrict__ coff,
+                                                                    int32_t* __restrict__ chunk_e) {
   using namespace rw;
-  __shared__ f32x4 part[NW][64];
-  const int e = blockIdx.x;
-  const int64_t cb = (int64_t)blockIdx.y * COLS;
-  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t c = cb + 4 * l;
-  const bool cok = c < d;
-  const int64_t r0 = off[e], r1 = off[e + 1];
+  __shared__ int64_t sc[SCAN_T];
+  const int tid = threadIdx.x;
+  const int per = (E + SCAN_T - 1) / SCAN_T;
+  const int e0 = tid * per;
+  int64_t mine = 0;
+  for (int i = 0; i < per; ++i)
+    if (e0 + i < E) mine += rw_chunks(off, e0 + i, A);
+  sc[tid] = mine;
+  __syncthreads();
+  for (int s = 1; s < SCAN_T; s <<= 1) {  // inclusive scan (Hillis-Steele)
+    const int64_t v = tid >= s ? sc[tid - s] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  int64_t c = sc[tid] - mine;  // exclusive
+  bool cut = false;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    coff[e] = (int32_t)(c < bound ? c : bound);
+    const int64_t n = rw_chunks(off, e, A);
+    for (int64_t j = 0; j < n; ++j) {
+      if (c + j < bound) chunk_e[c + j] = e;
+      else cut = true;
+    }
+    c += n;
+  }
+  if (tid == SCAN_T - 1) {
+    coff[E] = (int32_t)(sc[tid] < bound ? sc[tid] : bound);
+    cut = cut || sc[tid] > bound;
+  }
+  if (cut) atomicOr(&g_dev_err, MOE4_DEVERR_INDEX);
+}
+
+// Block (chunk c, column block): part[c, cb .. cb + 511] = the sum over the
+// chunk's rows of dz[t, e] * x[t, cols].  Wave w takes rows w, w + 4, ... of
+// the chunk (16 in flight) in row order; the four wave sums are added in wave
+// order.  Rows, tokens and dz are uniform per wave (scalar loads).
+__global__ void __launch_bounds__(rw::NT) k_router_wgrad_part(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ dlogits,
+                                                              const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ off,
+                                                              const int32_t* __restrict__ coff,
+                                                              const int32_t* __restrict__ chunk_e, int64_t T, int E,
+                                                              int k, int64_t d, float* __restrict__ part) {
+  using namespace rw;
+  __shared__ f32x4 red[NW - 1][64][2];
+  const int64_t c = blockIdx.x;
+  if (c >= coff[E]) return;
+  const int e = chunk_e[c];
   const int64_t A = T * k;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t r = r0 + wv; r < r1; r += 4 * NW) {
-    float dz[4];
-    u32x2 xv[4];
+  const int64_t r0 = (int64_t)off[e] + (c - coff[e]) * CH;
+  const int64_t r_end = (int64_t)off[e + 1] < r0 + CH ? (int64_t)off[e + 1] : r0 + CH;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.y * COLS + 8 * l;
+  const bool cok = col < d;
+  f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+  for (int64_t rb = r0 + w; rb < r_end; rb += NW * BATCH) {
+    float dz[BATCH];
+    u32x4 xv[BATCH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t rr = r + (int64_t)u * NW;
+    for (int u = 0; u < BATCH; ++u) {
+      const int64_t rr = rb + (int64_t)u * NW;
       dz[u] = 0.0f;
-      xv[u] = u32x2{0u, 0u};
-      if (rr < r1) {
+      xv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (rr < r_end) {
         const int64_t t = clamp_rt(perm[clamp_rt(rr, A)], A) / k;
         dz[u] = dlogits[t * E + e];
-        if (cok) xv[u] = *reinterpret_cast<const u32x2*>(x + t * d + c);
+        if (cok) xv[u] = *reinterpret_cast<const u32x4*>(x + t * d + col);
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (r + (int64_t)u * NW < r1) {
-        acc[0] = acc[0] + dz[u] * bf16_bits_to_f32(xv[u][0] & 0xFFFFu);
-        acc[1] = acc[1] + dz[u] * bf16_bits_to_f32(xv[u][0] >> 16);
-        acc[2] = acc[2] + dz[u] * bf16_bits_to_f32(xv[u][1] & 0xFFFFu);
-        acc[3] = acc[3] + dz[u] * bf16_bits_to_f32(xv[u][1] >> 16);
+    for (int u = 0; u < BATCH; ++u) {
+      if (rb + (int64_t)u * NW < r_end) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          a0[2 * i] = a0[2 * i] + dz[u] * bf16_bits_to_f32(xv[u][i] & 0xFFFFu);
+          a0[2 * i + 1] = a0[2 * i + 1] + dz[u] * bf16_bits_to_f32(xv[u][i] >> 16);
+          a1[2 * i] = a1[2 * i] + dz[u] * bf16_bits_to_f32(xv[u][2 + i] & 0xFFFFu);
+          a1[2 * i + 1] = a1[2 * i + 1] + dz[u] * bf16_bits_to_f32(xv[u][2 + i] >> 16);
+        }
       }
     }
   }
-  part[wv][l] = acc;
+  if (w > 0) {
+    red[w - 1][l][0] = a0;
+    red[w - 1][l][1] = a1;
+  }
   __syncthreads();
-  if (wv == 0 && cok) {
-    f32x4 s = part[0][l];
+  if (w == 0 && cok) {
 #pragma unroll
-    for (int q = 1; q < NW; ++q) s = s + part[q][l];
-    *reinterpret_cast<f32x4*>(dw + (int64_t)e * d + c) = s;
+    for (int q = 0; q < NW - 1; ++q) {
+      a0 = a0 + red[q][l][0];
+      a1 = a1 + red[q][l][1];
+    }
+    f32x4* o = reinterpret_cast<f32x4*>(part + c * d + col);
+    o[0] = a0;
+    o[1] = a1;
   }
+}
+
+// dw[e, cols] = the sum of expert e's partial rows in chunk order (zeros for
+// an expert without rows).
+__global__ void __launch_bounds__(rw::SUM_T) k_router_wgrad_sum(const int32_t* __restrict__ coff,
+                                                                const float* __restrict__ part, int64_t d,
+                                                                float* __restrict__ dw) {
+  using namespace rw;
+  const int e = blockIdx.x;
+  const int64_t col = (int64_t)blockIdx.y * SUM_COLS + 4 * threadIdx.x;
+  if (col >= d) return;
+  const int64_t c0 = coff[e], c1 = coff[e + 1];
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t c = c0;
+  for (; c + 8 <= c1; c += 8) {  // eight loads in flight, added in order
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(part + (c + u) * d + col);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = s + v[u];
+  }
+  for (; c < c1; ++c) s = s + *reinterpret_cast<const f32x4*>(part + c * d + col);
+  *reinterpret_cast<f32x4*>(dw + (int64_t)e * d + col) = s;
+}
+
+// Workspace of the router wgrad: coff [E + 1], chunk_e [bound], part [bound, d].
+struct RwLayout {
+  int64_t bound, off_chunk_e, off_part, bytes;
+};
+inline RwLayout rw_layout(int64_t T, int E, int k, int64_t d) {
+  RwLayout L;
+  L.bound = (T * k + rw::CH - 1) / rw::CH + E;
+  L.off_chunk_e = ((int64_t)(E + 1) * 4 + 255) / 256 * 256;
+  L.off_part = L.off_chunk_e + (L.bound * 4 + 255) / 256 * 256;
+  L.bytes = L.off_part + L.bound * d * 4;
+  return L;
 }
 
 }  // namespace moe4
@@ -262,15 +372,33 @@ extern "C" int moe_unpermute_sum_router(const float* dxp, const int32_t* inv_per
   return check_launch("moe_unpermute_sum_router");
 }
 
+extern "C" size_t moe_router_wgrad_ws_bytes(int64_t T, int32_t E, int32_t k, int64_t d) {
+  if (T < 0 || E < 1 || k < 1 || d < 1) return 0;
+  return (size_t)rw_layout(T, E, k, d).bytes;
+}
+
 extern "C" int moe_router_wgrad(const uint16_t* x, const float* dlogits, const int32_t* perm, const int32_t* expert_off,
-                                int64_t T, int32_t E, int32_t k, int64_t d, float* dw, void* stream) {
-  MOE4_REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && d > 0 && d % 4 == 0, MOE4_EINVAL,
-               "moe_router_wgrad: need 1 <= k <= E and d % 4 == 0");
+                                int64_t T, int32_t E, int32_t k, int64_t d, float* dw, void* ws, size_t ws_bytes,
+                                void* stream) {
+  MOE4_REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && d > 0 && d % 8 == 0, MOE4_EINVAL,
+               "moe_router_wgrad: need 1 <= k <= E and d % 8 == 0");
+  MOE4_REQUIRE(T * k < ((int64_t)1 << 31), MOE4_EINVAL, "moe_router_wgrad: T * k must be below 2^31");
   MOE4_REQUIRE(expert_off && dw && (T == 0 || (x && dlogits && perm)), MOE4_EINVAL, "moe_router_wgrad: NULL pointer");
-  MOE4_REQUIRE(((uintptr_t)x & 7u) == 0 && aligned16(dw), MOE4_EALIGN,
-               "moe_router_wgrad: x 8-byte, dw 16-byte aligned");
-  const dim3 grid((unsigned)E, (unsigned)((d + rw::COLS - 1) / rw::COLS));
-  hipLaunchKernelGGL(k_router_wgrad, grid, dim3(rw::NT), 0, as_stream(stream), x, dlogits, perm, expert_off, T, E, k, d,
-                     dw);
+  MOE4_REQUIRE(aligned16(x) && aligned16(dw), MOE4_EALIGN, "moe_router_wgrad: x and dw 16-byte aligned");
+  const RwLayout L = rw_layout(T, E, k, d);
+  MOE4_REQUIRE(ws != nullptr && ws_bytes >= (size_t)L.bytes, MOE4_EWORKSPACE,
+               "moe_router_wgrad: workspace of moe_router_wgrad_ws_bytes() bytes required");
+  MOE4_REQUIRE(aligned16(ws), MOE4_EALIGN, "moe_router_wgrad: ws 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  int32_t* coff = reinterpret_cast<int32_t*>(base);
+  int32_t* chunk_e = reinterpret_cast<int32_t*>(base + L.off_chunk_e);
+  float* part = reinterpret_cast<float*>(base + L.off_part);
+  const hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(k_router_wgrad_chunks, dim3(1), dim3(rw::SCAN_T), 0, s, expert_off, E, T * k, L.bound, coff,
+                     chunk_e);
+  hipLaunchKernelGGL(k_router_wgrad_part, dim3((unsigned)L.bound, (unsigned)((d + rw::COLS - 1) / rw::COLS)),
+                     dim3(rw::NT), 0, s, x, dlogits, perm, expert_off, coff, chunk_e, T, E, k, d, part);
+  hipLaunchKernelGGL(k_router_wgrad_sum, dim3((unsigned)E, (unsigned)((d + rw::SUM_COLS - 1) / rw::SUM_COLS)),
+                     dim3(rw::SUM_T), 0, s, coff, part, d, dw);
   return check_launch("moe_router_wgrad");
 }

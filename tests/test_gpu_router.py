@@ -71,7 +71,7 @@ def test_unpermute_sum_router_bit_exact(T, E, k, d):
     assert_bytes_equal(to_np(got), want, "dx with the router term")
 
 
-@pytest.mark.parametrize("T,E,k,d", [(200, 8, 2, 256), (1000, 64, 8, 4096), (50, 20, 16, 64)])
+@pytest.mark.parametrize("T,E,k,d", [(200, 8, 2, 256), (1000, 64, 8, 4096), (50, 20, 16, 64), (2500, 16, 2, 520)])
 def test_router_wgrad_tolerance(T, E, k, d):
     idx, P, dl = _routed(T, E, k, d, T + 7)
     xb = _bf16_np((T, d), 1.0, T + 9)
@@ -127,3 +127,30 @@ def test_router_logits_full_size_sampled():
     xs = fmt.bf16_to_f32(to_np(x[rows])).astype(np.float64)
     w64 = fmt.bf16_to_f32(to_np(w)).astype(np.float64)
     gemm_tol_check(to_np(lg[rows]).astype(np.float64), xs @ w64.T, np.abs(xs) @ np.abs(w64).T, "logits full size")
+
+
+def test_router_wgrad_full_size_sampled():
+    """T = 16384, E = 384, k = 8, d = 4096 with the Zipf(1.1)-biased routing of
+    the layer step (the most popular expert holds about 16000 of the 131072
+    rows, over a hundred chunks): whole rows of dW_r for the most and least
+    popular active experts, a middle one and an expert without rows."""
+    T, E, k, d = 16384, 384, 8, 4096
+    lg = (synth.randn((T, E), 1.0, "cpu", 0, "logits") + synth.zipf_bias(E, 1.1, "cpu")).numpy()
+    idx, gates = route.topk_gates(lg, k)
+    P = route.permutation(idx, E)
+    dg = (np.random.default_rng(5).standard_normal((T, k)) * 1e-2).astype(np.float32)
+    dl = route.route_backward(dg, gates, idx, E)
+    x = synth.activations(T, d, "cpu", 0)
+    xb = synth.bf16_bits(x)
+    dw = to_np(m4.moe_router_wgrad(x.cuda(), torch.from_numpy(dl).cuda(), cuda_i32(P["perm"]), cuda_i32(P["off"]), k))
+    cnt = np.diff(P["off"])
+    active = np.flatnonzero(cnt)
+    order = active[np.argsort(cnt[active], kind="stable")]
+    assert cnt.max() > 100 * 128
+    x64 = fmt.bf16_to_f32(xb).astype(np.float64)
+    for e in [order[-1], order[len(order) // 2], order[0]]:
+        tok = np.flatnonzero((idx == e).any(axis=1))
+        z = dl[tok, e].astype(np.float64)
+        gemm_tol_check(dw[e].astype(np.float64), z @ x64[tok], np.abs(z) @ np.abs(x64[tok]), f"dW_router[{e}]")
+    if (cnt == 0).any():
+        assert not dw[np.flatnonzero(cnt == 0)].any()
