@@ -19,8 +19,9 @@ their rounding):
 
 * ``e2m1_round``: round to nearest, ties to the even code, saturate at 6; the
   sign bit of the result is the sign bit of the input (so small negatives give
-  -0, code 8); a NaN input (only 0 * inf can make one) encodes as a signed
-  zero and +-inf saturates to +-6.
+  -0, code 8); +-inf saturates to +-6, and a NaN input encodes as a zero
+  with the NaN's sign bit (the NVFP4 encoder passes none: a zero element
+  under an infinite reciprocal scale stays that zero).
 * ``e4m3_round_mag``: for u >= 0, round to nearest on the E4M3 grid, ties to the
   even code, values above 448 clamp to 448.
 """
@@ -69,8 +70,7 @@ def e2m1_round(v):
     v = np.asarray(v, dtype=np.float32)
     a = np.abs(v).astype(np.float64)            # exact
     sign = _sign_bit(v)
-    # NaN can only arise as 0 * inf (a zero element under an overflowing
-    # reciprocal scale): it encodes as a signed zero.  +-inf saturates to +-6.
+    # +-inf saturates to +-6; a NaN encodes as a zero with its sign bit
     a = np.where(np.isnan(a), 0.0, np.minimum(a, 6.0))
     step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
     base = np.where(a < 2.0, 0.0, np.where(a < 4.0, 2.0, 4.0))

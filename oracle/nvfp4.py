@@ -19,7 +19,9 @@ Steps (float32 arithmetic, one rounding per operation, written fl(.)):
 2. per 16-block: amax_b = max|x_i|; for each candidate m (6, and 4 in 4/6 mode):
    d = fl(m * S); u = fl(amax_b / d); sc = e4m3(u).
 3. encode under m: if sc == 0 or eff = fl(dec(sc) * S) == 0, every code is a
-   signed zero; otherwise inv = fl(1 / eff) and q_i = e2m1(fl(x_i * inv)).
+   signed zero; otherwise inv = fl(1 / eff) and q_i = e2m1(fl(x_i * inv)),
+   where a zero x_i stays a zero of its own sign also when inv is infinite
+   (eff below 2**-128; every nonzero x_i then saturates to +-6).
 4. dequant: deq(q, sc, S) = fl(fl(dec(q) * dec(sc)) * S)  (the inner product
    is exact).
 5. error: err = 0; for i = 0..15: t = fl(x_i - deq_i); err = fl(err + fl(t * t)).
@@ -65,6 +67,10 @@ def _encode_candidate(xb, S, m):
         safe_eff = np.where(zero, F32(1.0), eff).astype(np.float32)
         inv = (F32(1.0) / safe_eff).astype(np.float32)
         y = (xb * inv[:, None]).astype(np.float32)
+        # an effective scale below 2**-128 has an infinite reciprocal: a zero
+        # element then stays that zero, with its own sign (0 * inf is a NaN
+        # whose sign the platform picks)
+        y = np.where(xb == F32(0.0), xb, y).astype(np.float32)
         q = fmt.e2m1_round(y)
         sign_only = ((xb.view(np.uint32) >> 31).astype(np.int64)) << 3
         q = np.where(zero[:, None], sign_only, q)

@@ -176,3 +176,25 @@ def test_bf16_input_equals_its_float32_value():
     a = nv.nvfp4_quantize(bits, nv.MODE_46)
     b = nv.nvfp4_quantize(fmt.bf16_to_f32(bits), nv.MODE_46)
     assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["sf"], b["sf"])
+
+
+@pytest.mark.parametrize("mode", [nv.MODE_6, nv.MODE_46])
+def test_infinite_reciprocal_keeps_zero_signs(mode):
+    """A group of float32 subnormals (about 2^-130): S = fl(amax / (m_max 448))
+    is subnormal, eff = fl(dec(sc) S) falls below 2^-128 and fl(1 / eff)
+    overflows.  By the definition every nonzero element then saturates to +-6
+    (codes 7 / 15) and every zero element keeps its own sign (codes 0 / 8),
+    whatever sign the platform gives the NaN of 0 * inf."""
+    t = np.float32(2.0 ** -130)
+    x = np.array([[t, -t / 2, 0.0, -0.0, 3 * t / 8, -5 * t / 8, 0.0, t / 4,
+                   -0.0, t / 2, -t, 0.0, t / 8, -t / 8, -0.0, 7 * t / 8]], dtype=np.float32)
+    assert np.signbit(x[0, 3]) and not np.signbit(x[0, 2])
+    q = nv.nvfp4_quantize(x, mode)
+    S = np.float32(q["ts"][0])
+    assert 0 < S < np.float32(2.0 ** -126)                     # subnormal tensor scale
+    sc = int(q["sf"][0, 0])
+    eff = np.float32(fmt.e4m3_decode(np.array([sc]))[0]) * S
+    with np.errstate(over="ignore", divide="ignore"):
+        assert np.isinf(np.float32(1.0) / eff)
+    want = np.where(x[0] == 0, np.where(np.signbit(x[0]), 8, 0), np.where(x[0] < 0, 15, 7))
+    assert np.array_equal(nv.unpack_codes(q["codes"])[0], want)
