@@ -64,6 +64,33 @@ __host__ __device__ inline uint32_t fmix32(uint32_t h) {
   return h;
 }
 
+// fmix32((x0 + p) ^ key) for p = 0..3, x0 % 4 == 0, with one first multiply
+// for the four: x0 + p = x0 ^ p, the first xor-shift keeps that difference
+// in the low two bits (h_p = h_0 ^ p), and (h ^ p) M = h M + ((t ^ p) - t) M
+// modulo 2^32 with t = h & 3, where (t ^ 3) - t = ((t ^ 1) - t) + ((t ^ 2) - t).
+// Made once per x0; word(p) finishes one of the four when it is needed.
+struct Fmix32x4 {
+  static constexpr uint32_t M1 = 0x85EBCA6Bu, M2 = 0xC2B2AE35u;
+  uint32_t m0, d1, d2;
+  __device__ Fmix32x4(uint32_t x0, uint32_t key) {
+    uint32_t h = x0 ^ key;
+    h ^= h >> 16;
+    m0 = h * M1;
+    // +-M1 and +-2 M1 as (c ^ s) - s with s = 0 or all ones (no select, whose
+    // constant operands would each take a register)
+    const uint32_t s1 = 0u - (h & 1u), s2 = 0u - ((h >> 1) & 1u);
+    d1 = (M1 ^ s1) - s1;
+    d2 = ((2u * M1) ^ s2) - s2;
+  }
+  __device__ uint32_t word(int p) const {
+    uint32_t t = m0 + ((p & 1) ? d1 : 0u) + ((p & 2) ? d2 : 0u);
+    t ^= t >> 13;
+    t *= M2;
+    asm("" : "+v"(t));  // (as in fmix32)
+    return t ^ (t >> 16);
+  }
+};
+
 // Seed/stream part of the stochastic-rounding key (host computes it once).
 inline uint32_t sr_base_key(uint64_t seed, uint32_t stream_id) {
   uint32_t k = fmix32(static_cast<uint32_t>(seed));

@@ -73,7 +73,9 @@ __device__ inline bool fold_scale_ok(float S) { return S >= 0x1p-100f && S < 0x1
 // rows leaves as one dword per column (byte i % 4 = row i) through
 // put(k, column, dword), k = row group.  Rows past nvalid are zero codes.
 // FAST: every element pair index of the block is below 2**32, so the
-// per-pair key is the constant key0 and the index arithmetic is 32-bit.
+// per-pair key is the constant key0 and the index arithmetic is 32-bit (and
+// j0, jstride are multiples of 4: a lane's 8 columns start at a multiple of 8
+// and the row length is a multiple of 32, so Fmix32x4 applies).
 // FULL: all 32 rows are valid (no row masks).
 // deq(i, q) gives row i's 8 exact source values (before the factor S).
 template <bool FAST, bool FULL, typename Deq, typename Put>
@@ -90,11 +92,12 @@ __device__ inline void requant_block(Deq deq, int nvalid, float S, const float (
       if (FULL || i < nvalid) {
         float q[8];
         deq(i, q);
+        const Fmix32x4 hw((uint32_t)j0 + (uint32_t)i * (uint32_t)jstride, key0);  // (used when FAST)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t word;
           if (FAST) {
-            word = fmix32(((uint32_t)j0 + (uint32_t)i * (uint32_t)jstride + (uint32_t)p) ^ key0);
+            word = hw.word(p);
           } else {
             const int64_t j = j0 + (int64_t)i * jstride + p;
             word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));

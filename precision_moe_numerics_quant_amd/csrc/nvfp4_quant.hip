@@ -19,6 +19,7 @@
 // is built with -ffp-contract=off), with correctly rounded division.
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "act.h"
 #include "gemm_common.h"
@@ -686,6 +687,10 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
   __shared__ uint8_t lmxs[TC];                                         // MX scale byte of each column
   __shared__ float s_red[WAVES];
   __shared__ float s_S[2];  // tensor scales of groups g (slot g & 1) and g + 1
+  // per slot: 1 / (e4m3(c) S) for every scale byte c (c = 127, a NaN code,
+  // as infinity), and 1 / (6 S)
+  __shared__ float s_inv[2][128];
+  __shared__ float s_r6[2];
   const uint32_t n_tile = gridDim.x;
   const int tid = threadIdx.x, l = tid & 63, cg = l & 7, rg = l >> 3;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -762,7 +767,13 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
     const float S = (sv == 0.0f) ? 1.0f : sv;
     if (l == 0) {
       s_S[g & 1] = S;
+      s_r6[g & 1] = 1.0f / (6.0f * S);
       if (ti == 0) ts[g] = S;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = l + 64 * k;
+      s_inv[g & 1][c] = c == 127 ? __builtin_inff() : 1.0f / (e4m3_to_f32((uint32_t)c) * S);
     }
   };
   // NVFP4 mode 6 of the lane's 4 x 8 values, then the SR MXFP8 bytes of the
@@ -773,6 +784,12 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
     const int cg = lx & 7, rg = lx >> 3;
     const float S = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(S_in)));  // (wave-uniform)
     const float d6 = 6.0f * S;
+    const float* inv_tab = s_inv[g & 1];
+    const float r6 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(s_r6[g & 1])));
+    // a * fl(1 / d6) lies within 3 ulps of fl(a / d6) when d6 and its
+    // reciprocal are normal: then if the E4M3 codes of the product 4 ulps down
+    // and 4 ulps up agree, fl(a / d6) (between them) has that code too
+    const bool r6_ok = d6 >= 0x1p-126f && r6 >= 0x1p-126f && r6 < __builtin_inff();
     uint32_t cw[4], scb[4];
     float am[8];
 #pragma unroll
@@ -785,13 +802,22 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
       a = fmaxf(a, lane_xor1(a));  // the block's other half
-      // encode_half's steps; its zero-scale and infinite-reciprocal cases
-      // (tiny values) go through it whenever a lane of the wave meets one
-      const uint32_t sc = e4m3_rne_u(a / d6);
-      const float eff = e4m3_to_f32(sc) * S;
-      const float inv = 1.0f / eff;
+      // encode_half's steps: sc = e4m3_rne_u(a / d6) (through the product
+      // check above; the division for lanes it leaves open) and the
+      // reciprocal of the effective scale from the table; its zero-scale and
+      // infinite-reciprocal cases (tiny values) go through encode_half
+      // whenever a lane of the wave meets one
+      const uint32_t ub = __float_as_uint(fminf(a * r6, 448.0f));
+      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(ub >= 4u ? ub - 4u : 0u),
+                                                                   __uint_as_float(ub + 4u), 0, false);
+      uint32_t sc = pk & 0xFFu;
+      const bool sc_ok = r6_ok && sc == ((pk >> 8) & 0xFFu);
+      if (__builtin_expect(__any(!sc_ok), 0)) {
+        if (!sc_ok) sc = e4m3_rne_u(a / d6);
+      }
+      const float inv = inv_tab[sc];  // infinite for sc = 0 and for an underflowing e4m3(sc) S
       uint32_t q = 0u;
-      if (__builtin_expect(__any(sc == 0u || eff == 0.0f || __builtin_isinf(inv)), 0)) {
+      if (__builtin_expect(__any(__builtin_isinf(inv)), 0)) {
         uint32_t sc2;
         q = encode_half(v, a, S, 6.0f, sc2);
       } else {
@@ -835,11 +861,13 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
       for (int i = 0; i < 4; ++i) {
         float q8[8];
         dequant8(cw[i], scb[i], q8);
+        // (used when FAST; jr0 and C / 2 are multiples of 4: columns in steps of 8, C % 256 == 0)
+        const Fmix32x4 hw((uint32_t)jr0 + (uint32_t)i * (uint32_t)(C / 2), key0);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t word;
           if (FAST) {
-            word = fmix32(((uint32_t)jr0 + (uint32_t)i * (uint32_t)(C / 2) + (uint32_t)p) ^ key0);
+            word = hw.word(p);
           } else {
             const int64_t j = jr0 + i * (C / 2) + p;
             word = fmix32((uint32_t)j ^ fmix32(base ^ (uint32_t)((uint64_t)j >> 32)));
@@ -858,37 +886,72 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
   // (waves 1-3) the staged tile of group g in runs of 64 pieces of one kind,
   // run r = (w - 1) + 3 k: 8 runs of MXFP8 codes (a column's 32 rows as two
   // 16-byte pieces), 4 of NVFP4 codes (16 bytes of a row), 4 of MX scale
-  // bytes (one per column) and half a run of NVFP4 scale bytes (16 per row)
+  // bytes (one per column) and half a run of NVFP4 scale bytes (16 per row).
+  // Each wave's runs are compile-time constants (one instantiation per
+  // wave), so no run test is kept live across the rounds.  Offsets are 24-bit
+  // products: a group's tile grid has at most 768 tiles of 32 x 256, so rows
+  // and columns stay below 2^23.
+  auto store_run = [&](auto run_c, int64_t gel, int li) {
+    constexpr int run = decltype(run_c)::value;
+    const int it = 64 * run + li;
+    if constexpr (run < 8) {
+      const int col = it >> 1, h = it & 1;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lq + col * TR + 16 * h);
+      __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]}, make_rsrc(out_c + gel, (uint64_t)grows * C),
+                                             __umul24((uint32_t)(c0 + col), (uint32_t)grows) + (uint32_t)(rt0 + 16 * h),
+                                             0, 0);
+    } else if constexpr (run < 12) {
+      const int jt = it - 512, row = jt >> 3, h = jt & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lcode + row * (TC / 2) + 16 * h);
+      __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
+                                             make_rsrc(codes + gel / 2, (uint64_t)grows * C / 2),
+                                             __umul24((uint32_t)(rt0 + row), (uint32_t)(C / 2)) +
+                                                 (uint32_t)(c0 / 2 + 16 * h),
+                                             0, 0);
+    } else if constexpr (run < 16) {
+      const int col = it - 768;
+      __builtin_amdgcn_raw_buffer_store_b8(lmxs[col], make_rsrc(out_s + gel / 32, (uint64_t)grows * C / 32),
+                                           __umul24((uint32_t)(c0 + col), (uint32_t)(grows / 32)) +
+                                               (uint32_t)(rt0 / 32),
+                                           0, 0);
+    } else if constexpr (run == 16) {
+      if (li < TR) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lsf + li * (TC / 16));
+        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
+                                               make_rsrc(sf + gel / 16, (uint64_t)grows * C / 16),
+                                               __umul24((uint32_t)(rt0 + li), (uint32_t)(C / 16)) +
+                                                   (uint32_t)(c0 / 16),
+                                               0, 0);
+      }
+    }
+  };
   auto store = [&](int g) {
     // (the lane index passes through an empty asm so that the addresses
     // below are made here, not kept live across the rounds)
     int li = l;
     asm volatile("" : "+v"(li));
     const int64_t gel = (int64_t)g * grows * C;  // the group's first element
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      const int run = (w - 1) + 3 * k, it = 64 * run + li;
-      if (run < 8) {
-        const int col = it >> 1, h = it & 1;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lq + col * TR + 16 * h);
-        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]}, make_rsrc(out_c + gel, (uint64_t)grows * C),
-                                               (uint32_t)((c0 + col) * grows + rt0 + 16 * h), 0, 0);
-      } else if (run < 12) {
-        const int jt = it - 512, row = jt >> 3, h = jt & 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lcode + row * (TC / 2) + 16 * h);
-        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
-                                               make_rsrc(codes + gel / 2, (uint64_t)grows * C / 2),
-                                               (uint32_t)((rt0 + row) * (C / 2) + c0 / 2 + 16 * h), 0, 0);
-      } else if (run < 16) {
-        const int col = it - 768;
-        __builtin_amdgcn_raw_buffer_store_b8(lmxs[col], make_rsrc(out_s + gel / 32, (uint64_t)grows * C / 32),
-                                             (uint32_t)((c0 + col) * (grows / 32) + rt0 / 32), 0, 0);
-      } else if (run == 16 && li < TR) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lsf + li * (TC / 16));
-        __builtin_amdgcn_raw_buffer_store_b128(v4u{v[0], v[1], v[2], v[3]},
-                                               make_rsrc(sf + gel / 16, (uint64_t)grows * C / 16),
-                                               (uint32_t)((rt0 + li) * (C / 16) + c0 / 16), 0, 0);
-      }
+    using std::integral_constant;
+    if (w == 1) {
+      store_run(integral_constant<int, 0>{}, gel, li);
+      store_run(integral_constant<int, 3>{}, gel, li);
+      store_run(integral_constant<int, 6>{}, gel, li);
+      store_run(integral_constant<int, 9>{}, gel, li);
+      store_run(integral_constant<int, 12>{}, gel, li);
+      store_run(integral_constant<int, 15>{}, gel, li);
+    } else if (w == 2) {
+      store_run(integral_constant<int, 1>{}, gel, li);
+      store_run(integral_constant<int, 4>{}, gel, li);
+      store_run(integral_constant<int, 7>{}, gel, li);
+      store_run(integral_constant<int, 10>{}, gel, li);
+      store_run(integral_constant<int, 13>{}, gel, li);
+      store_run(integral_constant<int, 16>{}, gel, li);
+    } else {
+      store_run(integral_constant<int, 2>{}, gel, li);
+      store_run(integral_constant<int, 5>{}, gel, li);
+      store_run(integral_constant<int, 8>{}, gel, li);
+      store_run(integral_constant<int, 11>{}, gel, li);
+      store_run(integral_constant<int, 14>{}, gel, li);
     }
   };
   // round g: X holds group g (its tensor scale in s_S[g & 1]), Y group g + 1

@@ -411,6 +411,41 @@ def test_fused_weight_quant_requant_bit_exact(G, Rg, C):
     assert_bytes_equal(to_np(ms), ms_ref, "mx scales")
 
 
+def test_fused_weight_quant_midpoint_scales():
+    """The single-read weight kernel where its shortcuts must step aside:
+    group 0 has the tensor scale S = 2^-8 exactly (amax 2688 * 2^-8) and
+    16-blocks whose amax / (6 S) is exactly a midpoint between two E4M3
+    values, so the product with the rounded reciprocal 1 / (6 S) cannot decide
+    the scale byte and the division must (ties to even); group 1 is so small
+    (about 2^-127, float32 subnormals) that 6 S is subnormal and every scale
+    byte comes from the division; group 2 is ordinary.  Byte for byte against
+    the oracle."""
+    G, Rg, C = 3, 256, 1024                                      # 8 x 4 = 32 tiles of 32 x 256 per group
+    rng = np.random.default_rng(77)
+    w = (rng.standard_normal((G * Rg, C)) * 0.004).astype(np.float32)
+    w[0, 0] = np.float32(2688.0 * 2.0 ** -8)                     # group 0's amax: S = 2^-8
+    mids = [(2 * n + 1) / 16.0 * 2.0 ** e for n in range(8, 16) for e in range(-4, 3)]
+    blocks = rng.choice(Rg * (C // 16) - 1, size=len(mids), replace=False) + 1
+    for m, b in zip(mids, blocks):                               # block amax 6 m 2^-8, the rest below it
+        r, c = divmod(int(b), C // 16)
+        blk = (rng.random(16) * 2 - 1) * (6.0 * m * 2.0 ** -8) * 0.9
+        blk[rng.integers(16)] = 6.0 * m * 2.0 ** -8 * (1 if rng.random() < 0.5 else -1)
+        w[r, 16 * c:16 * c + 16] = blk.astype(np.float32)
+    w[Rg:2 * Rg] *= np.float32(2.0 ** -120)
+    w[Rg:2 * Rg] *= np.float32(2.0 ** -7)                        # (two steps: the factor itself is normal)
+    assert np.float32(np.abs(w[Rg:2 * Rg]).max()) / np.float32(2688.0) * 6 < 2.0 ** -126
+    off = np.arange(G + 1) * Rg
+    q = nv.nvfp4_quantize(w, nv.MODE_6, off)
+    assert np.asarray(q["ts"], dtype=np.float32)[0] == np.float32(2.0 ** -8)
+    mc_ref, ms_ref = mx.requant_sr_t(q["codes"], q["sf"], q["ts"], off, True, seed=5, stream_id=3)
+    codes, sf, ts, mc, ms = m4.nvfp4_quant_requant_T(torch.from_numpy(w).cuda(), G, seed=5, stream_id=3)
+    assert_bytes_equal(to_np(ts).view(np.uint32), np.asarray(q["ts"], dtype=np.float32).view(np.uint32), "ts")
+    assert_bytes_equal(to_np(sf), q["sf"], "scales")
+    assert_bytes_equal(to_np(codes), q["codes"], "codes")
+    assert_bytes_equal(to_np(mc), mc_ref, "mx codes")
+    assert_bytes_equal(to_np(ms), ms_ref, "mx scales")
+
+
 @pytest.mark.parametrize("G,Rg,C", [(1, 32, 32), (3, 64, 1056), (2, 160, 512), (5, 96, 96), (320, 32, 512)])
 def test_fused_mx_weight_quant_requant_bit_exact(G, Rg, C):
     """mxfp8_quant_requant_T (the MXFP8-forward weights) equals MXFP8 RNE
