@@ -202,13 +202,15 @@ def trace_summary(trace_csv, min_frac=0.1):
     rows = []
     for name, v in durs.items():
         big = [x for x in v if x >= min_frac * max(v)]
-        rows.append((sum(v), name, len(v), len(big), float(np.mean(big))))
+        rows.append((sum(v), name, len(v), len(big), float(np.mean(big)), float(np.median(big))))
     rows.sort(reverse=True)
-    out = ["| kernel | launches | at layer shape | avg us at layer shape | total ms (all) | % of GPU time |",
-           "|---|---:|---:|---:|---:|---:|"]
-    for tot, name, n, nb, avg in rows[:30]:
+    out = ["| kernel | launches | at layer shape | avg us at layer shape | median us at layer shape | total ms (all) "
+           "| % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for tot, name, n, nb, avg, med in rows[:30]:
         short = name.split("(")[0] if "<" not in name.split("(")[0] else name.split(")")[0].split("(")[0]
-        out.append(f"| `{short[:90]}` | {n} | {nb} | {avg:.1f} | {tot / 1000.0:.2f} | {100.0 * tot / total:.2f} |")
+        out.append(f"| `{short[:90]}` | {n} | {nb} | {avg:.1f} | {med:.1f} | {tot / 1000.0:.2f} "
+                   f"| {100.0 * tot / total:.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -283,6 +285,14 @@ def gpu_run(steps, warmup, layer_only=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps
+    # device-side reports of the timed steps (a bounded wait that gave up, a
+    # clamped index): a step that had one did not compute what it should
+    try:
+        m4.moe4_debug_check()
+        device_error = None
+    except m4.Moe4DeviceError as exc:
+        device_error = str(exc)
+        print(f"bench: device-side error in the timed steps: {exc}", file=sys.stderr)
     # per-call breakdown over the same number of steps (events between calls)
     events.clear()
     torch.cuda.synchronize()
@@ -298,7 +308,7 @@ def gpu_run(steps, warmup, layer_only=False):
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
     if layer_only:          # (profiling runs: the layer's launches only)
-        return c, ms_step, wall, per, off, off_pad, None, None, None, None
+        return c, ms_step, wall, per, off, off_pad, None, None, None, None, device_error
     zero_fill = wgrad_zero_fill_bench(fw, bw, c, off)
     router_r = router_bench(inp, fw, bw, c)
     payload = combine_payload_bench(fw, c)
@@ -327,7 +337,8 @@ def gpu_run(steps, warmup, layer_only=False):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
-    return c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, (small, router_r), zero_fill
+    return (c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, (small, router_r), zero_fill,
+            device_error)
 
 
 def _median_ms(fn, reps):
@@ -623,7 +634,7 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill = gpu_run(args.steps, args.warmup,
+    c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill, device_error = gpu_run(args.steps, args.warmup,
                                                                                   args.layer_only)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
@@ -701,6 +712,8 @@ def main():
         "data_movement_gbps": round(pool["m"][0] / (pool["m"][1] * 1e-3) / 1e9, 1),
         "breakdown": calls,
         "roofline": roof,
+        # a device-side report during the timed steps (null: none)
+        "device_error": device_error,
     }
     if not args.layer_only:
         ms_mx, per_mx = mxv

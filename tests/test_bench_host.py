@@ -106,3 +106,4 @@ def test_trace_summary_keeps_the_layer_shape_launches(tmp_path):
     row = [line for line in out.splitlines() if "k_encode_requant_T" in line][0]
     cells = [x.strip() for x in row.strip("|").split("|")]
     assert cells[1] == "4" and cells[2] == "2" and abs(float(cells[3]) - 4100.0) < 1e-6
+    assert abs(float(cells[4]) - 4100.0) < 1e-6                              # median of the two
