@@ -698,7 +698,9 @@ __global__ void __launch_bounds__(wr::THREADS, wr::MIN_BLOCKS)
   // this workgroup's tile: 8 consecutive tiles run on 8 XCDs; each XCD takes
   // runs of 4 row-adjacent tiles (the 128 rows of four MX blocks)
   const uint32_t ti = blockIdx.x, q = ti >> 3, quad = (q >> 2) * 8 + (ti & 7);
-  const uint32_t n_cb = (uint32_t)(C / TC), rq = quad / n_cb, cb = quad - rq * n_cb;
+  // (the quotient through readfirstlane: the division runs on the VALU, and
+  // the tile's row and column block are uniform, kept in scalar registers)
+  const uint32_t n_cb = (uint32_t)(C / TC), rq = __builtin_amdgcn_readfirstlane(quad / n_cb), cb = quad - rq * n_cb;
   const int64_t rt0 = (int64_t)(4 * rq + (q & 3)) * TR, c0 = (int64_t)cb * TC;
   const int64_t lrow = rt0 + 4 * rg, lcol = c0 + 64 * w + 8 * cg;  // the lane's first row (in its group) and column
 
