@@ -870,14 +870,24 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
       for (int j = 0; j < NJ; ++j) {
         if (active) {
           const uint32_t fo = (uint32_t)(wm + i * 32) * ld + (uint32_t)(n0 + wn + j * 32) * ESZ;
+          const int rows_left = (int)nrows - (wm + i * 32 + g * 4);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const uint32_t so = fo + (uint32_t)((v >> 2) * 8 + (v & 3)) * ld;
             const float x = acc[i][j][v] * sab;
-            if (OUT_BF16)
-              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(x), rC, lane_off, so, 2);
-            else
+            if (OUT_BF16) {
+              const uint32_t b = f32_to_bf16_bits(x);
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)b, rC, lane_off, so, 2);
+              if (amx && (v >> 2) * 8 + (v & 3) < rows_left) {  // the stored values of the expert's rows
+                const uint32_t m = b & 0x7FFFu;
+                const bool neg = b >= 0x8000u;
+                pmax = max(pmax, neg ? 0u : m);
+                nlo = min(nlo, neg && m >= M1 ? m : 0x8000u);
+                nhi = max(nhi, neg && m < M1 ? m : 0u);
+              }
+            } else {
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rC, lane_off, so, 2);
+            }
             if constexpr (HMX8) {  // row (v / 4) 8 + 4 g + v % 4 of the fragment, column li
               hb[((v & 7) >> 2) * 8 * 36 + (g * 4 + (v & 3)) * 36 + li] = x;
               if ((v & 7) == 7) {  // a 16-row half is in the block
@@ -890,24 +900,7 @@ __global__ void __launch_bounds__(fws::Cfg<TN>::NT, 1)
           }
         }
       }
-    if (amx) {  // the same bf16 values, folded in a pass of their own
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int rows_left = (int)nrows - (wm + i * 32 + g * 4);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            if ((v >> 2) * 8 + (v & 3) < rows_left) {
-              const uint32_t b = f32_to_bf16_bits(acc[i][j][v] * sab);
-              const uint32_t m = b & 0x7FFFu;
-              const bool neg = b >= 0x8000u;
-              pmax = max(pmax, neg ? 0u : m);
-              nlo = min(nlo, neg && m >= M1 ? m : 0x8000u);
-              nhi = max(nhi, neg && m < M1 ? m : 0u);
-            }
-          }
-      }
+    if (amx) {  // the wave's extremes (folded in the store loop above), then one atomic
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         pmax = max(pmax, (uint32_t)__shfl_xor((int)pmax, o, 64));
