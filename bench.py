@@ -293,6 +293,7 @@ def gpu_run(steps, warmup, layer_only=False):
     except m4.Moe4DeviceError as exc:
         device_error = str(exc)
         print(f"bench: device-side error in the timed steps: {exc}", file=sys.stderr)
+    ref_outputs = None if layer_only else _fingerprint(fw, bw)
     # per-call breakdown over the same number of steps (events between calls)
     events.clear()
     torch.cuda.synchronize()
@@ -308,7 +309,7 @@ def gpu_run(steps, warmup, layer_only=False):
     off = fw["route"]["off"].cpu().numpy()
     off_pad = fw["route"]["off_pad"].cpu().numpy()
     if layer_only:          # (profiling runs: the layer's launches only)
-        return c, ms_step, wall, per, off, off_pad, None, None, None, None, device_error
+        return c, ms_step, wall, per, off, off_pad, None, None, None, None, device_error, None
     zero_fill = wgrad_zero_fill_bench(fw, bw, c, off)
     router_r = router_bench(inp, fw, bw, c)
     payload = combine_payload_bench(fw, c)
@@ -337,8 +338,11 @@ def gpu_run(steps, warmup, layer_only=False):
         if prev is not None and name is not None:
             per_mx[name] = round(prev.elapsed_time(ev), 4)
         prev = ev
+    # last, since its memory pool makes the caching allocator's later large
+    # allocations slow: the step replayed from one HIP graph
+    graph_run = graph_steps(step, steps, ref_outputs)
     return (c, ms_step, wall, per, off, off_pad, (ms_mx, per_mx), payload, (small, router_r), zero_fill,
-            device_error)
+            device_error, graph_run)
 
 
 def _median_ms(fn, reps):
@@ -401,6 +405,50 @@ def wgrad_zero_fill_bench(fw, bw, c, off, reps=10):
     return {"empty_experts": empty, "zero_fill_bytes": empty * 2.0 * d * F * 4.0,
             "ms_both_wgrad_skip": round(t_skip, 4), "ms_both_wgrad_zero_fill": round(t_fill, 4),
             "ms_zero_fill": round(t_fill - t_skip, 4)}
+
+
+def _fingerprint(fw, bw):
+    """Copies of a step's outputs to compare bit for bit: y, dx, dg and the
+    weight gradients of the first four experts that received tokens."""
+    off = fw["route"]["off"]
+    act = torch.nonzero(off[1:] > off[:-1]).flatten()[:4]
+    return [fw["y"].clone(), bw["dx"].clone(), bw["dg"].clone(), bw["dW_up"][act].clone(), bw["dW_down"][act].clone()]
+
+
+def graph_steps(step, steps, ref):
+    """The layer step captured once in a HIP graph (through torch.cuda.CUDAGraph,
+    the second stream's fork and join included) and replayed: every kernel of
+    the step runs on every replay, without the per-call launch and binding work
+    on the host.  The first replay must equal the eager step (ref) bit for bit;
+    then `steps` replays are timed.  Returns dict(bit_identical, ms_per_step)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # (warm-up on the capturing stream, as torch asks)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gfw, gbw = step()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, _fingerprint(gfw, gbw)))
+    ms = None
+    if same:
+        graph.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+    del gfw, gbw, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"bit_identical": same, "ms_per_step": ms}
 
 
 def small_configs_bench(inp4, wq, reps=20):
@@ -634,7 +682,7 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill, device_error = gpu_run(args.steps, args.warmup,
+    c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill, device_error, graph_run = gpu_run(args.steps, args.warmup,
                                                                                   args.layer_only)
     table = work_table(c, off, off_pad)
     peaks = {"hbm": PEAK_HBM, "f16": PEAK_F16, "fp8": PEAK_FP8}
@@ -715,6 +763,12 @@ def main():
         # a device-side report during the timed steps (null: none)
         "device_error": device_error,
     }
+    if graph_run is not None:
+        # the same step captured once in a HIP graph and replayed (every kernel
+        # runs on every replay; the first replay equals the eager step bit for bit)
+        out["graph_replay"] = {"bit_identical": graph_run["bit_identical"],
+                               "ms_per_step": None if graph_run["ms_per_step"] is None
+                               else round(graph_run["ms_per_step"], 3)}
     if not args.layer_only:
         ms_mx, per_mx = mxv
         out.update({

@@ -424,3 +424,49 @@ def test_layer_step_graph_replay_matches_eager(side_stream, monkeypatch):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, name)
         step()                         # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_full_layer_step_graph_replay_matches_eager():
+    """The benchmark's step (T=16384, d=4096, F=1536, E=384, top-8, Zipf
+    routing; the second stream in the forward and backward) captured in one
+    graph: three replays, with eager steps and host syncs between them, each
+    give the eager step's y, dx, dg, dlogits and the weight gradients of
+    sixteen experts that received tokens (the first and last eight) bit for
+    bit."""
+    c = synth.CONFIGS[4]
+    inp = synth.config_inputs(4, device="cuda", seed=0)
+
+    def step():
+        fw = layer.forward(inp["x"], inp["w_up"], inp["w_down"], inp["logits"], c["k"], inp["bias"],
+                           seed=synth.SR_SEED)
+        bw = layer.backward(fw, inp["dy"], seed=synth.SR_SEED, skip_empty_dw=True)
+        return fw, bw
+
+    def outputs(fw, bw, act):
+        return [fw["y"], bw["dx"], bw["dg"], bw["dlogits"], bw["dW_up"][act], bw["dW_down"][act]]
+
+    fw, bw = step()
+    off = fw["route"]["off"]
+    act = torch.nonzero(off[1:] > off[:-1]).flatten()
+    act = torch.cat([act[:8], act[-8:]])
+    ref = [t.clone() for t in outputs(fw, bw, act)]
+    del fw, bw
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gfw, gbw = step()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "dx", "dg", "dlogits", "dW_up", "dW_down"), outputs(gfw, gbw, act), ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, name)
+        step()                         # eager work between replays
+        torch.cuda.synchronize()
+    m4.moe4_debug_check()
