@@ -44,6 +44,21 @@ __device__ inline uint32_t mx_round(float w, uint32_t r16) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(w, 0.0f, 0, false) & 0xFFu;
 }
 
+// Four consecutive values, already scaled, as one word of E4M3 bytes (value i
+// in byte i): RNE two values per conversion, SR each into its byte, with the
+// pair words' halves as random bits as in mx_round (w0: values 0, 1; w1: 2, 3).
+template <bool SR>
+__device__ inline uint32_t mx_word4(float a, float b, float c, float d, uint32_t w0, uint32_t w1) {
+  if (SR) {
+    uint32_t o = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, a, w0 << 16, 1.0f, 0);
+    o = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(o, b, w0 & 0xFFFF0000u, 1.0f, 1);
+    o = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(o, c, w1 << 16, 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(o, d, w1 & 0xFFFF0000u, 1.0f, 3);
+  }
+  const uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)o, true);
+}
+
 // Random word of element pair j = i >> 1 (base = seed/stream key).
 __device__ inline uint32_t sr_word(uint32_t base, uint64_t j) {
   uint32_t key = fmix32(base ^ (uint32_t)(j >> 32));
@@ -511,11 +526,7 @@ __global__ void __launch_bounds__(256) k_mx_rows(GradSrc g, int64_t R, int64_t C
       w0 = sr_word(base, i0 >> 1);
       w1 = sr_word(base, (i0 >> 1) + 1);
     }
-    uint32_t b0 = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu);
-    uint32_t b1 = mx_round<SR>(v[4 * q + 1] * p, w0 >> 16);
-    uint32_t b2 = mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu);
-    uint32_t b3 = mx_round<SR>(v[4 * q + 3] * p, w1 >> 16);
-    outw[q] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    outw[q] = mx_word4<SR>(v[4 * q] * p, v[4 * q + 1] * p, v[4 * q + 2] * p, v[4 * q + 3] * p, w0, w1);
   }
   u32x4* o = reinterpret_cast<u32x4*>(out_c + r * C + c0);
   o[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
@@ -600,9 +611,7 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
             w0 = sr_word(base, i0 >> 1);
             w1 = sr_word(base, (i0 >> 1) + 1);
           }
-          ow[q] = mx_round<SR>(v[4 * q] * p, w0 & 0xFFFFu) | (mx_round<SR>(v[4 * q + 1] * p, w0 >> 16) << 8) |
-                  (mx_round<SR>(v[4 * q + 2] * p, w1 & 0xFFFFu) << 16) |
-                  (mx_round<SR>(v[4 * q + 3] * p, w1 >> 16) << 24);
+          ow[q] = mx_word4<SR>(v[4 * q] * p, v[4 * q + 1] * p, v[4 * q + 2] * p, v[4 * q + 3] * p, w0, w1);
         }
         *reinterpret_cast<u32x4*>(row_c + r_out * C + cg) = u32x4{ow[0], ow[1], ow[2], ow[3]};
         if (half == 0) row_s[r_out * (C / 32) + cg / 32] = (uint8_t)(e + 127);
