@@ -432,66 +432,79 @@ __device__ inline f32x4 grad_vals4(const GradSrc& g, int64_t r, int64_t C, int64
 }
 
 // grad_vals4 for 16 consecutive columns c .. c + 15 (c % 16 == 0, C % 16 ==
-// 0): the source row (and its map and scale) resolved once, 16-byte loads;
+// 0) in two parts, so that a tile's loads can be in flight while the previous
+// tile is quantised: grad_load16 resolves the source row (and its map and
+// scale) once and issues 16-byte loads, grad_finish16 makes the 16 values;
 // dtab is the narrow table (stage_act_table_narrow).
+struct GradRaw {
+  u32x4 w[4];  // the source values (bf16: w[0..1]; float32: w[0..3])
+  u32x4 u[2];  // MODE 2: the bf16 patterns of U
+  float sc;    // MODE 1: the row's scale
+};
+
 template <int DT, int MODE>
-__device__ inline void grad_vals16(const GradSrc& g, int64_t r, int64_t C, int64_t c, const float* dtab,
-                                   float (&v)[16]) {
+__device__ inline void grad_load16(const GradSrc& g, int64_t r, int64_t C, int64_t c, GradRaw& q) {
   int64_t src = r;
-  float sc = 1.0f;
+  q.sc = 1.0f;
   if (MODE == 1) {
     const int32_t a = g.row_map[r];
-    if (g.row_scale) sc = g.row_scale[a];
+    if (g.row_scale) q.sc = g.row_scale[a];
     src = a / g.map_div;
   }
   const int64_t idx = src * C + c;
-  if (MODE == 3) {  // (x holds bf16 bits)
+  if (MODE == 3 || DT != MOE4_F32) {  // (bf16 bits)
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.x) + idx);
+    q.w[0] = p[0];
+    q.w[1] = p[1];
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(g.x) + idx);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4 u = p[q];
+    for (int k = 0; k < 4; ++k) q.w[k] = p[k];
+  }
+  if (MODE == 2) {
+    const u32x4* pu = reinterpret_cast<const u32x4*>(g.dsilu_src + r * C + c);
+    q.u[0] = pu[0];
+    q.u[1] = pu[1];
+  }
+}
+
+template <int DT, int MODE>
+__device__ inline void grad_finish16(const GradRaw& q, const float* dtab, float (&v)[16]) {
+  if (MODE == 3) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * q + 2 * j] = act_eval_narrow<false>(u[j] & 0xFFFFu, dtab);
-        v[8 * q + 2 * j + 1] = act_eval_narrow<false>(u[j] >> 16, dtab);
+        v[8 * k + 2 * j] = act_eval_narrow<false>(q.w[k][j] & 0xFFFFu, dtab);
+        v[8 * k + 2 * j + 1] = act_eval_narrow<false>(q.w[k][j] >> 16, dtab);
       }
-    }
     return;
   }
   if (DT == MOE4_F32) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(g.x) + idx);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 t = p[q];
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * q + j] = t[j];
-    }
+      for (int j = 0; j < 4; ++j) v[4 * k + j] = __uint_as_float(q.w[k][j]);
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.x) + idx);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4 u = p[q];
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * q + 2 * j] = bf16_bits_to_f32(u[j] & 0xFFFFu);
-        v[8 * q + 2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+        v[8 * k + 2 * j] = bf16_bits_to_f32(q.w[k][j] & 0xFFFFu);
+        v[8 * k + 2 * j + 1] = bf16_bits_to_f32(q.w[k][j] >> 16);
       }
-    }
   }
   if (MODE == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = sc * v[i];
+    for (int i = 0; i < 16; ++i) v[i] = q.sc * v[i];
   } else if (MODE == 2) {
-    const u32x4* pu = reinterpret_cast<const u32x4*>(g.dsilu_src + r * C + c);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4 u = pu[q];
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * q + 2 * j] = v[8 * q + 2 * j] * act_eval_narrow<true>(u[j] & 0xFFFFu, dtab);
-        v[8 * q + 2 * j + 1] = v[8 * q + 2 * j + 1] * act_eval_narrow<true>(u[j] >> 16, dtab);
+        v[8 * k + 2 * j] = v[8 * k + 2 * j] * act_eval_narrow<true>(q.u[k][j] & 0xFFFFu, dtab);
+        v[8 * k + 2 * j + 1] = v[8 * k + 2 * j + 1] * act_eval_narrow<true>(q.u[k][j] >> 16, dtab);
       }
-    }
   }
 }
 
@@ -556,7 +569,8 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
   // go out.  For gathered rows (MODE 1) the column tiles of one row tile run
   // together instead, so they share the gathered source rows in L2 (measured:
   // each order is the faster one for its mode).  A workgroup takes cpw
-  // column tiles of its row tile in turn (the table staged once).
+  // column tiles of its row tile in turn (the table staged once; each tile's
+  // source loads issued while the previous tile is quantised).
   const int64_t n_cw = (n_ct + cpw - 1) / cpw;
   int64_t cw, rt;
   if (MODE == 1) {
@@ -571,15 +585,21 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
   TileT t;
   if (!tile_coords(off, offp, G, C, R, max_pr, rt, t)) return;
   const int tid = threadIdx.x;
-  const int64_t ct_end = (cw + 1) * cpw < n_ct ? (cw + 1) * cpw : n_ct;
-  for (int64_t ct = cw * cpw; ct < ct_end; ++ct) {
+  const int64_t ct0 = cw * cpw, ct_end = (cw + 1) * cpw < n_ct ? (cw + 1) * cpw : n_ct;
+  // staging: thread -> row tid/8, 16 columns at (tid%8)*16 of every column tile
+  const int srr = tid >> 3, scc = (tid & 7) * 16;
+  auto staged = [&](int64_t ct) { return srr < t.nvalid && ct * TC + scc < C; };
+  auto load = [&](int64_t ct, GradRaw& q) {
+    if (staged(ct)) grad_load16<DT, MODE>(g, t.src0 + srr, C, ct * TC + scc, q);
+  };
+  auto tile = [&](int64_t ct, const GradRaw& q) {
     const int64_t c0 = ct * TC;
-    if (ct != cw * cpw) __syncthreads();  // (the previous tile's readers are done with lv)
-    {  // stage: thread -> row tid/8, 16 columns at (tid%8)*16
-      const int rr = tid >> 3, cc = (tid & 7) * 16;
+    if (ct != ct0) __syncthreads();  // (the previous tile's readers are done with lv)
+    {
+      const int rr = srr, cc = scc;
       float v[16];
-      if (rr < t.nvalid && c0 + cc < C) {
-        grad_vals16<DT, MODE>(g, t.src0 + rr, C, c0 + cc, tab, v);
+      if (staged(ct)) {
+        grad_finish16<DT, MODE>(q, tab, v);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = 0.0f;
@@ -618,7 +638,7 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
       }
     }
     const int w = tid >> 6, l = tid & 63;
-    if (c0 + 32 * w >= C) continue;
+    if (c0 + 32 * w >= C) return;
     const int cp = l & 15, rseg = l >> 4;
     const int cl = 32 * w + 2 * cp;
     float v[8][2];
@@ -633,6 +653,26 @@ __global__ void __launch_bounds__(MXT) k_mx_T(GradSrc g, int64_t R, int64_t C, c
     // scale of (column c, block pr_in_g / 32): row-major [C][P/32] or block-major [P/32][C]
     uint8_t* s0 = out_s + t.out_base / 32 + (sfb ? (t.pr_in_g / 32) * C + c : c * (t.P / 32) + t.pr_in_g / 32);
     mx_quant_pair_T<SR>(v, rseg, t.src0 + rseg * 8, C, c, base, o0, o0 + t.P, s0, s0 + (sfb ? 1 : t.P / 32));
+  };
+  if constexpr (MODE >= 2) {
+    // several column tiles per workgroup: the next tile's loads in flight
+    // while a tile is staged and quantised (two named register sets, not
+    // indexed by the tile's parity)
+    GradRaw qa, qb;
+    load(ct0, qa);
+    for (int64_t ct = ct0; ct < ct_end; ct += 2) {
+      if (ct + 1 < ct_end) load(ct + 1, qb);
+      tile(ct, qa);
+      if (ct + 1 >= ct_end) break;
+      if (ct + 2 < ct_end) load(ct + 2, qa);
+      tile(ct + 1, qb);
+    }
+  } else {  // (one tile per workgroup: a second set would only cost occupancy)
+    for (int64_t ct = ct0; ct < ct_end; ++ct) {
+      GradRaw q;
+      load(ct, q);
+      tile(ct, q);
+    }
   }
 }
 
@@ -647,7 +687,9 @@ static void launch_grad(int transpose, bool sr, const GradSrc& g, int64_t R, int
     else hipLaunchKernelGGL((k_mx_rows<DT, MODE, false>), grid, dim3(256), 0, s, g, R, C, base, oc, os, tab);
   } else {
     const int64_t n_ct = (C + TC - 1) / TC, n_rt = (max_pr + TR - 1) / TR;
-    // column tiles per workgroup: MX_T_CPW with a table to stage, else 1
+    // column tiles per workgroup where a table is staged (staged once; the
+    // next tile's loads in flight during each tile), else 1 (measured: the
+    // gathered rows of MODE 1 go faster one tile per workgroup)
     const int cpw = MODE >= 2 ? MX_T_CPW : 1;
     const int64_t n_cw = (n_ct + cpw - 1) / cpw;
     // (MODE != 1: four row tiles per span and a multiple of 8 workgroups;
