@@ -679,7 +679,7 @@ def main():
             print(f"- source_sha256 = {source_sha256(PMC_PROFILE[args.pmc_summary[2]][1])}")
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     c, ms_step, wall, per, off, off_pad, mxv, payload, small, zero_fill, device_error, graph_run = gpu_run(args.steps, args.warmup,
